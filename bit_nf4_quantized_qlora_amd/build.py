@@ -1,0 +1,57 @@
+"""Build libqlora.so (gfx950) in-tree from csrc/*.hip with hipcc.
+
+Every call recompiles: the objects go to ``_build/`` next to this file and the
+shared library to ``libqlora.so`` beside them.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libqlora.so")
+SOURCES = ["capi.hip", "quantize.hip", "dequant.hip", "lora_gemm.hip", "linear_fwd.hip", "linear_bwd.hip"]
+ARCH = "gfx950"
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    # packed fp32 VALU ops stay off: the kernels use scalar fp32 only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(ln for ln in p.stderr.splitlines() if "not a recognized feature" not in ln)
+    if p.returncode != 0:
+        raise RuntimeError(f"command failed ({p.returncode}): {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
+    cmds = [[cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=jobs or min(8, len(cmds))) as ex:
+        for msg in ex.map(_run, cmds):
+            if verbose and msg.strip():
+                print(msg)
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,226 @@
+// capi.hip -- the extern "C" entry points declared in include/qlora.h:
+// host-side argument checks, workspace carving, and kernel enqueueing.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "qlora_internal.h"
+
+namespace qlora {
+
+const Thresholds &nf4_thresholds() {
+  // T_j = smallest float32 strictly above the exact midpoint of levels j and
+  // j+1 (the midpoint of two float32 values is exact in double).  Then
+  // x >= T_j <=> x is nearer to a level above j, with an exact tie at the
+  // midpoint going to the lower level.
+  static const Thresholds T = [] {
+    Thresholds t;
+    for (int j = 0; j < 15; ++j) {
+      float a, b;
+      std::memcpy(&a, &kNF4Bits[j], 4);
+      std::memcpy(&b, &kNF4Bits[j + 1], 4);
+      const double mid = ((double)a + (double)b) * 0.5;
+      float v = (float)mid;
+      if ((double)v <= mid) v = std::nextafter(v, INFINITY);
+      t.t[j] = v;
+    }
+    return t;
+  }();
+  return T;
+}
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *where) {
+  return fail(QLORA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // sanity bound on n*k and M*k, M*n
+
+int check_shape(int64_t n, int64_t k) {
+  if (n < 1 || k < kBlock || k % kBlock != 0)
+    return fail(QLORA_ERR_BAD_SHAPE, "weight shape [%lld, %lld]: need n >= 1, k >= 64, k %% 64 == 0",
+                (long long)n, (long long)k);
+  if (n > kMaxElems / k) return fail(QLORA_ERR_BAD_SHAPE, "weight too large");
+  return QLORA_OK;
+}
+
+int check_weight(const qlora_nf4_weight *w) {
+  if (!w) return fail(QLORA_ERR_NULL_ARG, "weight descriptor is NULL");
+  if (int e = check_shape(w->n, w->k)) return e;
+  if (!w->packed || !w->scale_code || !w->group_amax || !w->offset)
+    return fail(QLORA_ERR_NULL_ARG, "a weight buffer is NULL");
+  if (!aligned16(w->packed) || !aligned16(w->scale_code) || !aligned16(w->group_amax) || !aligned16(w->offset))
+    return fail(QLORA_ERR_MISALIGNED, "weight buffers must be 16-byte aligned");
+  return QLORA_OK;
+}
+
+Nf4View view_of(const qlora_nf4_weight *w) {
+  Nf4View v;
+  v.n = w->n;
+  v.k = w->k;
+  v.nb = w->n * w->k / kBlock;
+  v.ng = ceil_div(v.nb, kGroup);
+  v.packed = w->packed;
+  v.scale_code = w->scale_code;
+  v.group_amax = w->group_amax;
+  v.offset = w->offset;
+  return v;
+}
+
+int check_linear(const qlora_nf4_weight *w, int64_t M, int r, float alpha) {
+  if (int e = check_weight(w)) return e;
+  if (M < 0) return fail(QLORA_ERR_BAD_SHAPE, "M = %lld < 0", (long long)M);
+  if (M > kMaxElems / std::max<int64_t>(w->k, w->n)) return fail(QLORA_ERR_BAD_SHAPE, "M too large");
+  if (r < 1 || r > 128) return fail(QLORA_ERR_BAD_RANK, "rank r = %d outside [1, 128]", r);
+  if (!std::isfinite(alpha)) return fail(QLORA_ERR_BAD_ALPHA, "alpha is not finite");
+  return QLORA_OK;
+}
+
+int check_tensor(const void *p, const char *name) {
+  if (!p) return fail(QLORA_ERR_NULL_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(QLORA_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+  return QLORA_OK;
+}
+
+int check_ws(void *ws, size_t have, size_t need) {
+  if (need == 0) return QLORA_OK;
+  if (!ws) return fail(QLORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (have < need) return fail(QLORA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+  if (!aligned16(ws)) return fail(QLORA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  return QLORA_OK;
+}
+
+size_t quantize_ws(int64_t n, int64_t k) {
+  const int64_t nb = n * k / kBlock, ng = ceil_div(nb, kGroup);
+  return align_up((size_t)nb * sizeof(float), 256) + align_up((size_t)ng * sizeof(double), 256);
+}
+
+}  // namespace
+}  // namespace qlora
+
+using namespace qlora;
+
+extern "C" {
+
+int qlora_nf4_sizes(int64_t n, int64_t k, size_t *packed_bytes, size_t *scale_code_bytes, size_t *group_count) {
+  if (int e = check_shape(n, k)) return e;
+  const int64_t nb = n * k / kBlock;
+  if (packed_bytes) *packed_bytes = (size_t)(n * k / 2);
+  if (scale_code_bytes) *scale_code_bytes = (size_t)nb;
+  if (group_count) *group_count = (size_t)ceil_div(nb, kGroup);
+  return QLORA_OK;
+}
+
+size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k) {
+  if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k) return 0;
+  return quantize_ws(n, k);
+}
+
+int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws, size_t ws_bytes, void *stream) {
+  if (int e = check_weight(out)) return e;
+  if (int e = check_tensor(W, "W")) return e;
+  const size_t need = quantize_ws(out->n, out->k);
+  if (int e = check_ws(ws, ws_bytes, need)) return e;
+  const int64_t nb = out->n * out->k / kBlock;
+  float *ws_absmax = static_cast<float *>(ws);
+  double *ws_sum = reinterpret_cast<double *>(static_cast<char *>(ws) + align_up((size_t)nb * sizeof(float), 256));
+  hipError_t e = launch_quantize(W, out->n, out->k, out->packed, out->scale_code, out->group_amax, out->offset,
+                                 ws_absmax, ws_sum, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qlora_quantize_nf4_dq");
+  return QLORA_OK;
+}
+
+int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream) {
+  if (int e = check_weight(w)) return e;
+  if (int e = check_tensor(W_bf16, "W_bf16")) return e;
+  hipError_t e = launch_dequant(view_of(w), W_bf16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qlora_dequant_bf16");
+  return QLORA_OK;
+}
+
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r) {
+  if (n < 1 || k < kBlock || k % kBlock != 0 || M < 0 || r < 1 || r > 128) return 0;
+  if (n > kMaxElems / k || M > kMaxElems / std::max<int64_t>(k, n)) return 0;
+  if (M == 0) return 0;
+  return std::max(fwd_workspace_bytes(M, n, k, r), bwd_workspace_bytes(M, n, k, r));
+}
+
+int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B,
+                     int r, float alpha, uint16_t *Y, float *H_out, void *ws, size_t ws_bytes, void *stream) {
+  if (int e = check_linear(w, M, r, alpha)) return e;
+  if (M == 0) return QLORA_OK;
+  if (int e = check_tensor(X, "X")) return e;
+  if (int e = check_tensor(A, "A")) return e;
+  if (int e = check_tensor(B, "B")) return e;
+  if (int e = check_tensor(Y, "Y")) return e;
+  if (H_out && !aligned16(H_out)) return fail(QLORA_ERR_MISALIGNED, "H_out is not 16-byte aligned");
+  if (int e = check_ws(ws, ws_bytes, fwd_workspace_bytes(M, w->n, w->k, r))) return e;
+  LinearArgs a{view_of(w), M, r, (float)alpha / (float)r};
+  hipError_t e = launch_linear_fwd(a, X, A, B, Y, H_out, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd");
+  return QLORA_OK;
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int r, float alpha, const float *H, uint16_t *dX, uint16_t *dA,
+                     uint16_t *dB, void *ws, size_t ws_bytes, void *stream) {
+  if (int e = check_linear(w, M, r, alpha)) return e;
+  if (int e = check_tensor(dA, "dA")) return e;
+  if (int e = check_tensor(dB, "dB")) return e;
+  if (M > 0) {
+    if (int e = check_tensor(X, "X")) return e;
+    if (int e = check_tensor(dY, "dY")) return e;
+    if (int e = check_tensor(A, "A")) return e;
+    if (int e = check_tensor(B, "B")) return e;
+    if (dX && !aligned16(dX)) return fail(QLORA_ERR_MISALIGNED, "dX is not 16-byte aligned");
+    if (H && !aligned16(H)) return fail(QLORA_ERR_MISALIGNED, "H is not 16-byte aligned");
+    if (int e = check_ws(ws, ws_bytes, bwd_workspace_bytes(M, w->n, w->k, r))) return e;
+  }
+  LinearArgs a{view_of(w), M, r, (float)alpha / (float)r};
+  hipError_t e = launch_linear_bwd(a, X, dY, A, B, H, dX, dA, dB, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qlora_linear_bwd");
+  return QLORA_OK;
+}
+
+void qlora_nf4_codebook(float out[16]) {
+  for (int j = 0; j < 16; ++j) std::memcpy(&out[j], &kNF4Bits[j], 4);
+}
+
+void qlora_nf4_thresholds(float out[15]) {
+  const Thresholds &t = nf4_thresholds();
+  for (int j = 0; j < 15; ++j) out[j] = t.t[j];
+}
+
+const char *qlora_strerror(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL_ARG: return "null argument";
+    case QLORA_ERR_BAD_SHAPE: return "bad shape";
+    case QLORA_ERR_BAD_RANK: return "bad LoRA rank";
+    case QLORA_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_HIP: return "HIP runtime error";
+    case QLORA_ERR_BAD_ALPHA: return "alpha is not finite";
+    default: return "unknown status";
+  }
+}
+
+const char *qlora_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// lora_gemm.h -- skinny LoRA products and small layout kernels (lora_gemm.hip),
+// plus the guarded 8-element loader shared by the tiled kernels.
+#pragma once
+
+#include <algorithm>
+#include <type_traits>
+
+#include "qlora_internal.h"
+
+namespace qlora {
+
+__device__ __forceinline__ int64_t ceil_div_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// 8 consecutive bf16 of a row-major matrix (row stride ld) at (row, col..col+7);
+// elements outside [0, nrows) x [0, ncols) read as zero.  vec_ok: ld % 8 == 0
+// (then an in-range chunk is one 16-byte load).
+__device__ __forceinline__ u32x4_t load8(const uint16_t *m, int64_t ld, int64_t nrows, int64_t ncols, int64_t row,
+                                         int64_t col, bool vec_ok) {
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (row < nrows && col < ncols) {
+    const uint16_t *p = m + row * ld + col;
+    if (vec_ok && col + 8 <= ncols) {
+      v = *reinterpret_cast<const u32x4_t *>(p);
+    } else {
+      uint32_t e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = (col + i < ncols) ? p[i] : 0u;
+      v = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+    }
+  }
+  return v;
+}
+
+struct SplitPlan {
+  int splits = 1;
+  int steps_per_split = 1;
+};
+
+int lora_rank_pad(int r);  // r rounded up to a multiple of 32
+SplitPlan plan_split(int64_t tiles, int64_t steps);
+
+hipError_t launch_nt_splitk(const uint16_t *P, int64_t rowsP, const uint16_t *Q, int rowsQ, int RP, int64_t lenC,
+                            int64_t ld, const SplitPlan &sp, float *part, hipStream_t s);
+hipError_t launch_tn_splitk(const uint16_t *P, int64_t M, int64_t D, const uint16_t *Qt, int64_t ldq, int RP,
+                            const SplitPlan &sp, float *part, hipStream_t s);
+hipError_t launch_reduce_rows(const float *part, int S, int64_t R, int RP, int r, float scale, float *out_f32,
+                              uint16_t *out_b, uint16_t *out_bt, int64_t ldt, hipStream_t s);
+hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool transpose, uint16_t *out,
+                              hipStream_t s);
+hipError_t launch_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
+                                int64_t ldo, hipStream_t s);
+hipError_t launch_scale_transpose_f32(const float *H, int64_t M, int r, float scale, uint16_t *out, int RP,
+                                      int64_t ldo, hipStream_t s);
+hipError_t launch_fill_zero_u16(uint16_t *p, int64_t n, hipStream_t s);
+
+}  // namespace qlora

@@ -1,0 +1,53 @@
+// qlora_internal.h -- host-side launch interface between the C ABI (capi.hip)
+// and the kernel translation units.  Not part of the public API.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlora_device.h"
+
+namespace qlora {
+
+// Read-only view of a quantized weight as the kernels take it.
+struct Nf4View {
+  int64_t n, k;
+  int64_t nb;  // n*k/64 blocks
+  int64_t ng;  // ceil(nb/256) groups
+  const uint8_t *packed;
+  const uint8_t *scale_code;
+  const float *group_amax;
+  const float *offset;
+};
+
+const Thresholds &nf4_thresholds();
+
+// quantize.hip
+hipError_t launch_quantize(const float *W, int64_t n, int64_t k, uint8_t *packed, uint8_t *scale_code,
+                           float *group_amax, float *offset, float *ws_absmax, double *ws_group_sum,
+                           hipStream_t s);
+
+// dequant.hip
+hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s);
+
+// linear_fwd.hip / linear_bwd.hip
+struct LinearArgs {
+  Nf4View w;
+  int64_t M;
+  int r;
+  float s;  // fp32(alpha / r)
+};
+
+size_t fwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
+size_t bwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
+
+hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint16_t *A, const uint16_t *B,
+                             uint16_t *Y, float *H_out, void *ws, hipStream_t s);
+hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint16_t *dY, const uint16_t *A,
+                             const uint16_t *B, const float *H, uint16_t *dX, uint16_t *dA, uint16_t *dB,
+                             void *ws, hipStream_t s);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace qlora

@@ -1,0 +1,151 @@
+// quantize.hip -- NF4 + double-quantization encoder for gfx950.
+//
+// "QLoRA, explained." steps 1-3 and "QLoRA Paper Breakdown" sec. 3 (Level 1:
+// blockwise absmax and nearest NF4 code; Level 2: mean-subtracted block
+// constants coded to 8-bit floats with one fp32 constant per 256).
+//
+// Three launches, all HBM-streaming:
+//   k_quantize_blocks  one workgroup per group of 256 blocks (64 KiB of W):
+//                      absmax, codes, packed nibbles, and the group's fp64
+//                      in-order absmax sum;
+//   k_mean             one lane folds the group sums in order -> offset;
+//   k_encode_scales    one wave per group: dev = absmax - offset, group amax,
+//                      E4M3 codes.
+#include "qlora_internal.h"
+
+namespace qlora {
+namespace {
+
+// Index of the nearest NF4 level from the 15 thresholds: a 4-step binary
+// search (each step a compare and selects between uniform thresholds).
+__device__ __forceinline__ uint32_t nf4_code(float x, const Thresholds &T) {
+  const bool b3 = x >= T.t[7];
+  const bool b2 = x >= (b3 ? T.t[11] : T.t[3]);
+  const float t1 = b3 ? (b2 ? T.t[13] : T.t[9]) : (b2 ? T.t[5] : T.t[1]);
+  const bool b1 = x >= t1;
+  const float t0 = b3 ? (b2 ? (b1 ? T.t[14] : T.t[12]) : (b1 ? T.t[10] : T.t[8]))
+                      : (b2 ? (b1 ? T.t[6] : T.t[4]) : (b1 ? T.t[2] : T.t[0]));
+  const bool b0 = x >= t0;
+  return (uint32_t(b3) << 3) | (uint32_t(b2) << 2) | (uint32_t(b1) << 1) | uint32_t(b0);
+}
+
+// Eight consecutive weights per lane, eight lanes per 64-weight block, so a
+// wave covers 8 blocks (2 KiB) per step and a workgroup of 4 waves covers one
+// group of 256 blocks in 8 steps.
+__global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict__ W, int64_t nb,
+                                                         Thresholds T, uint8_t *__restrict__ packed,
+                                                         float *__restrict__ absmax_out,
+                                                         double *__restrict__ group_sum) {
+  __shared__ float s_absmax[kGroup];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t first = (int64_t)blockIdx.x * kGroup;
+  const int nblk = (int)min<int64_t>(kGroup, nb - first);
+
+#pragma unroll 2
+  for (int step = 0; step < 8; ++step) {
+    const int lb = wave * 64 + step * 8 + (lane >> 3);  // block within the group
+    const bool valid = lb < nblk;
+    const int64_t e0 = (first + lb) * kBlock + (lane & 7) * 8;
+    f32x4_t v0 = {0.f, 0.f, 0.f, 0.f}, v1 = v0;
+    if (valid) {
+      v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(W + e0));
+      v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(W + e0) + 1);
+    }
+    float m = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                    fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    m = fmaxf(m, __shfl_xor(m, 4, 64));
+    if (valid) {
+      const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // IEEE round-to-nearest division; an all-zero block normalizes to 0.
+        const float x = m > 0.f ? __fdiv_rn(w[i], m) : 0.f;
+        word |= nf4_code(x, T) << (4 * i);
+      }
+      *reinterpret_cast<uint32_t *>(packed + e0 / 2) = word;
+      if ((lane & 7) == 0) {
+        absmax_out[first + lb] = m;
+        s_absmax[lb] = m;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int i = 0; i < nblk; ++i) acc += (double)s_absmax[i];  // block order
+    group_sum[blockIdx.x] = acc;
+  }
+}
+
+// offset = fp32( (in-order fp64 fold of the group sums) / nb ).
+__global__ __launch_bounds__(64) void k_mean(const double *__restrict__ group_sum, int64_t ng, int64_t nb,
+                                            float *__restrict__ offset) {
+  if (threadIdx.x != 0) return;
+  double acc = 0.0;
+  int64_t g = 0;
+  for (; g + 4 <= ng; g += 4) {
+    const double a = group_sum[g], b = group_sum[g + 1], c = group_sum[g + 2], d = group_sum[g + 3];
+    acc += a;
+    acc += b;
+    acc += c;
+    acc += d;
+  }
+  for (; g < ng; ++g) acc += group_sum[g];
+  *offset = (float)(acc / (double)nb);
+}
+
+// One wave per group, four block constants per lane.
+__global__ __launch_bounds__(256) void k_encode_scales(const float *__restrict__ absmax, int64_t nb,
+                                                       int64_t ng, const float *__restrict__ offset_p,
+                                                       uint8_t *__restrict__ scale_code,
+                                                       float *__restrict__ group_amax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= ng) return;
+  const float offset = *offset_p;
+  const int64_t b0 = g * kGroup + lane * 4;
+  float dev[4];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dev[i] = 0.f;
+    if (b0 + i < nb) {
+      dev[i] = __fsub_rn(absmax[b0 + i], offset);
+      m = fmaxf(m, fabsf(dev[i]));
+    }
+  }
+  m = wave_max(m);
+  uint32_t codes = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t c = m > 0.f ? e4m3_encode_rne(__fdiv_rn(dev[i], m)) : 0u;
+    codes |= c << (8 * i);
+  }
+  if (b0 + 4 <= nb) {
+    *reinterpret_cast<uint32_t *>(scale_code + b0) = codes;
+  } else {
+    for (int i = 0; i < 4; ++i)
+      if (b0 + i < nb) scale_code[b0 + i] = (uint8_t)(codes >> (8 * i));
+  }
+  if (lane == 0) group_amax[g] = m;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float *W, int64_t n, int64_t k, uint8_t *packed, uint8_t *scale_code,
+                           float *group_amax, float *offset, float *ws_absmax, double *ws_group_sum,
+                           hipStream_t s) {
+  const int64_t nb = n * k / kBlock;
+  const int64_t ng = ceil_div(nb, kGroup);
+  hipLaunchKernelGGL(k_quantize_blocks, dim3((unsigned)ng), dim3(256), 0, s, W, nb, nf4_thresholds(), packed,
+                     ws_absmax, ws_group_sum);
+  hipLaunchKernelGGL(k_mean, dim3(1), dim3(64), 0, s, ws_group_sum, ng, nb, offset);
+  hipLaunchKernelGGL(k_encode_scales, dim3((unsigned)ceil_div(ng, 4)), dim3(256), 0, s, ws_absmax, nb, ng,
+                     offset, scale_code, group_amax);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

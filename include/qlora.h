@@ -1,0 +1,151 @@
+/*
+ * qlora.h -- C ABI of libqlora.so: the frozen-base linear layer of QLoRA with
+ * NF4 weights and double-quantized block constants, on AMD MI355X (gfx950).
+ *
+ * Method sources (web pages about QLoRA, Dettmers et al. 2023):
+ *   "QLoRA, explained."  method steps 1-5 and the symbol list;
+ *   "QLoRA Paper Breakdown: 4-Bit NormalFloat (NF4), Double Quantization, and
+ *    Paged Optimizers"  sections 2 (codebook), 3 (blockwise quantization and
+ *    double quantization), 4 (dequantization helper, forward pass, backward);
+ *   "QLoRA Explained: What Actually Trains in 4 Bits? | Part 2/6"  (worked
+ *    lookup and bits-per-weight arithmetic).
+ *
+ * Conventions shared by every call
+ *   - Shapes follow PyTorch nn.Linear: W is [n, k] row-major (out, in); the
+ *     activations X are [M, k]; Y and dY are [M, n]; LoRA A is [r, k] and
+ *     B is [n, r] (the breakdown's L_1 = A^T, L_2 = B^T).  All row-major,
+ *     densely packed (row stride == row length).
+ *   - bfloat16 tensors travel as uint16_t bit patterns.
+ *   - Every pointer argument to a tensor is DEVICE memory owned by the
+ *     caller; the library never allocates, frees or keeps a pointer after the
+ *     call returns.  Pointers must be 16-byte aligned.  Outputs must not
+ *     overlap inputs or each other.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Each call checks
+ *     its arguments on the host, enqueues its kernels on `stream` and returns
+ *     without synchronizing; faults inside a kernel surface at the caller's
+ *     next synchronization.
+ *   - Return value: QLORA_OK (0) or a negative QLORA_ERR_* code; nothing is
+ *     enqueued when an argument check fails.  qlora_last_error() gives a
+ *     per-thread message for the last failure.
+ *   - Weights must be finite; the encoding of NaN / Inf is not defined.
+ */
+#ifndef QLORA_H_
+#define QLORA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL_ARG = -1,    /* a required pointer is NULL                         */
+  QLORA_ERR_BAD_SHAPE = -2,   /* n < 1, k < 64, k % 64 != 0, M < 0, or too large      */
+  QLORA_ERR_BAD_RANK = -3,    /* r outside [1, 128]                                  */
+  QLORA_ERR_MISALIGNED = -4,  /* a tensor pointer is not 16-byte aligned              */
+  QLORA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes */
+  QLORA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed           */
+  QLORA_ERR_BAD_ALPHA = -7    /* alpha is not finite                                  */
+};
+
+/*
+ * A quantized frozen weight W [n, k] ("QLoRA, explained.", symbol list: W^NF4
+ * plus the per-block and per-group constants; "QLoRA Paper Breakdown" sec. 3).
+ * Block b = 64 consecutive elements of row-major W (so k % 64 == 0 keeps a
+ * block inside one row); group g = 256 consecutive blocks; nb = n*k/64,
+ * ng = ceil(nb/256).  All buffers are device memory owned by the caller.
+ */
+typedef struct qlora_nf4_weight {
+  int64_t n, k;
+  uint8_t *packed;      /* [n*k/2] NF4 codes, byte i = code[2i] | code[2i+1] << 4      */
+  uint8_t *scale_code;  /* [nb] OCP E4M3FN code of (absmax_b - offset) / group_amax_g   */
+  float *group_amax;    /* [ng] second-level constant: max |absmax_b - offset| in g     */
+  float *offset;        /* [1] per-tensor mean of the fp32 block absmax values          */
+} qlora_nf4_weight;
+
+/* Sizes of the four buffers of an [n, k] weight.  Host only; no GPU use.
+ * Returns QLORA_ERR_BAD_SHAPE unless n >= 1, k >= 64 and k % 64 == 0. */
+int qlora_nf4_sizes(int64_t n, int64_t k, size_t *packed_bytes, size_t *scale_code_bytes,
+                    size_t *group_count);
+
+/* Workspace (device bytes) needed by qlora_quantize_nf4_dq: nb fp32 block
+ * absmax values and ng fp64 group partial sums.  0 for an invalid shape. */
+size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
+
+/*
+ * Quantize a float32 weight W [n, k] (device) into `out` (its n, k must be
+ * set and its four buffers allocated).
+ * "QLoRA, explained." steps 1-3; "QLoRA Paper Breakdown" sec. 3 Level 1 and
+ * Level 2:
+ *   absmax_b = max |w| over block b;  x = fp32(w / absmax_b) (0 if absmax_b=0)
+ *   code = index of the nearest NF4 level (ties to the lower index)
+ *   offset = fp32( (sum over groups, in order, of the fp64 in-order sum of the
+ *            group's absmax) / nb )
+ *   dev_b = fp32(absmax_b - offset); group_amax_g = max |dev_b| over g
+ *   scale_code_b = E4M3FN round-to-nearest-even of fp32(dev_b / group_amax_g)
+ *                  (0x00 when group_amax_g == 0)
+ * The result is bit-for-bit deterministic.  `ws` >= qlora_quantize_workspace_bytes.
+ */
+int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/*
+ * Dequantize to bfloat16: W_bf16 [n, k] (device).  "QLoRA Paper Breakdown"
+ * sec. 4 Dequantization Helper; "QLoRA, explained." step 4:
+ *   s_b = fp32( fp32(decode(scale_code_b) * group_amax_g) + offset )
+ *   w_hat = bf16_round_nearest_even( fp32(q[code] * s_b) )
+ * Bit-for-bit identical to the operand the fused linear kernels use.
+ */
+int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream);
+
+/* Workspace (device bytes) for qlora_linear_fwd / qlora_linear_bwd at these
+ * sizes (the larger of the two).  0 for an invalid shape or rank. */
+size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
+
+/*
+ * Forward pass ("QLoRA Paper Breakdown" sec. 4 Forward Pass):
+ *   H = X A^T                               [M, r], fp32 accumulation
+ *   Y = bf16( X w_hat^T + s * H B^T ),      s = fp32(alpha / r)
+ * w_hat is dequantized on the fly inside the kernels (never written to HBM).
+ * X [M, k], A [r, k], B [n, r], Y [M, n] are bf16.  H_out [M, r] fp32 may be
+ * NULL; when given it receives H for qlora_linear_bwd.  M == 0 is a no-op.
+ * `ws` >= qlora_linear_workspace_bytes(M, n, k, r).
+ */
+int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int r, float alpha, uint16_t *Y, float *H_out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/*
+ * Backward pass ("QLoRA Paper Breakdown" sec. 4: dY/dX through the
+ * dequantized W, dL/dW never materialized; "QLoRA, explained." step 5: only
+ * the adapters receive gradients):
+ *   G  = s * dY B                      [M, r]
+ *   dX = bf16( dY w_hat + G A )        [M, k]   (skipped when dX == NULL)
+ *   dB = bf16( s * dY^T H )            [n, r]
+ *   dA = bf16( G^T X )                 [r, k]
+ * H [M, r] fp32 from qlora_linear_fwd, or NULL to recompute it from X and A.
+ * M == 0 writes zeros to dA and dB.  `ws` >= qlora_linear_workspace_bytes.
+ */
+int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY, int64_t M,
+                     const uint16_t *A, const uint16_t *B, int r, float alpha, const float *H,
+                     uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Host copies of the library's constants (host memory, no GPU use):
+ * the 16 NF4 levels ("QLoRA Paper Breakdown" sec. 2) and the 15 float32
+ * decision thresholds (T_j = smallest float32 above the exact midpoint of
+ * levels j and j+1; code = number of thresholds <= x). */
+void qlora_nf4_codebook(float out[16]);
+void qlora_nf4_thresholds(float out[15]);
+
+/* Static text for a status code; per-thread detail of the last failure. */
+const char *qlora_strerror(int status);
+const char *qlora_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_H_ */

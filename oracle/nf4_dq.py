@@ -193,6 +193,13 @@ def nearest_level(normalized, levels) -> np.ndarray:
     return out.reshape(np.shape(normalized))
 
 
+def block_absmax(x, block: int = BLOCK) -> np.ndarray:
+    """Per-block absolute maximum (float32, exact) of consecutive blocks of a
+    flat or row-major float32 tensor [explainer step 2]."""
+    xb = np.asarray(x, dtype=F32).reshape(-1, block)
+    return np.abs(xb).max(axis=1).astype(F32)
+
+
 def blockwise_quantize(x, levels, block: int):
     """Blockwise absmax quantization of a flat float32 vector.
 
@@ -207,7 +214,7 @@ def blockwise_quantize(x, levels, block: int):
     xb = np.asarray(x, dtype=F32).reshape(-1, block)
     if not np.isfinite(xb).all():
         raise ValueError("weights must be finite")
-    absmax = np.abs(xb).max(axis=1).astype(F32)
+    absmax = block_absmax(xb, block)
     safe = np.where(absmax > 0, absmax, F32(1.0)).astype(F32)
     normalized = np.where(absmax[:, None] > 0, xb / safe[:, None], F32(0.0)).astype(F32)
     return nearest_level(normalized, levels), absmax
@@ -343,9 +350,15 @@ def dequant_bf16(packed, scale_code, group_amax, offset, n: int, k: int) -> np.n
     if codes.size != n * k:
         raise ValueError("packed size does not match n*k")
     s = dq_block_scale(scale_code, group_amax, offset)
-    q = nf4_codebook()[codes].reshape(-1, BLOCK)
-    prod = (q * s[:, None]).astype(F32)
-    return bf16_rne_bits(prod).reshape(n, k)
+    return dequant_blocks_bf16(codes.reshape(-1, BLOCK), s).reshape(n, k)
+
+
+def dequant_blocks_bf16(codes, scales) -> np.ndarray:
+    """w_hat = bf16_rne(float32(q[code] * s_b)) for blocks of codes
+    [nblk, 64] with their block scales s_b [nblk] (any subset of blocks)."""
+    q = nf4_codebook()[np.asarray(codes, dtype=np.uint8)].reshape(-1, BLOCK)
+    prod = (q * np.asarray(scales, dtype=F32)[:, None]).astype(F32)
+    return bf16_rne_bits(prod)
 
 
 def storage_bits_per_weight(enc: dict, n: int, k: int) -> float:

@@ -1,0 +1,112 @@
+"""GPU parity of qlora_quantize_nf4_dq and qlora_dequant_bf16 against the
+oracle: bit-exact codes, packed bytes, 8-bit scale codes, group constants,
+mean offset and BF16 weights."""
+import numpy as np
+import pytest
+import torch
+
+from bit_nf4_quantized_qlora_amd import inputs as I
+from gpu_helpers import assert_encoding_equal, encoding_to_host, gpu_quantize, host_bf16, note
+from oracle import nf4_dq
+from oracle_views import OracleWeight
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_nf4_quantized_qlora_amd import qlora
+    return qlora
+
+
+def _gpu_dequant(q, w):
+    out = torch.empty(w.n, w.k, dtype=torch.bfloat16, device="cuda")
+    q.qlora_dequant_bf16(w, out)
+    torch.cuda.synchronize()
+    return host_bf16(out)
+
+
+def _full_check(q, W, ctx):
+    note(f"[encoding] {ctx} shape={W.shape}")
+    n, k = W.shape
+    w = gpu_quantize(q, W)
+    got = encoding_to_host(w)
+    ref = nf4_dq.quantize_nf4_dq(W)
+    assert_encoding_equal(got, ref, ctx)
+    wh = _gpu_dequant(q, w)
+    ref_wh = nf4_dq.dequant_bf16(ref["packed"], ref["scale_code"], ref["group_amax"], ref["offset"], n, k)
+    bad = np.flatnonzero(wh.reshape(-1) != ref_wh.reshape(-1))
+    assert bad.size == 0, f"{ctx} dequant: {bad.size} differ, first {bad[:5]}"
+
+
+def test_tiny_workload(q):
+    w = I.WORKLOADS["tiny"]
+    _full_check(q, I.weight(w, 0), "tiny")
+
+
+def test_decision_thresholds_and_special_values(q):
+    """Blocks whose absmax is exactly 1 carry the 15 thresholds, their float32
+    neighbours, every level, signed zeros and subnormals; other blocks scale
+    the same pattern, hold a single nonzero, or are all zero."""
+    t = np.array(q.qlora_nf4_thresholds(), np.float32)
+    lv = nf4_dq.nf4_codebook()
+    down = np.nextafter(t, np.float32(-np.inf), dtype=np.float32)
+    vals = np.concatenate([t, down, lv, np.array([0.0, -0.0, 1e-45, -1e-45, 1e-38, -3e-39], np.float32)])
+    rows = []
+    for start in range(0, vals.size, 63):
+        blk = np.zeros(64, np.float32)
+        chunk = vals[start:start + 63]
+        blk[0] = 1.0
+        blk[1:1 + chunk.size] = chunk
+        rows.append(blk)
+    base = np.stack(rows)
+    scaled = np.concatenate([base * np.float32(s) for s in (1.0, 0.02, 3.0e-3, 7.5e1, 1e-30)])
+    single = np.zeros((4, 64), np.float32)
+    single[0, 17] = -0.01
+    single[1, 63] = 2.5
+    single[2, 0] = 1e-40
+    W = np.concatenate([scaled, single, np.zeros((3, 64), np.float32)]).astype(np.float32)
+    _full_check(q, W, "thresholds")
+
+
+@pytest.mark.parametrize("shape,seed", [((1, 64), 1), ((5, 3840), 2), ((7, 64 * 37), 3), ((64, 4096), 4),
+                                        ((300, 640), 5)])
+def test_ragged_groups(q, shape, seed):
+    _full_check(q, I.custom_weight(*shape, seed=seed), f"ragged{shape}")
+
+
+def test_degenerate_tensors(q):
+    _full_check(q, np.zeros((16, 512), np.float32), "all-zero")
+    _full_check(q, np.tile(np.linspace(-0.5, 0.5, 64, dtype=np.float32), (32, 4)), "constant-absmax")
+    g = np.random.default_rng(12)
+    heavy = (g.standard_t(2, size=(128, 1024)) * 0.02).astype(np.float32)
+    _full_check(q, heavy, "student-t(2)")
+    _full_check(q, (I.custom_weight(64, 256, seed=6) * np.float32(1e30)).astype(np.float32), "huge")
+    _full_check(q, (I.custom_weight(64, 256, seed=7) * np.float32(1e-36)).astype(np.float32), "denormal-range")
+
+
+def test_q_proj_full_tensor(q):
+    w = I.WORKLOADS["q_proj_7b"]
+    _full_check(q, I.weight(w, 0), "q_proj_7b")
+
+
+@pytest.mark.parametrize("wname,li", [("mlp_7b", 0), ("mlp_7b", 2), ("up_65b", 0), ("block_65b", 0),
+                                      ("block_65b", 6)])
+def test_full_size_sampled(q, wname, li):
+    """Full-size layers: every scale code, group constant and the offset
+    compared whole; packed bytes and BF16 weights on sampled rows."""
+    wl = I.WORKLOADS[wname]
+    W = I.weight(wl, li)
+    note(f"[encoding] {wname}[{li}] {W.shape} sampled")
+    n, k = W.shape
+    ow = OracleWeight(W)
+    w = gpu_quantize(q, W)
+    got = encoding_to_host(w)
+    assert np.array_equal(got["scale_code"], ow.scale_code), "scale_code"
+    assert np.array_equal(got["group_amax"].view(np.uint32), ow.group_amax.view(np.uint32)), "group_amax"
+    assert np.float32(got["offset"]).view(np.uint32) == np.float32(ow.offset).view(np.uint32), "offset"
+    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(li).choice(n, 24, replace=False)]))
+    gp = got["packed"].reshape(n, k // 2)[rows]
+    assert np.array_equal(gp, ow.row_packed(rows)), "packed rows"
+    wh = _gpu_dequant(q, w)[rows]
+    assert np.array_equal(wh, ow.row_what_bits(rows)), "dequant rows"

@@ -1,0 +1,143 @@
+"""GPU parity of qlora_linear_fwd / qlora_linear_bwd against the fp64
+oracle on the same dequantized weights: relative Frobenius error <= 5e-3
+and max |diff| <= 2e-2 * max |ref| for Y, H, dX, dA and dB."""
+import numpy as np
+import pytest
+import torch
+
+from bit_nf4_quantized_qlora_amd import inputs as I
+from gpu_helpers import Linear, assert_close, gpu_quantize, host_bf16, note
+from oracle_views import OracleWeight, bf16_f64, bwd, fwd
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_nf4_quantized_qlora_amd import qlora
+    return qlora
+
+
+def _run_full(q, W, X, A, B, dY, r, alpha, ctx, h_none=False, want_dx=True):
+    """Full comparison of every output (small shapes)."""
+    note(f"[linear] {ctx} W={W.shape} M={X.shape[0]} r={r} alpha={alpha}")
+    ow = OracleWeight(W)
+    What = bf16_f64(ow.row_what_bits(np.arange(W.shape[0])))
+    Xf, Af, Bf, dYf = bf16_f64(X), bf16_f64(A), bf16_f64(B), bf16_f64(dY)
+    Yr, Hr = fwd(Xf, What, Af, Bf, alpha)
+    dXr, dAr, dBr, _ = bwd(Xf, dYf, What, Af, Bf, alpha)
+    lin = Linear(q, gpu_quantize(q, W), X, A, B, r, alpha)
+    Y, H = lin.fwd()
+    dX, dA, dB = lin.bwd(dY, H=None if h_none else H, want_dx=want_dx)
+    torch.cuda.synchronize()
+    if X.shape[0]:
+        assert_close(bf16_f64(host_bf16(Y)), Yr, f"{ctx} Y")
+        assert_close(H.cpu().numpy(), Hr, f"{ctx} H")
+        if want_dx:
+            assert_close(bf16_f64(host_bf16(dX)), dXr, f"{ctx} dX")
+    assert_close(bf16_f64(host_bf16(dA)), dAr, f"{ctx} dA")
+    assert_close(bf16_f64(host_bf16(dB)), dBr, f"{ctx} dB")
+
+
+def _workload_inputs(wl, li, m):
+    W = I.weight(wl, li)
+    A, B = I.adapters(wl, li)
+    return W, I.activation(wl, li, m), A, B, I.grad_output(wl, li, m)
+
+
+def test_tiny_workload(q):
+    wl = I.WORKLOADS["tiny"]
+    W, X, A, B, dY = _workload_inputs(wl, 0, wl.ms[0])
+    _run_full(q, W, X, A, B, dY, wl.r, wl.alpha, "tiny")
+
+
+def test_q_proj_full(q):
+    wl = I.WORKLOADS["q_proj_7b"]
+    W, X, A, B, dY = _workload_inputs(wl, 0, wl.ms[0])
+    _run_full(q, W, X, A, B, dY, wl.r, wl.alpha, "q_proj_7b")
+
+
+@pytest.mark.parametrize("n,k,m,r,alpha,seed", [
+    (200, 192, 37, 5, -3.5, 1),     # ragged n (not a multiple of 8), ragged M, odd rank, negative alpha
+    (1, 64, 1, 1, 16.0, 2),         # one row, one block
+    (300, 640, 130, 100, 32.0, 3),  # rank 100, partial tiles on every axis
+    (96, 256, 65, 128, 16.0, 4),    # maximum rank
+    (256, 1024, 300, 16, 0.0, 5),   # alpha = 0: adapters contribute nothing to Y
+])
+def test_edge_shapes(q, n, k, m, r, alpha, seed):
+    W = I.custom_weight(n, k, seed)
+    X = I.custom_bf16((m, k), seed, 1)
+    dY = I.custom_bf16((m, n), seed, 2)
+    A = I.custom_bf16((r, k), seed, 3, bound=0.05)
+    B = I.custom_bf16((n, r), seed, 4, bound=0.05)
+    _run_full(q, W, X, A, B, dY, r, alpha, f"edge n{n} k{k} m{m} r{r}")
+
+
+def test_bwd_recomputes_h_and_skips_dx(q):
+    W = I.custom_weight(192, 320, 8)
+    X, dY = I.custom_bf16((70, 320), 8, 1), I.custom_bf16((70, 192), 8, 2)
+    A, B = I.custom_bf16((8, 320), 8, 3, bound=0.05), I.custom_bf16((192, 8), 8, 4, bound=0.05)
+    _run_full(q, W, X, A, B, dY, 8, 16.0, "H=None", h_none=True)
+    _run_full(q, W, X, A, B, dY, 8, 16.0, "dX=None", want_dx=False)
+
+
+def test_zero_weight_and_empty_batch(q):
+    W = np.zeros((128, 256), np.float32)
+    X, dY = I.custom_bf16((40, 256), 9, 1), I.custom_bf16((40, 128), 9, 2)
+    A, B = I.custom_bf16((16, 256), 9, 3, bound=0.05), I.custom_bf16((128, 16), 9, 4, bound=0.05)
+    _run_full(q, W, X, A, B, dY, 16, 16.0, "zero W")
+    # M = 0: forward is a no-op; the adapter gradients are zero
+    lin = Linear(q, gpu_quantize(q, I.custom_weight(128, 256, 10)), X[:0], A, B, 16, 16.0)
+    lin.fwd()
+    _, dA, dB = lin.bwd(dY[:0], want_dx=False)
+    torch.cuda.synchronize()
+    assert torch.all(dA.float() == 0) and torch.all(dB.float() == 0)
+
+
+def _sampled(q, wname, li, m=None, backward=True):
+    """Full-size layer: Y and H on sampled rows/columns, dX and dA on sampled
+    64-column blocks over all M, dB on sampled rows."""
+    wl = I.WORKLOADS[wname]
+    m = m or wl.ms[0]
+    W, X, A, B, dY = _workload_inputs(wl, li, m)
+    n, k = W.shape
+    note(f"[linear] {wname}[{li}] W={W.shape} M={m} sampled")
+    lin = Linear(q, gpu_quantize(q, W), X, A, B, wl.r, wl.alpha)
+    Y, H = lin.fwd()
+    if backward:
+        dX, dA, dB = lin.bwd(dY, H=H)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1000 + li)
+    ns = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 40, replace=False)]))
+    ms = np.unique(np.concatenate([[0, m - 1], rng.choice(m, min(m, 24), replace=False)]))
+    kbs = sorted({0, k // 64 - 1, int(rng.integers(k // 64))})
+    kcols = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in kbs])
+    ow = OracleWeight(W)
+    Xf, Af, Bf, dYf = bf16_f64(X), bf16_f64(A), bf16_f64(B), bf16_f64(dY)
+    Yr, Hr = fwd(Xf[ms], bf16_f64(ow.row_what_bits(ns)), Af, Bf[ns], wl.alpha)
+    assert_close(bf16_f64(host_bf16(Y))[np.ix_(ms, ns)], Yr, f"{wname}[{li}] Y")
+    assert_close(H.cpu().numpy()[ms], Hr, f"{wname}[{li}] H")
+    if not backward:
+        return
+    Hfull = Xf @ Af.T
+    Wc = bf16_f64(ow.colblock_what_bits(kbs))
+    dXr, dAr, _, _ = bwd(Xf[:, kcols], dYf, Wc, Af[:, kcols], Bf, wl.alpha, H=Hfull)
+    assert_close(bf16_f64(host_bf16(dX))[:, kcols], dXr, f"{wname}[{li}] dX")
+    assert_close(bf16_f64(host_bf16(dA))[:, kcols], dAr, f"{wname}[{li}] dA")
+    _, _, dBr, _ = bwd(Xf, dYf[:, ns], bf16_f64(ow.row_what_bits(ns)), Af, Bf[ns], wl.alpha, H=Hfull)
+    assert_close(bf16_f64(host_bf16(dB))[ns], dBr, f"{wname}[{li}] dB")
+
+
+@pytest.mark.parametrize("li", [0, 1, 2])
+def test_mlp_7b(q, li):
+    _sampled(q, "mlp_7b", li)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_up_65b_small_m(q, m):
+    _sampled(q, "up_65b", 0, m=m, backward=False)
+
+
+@pytest.mark.parametrize("li", range(7))
+def test_block_65b(q, li):
+    _sampled(q, "block_65b", li)
