@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Benchmark of the NF4 + double-quantized QLoRA frozen-base linear layer on
+one MI355X.
+
+One step = forward of the three LLaMA-7B MLP linears (gate_proj and up_proj
+4096->11008, down_proj 11008->4096; batch 8 x seq 512 = M 4096 rows; LoRA
+r = 64, alpha = 16), then their backward (dX, dA, dB) in reverse order, on
+seeded synthetic inputs already resident in HBM.  `value` is the step's
+algorithmic TFLOP/s: per layer fwd 2MNK + 2Mr(K+N), bwd 2MNK + 4Mr(N+K)
+(the frozen base's dW, which the method never forms, is not counted).
+
+Also reported, each against its roofline:
+  rows.quantize     qlora_quantize_nf4_dq, GB/s on 4 B in + 0.5159 B out per weight
+  rows.dequant      qlora_dequant_bf16, GB/s on 0.5159 B in + 2 B out per weight
+  rows.fwd / .bwd   per-pass TFLOP/s
+  rows.small_m      65B up_proj (8192->22016) forward at M = 1, 4, 16, GB/s on the
+                    packed-weight bytes, rotating 6 weight copies (558 MB) so the
+                    256 MB last-level cache cannot hold them
+  kernels           per-kernel average duration from the library's event timer
+  roofline          the dominant kernel (largest summed time in a step)
+  cpu_baseline      the CPU oracle (NumPy fp64) on a bounded sample of the step
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused NF4-QLoRA linear fwd+bwd TFLOP/s & GB/s, % of MI355X roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="mlp_7b")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--no-extras", action="store_true", help="skip quantize/dequant/small-M rows")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_nf4_quantized_qlora_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def layer_flops(M, N, K, r):
+    fwd = 2 * M * N * K + 2 * M * r * (K + N)
+    bwd = 2 * M * N * K + 4 * M * r * (N + K)
+    return fwd, bwd
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_nf4_quantized_qlora_amd import inputs as I
+    from bit_nf4_quantized_qlora_amd import qlora as q
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    wl = I.WORKLOADS[args.workload]
+    M = wl.ms[0]
+    r, alpha = wl.r, wl.alpha
+    stream = torch.cuda.current_stream()
+
+    def dev16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    # ---------------------------------------------------------------- setup
+    layers = []
+    quant_ms, quant_bytes, deq_ms, deq_bytes = 0.0, 0, 0.0, 0
+    for li, L in enumerate(wl.layers):
+        W = torch.from_numpy(I.weight(wl, li)).to(dev)
+        w = q.NF4Weight.empty(L.n, L.k, dev)
+        qws = torch.empty(q.qlora_quantize_workspace_bytes(L.n, L.k), dtype=torch.uint8, device=dev)
+        q.qlora_quantize_nf4_dq(W, w, qws)                          # untimed first call
+        pb, sb, ng = q.qlora_nf4_sizes(L.n, L.k)
+        enc_bytes = pb + sb + 4 * ng + 4
+        if not args.no_extras:
+            reps = 5
+            e0, e1 = ev(), ev()
+            e0.record()
+            for _ in range(reps):
+                q.qlora_quantize_nf4_dq(W, w, qws)
+            e1.record()
+            torch.cuda.synchronize()
+            quant_ms += e0.elapsed_time(e1) / reps
+            quant_bytes += 4 * L.n * L.k + enc_bytes
+            Wh = torch.empty(L.n, L.k, dtype=torch.bfloat16, device=dev)
+            q.qlora_dequant_bf16(w, Wh)
+            e0, e1 = ev(), ev()
+            e0.record()
+            for _ in range(reps):
+                q.qlora_dequant_bf16(w, Wh)
+            e1.record()
+            torch.cuda.synchronize()
+            deq_ms += e0.elapsed_time(e1) / reps
+            deq_bytes += enc_bytes + 2 * L.n * L.k
+            del Wh
+        del W, qws
+        A, B = I.adapters(wl, li)
+        t = {"L": L, "w": w, "X": dev16(I.activation(wl, li, M)), "dY": dev16(I.grad_output(wl, li, M)),
+             "A": dev16(A), "B": dev16(B)}
+        t["Y"] = torch.empty(M, L.n, dtype=torch.bfloat16, device=dev)
+        t["H"] = torch.empty(M, r, dtype=torch.float32, device=dev)
+        t["dX"] = torch.empty(M, L.k, dtype=torch.bfloat16, device=dev)
+        t["dA"] = torch.empty(r, L.k, dtype=torch.bfloat16, device=dev)
+        t["dB"] = torch.empty(L.n, r, dtype=torch.bfloat16, device=dev)
+        layers.append(t)
+    ws_bytes = max(q.qlora_linear_workspace_bytes(M, t["L"].n, t["L"].k, r) for t in layers)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.empty_cache()
+
+    def fwd_pass():
+        for t in layers:
+            q.qlora_linear_fwd(t["w"], t["X"], t["A"], t["B"], r, alpha, t["Y"], t["H"], ws)
+
+    def bwd_pass():
+        for t in reversed(layers):
+            q.qlora_linear_bwd(t["w"], t["X"], t["dY"], t["A"], t["B"], r, alpha, t["H"], t["dX"], t["dA"],
+                               t["dB"], ws)
+
+    def step():
+        fwd_pass()
+        bwd_pass()
+
+    fwd_flops = bwd_flops = 0
+    for t in layers:
+        f, b = layer_flops(M, t["L"].n, t["L"].k, r)
+        fwd_flops += f
+        bwd_flops += b
+    step_flops = fwd_flops + bwd_flops
+
+    # ---------------------------------------------------------- timed steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # per-pass times
+    def timed(fn, n):
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    fwd_ms = timed(fwd_pass, max(3, args.steps // 2))
+    bwd_ms = timed(bwd_pass, max(3, args.steps // 2))
+
+    # --------------------------------------- per-kernel event timing (second pass)
+    q.qlora_profile_begin()
+    for _ in range(args.steps):
+        step()
+    prof = q.qlora_profile_end()
+    kernels = {name: {"launches_per_step": n / args.steps, "avg_us": 1e3 * ms / n,
+                      "ms_per_step": ms / args.steps} for name, (n, ms) in prof.items()}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    per_launch_flops = {
+        "k_fwd_main": sum(2 * M * t["L"].n * t["L"].k + 2 * M * t["L"].n * r for t in layers) / len(layers),
+        "k_bwd_dx": sum(2 * M * t["L"].n * t["L"].k + 2 * M * t["L"].k * r for t in layers) / len(layers),
+    }
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tc = json.load(f)
+        if tc.get("source_sha256") == source_digest() and dom in tc.get("kernels", {}):
+            kk = tc["kernels"][dom]
+            traffic = kk["fetch_bytes_per_launch"] + kk["write_bytes_per_launch"]
+    if dom in per_launch_flops:
+        ach = per_launch_flops[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                    "flops_per_launch": per_launch_flops[dom], "avg_launch_us": round(kernels[dom]["avg_us"], 2)}
+    else:
+        roofline = {"bound": "unknown", "kernel": dom, "achieved": None, "peak": None, "unit": None,
+                    "frac": None, "traffic": traffic}
+
+    rows = {
+        "fwd": {"ms": round(fwd_ms, 4), "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 1),
+                "frac_bf16_peak": round(fwd_flops / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(bwd_ms, 4), "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 1),
+                "frac_bf16_peak": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+    }
+    if not args.no_extras:
+        rows["quantize"] = {"ms_all_layers": round(quant_ms, 4),
+                            "gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+                            "frac_hbm_peak": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        rows["dequant"] = {"ms_all_layers": round(deq_ms, 4),
+                           "gbps": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1),
+                           "frac_hbm_peak": round(deq_bytes / (deq_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        rows["small_m"] = small_m_rows(q, I, np, torch, dev, dev16, ev)
+
+    calib = None
+    if args.calib_copy_mib:
+        nbytes = args.calib_copy_mib << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        calib = {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes}
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, I, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama7b_mlp_gate_up_down_fwd_bwd", "layers": [[t["L"].name, t["L"].n, t["L"].k]
+                                                                           for t in layers],
+                   "M": M, "global_batch": 8, "seq_len": 512, "lora_r": r, "lora_alpha": alpha,
+                   "weights": "NF4+DQ (block 64, 8-bit E4M3 constants per 256)", "parallelism": "single_gpu"},
+        "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+        "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in sorted(kernels.items())},
+        "source_sha256": source_digest(),
+    }
+    if calib:
+        out["calib_copy"] = calib
+    print(json.dumps(out), flush=True)
+
+
+def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
+    """65B up_proj forward at M = 1, 4, 16 on rotating weight copies."""
+    wl = I.WORKLOADS["up_65b"]
+    L = wl.layers[0]
+    W = torch.from_numpy(I.weight(wl, 0)).to(dev)
+    qws = torch.empty(q.qlora_quantize_workspace_bytes(L.n, L.k), dtype=torch.uint8, device=dev)
+    ws_list = []
+    for _ in range(copies):
+        w = q.NF4Weight.empty(L.n, L.k, dev)
+        q.qlora_quantize_nf4_dq(W, w, qws)
+        ws_list.append(w)
+    del W, qws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    pb, sb, ng = q.qlora_nf4_sizes(L.n, L.k)
+    packed_bytes = pb + sb + 4 * ng
+    A, B = I.adapters(wl, 0)
+    Ad, Bd = dev16(A), dev16(B)
+    out = {"workload": f"up_proj {L.k}->{L.n}", "packed_weight_bytes": packed_bytes, "copies": copies}
+    for m in wl.ms:
+        X = dev16(I.activation(wl, 0, m))
+        Y = torch.empty(m, L.n, dtype=torch.bfloat16, device=dev)
+        H = torch.empty(m, wl.r, dtype=torch.float32, device=dev)
+        lws = torch.empty(q.qlora_linear_workspace_bytes(m, L.n, L.k, wl.r), dtype=torch.uint8, device=dev)
+        for i in range(2 * copies):
+            q.qlora_linear_fwd(ws_list[i % copies], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws)
+        reps = 10 * copies
+        a, b = ev(), ev()
+        a.record()
+        for i in range(reps):
+            q.qlora_linear_fwd(ws_list[i % copies], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws)
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / reps
+        gbps = packed_bytes / (us * 1e-6) / 1e9
+        out[f"M{m}"] = {"us": round(us, 2), "gbps_packed": round(gbps, 1),
+                        "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+    return out
+
+
+def cpu_baseline(wl, I, target_s):
+    """The CPU oracle (as it stands) on a bounded sample of the step: every
+    layer sliced to its first 2048 weight rows (its own NF4+DQ tensor,
+    encoded untimed), all M rows; timed = oracle dequantization to BF16 +
+    fp64 forward + fp64 backward, repeated until target_s has elapsed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import linear, nf4_dq
+    n_s = 2048
+    M = wl.ms[0]
+    prep = []
+    flops = 0
+    for li, L in enumerate(wl.layers):
+        ns = min(n_s, L.n)
+        W = I.weight(wl, li, rows=slice(0, ns))
+        enc = nf4_dq.quantize_nf4_dq(W)
+        A, B = I.adapters(wl, li)
+        X = nf4_dq.bf16_bits_to_f64(I.activation(wl, li, M))
+        dY = nf4_dq.bf16_bits_to_f64(I.grad_output(wl, li, M))[:, :ns]
+        prep.append((enc, ns, L.k, X, dY, nf4_dq.bf16_bits_to_f64(A), nf4_dq.bf16_bits_to_f64(B)[:ns]))
+        f, b = layer_flops(M, ns, L.k, wl.r)
+        flops += f + b
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for enc, ns, k, X, dY, A, B in prep:
+            Wh = nf4_dq.bf16_bits_to_f64(
+                nf4_dq.dequant_bf16(enc["packed"], enc["scale_code"], enc["group_amax"], enc["offset"], ns, k))
+            _, H = linear.fwd(X, Wh, A, B, wl.alpha)
+            linear.bwd(X, dY, Wh, A, B, wl.alpha, H=H)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or reps >= 20:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {"value": round(flops * reps / el / 1e12, 4), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"mlp layers sliced to their first {n_s} weight rows, all {M} rows of X; "
+                      f"oracle bf16 dequant + fp64 fwd + bwd; {reps} rep(s) in {el:.1f} s",
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ pa
 hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s) {
   const int64_t ndw = w.n * w.k / 8;
   const int64_t grid = ceil_div(ndw, 4 * 256);
-  hipLaunchKernelGGL(k_dequant, dim3((unsigned)grid), dim3(256), 0, s,
+  QLORA_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(256), 0, s,
                      reinterpret_cast<const uint32_t *>(w.packed), w.scale_code, w.group_amax, w.offset, ndw,
                      reinterpret_cast<u32x4_t *>(out));
   return hipGetLastError();

@@ -212,7 +212,7 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   QLORA_TRY(launch_reduce_rows(part, l.sp_g.splits, M, RP, r, a.s, nullptr, Gb, Gt, l.Mp, s));
   if (dX != nullptr) {
     const dim3 grid((unsigned)ceil_div(K, DBK), (unsigned)ceil_div(M, DBM));
-    hipLaunchKernelGGL(k_bwd_dx, grid, dim3(256), 0, s, a.w, dY, M, At, Gb, RP, dX);
+    QLORA_LAUNCH("k_bwd_dx", k_bwd_dx, grid, dim3(256), 0, s, a.w, dY, M, At, Gb, RP, dX);
     QLORA_TRY(hipGetLastError());
   }
   QLORA_TRY(launch_tn_splitk(dY, M, N, sHt, l.Mp, RP, l.sp_b, part, s));

@@ -163,7 +163,7 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   e = launch_reduce_rows(part, l.sp.splits, M, l.RP, a.r, a.s, H_out, sH, nullptr, 0, s);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)ceil_div(N, FBN), (unsigned)ceil_div(M, FBM));
-  hipLaunchKernelGGL(k_fwd_main, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y);
+  QLORA_LAUNCH("k_fwd_main", k_fwd_main, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y);
   return hipGetLastError();
 }
 

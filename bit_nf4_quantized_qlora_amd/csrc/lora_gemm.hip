@@ -215,7 +215,7 @@ hipError_t launch_nt_splitk(const uint16_t *P, int64_t rowsP, const uint16_t *Q,
   const dim3 grid((unsigned)ceil_div(rowsP, 64), (unsigned)sp.splits);
   const bool vec_ok = (ld % 8) == 0;
   return dispatch_tj(RP, [&](auto tj) {
-    hipLaunchKernelGGL(k_nt_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, rowsP, Q, rowsQ, lenC, ld,
+    QLORA_LAUNCH("k_nt_splitk", k_nt_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, rowsP, Q, rowsQ, lenC, ld,
                        vec_ok, sp.steps_per_split, part);
     return hipGetLastError();
   });
@@ -226,7 +226,7 @@ hipError_t launch_tn_splitk(const uint16_t *P, int64_t M, int64_t D, const uint1
   const dim3 grid((unsigned)ceil_div(D, 64), (unsigned)sp.splits);
   const bool vec_ok = (D % 8) == 0;
   return dispatch_tj(RP, [&](auto tj) {
-    hipLaunchKernelGGL(k_tn_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, M, D, vec_ok, Qt, ldq,
+    QLORA_LAUNCH("k_tn_splitk", k_tn_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, M, D, vec_ok, Qt, ldq,
                        sp.steps_per_split, part);
     return hipGetLastError();
   });
@@ -235,35 +235,35 @@ hipError_t launch_tn_splitk(const uint16_t *P, int64_t M, int64_t D, const uint1
 hipError_t launch_reduce_rows(const float *part, int S, int64_t R, int RP, int r, float scale, float *out_f32,
                               uint16_t *out_b, uint16_t *out_bt, int64_t ldt, hipStream_t s) {
   const int64_t total = (out_bt ? ldt : R) * RP;
-  hipLaunchKernelGGL(k_reduce_rows, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s, part, S, R, RP, r,
+  QLORA_LAUNCH("k_reduce_rows", k_reduce_rows, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s, part, S, R, RP, r,
                      scale, out_f32, out_b, out_bt, ldt);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool transpose, uint16_t *out,
                               hipStream_t s) {
-  hipLaunchKernelGGL(k_reduce_cols, dim3((unsigned)ceil_div((int64_t)r * D, 256)), dim3(256), 0, s, part, S, D,
+  QLORA_LAUNCH("k_reduce_cols", k_reduce_cols, dim3((unsigned)ceil_div((int64_t)r * D, 256)), dim3(256), 0, s, part, S, D,
                      RP, r, transpose, out);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
                                 int64_t ldo, hipStream_t s) {
-  hipLaunchKernelGGL(k_transpose_pad, dim3((unsigned)ceil_div(out_rows * ldo, 256)), dim3(256), 0, s, in, rows,
+  QLORA_LAUNCH("k_transpose_pad", k_transpose_pad, dim3((unsigned)ceil_div(out_rows * ldo, 256)), dim3(256), 0, s, in, rows,
                      cols, out, out_rows, ldo);
   return hipGetLastError();
 }
 
 hipError_t launch_scale_transpose_f32(const float *H, int64_t M, int r, float scale, uint16_t *out, int RP,
                                       int64_t ldo, hipStream_t s) {
-  hipLaunchKernelGGL(k_scale_transpose_f32, dim3((unsigned)ceil_div((int64_t)RP * ldo, 256)), dim3(256), 0, s, H,
+  QLORA_LAUNCH("k_scale_transpose_f32", k_scale_transpose_f32, dim3((unsigned)ceil_div((int64_t)RP * ldo, 256)), dim3(256), 0, s, H,
                      M, r, scale, out, RP, ldo);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_zero_u16(uint16_t *p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_zero_u16, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, p, n);
+  QLORA_LAUNCH("k_fill_zero_u16", k_fill_zero_u16, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

@@ -65,20 +65,15 @@ __device__ __forceinline__ float block_scale(uint32_t c8, float group_amax, floa
 }
 
 // ---------------------------------------------------------------------------
-// bfloat16 round-to-nearest-even of two floats into one packed dword
-// (first argument in the low half).  Integer form: finite inputs only.
+// bfloat16 round-to-nearest-even of two floats into one packed dword (first
+// argument in the low half): gfx950's v_cvt_pk_bf16_f32.  Checked on MI355X
+// to equal integer round-to-nearest-even, u + 0x7FFF + ((u >> 16) & 1) >> 16,
+// for every non-NaN float32 input, denormals included.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
-#if QLORA_HW_BF16_CVT
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
-#else
-  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a += 0x7FFFu + ((a >> 16) & 1u);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // high halves of a (low) and b (high)
-#endif
 }
 
 // ---------------------------------------------------------------------------

@@ -47,6 +47,26 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
                              const uint16_t *B, const float *H, uint16_t *dX, uint16_t *dA, uint16_t *dB,
                              void *ws, hipStream_t s);
 
+// Opt-in per-kernel event timing (profile.hip): a scope around each launch.
+class ProfScope {
+ public:
+  ProfScope(const char *name, hipStream_t s);
+  ~ProfScope();
+  ProfScope(const ProfScope &) = delete;
+  ProfScope &operator=(const ProfScope &) = delete;
+
+ private:
+  const char *name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+};
+
+#define QLORA_LAUNCH(name, kernel, grid, block, shmem, stream, ...)            \
+  do {                                                                         \
+    ::qlora::ProfScope qlora_prof_scope_(name, stream);                        \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);       \
+  } while (0)
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

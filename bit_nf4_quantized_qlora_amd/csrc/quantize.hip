@@ -140,10 +140,10 @@ hipError_t launch_quantize(const float *W, int64_t n, int64_t k, uint8_t *packed
                            hipStream_t s) {
   const int64_t nb = n * k / kBlock;
   const int64_t ng = ceil_div(nb, kGroup);
-  hipLaunchKernelGGL(k_quantize_blocks, dim3((unsigned)ng), dim3(256), 0, s, W, nb, nf4_thresholds(), packed,
+  QLORA_LAUNCH("k_quantize_blocks", k_quantize_blocks, dim3((unsigned)ng), dim3(256), 0, s, W, nb, nf4_thresholds(), packed,
                      ws_absmax, ws_group_sum);
-  hipLaunchKernelGGL(k_mean, dim3(1), dim3(64), 0, s, ws_group_sum, ng, nb, offset);
-  hipLaunchKernelGGL(k_encode_scales, dim3((unsigned)ceil_div(ng, 4)), dim3(256), 0, s, ws_absmax, nb, ng,
+  QLORA_LAUNCH("k_mean", k_mean, dim3(1), dim3(64), 0, s, ws_group_sum, ng, nb, offset);
+  QLORA_LAUNCH("k_encode_scales", k_encode_scales, dim3((unsigned)ceil_div(ng, 4)), dim3(256), 0, s, ws_absmax, nb, ng,
                      offset, scale_code, group_amax);
   return hipGetLastError();
 }

@@ -52,6 +52,11 @@ _SIGS = {
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_nf4_thresholds": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_strerror": (ctypes.c_char_p, [_c_int]),
+    "qlora_profile_begin": (_c_int, []),
+    "qlora_profile_end": (_c_int, []),
+    "qlora_profile_count": (_c_int, []),
+    "qlora_profile_entry": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_c_i64),
+                                     ctypes.POINTER(ctypes.c_double)]),
     "qlora_last_error": (ctypes.c_char_p, []),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -192,6 +197,22 @@ def qlora_strerror(status: int) -> str:
 
 def qlora_last_error() -> str:
     return _lib.qlora_last_error().decode()
+
+
+def qlora_profile_begin() -> None:
+    _check("qlora_profile_begin", _lib.qlora_profile_begin())
+
+
+def qlora_profile_end() -> dict:
+    """Stop per-kernel event timing; {kernel name: (launches, total ms)}."""
+    _check("qlora_profile_end", _lib.qlora_profile_end())
+    out = {}
+    for i in range(_lib.qlora_profile_count()):
+        name, n, ms = ctypes.c_char_p(), _c_i64(), ctypes.c_double()
+        _check("qlora_profile_entry", _lib.qlora_profile_entry(i, ctypes.byref(name), ctypes.byref(n),
+                                                               ctypes.byref(ms)))
+        out[name.value.decode()] = (n.value, ms.value)
+    return out
 
 
 def raw_library() -> ctypes.CDLL:
