@@ -18,6 +18,9 @@ SOURCES = ["capi.hip", "profile.hip", "quantize.hip", "dequant.hip", "lora_gemm.
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    # every multiply and add is rounded on its own (the block scale is defined
+    # with two roundings); HIP would otherwise contract a*b+c into an FMA
+    "-ffp-contract=off",
     # packed fp32 VALU ops stay off: the kernels use scalar fp32 only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]

@@ -51,12 +51,13 @@ int hip_fail(hipError_t e, const char *where) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // sanity bound on n*k and M*k, M*n
+constexpr int64_t kMaxK = int64_t(1) << 22;      // tile-relative byte offsets in the GEMMs stay 32-bit
 
 int check_shape(int64_t n, int64_t k) {
   if (n < 1 || k < kBlock || k % kBlock != 0)
     return fail(QLORA_ERR_BAD_SHAPE, "weight shape [%lld, %lld]: need n >= 1, k >= 64, k %% 64 == 0",
                 (long long)n, (long long)k);
-  if (n > kMaxElems / k) return fail(QLORA_ERR_BAD_SHAPE, "weight too large");
+  if (n > kMaxElems / k || k > kMaxK) return fail(QLORA_ERR_BAD_SHAPE, "weight too large");
   return QLORA_OK;
 }
 
@@ -128,7 +129,7 @@ int qlora_nf4_sizes(int64_t n, int64_t k, size_t *packed_bytes, size_t *scale_co
 }
 
 size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k) {
-  if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k) return 0;
+  if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k || k > kMaxK) return 0;
   return quantize_ws(n, k);
 }
 
@@ -156,7 +157,7 @@ int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream
 
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r) {
   if (n < 1 || k < kBlock || k % kBlock != 0 || M < 0 || r < 1 || r > 128) return 0;
-  if (n > kMaxElems / k || M > kMaxElems / std::max<int64_t>(k, n)) return 0;
+  if (n > kMaxElems / k || k > kMaxK || M > kMaxElems / std::max<int64_t>(k, n)) return 0;
   if (M == 0) return 0;
   return std::max(fwd_workspace_bytes(M, n, k, r), bwd_workspace_bytes(M, n, k, r));
 }

@@ -20,113 +20,236 @@
 namespace qlora {
 namespace {
 
-constexpr int FBN = 128, FBM = 128, FLD = 72;
+constexpr int FBN = 256, FBM = 256;  // block tile: weight rows (n) x X rows (m)
 
-__global__ __launch_bounds__(256, 2) void k_fwd_main(Nf4View w, const uint16_t *__restrict__ X, int64_t M,
-                                                     const uint16_t *__restrict__ Bl, int r, int RP,
-                                                     const uint16_t *__restrict__ sH, uint16_t *__restrict__ Y) {
-  __shared__ __align__(16) uint16_t Ps[2 * FBN * FLD];  // W_hat tile [n][k]
-  __shared__ __align__(16) uint16_t Qs[2 * FBM * FLD];  // X tile [m][k]
+// X tile in LDS: [256 m][64 k] bf16, 128 B per row; 16-byte chunk c of row r
+// lives at chunk c ^ (r & 7), so the 16 rows one fragment read touches fall
+// in different banks.
+__device__ __forceinline__ int xsw(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+// Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
+// contiguous run of tiles (m-major, n fastest) so the tiles sharing an X
+// row-panel meet in the same L2.
+__device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
+  const int q = nblocks >> 3, rem = nblocks & 7, x = bid & 7, p = bid >> 3;
+  return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + p;
+}
+
+// C[n][m] = sum_k W_hat[n][k] X[m][k] + sum_j B[n][j] sH[m][j]  ->  Y[m][n]
+// Wave w owns weight rows n0 + 64w .. +63 (four 16-row MFMA tiles) and all
+// 256 X rows (sixteen 16-column tiles): 256 fp32 accumulators per lane.
+// Its NF4 rows are expanded straight into MFMA A-operand registers: lane
+// (li = lane & 15, g = lane >> 4) of row tile rt holds row n0+64w+16rt+li and
+// codes 16g .. 16g+15 of the current 64-weight block (one 8-byte load), used
+// as contraction slots 8t .. 8t+7 of sub-step t; the X fragment reads the
+// same k positions, so the contraction is unchanged.
+//
+// Per 64-wide K step: the X tile of step kt+1 streams global -> LDS with
+// buffer loads (no registers) into the other of two separate LDS arrays
+// (separate objects, so the compiler knows the in-flight copy does not alias
+// the tile being read), the packed codes of step kt+2 are loaded, and the
+// codes of step kt+1 are expanded in eight pieces interleaved with the eight
+// groups of 16 MFMAs of step kt.  Rows past N or M are clamped to a valid
+// row: they only feed accumulators that are never stored.
+struct FwdSmem {
+  uint16_t *x0, *x1;
+  float2 *pair;
+};
+
+template <int BUF>
+__device__ __forceinline__ uint16_t *xbuf(const FwdSmem &sm) { return BUF ? sm.x1 : sm.x0; }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// All per-lane addresses are one 32-bit VGPR offset into a buffer resource
+// plus uniform (scalar) offsets; rows past N or M fall outside the resource's
+// range and read as zero, and only feed accumulators that are never stored.
+template <bool kOddSteps>  // k/64 odd: one trailing step after the two-step loop
+__global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const uint16_t *__restrict__ X, int64_t M,
+                                                    const uint16_t *__restrict__ Bl, int r, int RP,
+                                                    const uint16_t *__restrict__ sH, uint16_t *__restrict__ Y,
+                                                    int tiles_n) {
+  __shared__ __align__(16) uint16_t Xs0[FBM * 64];
+  __shared__ __align__(16) uint16_t Xs1[FBM * 64];
   __shared__ float2 s_pair[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const FwdSmem sm{Xs0, Xs1, s_pair};
+  // wave is uniform across the wave; say so, or wave-dependent scalar
+  // offsets would be made uniform with a per-lane loop
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int64_t n0 = (int64_t)(tile % tiles_n) * FBN, m0 = (int64_t)(tile / tiles_n) * FBM;
   const int64_t N = w.n, K = w.k, nk = K / kBlock;
-  const int64_t n0 = (int64_t)blockIdx.x * FBN, m0 = (int64_t)blockIdx.y * FBM;
   fill_pair_table(s_pair, tid, 256);
   const float offset = *w.offset;
 
-  // Weight staging: thread -> (row tid/2, half tid%2): 16 packed bytes = 32 codes.
-  const int wr = tid >> 1, wh = tid & 1;
-  const bool wvalid = n0 + wr < N;
-  const int64_t wrow = wvalid ? n0 + wr : 0;
-  const uint8_t *wsrc = w.packed + wrow * (K / 2) + wh * 16;
-  const int64_t bbase = wrow * nk;
-
-  u32x4_t wreg = {0u, 0u, 0u, 0u};
-  uint32_t sc = 0;
-  float ga = 0.f;
-  u32x4_t xreg[4];
-  auto gload = [&](int64_t kt) {
-    wreg = *reinterpret_cast<const u32x4_t *>(wsrc + kt * 32);
-    sc = w.scale_code[bbase + kt];
-    ga = w.group_amax[(bbase + kt) >> 8];
+  // Weight rows n0 .. n0+255: lane's row in row tile rt is n0 + 64w + 16rt + li.
+  const int64_t nrows = min<int64_t>(FBN, N - n0);
+  const __amdgpu_buffer_rsrc_t wrs = rsrc(w.packed + n0 * (K / 2), nrows * (K / 2));
+  const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code + n0 * nk, nrows * nk);
+  const __amdgpu_buffer_rsrc_t grs = rsrc(w.group_amax, ceil_div_d(w.nb, kGroup) * 4);
+  const uint32_t wv = (uint32_t)(li * (K / 2) + 8 * g), sv = (uint32_t)(li * nk);
+  const int64_t wrow_w = 64 * wave;  // wave's first row within the tile
+  // X rows m0 .. m0+255, staged global -> LDS: wave-instruction i fills LDS
+  // chunks [512w + 64i, +64): row 64w + 8i + lane/8, logical chunk
+  // (lane & 7) ^ ((lane/8) & 7) (the swizzle of xsw), so only the row term
+  // varies with i and it is uniform.
+  const int64_t xrows = min<int64_t>(FBM, M - m0);
+  const __amdgpu_buffer_rsrc_t xrs = rsrc(X + m0 * K, xrows * K * 2);
+  const uint32_t xv = (uint32_t)(((lane >> 3) * K + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
+  auto xload = [&](int64_t kt, auto BUF) {
+    uint16_t *dst = xbuf<decltype(BUF)::value>(sm);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      xreg[i] = load8(X, K, M, K, m0 + row, kt * 64 + col, true);
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t *P = Ps + buf * FBN * FLD + wr * FLD + wh * 32;
-    const float s = block_scale(sc, ga, offset);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t o[4];
-      dequant_word(wreg[q], s, s_pair, o);
-      *reinterpret_cast<u32x4_t *>(P + 8 * q) = wvalid ? u32x4_t{o[0], o[1], o[2], o[3]} : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    uint16_t *Qb = Qs + buf * FBM * FLD;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<u32x4_t *>(Qb + row * FLD + col) = xreg[i];
-    }
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16, xv,
+                                               (int)((64 * wave + 8 * i) * K * 2 + kt * 128), 0, 0);
   };
 
-  __syncthreads();  // pair table ready
-  gload(0);
-  lstore(0);
+  // Codes of step kt+1 (wa: expanded during step kt) and kt+2 (wb: loaded
+  // during step kt), rotated by copies.
+  u32x2_t wa[4], wb[4];
+  uint32_t sca[4], scb[4];
+  float gaa[4], gab[4];
+  auto wload = [&](int64_t kt, u32x2_t(&wc)[4], uint32_t(&sc)[4], float(&ga)[4]) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int64_t row = wrow_w + 16 * rt;  // uniform part of the lane's row
+      wc[rt] = __builtin_amdgcn_raw_buffer_load_b64(wrs, wv, (int)(row * (K / 2) + kt * 32), 0);
+      sc[rt] = __builtin_amdgcn_raw_buffer_load_b8(srs, sv, (int)(row * nk + kt), 0);
+      const uint32_t gidx = (uint32_t)(((n0 + row) * nk + kt + sv) >> 8);
+      ga[rt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grs, gidx * 4, 0, 0));
+    }
+  };
+  // a[rt][t]: operands of the current step.  The next step's sub-step-1
+  // halves are expanded into an[] during MFMA groups 0-7 (a[][1] is still in
+  // use); its sub-step-0 halves go straight into a[][0] during groups 8-15.
+  u32x4_t a[4][2], an[4];
+  float sn[4];
+  auto expand = [&](int rt, int t, u32x4_t &dst) {
+    if (t == 1) sn[rt] = block_scale(sca[rt], gaa[rt], offset);
+    uint32_t o[4];
+    dequant_word(wa[rt][t], sn[rt], s_pair, o);
+    dst = u32x4_t{o[0], o[1], o[2], o[3]};
+  };
+
+  f32x4_t acc[4][16];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  __syncthreads();  // pair table
+  xload(0, std::integral_constant<int, 0>());
+  wload(0, wa, sca, gaa);
+  wload(min<int64_t>(1, nk - 1), wb, scb, gab);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    expand(rt, 1, a[rt][1]);
+    expand(rt, 0, a[rt][0]);
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) wa[rt] = wb[rt], sca[rt] = scb[rt], gaa[rt] = gab[rt];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  const int wi = wave >> 1, wj = wave & 1;
-  f32x4_t acc[4][4];
+  auto step = [&](int64_t kt, auto BUF) {
+    constexpr int buf = decltype(BUF)::value;
+    // Prefetches past the last step re-read the last step (in bounds, unused).
+    xload(min<int64_t>(kt + 1, nk - 1), std::integral_constant<int, buf ^ 1>());
+    wload(min<int64_t>(kt + 2, nk - 1), wb, scb, gab);
+    // Fragment (column tile ct, sub-step t) sits at xrow[t] + 1024*ct: the
+    // swizzle term depends on (row & 7) == (li & 7) only.
+    const uint16_t *xs = xbuf<buf>(sm);
+    const uint16_t *xrow0 = xs + xsw(li, 2 * g), *xrow1 = xs + xsw(li, 2 * g + 1);
+    u32x4_t bq[2][2];
+    bq[0][0] = *reinterpret_cast<const u32x4_t *>(xrow0);
+    bq[0][1] = *reinterpret_cast<const u32x4_t *>(xrow0 + 1024);
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int q = 0; q < 16; ++q) {  // group q: sub-step t = q/8, column tiles 2(q%8), +1
+      const int t = q >> 3, ct0 = 2 * (q & 7);
+      if (q < 15) {
+        const int t1 = (q + 1) >> 3, c1 = 2 * ((q + 1) & 7);
+        const uint16_t *xr = t1 ? xrow1 : xrow0;
+        bq[(q + 1) & 1][0] = *reinterpret_cast<const u32x4_t *>(xr + 1024 * c1);
+        bq[(q + 1) & 1][1] = *reinterpret_cast<const u32x4_t *>(xr + 1024 * (c1 + 1));
+      }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct0 + c], a[rt][t], bq[q & 1][c]);
+      // next step's operands, one piece every other group (on the last step:
+      // codes that are never used)
+      if ((q & 1) == 1) {
+        const int piece = q >> 1;
+        if (piece < 4) expand(piece, 1, an[piece]);
+        else expand(piece - 4, 0, a[piece - 4][0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) a[rt][1] = an[rt];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) wa[rt] = wb[rt], sca[rt] = scb[rt], gaa[rt] = gab[rt];
+    __syncthreads();
+  };
+  const int64_t npairs = nk >> 1;
+  for (int64_t p = 0; p < npairs; ++p) {
+    step(2 * p, std::integral_constant<int, 0>());
+    step(2 * p + 1, std::integral_constant<int, 1>());
+  }
+  if constexpr (kOddSteps) step(nk - 1, std::integral_constant<int, 0>());
 
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = (int)(kt & 1);
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t *Pb = Ps + buf * FBN * FLD, *Qb = Qs + buf * FBM * FLD;
-    mma_step<4, 4>(acc, Pb, Qb, FLD, 64 * wi, 64 * wj, 0, lane);
-    mma_step<4, 4>(acc, Pb, Qb, FLD, 64 * wi, 64 * wj, 32, lane);
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  // LoRA up-projection in 64-wide chunks of the padded rank: the same
+  // fragment layout with A = B_lora rows (direct loads) and the sH tile in LDS.
+  const bool bvec = (r % 8) == 0;
+  for (int jc = 0; jc < RP; jc += 64) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4_t *>(&Xs0[xsw(c >> 3, c & 7)]) =
+          load8(sH, RP, M, RP, m0 + (c >> 3), jc + 8 * (c & 7), true);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        a[rt][t] = load8(Bl, r, N, r, n0 + 64 * wave + 16 * rt + li, jc + 16 * g + 8 * t, bvec);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 16; ++ct) {
+        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&Xs0[xsw(16 * ct + li, 2 * g + t)]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct], a[rt][t], b);
+      }
     __syncthreads();
   }
+  mfma_acc_fence();
 
-  // LoRA up-projection: acc += B[n][:] . sH[m][:] over the padded rank.
-  const int LE = RP + 8;
-  const int cpr = RP / 8;  // 16-byte chunks per row
-  const bool bvec = (r % 8) == 0;
-  for (int c = tid; c < FBN * cpr; c += 256) {
-    const int row = c / cpr, col = (c % cpr) * 8;
-    *reinterpret_cast<u32x4_t *>(Ps + row * LE + col) = load8(Bl, r, N, r, n0 + row, col, bvec);
-  }
-  for (int c = tid; c < FBM * cpr; c += 256) {
-    const int row = c / cpr, col = (c % cpr) * 8;
-    *reinterpret_cast<u32x4_t *>(Qs + row * LE + col) = load8(sH, RP, M, RP, m0 + row, col, true);
-  }
-  __syncthreads();
-  for (int kk = 0; kk < RP; kk += 32) mma_step<4, 4>(acc, Ps, Qs, LE, 64 * wi, 64 * wj, kk, lane);
-
-  // acc[ti][tj][v] = C[n][m], n = .. + 4*(lane>>4) + v, m = .. + (lane & 15): four consecutive n of one Y row.
+  // acc[rt][ct][v] = C[n][m]: n = n0+64w+16rt+4g+v, m = m0+16ct+li (four consecutive n of one Y row).
   const bool nvec = (N & 3) == 0;
 #pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
+  for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) {
-      const int64_t n = n0 + 64 * wi + 16 * ti + 4 * (lane >> 4);
-      const int64_t m = m0 + 64 * wj + 16 * tj + (lane & 15);
-      if (m >= M) continue;
-      const f32x4_t a = acc[ti][tj];
-      uint16_t *dst = Y + m * N + n;
-      if (nvec && n + 4 <= N) {
-        *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{bf16x2_rne(a[0], a[1]), bf16x2_rne(a[2], a[3])};
-      } else {
+    for (int ct = 0; ct < 16; ++ct) {
+      const int64_t n = n0 + 64 * wave + 16 * rt + 4 * g;
+      const int64_t m = m0 + 16 * ct + li;
+      if (m < M) {
+        const f32x4_t v = acc[rt][ct];
+        uint16_t *dst = Y + m * N + n;
+        if (nvec && n + 4 <= N) {
+          *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+        } else {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (n + v < N) dst[v] = f32_to_bf16_bits(a[v]);
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) dst[e] = f32_to_bf16_bits(v[e]);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -162,8 +285,12 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   if (e != hipSuccess) return e;
   e = launch_reduce_rows(part, l.sp.splits, M, l.RP, a.r, a.s, H_out, sH, nullptr, 0, s);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)ceil_div(N, FBN), (unsigned)ceil_div(M, FBM));
-  QLORA_LAUNCH("k_fwd_main", k_fwd_main, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y);
+  const int tiles_n = (int)ceil_div(N, FBN), tiles_m = (int)ceil_div(M, FBM);
+  const dim3 grid((unsigned)(tiles_n * tiles_m));
+  if ((K / kBlock) & 1)
+    QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<true>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n);
+  else
+    QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<false>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n);
   return hipGetLastError();
 }
 

@@ -8,12 +8,19 @@
 
 #include "../../include/qlora.h"
 
+// Every multiply and add below is rounded on its own: the block scale is
+// defined with two roundings, and the library is also built with
+// -ffp-contract=off, so no a*b+c is ever fused into one FMA.
+#pragma clang fp contract(off)
+
 namespace qlora {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void *lds_ptr;        // for global_load_lds destinations
+typedef __attribute__((address_space(1))) const void *glb_ptr;  // and sources
 
 constexpr int kBlock = 64;   // weights per NF4 block ("QLoRA, explained." step 2)
 constexpr int kGroup = 256;  // block constants per second-level group (step 3)
@@ -107,6 +114,16 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t &a, const u32x4_t &b, co
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+
+// The same MFMA with the accumulator pinned to AGPRs ("+a"): the register
+// allocator can then neither move accumulator tiles between register files
+// nor copy them around a loop.  Only MFMAs touch these accumulators until
+// mfma_acc_fence(), which waits out the MFMA result latency before ordinary
+// code reads them.
+__device__ __forceinline__ void mfma16_acc(f32x4_t &acc, const u32x4_t &a, const u32x4_t &b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_acc_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
 // Fragment of a row-major LDS tile (row stride `ld` elements, contraction
 // contiguous) for rows row0..row0+15 and contraction kk0..kk0+31.

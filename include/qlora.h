@@ -42,7 +42,7 @@ extern "C" {
 enum {
   QLORA_OK = 0,
   QLORA_ERR_NULL_ARG = -1,    /* a required pointer is NULL                         */
-  QLORA_ERR_BAD_SHAPE = -2,   /* n < 1, k < 64, k % 64 != 0, M < 0, or too large      */
+  QLORA_ERR_BAD_SHAPE = -2,   /* n < 1, k < 64, k % 64 != 0, k > 2^22, M < 0, too large */
   QLORA_ERR_BAD_RANK = -3,    /* r outside [1, 128]                                  */
   QLORA_ERR_MISALIGNED = -4,  /* a tensor pointer is not 16-byte aligned              */
   QLORA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes */
