@@ -194,10 +194,11 @@ def main():
     kernels = {name: {"launches_per_step": n / args.steps, "avg_us": 1e3 * ms / n,
                       "ms_per_step": ms / args.steps} for name, (n, ms) in prof.items()}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    per_launch_flops = {
-        "k_fwd_main": sum(2 * M * t["L"].n * t["L"].k + 2 * M * t["L"].n * r for t in layers) / len(layers),
-        "k_bwd_dx": sum(2 * M * t["L"].n * t["L"].k + 2 * M * t["L"].k * r for t in layers) / len(layers),
-    }
+    # algorithmic flops of one launch (same M*N*K for every MLP layer): the
+    # forward GEMM carries the LoRA up-projection, the dX GEMM the G A term
+    fwd_launch = sum(2 * M * t["L"].n * t["L"].k + 2 * M * t["L"].n * r for t in layers) / len(layers)
+    dx_launch = sum(2 * M * t["L"].n * t["L"].k + 2 * M * t["L"].k * r for t in layers) / len(layers)
+    per_launch_flops = {"k_fwd_nf4": fwd_launch, "k_bwd_dx_nf4": dx_launch, "k_bwd_dx": dx_launch}
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:

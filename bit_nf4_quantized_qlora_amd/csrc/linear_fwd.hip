@@ -22,19 +22,6 @@ namespace {
 
 constexpr int FBN = 256, FBM = 256;  // block tile: weight rows (n) x X rows (m)
 
-// X tile in LDS: [256 m][64 k] bf16, 128 B per row; 16-byte chunk c of row r
-// lives at chunk c ^ (r & 7), so the 16 rows one fragment read touches fall
-// in different banks.
-__device__ __forceinline__ int xsw(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
-
-// Blocks are dispatched round-robin over the 8 XCDs; give each XCD a
-// contiguous run of tiles (m-major, n fastest) so the tiles sharing an X
-// row-panel meet in the same L2.
-__device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
-  const int q = nblocks >> 3, rem = nblocks & 7, x = bid & 7, p = bid >> 3;
-  return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + p;
-}
-
 // C[n][m] = sum_k W_hat[n][k] X[m][k] + sum_j B[n][j] sH[m][j]  ->  Y[m][n]
 // Wave w owns weight rows n0 + 64w .. +63 (four 16-row MFMA tiles) and all
 // 256 X rows (sixteen 16-column tiles): 256 fp32 accumulators per lane.
@@ -58,10 +45,6 @@ struct FwdSmem {
 
 template <int BUF>
 __device__ __forceinline__ uint16_t *xbuf(const FwdSmem &sm) { return BUF ? sm.x1 : sm.x0; }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // All per-lane addresses are one 32-bit VGPR offset into a buffer resource
 // plus uniform (scalar) offsets; rows past N or M fall outside the resource's

@@ -31,6 +31,24 @@ __device__ __forceinline__ u32x4_t load8(const uint16_t *m, int64_t ld, int64_t 
   return v;
 }
 
+// A [rows][64] bf16 tile in LDS, 128 B per row; 16-byte chunk c of row r
+// lives at chunk c ^ (r & 7), so the 16 rows one MFMA fragment read touches,
+// and the 8 chunks of a row, fall in different banks.
+__device__ __forceinline__ int xsw(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+// contiguous run of tiles so tiles that share an operand panel meet in the
+// same L2.  A bijection on [0, nblocks).
+__device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
+  const int q = nblocks >> 3, rem = nblocks & 7, x = bid & 7, p = bid >> 3;
+  return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + p;
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void *base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 struct SplitPlan {
   int splits = 1;
   int steps_per_split = 1;
