@@ -38,26 +38,29 @@ constexpr int FBN = 256, FBM = 256;  // block tile: weight rows (n) x X rows (m)
 // codes of step kt+1 are expanded in eight pieces interleaved with the eight
 // groups of 16 MFMAs of step kt.  Rows past N or M are clamped to a valid
 // row: they only feed accumulators that are never stored.
-struct FwdSmem {
-  uint16_t *x0, *x1;
-  float2 *pair;
-};
-
-template <int BUF>
-__device__ __forceinline__ uint16_t *xbuf(const FwdSmem &sm) { return BUF ? sm.x1 : sm.x0; }
-
 // All per-lane addresses are one 32-bit VGPR offset into a buffer resource
 // plus uniform (scalar) offsets; rows past N or M fall outside the resource's
 // range and read as zero, and only feed accumulators that are never stored.
-template <bool kOddSteps>  // k/64 odd: one trailing step after the two-step loop
+//
+// Pipeline (per 64-wide K step kt, the loop unrolled by 4 so every buffer
+// index is a compile-time constant):
+//   X tile of step kt+2  -> LDS buffer (kt+2) % 4 by buffer_load ... lds
+//   codes of step kt+3   -> registers (three code sets rotate)
+//   codes of step kt+1   -> expanded into next-step operands, in 8 pieces;
+//                           a piece's LDS table reads are issued one MFMA
+//                           group before the arithmetic that uses them
+//   MFMAs of step kt     on LDS buffer kt % 4 and the current operands
+// The step ends waiting only for the loads issued one step earlier.
+template <int kTail>  // (k/64) % 4: steps after the unrolled loop
 __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const uint16_t *__restrict__ X, int64_t M,
                                                     const uint16_t *__restrict__ Bl, int r, int RP,
                                                     const uint16_t *__restrict__ sH, uint16_t *__restrict__ Y,
                                                     int tiles_n) {
   __shared__ __align__(16) uint16_t Xs0[FBM * 64];
   __shared__ __align__(16) uint16_t Xs1[FBM * 64];
+  __shared__ __align__(16) uint16_t Xs2[FBM * 64];
+  __shared__ __align__(16) uint16_t Xs3[FBM * 64];
   __shared__ float2 s_pair[256];
-  const FwdSmem sm{Xs0, Xs1, s_pair};
   // wave is uniform across the wave; say so, or wave-dependent scalar
   // offsets would be made uniform with a per-lane loop
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
@@ -67,6 +70,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const uint16_t *_
   const int64_t N = w.n, K = w.k, nk = K / kBlock;
   fill_pair_table(s_pair, tid, 256);
   const float offset = *w.offset;
+  auto xbuf = [&](auto B) -> uint16_t * {
+    constexpr int b = decltype(B)::value & 3;
+    return b == 0 ? Xs0 : b == 1 ? Xs1 : b == 2 ? Xs2 : Xs3;
+  };
 
   // Weight rows n0 .. n0+255: lane's row in row tile rt is n0 + 64w + 16rt + li.
   const int64_t nrows = min<int64_t>(FBN, N - n0);
@@ -82,39 +89,57 @@ __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const uint16_t *_
   const int64_t xrows = min<int64_t>(FBM, M - m0);
   const __amdgpu_buffer_rsrc_t xrs = rsrc(X + m0 * K, xrows * K * 2);
   const uint32_t xv = (uint32_t)(((lane >> 3) * K + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
-  auto xload = [&](int64_t kt, auto BUF) {
-    uint16_t *dst = xbuf<decltype(BUF)::value>(sm);
+  auto xload = [&](int64_t kt, auto B) {
+    uint16_t *dst = xbuf(B);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16, xv,
                                                (int)((64 * wave + 8 * i) * K * 2 + kt * 128), 0, 0);
   };
+  constexpr int kVmemPerStep = 8 + 12;  // X copy + codes, scale codes, group constants
 
-  // Codes of step kt+1 (wa: expanded during step kt) and kt+2 (wb: loaded
-  // during step kt), rotated by copies.
-  u32x2_t wa[4], wb[4];
-  uint32_t sca[4], scb[4];
-  float gaa[4], gab[4];
-  auto wload = [&](int64_t kt, u32x2_t(&wc)[4], uint32_t(&sc)[4], float(&ga)[4]) {
+  // Code sets, indexed by step mod 4 (compile-time in the unrolled loop, so
+  // nothing is copied while its load is in flight): during step kt the set of
+  // step kt+1 is expanded and the set of step kt+3 is loaded.
+  struct Codes {
+    u32x2_t wc[4];
+    uint32_t sc[4];
+    float ga[4];
+  };
+  Codes c[4];
+  auto wload = [&](int64_t kt, Codes &d) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int64_t row = wrow_w + 16 * rt;  // uniform part of the lane's row
-      wc[rt] = __builtin_amdgcn_raw_buffer_load_b64(wrs, wv, (int)(row * (K / 2) + kt * 32), 0);
-      sc[rt] = __builtin_amdgcn_raw_buffer_load_b8(srs, sv, (int)(row * nk + kt), 0);
+      d.wc[rt] = __builtin_amdgcn_raw_buffer_load_b64(wrs, wv, (int)(row * (K / 2) + kt * 32), 0);
+      d.sc[rt] = __builtin_amdgcn_raw_buffer_load_b8(srs, sv, (int)(row * nk + kt), 0);
       const uint32_t gidx = (uint32_t)(((n0 + row) * nk + kt + sv) >> 8);
-      ga[rt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grs, gidx * 4, 0, 0));
+      d.ga[rt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grs, gidx * 4, 0, 0));
     }
   };
-  // a[rt][t]: operands of the current step.  The next step's sub-step-1
-  // halves are expanded into an[] during MFMA groups 0-7 (a[][1] is still in
-  // use); its sub-step-0 halves go straight into a[][0] during groups 8-15.
+  // a[rt][t]: operands of the current step.  Piece p of the next step's
+  // expansion: p < 4 -> row tile p, sub-step 1 into an[p] (a[][1] is still
+  // in use); p >= 4 -> row tile p-4, sub-step 0 straight into a[p-4][0]
+  // (written in MFMA groups 9..15, after its last read in group 7).
   u32x4_t a[4][2], an[4];
   float sn[4];
-  auto expand = [&](int rt, int t, u32x4_t &dst) {
-    if (t == 1) sn[rt] = block_scale(sca[rt], gaa[rt], offset);
-    uint32_t o[4];
-    dequant_word(wa[rt][t], sn[rt], s_pair, o);
-    dst = u32x4_t{o[0], o[1], o[2], o[3]};
+  float2 pq[4];  // table reads of the piece in flight
+  auto piece_read = [&](const Codes &cs, int p) {
+    const int rt = p & 3, t = p < 4 ? 1 : 0;
+    const uint32_t word = cs.wc[rt][t];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pq[i] = s_pair[(word >> (8 * i)) & 0xFFu];
+  };
+  auto piece_math = [&](const Codes &cs, int p) {
+    const int rt = p & 3;
+    if (p < 4) sn[rt] = block_scale(cs.sc[rt], cs.ga[rt], offset);
+    const float s = sn[rt];
+    const u32x4_t v = {bf16x2_rne(__fmul_rn(pq[0].x, s), __fmul_rn(pq[0].y, s)),
+                       bf16x2_rne(__fmul_rn(pq[1].x, s), __fmul_rn(pq[1].y, s)),
+                       bf16x2_rne(__fmul_rn(pq[2].x, s), __fmul_rn(pq[2].y, s)),
+                       bf16x2_rne(__fmul_rn(pq[3].x, s), __fmul_rn(pq[3].y, s))};
+    if (p < 4) an[rt] = v;
+    else a[rt][0] = v;
   };
 
   f32x4_t acc[4][16];
@@ -123,28 +148,32 @@ __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const uint16_t *_
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Prologue: X of steps 0 and 1 in flight, step 0 expanded, codes of 1..3.
   __syncthreads();  // pair table
   xload(0, std::integral_constant<int, 0>());
-  wload(0, wa, sca, gaa);
-  wload(min<int64_t>(1, nk - 1), wb, scb, gab);
+  xload(min<int64_t>(1, nk - 1), std::integral_constant<int, 1>());
+  wload(0, c[0]);
+  wload(min<int64_t>(1, nk - 1), c[1]);
+  wload(min<int64_t>(2, nk - 1), c[2]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    expand(rt, 1, a[rt][1]);
-    expand(rt, 0, a[rt][0]);
+  for (int p = 0; p < 8; ++p) {
+    piece_read(c[0], p);
+    piece_math(c[0], p);
   }
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) wa[rt] = wb[rt], sca[rt] = scb[rt], gaa[rt] = gab[rt];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int rt = 0; rt < 4; ++rt) a[rt][1] = an[rt];
   __syncthreads();
 
-  auto step = [&](int64_t kt, auto BUF) {
-    constexpr int buf = decltype(BUF)::value;
+  auto step = [&](int64_t kt, auto B) {
+    constexpr int buf = decltype(B)::value & 3;
     // Prefetches past the last step re-read the last step (in bounds, unused).
-    xload(min<int64_t>(kt + 1, nk - 1), std::integral_constant<int, buf ^ 1>());
-    wload(min<int64_t>(kt + 2, nk - 1), wb, scb, gab);
+    xload(min<int64_t>(kt + 2, nk - 1), std::integral_constant<int, (buf + 2) & 3>());
+    wload(min<int64_t>(kt + 3, nk - 1), c[(buf + 3) & 3]);
+    const Codes &cn = c[(buf + 1) & 3];  // step kt+1
     // Fragment (column tile ct, sub-step t) sits at xrow[t] + 1024*ct: the
     // swizzle term depends on (row & 7) == (li & 7) only.
-    const uint16_t *xs = xbuf<buf>(sm);
+    const uint16_t *xs = xbuf(B);
     const uint16_t *xrow0 = xs + xsw(li, 2 * g), *xrow1 = xs + xsw(li, 2 * g + 1);
     u32x4_t bq[2][2];
     bq[0][0] = *reinterpret_cast<const u32x4_t *>(xrow0);
@@ -158,32 +187,35 @@ __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const uint16_t *_
         bq[(q + 1) & 1][0] = *reinterpret_cast<const u32x4_t *>(xr + 1024 * c1);
         bq[(q + 1) & 1][1] = *reinterpret_cast<const u32x4_t *>(xr + 1024 * (c1 + 1));
       }
+      if ((q & 1) == 0) piece_read(cn, q >> 1);  // consumed by the next group
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct0 + c], a[rt][t], bq[q & 1][c]);
-      // next step's operands, one piece every other group (on the last step:
-      // codes that are never used)
-      if ((q & 1) == 1) {
-        const int piece = q >> 1;
-        if (piece < 4) expand(piece, 1, an[piece]);
-        else expand(piece - 4, 0, a[piece - 4][0]);
-      }
+        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct0 + cc], a[rt][t], bq[q & 1][cc]);
+      if ((q & 1) == 1) piece_math(cn, q >> 1);  // (on the last step: codes that are never used)
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) a[rt][1] = an[rt];
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) wa[rt] = wb[rt], sca[rt] = scb[rt], gaa[rt] = gab[rt];
-    __syncthreads();
+    // Everything but this step's own loads has landed (X of step kt+1, codes
+    // of kt+2), then a bare barrier: the only LDS writes in the loop are
+    // those copies, so __syncthreads()'s release fence would merely wait for
+    // the copies still in flight for step kt+2.  A buffer is refilled two
+    // barriers after its last read.
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVmemPerStep) : "memory");
   };
-  const int64_t npairs = nk >> 1;
-  for (int64_t p = 0; p < npairs; ++p) {
-    step(2 * p, std::integral_constant<int, 0>());
-    step(2 * p + 1, std::integral_constant<int, 1>());
+  const int64_t nquads = nk >> 2;
+  for (int64_t p = 0; p < nquads; ++p) {
+    step(4 * p, std::integral_constant<int, 0>());
+    step(4 * p + 1, std::integral_constant<int, 1>());
+    step(4 * p + 2, std::integral_constant<int, 2>());
+    step(4 * p + 3, std::integral_constant<int, 3>());
   }
-  if constexpr (kOddSteps) step(nk - 1, std::integral_constant<int, 0>());
+  if constexpr (kTail >= 1) step(nk - kTail, std::integral_constant<int, 0>());
+  if constexpr (kTail >= 2) step(nk - kTail + 1, std::integral_constant<int, 1>());
+  if constexpr (kTail >= 3) step(nk - kTail + 2, std::integral_constant<int, 2>());
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // LoRA up-projection in 64-wide chunks of the padded rank: the same
   // fragment layout with A = B_lora rows (direct loads) and the sH tile in LDS.
@@ -270,10 +302,12 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   if (e != hipSuccess) return e;
   const int tiles_n = (int)ceil_div(N, FBN), tiles_m = (int)ceil_div(M, FBM);
   const dim3 grid((unsigned)(tiles_n * tiles_m));
-  if ((K / kBlock) & 1)
-    QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<true>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n);
-  else
-    QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<false>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n);
+  switch ((K / kBlock) & 3) {
+    case 0: QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<0>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n); break;
+    case 1: QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<1>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n); break;
+    case 2: QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<2>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n); break;
+    default: QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<3>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n); break;
+  }
   return hipGetLastError();
 }
 
