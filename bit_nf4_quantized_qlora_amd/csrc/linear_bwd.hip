@@ -168,20 +168,22 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx_nf4(Nf4View w, const uint16_t
   fill_pair_table(s_pair, tid, 256);
   const float offset = *w.offset;
 
-  // dY rows m0 .. m0+255 (buffer range ends at row M: rows past it read 0).
+  // dY rows m0 .. m0+255 (buffer range ends at row M; the row offset is in
+  // the range-checked per-lane offset, so rows past M read 0).
   const int64_t yrows = min<int64_t>(256, M - m0);
   const __amdgpu_buffer_rsrc_t yrs = rsrc(dY + m0 * N, yrows * N * 2);
-  const uint32_t yv = (uint32_t)(((lane >> 3) * N + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
+  const uint32_t yv = (uint32_t)(((64 * wave + (lane >> 3)) * N + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
   auto yload = [&](int64_t st, auto BUF) {
     uint16_t *dst = decltype(BUF)::value ? Ds1 : Ds0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(yrs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16, yv,
-                                               (int)((64 * wave + 8 * i) * N * 2 + st * 128), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(yrs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
+                                               yv + (uint32_t)(i * 16 * N), (int)(st * 128), 0, 0);
   };
   // Codes: thread (ng = tid >> 5, kg = tid & 31) covers rows 8ng .. 8ng+7 of
   // the step and columns k0 + 8kg .. +7 (one dword per row; columns past K
-  // only feed rows of C that are never stored).
+  // only feed rows of C that are never stored, and past the last row they
+  // fall outside the range-checked offset and read 0).
   const int ng = tid >> 5, kg = tid & 31;
   const __amdgpu_buffer_rsrc_t wrs = rsrc(w.packed, w.n * (K / 2));
   const uint32_t wv = (uint32_t)(8 * ng * (K / 2) + (k0 + 8 * kg) / 2);
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dx_nf4(Nf4View w, const uint16_t
   auto wload = [&](int64_t st, uint32_t(&wc)[8]) {
 #pragma unroll
     for (int rho = 0; rho < 8; ++rho)
-      wc[rho] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wv, (int)((st * 64 + rho) * (K / 2)), 0);
+      wc[rho] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wv + (uint32_t)((st * 64 + rho) * (K / 2)), 0, 0);
   };
   auto sload = [&](int64_t st) {
     const int64_t b = (st * 64 + srow) * nkb + sb_kb;

@@ -8,13 +8,13 @@
 //   1. H = X A^T (k_nt_splitk + reduction): fp32 H (optional output) and
 //      bf16(s*H) for the epilogue.
 //   2. k_tile_scales: s_b of every block, once per call, in the order the
-//      main kernel streams them (k % 256 == 0).
-//   3. k_fwd_nf4 (k % 256 == 0) or k_fwd_nf4_any (any k % 64 == 0):
-//      C[n][m] = sum_k W_hat[n][k] X[m][k] + sum_j B[n][j] sH[m][j] on
-//      256x256 tiles.  NF4 codes are expanded in registers straight into MFMA
-//      operands through a 256-entry table of level pairs, bit-identical to
-//      the standalone dequantization; the LoRA up-projection is a few more
+//      main kernel streams them.
+//   3. k_fwd_nf4: C[n][m] = sum_k W_hat[n][k] X[m][k] + sum_j B[n][j] sH[m][j]
+//      on 256x256 tiles.  NF4 codes are expanded in registers straight into
+//      MFMA operands through a 256-entry table of level pairs, bit-identical
+//      to the standalone dequantization; the LoRA up-projection is a few more
 //      MFMA steps on the same accumulators; Y is rounded to bf16 once.
+
 #include "lora_gemm.h"
 
 namespace qlora {
@@ -22,7 +22,7 @@ namespace {
 
 constexpr int FBN = 256, FBM = 256;  // block tile: weight rows (n) x X rows (m)
 
-// Shared tail of both forward kernels, after the main loop has drained
+// Tail of the forward kernel, after the main loop has drained
 // (every copy landed, all waves past a barrier): the LoRA up-projection in
 // 64-wide chunks of the padded rank -- the same fragment layout with
 // A = B_lora rows (direct loads) and the sH tile staged in LDS (stage: 32 KB)
@@ -81,252 +81,79 @@ __device__ __forceinline__ void fwd_epilogue(f32x4_t (&acc)[4][16], uint16_t *st
     }
 }
 
-// C[n][m] = sum_k W_hat[n][k] X[m][k] + sum_j B[n][j] sH[m][j]  ->  Y[m][n]
-// Wave w owns weight rows n0 + 64w .. +63 (four 16-row MFMA tiles) and all
-// 256 X rows (sixteen 16-column tiles): 256 fp32 accumulators per lane.
-// Its NF4 rows are expanded straight into MFMA A-operand registers: lane
-// (li = lane & 15, g = lane >> 4) of row tile rt holds row n0+64w+16rt+li and
-// codes 16g .. 16g+15 of the current 64-weight block (one 8-byte load), used
-// as contraction slots 8t .. 8t+7 of sub-step t; the X fragment reads the
-// same k positions, so the contraction is unchanged.
-//
-// Per 64-wide K step: the X tile of step kt+1 streams global -> LDS with
-// buffer loads (no registers) into the other of two separate LDS arrays
-// (separate objects, so the compiler knows the in-flight copy does not alias
-// the tile being read), the packed codes of step kt+2 are loaded, and the
-// codes of step kt+1 are expanded in eight pieces interleaved with the eight
-// groups of 16 MFMAs of step kt.  Rows past N or M are clamped to a valid
-// row: they only feed accumulators that are never stored.
-// All per-lane addresses are one 32-bit VGPR offset into a buffer resource
-// plus uniform (scalar) offsets; rows past N or M fall outside the resource's
-// range and read as zero, and only feed accumulators that are never stored.
-//
-// Pipeline (per 64-wide K step kt, the loop unrolled by 4 so every buffer
-// index is a compile-time constant):
-//   X tile of step kt+2  -> LDS buffer (kt+2) % 4 by buffer_load ... lds
-//   codes of step kt+3   -> registers (three code sets rotate)
-//   codes of step kt+1   -> expanded into next-step operands, in 8 pieces;
-//                           a piece's LDS table reads are issued one MFMA
-//                           group before the arithmetic that uses them
-//   MFMAs of step kt     on LDS buffer kt % 4 and the current operands
-// The step ends waiting only for the loads issued one step earlier.
-template <int kTail>  // (k/64) % 4: steps after the unrolled loop
-__global__ __launch_bounds__(256, 1) void k_fwd_nf4_any(Nf4View w, const uint16_t *__restrict__ X, int64_t M,
-                                                    const uint16_t *__restrict__ Bl, int r, int RP,
-                                                    const uint16_t *__restrict__ sH, uint16_t *__restrict__ Y,
-                                                    int tiles_n) {
-  __shared__ __align__(16) uint16_t Xs0[FBM * 64];
-  __shared__ __align__(16) uint16_t Xs1[FBM * 64];
-  __shared__ __align__(16) uint16_t Xs2[FBM * 64];
-  __shared__ __align__(16) uint16_t Xs3[FBM * 64];
-  __shared__ float2 s_pair[256];
-  // wave is uniform across the wave; say so, or wave-dependent scalar
-  // offsets would be made uniform with a per-lane loop
-  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t n0 = (int64_t)(tile % tiles_n) * FBN, m0 = (int64_t)(tile / tiles_n) * FBM;
-  const int64_t N = w.n, K = w.k, nk = K / kBlock;
-  fill_pair_table(s_pair, tid, 256);
-  const float offset = *w.offset;
-  auto xbuf = [&](auto B) -> uint16_t * {
-    constexpr int b = decltype(B)::value & 3;
-    return b == 0 ? Xs0 : b == 1 ? Xs1 : b == 2 ? Xs2 : Xs3;
-  };
-
-  // Weight rows n0 .. n0+255: lane's row in row tile rt is n0 + 64w + 16rt + li.
-  const int64_t nrows = min<int64_t>(FBN, N - n0);
-  const __amdgpu_buffer_rsrc_t wrs = rsrc(w.packed + n0 * (K / 2), nrows * (K / 2));
-  const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code + n0 * nk, nrows * nk);
-  const __amdgpu_buffer_rsrc_t grs = rsrc(w.group_amax, ceil_div_d(w.nb, kGroup) * 4);
-  const uint32_t wv = (uint32_t)(li * (K / 2) + 8 * g), sv = (uint32_t)(li * nk);
-  const int64_t wrow_w = 64 * wave;  // wave's first row within the tile
-  // X rows m0 .. m0+255, staged global -> LDS: wave-instruction i fills LDS
-  // chunks [512w + 64i, +64): row 64w + 8i + lane/8, logical chunk
-  // (lane & 7) ^ ((lane/8) & 7) (the swizzle of xsw), so only the row term
-  // varies with i and it is uniform.
-  const int64_t xrows = min<int64_t>(FBM, M - m0);
-  const __amdgpu_buffer_rsrc_t xrs = rsrc(X + m0 * K, xrows * K * 2);
-  const uint32_t xv = (uint32_t)(((lane >> 3) * K + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
-  auto xload = [&](int64_t kt, auto B) {
-    uint16_t *dst = xbuf(B);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16, xv,
-                                               (int)((64 * wave + 8 * i) * K * 2 + kt * 128), 0, 0);
-  };
-  constexpr int kVmemPerStep = 8 + 12;  // X copy + codes, scale codes, group constants
-
-  // Code sets, indexed by step mod 4 (compile-time in the unrolled loop, so
-  // nothing is copied while its load is in flight): during step kt the set of
-  // step kt+1 is expanded and the set of step kt+3 is loaded.
-  struct Codes {
-    u32x2_t wc[4];
-    uint32_t sc[4];
-    float ga[4];
-  };
-  Codes c[4];
-  auto wload = [&](int64_t kt, Codes &d) {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int64_t row = wrow_w + 16 * rt;  // uniform part of the lane's row
-      d.wc[rt] = __builtin_amdgcn_raw_buffer_load_b64(wrs, wv, (int)(row * (K / 2) + kt * 32), 0);
-      d.sc[rt] = __builtin_amdgcn_raw_buffer_load_b8(srs, sv, (int)(row * nk + kt), 0);
-      const uint32_t gidx = (uint32_t)(((n0 + row) * nk + kt + sv) >> 8);
-      d.ga[rt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grs, gidx * 4, 0, 0));
-    }
-  };
-  // a[rt][t]: operands of the current step.  Piece p of the next step's
-  // expansion: p < 4 -> row tile p, sub-step 1 into an[p] (a[][1] is still
-  // in use); p >= 4 -> row tile p-4, sub-step 0 straight into a[p-4][0]
-  // (written in MFMA groups 9..15, after its last read in group 7).
-  u32x4_t a[4][2], an[4];
-  float sn[4];
-  float2 pq[4];  // table reads of the piece in flight
-  auto piece_read = [&](const Codes &cs, int p) {
-    const int rt = p & 3, t = p < 4 ? 1 : 0;
-    const uint32_t word = cs.wc[rt][t];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pq[i] = s_pair[(word >> (8 * i)) & 0xFFu];
-  };
-  auto piece_math = [&](const Codes &cs, int p) {
-    const int rt = p & 3;
-    if (p < 4) sn[rt] = block_scale(cs.sc[rt], cs.ga[rt], offset);
-    const float s = sn[rt];
-    const u32x4_t v = {bf16x2_rne(__fmul_rn(pq[0].x, s), __fmul_rn(pq[0].y, s)),
-                       bf16x2_rne(__fmul_rn(pq[1].x, s), __fmul_rn(pq[1].y, s)),
-                       bf16x2_rne(__fmul_rn(pq[2].x, s), __fmul_rn(pq[2].y, s)),
-                       bf16x2_rne(__fmul_rn(pq[3].x, s), __fmul_rn(pq[3].y, s))};
-    if (p < 4) an[rt] = v;
-    else a[rt][0] = v;
-  };
-
-  f32x4_t acc[4][16];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 16; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Prologue: X of steps 0 and 1 in flight, step 0 expanded, codes of 1..3.
-  __syncthreads();  // pair table
-  xload(0, std::integral_constant<int, 0>());
-  xload(min<int64_t>(1, nk - 1), std::integral_constant<int, 1>());
-  wload(0, c[0]);
-  wload(min<int64_t>(1, nk - 1), c[1]);
-  wload(min<int64_t>(2, nk - 1), c[2]);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    piece_read(c[0], p);
-    piece_math(c[0], p);
-  }
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) a[rt][1] = an[rt];
-  __syncthreads();
-
-  auto step = [&](int64_t kt, auto B) {
-    constexpr int buf = decltype(B)::value & 3;
-    // Prefetches past the last step re-read the last step (in bounds, unused).
-    xload(min<int64_t>(kt + 2, nk - 1), std::integral_constant<int, (buf + 2) & 3>());
-    wload(min<int64_t>(kt + 3, nk - 1), c[(buf + 3) & 3]);
-    const Codes &cn = c[(buf + 1) & 3];  // step kt+1
-    // Fragment (column tile ct, sub-step t) sits at xrow[t] + 1024*ct: the
-    // swizzle term depends on (row & 7) == (li & 7) only.
-    const uint16_t *xs = xbuf(B);
-    const uint16_t *xrow0 = xs + xsw(li, 2 * g), *xrow1 = xs + xsw(li, 2 * g + 1);
-    u32x4_t bq[2][2];
-    bq[0][0] = *reinterpret_cast<const u32x4_t *>(xrow0);
-    bq[0][1] = *reinterpret_cast<const u32x4_t *>(xrow0 + 1024);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {  // group q: sub-step t = q/8, column tiles 2(q%8), +1
-      const int t = q >> 3, ct0 = 2 * (q & 7);
-      if (q < 15) {
-        const int t1 = (q + 1) >> 3, c1 = 2 * ((q + 1) & 7);
-        const uint16_t *xr = t1 ? xrow1 : xrow0;
-        bq[(q + 1) & 1][0] = *reinterpret_cast<const u32x4_t *>(xr + 1024 * c1);
-        bq[(q + 1) & 1][1] = *reinterpret_cast<const u32x4_t *>(xr + 1024 * (c1 + 1));
-      }
-      if ((q & 1) == 0) piece_read(cn, q >> 1);  // consumed by the next group
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct0 + cc], a[rt][t], bq[q & 1][cc]);
-      if ((q & 1) == 1) piece_math(cn, q >> 1);  // (on the last step: codes that are never used)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) a[rt][1] = an[rt];
-    // Everything but this step's own loads has landed (X of step kt+1, codes
-    // of kt+2), then a bare barrier: the only LDS writes in the loop are
-    // those copies, so __syncthreads()'s release fence would merely wait for
-    // the copies still in flight for step kt+2.  A buffer is refilled two
-    // barriers after its last read.
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVmemPerStep) : "memory");
-  };
-  const int64_t nquads = nk >> 2;
-  for (int64_t p = 0; p < nquads; ++p) {
-    step(4 * p, std::integral_constant<int, 0>());
-    step(4 * p + 1, std::integral_constant<int, 1>());
-    step(4 * p + 2, std::integral_constant<int, 2>());
-    step(4 * p + 3, std::integral_constant<int, 3>());
-  }
-  if constexpr (kTail >= 1) step(nk - kTail, std::integral_constant<int, 0>());
-  if constexpr (kTail >= 2) step(nk - kTail + 1, std::integral_constant<int, 1>());
-  if constexpr (kTail >= 3) step(nk - kTail + 2, std::integral_constant<int, 2>());
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  fwd_epilogue(acc, Xs0, Bl, r, RP, sH, Y, N, M, n0 + 64 * wave, m0);
-}
-
 constexpr int kSup = 4;  // K steps per staged weight chunk: 128 packed bytes per row
 
 // s_b of every block, in the order k_fwd_nf4 streams them: for weight tile tn
 // (rows 256tn .. 256tn+255) and super-step sp (blocks 4sp .. 4sp+3 of each
 // row) one contiguous 4 KB run, Sp[((tn*nsup + sp)*256 + row)*4 + j]; rows
-// past n hold 0.  block_scale is the dequantization's own (bit-identical).
+// past n and blocks past k/64 hold 0.  block_scale is the dequantization's
+// own (bit-identical).
 __global__ __launch_bounds__(256) void k_tile_scales(Nf4View w, int64_t nsup, int64_t total,
                                                      float *__restrict__ Sp) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= total) return;
   const int64_t q = t >> 8, tn = q / nsup, sp = q - tn * nsup;
-  const int64_t n = tn * FBN + (t & 255);
+  const int64_t n = tn * FBN + (t & 255), nk = w.k / kBlock;
   f32x4_t v = {0.f, 0.f, 0.f, 0.f};
   if (n < w.n) {
-    const int64_t b = n * (nsup * kSup) + kSup * sp;  // 4 blocks in one group (256 % 4 == 0)
-    const uint32_t c4 = *reinterpret_cast<const uint32_t *>(w.scale_code + b);
-    const float ga = w.group_amax[b / kGroup], off = *w.offset;
+    const float off = *w.offset;
 #pragma unroll
-    for (int j = 0; j < kSup; ++j) v[j] = block_scale((c4 >> (8 * j)) & 0xFFu, ga, off);
+    for (int j = 0; j < kSup; ++j) {
+      const int64_t kb = kSup * sp + j, b = n * nk + kb;
+      if (kb < nk) v[j] = block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
+    }
   }
   *reinterpret_cast<f32x4_t *>(Sp + 4 * t) = v;
 }
 
-// The forward for k % 256 == 0, with every operand streamed by LDS DMA.
-// Same tiles, wave roles, fragment layout and expansion as k_fwd_nf4_any;
-// the weight side differs: packed codes arrive 4 K steps (128 B = one cache
-// line per row) at a time, with their precomputed block scales (k_tile_scales),
-// straight into LDS, and each lane reads its 8-byte code chunks and scales
-// from there.  (Per-step scattered loads of codes, scale codes and group
-// constants from every lane were the kernel's main stall.)
+// C[n][m] = sum_k W_hat[n][k] X[m][k] + sum_j B[n][j] sH[m][j]  ->  Y[m][n]
+// Wave w owns weight rows n0 + 64w .. +63 (four 16-row MFMA tiles) and all
+// 256 X rows (sixteen 16-column tiles): 256 fp32 accumulators per lane (all
+// in AGPRs).  Its NF4 rows are expanded straight into MFMA A-operand
+// registers: lane (li = lane & 15, g = lane >> 4) of row tile rt holds row
+// n0+64w+16rt+li and codes 16g .. 16g+15 of the current 64-weight block,
+// used as contraction slots 8t .. 8t+7 of sub-step t; the X fragment reads
+// the same k positions, so the contraction is unchanged.  Every operand is
+// streamed global -> LDS by buffer loads that write LDS directly: the X tile
+// one 64-wide K step at a time, packed codes 4 K steps (128 B = one cache
+// line per row) at a time with their precomputed block scales
+// (k_tile_scales); lanes read their 8-byte code chunks and scales from LDS.
 //
 // LDS: X tiles Xs0/Xs1 (2 x 32 KB), code tiles Wc0/Wc1 (2 x 32 KB: 256 rows x
 // 128 B, 16-byte chunk c of row R at chunk c ^ (R & 7)), scale tiles Sc0/Sc1
 // (2 x 4 KB: 256 rows x 4 fp32), pair table 2 KB.  Wave w copies and reads
 // only its own 64 weight rows.
 //
-// Per K step kt (u = kt % 8, j = kt % 4, super-step sp = kt / 4; the loop is
-// unrolled by 8 so every buffer choice is a compile-time constant):
-//   X tile of step kt+1        -> Xs[(kt+1) % 2]         (DMA)
-//   if j == 0: codes + scales of super-step sp+1 -> Wc/Sc[(sp+1) % 2] (DMA)
-//   16 MFMA groups of step kt on Xs[kt % 2], interleaved with the expansion
-//   of step kt+1 from the code/scale registers
-//   LDS -> registers: codes and scales of step kt+2
-//   wait for this step's X copy (and, from j == 1, the weight copy), barrier
-// A weight buffer is refilled one step after its last register read; its
-// copy has until the end of step 4sp+1, and is first read at the end of
-// step 4sp+2.
-template <int kOddSup>  // (k/256) odd: one 4-step super-step after the 8-step loop
+// One wave per SIMD, so the wave's own instruction stream has to hide every
+// latency: a K step is eight "pairs" of 16 MFMAs (pair P: sub-step P/4,
+// column tiles 4(P%4) .. +3), and after each MFMA the wave issues one small
+// piece of other work, all of it for later pairs:
+//   the four X fragments of pair P+1            (LDS reads)
+//   the four table reads of expansion piece P+1  (LDS reads)
+//   the arithmetic of expansion piece P          (8 multiplies, 4 roundings)
+//   in pair 6: codes and scales of step kt+2     (LDS reads)
+// Expansion piece p covers row tile p % 4 and sub-step 1 (p < 4) or 0
+// (p >= 4) of step kt+1; sub-step-1 operands alternate between two register
+// sets by step parity, sub-step-0 operands are rewritten after their last
+// use in pair 3.
+//
+// Barrier B(kt) sits between pairs 6 and 7 of step kt: it waits for the X
+// tile of step kt+1 (so pair 7 can already read the next step's first
+// fragments) and for this wave's reads of Xs[kt % 2]; right after it the X
+// tile of step kt+2 is copied into Xs[kt % 2], and when kt % 4 == 3 the
+// codes and scales of super-step kt/4 + 2 into the weight buffers of the
+// current super-step, whose last register read was two steps earlier.  A
+// weight copy lands by B(kt+2) and is first read in pair 6 of step kt+3.
+// The loop is unrolled by 8 steps so every buffer choice is a compile-time
+// constant.  k/64 is rounded up to a multiple of 8 steps: steps past the end
+// copy zeros for X (zero-length buffer resource) and their blocks have zero
+// scales, so they add nothing; this keeps a single loop with no tail (a tail
+// would make the compiler move accumulators between register files right
+// behind MFMAs it does not track).
+//
+// Every row-dependent offset goes in the per-lane VGPR offset, which the
+// buffer range check covers: rows past M or N read zero and never touch
+// memory past the tensors.
 __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const float *__restrict__ Sp,
                                                     const uint16_t *__restrict__ X, int64_t M,
                                                     const uint16_t *__restrict__ Bl, int r, int RP,
@@ -344,78 +171,87 @@ __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const float *__re
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int tn = tile % tiles_n;
   const int64_t n0 = (int64_t)tn * FBN, m0 = (int64_t)(tile / tiles_n) * FBM;
-  const int64_t N = w.n, K = w.k, nk = K / kBlock, nsup = nk / kSup;
+  const int64_t N = w.n, K = w.k, nk = K / kBlock, nsup = ceil_div_d(nk, kSup);
+  const int64_t nk8 = ceil_div_d(nk, 8) * 8;  // steps run: whole 8-step rounds
   fill_pair_table(s_pair, tid, 256);
 
   // X rows m0 .. m0+255: wave-instruction i fills LDS chunks [512w + 64i,
   // +64): row 64w + 8i + lane/8, logical chunk (lane & 7) ^ ((lane/8) & 7)
-  // (the swizzle of xsw); rows past M read as zero.
-  const int64_t xrows = min<int64_t>(FBM, M - m0);
-  const __amdgpu_buffer_rsrc_t xrs = rsrc(X + m0 * K, xrows * K * 2);
-  const uint32_t xv = (uint32_t)(((lane >> 3) * K + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
+  // (the swizzle of xsw).
+  const int xbytes = (int)(min<int64_t>(FBM, M - m0) * K * 2);
+  const uint32_t xv = (uint32_t)(((64 * wave + (lane >> 3)) * K + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
   auto xload = [&](int64_t kt, auto B) {
     uint16_t *dst = decltype(B)::value ? Xs1 : Xs0;
+    const __amdgpu_buffer_rsrc_t rs = rsrc(X + m0 * K, kt < nk ? xbytes : 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16, xv,
-                                               (int)((64 * wave + 8 * i) * K * 2 + kt * 128), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
+                                               xv + (uint32_t)(i * 16 * K), (int)(kt * 128), 0, 0);
   };
   // Weight rows n0 .. n0+255, 128 B of codes per row per super-step, in the
-  // same swizzled order; rows past N read as zero.  Scales: 16 B per row,
-  // lane = row within the wave's 64.
-  const int64_t nrows = min<int64_t>(FBN, N - n0);
-  const __amdgpu_buffer_rsrc_t wrs = rsrc(w.packed + n0 * (K / 2), nrows * (K / 2));
-  const uint32_t wv = (uint32_t)((lane >> 3) * (K / 2) + 16 * ((lane & 7) ^ ((lane >> 3) & 7)));
-  const __amdgpu_buffer_rsrc_t srs = rsrc(Sp + (int64_t)tn * nsup * FBN * kSup, nsup * FBN * kSup * 4);
+  // same swizzled order (the column offset is in the range-checked offset
+  // too: a partial last super-step of the last row reads zeros, not past the
+  // tensor).  Scales: 16 B per row, lane = row within the wave's 64 (the
+  // table is padded to whole tiles and super-steps).
+  const int wbytes = (int)(min<int64_t>(FBN, N - n0) * (K / 2));
+  const uint32_t wv = (uint32_t)((64 * wave + (lane >> 3)) * (K / 2) + 16 * ((lane & 7) ^ ((lane >> 3) & 7)));
+  const float *Spt = Sp + (int64_t)tn * nsup * FBN * kSup;
   auto wload = [&](int64_t sp, auto B) {
     uint8_t *dst = decltype(B)::value ? Wc1 : Wc0;
     float *sdst = decltype(B)::value ? Sc1 : Sc0;
+    const bool real = sp < nsup;
+    const __amdgpu_buffer_rsrc_t rs = rsrc(w.packed + n0 * (K / 2), real ? wbytes : 0);
+    const __amdgpu_buffer_rsrc_t ss = rsrc(Spt, real ? (int)(nsup * FBN * kSup * 4) : 0);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (lds_ptr)(dst + (512 * wave + 64 * i) * 16), 16, wv,
-                                               (int)((64 * wave + 8 * i) * (K / 2) + sp * 128), 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_ptr)(sdst + 64 * wave * kSup), 16, (uint32_t)(lane * 16),
-                                             (int)(sp * FBN * kSup * 4 + wave * 1024), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 16), 16,
+                                               wv + (uint32_t)(i * 4 * K + sp * 128), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ss, (lds_ptr)(sdst + 64 * wave * kSup), 16,
+                                             (uint32_t)(wave * 1024 + lane * 16), (int)(sp * FBN * kSup * 4), 0, 0);
   };
   constexpr int kVmemW = 9;  // weight copy instructions per wave and super-step
 
-  // Lane (li, g) of row tile rt expands row 64w + 16rt + li, codes 16g ..
-  // 16g+15 of the step's block: bytes 8g .. 8g+7 = chunk 2j + g/2, half g%2.
-  u32x2_t wcr[4];
-  float sreg[4];
+  // Codes and scales of step s live in set s % 2.  Lane (li, g) of row tile
+  // rt expands row 64w + 16rt + li, codes 16g .. 16g+15 of the step's block:
+  // bytes 8g .. 8g+7 = chunk 2j + g/2, half g%2.
+  u32x2_t wcr[2][4];
+  float sreg[2][4];
   const int wbase = wave * 8192 + li * 128 + 8 * (g & 1);
   const int sbase = (64 * wave + li) * kSup;
-  auto cread = [&](auto S) {  // codes and scales of a step with (step % 8) == S
-    constexpr int s8 = decltype(S)::value, j = s8 & 3;
+  auto cread = [&](auto S, int half) {  // step with (step % 8) == S; row tiles 2half, 2half+1
+    constexpr int s8 = decltype(S)::value, j = s8 & 3, d = s8 & 1;
     const uint8_t *wc = ((s8 >> 2) & 1) ? Wc1 : Wc0;
-    const float *sc = ((s8 >> 2) & 1) ? Sc1 : Sc0;
     const int off = wbase + (((2 * j + (g >> 1)) ^ (li & 7)) << 4);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      wcr[rt] = *reinterpret_cast<const u32x2_t *>(wc + off + rt * 2048);
-      sreg[rt] = sc[sbase + 16 * kSup * rt + j];
-    }
+    for (int rt = 2 * half; rt < 2 * half + 2; ++rt) wcr[d][rt] = *reinterpret_cast<const u32x2_t *>(wc + off + rt * 2048);
   };
-  // Piece p of the next step's expansion: p < 4 -> row tile p, sub-step 1
-  // into an[p] (a[][1] is still in use); p >= 4 -> row tile p-4, sub-step 0
-  // straight into a[p-4][0] (written in MFMA groups 9..15, after its last
-  // read in group 7).
-  u32x4_t a[4][2], an[4];
-  float2 pq[4];  // table reads of the piece in flight
-  auto piece_read = [&](int p) {
-    const uint32_t word = wcr[p & 3][p < 4 ? 1 : 0];
+  auto sread = [&](auto S, int half) {
+    constexpr int s8 = decltype(S)::value, j = s8 & 3, d = s8 & 1;
+    const float *sc = ((s8 >> 2) & 1) ? Sc1 : Sc0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pq[i] = s_pair[(word >> (8 * i)) & 0xFFu];
+    for (int rt = 2 * half; rt < 2 * half + 2; ++rt) sreg[d][rt] = sc[sbase + 16 * kSup * rt + j];
   };
-  auto piece_math = [&](int p) {
-    const int rt = p & 3;
-    const float s = sreg[rt];
-    const u32x4_t v = {bf16x2_rne(__fmul_rn(pq[0].x, s), __fmul_rn(pq[0].y, s)),
-                       bf16x2_rne(__fmul_rn(pq[1].x, s), __fmul_rn(pq[1].y, s)),
-                       bf16x2_rne(__fmul_rn(pq[2].x, s), __fmul_rn(pq[2].y, s)),
-                       bf16x2_rne(__fmul_rn(pq[3].x, s), __fmul_rn(pq[3].y, s))};
-    if (p < 4) an[rt] = v;
-    else a[rt][0] = v;
+
+  u32x4_t a0[4], a1[2][4];  // A operands: sub-step 0; sub-step 1 by step parity
+  u32x4_t bq[2][4];         // X fragments of a pair, by pair parity
+  float2 pq[2][4];          // table reads of an expansion piece, by piece parity
+  // Table read i of piece p from code set d into pq[p % 2][i].
+  auto tread = [&](int d, int p, int i) {
+    const uint32_t word = wcr[d][p & 3][p < 4 ? 1 : 0];
+    pq[p & 1][i] = s_pair[(word >> (8 * i)) & 0xFFu];
+  };
+  // Quarter i of piece p's arithmetic (scales of set d); operands for a
+  // step of parity e.
+  auto tmath = [&](int d, int e, int p, int i) {
+    const float s = sreg[d][p & 3];
+    const float2 v = pq[p & 1][i];
+    const uint32_t x = bf16x2_rne(__fmul_rn(v.x, s), __fmul_rn(v.y, s));
+    if (p < 4) a1[e][p & 3][i] = x;
+    else a0[p & 3][i] = x;
+  };
+  auto xfrag = [&](const uint16_t *xs, int P, int cc) -> u32x4_t {
+    const int t = P >> 2, ct = 4 * (P & 3) + cc;
+    return *reinterpret_cast<const u32x4_t *>(xs + xsw(16 * ct + li, 2 * g + t));
   };
 
   f32x4_t acc[4][16];
@@ -424,66 +260,82 @@ __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const float *__re
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Prologue: X of step 0 and super-step 0's weights landed, step 0
-  // expanded, codes of step 1 in registers.
+  // Prologue: X of step 0 and super-step 0's weights landed; X of step 1
+  // and super-step 1's weights in flight (the copy slot before B(0)); step 0
+  // expanded; codes of step 1 in set 1; pair 0's fragments and piece 0's
+  // table reads issued.
   __syncthreads();  // pair table
   xload(0, std::integral_constant<int, 0>());
   wload(0, std::integral_constant<int, 0>());
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  cread(std::integral_constant<int, 0>());
+  xload(1, std::integral_constant<int, 1>());
+  wload(1, std::integral_constant<int, 1>());
+  cread(std::integral_constant<int, 0>(), 0);
+  cread(std::integral_constant<int, 0>(), 1);
+  sread(std::integral_constant<int, 0>(), 0);
+  sread(std::integral_constant<int, 0>(), 1);
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    piece_read(p);
-    piece_math(p);
-  }
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) a[rt][1] = an[rt];
-  cread(std::integral_constant<int, 1>());
+    for (int i = 0; i < 4; ++i) tread(0, p, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmath(0, 0, p, i);
+  }
+  cread(std::integral_constant<int, 1>(), 0);
+  cread(std::integral_constant<int, 1>(), 1);
+  sread(std::integral_constant<int, 1>(), 0);
+  sread(std::integral_constant<int, 1>(), 1);
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) bq[0][cc] = xfrag(Xs0, 0, cc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tread(1, 0, i);
 
   auto step = [&](int64_t kt, auto U) {
-    constexpr int u = decltype(U)::value, j = u & 3;
-    // Copies past the last step re-read the last one (in bounds, unused).
-    xload(min<int64_t>(kt + 1, nk - 1), std::integral_constant<int, (u + 1) & 1>());
-    if constexpr (j == 0)
-      wload(min<int64_t>((kt >> 2) + 1, nsup - 1), std::integral_constant<int, ((u >> 2) + 1) & 1>());
-    // Fragment (column tile ct, sub-step t) sits at xrow[t] + 1024*ct: the
-    // swizzle term depends on (row & 7) == (li & 7) only.
-    const uint16_t *xs = (u & 1) ? Xs1 : Xs0;
-    const uint16_t *xrow0 = xs + xsw(li, 2 * g), *xrow1 = xs + xsw(li, 2 * g + 1);
-    u32x4_t bq[2][2];
-    bq[0][0] = *reinterpret_cast<const u32x4_t *>(xrow0);
-    bq[0][1] = *reinterpret_cast<const u32x4_t *>(xrow0 + 1024);
+    constexpr int u = decltype(U)::value, j = u & 3, e = u & 1;
+    const uint16_t *xs = e ? Xs1 : Xs0, *xn = e ? Xs0 : Xs1;
+    constexpr int dc = (u + 1) & 1;  // code set of step kt+1 (expanded now)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {  // group q: sub-step t = q/8, column tiles 2(q%8), +1
-      const int t = q >> 3, ct0 = 2 * (q & 7);
-      if (q < 15) {
-        const int t1 = (q + 1) >> 3, c1 = 2 * ((q + 1) & 7);
-        const uint16_t *xr = t1 ? xrow1 : xrow0;
-        bq[(q + 1) & 1][0] = *reinterpret_cast<const u32x4_t *>(xr + 1024 * c1);
-        bq[(q + 1) & 1][1] = *reinterpret_cast<const u32x4_t *>(xr + 1024 * (c1 + 1));
+    for (int P = 0; P < 8; ++P) {
+      const int t = P >> 2, ct0 = 4 * (P & 3);
+      if (P == 7) {
+        // B(kt): the X tile of step kt+1 landed everywhere, every wave done
+        // reading Xs[kt % 2]; then refill it with step kt+2.
+        if constexpr (j == 0)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kVmemW) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // (copies past the end read zeros; their data is never used)
+        xload(kt + 2, std::integral_constant<int, e>());
+        if constexpr (j == 3) wload((kt >> 2) + 2, std::integral_constant<int, (u >> 2) & 1>());
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if ((q & 1) == 0) piece_read(q >> 1);  // consumed by the next group
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct0 + cc], a[rt][t], bq[q & 1][cc]);
-      if ((q & 1) == 1) piece_math(q >> 1);  // (on the last step: codes that are never used)
-      __builtin_amdgcn_sched_barrier(0);
+      for (int s = 0; s < 16; ++s) {
+        const int cc = s >> 2, rt = s & 3;
+        mfma16_acc(acc[rt][ct0 + cc], t ? a1[e][rt] : a0[rt], bq[P & 1][cc]);
+        if (s < 12) {
+          const int q = s / 3, kind = s % 3;
+          if (kind == 0) {  // X fragment q of the next pair
+            if (P < 7) bq[(P + 1) & 1][q] = xfrag(xs, P + 1, q);
+            else bq[0][q] = xfrag(xn, 0, q);
+          } else if (kind == 1) {  // table read q of the next piece
+            if (P < 7) tread(dc, P + 1, q);
+            else tread(e, 0, q);  // piece 0 of step kt+1's expansion: codes of kt+2
+          } else {
+            tmath(dc, e ^ 1, P, q);
+          }
+        } else if (P == 6) {  // codes and scales of step kt+2
+          if (s == 12) cread(std::integral_constant<int, (u + 2) & 7>(), 0);
+          if (s == 13) cread(std::integral_constant<int, (u + 2) & 7>(), 1);
+          if (s == 14) sread(std::integral_constant<int, (u + 2) & 7>(), 0);
+          if (s == 15) sread(std::integral_constant<int, (u + 2) & 7>(), 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) a[rt][1] = an[rt];
-    cread(std::integral_constant<int, (u + 2) & 7>());  // (past the end: stale, unused)
-    // Bare barrier: the loop's only LDS writes are the copies, so
-    // __syncthreads()'s release fence would merely wait for the weight copy
-    // that may stay in flight after a j == 0 step.
-    if constexpr (j == 0)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kVmemW) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   };
-  const int64_t n8 = nk >> 3;
-  for (int64_t p = 0; p < n8; ++p) {
+  for (int64_t p = 0; p < nk8 / 8; ++p) {
     step(8 * p, std::integral_constant<int, 0>());
     step(8 * p + 1, std::integral_constant<int, 1>());
     step(8 * p + 2, std::integral_constant<int, 2>());
@@ -493,12 +345,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const float *__re
     step(8 * p + 6, std::integral_constant<int, 6>());
     step(8 * p + 7, std::integral_constant<int, 7>());
   }
-  if constexpr (kOddSup) {
-    step(nk - 4, std::integral_constant<int, 0>());
-    step(nk - 3, std::integral_constant<int, 1>());
-    step(nk - 2, std::integral_constant<int, 2>());
-    step(nk - 1, std::integral_constant<int, 3>());
-  }
+  mfma_acc_fence();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   fwd_epilogue(acc, Xs0, Bl, r, RP, sH, Y, N, M, n0 + 64 * wave, m0);
@@ -507,7 +354,6 @@ __global__ __launch_bounds__(256, 1) void k_fwd_nf4(Nf4View w, const float *__re
 struct FwdWs {
   SplitPlan sp;
   int RP;
-  bool staged;  // k % 256 == 0: k_fwd_nf4 with precomputed tile scales
   size_t part_off, sh_off, scale_off, total;
 };
 
@@ -515,11 +361,11 @@ FwdWs fwd_ws_layout(int64_t M, int64_t n, int64_t k, int r) {
   FwdWs l;
   l.RP = lora_rank_pad(r);
   l.sp = plan_split(ceil_div(M, 64), ceil_div(k, 64));
-  l.staged = (k % (kBlock * kSup)) == 0;
   l.part_off = 0;
   l.sh_off = align_up((size_t)l.sp.splits * M * l.RP * sizeof(float), 256);
   l.scale_off = l.sh_off + align_up((size_t)M * l.RP * sizeof(uint16_t), 256);
-  l.total = l.scale_off + (l.staged ? align_up((size_t)ceil_div(n, FBN) * FBN * (k / kBlock) * sizeof(float), 256) : 0);
+  l.total = l.scale_off +
+            align_up((size_t)ceil_div(n, FBN) * ceil_div(k / kBlock, kSup) * FBN * kSup * sizeof(float), 256);
   return l;
 }
 
@@ -539,23 +385,11 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   e = launch_reduce_rows(part, l.sp.splits, M, l.RP, a.r, a.s, H_out, sH, nullptr, 0, s);
   if (e != hipSuccess) return e;
   const int tiles_n = (int)ceil_div(N, FBN), tiles_m = (int)ceil_div(M, FBM);
-  const dim3 grid((unsigned)(tiles_n * tiles_m));
-  if (l.staged) {
-    float *Sp = reinterpret_cast<float *>(static_cast<char *>(ws) + l.scale_off);
-    const int64_t nsup = K / (kBlock * kSup), total = (int64_t)tiles_n * nsup * FBN;
-    QLORA_LAUNCH("k_tile_scales", k_tile_scales, dim3((unsigned)(total / 256)), dim3(256), 0, s, a.w, nsup, total, Sp);
-    if (nsup & 1)
-      QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<1>, grid, dim3(256), 0, s, a.w, Sp, X, M, B, a.r, l.RP, sH, Y, tiles_n);
-    else
-      QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4<0>, grid, dim3(256), 0, s, a.w, Sp, X, M, B, a.r, l.RP, sH, Y, tiles_n);
-    return hipGetLastError();
-  }
-  switch ((K / kBlock) & 3) {
-    case 0: QLORA_LAUNCH("k_fwd_nf4_any", k_fwd_nf4_any<0>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n); break;
-    case 1: QLORA_LAUNCH("k_fwd_nf4_any", k_fwd_nf4_any<1>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n); break;
-    case 2: QLORA_LAUNCH("k_fwd_nf4_any", k_fwd_nf4_any<2>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n); break;
-    default: QLORA_LAUNCH("k_fwd_nf4_any", k_fwd_nf4_any<3>, grid, dim3(256), 0, s, a.w, X, M, B, a.r, l.RP, sH, Y, tiles_n); break;
-  }
+  float *Sp = reinterpret_cast<float *>(static_cast<char *>(ws) + l.scale_off);
+  const int64_t nsup = ceil_div(K / kBlock, kSup), total = (int64_t)tiles_n * nsup * FBN;
+  QLORA_LAUNCH("k_tile_scales", k_tile_scales, dim3((unsigned)(total / 256)), dim3(256), 0, s, a.w, nsup, total, Sp);
+  QLORA_LAUNCH("k_fwd_nf4", k_fwd_nf4, dim3((unsigned)(tiles_n * tiles_m)), dim3(256), 0, s, a.w, Sp, X, M, B, a.r,
+               l.RP, sH, Y, tiles_n);
   return hipGetLastError();
 }
 
