@@ -5,17 +5,18 @@
 // explained." step 5: gradients reach the adapters only.  With
 // Y = X W_hat^T + s (X A^T) B^T:
 //   G  = s dY B            (k_nt_splitk on dY and B^T)
-//   dX = dY W_hat + G A    (k_bwd_dx, below)
+//   dX = dY W_hat + G A    (k_bwd_dx_nf4 in nf4_tile.hip; k_bwd_dx below when
+//                           n % 64 != 0)
 //   dB = s dY^T H          (k_tn_splitk on dY and (sH)^T)
 //   dA = G^T X             (k_tn_splitk on X and G^T)
 //
-// k_bwd_dx contracts over n, the row index of W, so the dequantized tile is
-// laid into LDS transposed: each thread expands one packed dword (8 codes
-// along k) from each of 4 consecutive rows n, transposes the 4x8 block in
-// registers with byte permutes and writes eight 8-byte runs of [k][n].  The
-// output tile is computed as C[k][m] so a lane's four accumulators are four
-// consecutive k of one dX row.
-#include "lora_gemm.h"
+// k_bwd_dx, the general fallback, contracts over n, the row index of W, by
+// laying the dequantized tile into LDS transposed: each thread expands one
+// packed dword (8 codes along k) from each of 4 consecutive rows n,
+// transposes the 4x8 block in registers with byte permutes and writes eight
+// 8-byte runs of [k][n].  The output tile is computed as C[k][m] so a lane's
+// four accumulators are four consecutive k of one dX row.
+#include "nf4_tile.h"
 
 namespace qlora {
 namespace {
@@ -133,230 +134,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(Nf4View w, const uint16_t *__
     }
 }
 
-// ---------------------------------------------------------------------------
-// k_bwd_dx_nf4: the same product on 256 (k) x 256 (m) tiles, for n % 64 == 0.
-// Wave w owns dX columns k0 + 64w .. +63 (four 16-row MFMA tiles of C[k][m])
-// and all 256 m: 256 fp32 accumulators per lane, pinned to AGPRs.  Per
-// 64-wide step over n:
-//   * the dY tile [256 m][64 n] streams global -> LDS by buffer loads into
-//     the other of two LDS arrays (the B operand, as X is in the forward);
-//   * each thread expands an 8-row x 8-column block of codes (rows n, one
-//     packed dword per row), transposes it with byte permutes and writes
-//     eight 16-byte runs of W_hat^T [256 k][64 n] (the A operand) into the
-//     other of two LDS arrays; the 256 block scales of a step are computed
-//     once (one per thread) and shared through a small LDS table.
-// Expansion of step s+1 is interleaved with the MFMA groups of step s.
-// Lane (li, g) reads contraction slots 16g .. 16g+15 of the step (sub-step t:
-// 16g + 8t .. +7) from both operands.
-template <bool kOddSteps>
-__global__ __launch_bounds__(256, 1) void k_bwd_dx_nf4(Nf4View w, const uint16_t *__restrict__ dY, int64_t M,
-                                                       const uint16_t *__restrict__ At,
-                                                       const uint16_t *__restrict__ Gb, int RP,
-                                                       uint16_t *__restrict__ dX, int tiles_k) {
-  __shared__ __align__(16) uint16_t Ds0[256 * 64];
-  __shared__ __align__(16) uint16_t Ds1[256 * 64];
-  __shared__ __align__(16) uint16_t Ws0[256 * 64];
-  __shared__ __align__(16) uint16_t Ws1[256 * 64];
-  __shared__ __align__(16) float Ss0[4 * 64];  // block scales of a step, [k-block][n]
-  __shared__ __align__(16) float Ss1[4 * 64];
-  __shared__ float2 s_pair[256];
-  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t k0 = (int64_t)(tile % tiles_k) * 256, m0 = (int64_t)(tile / tiles_k) * 256;
-  const int64_t N = w.n, K = w.k, nkb = K / kBlock, nsteps = N / 64;
-  fill_pair_table(s_pair, tid, 256);
-  const float offset = *w.offset;
-
-  // dY rows m0 .. m0+255 (buffer range ends at row M; the row offset is in
-  // the range-checked per-lane offset, so rows past M read 0).
-  const int64_t yrows = min<int64_t>(256, M - m0);
-  const __amdgpu_buffer_rsrc_t yrs = rsrc(dY + m0 * N, yrows * N * 2);
-  const uint32_t yv = (uint32_t)(((64 * wave + (lane >> 3)) * N + 8 * ((lane & 7) ^ ((lane >> 3) & 7))) * 2);
-  auto yload = [&](int64_t st, auto BUF) {
-    uint16_t *dst = decltype(BUF)::value ? Ds1 : Ds0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(yrs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
-                                               yv + (uint32_t)(i * 16 * N), (int)(st * 128), 0, 0);
-  };
-  // Codes: thread (ng = tid >> 5, kg = tid & 31) covers rows 8ng .. 8ng+7 of
-  // the step and columns k0 + 8kg .. +7 (one dword per row; columns past K
-  // only feed rows of C that are never stored, and past the last row they
-  // fall outside the range-checked offset and read 0).
-  const int ng = tid >> 5, kg = tid & 31;
-  const __amdgpu_buffer_rsrc_t wrs = rsrc(w.packed, w.n * (K / 2));
-  const uint32_t wv = (uint32_t)(8 * ng * (K / 2) + (k0 + 8 * kg) / 2);
-  // Scales: thread t computes the scale of step-row t >> 2, k-block t & 3.
-  const int srow = tid >> 2, sblk = tid & 3;
-  const int64_t sb_kb = min<int64_t>(k0 / kBlock + sblk, nkb - 1);
-  const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code, w.nb);
-  const __amdgpu_buffer_rsrc_t grs = rsrc(w.group_amax, ceil_div_d(w.nb, kGroup) * 4);
-
-  uint32_t wa[8], wb[8];
-  uint32_t scb = 0;
-  float gab = 0.f;
-  auto wload = [&](int64_t st, uint32_t(&wc)[8]) {
-#pragma unroll
-    for (int rho = 0; rho < 8; ++rho)
-      wc[rho] = __builtin_amdgcn_raw_buffer_load_b32(wrs, wv + (uint32_t)((st * 64 + rho) * (K / 2)), 0, 0);
-  };
-  auto sload = [&](int64_t st) {
-    const int64_t b = (st * 64 + srow) * nkb + sb_kb;
-    scb = __builtin_amdgcn_raw_buffer_load_b8(srs, (uint32_t)b, 0, 0);
-    gab = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grs, (uint32_t)((b >> 8) * 4), 0, 0));
-  };
-  auto sstore = [&](float *S) { S[sblk * 64 + srow] = block_scale(scb, gab, offset); };
-
-  // Expansion of one step's codes (wa) into W_hat^T, in 8 pieces: pieces
-  // 0-3 expand rows 2p, 2p+1; pieces 4-7 transpose and write columns
-  // 2(p-4), 2(p-4)+1.
-  uint32_t ex[8][4];
-  float sx[8];
-  auto expand_piece = [&](int p, const float *S, uint16_t *Wd) {
-    if (p == 0) {
-      const f32x4_t s0 = *reinterpret_cast<const f32x4_t *>(&S[(kg >> 3) * 64 + 8 * ng]);
-      const f32x4_t s1 = *reinterpret_cast<const f32x4_t *>(&S[(kg >> 3) * 64 + 8 * ng + 4]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sx[i] = s0[i], sx[4 + i] = s1[i];
-    }
-    if (p < 4) {
-      dequant_word(wa[2 * p], sx[2 * p], s_pair, ex[2 * p]);
-      dequant_word(wa[2 * p + 1], sx[2 * p + 1], s_pair, ex[2 * p + 1]);
-    } else {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kc = 2 * (p - 4) + h, d = kc >> 1;
-        u32x4_t v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = (kc & 1) ? pack_hi(ex[2 * e][d], ex[2 * e + 1][d]) : pack_lo(ex[2 * e][d], ex[2 * e + 1][d]);
-        *reinterpret_cast<u32x4_t *>(&Wd[xsw(8 * kg + kc, ng)]) = v;
-      }
-    }
-  };
-
-  f32x4_t acc[4][16];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 16; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // Prologue: scales of steps 0 and 1, expanded step 0, codes of step 1.
-  __syncthreads();  // pair table
-  sload(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  sstore(Ss0);
-  sload(min<int64_t>(1, nsteps - 1));
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  sstore(Ss1);
-  wload(0, wa);
-  yload(0, std::integral_constant<int, 0>());
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-#pragma unroll
-  for (int p = 0; p < 8; ++p) expand_piece(p, Ss0, Ws0);
-  wload(min<int64_t>(1, nsteps - 1), wa);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  auto step = [&](int64_t st, auto BUF) {
-    constexpr int buf = decltype(BUF)::value;
-    const uint16_t *Ws = buf ? Ws1 : Ws0;
-    const uint16_t *Ds = buf ? Ds1 : Ds0;
-    uint16_t *Wn = buf ? Ws0 : Ws1;
-    const float *Sn = buf ? Ss0 : Ss1;  // scales of step st+1
-    float *Sf = buf ? Ss1 : Ss0;        // slot for step st+2's scales
-    yload(min<int64_t>(st + 1, nsteps - 1), std::integral_constant<int, buf ^ 1>());
-    wload(min<int64_t>(st + 2, nsteps - 1), wb);
-    sload(min<int64_t>(st + 2, nsteps - 1));
-    const uint16_t *d0 = Ds + xsw(li, 2 * g), *d1 = Ds + xsw(li, 2 * g + 1);
-    u32x4_t a[4], bq[2][2];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) a[rt] = *reinterpret_cast<const u32x4_t *>(&Ws[xsw(64 * wave + 16 * rt + li, 2 * g)]);
-    bq[0][0] = *reinterpret_cast<const u32x4_t *>(d0);
-    bq[0][1] = *reinterpret_cast<const u32x4_t *>(d0 + 1024);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {  // group q: sub-step t = q/8, column tiles 2(q%8), +1
-      const int ct0 = 2 * (q & 7);
-      if (q == 8) {
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          a[rt] = *reinterpret_cast<const u32x4_t *>(&Ws[xsw(64 * wave + 16 * rt + li, 2 * g + 1)]);
-      }
-      if (q < 15) {
-        const int t1 = (q + 1) >> 3, c1 = 2 * ((q + 1) & 7);
-        const uint16_t *dr = t1 ? d1 : d0;
-        bq[(q + 1) & 1][0] = *reinterpret_cast<const u32x4_t *>(dr + 1024 * c1);
-        bq[(q + 1) & 1][1] = *reinterpret_cast<const u32x4_t *>(dr + 1024 * (c1 + 1));
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct0 + c], a[rt], bq[q & 1][c]);
-      if ((q & 1) == 1) expand_piece(q >> 1, Sn, Wn);  // step st+1 (stale codes on the last step)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    sstore(Sf);
-#pragma unroll
-    for (int rho = 0; rho < 8; ++rho) wa[rho] = wb[rho];
-    __syncthreads();
-  };
-  const int64_t npairs = nsteps >> 1;
-  for (int64_t p = 0; p < npairs; ++p) {
-    step(2 * p, std::integral_constant<int, 0>());
-    step(2 * p + 1, std::integral_constant<int, 1>());
-  }
-  if constexpr (kOddSteps) step(nsteps - 1, std::integral_constant<int, 0>());
-
-  // LoRA term: acc += A^T[k][:] . G[m][:] over the padded rank, in 64-wide
-  // chunks (A operand: rows of A^T straight from global; G tile in LDS).
-  for (int jc = 0; jc < RP; jc += 64) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4_t *>(&Ds0[xsw(c >> 3, c & 7)]) =
-          load8(Gb, RP, M, RP, m0 + (c >> 3), jc + 8 * (c & 7), true);
-    }
-    u32x4_t a[4][2];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) a[rt][t] = load8(At, RP, K, RP, k0 + 64 * wave + 16 * rt + li, jc + 16 * g + 8 * t, true);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct) {
-        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&Ds0[xsw(16 * ct + li, 2 * g + t)]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct], a[rt][t], b);
-      }
-    __syncthreads();
-  }
-  mfma_acc_fence();
-
-  // acc[rt][ct][v] = C[k][m]: k = k0+64w+16rt+4g+v, m = m0+16ct+li -> dX[m][k..k+3].
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 16; ++ct) {
-      const int64_t k = k0 + 64 * wave + 16 * rt + 4 * g;
-      const int64_t m = m0 + 16 * ct + li;
-      if (m < M && k < K) {
-        const f32x4_t v = acc[rt][ct];
-        *reinterpret_cast<u32x2_t *>(dX + m * K + k) = u32x2_t{bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
 struct BwdWs {
   int RP;
   int64_t Mp;
   SplitPlan sp_h, sp_g, sp_b, sp_a;
-  size_t part_off, h_off, sht_off, bt_off, at_off, gb_off, gt_off, total;
+  size_t part_off, h_off, sht_off, bt_off, at_off, gb_off, gt_off, scale_off, total;
 };
 
 BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, int r) {
@@ -383,6 +165,7 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, int r) {
   l.at_off = take((size_t)K * l.RP * 2);
   l.gb_off = take((size_t)M * l.RP * 2);
   l.gt_off = take((size_t)l.RP * l.Mp * 2);
+  l.scale_off = take(tile_scales_bytes(N, K));
   l.total = off;
   return l;
 }
@@ -430,14 +213,8 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   QLORA_TRY(launch_nt_splitk(dY, M, Bt, RP, RP, N, N, l.sp_g, part, s));
   QLORA_TRY(launch_reduce_rows(part, l.sp_g.splits, M, RP, r, a.s, nullptr, Gb, Gt, l.Mp, s));
   if (dX != nullptr) {
-    // whole-tensor code offsets stay 32-bit below 2^31 bytes
-    if (N % 64 == 0 && N * (K / 2) < (int64_t(1) << 31)) {
-      const int tiles_k = (int)ceil_div(K, 256), tiles_m = (int)ceil_div(M, 256);
-      const dim3 grid((unsigned)(tiles_k * tiles_m));
-      if ((N / 64) & 1)
-        QLORA_LAUNCH("k_bwd_dx_nf4", k_bwd_dx_nf4<true>, grid, dim3(256), 0, s, a.w, dY, M, At, Gb, RP, dX, tiles_k);
-      else
-        QLORA_LAUNCH("k_bwd_dx_nf4", k_bwd_dx_nf4<false>, grid, dim3(256), 0, s, a.w, dY, M, At, Gb, RP, dX, tiles_k);
+    if (bwd_tiles_supported(N, K)) {
+      QLORA_TRY(launch_bwd_dx_tiles(a.w, reinterpret_cast<float *>(base + l.scale_off), dY, M, At, RP, Gb, dX, s));
     } else {  // ragged n: the general 128 x 128 kernel
       const dim3 grid((unsigned)ceil_div(K, DBK), (unsigned)ceil_div(M, DBM));
       QLORA_LAUNCH("k_bwd_dx", k_bwd_dx, grid, dim3(256), 0, s, a.w, dY, M, At, Gb, RP, dX);

@@ -1,0 +1,28 @@
+// nf4_tile.h -- launch interface of the NF4 x BF16 tile kernels (nf4_tile.hip).
+#pragma once
+
+#include "lora_gemm.h"
+
+namespace qlora {
+
+// Device bytes of the block-scale table either pass stages for an [n, k]
+// weight (the larger of the two layouts).
+size_t tile_scales_bytes(int64_t n, int64_t k);
+
+// Whether launch_bwd_dx_tiles handles this weight shape: n % 64 == 0 and the
+// packed weight below 2^31 bytes (32-bit offsets into it).
+bool bwd_tiles_supported(int64_t n, int64_t k);
+
+// Y[M, n] = bf16( X W_hat^T + sH B_lora^T ):  X [M, k], sH [M, RP] = bf16(s H)
+// with the rank padded to RP by zeros, B_lora [n, r] (row stride r).
+// `scales`: device scratch of tile_scales_bytes(n, k).
+hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, int64_t M, const uint16_t *Bl, int r,
+                            int RP, const uint16_t *sH, uint16_t *Y, hipStream_t s);
+
+// dX[M, k] = bf16( dY W_hat + G At^T ):  dY [M, n], At [k, RP] (A_lora
+// transposed, rank padded), G [M, RP].  Requires bwd_tiles_supported;
+// `scales` as above.
+hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
+                               int RP, const uint16_t *Gb, uint16_t *dX, hipStream_t s);
+
+}  // namespace qlora

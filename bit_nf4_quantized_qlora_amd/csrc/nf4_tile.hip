@@ -1,0 +1,466 @@
+// nf4_tile.hip -- the dense NF4 x BF16 tile kernel of the forward pass and of
+// the input-gradient pass, and the block-scale pre-passes that feed it.
+//
+// "QLoRA Paper Breakdown" sec. 4: the forward multiplies X by the weights
+// dequantized on the fly, and the backward pass needs dY W_hat through the
+// same on-the-fly dequantization, never forming dL/dW ("QLoRA, explained."
+// steps 4-5; "reading note": the multiply runs in 16 bits).  Both passes are
+//   C[o][m] = sum_c A[o][c] B[m][c] + sum_j L[o][j] R[m][j],  out[m][o] = bf16(C[o][m])
+//   forward:  o = n, c = k, A = W_hat,   B = X,  L = B_lora,    R = bf16(s H), out = Y
+//   backward: o = k, c = n, A = W_hat^T, B = dY, L = A_lora^T, R = G,          out = dX
+// on 256 (o) x 256 (m) tiles, one workgroup of four waves per tile.
+//
+// Wave w owns o-rows o0 + 64w .. +63 (four 16-row MFMA tiles rt) and all 256
+// m (sixteen 16-column tiles ct): 256 fp32 accumulators per lane, pinned to
+// AGPRs.  The A operand never exists as a BF16 tile: lane (li = lane & 15,
+// g = lane >> 4) of row tile rt holds 16 NF4 codes of row o = o0+64w+16rt+li
+// at contraction positions 16g .. 16g+15 of the current 64-wide step, and
+// expands them in registers (256-entry table of level pairs, times the block
+// scale, rounded to BF16 -- bit-identical to the standalone dequantization)
+// straight into MFMA operands; sub-step t uses positions 16g+8t .. +7.  The B
+// fragment of the same lane reads the same contraction positions, so the sum
+// is unchanged.
+//   forward:  the 16 codes are 8 consecutive bytes of weight row o (one
+//             block, one scale), read from the staged code tile by ds_read_b64;
+//   backward: they are one column k of 16 consecutive weight rows n, which
+//             ds_read_b64_tr_b4 (a 16x16 nibble transpose across the 16 lanes
+//             of a group) gathers from the staged code tile; each row has its
+//             own block scale.
+//
+// Every operand streams global -> LDS by buffer loads that write LDS
+// directly (no registers): the B tile one 64-wide step at a time, the packed
+// codes 4 steps at a time (a "super-step": 256 rows x 128 B) together with
+// their precomputed block scales (k_scales_fwd / k_scales_bwd).
+//
+// LDS: B tiles Bs0/Bs1 (2 x 32 KB), code tiles Wc0/Wc1 (2 x 32 KB), scale
+// tiles Sc0/Sc1 (2 x 4 KB), pair table 2 KB.  Swizzles for 64 banks (256 B
+// per bank row): in a B tile, row R (128 B) holds its 16-byte chunk c at
+// chunk c ^ ((R >> 1) & 7), and each fragment is read as two 8-byte halves,
+// the first being half g % 2, so every 32-lane half-wave read covers 32
+// distinct bank pairs; code tiles use the same chunk swizzle.
+//
+// One wave per SIMD, so the wave's own instruction stream hides every
+// latency: a step is eight "pairs" of 16 MFMAs (pair P: sub-step P/4, column
+// tiles 4(P%4) .. +3), and after each MFMA the wave issues one small piece of
+// other work for later pairs: a B fragment of pair P+1, a table read of
+// expansion piece P+1, a quarter of the arithmetic of piece P, or (pair 6)
+// the codes and scales of step kt+2.  Piece p covers row tile p % 4 and
+// sub-step 1 (p < 4) or 0 (p >= 4) of step kt+1; sub-step-1 operands
+// alternate between two register sets by step parity, sub-step-0 operands
+// are rewritten after their last use in pair 3.
+//
+// Barrier B(kt) sits between pairs 6 and 7 of step kt: it waits for the B
+// tile of step kt+1 (so pair 7 can already read the next step's first
+// fragments) and for this wave's reads of Bs[kt % 2]; right after it the B
+// tile of step kt+2 is copied into Bs[kt % 2], and when kt % 4 == 3 the codes
+// and scales of super-step kt/4 + 2 into the code buffers of the current
+// super-step, whose last register read was two steps earlier.  A code copy
+// lands by B(kt+2) and is first read in pair 6 of step kt+3.  The loop is
+// unrolled by 8 steps so every buffer choice is a compile-time constant; the
+// step count is rounded up to a multiple of 8, and steps past the end copy
+// zeros for B (zero-length buffer resource) and have zero scales, so they add
+// nothing.  A single loop with no tail also keeps the compiler from moving
+// accumulators between register files right behind MFMAs it does not track.
+//
+// Every row-dependent offset goes in the per-lane VGPR offset, which the
+// buffer range check covers: rows past M, N or the end of the weight read
+// zero and never touch memory past the tensors.
+#include "nf4_tile.h"
+
+namespace qlora {
+namespace {
+
+constexpr int TO = 256, TM = 256;  // tile: o rows x m rows
+constexpr int kSup = 4;            // steps per staged code chunk
+
+__host__ __device__ inline int64_t fwd_nsup(int64_t k) { return (k / kBlock + kSup - 1) / kSup; }
+__host__ __device__ inline int64_t bwd_nsup(int64_t n) { return (n + TO - 1) / TO; }
+
+// Forward scale table: for weight tile to (rows 256to ..) and super-step sp
+// (blocks 4sp .. 4sp+3 of each row) one contiguous 4 KB run,
+// Sp[((to*nsup + sp)*256 + row)*4 + j]; rows past n and blocks past k/64 hold
+// 0.  block_scale is the dequantization's own (bit-identical).
+__global__ __launch_bounds__(256) void k_scales_fwd(Nf4View w, int64_t nsup, int64_t total, float *__restrict__ Sp) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int64_t q = t >> 8, to = q / nsup, sp = q - to * nsup;
+  const int64_t n = to * TO + (t & 255), nkb = w.k / kBlock;
+  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+  if (n < w.n) {
+    const float off = *w.offset;
+#pragma unroll
+    for (int j = 0; j < kSup; ++j) {
+      const int64_t kb = kSup * sp + j, b = n * nkb + kb;
+      if (kb < nkb) v[j] = block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
+    }
+  }
+  *reinterpret_cast<f32x4_t *>(Sp + 4 * t) = v;
+}
+
+// Backward scale table: for column tile tk (k-blocks 4tk .. 4tk+3) and
+// super-step sp (weight rows 256sp .. 256sp+255) one contiguous 4 KB run,
+// Sp[((tk*nsup + sp)*4 + blk)*256 + row]; rows past n and blocks past k/64
+// hold 0.
+__global__ __launch_bounds__(256) void k_scales_bwd(Nf4View w, int64_t nsup, int64_t total, float *__restrict__ Sp) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int64_t q = t >> 10, tk = q / nsup, sp = q - tk * nsup;
+  const int64_t n = sp * TO + (t & 255), kb = tk * 4 + ((t >> 8) & 3), nkb = w.k / kBlock;
+  float v = 0.f;
+  if (n < w.n && kb < nkb) {
+    const int64_t b = n * nkb + kb;
+    v = block_scale(w.scale_code[b], w.group_amax[b / kGroup], *w.offset);
+  }
+  Sp[t] = v;
+}
+
+// Tail after the main loop has drained (every copy landed, all waves past a
+// barrier): the LoRA term in 64-wide chunks of the padded rank -- the same
+// fragment layout with A = rows of L (direct loads, row stride lda) and the R
+// tile staged in LDS (stage: 32 KB, classic xsw swizzle) -- then out.
+// acc[rt][ct][v] = C[o][m] with o = ow + 16rt + 4g + v and m = m0 + 16ct + li
+// (four consecutive o of one output row).
+__device__ __forceinline__ void lora_and_store(f32x4_t (&acc)[4][16], uint16_t *stage,
+                                               const uint16_t *__restrict__ L, int lda, int RP,
+                                               const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
+                                               int64_t NO, int64_t M, int64_t ow, int64_t m0) {
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const bool lvec = (lda % 8) == 0;
+  for (int jc = 0; jc < RP; jc += 64) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 256 * i;
+      *reinterpret_cast<u32x4_t *>(&stage[xsw(c >> 3, c & 7)]) =
+          load8(R, RP, M, RP, m0 + (c >> 3), jc + 8 * (c & 7), true);
+    }
+    u32x4_t a[4][2];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) a[rt][t] = load8(L, lda, NO, lda, ow + 16 * rt + li, jc + 16 * g + 8 * t, lvec);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ct = 0; ct < 16; ++ct) {
+        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&stage[xsw(16 * ct + li, 2 * g + t)]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct], a[rt][t], b);
+      }
+    __syncthreads();
+  }
+  mfma_acc_fence();
+
+  const bool ovec = (NO & 3) == 0;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct) {
+      const int64_t o = ow + 16 * rt + 4 * g;
+      const int64_t m = m0 + 16 * ct + li;
+      if (m < M) {
+        const f32x4_t v = acc[rt][ct];
+        uint16_t *dst = out + m * NO + o;
+        if (ovec && o + 4 <= NO) {
+          *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (o + e < NO) dst[e] = f32_to_bf16_bits(v[e]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool kBwd>
+__global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__restrict__ Sp,
+                                                     const uint16_t *__restrict__ Bact, int64_t M,
+                                                     const uint16_t *__restrict__ L, int lda, int RP,
+                                                     const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
+                                                     int tiles_o) {
+  __shared__ __align__(16) uint16_t Bs0[TM * 64];
+  __shared__ __align__(16) uint16_t Bs1[TM * 64];
+  __shared__ __align__(16) uint8_t Wc0[256 * 128];
+  __shared__ __align__(16) uint8_t Wc1[256 * 128];
+  __shared__ __align__(16) float Sc0[256 * kSup];
+  __shared__ __align__(16) float Sc1[256 * kSup];
+  __shared__ float2 s_pair[256];
+  // wave is uniform across the wave; say so, or wave-dependent scalar
+  // offsets would be made uniform with a per-lane loop
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int to = tile % tiles_o;
+  const int64_t o0 = (int64_t)to * TO, m0 = (int64_t)(tile / tiles_o) * TM;
+  const int64_t N = w.n, K = w.k;
+  const int64_t NO = kBwd ? K : N, NC = kBwd ? N : K;  // output width, contraction length
+  const int64_t nk = NC / kBlock;                      // 64-wide steps
+  const int64_t nsup = kBwd ? bwd_nsup(N) : fwd_nsup(K);
+  const int64_t nk8 = ceil_div_d(nk, 8) * 8;  // steps run: whole 8-step rounds
+  fill_pair_table(s_pair, tid, 256);
+
+  // B rows m0 .. m0+255 (row stride NC): wave-instruction i fills LDS chunks
+  // [512w + 64i, +64): row 64w + 8i + lane/8, physical chunk lane & 7, so the
+  // logical chunk it copies depends on the parity of i.
+  const int bbytes = (int)(min<int64_t>(TM, M - m0) * NC * 2);
+  uint32_t bv[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    bv[par] = (uint32_t)(((64 * wave + (lane >> 3)) * NC + 8 * ((lane & 7) ^ (4 * par + (lane >> 4)))) * 2);
+  auto bload = [&](int64_t kt, auto D) {
+    uint16_t *dst = decltype(D)::value ? Bs1 : Bs0;
+    const __amdgpu_buffer_rsrc_t rs = rsrc(Bact + m0 * NC, kt < nk ? bbytes : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
+                                               bv[i & 1] + (uint32_t)(i * 16 * NC), (int)(kt * 128), 0, 0);
+  };
+  // Code tile of a super-step: 256 rows x 128 B, same copy pattern and
+  // swizzle.  Forward: row r = weight row o0 + r, bytes 128sp .. (4 steps of
+  // k).  Backward: row r = weight row 256sp + r, bytes o0/2 .. (the tile's
+  // 256 columns k).  Scales: 4 KB per super-step, 1 KB per wave.
+  const int64_t kb2 = K / 2;  // packed bytes per weight row
+  const uint8_t *wbase_g = kBwd ? w.packed : w.packed + o0 * kb2;
+  const int wbytes = (int)(kBwd ? N * kb2 : min<int64_t>(TO, N - o0) * kb2);
+  uint32_t wv[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par)
+    wv[par] = (uint32_t)((64 * wave + (lane >> 3)) * kb2 + (kBwd ? o0 / 2 : 0) +
+                         16 * ((lane & 7) ^ (4 * par + (lane >> 4))));
+  const float *Spt = Sp + (int64_t)to * nsup * 256 * kSup;
+  auto wload = [&](int64_t sp, auto D) {
+    uint8_t *dst = decltype(D)::value ? Wc1 : Wc0;
+    float *sdst = decltype(D)::value ? Sc1 : Sc0;
+    const bool real = sp < nsup;
+    const __amdgpu_buffer_rsrc_t rs = rsrc(wbase_g, real ? wbytes : 0);
+    const __amdgpu_buffer_rsrc_t ss = rsrc(Spt, real ? (int)(nsup * 256 * kSup * 4) : 0);
+    const uint32_t spo = (uint32_t)(kBwd ? sp * 256 * kb2 : sp * 128);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 16), 16,
+                                               wv[i & 1] + (uint32_t)(i * 8 * kb2) + spo, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ss, (lds_ptr)(sdst + 64 * wave * kSup), 16,
+                                             (uint32_t)(wave * 1024 + lane * 16), (int)(sp * 256 * kSup * 4), 0, 0);
+  };
+  constexpr int kVmemW = 9;  // code-copy instructions per wave and super-step
+
+  // Codes and scales of step s live in set s % 2 (q4 = s % 4 within its
+  // super-step).  Forward: lane reads bytes 8g .. 8g+7 of its row's 32 bytes
+  // of the step (chunk 2q4 + g/2, half g%2) and one scale per row tile.
+  // Backward: lane (li, g) points at row 64q4 + 16g + li; the transposed read
+  // returns for lane (li, g) column o0+64w+16rt+li of rows 64q4+16g .. +15
+  // (chunk 2w + rt/2, half rt%2); the 16 row scales of block w are shared by
+  // the four row tiles.
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  u32x2_t wcr[2][4];
+  float sreg[2][kBwd ? 16 : 4];
+  const int crow = kBwd ? 16 * g + li : 64 * wave + li;  // + 64q4 (bwd) / + 16rt (fwd)
+  auto cread = [&](auto S, int half) {  // step with (step % 8) == S; row tiles 2half, 2half+1
+    constexpr int s8 = decltype(S)::value, q4 = s8 & 3, d = s8 & 1;
+    const uint8_t *wc = ((s8 >> 2) & 1) ? Wc1 : Wc0;
+#pragma unroll
+    for (int rt = 2 * half; rt < 2 * half + 2; ++rt) {
+      if constexpr (kBwd) {
+        const int off = (64 * q4 + crow) * 128 + (((2 * wave + (rt >> 1)) ^ (li >> 1)) << 4) + 8 * (rt & 1);
+        const auto v = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t *)(wc + off));
+        wcr[d][rt] = u32x2_t{(uint32_t)v[0], (uint32_t)v[1]};
+      } else {
+        const int off = (crow + 16 * rt) * 128 + (((2 * q4 + (g >> 1)) ^ (li >> 1)) << 4) + 8 * (g & 1);
+        wcr[d][rt] = *reinterpret_cast<const u32x2_t *>(wc + off);
+      }
+    }
+  };
+  // Backward scales: register chunk a (4 floats) of lane (li, g) holds rows
+  // 16g + 4(a ^ (g%2)) .. +3 -- the same half swap as the code bytes (tread).
+  auto sread = [&](auto S, int half) {
+    constexpr int s8 = decltype(S)::value, q4 = s8 & 3, d = s8 & 1;
+    const float *sc = ((s8 >> 2) & 1) ? Sc1 : Sc0;
+    if constexpr (kBwd) {
+#pragma unroll
+      for (int a = 2 * half; a < 2 * half + 2; ++a) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(sc + wave * 256 + 64 * q4 + 16 * g + 4 * (a ^ (g & 1)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sreg[d][4 * a + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int rt = 2 * half; rt < 2 * half + 2; ++rt) sreg[d][rt] = sc[(crow + 16 * rt) * kSup + q4];
+    }
+  };
+
+  u32x4_t a0[4], a1[2][4];  // A operands: sub-step 0; sub-step 1 by step parity
+  u32x4_t bq[2][4];         // B fragments of a pair, by pair parity
+  float2 pq[2][4];          // table reads of an expansion piece, by piece parity
+  // Lanes of odd g hold their B fragment halves swapped (see bfrag), so
+  // operand dword i takes code byte i ^ 2 there.
+  uint32_t bsh[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bsh[i] = (uint32_t)(8 * (i ^ (2 * (g & 1))));
+  // Table read i of piece p from code set d into pq[p % 2][i].
+  auto tread = [&](int d, int p, int i) {
+    const uint32_t word = wcr[d][p & 3][p < 4 ? 1 : 0];
+    pq[p & 1][i] = s_pair[__builtin_amdgcn_ubfe(word, bsh[i], 8)];
+  };
+  // Quarter i of piece p's arithmetic (scales of set d); operands for a step
+  // of parity e.
+  auto tmath = [&](int d, int e, int p, int i) {
+    const float2 v = pq[p & 1][i];
+    float sa, sb;
+    if constexpr (kBwd) {
+      const int t = p < 4 ? 1 : 0, base = 4 * (2 * t + (i >> 1)) + 2 * (i & 1);
+      sa = sreg[d][base];
+      sb = sreg[d][base + 1];
+    } else {
+      sa = sb = sreg[d][p & 3];
+    }
+    const uint32_t x = bf16x2_rne(__fmul_rn(v.x, sa), __fmul_rn(v.y, sb));
+    if (p < 4) a1[e][p & 3][i] = x;
+    else a0[p & 3][i] = x;
+  };
+  // B fragment (column tile ct, sub-step t) of lane (li, g): row 16ct + li,
+  // logical chunk 2g + t, read as two 8-byte halves, the first being half
+  // g % 2.  The row term 16ct*64 elements is an immediate.
+  uint32_t xb[2][2];  // [t][read] element offsets within a tile
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xb[t][i] = (uint32_t)(li * 64 + (((2 * g + t) ^ (li >> 1)) << 3) + 4 * (i ^ (g & 1)));
+  auto bfrag = [&](const uint16_t *bs, int P, int cc) -> u32x4_t {
+    const int t = P >> 2, ct = 4 * (P & 3) + cc;
+    const u32x2_t h0 = *reinterpret_cast<const u32x2_t *>(bs + xb[t][0] + 1024 * ct);
+    const u32x2_t h1 = *reinterpret_cast<const u32x2_t *>(bs + xb[t][1] + 1024 * ct);
+    return u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+  };
+
+  f32x4_t acc[4][16];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Prologue: B of step 0 and super-step 0's codes landed; B of step 1 and
+  // super-step 1's codes in flight (the copy slot before B(0)); step 0
+  // expanded; codes of step 1 in set 1; pair 0's fragments and piece 0's
+  // table reads issued.
+  __syncthreads();  // pair table
+  bload(0, std::integral_constant<int, 0>());
+  wload(0, std::integral_constant<int, 0>());
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  bload(1, std::integral_constant<int, 1>());
+  wload(1, std::integral_constant<int, 1>());
+  cread(std::integral_constant<int, 0>(), 0);
+  cread(std::integral_constant<int, 0>(), 1);
+  sread(std::integral_constant<int, 0>(), 0);
+  sread(std::integral_constant<int, 0>(), 1);
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tread(0, p, i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmath(0, 0, p, i);
+  }
+  cread(std::integral_constant<int, 1>(), 0);
+  cread(std::integral_constant<int, 1>(), 1);
+  sread(std::integral_constant<int, 1>(), 0);
+  sread(std::integral_constant<int, 1>(), 1);
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) bq[0][cc] = bfrag(Bs0, 0, cc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) tread(1, 0, i);
+
+  auto step = [&](int64_t kt, auto U) {
+    constexpr int u = decltype(U)::value, j = u & 3, e = u & 1;
+    const uint16_t *bs = e ? Bs1 : Bs0, *bn = e ? Bs0 : Bs1;
+    constexpr int dc = (u + 1) & 1;  // code set of step kt+1 (expanded now)
+#pragma unroll
+    for (int P = 0; P < 8; ++P) {
+      const int t = P >> 2, ct0 = 4 * (P & 3);
+      if (P == 7) {
+        // B(kt): the B tile of step kt+1 landed everywhere, every wave done
+        // reading Bs[kt % 2]; then refill it with step kt+2.
+        if constexpr (j == 0)
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kVmemW) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // (copies past the end read zeros; their data is never used)
+        bload(kt + 2, std::integral_constant<int, e>());
+        if constexpr (j == 3) wload((kt >> 2) + 2, std::integral_constant<int, (u >> 2) & 1>());
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int cc = s >> 2, rt = s & 3;
+        mfma16_acc(acc[rt][ct0 + cc], t ? a1[e][rt] : a0[rt], bq[P & 1][cc]);
+        if (s < 12) {
+          const int q = s / 3, kind = s % 3;
+          if (kind == 0) {  // B fragment q of the next pair
+            if (P < 7) bq[(P + 1) & 1][q] = bfrag(bs, P + 1, q);
+            else bq[0][q] = bfrag(bn, 0, q);
+          } else if (kind == 1) {  // table read q of the next piece
+            if (P < 7) tread(dc, P + 1, q);
+            else tread(e, 0, q);  // piece 0 of step kt+1's expansion: codes of kt+2
+          } else {
+            tmath(dc, e ^ 1, P, q);
+          }
+        } else if (P == 6) {  // codes and scales of step kt+2
+          if (s == 12) cread(std::integral_constant<int, (u + 2) & 7>(), 0);
+          if (s == 13) cread(std::integral_constant<int, (u + 2) & 7>(), 1);
+          if (s == 14) sread(std::integral_constant<int, (u + 2) & 7>(), 0);
+          if (s == 15) sread(std::integral_constant<int, (u + 2) & 7>(), 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  for (int64_t p = 0; p < nk8 / 8; ++p) {
+    step(8 * p, std::integral_constant<int, 0>());
+    step(8 * p + 1, std::integral_constant<int, 1>());
+    step(8 * p + 2, std::integral_constant<int, 2>());
+    step(8 * p + 3, std::integral_constant<int, 3>());
+    step(8 * p + 4, std::integral_constant<int, 4>());
+    step(8 * p + 5, std::integral_constant<int, 5>());
+    step(8 * p + 6, std::integral_constant<int, 6>());
+    step(8 * p + 7, std::integral_constant<int, 7>());
+  }
+  mfma_acc_fence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  lora_and_store(acc, Bs0, L, lda, RP, R, out, NO, M, o0 + 64 * wave, m0);
+}
+
+}  // namespace
+
+size_t tile_scales_bytes(int64_t n, int64_t k) {
+  const size_t f = (size_t)ceil_div(n, TO) * fwd_nsup(k) * 256 * kSup;
+  const size_t b = (size_t)ceil_div(k, TO) * bwd_nsup(n) * 256 * kSup;
+  return std::max(f, b) * sizeof(float);
+}
+
+bool bwd_tiles_supported(int64_t n, int64_t k) { return n % 64 == 0 && n * (k / 2) < (int64_t(1) << 31); }
+
+hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, int64_t M, const uint16_t *Bl, int r,
+                            int RP, const uint16_t *sH, uint16_t *Y, hipStream_t s) {
+  const int64_t nsup = fwd_nsup(w.k);
+  const int tiles_o = (int)ceil_div(w.n, TO), tiles_m = (int)ceil_div(M, TM);
+  const int64_t total = (int64_t)tiles_o * nsup * 256;
+  QLORA_LAUNCH("k_scales_fwd", k_scales_fwd, dim3((unsigned)(total / 256)), dim3(256), 0, s, w, nsup, total, scales);
+  QLORA_LAUNCH("k_fwd_nf4", k_nf4_tile<false>, dim3((unsigned)(tiles_o * tiles_m)), dim3(256), 0, s, w, scales, X,
+               M, Bl, r, RP, sH, Y, tiles_o);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
+                               int RP, const uint16_t *Gb, uint16_t *dX, hipStream_t s) {
+  const int64_t nsup = bwd_nsup(w.n);
+  const int tiles_o = (int)ceil_div(w.k, TO), tiles_m = (int)ceil_div(M, TM);
+  const int64_t total = (int64_t)tiles_o * nsup * 1024;
+  QLORA_LAUNCH("k_scales_bwd", k_scales_bwd, dim3((unsigned)(total / 256)), dim3(256), 0, s, w, nsup, total, scales);
+  QLORA_LAUNCH("k_bwd_dx_nf4", k_nf4_tile<true>, dim3((unsigned)(tiles_o * tiles_m)), dim3(256), 0, s, w, scales,
+               dY, M, At, RP, RP, Gb, dX, tiles_o);
+  return hipGetLastError();
+}
+
+}  // namespace qlora
