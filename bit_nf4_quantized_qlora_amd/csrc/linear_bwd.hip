@@ -221,9 +221,9 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     }
     QLORA_TRY(hipGetLastError());
   }
-  QLORA_TRY(launch_tn_splitk(dY, M, N, sHt, l.Mp, RP, l.sp_b, part, s));
+  QLORA_TRY(launch_tn_splitk(dY, M, N, sHt, l.Mp, RP, l.sp_b, true, part, s));
   QLORA_TRY(launch_reduce_cols(part, l.sp_b.splits, N, RP, r, true, dB, s));
-  QLORA_TRY(launch_tn_splitk(X, M, K, Gt, l.Mp, RP, l.sp_a, part, s));
+  QLORA_TRY(launch_tn_splitk(X, M, K, Gt, l.Mp, RP, l.sp_a, false, part, s));
   QLORA_TRY(launch_reduce_cols(part, l.sp_a.splits, K, RP, r, false, dA, s));
 #undef QLORA_TRY
   return hipSuccess;

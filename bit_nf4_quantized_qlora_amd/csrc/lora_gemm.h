@@ -59,11 +59,13 @@ SplitPlan plan_split(int64_t tiles, int64_t steps);
 
 hipError_t launch_nt_splitk(const uint16_t *P, int64_t rowsP, const uint16_t *Q, int rowsQ, int RP, int64_t lenC,
                             int64_t ld, const SplitPlan &sp, float *part, hipStream_t s);
+// rows_out: partials as [S][D][RP] (reduced with rows_out into [D][r]);
+// otherwise [S][RP][D].
 hipError_t launch_tn_splitk(const uint16_t *P, int64_t M, int64_t D, const uint16_t *Qt, int64_t ldq, int RP,
-                            const SplitPlan &sp, float *part, hipStream_t s);
+                            const SplitPlan &sp, bool rows_out, float *part, hipStream_t s);
 hipError_t launch_reduce_rows(const float *part, int S, int64_t R, int RP, int r, float scale, float *out_f32,
                               uint16_t *out_b, uint16_t *out_bt, int64_t ldt, hipStream_t s);
-hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool transpose, uint16_t *out,
+hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool rows_out, uint16_t *out,
                               hipStream_t s);
 hipError_t launch_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
                                 int64_t ldo, hipStream_t s);

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void k_nt_splitk(const uint16_t *__restrict__ 
 template <int TJ>
 __global__ __launch_bounds__(256) void k_tn_splitk(const uint16_t *__restrict__ P, int64_t M, int64_t D,
                                                    bool vec_ok, const uint16_t *__restrict__ Qt, int64_t ldq,
-                                                   int steps_per_split, float *__restrict__ part) {
+                                                   int steps_per_split, bool rows_out, float *__restrict__ part) {
   constexpr int RP = 16 * TJ;
   __shared__ __align__(16) uint16_t Ps[64 * LD];  // [i][m]
   __shared__ __align__(16) uint16_t Qs[RP * LD];  // [j][m]
@@ -107,12 +107,210 @@ __global__ __launch_bounds__(256) void k_tn_splitk(const uint16_t *__restrict__ 
   for (int t = 0; t < TJ; ++t) {
     const int j = 16 * t + (lane & 15);
     const int64_t i = i0 + wave * 16 + 4 * (lane >> 4);
-    if (i + 4 <= D && (D & 3) == 0) {
+    if (rows_out) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (i + v < D) out[(i + v) * RP + j] = acc[0][t][v];
+    } else if (i + 4 <= D && (D & 3) == 0) {
       *reinterpret_cast<f32x4_t *>(out + j * D + i) = acc[0][t];
     } else {
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (i + v < D) out[j * D + i + v] = acc[0][t][v];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// DMA-pipelined forms (row strides % 8 == 0).  Operand tiles stream global ->
+// LDS by buffer loads that write LDS directly, four steps in flight (buffers
+// b0..b3, one per step mod 4; separate arrays so the compiler sees that an
+// in-flight copy never aliases the tile being read).  A 64-wide tile row is
+// 128 B with its 16-byte chunk c at chunk c ^ ((row >> 1) & 7) (conflict-free
+// MFMA fragment reads with 64 LDS banks); wave-instruction i of a copy fills
+// rows 8i .. 8i+7, lane l taking row 8i + l/8 and physical chunk l & 7, so
+// the logical chunk it copies depends on the parity of i.  Columns past the
+// contraction length and rows past the operand are steered out of the buffer
+// range (per-lane offset), so they read zero; steps past a split's end use
+// zero-length resources.  The step count per split is a multiple of 4.
+
+constexpr uint32_t kOOB = 0x80000000u;  // a per-lane offset past every buffer range
+
+__device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 1) & 7); }
+
+// One copy of a [rows][64] bf16 tile (rows = 8 * ninstr per wave... see caller).
+// base: operand origin; nrows/ncols: its extent; ld: row stride (elements);
+// row0/col0: tile origin; dst: LDS tile; first: first tile row this wave copies.
+template <int NI>
+__device__ __forceinline__ void dma_tile(const uint16_t *base, int64_t nrows, int64_t ncols, int64_t ld, int64_t row0,
+                                         int64_t col0, bool live, uint16_t *dst, int first, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = rsrc(base, live ? nrows * ld * 2 : 0);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = first + 8 * i + (lane >> 3);
+    const int lc = swz_chunk(row, lane & 7);  // logical chunk this lane copies
+    const int64_t gr = row0 + row, gc = col0 + 8 * lc;
+    const uint32_t off = (gr < nrows && gc < ncols) ? (uint32_t)((gr * ld + gc) * 2) : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (first + 8 * i) * 64), 16, off, 0, 0, 0);
+  }
+}
+
+// part[s][i][j] = sum over split s of P[i][c] Q[j][c]: 64 rows of P per
+// workgroup (16 per wave), all RP rows of Q.
+template <int TJ>
+__global__ __launch_bounds__(256) void k_nt_dma(const uint16_t *__restrict__ P, int64_t rowsP,
+                                                const uint16_t *__restrict__ Q, int rowsQ, int64_t lenC, int64_t ld,
+                                                int steps_per_split, float *__restrict__ part) {
+  constexpr int RP = 16 * TJ, NQ = RP / 32, NV = 2 + NQ;  // copy instructions per wave and step
+  __shared__ __align__(16) uint16_t P0[64 * 64], P1[64 * 64], P2[64 * 64], P3[64 * 64];
+  __shared__ __align__(16) uint16_t Q0[RP * 64], Q1[RP * 64], Q2[RP * 64], Q3[RP * 64];
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t i0 = (int64_t)blockIdx.x * 64;
+  const int64_t nsteps = ceil_div_d(lenC, 64);
+  const int64_t s0 = (int64_t)blockIdx.y * steps_per_split;
+  const int64_t s1 = min<int64_t>(nsteps, s0 + steps_per_split);
+  auto pbuf = [&](auto B) -> uint16_t * {
+    constexpr int b = decltype(B)::value & 3;
+    return b == 0 ? P0 : b == 1 ? P1 : b == 2 ? P2 : P3;
+  };
+  auto qbuf = [&](auto B) -> uint16_t * {
+    constexpr int b = decltype(B)::value & 3;
+    return b == 0 ? Q0 : b == 1 ? Q1 : b == 2 ? Q2 : Q3;
+  };
+  auto copy = [&](int64_t st, auto B) {
+    const bool live = st < s1;
+    dma_tile<2>(P, rowsP, lenC, ld, i0, st * 64, live, pbuf(B), 16 * wave, lane);
+    dma_tile<NQ>(Q, rowsQ, lenC, ld, 0, st * 64, live, qbuf(B), 8 * NQ * wave, lane);
+  };
+  f32x4_t acc[TJ];
+#pragma unroll
+  for (int t = 0; t < TJ; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  copy(s0, std::integral_constant<int, 0>());
+  copy(s0 + 1, std::integral_constant<int, 1>());
+  copy(s0 + 2, std::integral_constant<int, 2>());
+  auto step = [&](int64_t st, auto B) {
+    // this step's copies (three steps old) landed everywhere; every wave is
+    // done reading the buffer the next copy refills
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * NV) : "memory");
+    copy(st + 3, std::integral_constant<int, (decltype(B)::value + 3) & 3>());
+    const uint16_t *ps = pbuf(B), *qs = qbuf(B);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = 16 * wave + li, c = 4 * t + g;
+      const u32x4_t a = *reinterpret_cast<const u32x4_t *>(ps + row * 64 + swz_chunk(row, c) * 8);
+#pragma unroll
+      for (int jt = 0; jt < TJ; ++jt) {
+        const int qr = 16 * jt + li;
+        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(qs + qr * 64 + swz_chunk(qr, c) * 8);
+        acc[jt] = mfma16(a, b, acc[jt]);
+      }
+    }
+  };
+  for (int64_t st = s0; st < s1; st += 4) {
+    step(st, std::integral_constant<int, 0>());
+    step(st + 1, std::integral_constant<int, 1>());
+    step(st + 2, std::integral_constant<int, 2>());
+    step(st + 3, std::integral_constant<int, 3>());
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  float *out = part + (size_t)blockIdx.y * rowsP * RP;
+#pragma unroll
+  for (int jt = 0; jt < TJ; ++jt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + 16 * wave + 4 * g + v;
+      if (i < rowsP) out[i * RP + 16 * jt + li] = acc[jt][v];
+    }
+}
+
+// part = sum over split s of Qt[j][m] P[m][d]: 64 columns d per workgroup
+// (16 per wave), all RP rows j.  The P tile [64 m][64 d] is read into MFMA B
+// operands (contraction along m, down a column) by ds_read_b64_tr_b16: in a
+// 16-lane group, lane i receives element i & 3 of the 8 bytes addressed by
+// lanes 4q + i/4 (q = 0..3), so lanes addressing rows m + q, columns 4(j & 3)
+// hand lane i four consecutive m of column i; two reads give the fragment.
+// rows_out == true: part[s][d][j] (reduced into [D][r]); else part[s][j][d].
+template <int TJ>
+__global__ __launch_bounds__(256) void k_tn_dma(const uint16_t *__restrict__ P, int64_t M, int64_t D,
+                                                const uint16_t *__restrict__ Qt, int64_t ldq, int steps_per_split,
+                                                bool rows_out, float *__restrict__ part) {
+  constexpr int RP = 16 * TJ, NQ = RP / 32, NV = 2 + NQ;
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) uint16_t P0[64 * 64], P1[64 * 64], P2[64 * 64], P3[64 * 64];
+  __shared__ __align__(16) uint16_t Q0[RP * 64], Q1[RP * 64], Q2[RP * 64], Q3[RP * 64];
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t d0 = (int64_t)blockIdx.x * 64;
+  const int64_t nsteps = ceil_div_d(M, 64);
+  const int64_t s0 = (int64_t)blockIdx.y * steps_per_split;
+  const int64_t s1 = min<int64_t>(nsteps, s0 + steps_per_split);
+  auto pbuf = [&](auto B) -> uint16_t * {
+    constexpr int b = decltype(B)::value & 3;
+    return b == 0 ? P0 : b == 1 ? P1 : b == 2 ? P2 : P3;
+  };
+  auto qbuf = [&](auto B) -> uint16_t * {
+    constexpr int b = decltype(B)::value & 3;
+    return b == 0 ? Q0 : b == 1 ? Q1 : b == 2 ? Q2 : Q3;
+  };
+  auto copy = [&](int64_t st, auto B) {
+    const bool live = st < s1;
+    dma_tile<2>(P, M, D, D, st * 64, d0, live, pbuf(B), 16 * wave, lane);
+    dma_tile<NQ>(Qt, RP, ldq, ldq, 0, st * 64, live, qbuf(B), 8 * NQ * wave, lane);
+  };
+  f32x4_t acc[TJ];
+#pragma unroll
+  for (int t = 0; t < TJ; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // transposed-read address of lane (j = li, g) for sub-step t, half h:
+  // row 32t + 8g + 4h + j/4, columns 16*wave + 4(j & 3) .. +3
+  auto tr_off = [&](int t, int h) -> int {
+    const int row = 32 * t + 8 * g + 4 * h + (li >> 2), col = 16 * wave + 4 * (li & 3);
+    return row * 64 + swz_chunk(row, col >> 3) * 8 + (col & 7);
+  };
+
+  copy(s0, std::integral_constant<int, 0>());
+  copy(s0 + 1, std::integral_constant<int, 1>());
+  copy(s0 + 2, std::integral_constant<int, 2>());
+  auto step = [&](int64_t st, auto B) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * NV) : "memory");
+    copy(st + 3, std::integral_constant<int, (decltype(B)::value + 3) & 3>());
+    const uint16_t *ps = pbuf(B), *qs = qbuf(B);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t *)(ps + tr_off(t, 0)));
+      const s16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t *)(ps + tr_off(t, 1)));
+      const u32x4_t b = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int jt = 0; jt < TJ; ++jt) {
+        const int qr = 16 * jt + li, c = 4 * t + g;
+        const u32x4_t a = *reinterpret_cast<const u32x4_t *>(qs + qr * 64 + swz_chunk(qr, c) * 8);
+        acc[jt] = mfma16(a, b, acc[jt]);
+      }
+    }
+  };
+  for (int64_t st = s0; st < s1; st += 4) {
+    step(st, std::integral_constant<int, 0>());
+    step(st + 1, std::integral_constant<int, 1>());
+    step(st + 2, std::integral_constant<int, 2>());
+    step(st + 3, std::integral_constant<int, 3>());
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // acc[jt][v] = C[j = 16jt + 4g + v][d = d0 + 16*wave + li]
+  const int64_t d = d0 + 16 * wave + li;
+  if (d < D) {
+    if (rows_out) {
+      float *out = part + ((size_t)blockIdx.y * D + d) * RP;
+#pragma unroll
+      for (int jt = 0; jt < TJ; ++jt) *reinterpret_cast<f32x4_t *>(out + 16 * jt + 4 * g) = acc[jt];
+    } else {
+      float *out = part + (size_t)blockIdx.y * RP * D;
+#pragma unroll
+      for (int jt = 0; jt < TJ; ++jt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) out[(int64_t)(16 * jt + 4 * g + v) * D + d] = acc[jt][v];
     }
   }
 }
@@ -139,24 +337,22 @@ __global__ __launch_bounds__(256) void k_reduce_rows(const float *__restrict__ p
   if (out_bt) out_bt[(int64_t)j * ldt + i] = i < R ? f32_to_bf16_bits(scale * v) : (uint16_t)0;
 }
 
-// Columns form: part [S][RP][D] -> v = sum_s part[s][j][i];
-//   transpose == false: out [r][D] = bf16(v)   (dA)
-//   transpose == true:  out [D][r] = bf16(v)   (dB)
+// Transposed-product partials -> bf16, summed over splits in a fixed order:
+//   rows_out == false: part [S][RP][D] -> out [r][D]  (dA)
+//   rows_out == true:  part [S][D][RP] -> out [D][r]  (dB)
+// (consecutive threads read consecutive partials in both forms).
 __global__ __launch_bounds__(256) void k_reduce_cols(const float *__restrict__ part, int S, int64_t D, int RP,
-                                                     int r, bool transpose, uint16_t *__restrict__ out) {
+                                                     int r, bool rows_out, uint16_t *__restrict__ out) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)r * D) return;
-  int64_t i;
-  int j;
-  if (transpose) {
-    i = idx / r;
-    j = (int)(idx % r);
+  int64_t src;
+  if (rows_out) {
+    src = (idx / r) * RP + idx % r;
   } else {
-    j = (int)(idx / D);
-    i = idx % D;
+    src = idx;  // j * D + i, j < r
   }
   float v = 0.f;
-  for (int s = 0; s < S; ++s) v += part[(size_t)s * RP * D + (int64_t)j * D + i];
+  for (int s = 0; s < S; ++s) v += part[(size_t)s * RP * D + src];
   out[idx] = f32_to_bf16_bits(v);
 }
 
@@ -201,11 +397,12 @@ hipError_t dispatch_tj(int RP, F &&f) {
 int lora_rank_pad(int r) { return (r + 31) / 32 * 32; }
 
 SplitPlan plan_split(int64_t tiles, int64_t steps) {
-  // Aim for >= ~1024 workgroups (4 per CU) with >= 4 contraction steps each.
+  // Aim for ~512 workgroups (two per CU; each keeps four steps of copies in
+  // flight) with >= 8 contraction steps each, a multiple of 4.
   SplitPlan p;
-  int64_t want = tiles >= 1024 ? 1 : ceil_div(1024, tiles);
-  want = std::max<int64_t>(1, std::min<int64_t>(want, steps / 4 > 0 ? steps / 4 : 1));
-  p.steps_per_split = (int)ceil_div(steps, want);
+  int64_t want = tiles >= 512 ? 1 : ceil_div(512, tiles);
+  want = std::max<int64_t>(1, std::min<int64_t>(want, steps / 8 > 0 ? steps / 8 : 1));
+  p.steps_per_split = (int)(ceil_div(ceil_div(steps, want), 4) * 4);
   p.splits = (int)ceil_div(steps, p.steps_per_split);
   return p;
 }
@@ -215,19 +412,27 @@ hipError_t launch_nt_splitk(const uint16_t *P, int64_t rowsP, const uint16_t *Q,
   const dim3 grid((unsigned)ceil_div(rowsP, 64), (unsigned)sp.splits);
   const bool vec_ok = (ld % 8) == 0;
   return dispatch_tj(RP, [&](auto tj) {
-    QLORA_LAUNCH("k_nt_splitk", k_nt_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, rowsP, Q, rowsQ, lenC, ld,
-                       vec_ok, sp.steps_per_split, part);
+    if (vec_ok)
+      QLORA_LAUNCH("k_nt_dma", k_nt_dma<decltype(tj)::value>, grid, dim3(256), 0, s, P, rowsP, Q, rowsQ, lenC, ld,
+                   sp.steps_per_split, part);
+    else
+      QLORA_LAUNCH("k_nt_splitk", k_nt_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, rowsP, Q, rowsQ, lenC,
+                   ld, vec_ok, sp.steps_per_split, part);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_tn_splitk(const uint16_t *P, int64_t M, int64_t D, const uint16_t *Qt, int64_t ldq, int RP,
-                            const SplitPlan &sp, float *part, hipStream_t s) {
+                            const SplitPlan &sp, bool rows_out, float *part, hipStream_t s) {
   const dim3 grid((unsigned)ceil_div(D, 64), (unsigned)sp.splits);
   const bool vec_ok = (D % 8) == 0;
   return dispatch_tj(RP, [&](auto tj) {
-    QLORA_LAUNCH("k_tn_splitk", k_tn_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, M, D, vec_ok, Qt, ldq,
-                       sp.steps_per_split, part);
+    if (vec_ok && ldq % 8 == 0)
+      QLORA_LAUNCH("k_tn_dma", k_tn_dma<decltype(tj)::value>, grid, dim3(256), 0, s, P, M, D, Qt, ldq,
+                   sp.steps_per_split, rows_out, part);
+    else
+      QLORA_LAUNCH("k_tn_splitk", k_tn_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, M, D, vec_ok, Qt, ldq,
+                   sp.steps_per_split, rows_out, part);
     return hipGetLastError();
   });
 }
@@ -240,10 +445,10 @@ hipError_t launch_reduce_rows(const float *part, int S, int64_t R, int RP, int r
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool transpose, uint16_t *out,
+hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool rows_out, uint16_t *out,
                               hipStream_t s) {
   QLORA_LAUNCH("k_reduce_cols", k_reduce_cols, dim3((unsigned)ceil_div((int64_t)r * D, 256)), dim3(256), 0, s, part, S, D,
-                     RP, r, transpose, out);
+                     RP, r, rows_out, out);
   return hipGetLastError();
 }
 
