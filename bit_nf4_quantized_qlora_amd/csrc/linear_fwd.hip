@@ -9,7 +9,8 @@
 //   2. k_scales_fwd + k_fwd_nf4 (nf4_tile.hip): Y = X W_hat^T + sH B^T on
 //      256x256 tiles, the NF4 codes expanded in registers straight into MFMA
 //      operands and the LoRA up-projection added on the same accumulators;
-//      Y is rounded to bf16 once.
+//      Y is rounded to bf16 once.  For M <= 16, k_gemv_nf4 (nf4_gemv.hip)
+//      instead: one bandwidth-bound pass over the packed weight.
 #include "nf4_tile.h"
 
 namespace qlora {
@@ -49,6 +50,7 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   if (e != hipSuccess) return e;
   e = launch_reduce_rows(part, l.sp.splits, M, l.RP, a.r, a.s, H_out, sH, nullptr, 0, s);
   if (e != hipSuccess) return e;
+  if (M <= kGemvMaxM) return launch_fwd_gemv(a.w, X, M, B, a.r, l.RP, sH, Y, s);
   return launch_fwd_tiles(a.w, scales, X, M, B, a.r, l.RP, sH, Y, s);
 }
 

@@ -25,4 +25,10 @@ hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, 
 hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
                                int RP, const uint16_t *Gb, uint16_t *dX, hipStream_t s);
 
+// Small-M forward (nf4_gemv.hip): the same Y for M <= kGemvMaxM, one pass
+// over the packed weight with the K split inside each workgroup.
+constexpr int64_t kGemvMaxM = 16;
+hipError_t launch_fwd_gemv(const Nf4View &w, const uint16_t *X, int64_t M, const uint16_t *Bl, int r, int RP,
+                           const uint16_t *sH, uint16_t *Y, hipStream_t s);
+
 }  // namespace qlora
