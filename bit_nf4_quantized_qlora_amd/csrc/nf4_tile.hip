@@ -51,11 +51,13 @@
 //
 // Barrier B(kt) sits between pairs 6 and 7 of step kt: it waits for the B
 // tile of step kt+1 (so pair 7 can already read the next step's first
-// fragments) and for this wave's reads of Bs[kt % 2]; right after it the B
-// tile of step kt+2 is copied into Bs[kt % 2], and when kt % 4 == 3 the codes
-// and scales of super-step kt/4 + 2 into the code buffers of the current
-// super-step, whose last register read was two steps earlier.  A code copy
-// lands by B(kt+2) and is first read in pair 6 of step kt+3.  The loop is
+// fragments) and for this wave's reads of Bs[kt % 2]; in pair 7, right after
+// it, the B tile of step kt+2 is copied into Bs[kt % 2].  When kt % 4 == 0,
+// pairs 0-2 copy the codes and scales of super-step kt/4 + 1 into the set of
+// super-step kt/4 - 1, whose last register read was in step kt-3; that copy
+// lands by B(kt+1) and is first read in pair 6 of step kt+2.  Copies go one
+// per MFMA slot: issued back to back, the four waves' copies queue in the
+// address unit and stall every wave's instruction stream.  The loop is
 // unrolled by 8 steps so every buffer choice is a compile-time constant; the
 // step count is rounded up to a multiple of 8, and steps past the end copy
 // zeros for B (zero-length buffer resource) and have zero scales, so they add
@@ -208,13 +210,12 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
 #pragma unroll
   for (int par = 0; par < 2; ++par)
     bv[par] = (uint32_t)(((64 * wave + (lane >> 3)) * NC + 8 * ((lane & 7) ^ (4 * par + (lane >> 4)))) * 2);
-  auto bload = [&](int64_t kt, auto D) {
+  // Instruction i (0..7) of the B-tile copy of step kt.
+  auto bload = [&](int64_t kt, auto D, int i) {
     uint16_t *dst = decltype(D)::value ? Bs1 : Bs0;
     const __amdgpu_buffer_rsrc_t rs = rsrc(Bact + m0 * NC, kt < nk ? bbytes : 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
-                                               bv[i & 1] + (uint32_t)(i * 16 * NC), (int)(kt * 128), 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
+                                             bv[i & 1] + (uint32_t)(i * 16 * NC), (int)(kt * 128), 0, 0);
   };
   // Code tile of a super-step: 256 rows x 128 B, same copy pattern and
   // swizzle.  Forward: row r = weight row o0 + r, bytes 128sp .. (4 steps of
@@ -229,19 +230,22 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
     wv[par] = (uint32_t)((64 * wave + (lane >> 3)) * kb2 + (kBwd ? o0 / 2 : 0) +
                          16 * ((lane & 7) ^ (4 * par + (lane >> 4))));
   const float *Spt = Sp + (int64_t)to * nsup * 256 * kSup;
-  auto wload = [&](int64_t sp, auto D) {
-    uint8_t *dst = decltype(D)::value ? Wc1 : Wc0;
-    float *sdst = decltype(D)::value ? Sc1 : Sc0;
+  // Instruction i (0..8) of the code and scale copy of super-step sp: eight
+  // for the codes, the last for the scales.
+  auto wload = [&](int64_t sp, auto D, int i) {
     const bool real = sp < nsup;
-    const __amdgpu_buffer_rsrc_t rs = rsrc(wbase_g, real ? wbytes : 0);
-    const __amdgpu_buffer_rsrc_t ss = rsrc(Spt, real ? (int)(nsup * 256 * kSup * 4) : 0);
-    const uint32_t spo = (uint32_t)(kBwd ? sp * 256 * kb2 : sp * 128);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
+    if (i < 8) {
+      uint8_t *dst = decltype(D)::value ? Wc1 : Wc0;
+      const __amdgpu_buffer_rsrc_t rs = rsrc(wbase_g, real ? wbytes : 0);
+      const uint32_t spo = (uint32_t)(kBwd ? sp * 256 * kb2 : sp * 128);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 16), 16,
                                                wv[i & 1] + (uint32_t)(i * 8 * kb2) + spo, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ss, (lds_ptr)(sdst + 64 * wave * kSup), 16,
-                                             (uint32_t)(wave * 1024 + lane * 16), (int)(sp * 256 * kSup * 4), 0, 0);
+    } else {
+      float *sdst = decltype(D)::value ? Sc1 : Sc0;
+      const __amdgpu_buffer_rsrc_t ss = rsrc(Spt, real ? (int)(nsup * 256 * kSup * 4) : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ss, (lds_ptr)(sdst + 64 * wave * kSup), 16,
+                                               (uint32_t)(wave * 1024 + lane * 16), (int)(sp * 256 * kSup * 4), 0, 0);
+    }
   };
   constexpr int kVmemW = 9;  // code-copy instructions per wave and super-step
 
@@ -340,17 +344,19 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
 #pragma unroll
     for (int ct = 0; ct < 16; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Prologue: B of step 0 and super-step 0's codes landed; B of step 1 and
-  // super-step 1's codes in flight (the copy slot before B(0)); step 0
+  // Prologue: B of step 0 and super-step 0's codes landed; B of step 1 in
+  // flight (super-step 1's codes follow in step 0's pairs 0-2); step 0
   // expanded; codes of step 1 in set 1; pair 0's fragments and piece 0's
   // table reads issued.
   __syncthreads();  // pair table
-  bload(0, std::integral_constant<int, 0>());
-  wload(0, std::integral_constant<int, 0>());
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bload(0, std::integral_constant<int, 0>(), i);
+#pragma unroll
+  for (int i = 0; i < kVmemW; ++i) wload(0, std::integral_constant<int, 0>(), i);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  bload(1, std::integral_constant<int, 1>());
-  wload(1, std::integral_constant<int, 1>());
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bload(1, std::integral_constant<int, 1>(), i);
   cread(std::integral_constant<int, 0>(), 0);
   cread(std::integral_constant<int, 0>(), 1);
   sread(std::integral_constant<int, 0>(), 0);
@@ -385,15 +391,21 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
           asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kVmemW) : "memory");
         else
           asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // (copies past the end read zeros; their data is never used)
-        bload(kt + 2, std::integral_constant<int, e>());
-        if constexpr (j == 3) wload((kt >> 2) + 2, std::integral_constant<int, (u >> 2) & 1>());
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int cc = s >> 2, rt = s & 3;
         mfma16_acc(acc[rt][ct0 + cc], t ? a1[e][rt] : a0[rt], bq[P & 1][cc]);
+        // Copies, one per slot, never in a burst (copies past the end read
+        // zeros; their data is never used): in pair 7, after B(kt), the B
+        // tile of step kt+2 into Bs[kt % 2]; when kt % 4 == 0, in pairs 0-2,
+        // the codes and scales of super-step kt/4 + 1 into set (kt/4 + 1) % 2.
+        if (P == 7 && (s & 1) == 0) bload(kt + 2, std::integral_constant<int, e>(), s >> 1);
+        if constexpr (j == 0) {
+          if (P < 3 && s % 5 == 0 && 4 * P + s / 5 < kVmemW)
+            wload((kt >> 2) + 1, std::integral_constant<int, ((u >> 2) + 1) & 1>(), 4 * P + s / 5);
+        }
         if (s < 12) {
           const int q = s / 3, kind = s % 3;
           if (kind == 0) {  // B fragment q of the next pair
