@@ -116,63 +116,50 @@ __global__ __launch_bounds__(256) void k_scales_bwd(Nf4View w, int64_t nsup, int
   Sp[t] = v;
 }
 
-// Tail after the main loop has drained (every copy landed, all waves past a
-// barrier): the LoRA term in 64-wide chunks of the padded rank -- the same
-// fragment layout with A = rows of L (direct loads, row stride lda) and the R
-// tile staged in LDS (stage: 32 KB, classic xsw swizzle) -- then out.
-// acc[rt][ct][v] = C[o][m] with o = ow + 16rt + 4g + v and m = m0 + 16ct + li
-// (four consecutive o of one output row).
-__device__ __forceinline__ void lora_and_store(f32x4_t (&acc)[4][16], uint16_t *stage,
-                                               const uint16_t *__restrict__ L, int lda, int RP,
-                                               const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
-                                               int64_t NO, int64_t M, int64_t ow, int64_t m0) {
-  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
-  const bool lvec = (lda % 8) == 0;
-  for (int jc = 0; jc < RP; jc += 64) {
+// Output through LDS, once the main loop has drained (every copy landed,
+// all waves past a barrier).  acc[rt][ct][v] = C[o][m] with o = ow + 16rt +
+// 4g + v and m = m0 + 16ct + li.  Each wave writes its 64 o x 256 m block as
+// bf16 into the four free 32 KB buffers (buffer q: tile rows m 64q .. +63, 512
+// B per row, 16-byte chunk c of row r at c ^ (r & 15), so the 16 rows of one
+// write land in distinct banks); then wave w stores tile rows 64w .. +63, two
+// full 512-byte rows per instruction.
+__device__ __forceinline__ void store_tile(const f32x4_t (&acc)[4][16], uint8_t *const (&buf)[4],
+                                           uint16_t *__restrict__ out, int64_t NO, int64_t M, int64_t o0,
+                                           int64_t m0, int wave) {
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i;
-      *reinterpret_cast<u32x4_t *>(&stage[xsw(c >> 3, c & 7)]) =
-          load8(R, RP, M, RP, m0 + (c >> 3), jc + 8 * (c & 7), true);
+  for (int ct = 0; ct < 16; ++ct)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const f32x4_t v = acc[rt][ct];
+      const int c = 8 * wave + 2 * rt + (g >> 1);
+      *reinterpret_cast<u32x2_t *>(buf[ct >> 2] + (16 * (ct & 3) + li) * 512 + ((c ^ li) << 4) + 8 * (g & 1)) =
+          u32x2_t{bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
     }
-    u32x4_t a[4][2];
+  __syncthreads();
+  const uint8_t *src = buf[0];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+  for (int q = 1; q < 4; ++q)
+    if (wave == q) src = buf[q];
+  const bool ovec = (NO & 7) == 0;
+  const int c = lane & 31;
+  const int64_t o = o0 + 8 * c;
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    const int r = 2 * i + (lane >> 5);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(src + r * 512 + ((c ^ (r & 15)) << 4));
+    const int64_t m = m0 + 64 * wave + r;
+    if (m < M && o < NO) {
+      uint16_t *dst = out + m * NO + o;
+      if (ovec) {
+        *reinterpret_cast<u32x4_t *>(dst) = v;
+      } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) a[rt][t] = load8(L, lda, NO, lda, ow + 16 * rt + li, jc + 16 * g + 8 * t, lvec);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ct = 0; ct < 16; ++ct) {
-        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(&stage[xsw(16 * ct + li, 2 * g + t)]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct], a[rt][t], b);
+        for (int e = 0; e < 8; ++e)
+          if (o + e < NO) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
       }
-    __syncthreads();
+    }
   }
-  mfma_acc_fence();
-
-  const bool ovec = (NO & 3) == 0;
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < 16; ++ct) {
-      const int64_t o = ow + 16 * rt + 4 * g;
-      const int64_t m = m0 + 16 * ct + li;
-      if (m < M) {
-        const f32x4_t v = acc[rt][ct];
-        uint16_t *dst = out + m * NO + o;
-        if (ovec && o + 4 <= NO) {
-          *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (o + e < NO) dst[e] = f32_to_bf16_bits(v[e]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
 }
 
 template <bool kBwd>
@@ -353,6 +340,53 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   for (int i = 0; i < 8; ++i) bload(0, std::integral_constant<int, 0>(), i);
 #pragma unroll
   for (int i = 0; i < kVmemW; ++i) wload(0, std::integral_constant<int, 0>(), i);
+
+  // The LoRA term first, while those copies are in flight: C += L R^T over
+  // the padded rank in 64-wide chunks, each chunk of R (rows m0 .. +255,
+  // row stride RP; columns past RP and rows past M read zero) copied into
+  // Wc1 -- idle until step 0 copies super-step 1 -- with the B-tile layout,
+  // and the matching L operands (rows o, row stride lda) loaded straight
+  // into registers.
+  {
+    const __amdgpu_buffer_rsrc_t rr = rsrc(R + m0 * RP, min<int64_t>(TM, M - m0) * RP * 2);
+    uint16_t *rtile = reinterpret_cast<uint16_t *>(Wc1);
+    const bool lvec = (lda % 8) == 0;
+    for (int jc = 0; jc < RP; jc += 64) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = 64 * wave + 8 * i + (lane >> 3);
+        const int col = jc + 8 * ((lane & 7) ^ (4 * (i & 1) + (lane >> 4)));
+        const uint32_t off = col < RP ? (uint32_t)((row * RP + col) * 2) : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr)(rtile + (512 * wave + 64 * i) * 8), 16, off, 0, 0, 0);
+      }
+      // bfrag hands odd-g lanes their two 8-byte halves swapped; swap the
+      // L operand the same way so products pair up.
+      u32x4_t la[4][2];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4_t v = load8(L, lda, NO, lda, o0 + 64 * wave + 16 * rt + li, jc + 16 * g + 8 * t, lvec);
+          la[rt][t] = (g & 1) ? u32x4_t{v[2], v[3], v[0], v[1]} : v;
+        }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      // The MFMAs are inline asm, so the compiler does not pad the gap after
+      // the VALU writes of the swap: keep those writes above this point and
+      // add the wait states a VALU-written MFMA source needs.
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_nop 4" ::: "memory");
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ct = 0; ct < 16; ++ct) {
+          const u32x4_t b = bfrag(rtile, 4 * t + (ct >> 2), ct & 3);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) mfma16_acc(acc[rt][ct], la[rt][t], b);
+        }
+      __syncthreads();
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 #pragma unroll
@@ -427,6 +461,9 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
       }
     }
   };
+  // (inside the loop every MFMA source is written at least a pair ahead)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 4" ::: "memory");
   for (int64_t p = 0; p < nk8 / 8; ++p) {
     step(8 * p, std::integral_constant<int, 0>());
     step(8 * p + 1, std::integral_constant<int, 1>());
@@ -440,7 +477,8 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   mfma_acc_fence();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  lora_and_store(acc, Bs0, L, lda, RP, R, out, NO, M, o0 + 64 * wave, m0);
+  uint8_t *const bufs[4] = {reinterpret_cast<uint8_t *>(Bs0), reinterpret_cast<uint8_t *>(Bs1), Wc0, Wc1};
+  store_tile(acc, bufs, out, NO, M, o0, m0, wave);
 }
 
 }  // namespace
