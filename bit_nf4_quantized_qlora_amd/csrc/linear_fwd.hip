@@ -9,8 +9,9 @@
 //   2. k_scales_fwd + k_fwd_nf4 (nf4_tile.hip): Y = X W_hat^T + sH B^T on
 //      256x256 tiles, the NF4 codes expanded in registers straight into MFMA
 //      operands and the LoRA up-projection added on the same accumulators;
-//      Y is rounded to bf16 once.  For M <= 16, k_gemv_nf4 (nf4_gemv.hip)
-//      instead: one bandwidth-bound pass over the packed weight.
+//      Y is rounded to bf16 once.
+// For 1 <= M <= 16 the whole forward is nf4_gemv.hip's instead (k_gemv_nf4,
+// k_gemv_finish): one bandwidth-bound pass over the packed weight.
 #include "nf4_tile.h"
 
 namespace qlora {
@@ -30,6 +31,7 @@ FwdWs fwd_ws_layout(int64_t M, int64_t n, int64_t k, int r) {
   l.sh_off = align_up((size_t)l.sp.splits * M * l.RP * sizeof(float), 256);
   l.scale_off = l.sh_off + align_up((size_t)M * l.RP * sizeof(uint16_t), 256);
   l.total = l.scale_off + align_up(tile_scales_bytes(n, k), 256);
+  if (small_m_supported(M, n, k, r)) l.total = std::max(l.total, small_m_workspace_bytes(M, n, k, r));
   return l;
 }
 
@@ -41,6 +43,7 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
                              uint16_t *Y, float *H_out, void *ws, hipStream_t s) {
   const int64_t M = a.M, N = a.w.n, K = a.w.k;
   if (M == 0) return hipSuccess;
+  if (small_m_supported(M, N, K, a.r)) return launch_fwd_small(a.w, X, M, A, B, a.r, a.s, Y, H_out, ws, s);
   const FwdWs l = fwd_ws_layout(M, N, K, a.r);
   char *base = static_cast<char *>(ws);
   float *part = reinterpret_cast<float *>(base + l.part_off);
@@ -50,7 +53,6 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   if (e != hipSuccess) return e;
   e = launch_reduce_rows(part, l.sp.splits, M, l.RP, a.r, a.s, H_out, sH, nullptr, 0, s);
   if (e != hipSuccess) return e;
-  if (M <= kGemvMaxM) return launch_fwd_gemv(a.w, X, M, B, a.r, l.RP, sH, Y, s);
   return launch_fwd_tiles(a.w, scales, X, M, B, a.r, l.RP, sH, Y, s);
 }
 

@@ -6,138 +6,407 @@
 // a matrix-vector product, so the cost is streaming the packed codes and the
 // two-level block constants (0.516 B per weight).
 //
-// k_gemv_nf4: one workgroup of eight waves per 64 weight rows; wave q takes
-// the q-th eighth of the 256-wide K chunks (4 blocks per row).  Lane (li, g)
-// of row tile rt (rows n0 + 16rt + li) owns block g of each chunk: it loads
-// the block's 32 bytes of codes (two 16-byte loads), its scale code and group
-// constant, and expands the 64 codes into eight BF16 MFMA A operands (256-entry
-// table of level pairs, exactly as the standalone dequantization does).  X
-// (M rows padded to 16 by out-of-range reads) is the B operand, read straight
-// from global/L2: lane (li, g) takes X[li][256c + 64g + 8t .. +7] for
-// sub-step t, the same k as its codes, and applies it to all four row tiles.
-// No register prefetch: at ~120 VGPRs two workgroups (16 waves) fit per CU
-// and every workgroup of a 65B-sized layer is resident at once.  The
-// level-pair table has 32 copies, copy c in bank pair c (entry e at
-// e*256 + 8c), so the 32 lanes of a half-wave never conflict on their random
-// lookups; the table reads of a sub-step are issued before the arithmetic of
-// the previous one.  The eight per-wave partial tiles are summed in LDS in
-// wave order (deterministic; the table's space is reused), the LoRA term
-// sum_j sH[m][j] B[n][j] is added in fp32, and Y is rounded to bf16 once.
+// Two launches:
+//   k_gemv_nf4    partial sums of Y = X W_hat^T per workgroup and row group,
+//                 and partial sums of H = X A^T over 512-wide K slices;
+//   k_gemv_finish Y = bf16(sum of the partials + bf16(s H) B^T), H (fp32,
+//                 the optional output).
+//
+// k_gemv_nf4 runs one 1024-thread workgroup per CU.  The weight rows are cut
+// into groups of 256 (16 row tiles of 16) and each row into 64-wide blocks;
+// the (group, block) pairs, taken group-major, are split into G equal
+// contiguous ranges, one per workgroup (stream-K), so every CU streams the
+// same number of bytes whatever the shape.  All 16 waves walk the
+// workgroup's range together, wave w on row tile w of the current group, and
+// write one partial per row group they touch.
+//
+// Per block the MFMA takes X as its A operand (rows m < M, the rest zero) and
+// the weights as its B operand (columns = the 16 rows of the tile); a lane's
+// four accumulators then belong to one weight row, whose block scale it
+// computes exactly as the standalone dequantization does (E4M3 decode from
+// a 256-entry LDS table, then the two separately rounded operations).  The
+// weights are bf16(fp32(q * s)), bit for bit the dequantized BF16 weights:
+// one LDS read of a level pair per packed byte from a 256-entry table with
+// 32 copies (entry e of copy c at byte 256e + 8c, copy = lane % 32, so no
+// half-wave read ever conflicts), addressed by a single byte permute of the
+// code byte and the lane's offset.  Lane (li, g) holds, for row li of the
+// tile, the 8 code bytes of contraction positions 16g .. 16g+15 of the block
+// (MFMA h takes 16g + 8h .. +7), fetched 8 blocks ahead; X is staged in LDS
+// for the whole range (row m's 16-byte chunk c at c ^ ((m >> 1) & 7)).
+//
+// H: workgroup t < nh takes rank tile t % (RP/16) and K slice t / (RP/16)
+// (512 wide, 32 per wave); its operands are loaded before anything else so
+// their latency hides under the table fill, one MFMA per wave, and the 16
+// wave results are summed in LDS after the main loop.  k_gemv_finish sums
+// the slices in order, adds the partial sums of each row group in workgroup
+// order and the LoRA term (bf16 operands, exact products, fp32 sum), and
+// rounds Y to bf16 once.
 #include "nf4_tile.h"
 
 namespace qlora {
 namespace {
 
-constexpr int GW = 8;  // waves per workgroup: K split eight ways
+constexpr int kGvWaves = 16;               // waves per workgroup = row tiles per group
+constexpr int kGvRows = 16 * kGvWaves;     // weight rows per row group
+constexpr int kLdsAll = 160 * 1024;        // LDS of one workgroup
+constexpr int kGvD = 8;                    // blocks of codes in flight per lane
+constexpr int kLdsTab = 256 * 256;         // level-pair table, 32 copies
+constexpr int kLdsDec = 256 * 4;           // E4M3 decode table
+constexpr int kLdsVar = kLdsAll - kLdsTab - kLdsDec - 128;  // group constants + staged X
+constexpr int kHSlice = 32 * kGvWaves;     // K per H slice: one 32-deep MFMA per wave
+constexpr int kMaxG = 4096;                // most workgroups
 
-__global__ __launch_bounds__(GW * 64) void k_gemv_nf4(Nf4View w, const uint16_t *__restrict__ X, int M,
-                                                      const uint16_t *__restrict__ Bl, int r, int RP,
-                                                      const uint16_t *__restrict__ sH, uint16_t *__restrict__ Y) {
-  __shared__ __align__(16) float2 s_tab[256 * 32];  // 64 KB; later the reduction buffer
-  f32x4_t(*red)[4][64] = reinterpret_cast<f32x4_t(*)[4][64]>(s_tab);  // [GW][4][64] = 32 KB
+struct GemvPlan {
+  int64_t nkb = 0, ngroups = 0, T = 0;  // blocks per row, row groups, (group, block) pairs
+  int G = 0;                            // workgroups
+  int seg = 1;                          // most row groups one workgroup touches
+  int nht = 0, nh = 0;                  // rank tiles of 16; H slices x rank tiles
+  int xoff = 0;                         // byte offset of the staged X in the variable area
+  int q4 = 1;                           // ranges start on multiples of q4 blocks (4 if nkb % 4 == 0)
+};
+
+GemvPlan gemv_plan(int64_t M, int64_t n, int64_t k, int RP) {
+  GemvPlan p;
+  p.nkb = k / kBlock;
+  p.ngroups = ceil_div(n, kGvRows);
+  p.T = p.ngroups * p.nkb;
+  p.nht = RP / 16;
+  p.nh = (int)(ceil_div(k, kHSlice) * p.nht);
+  // A row group's 256 x nkb blocks use exactly nkb group constants (one per
+  // 256 consecutive blocks, rows laid end to end); a workgroup stages those
+  // of the row groups its range touches, then its X columns.
+  p.q4 = 4;  // needs nkb % 4 == 0 (small_m_supported)
+  auto fit = [&](int64_t G) {
+    int64_t seg = 1, nbmax = 0;
+    for (int64_t i = 0; i < G; ++i) {
+      const int64_t b0 = p.q4 * (i * (p.T / p.q4) / G), b1 = p.q4 * ((i + 1) * (p.T / p.q4) / G);
+      if (b1 > b0) seg = std::max<int64_t>(seg, (b1 - 1) / p.nkb - b0 / p.nkb + 1);
+      nbmax = std::max<int64_t>(nbmax, b1 - b0);
+    }
+    p.seg = (int)seg;
+    p.xoff = (int)align_up((size_t)seg * p.nkb * 4, 16);
+    return p.xoff + nbmax * M * 128 <= kLdsVar;
+  };
+  // one workgroup per CU (more only if the staged X or the H slices need
+  // them), never more than there are blocks or H slices to take
+  int64_t G = std::max<int64_t>(std::min<int64_t>(256, p.T / p.q4), p.nh);
+  while (G < kMaxG && !fit(G)) G = std::min<int64_t>(G + 256, kMaxG);
+  p.G = fit(G) ? (int)G : kMaxG + 1;  // no fit: small_m_supported says no
+  return p;
+}
+
+struct SmallWs {
+  GemvPlan p;
+  size_t h_off, part_off, total;
+};
+
+SmallWs small_ws_layout(int64_t M, int64_t n, int64_t k, int RP) {
+  SmallWs l;
+  l.p = gemv_plan(M, n, k, RP);
+  l.h_off = 0;
+  l.part_off = align_up((size_t)(l.p.nh / l.p.nht) * M * RP * sizeof(float), 256);
+  l.total = l.part_off + (size_t)l.p.G * l.p.seg * M * kGvRows * sizeof(float);
+  return l;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t *__restrict__ X, int M,
+                                                      const uint16_t *__restrict__ A, int r, int RP,
+                                                      float *__restrict__ hpart, float *__restrict__ part,
+                                                      int64_t T, int G, int seg, int nh, int nht, int xoff_b) {
+  // LDS: level-pair table (64 KB, first so its reads need no base add),
+  // E4M3 decode table (1 KB), a zero row, then the group constants of the
+  // row groups the range touches and the staged X.
+  __shared__ __align__(16) uint8_t lds[kLdsAll];
+  float2 *s_tab = reinterpret_cast<float2 *>(lds);
+  float *s_dec = reinterpret_cast<float *>(lds + kLdsTab);
+  constexpr int kZeroOff = kLdsTab + kLdsDec, kGaOff = kZeroOff + 128;
+  float *s_ga = reinterpret_cast<float *>(lds + kGaOff);
+  const int xbase = kGaOff + xoff_b;
+  uint8_t *s_x = lds + xbase;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t N = w.n, K = w.k, nkb = K / kBlock, nch = ceil_div_d(nkb, 4);
-  const int64_t n0 = (int64_t)blockIdx.x * 64;
-  const int64_t cpw = ceil_div_d(nch, GW), c0 = min<int64_t>(nch, wave * cpw), c1 = min<int64_t>(nch, c0 + cpw);
-  for (int i = tid; i < 256 * 32; i += GW * 64) {
-    const int e = i >> 5;
-    s_tab[i] = make_float2(__uint_as_float(kNF4Bits[e & 15]), __uint_as_float(kNF4Bits[e >> 4]));
-  }
-  const uint32_t tab_lane = (uint32_t)(lane & 31) * 8;  // byte offset of this lane's copy
-  const char *tab = reinterpret_cast<const char *>(s_tab);
-  const float offset = *w.offset;
+  const int64_t N = w.n, K = w.k, nkb = K / kBlock, kb2 = K / 2;
+  const int wg = blockIdx.x;
+  const int64_t b0 = 4 * ((int64_t)wg * (T / 4) / G), b1 = 4 * ((int64_t)(wg + 1) * (T / 4) / G);
+  const int nb = (int)(b1 - b0);
 
-  // Buffer resources: rows past N and blocks past k/64 fall outside the
-  // ranges (per-lane offsets) and read zero; X rows past M likewise.
-  const int64_t nrows = min<int64_t>(64, N - n0);
-  const __amdgpu_buffer_rsrc_t crs = rsrc(w.packed + n0 * (K / 2), nrows * (K / 2));
-  const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code + n0 * nkb, nrows * nkb);
-  const __amdgpu_buffer_rsrc_t grs = rsrc(w.group_amax, w.ng * 4);
-  const __amdgpu_buffer_rsrc_t xrs = rsrc(X, (int64_t)M * K * 2);
+  // H slice operands first: X rows li < M and A rows 16 jt + li < r at
+  // k = 512 ks + 32 wave + 8g .. +7 (zero outside).
+  const bool hwork = wg < nh;
+  const int jt = wg % nht, ks = wg / nht;
+  u32x4_t hx = {0u, 0u, 0u, 0u}, ha = {0u, 0u, 0u, 0u};
+  {
+    const int64_t kh = (int64_t)ks * kHSlice + 32 * wave + 8 * g;
+    const int j = 16 * jt + li;
+    const bool kin = hwork && kh < K;
+    const __amdgpu_buffer_rsrc_t xr = rsrc(X, (int64_t)M * K * 2), ar = rsrc(A, (int64_t)r * K * 2);
+    hx = __builtin_amdgcn_raw_buffer_load_b128(xr, kin && li < M ? (uint32_t)((li * K + kh) * 2) : 0x80000000u, 0, 0);
+    ha = __builtin_amdgcn_raw_buffer_load_b128(ar, kin && j < r ? (uint32_t)((j * K + kh) * 2) : 0x80000000u, 0, 0);
+  }
+
+  // Level-pair table: entry e = {q[e & 15], q[e >> 4]} (low nibble = first
+  // weight), copy c at byte 256e + 8c.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = (tid >> 5) + 32 * i, c = tid & 31;
+    s_tab[e * 32 + c] = make_float2(__uint_as_float(kNF4Bits[e & 15]), __uint_as_float(kNF4Bits[e >> 4]));
+  }
+  if (tid < 256) s_dec[tid] = e4m3_decode((uint32_t)tid);
+  // X columns of the range: staged row R = i*M + m holds X[m][64 kb(i) ..
+  // +63], 16-byte chunk c at c ^ ((m >> 1) & 7); the 16 lanes of one read
+  // (m = 0..15 of one block) then hit 16 distinct bank groups for any M.
+  for (int c = tid; c < nb * M * 8; c += 1024) {
+    const int ch = c & 7, R = c >> 3, i = R / M, m = R - i * M;
+    const int64_t kb = (b0 + i) % nkb;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(X + (int64_t)m * K + kb * kBlock + 8 * ch);
+    *reinterpret_cast<u32x4_t *>(s_x + R * 128 + ((ch ^ ((m >> 1) & 7)) << 4)) = v;
+  }
+  if (tid < 8) *reinterpret_cast<u32x4_t *>(lds + kZeroOff + 16 * tid) = u32x4_t{0u, 0u, 0u, 0u};
+  // group constants of the touched row groups: s_ga[t] = group_amax[gfirst*nkb + t]
+  {
+    const int64_t gi0 = (b0 / nkb) * nkb, nga = (int64_t)seg * nkb;
+    for (int64_t t = tid; t < nga; t += 1024) s_ga[t] = gi0 + t < w.ng ? w.group_amax[gi0 + t] : 0.f;
+  }
+
+  // Per-lane streams (32-bit offsets): 8 code bytes of block kb of row n, the
+  // block's scale code and its group constant, 8 blocks ahead.  Rows past N
+  // read zero and give partial sums that are never used; loads past the
+  // workgroup's last block take an out-of-range offset (no memory traffic).
+  const __amdgpu_buffer_rsrc_t crs = rsrc(w.packed, N * kb2);
+  const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code, w.nb);
   constexpr uint32_t kOut = 0x80000000u;
-
-  f32x4_t acc[4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();  // pair table
-
-  for (int64_t c = c0; c < c1; ++c) {
-    const int64_t kb = 4 * c + g;
-    const bool bok = kb < nkb;
-    u32x4_t code[4][2];  // [rt][half]: codes 64g + 32h .. +31 of row 16rt + li
-    uint32_t sc[4];
-    float ga[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int row = 16 * rt + li;
-      const uint32_t co = bok ? (uint32_t)(row * (K / 2) + 128 * c + 32 * g) : kOut;
-      code[rt][0] = __builtin_amdgcn_raw_buffer_load_b128(crs, co, 0, 0);
-      code[rt][1] = __builtin_amdgcn_raw_buffer_load_b128(crs, co + 16, 0, 0);
-      sc[rt] = __builtin_amdgcn_raw_buffer_load_b8(srs, bok ? (uint32_t)(row * nkb + kb) : kOut, 0, 0);
-      ga[rt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             grs, (uint32_t)(((n0 + row) * nkb + kb) >> 8) * 4, 0, 0));
+  const float offset = *w.offset;
+  const int nrow = 16 * wave + li;  // row within the group
+  const int64_t gfirst = b0 / nkb;
+  int lkb = (int)(b0 - gfirst * nkb);
+  uint32_t lco = (uint32_t)((gfirst * kGvRows + nrow) * kb2 + lkb * 32 + 8 * g);
+  uint32_t lbi = (uint32_t)((gfirst * kGvRows + nrow) * nkb + lkb);
+  const uint32_t gstep_c = (uint32_t)(kGvRows * kb2 - nkb * 32), gstep_b = (uint32_t)(kGvRows * nkb - nkb);
+  u32x2_t cq[kGvD];
+  auto load = [&](int slot, bool real) {
+    cq[slot] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(crs, real ? lco : kOut, 0, 0));
+    lco += 32;
+    if (++lkb == nkb) {
+      lkb = 0;
+      lco += gstep_c;
     }
-    const uint32_t xo = (bok && li < M) ? (uint32_t)((li * K + 256 * c + 64 * g) * 2) : kOut;
-    u32x4_t xf[8];
+  };
+  // Scale codes four blocks per load (ranges and row groups start on
+  // multiples of 4 blocks, and nkb % 4 == 0): word w of the row's codes, all
+  // four lanes of a row reading the same word; two words in flight.
+  uint32_t scw[2];
+  int skb = lkb;
+  auto sload = [&](int slot, bool real) {
+    scw[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, real ? lbi : kOut, 0, 0);
+    lbi += 4;
+    if ((skb += 4) == nkb) {
+      skb = 0;
+      lbi += gstep_b;
+    }
+  };
+  sload(0, 0 < nb);
+  sload(1, 4 < nb);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) xf[t] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * t, 0, 0);
-    float s[4];
+  for (int j = 0; j < kGvD; ++j) load(j, j < nb);
+  __syncthreads();  // table and X staged
+
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  const f32x4_t hacc = mfma16(hx, ha, zero);  // C[m = 4g+v][j = 16 jt + li]
+
+  const char *tab = reinterpret_cast<const char *>(s_tab);
+  const uint32_t lane_off = (uint32_t)(lane & 31) * 8;
+  // X fragments of block i for MFMA h: chunk 2g + h of staged row i*M + li
+  // (lanes li >= M read the zero row, which takes no row step).
+  const bool xreal = li < M;
+  const int sw = (li >> 1) & 7;
+  const uint32_t xo0 = xreal ? (uint32_t)(xbase + li * 128 + (((2 * g) ^ sw) << 4)) : (uint32_t)kZeroOff;
+  const uint32_t xo1 = xreal ? (uint32_t)(xbase + li * 128 + (((2 * g + 1) ^ sw) << 4)) : (uint32_t)kZeroOff + 16;
+  const uint32_t xstep = xreal ? (uint32_t)M * 128 : 0u;
+  uint32_t xoff = 0;
+
+  // Block i: its LDS reads (decode entry, X fragments, level pairs), then
+  // the code load of block i + 8 into the freed ring slot, then scale,
+  // round and multiply; the four waves of a SIMD hide each other's LDS
+  // latency.  Blocks past the end (the loop runs whole rounds of 8) read
+  // zeros and the last real X row, and their sums are never stored.
+  // this lane's partial slots: [(wg*seg + seg_i) * M + m] * 256 + nrow
+  float *pbase = part + (int64_t)wg * seg * M * kGvRows + nrow;
+  int seg_i = 0;
+  int ckb = (int)(b0 - gfirst * nkb);
+  // block index n*nkb + kb of the block being computed; its group constant
+  // is s_ga[(cbi >> 8) - gfirst*nkb]
+  uint32_t cbi = (uint32_t)((gfirst * kGvRows + nrow) * nkb + ckb);
+  const uint32_t ga_base = (uint32_t)kGaOff - (uint32_t)(gfirst * nkb) * 4;
+  f32x4_t acc = zero;
+  for (int i0 = 0; i0 < nb; i0 += kGvD) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) s[rt] = block_scale(sc[rt], ga[rt], offset);
-    // Piece (t, rt): codes 64g + 8t .. +7 of row tile rt.  Its table reads
-    // are issued one piece ahead.
-    float2 pq[2][4];
-    auto look = [&](int p) {
-      const int t = p >> 2, rt = p & 3;
-      const uint32_t word = code[rt][t >> 2][t & 3];
+    for (int j = 0; j < kGvD; ++j) {
+      const int i = i0 + j;
+      const float sdj = s_dec[(scw[j >> 2] >> (8 * (j & 3))) & 0xFFu];
+      if ((j & 3) == 3) sload(j >> 2, i + 5 < nb);  // blocks i+5 .. i+8
+      const float gaj = *reinterpret_cast<const float *>(lds + ga_base + ((cbi >> 8) << 2));
+      const u32x4_t xa0 = *reinterpret_cast<const u32x4_t *>(lds + xo0 + xoff);
+      const u32x4_t xa1 = *reinterpret_cast<const u32x4_t *>(lds + xo1 + xoff);
+      if (i + 1 < nb) xoff += xstep;
+      const u32x2_t cw = cq[j];
+      float2 lv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pq[p & 1][i] = *reinterpret_cast<const float2 *>(tab + ((__builtin_amdgcn_ubfe(word, 8 * i, 8) << 8) | tab_lane));
-    };
-    look(0);
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int p = 0; p < 32; ++p) {
-      const int t = p >> 2, rt = p & 3;
-      if (p + 1 < 32) look(p + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      u32x4_t a;
+        for (int q = 0; q < 4; ++q)
+          lv[4 * h + q] = *reinterpret_cast<const float2 *>(
+              tab + __builtin_amdgcn_perm(cw[h], lane_off, 0x0C0C0000u | ((4u + q) << 8)));
+      load(j, i + kGvD < nb);
+      // the block scale, bit for bit the dequantization's block_scale
+      const float s = __fadd_rn(__fmul_rn(sdj, gaj), offset);
+      u32x4_t wb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = bf16x2_rne(__fmul_rn(pq[p & 1][i].x, s[rt]), __fmul_rn(pq[p & 1][i].y, s[rt]));
-      acc[rt] = mfma16(a, xf[t], acc[rt]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          wb[h][q] = bf16x2_rne(__fmul_rn(lv[4 * h + q].x, s), __fmul_rn(lv[4 * h + q].y, s));
+      acc = mfma16(xa0, wb[0], acc);
+      acc = mfma16(xa1, wb[1], acc);
+      cbi += 1;
+      if (i < nb && (++ckb == nkb || i == nb - 1)) {  // leaving a row group: partial out
+        float *p = pbase + (int64_t)seg_i * M * kGvRows;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (4 * g + v < M) p[(4 * g + v) * kGvRows] = acc[v];
+        acc = zero;
+        ++seg_i;
+        if (ckb == nkb) {
+          ckb = 0;
+          cbi += gstep_b;
+        }
+      }
     }
   }
 
-  // acc[rt][v] = partial C[n = n0 + 16rt + 4g + v][m = li]
-  __syncthreads();  // every wave done with the table
+  if (hwork) {  // sum the 16 wave results of the H slice in wave order
+    __syncthreads();
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
+    red[wave * 64 + lane] = hacc;
+    __syncthreads();
+    if (wave == 0) {
+      f32x4_t t = zero;
+      for (int q = 0; q < kGvWaves; ++q) {
+        const f32x4_t v = red[q * 64 + lane];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt];
-  __syncthreads();
-  for (int e = tid; e < 4 * 64 * 4; e += GW * 64) {
-    const int rt = e >> 8, l = (e >> 2) & 63, v = e & 3;
-    const int64_t n = n0 + 16 * rt + 4 * (l >> 4) + v;
-    const int m = l & 15;
-    if (m >= M || n >= N) continue;
-    float sum = 0.f;
+        for (int e = 0; e < 4; ++e) t[e] += v[e];
+      }
+      const int j = 16 * jt + li;
 #pragma unroll
-    for (int q = 0; q < GW; ++q) sum += red[q][rt][l][v];
-    float lo = 0.f;  // LoRA term: bf16 operands, exact products, fp32 sum
-    for (int j = 0; j < r; ++j) {
-      const float a = __uint_as_float((uint32_t)sH[(int64_t)m * RP + j] << 16);
-      const float b = __uint_as_float((uint32_t)Bl[n * r + j] << 16);
-      lo = __fmaf_rn(a, b, lo);
+      for (int v = 0; v < 4; ++v)
+        if (4 * g + v < M && j < r) hpart[((int64_t)ks * M + 4 * g + v) * RP + j] = t[v];
     }
-    Y[(int64_t)m * N + n] = f32_to_bf16_bits(sum + lo);
   }
+}
+
+// One workgroup per row group, one thread per row: H from its slices, then
+// y[m][n] = bf16(sum of the group's partials (workgroup order) +
+// sum_j bf16(s H[m][j]) B[n][j]).  Every load a thread needs is issued before
+// its sums start.
+__global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const float *__restrict__ hpart, int nslices,
+                                                     const float *__restrict__ part, const uint16_t *__restrict__ Bl,
+                                                     int r, int RP, float s, int64_t T, int G, int seg,
+                                                     int64_t nkb, uint16_t *__restrict__ Y, float *__restrict__ H_out) {
+  __shared__ float s_h[16 * 128];  // bf16(s H) as floats, [m][j]
+  const int tid = threadIdx.x;
+  const int64_t gr = blockIdx.x;
+  for (int e = tid; e < M * r; e += 256) {
+    const int m = e / r, j = e % r;
+    float v[8];
+    float h = 0.f;
+    for (int q0 = 0; q0 < nslices; q0 += 8) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = q0 + q < nslices ? hpart[((int64_t)(q0 + q) * M + m) * RP + j] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) h += v[q];
+    }
+    if (gr == 0 && H_out) H_out[(int64_t)m * r + j] = h;
+    s_h[m * 128 + j] = bf16_to_f32(f32_to_bf16_bits(__fmul_rn(s, h)));
+  }
+  const int64_t n = gr * kGvRows + tid;
+  const bool live = n < N;
+  // partial sums of the workgroups covering this group, workgroup order;
+  // workgroup q's range starts at block 4 floor(q (T/4) / G), so block b
+  // lies in workgroup ((b/4 + 1) G - 1) / (T/4)
+  const int64_t T4 = T / 4;
+  const int64_t wlo = ((gr * nkb / 4 + 1) * G - 1) / T4, whi = ((((gr + 1) * nkb - 1) / 4 + 1) * G - 1) / T4;
+  float y[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) y[m] = 0.f;
+  if (live) {
+    for (int64_t q = wlo; q <= whi; ++q) {
+      const int64_t qb = 4 * (q * T4 / G);
+      if (4 * ((q + 1) * T4 / G) == qb) continue;  // an empty range
+      const float *p = part + ((q * seg + (gr - qb / nkb)) * M) * kGvRows + tid;
+      float v[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) v[m] = m < M ? p[m * kGvRows] : 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) y[m] += v[m];
+    }
+  }
+  __syncthreads();  // s_h
+  if (!live) return;
+  float lo[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) lo[m] = 0.f;
+  const uint16_t *brow = Bl + n * r;
+  for (int j0 = 0; j0 < r; j0 += 8) {
+    uint32_t bw[4];
+    if ((r & 7) == 0) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(brow + j0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bw[e] = v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t a = j0 + 2 * e < r ? brow[j0 + 2 * e] : 0u, b = j0 + 2 * e + 1 < r ? brow[j0 + 2 * e + 1] : 0u;
+        bw[e] = a | (b << 16);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (j0 + t >= r) break;
+      const float b = bf16_to_f32((bw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
+#pragma unroll
+      for (int m = 0; m < 16; ++m)
+        if (m < M) lo[m] = __fmaf_rn(s_h[m * 128 + j0 + t], b, lo[m]);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+    if (m < M) Y[(int64_t)m * N + n] = f32_to_bf16_bits(y[m] + lo[m]);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_gemv(const Nf4View &w, const uint16_t *X, int64_t M, const uint16_t *Bl, int r, int RP,
-                           const uint16_t *sH, uint16_t *Y, hipStream_t s) {
-  QLORA_LAUNCH("k_gemv_nf4", k_gemv_nf4, dim3((unsigned)ceil_div(w.n, 64)), dim3(GW * 64), 0, s, w, X, (int)M, Bl, r, RP,
-               sH, Y);
+bool small_m_supported(int64_t M, int64_t n, int64_t k, int r) {
+  if (M < 1 || M > kGemvMaxM || r > 128 || k % (4 * kBlock) != 0 || n * (k / 2) >= (int64_t(1) << 31)) return false;
+  return gemv_plan(M, n, k, lora_rank_pad(r)).G <= kMaxG;
+}
+
+size_t small_m_workspace_bytes(int64_t M, int64_t n, int64_t k, int r) {
+  return small_ws_layout(M, n, k, lora_rank_pad(r)).total;
+}
+
+hipError_t launch_fwd_small(const Nf4View &w, const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B,
+                            int r, float s, uint16_t *Y, float *H_out, void *ws, hipStream_t st) {
+  const int RP = lora_rank_pad(r);
+  const SmallWs l = small_ws_layout(M, w.n, w.k, RP);
+  const GemvPlan &p = l.p;
+  char *base = static_cast<char *>(ws);
+  float *hpart = reinterpret_cast<float *>(base + l.h_off);
+  float *part = reinterpret_cast<float *>(base + l.part_off);
+  QLORA_LAUNCH("k_gemv_nf4", k_gemv_nf4, dim3((unsigned)p.G), dim3(1024), 0, st, w, X, (int)M, A, r, RP, hpart, part,
+               p.T, p.G, p.seg, p.nh, p.nht, p.xoff);
+  QLORA_LAUNCH("k_gemv_finish", k_gemv_finish, dim3((unsigned)p.ngroups), dim3(256), 0, st, w.n, (int)M, hpart,
+               p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.seg, p.nkb, Y, H_out);
   return hipGetLastError();
 }
 

@@ -25,10 +25,15 @@ hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, 
 hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
                                int RP, const uint16_t *Gb, uint16_t *dX, hipStream_t s);
 
-// Small-M forward (nf4_gemv.hip): the same Y for M <= kGemvMaxM, one pass
-// over the packed weight with the K split inside each workgroup.
+// Small-M forward (nf4_gemv.hip): the whole forward -- H, and
+// Y = X W_hat^T + bf16(s H) B^T -- for 1 <= M <= kGemvMaxM in one pass over
+// the packed weight.  Needs small_m_supported (k % 256 == 0, packed weight
+// below 2^31 bytes, rank at most 128) and small_m_workspace_bytes of device
+// scratch.
 constexpr int64_t kGemvMaxM = 16;
-hipError_t launch_fwd_gemv(const Nf4View &w, const uint16_t *X, int64_t M, const uint16_t *Bl, int r, int RP,
-                           const uint16_t *sH, uint16_t *Y, hipStream_t s);
+bool small_m_supported(int64_t M, int64_t n, int64_t k, int r);
+size_t small_m_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
+hipError_t launch_fwd_small(const Nf4View &w, const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B,
+                            int r, float s, uint16_t *Y, float *H_out, void *ws, hipStream_t st);
 
 }  // namespace qlora

@@ -73,6 +73,24 @@ def test_edge_shapes(q, n, k, m, r, alpha, seed):
     _run_full(q, W, X, A, B, dY, r, alpha, f"edge n{n} k{k} m{m} r{r}")
 
 
+@pytest.mark.parametrize("n,k,m,r,alpha,seed", [
+    (300, 768, 5, 100, 32.0, 11),    # two ragged row groups, one 4-block unit per workgroup, rank 100
+    (1000, 4096, 3, 16, 16.0, 12),   # 256 workgroups, ragged last group
+    (4000, 2560, 7, 8, -2.0, 13),    # odd M, groups split across workgroups
+    (2048, 8192, 16, 64, 16.0, 14),  # M = 16, 16 blocks per workgroup
+    (64, 256, 2, 1, 16.0, 15),       # one partial row group, one unit, rank 1
+    (300, 640, 4, 8, 16.0, 16),      # k % 256 != 0: the tile kernels serve M <= 16 too
+])
+def test_small_m_shapes(q, n, k, m, r, alpha, seed):
+    """M <= 16 takes the GEMV forward when k % 256 == 0; every output is compared."""
+    W = I.custom_weight(n, k, seed)
+    X = I.custom_bf16((m, k), seed, 1)
+    dY = I.custom_bf16((m, n), seed, 2)
+    A = I.custom_bf16((r, k), seed, 3, bound=0.05)
+    B = I.custom_bf16((n, r), seed, 4, bound=0.05)
+    _run_full(q, W, X, A, B, dY, r, alpha, f"small-M n{n} k{k} m{m} r{r}")
+
+
 def test_bwd_recomputes_h_and_skips_dx(q):
     W = I.custom_weight(192, 320, 8)
     X, dY = I.custom_bf16((70, 320), 8, 1), I.custom_bf16((70, 192), 8, 2)
