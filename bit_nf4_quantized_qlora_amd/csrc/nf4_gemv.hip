@@ -60,6 +60,8 @@ struct GemvPlan {
   int64_t nkb = 0, ngroups = 0, T = 0;  // blocks per row, row groups, (group, block) pairs
   int G = 0;                            // workgroups
   int seg = 1;                          // most row groups one workgroup touches
+  int maxcov = 1;                       // most workgroups covering one row group
+  bool sparse = false;                  // some workgroups have empty ranges
   int nht = 0, nh = 0;                  // rank tiles of 16; H slices x rank tiles
   int xoff = 0;                         // byte offset of the staged X in the variable area
   int q4 = 1;                           // ranges start on multiples of q4 blocks (4 if nkb % 4 == 0)
@@ -92,6 +94,15 @@ GemvPlan gemv_plan(int64_t M, int64_t n, int64_t k, int RP) {
   int64_t G = std::max<int64_t>(std::min<int64_t>(256, p.T / p.q4), p.nh);
   while (G < kMaxG && !fit(G)) G = std::min<int64_t>(G + 256, kMaxG);
   p.G = fit(G) ? (int)G : kMaxG + 1;  // no fit: small_m_supported says no
+  // partial sums are kept per (row group, covering workgroup): workgroup
+  // q's range starts at block 4 floor(q (T/4) / G), so block b lies in
+  // workgroup ((b/4 + 1) G - 1) / (T/4)
+  const int64_t T4 = p.T / 4;
+  p.sparse = p.G > T4;
+  for (int64_t gr = 0; gr < p.ngroups && p.G <= kMaxG; ++gr) {
+    const int64_t wlo = ((gr * p.nkb / 4 + 1) * p.G - 1) / T4, whi = ((((gr + 1) * p.nkb - 1) / 4 + 1) * p.G - 1) / T4;
+    p.maxcov = (int)std::max<int64_t>(p.maxcov, whi - wlo + 1);
+  }
   return p;
 }
 
@@ -105,7 +116,7 @@ SmallWs small_ws_layout(int64_t M, int64_t n, int64_t k, int RP) {
   l.p = gemv_plan(M, n, k, RP);
   l.h_off = 0;
   l.part_off = align_up((size_t)(l.p.nh / l.p.nht) * M * RP * sizeof(float), 256);
-  l.total = l.part_off + (size_t)l.p.G * l.p.seg * M * kGvRows * sizeof(float);
+  l.total = l.part_off + (size_t)l.p.ngroups * l.p.maxcov * M * kGvRows * sizeof(float);
   return l;
 }
 
@@ -114,7 +125,8 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t *__restrict__ X, int M,
                                                       const uint16_t *__restrict__ A, int r, int RP,
                                                       float *__restrict__ hpart, float *__restrict__ part,
-                                                      int64_t T, int G, int seg, int nh, int nht, int xoff_b) {
+                                                      int64_t T, int G, int seg, int maxcov, int nh, int nht,
+                                                      int xoff_b) {
   // LDS: level-pair table (64 KB, first so its reads need no base add),
   // E4M3 decode table (1 KB), a zero row, then the group constants of the
   // row groups the range touches and the staged X.
@@ -231,9 +243,10 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   // round and multiply; the four waves of a SIMD hide each other's LDS
   // latency.  Blocks past the end (the loop runs whole rounds of 8) read
   // zeros and the last real X row, and their sums are never stored.
-  // this lane's partial slots: [(wg*seg + seg_i) * M + m] * 256 + nrow
-  float *pbase = part + (int64_t)wg * seg * M * kGvRows + nrow;
-  int seg_i = 0;
+  // partial slot of (row group gr, covering workgroup k = wg - first
+  // covering workgroup): [(gr * maxcov + k) * M + m] * 256 + row
+  const int64_t T4 = T / 4;
+  int64_t cgr = gfirst;
   int ckb = (int)(b0 - gfirst * nkb);
   // block index n*nkb + kb of the block being computed; its group constant
   // is s_ga[(cbi >> 8) - gfirst*nkb]
@@ -271,15 +284,16 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
       acc = mfma16(xa1, wb[1], acc);
       cbi += 1;
       if (i < nb && (++ckb == nkb || i == nb - 1)) {  // leaving a row group: partial out
-        float *p = pbase + (int64_t)seg_i * M * kGvRows;
+        const int64_t wlo = ((cgr * nkb / 4 + 1) * G - 1) / T4;
+        float *p = part + ((cgr * maxcov + (wg - wlo)) * M) * kGvRows + nrow;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if (4 * g + v < M) p[(4 * g + v) * kGvRows] = acc[v];
         acc = zero;
-        ++seg_i;
         if (ckb == nkb) {
           ckb = 0;
           cbi += gstep_b;
+          ++cgr;
         }
       }
     }
@@ -305,83 +319,75 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   }
 }
 
-// One workgroup per row group, one thread per row: H from its slices, then
+// One workgroup per (row group, m), one thread per row n:
 // y[m][n] = bf16(sum of the group's partials (workgroup order) +
-// sum_j bf16(s H[m][j]) B[n][j]).  Every load a thread needs is issued before
-// its sums start.
+// sum_j bf16(s H[m][j]) B[n][j]), H[m][j] summed over its slices in order.
+// The group's rows of B (contiguous, 256 r bf16) are staged in LDS with
+// coalesced loads; the kernel is kept small (it runs once per call, from a
+// cold instruction cache).
+template <bool kVecB>  // r % 8 == 0: B staged by 16-byte loads
 __global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const float *__restrict__ hpart, int nslices,
                                                      const float *__restrict__ part, const uint16_t *__restrict__ Bl,
-                                                     int r, int RP, float s, int64_t T, int G, int seg,
-                                                     int64_t nkb, uint16_t *__restrict__ Y, float *__restrict__ H_out) {
-  __shared__ float s_h[16 * 128];  // bf16(s H) as floats, [m][j]
-  const int tid = threadIdx.x;
+                                                     int r, int RP, float s, int64_t T, int G, int maxcov,
+                                                     bool sparse, int64_t nkb, uint16_t *__restrict__ Y,
+                                                     float *__restrict__ H_out) {
+  __shared__ float s_h[128];                             // bf16(s H[m][j]) as floats
+  __shared__ __align__(16) uint16_t s_b[kGvRows * 128];  // B rows of the group, row stride r
+  const int tid = threadIdx.x, m = blockIdx.y;
   const int64_t gr = blockIdx.x;
-  for (int e = tid; e < M * r; e += 256) {
-    const int m = e / r, j = e % r;
-    float v[8];
+  const int64_t n = gr * kGvRows + tid;
+  const int64_t rows = std::min<int64_t>(kGvRows, N - gr * kGvRows);
+  const uint16_t *bsrc = Bl + gr * kGvRows * r;
+  if constexpr (kVecB) {
+    const int nch = (int)(rows * r / 8);
+    for (int c = tid; c < nch; c += 256)
+      *reinterpret_cast<u32x4_t *>(s_b + 8 * c) = *reinterpret_cast<const u32x4_t *>(bsrc + 8 * c);
+  } else {
+    for (int c = tid; c < rows * r; c += 256) s_b[c] = bsrc[c];
+  }
+  if (tid < r) {  // H[m][tid], slice order, 8 loads in flight
     float h = 0.f;
     for (int q0 = 0; q0 < nslices; q0 += 8) {
+      float v[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = q0 + q < nslices ? hpart[((int64_t)(q0 + q) * M + m) * RP + j] : 0.f;
+      for (int q = 0; q < 8; ++q) v[q] = q0 + q < nslices ? hpart[((int64_t)(q0 + q) * M + m) * RP + tid] : 0.f;
 #pragma unroll
       for (int q = 0; q < 8; ++q) h += v[q];
     }
-    if (gr == 0 && H_out) H_out[(int64_t)m * r + j] = h;
-    s_h[m * 128 + j] = bf16_to_f32(f32_to_bf16_bits(__fmul_rn(s, h)));
+    if (gr == 0 && H_out) H_out[(int64_t)m * r + tid] = h;
+    s_h[tid] = bf16_to_f32(f32_to_bf16_bits(__fmul_rn(s, h)));
   }
-  const int64_t n = gr * kGvRows + tid;
-  const bool live = n < N;
-  // partial sums of the workgroups covering this group, workgroup order;
-  // workgroup q's range starts at block 4 floor(q (T/4) / G), so block b
-  // lies in workgroup ((b/4 + 1) G - 1) / (T/4)
+  // partial sums of the covering workgroups, workgroup order; workgroup q's
+  // range starts at block 4 floor(q (T/4) / G), so block b lies in
+  // workgroup ((b/4 + 1) G - 1) / (T/4)
   const int64_t T4 = T / 4;
   const int64_t wlo = ((gr * nkb / 4 + 1) * G - 1) / T4, whi = ((((gr + 1) * nkb - 1) / 4 + 1) * G - 1) / T4;
-  float y[16];
+  const float *p = part + ((gr * maxcov) * M + m) * kGvRows + tid;
+  float y = 0.f;
+  if (n < N) {
+    if (!sparse) {  // 4 loads in flight
+      const int nc = (int)(whi - wlo + 1);
+      for (int k0 = 0; k0 < nc; k0 += 4) {
+        float v[4];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) y[m] = 0.f;
-  if (live) {
-    for (int64_t q = wlo; q <= whi; ++q) {
-      const int64_t qb = 4 * (q * T4 / G);
-      if (4 * ((q + 1) * T4 / G) == qb) continue;  // an empty range
-      const float *p = part + ((q * seg + (gr - qb / nkb)) * M) * kGvRows + tid;
-      float v[16];
+        for (int k = 0; k < 4; ++k) v[k] = k0 + k < nc ? p[(int64_t)(k0 + k) * M * kGvRows] : 0.f;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) v[m] = m < M ? p[m * kGvRows] : 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) y[m] += v[m];
-    }
-  }
-  __syncthreads();  // s_h
-  if (!live) return;
-  float lo[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m) lo[m] = 0.f;
-  const uint16_t *brow = Bl + n * r;
-  for (int j0 = 0; j0 < r; j0 += 8) {
-    uint32_t bw[4];
-    if ((r & 7) == 0) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(brow + j0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bw[e] = v[e];
+        for (int k = 0; k < 4; ++k) y += v[k];
+      }
     } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t a = j0 + 2 * e < r ? brow[j0 + 2 * e] : 0u, b = j0 + 2 * e + 1 < r ? brow[j0 + 2 * e + 1] : 0u;
-        bw[e] = a | (b << 16);
+      for (int64_t q = wlo; q <= whi; ++q) {
+        // an empty range (more workgroups than 4-block units) wrote nothing
+        if (4 * ((q + 1) * T4 / G) == 4 * (q * T4 / G)) continue;
+        y += p[(q - wlo) * M * kGvRows];
       }
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (j0 + t >= r) break;
-      const float b = bf16_to_f32((bw[t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-        if (m < M) lo[m] = __fmaf_rn(s_h[m * 128 + j0 + t], b, lo[m]);
-    }
   }
-#pragma unroll
-  for (int m = 0; m < 16; ++m)
-    if (m < M) Y[(int64_t)m * N + n] = f32_to_bf16_bits(y[m] + lo[m]);
+  __syncthreads();  // s_h, s_b
+  if (n >= N) return;
+  float lo = 0.f;
+  const uint16_t *brow = s_b + tid * r;
+  for (int j = 0; j < r; ++j) lo = __fmaf_rn(s_h[j], bf16_to_f32(brow[j]), lo);
+  Y[(int64_t)m * N + n] = f32_to_bf16_bits(y + lo);
 }
 
 }  // namespace
@@ -404,9 +410,13 @@ hipError_t launch_fwd_small(const Nf4View &w, const uint16_t *X, int64_t M, cons
   float *hpart = reinterpret_cast<float *>(base + l.h_off);
   float *part = reinterpret_cast<float *>(base + l.part_off);
   QLORA_LAUNCH("k_gemv_nf4", k_gemv_nf4, dim3((unsigned)p.G), dim3(1024), 0, st, w, X, (int)M, A, r, RP, hpart, part,
-               p.T, p.G, p.seg, p.nh, p.nht, p.xoff);
-  QLORA_LAUNCH("k_gemv_finish", k_gemv_finish, dim3((unsigned)p.ngroups), dim3(256), 0, st, w.n, (int)M, hpart,
-               p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.seg, p.nkb, Y, H_out);
+               p.T, p.G, p.seg, p.maxcov, p.nh, p.nht, p.xoff);
+  if (r % 8 == 0)
+    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<true>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), 0, st, w.n, (int)M,
+                 hpart, p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.maxcov, p.sparse, p.nkb, Y, H_out);
+  else
+    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<false>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), 0, st, w.n, (int)M,
+                 hpart, p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.maxcov, p.sparse, p.nkb, Y, H_out);
   return hipGetLastError();
 }
 
