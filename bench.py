@@ -19,10 +19,19 @@ Also reported, each against its roofline:
   kernels           per-kernel average duration from the library's event timer
   roofline          the dominant kernel (largest summed time in a step)
   cpu_baseline      the CPU oracle (NumPy fp64) on a bounded sample of the step
+
+roofline.traffic (HBM bytes per launch of the dominant kernel) comes from
+profiles/traffic_counters.json when its source digest matches the library
+sources.  That file is written by --ingest-pmc from two rocprofv3 counter
+runs of this script with --calib-copy-mib (FETCH_SIZE, then WRITE_SIZE);
+both counters are scaled by what they read for the calibration copy, an
+elementwise kernel that reads and writes exactly that many bytes.
 """
 from __future__ import annotations
 
 import argparse
+import collections
+import csv
 import glob
 import hashlib
 import json
@@ -50,6 +59,9 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip quantize/dequant/small-M rows")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/traffic_counters.json from two rocprofv3 --pmc output folders "
+                        "(FETCH_SIZE, WRITE_SIZE) of a run with --calib-copy-mib, then exit")
     return p.parse_args()
 
 
@@ -67,8 +79,63 @@ def layer_flops(M, N, K, r):
     return fwd, bwd
 
 
+# rocprofv3 kernel names -> the names the library's event timer uses
+KERNEL_ALIASES = {"k_nf4_tile<false>": "k_fwd_nf4", "k_nf4_tile<true>": "k_bwd_dx_nf4"}
+
+
+def short_kernel_name(name: str) -> str:
+    base = name.replace("qlora::(anonymous namespace)::", "").replace("qlora::", "")
+    base = base.split("(")[0].replace("void ", "").strip()
+    return KERNEL_ALIASES.get(base, base)
+
+
+def ingest_pmc(fetch_dir: str, write_dir: str) -> None:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) -> bytes per launch, each
+    scaled so the calibration copy reads and writes its known size."""
+    def load(folder, counter):
+        per = collections.defaultdict(float)  # (kernel, dispatch) -> value
+        for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if row["Counter_Name"] == counter:
+                        per[(short_kernel_name(row["Kernel_Name"]), row["Dispatch_Id"])] += float(row["Counter_Value"])
+        by = collections.defaultdict(list)
+        for (k, _), v in per.items():
+            by[k].append(v)
+        return by
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    calib_path = os.path.join(fetch_dir, "calib_copy.json")
+    with open(calib_path) as fh:
+        copy_bytes = json.load(fh)["copy_bytes_read"]
+    # the calibration copy: the elementwise kernel with the largest dispatch
+    cands = [k for k in fetch if "elementwise" in k]
+    ck = max(cands, key=lambda k: max(fetch[k]))
+    f_raw, w_raw = max(fetch[ck]), max(write[ck])
+    f_scale, w_scale = copy_bytes / f_raw, copy_bytes / w_raw
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        if k.startswith("k_"):
+            fm, wm = sum(fetch[k]) / len(fetch[k]), sum(write[k]) / len(write[k])
+            kernels[k] = {"dispatches": len(fetch[k]), "fetch_raw_per_launch": round(fm, 1),
+                          "write_raw_per_launch": round(wm, 1),
+                          "fetch_bytes_per_launch": round(fm * f_scale), "write_bytes_per_launch": round(wm * w_scale)}
+    out = {"source_sha256": source_digest(), "counters": ["FETCH_SIZE", "WRITE_SIZE"],
+           "calibration": {"kernel": ck, "copy_bytes": copy_bytes, "fetch_raw": f_raw, "write_raw": w_raw,
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "kernels": kernels}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out["calibration"]))
+    for k, v in kernels.items():
+        print(f"{k:28s} {v['dispatches']:4d} fetch {v['fetch_bytes_per_launch'] / 1e6:10.1f} MB  "
+              f"write {v['write_bytes_per_launch'] / 1e6:10.1f} MB per launch")
+
+
 def main():
     args = parse()
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -235,11 +302,14 @@ def main():
         nbytes = args.calib_copy_mib << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        for _ in range(3):  # an elementwise kernel (a plain copy_ may go to a DMA engine)
+            torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
-        calib = {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes}
+        calib = {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "kernel": "elementwise mul by 1"}
         del src, dst
+        if os.environ.get("QLORA_CALIB_DIR"):
+            with open(os.path.join(os.environ["QLORA_CALIB_DIR"], "calib_copy.json"), "w") as fh:
+                json.dump(calib, fh)
 
     cpu = None
     if not args.no_cpu_baseline:
