@@ -179,9 +179,16 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   // offsets would be made uniform with a per-lane loop
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Tiles in bands of ob o-tiles, m-major inside a band; each XCD takes a
+  // contiguous run of that order (xcd_tile), so the tiles it holds form an
+  // m x ob block and share both operand panels in its L2.
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int to = tile % tiles_o;
-  const int64_t o0 = (int64_t)to * TO, m0 = (int64_t)(tile / tiles_o) * TM;
+  const int tiles_m = gridDim.x / tiles_o;
+  const int ob = (tiles_o + 1) / 2;
+  const int band = tile / (ob * tiles_m), within = tile - band * ob * tiles_m;
+  const int obw = min(ob, tiles_o - band * ob);  // the last band may be narrower
+  const int to = band * ob + within % obw;
+  const int64_t o0 = (int64_t)to * TO, m0 = (int64_t)(within / obw) * TM;
   const int64_t N = w.n, K = w.k;
   const int64_t NO = kBwd ? K : N, NC = kBwd ? N : K;  // output width, contraction length
   const int64_t nk = NC / kBlock;                      // 64-wide steps
