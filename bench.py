@@ -15,7 +15,8 @@ Also reported, each against its roofline:
   rows.fwd / .bwd   per-pass TFLOP/s
   rows.small_m      65B up_proj (8192->22016) forward at M = 1, 4, 16, GB/s on the
                     packed-weight bytes, rotating 6 weight copies (558 MB) so the
-                    256 MB last-level cache cannot hold them
+                    256 MB last-level cache cannot hold them: the whole call, and
+                    the streaming kernel alone
   kernels           per-kernel average duration from the library's event timer
   roofline          the dominant kernel (largest summed time in a step)
   cpu_baseline      the CPU oracle (NumPy fp64) on a bounded sample of the step
@@ -59,6 +60,8 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="skip quantize/dequant/small-M rows")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--small-m-only", action="store_true",
+                   help="print only rows.small_m (the small-M forward), as one JSON line")
     p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/traffic_counters.json from two rocprofv3 --pmc output folders "
                         "(FETCH_SIZE, WRITE_SIZE) of a run with --calib-copy-mib, then exit")
@@ -156,6 +159,11 @@ def main():
 
     def dev16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.small_m_only:
+        print(json.dumps({"small_m": small_m_rows(q, I, np, torch, dev, dev16, lambda: torch.cuda.Event(enable_timing=True))}),
+              flush=True)
+        return
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
@@ -371,8 +379,20 @@ def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
         torch.cuda.synchronize()
         us = 1e3 * a.elapsed_time(b) / reps
         gbps = packed_bytes / (us * 1e-6) / 1e9
-        out[f"M{m}"] = {"us": round(us, 2), "gbps_packed": round(gbps, 1),
-                        "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        row = {"us": round(us, 2), "gbps_packed": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        # the streaming kernel on its own (library event timer, separate pass)
+        q.qlora_profile_begin()
+        for i in range(reps):
+            q.qlora_linear_fwd(ws_list[i % copies], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws)
+        prof = q.qlora_profile_end()
+        if "k_gemv_nf4" in prof:
+            n, ms = prof["k_gemv_nf4"]
+            kus = 1e3 * ms / n
+            row["kernel"] = "k_gemv_nf4"
+            row["kernel_us"] = round(kus, 2)
+            row["kernel_gbps_packed"] = round(packed_bytes / (kus * 1e-6) / 1e9, 1)
+            row["kernel_frac_hbm_peak"] = round(packed_bytes / (kus * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+        out[f"M{m}"] = row
     return out
 
 
