@@ -29,10 +29,13 @@
 // one LDS read of a level pair per packed byte from a 256-entry table with
 // 32 copies (entry e of copy c at byte 256e + 8c, copy = lane % 32, so no
 // half-wave read ever conflicts), addressed by a single byte permute of the
-// code byte and the lane's offset.  Lane (li, g) holds, for row li of the
-// tile, the 8 code bytes of contraction positions 16g .. 16g+15 of the block
-// (MFMA h takes 16g + 8h .. +7), fetched 8 blocks ahead; X is staged in LDS
-// for the whole range (row m's 16-byte chunk c at c ^ ((m >> 1) & 7)).
+// code byte and the lane's offset.  Blocks go in pairs: lane (li, g) holds
+// the 16 code bytes at byte 16g of row li's 64 bytes of the pair (block g/2,
+// positions 32(g % 2) .. +31 of it; MFMA t takes bytes 4t .. 4t+3), so one
+// load instruction reads 64 contiguous bytes of each of 16 rows and a lane
+// needs one block scale per pair; codes are fetched 4 pairs ahead.  X is
+// staged in LDS for the whole range (row m's 16-byte chunk c at
+// c ^ ((m >> 1) & 7)), so X and the weights meet in the same order.
 //
 // H: workgroup t < nh takes rank tile t % (RP/16) and K slice t / (RP/16)
 // (512 wide, 32 per wave); its operands are loaded before anything else so
@@ -49,7 +52,7 @@ namespace {
 constexpr int kGvWaves = 16;               // waves per workgroup = row tiles per group
 constexpr int kGvRows = 16 * kGvWaves;     // weight rows per row group
 constexpr int kLdsAll = 160 * 1024;        // LDS of one workgroup
-constexpr int kGvD = 8;                    // blocks of codes in flight per lane
+constexpr int kGvP = 4;                    // pairs of blocks of codes in flight per lane
 constexpr int kLdsTab = 256 * 256;         // level-pair table, 32 copies
 constexpr int kLdsDec = 256 * 4;           // E4M3 decode table
 constexpr int kLdsVar = kLdsAll - kLdsTab - kLdsDec - 128;  // group constants + staged X
@@ -192,28 +195,33 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   const float offset = *w.offset;
   const int nrow = 16 * wave + li;  // row within the group
   const int64_t gfirst = b0 / nkb;
+  const int nkb32 = (int)nkb;
+  const int hb = g >> 1;  // which block of a pair this lane's codes come from
   int lkb = (int)(b0 - gfirst * nkb);
-  uint32_t lco = (uint32_t)((gfirst * kGvRows + nrow) * kb2 + lkb * 32 + 8 * g);
+  uint32_t lco = (uint32_t)((gfirst * kGvRows + nrow) * kb2 + lkb * 32 + 16 * g);
   uint32_t lbi = (uint32_t)((gfirst * kGvRows + nrow) * nkb + lkb);
   const uint32_t gstep_c = (uint32_t)(kGvRows * kb2 - nkb * 32), gstep_b = (uint32_t)(kGvRows * nkb - nkb);
-  u32x2_t cq[kGvD];
+  // codes of a pair of blocks: lane (li, g) takes the 16 bytes at 16g of the
+  // row's 64 bytes (block hb, contraction positions 32(g & 1) .. +31), so a
+  // wave instruction reads 64 contiguous bytes of each of its 16 rows
+  u32x4_t cq[kGvP];
   auto load = [&](int slot, bool real) {
-    cq[slot] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(crs, real ? lco : kOut, 0, 0));
-    lco += 32;
-    if (++lkb == nkb) {
+    cq[slot] = __builtin_amdgcn_raw_buffer_load_b128(crs, real ? lco : kOut, 0, 0);
+    lco += 64;
+    if ((lkb += 2) == nkb32) {
       lkb = 0;
       lco += gstep_c;
     }
   };
-  // Scale codes four blocks per load (ranges and row groups start on
-  // multiples of 4 blocks, and nkb % 4 == 0): word w of the row's codes, all
-  // four lanes of a row reading the same word; two words in flight.
+  // Scale codes four blocks (two pairs) per load (ranges and row groups
+  // start on multiples of 4 blocks, and nkb % 4 == 0): word w of the row's
+  // codes, all four lanes of a row reading the same word; two in flight.
   uint32_t scw[2];
   int skb = lkb;
   auto sload = [&](int slot, bool real) {
     scw[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, real ? lbi : kOut, 0, 0);
     lbi += 4;
-    if ((skb += 4) == nkb) {
+    if ((skb += 4) == nkb32) {
       skb = 0;
       lbi += gstep_b;
     }
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   sload(0, 0 < nb);
   sload(1, 4 < nb);
 #pragma unroll
-  for (int j = 0; j < kGvD; ++j) load(j, j < nb);
+  for (int j = 0; j < kGvP; ++j) load(j, 2 * j < nb);
   __syncthreads();  // table and X staged
 
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -229,68 +237,72 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
 
   const char *tab = reinterpret_cast<const char *>(s_tab);
   const uint32_t lane_off = (uint32_t)(lane & 31) * 8;
-  // X fragments of block i for MFMA h: chunk 2g + h of staged row i*M + li
-  // (lanes li >= M read the zero row, which takes no row step).
+  // X fragment of a pair for MFMA t: staged row (2ip + hb)*M + li, chunk
+  // 4(g & 1) + t (lanes li >= M read the zero row, which takes no step).
   const bool xreal = li < M;
   const int sw = (li >> 1) & 7;
-  const uint32_t xo0 = xreal ? (uint32_t)(xbase + li * 128 + (((2 * g) ^ sw) << 4)) : (uint32_t)kZeroOff;
-  const uint32_t xo1 = xreal ? (uint32_t)(xbase + li * 128 + (((2 * g + 1) ^ sw) << 4)) : (uint32_t)kZeroOff + 16;
-  const uint32_t xstep = xreal ? (uint32_t)M * 128 : 0u;
+  uint32_t xo[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    xo[t] = xreal ? (uint32_t)(xbase + (hb * M + li) * 128 + (((4 * (g & 1) + t) ^ sw) << 4)) : (uint32_t)kZeroOff;
+  const uint32_t xstep = xreal ? (uint32_t)M * 256 : 0u;
   uint32_t xoff = 0;
+  // scale code byte of this lane's block in the word: 2(ip & 1) + hb
+  const uint32_t ssh0 = 8u * hb, ssh1 = 16u + 8u * hb;
+  // block index n*nkb + kb of this lane's block of the current pair; its
+  // group constant is s_ga[(cbi >> 8) - gfirst*nkb]
+  uint32_t cbi = (uint32_t)((gfirst * kGvRows + nrow) * nkb + (b0 - gfirst * nkb) + hb);
+  const uint32_t ga_base = (uint32_t)kGaOff - (uint32_t)(gfirst * nkb) * 4;
 
-  // Block i: its LDS reads (decode entry, X fragments, level pairs), then
-  // the code load of block i + 8 into the freed ring slot, then scale,
-  // round and multiply; the four waves of a SIMD hide each other's LDS
-  // latency.  Blocks past the end (the loop runs whole rounds of 8) read
-  // zeros and the last real X row, and their sums are never stored.
   // partial slot of (row group gr, covering workgroup k = wg - first
   // covering workgroup): [(gr * maxcov + k) * M + m] * 256 + row
   const int64_t T4 = T / 4;
   int64_t cgr = gfirst;
   int ckb = (int)(b0 - gfirst * nkb);
-  // block index n*nkb + kb of the block being computed; its group constant
-  // is s_ga[(cbi >> 8) - gfirst*nkb]
-  uint32_t cbi = (uint32_t)((gfirst * kGvRows + nrow) * nkb + ckb);
-  const uint32_t ga_base = (uint32_t)kGaOff - (uint32_t)(gfirst * nkb) * 4;
+  const int np = nb >> 1;
   f32x4_t acc = zero;
-  for (int i0 = 0; i0 < nb; i0 += kGvD) {
+  // Pairs past the end (the loop runs whole rounds of kGvP) read zero codes,
+  // the last real X rows and in-range group constants; their sums are never
+  // stored.
+  for (int p0 = 0; p0 < np; p0 += kGvP) {
 #pragma unroll
-    for (int j = 0; j < kGvD; ++j) {
-      const int i = i0 + j;
-      const float sdj = s_dec[(scw[j >> 2] >> (8 * (j & 3))) & 0xFFu];
-      if ((j & 3) == 3) sload(j >> 2, i + 5 < nb);  // blocks i+5 .. i+8
-      const float gaj = *reinterpret_cast<const float *>(lds + ga_base + ((cbi >> 8) << 2));
-      const u32x4_t xa0 = *reinterpret_cast<const u32x4_t *>(lds + xo0 + xoff);
-      const u32x4_t xa1 = *reinterpret_cast<const u32x4_t *>(lds + xo1 + xoff);
-      if (i + 1 < nb) xoff += xstep;
-      const u32x2_t cw = cq[j];
-      float2 lv[8];
+    for (int q = 0; q < kGvP; ++q) {
+      const int ip = p0 + q;
+      const uint32_t sc = (scw[(q >> 1) & 1] >> ((q & 1) ? ssh1 : ssh0)) & 0xFFu;
+      const float sd = s_dec[sc];
+      if (q & 1) sload((q >> 1) & 1, 2 * ip + 6 < nb);  // blocks 2ip+6 .. 2ip+9
+      const float ga = *reinterpret_cast<const float *>(lds + ga_base + ((cbi >> 8) << 2));
+      u32x4_t xa[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int t = 0; t < 4; ++t) xa[t] = *reinterpret_cast<const u32x4_t *>(lds + xo[t] + xoff);
+      if (2 * ip + 2 < nb) xoff += xstep;
+      const u32x4_t cw = cq[q];
+      float2 lv[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          lv[4 * h + q] = *reinterpret_cast<const float2 *>(
-              tab + __builtin_amdgcn_perm(cw[h], lane_off, 0x0C0C0000u | ((4u + q) << 8)));
-      load(j, i + kGvD < nb);
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          lv[4 * t + e] = *reinterpret_cast<const float2 *>(
+              tab + __builtin_amdgcn_perm(cw[t], lane_off, 0x0C0C0000u | ((4u + e) << 8)));
+      load(q, 2 * ip + 2 * kGvP < nb);
       // the block scale, bit for bit the dequantization's block_scale
-      const float s = __fadd_rn(__fmul_rn(sdj, gaj), offset);
-      u32x4_t wb[2];
+      const float s = __fadd_rn(__fmul_rn(sd, ga), offset);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int t = 0; t < 4; ++t) {
+        u32x4_t wb;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          wb[h][q] = bf16x2_rne(__fmul_rn(lv[4 * h + q].x, s), __fmul_rn(lv[4 * h + q].y, s));
-      acc = mfma16(xa0, wb[0], acc);
-      acc = mfma16(xa1, wb[1], acc);
-      cbi += 1;
-      if (i < nb && (++ckb == nkb || i == nb - 1)) {  // leaving a row group: partial out
+        for (int e = 0; e < 4; ++e) wb[e] = bf16x2_rne(__fmul_rn(lv[4 * t + e].x, s), __fmul_rn(lv[4 * t + e].y, s));
+        acc = mfma16(xa[t], wb, acc);
+      }
+      cbi += 2;
+      if (ip < np && ((ckb += 2) == nkb32 || ip == np - 1)) {  // leaving a row group: partial out
         const int64_t wlo = ((cgr * nkb / 4 + 1) * G - 1) / T4;
-        float *p = part + ((cgr * maxcov + (wg - wlo)) * M) * kGvRows + nrow;
+        float *pp = part + ((cgr * maxcov + (wg - wlo)) * M) * kGvRows + nrow;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-          if (4 * g + v < M) p[(4 * g + v) * kGvRows] = acc[v];
+          if (4 * g + v < M) pp[(4 * g + v) * kGvRows] = acc[v];
         acc = zero;
-        if (ckb == nkb) {
+        if (ckb == nkb32) {
           ckb = 0;
           cbi += gstep_b;
           ++cgr;
