@@ -55,9 +55,11 @@ constexpr int kLdsAll = 160 * 1024;        // LDS of one workgroup
 constexpr int kGvP = 4;                    // pairs of blocks of codes in flight per lane
 constexpr int kLdsTab = 256 * 256;         // level-pair table, 32 copies
 constexpr int kLdsDec = 256 * 4;           // E4M3 decode table
-constexpr int kLdsVar = kLdsAll - kLdsTab - kLdsDec - 128;  // group constants + staged X
+constexpr int kLdsVar = kLdsAll - kLdsTab - kLdsDec - 128 - 16;  // group constants + staged X
 constexpr int kHSlice = 32 * kGvWaves;     // K per H slice: one 32-deep MFMA per wave
 constexpr int kMaxG = 4096;                // most workgroups
+constexpr int kXPer = 6;                   // staged X chunks per thread: 6 * 1024 * 16 B >= kLdsVar
+constexpr int kGaPer = 2;                  // group constants per thread loaded ahead of the table fill
 
 struct GemvPlan {
   int64_t nkb = 0, ngroups = 0, T = 0;  // blocks per row, row groups, (group, block) pairs
@@ -128,76 +130,48 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t *__restrict__ X, int M,
                                                       const uint16_t *__restrict__ A, int r, int RP,
                                                       float *__restrict__ hpart, float *__restrict__ part,
-                                                      int64_t T, int G, int seg, int maxcov, int nh, int nht,
-                                                      int xoff_b) {
+                                                      int T4, int G, int gq, int grem, int seg, int maxcov, int nh,
+                                                      int nht, int xoff_b) {
   // LDS: level-pair table (64 KB, first so its reads need no base add),
   // E4M3 decode table (1 KB), a zero row, then the group constants of the
   // row groups the range touches and the staged X.
   __shared__ __align__(16) uint8_t lds[kLdsAll];
   float2 *s_tab = reinterpret_cast<float2 *>(lds);
   float *s_dec = reinterpret_cast<float *>(lds + kLdsTab);
-  constexpr int kZeroOff = kLdsTab + kLdsDec, kGaOff = kZeroOff + 128;
+  constexpr int kZeroOff = kLdsTab + kLdsDec, kMiscOff = kZeroOff + 128, kGaOff = kMiscOff + 16;
   float *s_ga = reinterpret_cast<float *>(lds + kGaOff);
   const int xbase = kGaOff + xoff_b;
   uint8_t *s_x = lds + xbase;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t N = w.n, K = w.k, nkb = K / kBlock, kb2 = K / 2;
+  const int64_t N = w.n, K = w.k, kb2 = K / 2;
+  const int nkb = (int)(K / kBlock);
   const int wg = blockIdx.x;
-  const int64_t b0 = 4 * ((int64_t)wg * (T / 4) / G), b1 = 4 * ((int64_t)(wg + 1) * (T / 4) / G);
-  const int nb = (int)(b1 - b0);
+  // range [b0, b1) = 4 floor(wg (T/4) / G) .. with T/4 = gq G + grem, in
+  // 32-bit arithmetic (wg grem < 2^24); every wave of the 16 computes these
+  // scalars, so they are kept cheap
+  const int b0 = 4 * (wg * gq + (int)(((uint32_t)wg * (uint32_t)grem) / (uint32_t)G));
+  const int b1 = 4 * ((wg + 1) * gq + (int)(((uint32_t)(wg + 1) * (uint32_t)grem) / (uint32_t)G));
+  const int nb = b1 - b0;
+  const int gfirst = b0 / nkb;
+  const int lkb0 = b0 - gfirst * nkb;
 
-  // H slice operands first: X rows li < M and A rows 16 jt + li < r at
-  // k = 512 ks + 32 wave + 8g .. +7 (zero outside).
-  const bool hwork = wg < nh;
-  const int jt = wg % nht, ks = wg / nht;
-  u32x4_t hx = {0u, 0u, 0u, 0u}, ha = {0u, 0u, 0u, 0u};
-  {
-    const int64_t kh = (int64_t)ks * kHSlice + 32 * wave + 8 * g;
-    const int j = 16 * jt + li;
-    const bool kin = hwork && kh < K;
-    const __amdgpu_buffer_rsrc_t xr = rsrc(X, (int64_t)M * K * 2), ar = rsrc(A, (int64_t)r * K * 2);
-    hx = __builtin_amdgcn_raw_buffer_load_b128(xr, kin && li < M ? (uint32_t)((li * K + kh) * 2) : 0x80000000u, 0, 0);
-    ha = __builtin_amdgcn_raw_buffer_load_b128(ar, kin && j < r ? (uint32_t)((j * K + kh) * 2) : 0x80000000u, 0, 0);
-  }
-
-  // Level-pair table: entry e = {q[e & 15], q[e >> 4]} (low nibble = first
-  // weight), copy c at byte 256e + 8c.
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = (tid >> 5) + 32 * i, c = tid & 31;
-    s_tab[e * 32 + c] = make_float2(__uint_as_float(kNF4Bits[e & 15]), __uint_as_float(kNF4Bits[e >> 4]));
-  }
-  if (tid < 256) s_dec[tid] = e4m3_decode((uint32_t)tid);
-  // X columns of the range: staged row R = i*M + m holds X[m][64 kb(i) ..
-  // +63], 16-byte chunk c at c ^ ((m >> 1) & 7); the 16 lanes of one read
-  // (m = 0..15 of one block) then hit 16 distinct bank groups for any M.
-  for (int c = tid; c < nb * M * 8; c += 1024) {
-    const int ch = c & 7, R = c >> 3, i = R / M, m = R - i * M;
-    const int64_t kb = (b0 + i) % nkb;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(X + (int64_t)m * K + kb * kBlock + 8 * ch);
-    *reinterpret_cast<u32x4_t *>(s_x + R * 128 + ((ch ^ ((m >> 1) & 7)) << 4)) = v;
-  }
-  if (tid < 8) *reinterpret_cast<u32x4_t *>(lds + kZeroOff + 16 * tid) = u32x4_t{0u, 0u, 0u, 0u};
-  // group constants of the touched row groups: s_ga[t] = group_amax[gfirst*nkb + t]
-  {
-    const int64_t gi0 = (b0 / nkb) * nkb, nga = (int64_t)seg * nkb;
-    for (int64_t t = tid; t < nga; t += 1024) s_ga[t] = gi0 + t < w.ng ? w.group_amax[gi0 + t] : 0.f;
-  }
-
-  // Per-lane streams (32-bit offsets): 8 code bytes of block kb of row n, the
-  // block's scale code and its group constant, 8 blocks ahead.  Rows past N
-  // read zero and give partial sums that are never used; loads past the
-  // workgroup's last block take an out-of-range offset (no memory traffic).
+  // Global loads go out first: the first pairs of codes and scale words
+  // (the stream the loop waits on), then the X columns and group constants
+  // the range stages into LDS, the H slice operands and the scalar offset.
+  // The table fill runs while they are in flight.
+  constexpr uint32_t kOut = 0x80000000u;
+  // Per-lane streams (32-bit offsets): the codes of a pair of blocks of row
+  // n, a word of four scale codes per two pairs, and the blocks' group
+  // constants.  Rows past N read zero and give partial sums that are never
+  // used; loads past the workgroup's last block take an out-of-range offset
+  // (no memory traffic).
   const __amdgpu_buffer_rsrc_t crs = rsrc(w.packed, N * kb2);
   const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code, w.nb);
-  constexpr uint32_t kOut = 0x80000000u;
-  const float offset = *w.offset;
   const int nrow = 16 * wave + li;  // row within the group
-  const int64_t gfirst = b0 / nkb;
-  const int nkb32 = (int)nkb;
+  const int nkb32 = nkb;
   const int hb = g >> 1;  // which block of a pair this lane's codes come from
-  int lkb = (int)(b0 - gfirst * nkb);
+  int lkb = lkb0;
   uint32_t lco = (uint32_t)((gfirst * kGvRows + nrow) * kb2 + lkb * 32 + 16 * g);
   uint32_t lbi = (uint32_t)((gfirst * kGvRows + nrow) * nkb + lkb);
   const uint32_t gstep_c = (uint32_t)(kGvRows * kb2 - nkb * 32), gstep_b = (uint32_t)(kGvRows * nkb - nkb);
@@ -230,6 +204,92 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   sload(1, 4 < nb);
 #pragma unroll
   for (int j = 0; j < kGvP; ++j) load(j, 2 * j < nb);
+
+  // X columns of the range: staged row R = i*M + m holds X[m][64 kb(i) ..
+  // +63], 16-byte chunk c at c ^ ((m >> 1) & 7); the 16 lanes of one read
+  // (m = 0..15 of one block) then hit 16 distinct bank groups for any M.
+  // The LDS plan keeps nb * M * 8 <= kXPer * 1024.
+  const int nxc = nb * M * 8;
+  const __amdgpu_buffer_rsrc_t xrs = rsrc(X, (int64_t)M * K * 2);
+  const uint32_t inv_m = (65536u + (uint32_t)M - 1) / (uint32_t)M;  // R / M = (R inv_m) >> 16 for R < 768, M <= 16
+  // (a wave whose chunks all lie past the end issues no load: the address
+  // unit is the prologue's bottleneck when 16 waves start at once)
+  u32x4_t xv[kXPer];
+#pragma unroll
+  for (int u = 0; u < kXPer; ++u) {
+    const int c = tid + 1024 * u;
+    xv[u] = u32x4_t{0u, 0u, 0u, 0u};
+    if (64 * wave + 1024 * u < nxc) {
+      const int ch = c & 7, R = c >> 3, i = (int)(((uint32_t)R * inv_m) >> 16), m = R - i * M;
+      int kb = lkb0 + i;
+      while (kb >= nkb) kb -= nkb;
+      xv[u] = __builtin_amdgcn_raw_buffer_load_b128(
+          xrs, c < nxc ? (uint32_t)((m * K + kb * kBlock + 8 * ch) * 2) : kOut, 0, 0);
+    }
+  }
+  // group constants of the touched row groups: s_ga[t] = group_amax[gfirst*nkb + t]
+  // (past the last group: zero, from the buffer range)
+  const int64_t gi0 = (int64_t)gfirst * nkb;
+  const int nga = seg * nkb;
+  const __amdgpu_buffer_rsrc_t grs = rsrc(w.group_amax + gi0, (w.ng - gi0) * 4);
+  float gv[kGaPer];
+#pragma unroll
+  for (int u = 0; u < kGaPer; ++u) {
+    const int t = tid + 1024 * u;
+    gv[u] = 0.f;
+    if (64 * wave + 1024 * u < nga)
+      gv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, t < nga ? (uint32_t)t * 4 : kOut, 0, 0));
+  }
+
+  // H slice operands: X rows li < M and A rows 16 jt + li < r at
+  // k = 512 ks + 32 wave + 8g .. +7 (zero outside).
+  const bool hwork = wg < nh;
+  const int jt = wg % nht, ks = wg / nht;
+  u32x4_t hx = {0u, 0u, 0u, 0u}, ha = {0u, 0u, 0u, 0u};
+  if (hwork) {
+    const int64_t kh = (int64_t)ks * kHSlice + 32 * wave + 8 * g;
+    const int j = 16 * jt + li;
+    const bool kin = hwork && kh < K;
+    const __amdgpu_buffer_rsrc_t ar = rsrc(A, (int64_t)r * K * 2);
+    hx = __builtin_amdgcn_raw_buffer_load_b128(xrs, kin && li < M ? (uint32_t)((li * K + kh) * 2) : kOut, 0, 0);
+    ha = __builtin_amdgcn_raw_buffer_load_b128(ar, kin && j < r ? (uint32_t)((j * K + kh) * 2) : kOut, 0, 0);
+  }
+  const float offset = *w.offset;
+
+  // Level-pair table: entry e = {q[e & 15], q[e >> 4]} (low nibble = first
+  // weight), copy c at byte 256e + 8c.  Wave w writes entries 16w .. 16w+15,
+  // so q[e >> 4] is wave-uniform and q[e & 15] one of two constants: no
+  // per-lane loads of the codebook (they would wait behind the loads above).
+  {
+    const float qhi = __uint_as_float(kNF4Bits[wave]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = 16 * wave + 2 * i + (lane >> 5), c = lane & 31;
+      const uint32_t hi_half = 0u - (uint32_t)(lane >> 5);  // all ones for lanes 32..63
+      const float qlo = __uint_as_float((kNF4Bits[2 * i] & ~hi_half) | (kNF4Bits[2 * i + 1] & hi_half));
+      s_tab[e * 32 + c] = make_float2(qlo, qhi);
+    }
+  }
+  if (tid < 256) s_dec[tid] = e4m3_decode((uint32_t)tid);
+  if (tid < 8) *reinterpret_cast<u32x4_t *>(lds + kZeroOff + 16 * tid) = u32x4_t{0u, 0u, 0u, 0u};
+  // this workgroup's partial slot in its first row group: block b lies in
+  // workgroup ((b/4 + 1) G - 1) / (T/4), so the group's first covering
+  // workgroup is that of its block 0 (in later row groups of the range this
+  // workgroup is the first); one 64-bit division, by one thread
+  if (tid == 0)
+    *reinterpret_cast<int *>(lds + kMiscOff) =
+        wg - (int)((((int64_t)gfirst * nkb / 4 + 1) * G - 1) / T4);
+#pragma unroll
+  for (int u = 0; u < kXPer; ++u) {
+    const int c = tid + 1024 * u;
+    const int ch = c & 7, R = c >> 3, m = R - (int)(((uint32_t)R * inv_m) >> 16) * M;
+    if (c < nxc) *reinterpret_cast<u32x4_t *>(s_x + R * 128 + ((ch ^ ((m >> 1) & 7)) << 4)) = xv[u];
+  }
+#pragma unroll
+  for (int u = 0; u < kGaPer; ++u)
+    if (tid + 1024 * u < nga) s_ga[tid + 1024 * u] = gv[u];
+  for (int t = tid + 1024 * kGaPer; t < nga; t += 1024)  // very long rows only
+    s_ga[t] = gi0 + t < w.ng ? w.group_amax[gi0 + t] : 0.f;
   __syncthreads();  // table and X staged
 
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
@@ -256,9 +316,9 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
 
   // partial slot of (row group gr, covering workgroup k = wg - first
   // covering workgroup): [(gr * maxcov + k) * M + m] * 256 + row
-  const int64_t T4 = T / 4;
+  int kslot = *reinterpret_cast<const int *>(lds + kMiscOff);
   int64_t cgr = gfirst;
-  int ckb = (int)(b0 - gfirst * nkb);
+  int ckb = lkb0;
   const int np = nb >> 1;
   f32x4_t acc = zero;
   // Pairs past the end (the loop runs whole rounds of kGvP) read zero codes,
@@ -296,8 +356,8 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
       }
       cbi += 2;
       if (ip < np && ((ckb += 2) == nkb32 || ip == np - 1)) {  // leaving a row group: partial out
-        const int64_t wlo = ((cgr * nkb / 4 + 1) * G - 1) / T4;
-        float *pp = part + ((cgr * maxcov + (wg - wlo)) * M) * kGvRows + nrow;
+        float *pp = part + ((cgr * maxcov + kslot) * M) * kGvRows + nrow;
+        kslot = 0;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           if (4 * g + v < M) pp[(4 * g + v) * kGvRows] = acc[v];
@@ -334,15 +394,16 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
 // One workgroup per (row group, m), one thread per row n:
 // y[m][n] = bf16(sum of the group's partials (workgroup order) +
 // sum_j bf16(s H[m][j]) B[n][j]), H[m][j] summed over its slices in order.
-// The group's rows of B (contiguous, 256 r bf16) are staged in LDS with
-// coalesced loads; the kernel is kept small (it runs once per call, from a
-// cold instruction cache).
+// Every global load (partials, H slices, the group's B rows) is issued
+// before any of them is used, so the kernel waits for memory once; B rows
+// (contiguous, 256 r bf16) then go through LDS.
 template <bool kVecB>  // r % 8 == 0: B staged by 16-byte loads
 __global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const float *__restrict__ hpart, int nslices,
                                                      const float *__restrict__ part, const uint16_t *__restrict__ Bl,
                                                      int r, int RP, float s, int64_t T, int G, int maxcov,
                                                      bool sparse, int64_t nkb, uint16_t *__restrict__ Y,
                                                      float *__restrict__ H_out) {
+  constexpr int kPv = 8, kHv = 16, kBv = kGvRows * 128 / 8 / 256;  // loads in flight per thread
   __shared__ float s_h[128];                             // bf16(s H[m][j]) as floats
   __shared__ __align__(16) uint16_t s_b[kGvRows * 128];  // B rows of the group, row stride r
   const int tid = threadIdx.x, m = blockIdx.y;
@@ -350,42 +411,52 @@ __global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const flo
   const int64_t n = gr * kGvRows + tid;
   const int64_t rows = std::min<int64_t>(kGvRows, N - gr * kGvRows);
   const uint16_t *bsrc = Bl + gr * kGvRows * r;
+  // covering workgroups of the group: workgroup q's range starts at block
+  // 4 floor(q (T/4) / G), so block b lies in workgroup ((b/4 + 1) G - 1) / (T/4)
+  const int64_t T4 = T / 4;
+  const int64_t wlo = ((gr * nkb / 4 + 1) * G - 1) / T4, whi = ((((gr + 1) * nkb - 1) / 4 + 1) * G - 1) / T4;
+  const int nc = (int)(whi - wlo + 1);
+  const float *p = part + ((gr * maxcov) * M + m) * kGvRows + tid;
+  const bool live = n < N && !sparse;
+  float pv[kPv];
+#pragma unroll
+  for (int k = 0; k < kPv; ++k) pv[k] = live && k < nc ? p[(int64_t)k * M * kGvRows] : 0.f;
+  float hv[kHv];
+#pragma unroll
+  for (int q = 0; q < kHv; ++q) hv[q] = tid < r && q < nslices ? hpart[((int64_t)q * M + m) * RP + tid] : 0.f;
+  u32x4_t bv[kBv];
+  const int nch = kVecB ? (int)(rows * r / 8) : 0;
   if constexpr (kVecB) {
-    const int nch = (int)(rows * r / 8);
-    for (int c = tid; c < nch; c += 256)
-      *reinterpret_cast<u32x4_t *>(s_b + 8 * c) = *reinterpret_cast<const u32x4_t *>(bsrc + 8 * c);
-  } else {
-    for (int c = tid; c < rows * r; c += 256) s_b[c] = bsrc[c];
-  }
-  if (tid < r) {  // H[m][tid], slice order, 8 loads in flight
-    float h = 0.f;
-    for (int q0 = 0; q0 < nslices; q0 += 8) {
-      float v[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = q0 + q < nslices ? hpart[((int64_t)(q0 + q) * M + m) * RP + tid] : 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) h += v[q];
+    for (int u = 0; u < kBv; ++u) {
+      const int c = tid + 256 * u;
+      bv[u] = c < nch ? *reinterpret_cast<const u32x4_t *>(bsrc + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
     }
+  }
+
+  if (tid < r) {  // H[m][tid], slice order
+    float h = 0.f;
+#pragma unroll
+    for (int q = 0; q < kHv; ++q) h += hv[q];
+    for (int q = kHv; q < nslices; ++q) h += hpart[((int64_t)q * M + m) * RP + tid];
     if (gr == 0 && H_out) H_out[(int64_t)m * r + tid] = h;
     s_h[tid] = bf16_to_f32(f32_to_bf16_bits(__fmul_rn(s, h)));
   }
-  // partial sums of the covering workgroups, workgroup order; workgroup q's
-  // range starts at block 4 floor(q (T/4) / G), so block b lies in
-  // workgroup ((b/4 + 1) G - 1) / (T/4)
-  const int64_t T4 = T / 4;
-  const int64_t wlo = ((gr * nkb / 4 + 1) * G - 1) / T4, whi = ((((gr + 1) * nkb - 1) / 4 + 1) * G - 1) / T4;
-  const float *p = part + ((gr * maxcov) * M + m) * kGvRows + tid;
+  if constexpr (kVecB) {
+#pragma unroll
+    for (int u = 0; u < kBv; ++u) {
+      const int c = tid + 256 * u;
+      if (c < nch) *reinterpret_cast<u32x4_t *>(s_b + 8 * c) = bv[u];
+    }
+  } else {
+    for (int c = tid; c < rows * r; c += 256) s_b[c] = bsrc[c];
+  }
   float y = 0.f;
   if (n < N) {
-    if (!sparse) {  // 4 loads in flight
-      const int nc = (int)(whi - wlo + 1);
-      for (int k0 = 0; k0 < nc; k0 += 4) {
-        float v[4];
+    if (!sparse) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = k0 + k < nc ? p[(int64_t)(k0 + k) * M * kGvRows] : 0.f;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) y += v[k];
-      }
+      for (int k = 0; k < kPv; ++k) y += pv[k];
+      for (int k = kPv; k < nc; ++k) y += p[(int64_t)k * M * kGvRows];
     } else {
       for (int64_t q = wlo; q <= whi; ++q) {
         // an empty range (more workgroups than 4-block units) wrote nothing
@@ -421,8 +492,9 @@ hipError_t launch_fwd_small(const Nf4View &w, const uint16_t *X, int64_t M, cons
   char *base = static_cast<char *>(ws);
   float *hpart = reinterpret_cast<float *>(base + l.h_off);
   float *part = reinterpret_cast<float *>(base + l.part_off);
+  const int T4 = (int)(p.T / 4);
   QLORA_LAUNCH("k_gemv_nf4", k_gemv_nf4, dim3((unsigned)p.G), dim3(1024), 0, st, w, X, (int)M, A, r, RP, hpart, part,
-               p.T, p.G, p.seg, p.maxcov, p.nh, p.nht, p.xoff);
+               T4, p.G, T4 / p.G, T4 % p.G, p.seg, p.maxcov, p.nh, p.nht, p.xoff);
   if (r % 8 == 0)
     QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<true>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), 0, st, w.n, (int)M,
                  hpart, p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.maxcov, p.sparse, p.nkb, Y, H_out);
