@@ -89,9 +89,25 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
 // w_hat = bf16_rne(fp32(q[code] * s)); every NF4 consumer goes through
 // dequant_word, so the fused kernels see exactly the standalone dequant.
 // ---------------------------------------------------------------------------
+// Level c (0..15) selected in registers by the bits of c: a per-lane index
+// into the constant array would become a memory load whose wait holds up
+// the copies a kernel issues next.
+__device__ __forceinline__ uint32_t nf4_level_bits(uint32_t c) {
+  uint32_t v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = kNF4Bits[j];
+#pragma unroll
+  for (int b = 0, n = 8; b < 4; ++b, n >>= 1) {
+    const uint32_t m = 0u - ((c >> b) & 1u);
+#pragma unroll
+    for (int j = 0; j < n; ++j) v[j] = (v[2 * j] & ~m) | (v[2 * j + 1] & m);
+  }
+  return v[0];
+}
+
 __device__ __forceinline__ void fill_pair_table(float2 *table, int tid, int nthreads) {
   for (int e = tid; e < 256; e += nthreads)
-    table[e] = make_float2(__uint_as_float(kNF4Bits[e & 15]), __uint_as_float(kNF4Bits[e >> 4]));
+    table[e] = make_float2(__uint_as_float(nf4_level_bits(e & 15)), __uint_as_float(nf4_level_bits(e >> 4)));
 }
 
 // Eight codes (one packed dword) -> eight bf16 weights in four dwords.
