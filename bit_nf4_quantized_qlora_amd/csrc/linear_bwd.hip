@@ -8,7 +8,10 @@
 //   dX = dY W_hat + G A    (k_bwd_dx_nf4 in nf4_tile.hip; k_bwd_dx below when
 //                           n % 64 != 0)
 //   dB = s dY^T H          (k_tn_splitk on dY and (sH)^T)
-//   dA = G^T X             (k_tn_splitk on X and G^T)
+//   dA = G^T X             (k_tn_splitk on X and G^T; one launch with dB's)
+// The small layout copies (B^T, A^T, (sH)^T), the tile kernel's block-scale
+// table and the partial reductions run as jobs.hip launches, several jobs
+// per launch.
 //
 // k_bwd_dx, the general fallback, contracts over n, the row index of W, by
 // laying the dequantized tile into LDS transposed: each thread expands one
@@ -138,7 +141,7 @@ struct BwdWs {
   int RP;
   int64_t Mp;
   SplitPlan sp_h, sp_g, sp_b, sp_a;
-  size_t part_off, h_off, sht_off, bt_off, at_off, gb_off, gt_off, scale_off, total;
+  size_t part_off, parta_off, h_off, sht_off, bt_off, at_off, gb_off, gt_off, scale_off, total;
 };
 
 BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, int r) {
@@ -149,9 +152,11 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, int r) {
   l.sp_g = plan_split(ceil_div(M, 64), ceil_div(N, 64));
   l.sp_b = plan_split(ceil_div(N, 64), ceil_div(M, 64));
   l.sp_a = plan_split(ceil_div(K, 64), ceil_div(M, 64));
-  size_t part = std::max({(size_t)l.sp_h.splits * M * l.RP, (size_t)l.sp_g.splits * M * l.RP,
-                          (size_t)l.sp_b.splits * l.RP * N, (size_t)l.sp_a.splits * l.RP * K}) *
-                sizeof(float);
+  // one partials region: H's or G's split partials, later dB's and dA's side by side
+  l.parta_off = align_up((size_t)l.sp_b.splits * l.RP * N * sizeof(float), 256);
+  size_t part = std::max({(size_t)l.sp_h.splits * M * l.RP * sizeof(float),
+                          (size_t)l.sp_g.splits * M * l.RP * sizeof(float),
+                          l.parta_off + (size_t)l.sp_a.splits * l.RP * K * sizeof(float)});
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -206,25 +211,37 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     QLORA_TRY(launch_reduce_rows(part, l.sp_h.splits, M, RP, r, 1.f, Hw, nullptr, nullptr, 0, s));
     H = Hw;
   }
-  QLORA_TRY(launch_scale_transpose_f32(H, M, r, a.s, sHt, RP, l.Mp, s));
-  QLORA_TRY(launch_transpose_pad(B, N, r, Bt, RP, N, s));  // Bt [RP][N]
-  QLORA_TRY(launch_transpose_pad(A, r, K, At, K, RP, s));  // At [K][RP]
+  // layouts: sHt = bf16(s H)^T [RP][Mp], Bt [RP][N], At [K][RP]; and the dX
+  // tile kernel's block-scale table -- one launch
+  const bool tiles = dX != nullptr && bwd_tiles_supported(N, K);
+  float *scales = reinterpret_cast<float *>(base + l.scale_off);
+  SmallJob prep[kMaxJobs];
+  int np = 0;
+  prep[np++] = job_scale_transpose(H, M, r, a.s, sHt, RP, l.Mp);
+  prep[np++] = job_transpose_pad(B, N, r, Bt, RP, N);
+  prep[np++] = job_transpose_pad(A, r, K, At, K, RP);
+  if (tiles) prep[np++] = job_scales_bwd(a.w, scales);
+  QLORA_TRY(launch_jobs("k_prep_bwd", prep, np, s));
   // G = s dY B -> Gb [M][RP], Gt [RP][Mp]
   QLORA_TRY(launch_nt_splitk(dY, M, Bt, RP, RP, N, N, l.sp_g, part, s));
   QLORA_TRY(launch_reduce_rows(part, l.sp_g.splits, M, RP, r, a.s, nullptr, Gb, Gt, l.Mp, s));
   if (dX != nullptr) {
-    if (bwd_tiles_supported(N, K)) {
-      QLORA_TRY(launch_bwd_dx_tiles(a.w, reinterpret_cast<float *>(base + l.scale_off), dY, M, At, RP, Gb, dX, s));
+    if (tiles) {
+      QLORA_TRY(launch_bwd_dx_tiles(a.w, scales, dY, M, At, RP, Gb, dX, s));
     } else {  // ragged n: the general 128 x 128 kernel
       const dim3 grid((unsigned)ceil_div(K, DBK), (unsigned)ceil_div(M, DBM));
       QLORA_LAUNCH("k_bwd_dx", k_bwd_dx, grid, dim3(256), 0, s, a.w, dY, M, At, Gb, RP, dX);
     }
     QLORA_TRY(hipGetLastError());
   }
-  QLORA_TRY(launch_tn_splitk(dY, M, N, sHt, l.Mp, RP, l.sp_b, true, part, s));
-  QLORA_TRY(launch_reduce_cols(part, l.sp_b.splits, N, RP, r, true, dB, s));
-  QLORA_TRY(launch_tn_splitk(X, M, K, Gt, l.Mp, RP, l.sp_a, false, part, s));
-  QLORA_TRY(launch_reduce_cols(part, l.sp_a.splits, K, RP, r, false, dA, s));
+  // dB = dY^T sH and dA = G^T X: one launch of split partials, one of their
+  // fixed-order reductions
+  float *part_b = part, *part_a = reinterpret_cast<float *>(base + l.part_off + l.parta_off);
+  QLORA_TRY(launch_tn_pair(TnProblem{dY, N, sHt, l.Mp, l.sp_b, true, part_b},
+                           TnProblem{X, K, Gt, l.Mp, l.sp_a, false, part_a}, M, RP, s));
+  const SmallJob red[2] = {job_reduce_cols(part_b, l.sp_b.splits, N, RP, r, true, dB),
+                           job_reduce_cols(part_a, l.sp_a.splits, K, RP, r, false, dA)};
+  QLORA_TRY(launch_jobs("k_reduce_grads", red, 2, s));
 #undef QLORA_TRY
   return hipSuccess;
 }

@@ -4,9 +4,10 @@
 // (alpha/r) X L_1 L_2, with the weights expanded from NF4 to BF16 on every
 // use ("QLoRA, explained." step 4).
 //
-//   1. H = X A^T (k_nt_splitk + reduction): fp32 H (optional output) and
+//   1. H = X A^T (k_nt_splitk, then its reduction in one launch with the
+//      tile kernel's block-scale table): fp32 H (optional output) and
 //      bf16(s*H) for the LoRA term.
-//   2. k_scales_fwd + k_fwd_nf4 (nf4_tile.hip): Y = X W_hat^T + sH B^T on
+//   2. k_fwd_nf4 (nf4_tile.hip): Y = X W_hat^T + sH B^T on
 //      256x256 tiles, the NF4 codes expanded in registers straight into MFMA
 //      operands and the LoRA up-projection added on the same accumulators;
 //      Y is rounded to bf16 once.
@@ -51,7 +52,10 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   float *scales = reinterpret_cast<float *>(base + l.scale_off);
   hipError_t e = launch_nt_splitk(X, M, A, a.r, l.RP, K, K, l.sp, part, s);
   if (e != hipSuccess) return e;
-  e = launch_reduce_rows(part, l.sp.splits, M, l.RP, a.r, a.s, H_out, sH, nullptr, 0, s);
+  // H's reduction and the tile kernel's scale table in one launch
+  const SmallJob jobs[2] = {job_reduce_rows(part, l.sp.splits, M, l.RP, a.r, a.s, H_out, sH, nullptr, 0),
+                            job_scales_fwd(a.w, scales)};
+  e = launch_jobs("k_prep_fwd", jobs, 2, s);
   if (e != hipSuccess) return e;
   return launch_fwd_tiles(a.w, scales, X, M, B, a.r, l.RP, sH, Y, s);
 }

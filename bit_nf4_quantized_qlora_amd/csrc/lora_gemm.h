@@ -73,4 +73,53 @@ hipError_t launch_scale_transpose_f32(const float *H, int64_t M, int r, float sc
                                       int64_t ldo, hipStream_t s);
 hipError_t launch_fill_zero_u16(uint16_t *p, int64_t n, hipStream_t s);
 
+// Both transposed products of the backward in one launch (consecutive block
+// ranges): problem q computes partials of Qt_q^T-weighted sums of P_q over M,
+// exactly as launch_tn_splitk does for it alone.  Falls back to two launches
+// when a problem cannot take the DMA kernel.
+struct TnProblem {
+  const uint16_t *P;  // [M][D]
+  int64_t D;
+  const uint16_t *Qt;  // [RP][ldq]
+  int64_t ldq;
+  SplitPlan sp;
+  bool rows_out;
+  float *part;
+};
+hipError_t launch_tn_pair(const TnProblem &p0, const TnProblem &p1, int64_t M, int RP, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Small elementwise jobs (jobs.hip): layout copies, split-partial reductions
+// and the tile kernels' block-scale tables.  Up to kMaxJobs independent jobs
+// run as one launch over consecutive block ranges, which saves a launch ramp
+// per job; each job is the elementwise kernel the launch_* function above
+// of the same name describes.
+// ---------------------------------------------------------------------------
+enum JobKind : int {
+  kJobTransposePad,
+  kJobScaleTranspose,
+  kJobReduceRows,
+  kJobReduceCols,
+  kJobScalesFwd,
+  kJobScalesBwd,
+};
+struct SmallJob {
+  int kind = 0;
+  int64_t count = 0;  // elements (one thread each)
+  const void *in = nullptr;
+  void *out = nullptr, *out2 = nullptr, *out3 = nullptr;
+  int64_t a = 0, b = 0, c = 0, d = 0;
+  int i = 0, j = 0;
+  float f = 0.f;
+  Nf4View w{};
+};
+constexpr int kMaxJobs = 4;
+hipError_t launch_jobs(const char *name, const SmallJob *jobs, int n, hipStream_t s);
+SmallJob job_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
+                           int64_t ldo);
+SmallJob job_scale_transpose(const float *H, int64_t M, int r, float scale, uint16_t *out, int RP, int64_t ldo);
+SmallJob job_reduce_rows(const float *part, int S, int64_t R, int RP, int r, float scale, float *out_f32,
+                         uint16_t *out_b, uint16_t *out_bt, int64_t ldt);
+SmallJob job_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool rows_out, uint16_t *out);
+
 }  // namespace qlora

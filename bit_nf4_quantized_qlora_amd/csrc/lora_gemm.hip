@@ -232,19 +232,40 @@ __global__ __launch_bounds__(256) void k_nt_dma(const uint16_t *__restrict__ P, 
 // lanes 4q + i/4 (q = 0..3), so lanes addressing rows m + q, columns 4(j & 3)
 // hand lane i four consecutive m of column i; two reads give the fragment.
 // rows_out == true: part[s][d][j] (reduced into [D][r]); else part[s][j][d].
+// One transposed product of a launch: see TnProblem.
+struct TnArgs {
+  const uint16_t *P;
+  int64_t D;
+  const uint16_t *Qt;
+  int64_t ldq;
+  int steps_per_split, tiles;
+  bool rows_out;
+  float *part;
+};
+
+// Blocks [0, nb0) take problem a0 (tile b % tiles, split b / tiles), the
+// rest problem a1.
 template <int TJ>
-__global__ __launch_bounds__(256) void k_tn_dma(const uint16_t *__restrict__ P, int64_t M, int64_t D,
-                                                const uint16_t *__restrict__ Qt, int64_t ldq, int steps_per_split,
-                                                bool rows_out, float *__restrict__ part) {
+__global__ __launch_bounds__(256) void k_tn_dma(TnArgs a0, TnArgs a1, int nb0, int64_t M) {
   constexpr int RP = 16 * TJ, NQ = RP / 32, NV = 2 + NQ;
   typedef short s16x4_t __attribute__((ext_vector_type(4)));
   __shared__ __align__(16) uint16_t P0[64 * 64], P1[64 * 64], P2[64 * 64], P3[64 * 64];
   __shared__ __align__(16) uint16_t Q0[RP * 64], Q1[RP * 64], Q2[RP * 64], Q3[RP * 64];
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t d0 = (int64_t)blockIdx.x * 64;
+  const bool second = (int)blockIdx.x >= nb0;
+  const TnArgs &ta = second ? a1 : a0;
+  const int bl = second ? (int)blockIdx.x - nb0 : (int)blockIdx.x;
+  const uint16_t *__restrict__ P = ta.P;
+  const uint16_t *__restrict__ Qt = ta.Qt;
+  const int64_t D = ta.D, ldq = ta.ldq;
+  const int steps_per_split = ta.steps_per_split;
+  const bool rows_out = ta.rows_out;
+  float *__restrict__ part = ta.part;
+  const int split = bl / ta.tiles;
+  const int64_t d0 = (int64_t)(bl - split * ta.tiles) * 64;
   const int64_t nsteps = ceil_div_d(M, 64);
-  const int64_t s0 = (int64_t)blockIdx.y * steps_per_split;
+  const int64_t s0 = (int64_t)split * steps_per_split;
   const int64_t s1 = min<int64_t>(nsteps, s0 + steps_per_split);
   auto pbuf = [&](auto B) -> uint16_t * {
     constexpr int b = decltype(B)::value & 3;
@@ -302,78 +323,17 @@ __global__ __launch_bounds__(256) void k_tn_dma(const uint16_t *__restrict__ P, 
   const int64_t d = d0 + 16 * wave + li;
   if (d < D) {
     if (rows_out) {
-      float *out = part + ((size_t)blockIdx.y * D + d) * RP;
+      float *out = part + ((size_t)split * D + d) * RP;
 #pragma unroll
       for (int jt = 0; jt < TJ; ++jt) *reinterpret_cast<f32x4_t *>(out + 16 * jt + 4 * g) = acc[jt];
     } else {
-      float *out = part + (size_t)blockIdx.y * RP * D;
+      float *out = part + (size_t)split * RP * D;
 #pragma unroll
       for (int jt = 0; jt < TJ; ++jt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) out[(int64_t)(16 * jt + 4 * g + v) * D + d] = acc[jt][v];
     }
   }
-}
-
-// Rows form: part [S][R][RP] -> v = sum_s part[s][i][j].
-//   out_f32 [R][r]   = v            (j < r)
-//   out_b   [R][RP]  = bf16(scale*v)  (all j; columns >= r are zero)
-//   out_bt  [RP][ldt] = bf16(scale*v) transposed; columns i >= R zero-filled
-__global__ __launch_bounds__(256) void k_reduce_rows(const float *__restrict__ part, int S, int64_t R, int RP,
-                                                     int r, float scale, float *__restrict__ out_f32,
-                                                     uint16_t *__restrict__ out_b, uint16_t *__restrict__ out_bt,
-                                                     int64_t ldt) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t Rt = out_bt ? ldt : R;
-  if (idx >= Rt * RP) return;
-  const int64_t i = idx / RP;
-  const int j = (int)(idx % RP);
-  float v = 0.f;
-  if (i < R) {
-    for (int s = 0; s < S; ++s) v += part[(size_t)s * R * RP + idx];
-    if (out_f32 && j < r) out_f32[i * r + j] = v;
-    if (out_b) out_b[idx] = f32_to_bf16_bits(scale * v);
-  }
-  if (out_bt) out_bt[(int64_t)j * ldt + i] = i < R ? f32_to_bf16_bits(scale * v) : (uint16_t)0;
-}
-
-// Transposed-product partials -> bf16, summed over splits in a fixed order:
-//   rows_out == false: part [S][RP][D] -> out [r][D]  (dA)
-//   rows_out == true:  part [S][D][RP] -> out [D][r]  (dB)
-// (consecutive threads read consecutive partials in both forms).
-__global__ __launch_bounds__(256) void k_reduce_cols(const float *__restrict__ part, int S, int64_t D, int RP,
-                                                     int r, bool rows_out, uint16_t *__restrict__ out) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)r * D) return;
-  int64_t src;
-  if (rows_out) {
-    src = (idx / r) * RP + idx % r;
-  } else {
-    src = idx;  // j * D + i, j < r
-  }
-  float v = 0.f;
-  for (int s = 0; s < S; ++s) v += part[(size_t)s * RP * D + src];
-  out[idx] = f32_to_bf16_bits(v);
-}
-
-// out [RP][ldo] = in^T for a row-major in [rows][cols] (bf16), zero outside.
-__global__ __launch_bounds__(256) void k_transpose_pad(const uint16_t *__restrict__ in, int64_t rows, int64_t cols,
-                                                       uint16_t *__restrict__ out, int64_t out_rows,
-                                                       int64_t ldo) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= out_rows * ldo) return;
-  const int64_t c = idx / ldo, rr = idx % ldo;  // out[c][rr] = in[rr][c]
-  out[idx] = (c < cols && rr < rows) ? in[rr * cols + c] : (uint16_t)0;
-}
-
-// out [RP][ldo] = bf16(scale * H^T) for H [M][r] fp32, zero outside.
-__global__ __launch_bounds__(256) void k_scale_transpose_f32(const float *__restrict__ H, int64_t M, int r,
-                                                             float scale, uint16_t *__restrict__ out, int RP,
-                                                             int64_t ldo) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)RP * ldo) return;
-  const int64_t j = idx / ldo, m = idx % ldo;
-  out[idx] = (j < r && m < M) ? f32_to_bf16_bits(scale * H[m * r + j]) : (uint16_t)0;
 }
 
 __global__ __launch_bounds__(256) void k_fill_zero_u16(uint16_t *__restrict__ p, int64_t n) {
@@ -424,46 +384,60 @@ hipError_t launch_nt_splitk(const uint16_t *P, int64_t rowsP, const uint16_t *Q,
 
 hipError_t launch_tn_splitk(const uint16_t *P, int64_t M, int64_t D, const uint16_t *Qt, int64_t ldq, int RP,
                             const SplitPlan &sp, bool rows_out, float *part, hipStream_t s) {
-  const dim3 grid((unsigned)ceil_div(D, 64), (unsigned)sp.splits);
   const bool vec_ok = (D % 8) == 0;
   return dispatch_tj(RP, [&](auto tj) {
-    if (vec_ok && ldq % 8 == 0)
-      QLORA_LAUNCH("k_tn_dma", k_tn_dma<decltype(tj)::value>, grid, dim3(256), 0, s, P, M, D, Qt, ldq,
-                   sp.steps_per_split, rows_out, part);
-    else
+    if (vec_ok && ldq % 8 == 0) {
+      const TnArgs a{P, D, Qt, ldq, sp.steps_per_split, (int)ceil_div(D, 64), rows_out, part};
+      const int nb = a.tiles * sp.splits;
+      QLORA_LAUNCH("k_tn_dma", k_tn_dma<decltype(tj)::value>, dim3((unsigned)nb), dim3(256), 0, s, a, a, nb, M);
+    } else {
+      const dim3 grid((unsigned)ceil_div(D, 64), (unsigned)sp.splits);
       QLORA_LAUNCH("k_tn_splitk", k_tn_splitk<decltype(tj)::value>, grid, dim3(256), 0, s, P, M, D, vec_ok, Qt, ldq,
                    sp.steps_per_split, rows_out, part);
+    }
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_tn_pair(const TnProblem &p0, const TnProblem &p1, int64_t M, int RP, hipStream_t s) {
+  auto dma_ok = [](const TnProblem &p) { return p.D % 8 == 0 && p.ldq % 8 == 0; };
+  if (!dma_ok(p0) || !dma_ok(p1)) {
+    hipError_t e = launch_tn_splitk(p0.P, M, p0.D, p0.Qt, p0.ldq, RP, p0.sp, p0.rows_out, p0.part, s);
+    if (e != hipSuccess) return e;
+    return launch_tn_splitk(p1.P, M, p1.D, p1.Qt, p1.ldq, RP, p1.sp, p1.rows_out, p1.part, s);
+  }
+  return dispatch_tj(RP, [&](auto tj) {
+    const TnArgs a0{p0.P, p0.D, p0.Qt, p0.ldq, p0.sp.steps_per_split, (int)ceil_div(p0.D, 64), p0.rows_out, p0.part};
+    const TnArgs a1{p1.P, p1.D, p1.Qt, p1.ldq, p1.sp.steps_per_split, (int)ceil_div(p1.D, 64), p1.rows_out, p1.part};
+    const int nb0 = a0.tiles * p0.sp.splits, nb1 = a1.tiles * p1.sp.splits;
+    QLORA_LAUNCH("k_tn_dma", k_tn_dma<decltype(tj)::value>, dim3((unsigned)(nb0 + nb1)), dim3(256), 0, s, a0, a1, nb0,
+                 M);
     return hipGetLastError();
   });
 }
 
 hipError_t launch_reduce_rows(const float *part, int S, int64_t R, int RP, int r, float scale, float *out_f32,
                               uint16_t *out_b, uint16_t *out_bt, int64_t ldt, hipStream_t s) {
-  const int64_t total = (out_bt ? ldt : R) * RP;
-  QLORA_LAUNCH("k_reduce_rows", k_reduce_rows, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s, part, S, R, RP, r,
-                     scale, out_f32, out_b, out_bt, ldt);
-  return hipGetLastError();
+  const SmallJob j = job_reduce_rows(part, S, R, RP, r, scale, out_f32, out_b, out_bt, ldt);
+  return launch_jobs("k_reduce_rows", &j, 1, s);
 }
 
 hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool rows_out, uint16_t *out,
                               hipStream_t s) {
-  QLORA_LAUNCH("k_reduce_cols", k_reduce_cols, dim3((unsigned)ceil_div((int64_t)r * D, 256)), dim3(256), 0, s, part, S, D,
-                     RP, r, rows_out, out);
-  return hipGetLastError();
+  const SmallJob j = job_reduce_cols(part, S, D, RP, r, rows_out, out);
+  return launch_jobs("k_reduce_cols", &j, 1, s);
 }
 
 hipError_t launch_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
                                 int64_t ldo, hipStream_t s) {
-  QLORA_LAUNCH("k_transpose_pad", k_transpose_pad, dim3((unsigned)ceil_div(out_rows * ldo, 256)), dim3(256), 0, s, in, rows,
-                     cols, out, out_rows, ldo);
-  return hipGetLastError();
+  const SmallJob j = job_transpose_pad(in, rows, cols, out, out_rows, ldo);
+  return launch_jobs("k_transpose_pad", &j, 1, s);
 }
 
 hipError_t launch_scale_transpose_f32(const float *H, int64_t M, int r, float scale, uint16_t *out, int RP,
                                       int64_t ldo, hipStream_t s) {
-  QLORA_LAUNCH("k_scale_transpose_f32", k_scale_transpose_f32, dim3((unsigned)ceil_div((int64_t)RP * ldo, 256)), dim3(256), 0, s, H,
-                     M, r, scale, out, RP, ldo);
-  return hipGetLastError();
+  const SmallJob j = job_scale_transpose(H, M, r, scale, out, RP, ldo);
+  return launch_jobs("k_scale_transpose_f32", &j, 1, s);
 }
 
 hipError_t launch_fill_zero_u16(uint16_t *p, int64_t n, hipStream_t s) {

@@ -30,7 +30,7 @@
 // Every operand streams global -> LDS by buffer loads that write LDS
 // directly (no registers): the B tile one 64-wide step at a time, the packed
 // codes 4 steps at a time (a "super-step": 256 rows x 128 B) together with
-// their precomputed block scales (k_scales_fwd / k_scales_bwd).
+// their precomputed block scales (the scale-table jobs of jobs.hip).
 //
 // LDS: B tiles Bs0/Bs1 (2 x 32 KB), code tiles Wc0/Wc1 (2 x 32 KB), scale
 // tiles Sc0/Sc1 (2 x 4 KB), pair table 2 KB.  Swizzles for 64 banks (256 B
@@ -72,49 +72,8 @@
 namespace qlora {
 namespace {
 
-constexpr int TO = 256, TM = 256;  // tile: o rows x m rows
-constexpr int kSup = 4;            // steps per staged code chunk
-
-__host__ __device__ inline int64_t fwd_nsup(int64_t k) { return (k / kBlock + kSup - 1) / kSup; }
-__host__ __device__ inline int64_t bwd_nsup(int64_t n) { return (n + TO - 1) / TO; }
-
-// Forward scale table: for weight tile to (rows 256to ..) and super-step sp
-// (blocks 4sp .. 4sp+3 of each row) one contiguous 4 KB run,
-// Sp[((to*nsup + sp)*256 + row)*4 + j]; rows past n and blocks past k/64 hold
-// 0.  block_scale is the dequantization's own (bit-identical).
-__global__ __launch_bounds__(256) void k_scales_fwd(Nf4View w, int64_t nsup, int64_t total, float *__restrict__ Sp) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;
-  const int64_t q = t >> 8, to = q / nsup, sp = q - to * nsup;
-  const int64_t n = to * TO + (t & 255), nkb = w.k / kBlock;
-  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-  if (n < w.n) {
-    const float off = *w.offset;
-#pragma unroll
-    for (int j = 0; j < kSup; ++j) {
-      const int64_t kb = kSup * sp + j, b = n * nkb + kb;
-      if (kb < nkb) v[j] = block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
-    }
-  }
-  *reinterpret_cast<f32x4_t *>(Sp + 4 * t) = v;
-}
-
-// Backward scale table: for column tile tk (k-blocks 4tk .. 4tk+3) and
-// super-step sp (weight rows 256sp .. 256sp+255) one contiguous 4 KB run,
-// Sp[((tk*nsup + sp)*4 + blk)*256 + row]; rows past n and blocks past k/64
-// hold 0.
-__global__ __launch_bounds__(256) void k_scales_bwd(Nf4View w, int64_t nsup, int64_t total, float *__restrict__ Sp) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= total) return;
-  const int64_t q = t >> 10, tk = q / nsup, sp = q - tk * nsup;
-  const int64_t n = sp * TO + (t & 255), kb = tk * 4 + ((t >> 8) & 3), nkb = w.k / kBlock;
-  float v = 0.f;
-  if (n < w.n && kb < nkb) {
-    const int64_t b = n * nkb + kb;
-    v = block_scale(w.scale_code[b], w.group_amax[b / kGroup], *w.offset);
-  }
-  Sp[t] = v;
-}
+constexpr int TO = kTileRows, TM = 256;  // tile: o rows x m rows
+constexpr int kSup = kTileSup;           // steps per staged code chunk
 
 // Output through LDS, once the main loop has drained (every copy landed,
 // all waves past a barrier).  acc[rt][ct][v] = C[o][m] with o = ow + 16rt +
@@ -192,7 +151,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   const int64_t N = w.n, K = w.k;
   const int64_t NO = kBwd ? K : N, NC = kBwd ? N : K;  // output width, contraction length
   const int64_t nk = NC / kBlock;                      // 64-wide steps
-  const int64_t nsup = kBwd ? bwd_nsup(N) : fwd_nsup(K);
+  const int64_t nsup = kBwd ? tile_bwd_nsup(N) : tile_fwd_nsup(K);
   const int64_t nk8 = ceil_div_d(nk, 8) * 8;  // steps run: whole 8-step rounds
   fill_pair_table(s_pair, tid, 256);
 
@@ -491,8 +450,8 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
 }  // namespace
 
 size_t tile_scales_bytes(int64_t n, int64_t k) {
-  const size_t f = (size_t)ceil_div(n, TO) * fwd_nsup(k) * 256 * kSup;
-  const size_t b = (size_t)ceil_div(k, TO) * bwd_nsup(n) * 256 * kSup;
+  const size_t f = (size_t)ceil_div(n, TO) * tile_fwd_nsup(k) * 256 * kSup;
+  const size_t b = (size_t)ceil_div(k, TO) * tile_bwd_nsup(n) * 256 * kSup;
   return std::max(f, b) * sizeof(float);
 }
 
@@ -500,10 +459,7 @@ bool bwd_tiles_supported(int64_t n, int64_t k) { return n % 64 == 0 && n * (k / 
 
 hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, int64_t M, const uint16_t *Bl, int r,
                             int RP, const uint16_t *sH, uint16_t *Y, hipStream_t s) {
-  const int64_t nsup = fwd_nsup(w.k);
   const int tiles_o = (int)ceil_div(w.n, TO), tiles_m = (int)ceil_div(M, TM);
-  const int64_t total = (int64_t)tiles_o * nsup * 256;
-  QLORA_LAUNCH("k_scales_fwd", k_scales_fwd, dim3((unsigned)(total / 256)), dim3(256), 0, s, w, nsup, total, scales);
   QLORA_LAUNCH("k_fwd_nf4", k_nf4_tile<false>, dim3((unsigned)(tiles_o * tiles_m)), dim3(256), 0, s, w, scales, X,
                M, Bl, r, RP, sH, Y, tiles_o);
   return hipGetLastError();
@@ -511,10 +467,7 @@ hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, 
 
 hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
                                int RP, const uint16_t *Gb, uint16_t *dX, hipStream_t s) {
-  const int64_t nsup = bwd_nsup(w.n);
   const int tiles_o = (int)ceil_div(w.k, TO), tiles_m = (int)ceil_div(M, TM);
-  const int64_t total = (int64_t)tiles_o * nsup * 1024;
-  QLORA_LAUNCH("k_scales_bwd", k_scales_bwd, dim3((unsigned)(total / 256)), dim3(256), 0, s, w, nsup, total, scales);
   QLORA_LAUNCH("k_bwd_dx_nf4", k_nf4_tile<true>, dim3((unsigned)(tiles_o * tiles_m)), dim3(256), 0, s, w, scales,
                dY, M, At, RP, RP, Gb, dX, tiles_o);
   return hipGetLastError();
