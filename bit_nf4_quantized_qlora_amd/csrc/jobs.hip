@@ -16,37 +16,72 @@ struct SmallJobs {
   int n;
 };
 
-// out [out_rows][ldo] = in^T for a row-major in [rows][cols] (bf16), zero outside.
-__device__ __forceinline__ void run_transpose_pad(const SmallJob &j, int64_t idx) {
-  const uint16_t *in = static_cast<const uint16_t *>(j.in);
-  const int64_t rows = j.a, cols = j.b, ldo = j.d;
-  const int64_t c = idx / ldo, rr = idx - c * ldo;  // out[c][rr] = in[rr][c]
-  static_cast<uint16_t *>(j.out)[idx] = (c < cols && rr < rows) ? in[rr * cols + c] : (uint16_t)0;
+// Index arithmetic is 32-bit (every job's element count is below 2^31, which
+// launch_jobs checks): a 64-bit division per element costs more than the
+// element's memory traffic.
+
+// Tiled transpose, one 256-thread block per 64 x 64 tile of the output:
+// out[c][rr] = conv(in[rr][c]) for rr < rows, c < cols, zero elsewhere in
+// out [out_rows][ldo]; conv copies bf16, or rounds scale * x for fp32 input
+// (j.i == 1).  Each wave instruction reads 64 consecutive elements of one
+// input row and writes 64 consecutive elements of one output row; the tile
+// turns in LDS (row stride 65, so the column reads hit distinct banks).
+__device__ __forceinline__ void run_transpose(const SmallJob &j, uint32_t idx, uint16_t (*t)[65]) {
+  const uint32_t tile = idx >> 8, tid = idx & 255;
+  const int64_t rows = j.a, cols = j.b, out_rows = j.c, ldo = j.d;
+  const uint32_t tiles_rr = (uint32_t)((ldo + 63) / 64);
+  const uint32_t tc = tile / tiles_rr, tr = tile - tc * tiles_rr;
+  const int64_t c0 = (int64_t)tc * 64, rr0 = (int64_t)tr * 64;
+  const int col = tid & 63;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = (int)(tid >> 6) + 4 * e;
+    const int64_t rr = rr0 + row, c = c0 + col;
+    uint16_t v = 0;
+    if (rr < rows && c < cols)
+      v = j.i ? f32_to_bf16_bits(j.f * static_cast<const float *>(j.in)[rr * cols + c])
+              : static_cast<const uint16_t *>(j.in)[rr * cols + c];
+    t[row][col] = v;
+  }
+  __syncthreads();
+  uint16_t *out = static_cast<uint16_t *>(j.out);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int oc = (int)(tid >> 6) + 4 * e;
+    const int64_t c = c0 + oc, rr = rr0 + col;
+    if (c < out_rows && rr < ldo) out[c * ldo + rr] = t[col][oc];
+  }
 }
 
-// out [RP][ldo] = bf16(scale * H^T) for H [M][r] fp32, zero outside.
-__device__ __forceinline__ void run_scale_transpose(const SmallJob &j, int64_t idx) {
-  const float *H = static_cast<const float *>(j.in);
-  const int64_t M = j.a, ldo = j.d;
-  const int r = j.i;
-  const int64_t jj = idx / ldo, m = idx - jj * ldo;
-  static_cast<uint16_t *>(j.out)[idx] = (jj < r && m < M) ? f32_to_bf16_bits(j.f * H[m * r + jj]) : (uint16_t)0;
+// Sum over s < S of part[s * stride + src], in order of s: the first kSumBatch
+// loads are issued together, so the sum waits for memory once.
+constexpr int kSumBatch = 8;
+__device__ __forceinline__ float sum_splits(const float *part, int S, size_t stride, size_t src) {
+  float v[kSumBatch];
+#pragma unroll
+  for (int s = 0; s < kSumBatch; ++s) v[s] = s < S ? part[s * stride + src] : 0.f;
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < kSumBatch; ++s) acc += v[s];
+  for (int s = kSumBatch; s < S; ++s) acc += part[s * stride + src];
+  return acc;
 }
 
 // Rows form: part [S][R][RP] -> v = sum_s part[s][i][jj] (s in order):
 //   out  (fp32) [R][r]    = v              (jj < r)
 //   out2 (bf16) [R][RP]   = bf16(scale*v)  (all jj; columns >= r are zero)
 //   out3 (bf16) [RP][ldt] = bf16(scale*v) transposed; columns i >= R zero
-__device__ __forceinline__ void run_reduce_rows(const SmallJob &j, int64_t idx) {
+__device__ __forceinline__ void run_reduce_rows(const SmallJob &j, uint32_t idx) {
   const float *part = static_cast<const float *>(j.in);
   const int64_t R = j.a, ldt = j.d;
-  const int S = j.i, RP = (int)j.b, r = j.j;
-  const int64_t i = idx / RP;
+  const int S = j.i, r = j.j;
+  const uint32_t RP = (uint32_t)j.b;
+  const uint32_t i = idx / RP;
   const int jj = (int)(idx - i * RP);
   float v = 0.f;
   if (i < R) {
-    for (int s = 0; s < S; ++s) v += part[(size_t)s * R * RP + idx];
-    if (j.out && jj < r) static_cast<float *>(j.out)[i * r + jj] = v;
+    v = sum_splits(part, S, (size_t)R * RP, idx);
+    if (j.out && jj < r) static_cast<float *>(j.out)[(int64_t)i * r + jj] = v;
     if (j.out2) static_cast<uint16_t *>(j.out2)[idx] = f32_to_bf16_bits(j.f * v);
   }
   if (j.out3) static_cast<uint16_t *>(j.out3)[(int64_t)jj * ldt + i] = i < R ? f32_to_bf16_bits(j.f * v) : (uint16_t)0;
@@ -55,24 +90,24 @@ __device__ __forceinline__ void run_reduce_rows(const SmallJob &j, int64_t idx) 
 // Transposed-product partials -> bf16, summed over splits in order:
 //   c == 0: part [S][RP][D] -> out [r][D]  (dA)
 //   c == 1: part [S][D][RP] -> out [D][r]  (dB)
-__device__ __forceinline__ void run_reduce_cols(const SmallJob &j, int64_t idx) {
+__device__ __forceinline__ void run_reduce_cols(const SmallJob &j, uint32_t idx) {
   const float *part = static_cast<const float *>(j.in);
   const int64_t D = j.a;
-  const int S = j.i, RP = (int)j.b, r = j.j;
-  const int64_t src = j.c ? (idx / r) * RP + idx % r : idx;
-  float v = 0.f;
-  for (int s = 0; s < S; ++s) v += part[(size_t)s * RP * D + src];
-  static_cast<uint16_t *>(j.out)[idx] = f32_to_bf16_bits(v);
+  const int S = j.i;
+  const uint32_t RP = (uint32_t)j.b, r = (uint32_t)j.j;
+  const uint32_t q = idx / r;
+  const size_t src = j.c ? (size_t)q * RP + (idx - q * r) : idx;
+  static_cast<uint16_t *>(j.out)[idx] = f32_to_bf16_bits(sum_splits(part, S, (size_t)RP * D, src));
 }
 
 // Forward scale table: for weight tile to (rows 256to ..) and super-step sp
 // (blocks 4sp .. 4sp+3 of each row) one contiguous 4 KB run,
 // Sp[((to*nsup + sp)*256 + row)*4 + q]; rows past n and blocks past k/64 hold
 // 0.  block_scale is the dequantization's own (bit-identical).
-__device__ __forceinline__ void run_scales_fwd(const SmallJob &j, int64_t t) {
+__device__ __forceinline__ void run_scales_fwd(const SmallJob &j, uint32_t t) {
   const Nf4View &w = j.w;
-  const int64_t nsup = j.a;
-  const int64_t q = t >> 8, to = q / nsup, sp = q - to * nsup;
+  const uint32_t nsup = (uint32_t)j.a;
+  const uint32_t q = t >> 8, to = q / nsup, sp = q - to * nsup;
   const int64_t n = to * kTileRows + (t & 255), nkb = w.k / kBlock;
   f32x4_t v = {0.f, 0.f, 0.f, 0.f};
   if (n < w.n) {
@@ -89,30 +124,37 @@ __device__ __forceinline__ void run_scales_fwd(const SmallJob &j, int64_t t) {
 // Backward scale table: for column tile tk (k-blocks 4tk .. 4tk+3) and
 // super-step sp (weight rows 256sp .. 256sp+255) one contiguous 4 KB run,
 // Sp[((tk*nsup + sp)*4 + blk)*256 + row]; rows past n and blocks past k/64
-// hold 0.
-__device__ __forceinline__ void run_scales_bwd(const SmallJob &j, int64_t t) {
+// hold 0.  One thread per (tk, sp, row): the row's four consecutive scale
+// codes, four coalesced stores.
+__device__ __forceinline__ void run_scales_bwd(const SmallJob &j, uint32_t t) {
   const Nf4View &w = j.w;
-  const int64_t nsup = j.a;
-  const int64_t q = t >> 10, tk = q / nsup, sp = q - tk * nsup;
-  const int64_t n = sp * kTileRows + (t & 255), kb = tk * kTileSup + ((t >> 8) & 3), nkb = w.k / kBlock;
-  float v = 0.f;
-  if (n < w.n && kb < nkb) {
-    const int64_t b = n * nkb + kb;
-    v = block_scale(w.scale_code[b], w.group_amax[b / kGroup], *w.offset);
+  const uint32_t nsup = (uint32_t)j.a;
+  const uint32_t q = t >> 8, tk = q / nsup, sp = q - tk * nsup;
+  const int64_t n = (int64_t)sp * kTileRows + (t & 255), nkb = w.k / kBlock;
+  float *out = static_cast<float *>(j.out) + (size_t)q * 4 * 256 + (t & 255);
+  const float off = *w.offset;
+#pragma unroll
+  for (int blk = 0; blk < kTileSup; ++blk) {
+    const int64_t kb = (int64_t)tk * kTileSup + blk;
+    float v = 0.f;
+    if (n < w.n && kb < nkb) {
+      const int64_t b = n * nkb + kb;
+      v = block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
+    }
+    out[blk * 256] = v;
   }
-  static_cast<float *>(j.out)[t] = v;
 }
 
 __global__ __launch_bounds__(256) void k_small_jobs(SmallJobs js) {
+  __shared__ uint16_t t[64][65];  // the tiled jobs' transpose buffer
   const int64_t blk = blockIdx.x;
   int q = 0;
   while (q + 1 < js.n && blk >= js.start[q + 1]) ++q;
   const SmallJob &j = js.j[q];
-  const int64_t idx = (blk - js.start[q]) * 256 + threadIdx.x;
+  const uint32_t idx = (uint32_t)(blk - js.start[q]) * 256u + threadIdx.x;
   if (idx >= j.count) return;
   switch (j.kind) {
-    case kJobTransposePad: run_transpose_pad(j, idx); break;
-    case kJobScaleTranspose: run_scale_transpose(j, idx); break;
+    case kJobTranspose: run_transpose(j, idx, t); break;
     case kJobReduceRows: run_reduce_rows(j, idx); break;
     case kJobReduceCols: run_reduce_cols(j, idx); break;
     case kJobScalesFwd: run_scales_fwd(j, idx); break;
@@ -130,6 +172,7 @@ hipError_t launch_jobs(const char *name, const SmallJob *jobs, int n, hipStream_
   int64_t blocks = 0;
   for (int q = 0; q < n; ++q) {
     if (jobs[q].count <= 0) continue;
+    if (jobs[q].count >= (int64_t(1) << 31) - 256) return hipErrorInvalidValue;  // 32-bit element indices
     js.j[js.n] = jobs[q];
     js.start[js.n] = blocks;
     blocks += ceil_div(jobs[q].count, 256);
@@ -141,28 +184,35 @@ hipError_t launch_jobs(const char *name, const SmallJob *jobs, int n, hipStream_
   return hipGetLastError();
 }
 
+namespace {
+int64_t tiles64(int64_t a, int64_t b) { return ((a + 63) / 64) * ((b + 63) / 64); }
+}  // namespace
+
 SmallJob job_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
                            int64_t ldo) {
   SmallJob j;
-  j.kind = kJobTransposePad;
-  j.count = out_rows * ldo;
+  j.kind = kJobTranspose;
+  j.count = tiles64(out_rows, ldo) * 256;
   j.in = in;
   j.out = out;
   j.a = rows;
   j.b = cols;
+  j.c = out_rows;
   j.d = ldo;
   return j;
 }
 
 SmallJob job_scale_transpose(const float *H, int64_t M, int r, float scale, uint16_t *out, int RP, int64_t ldo) {
   SmallJob j;
-  j.kind = kJobScaleTranspose;
-  j.count = (int64_t)RP * ldo;
+  j.kind = kJobTranspose;
+  j.count = tiles64(RP, ldo) * 256;
   j.in = H;
   j.out = out;
   j.a = M;
+  j.b = r;
+  j.c = RP;
   j.d = ldo;
-  j.i = r;
+  j.i = 1;
   j.f = scale;
   return j;
 }
@@ -213,7 +263,7 @@ SmallJob job_scales_bwd(const Nf4View &w, float *scales) {
   SmallJob j;
   j.kind = kJobScalesBwd;
   j.a = tile_bwd_nsup(w.n);
-  j.count = ceil_div(w.k, kTileRows) * j.a * 1024;
+  j.count = ceil_div(w.k, kTileRows) * j.a * 256;
   j.out = scales;
   j.w = w;
   return j;

@@ -67,10 +67,6 @@ hipError_t launch_reduce_rows(const float *part, int S, int64_t R, int RP, int r
                               uint16_t *out_b, uint16_t *out_bt, int64_t ldt, hipStream_t s);
 hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r, bool rows_out, uint16_t *out,
                               hipStream_t s);
-hipError_t launch_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
-                                int64_t ldo, hipStream_t s);
-hipError_t launch_scale_transpose_f32(const float *H, int64_t M, int r, float scale, uint16_t *out, int RP,
-                                      int64_t ldo, hipStream_t s);
 hipError_t launch_fill_zero_u16(uint16_t *p, int64_t n, hipStream_t s);
 
 // Both transposed products of the backward in one launch (consecutive block
@@ -92,13 +88,11 @@ hipError_t launch_tn_pair(const TnProblem &p0, const TnProblem &p1, int64_t M, i
 // Small elementwise jobs (jobs.hip): layout copies, split-partial reductions
 // and the tile kernels' block-scale tables.  Up to kMaxJobs independent jobs
 // run as one launch over consecutive block ranges, which saves a launch ramp
-// per job; each job is the elementwise kernel the launch_* function above
-// of the same name describes.
+// per job.  The reductions are those of the launch_reduce_* functions above.
 // ---------------------------------------------------------------------------
 enum JobKind : int {
-  kJobTransposePad,
-  kJobScaleTranspose,
-  kJobReduceRows,
+  kJobTranspose,    // 64 x 64 tiles through LDS
+  kJobReduceRows,   // elementwise
   kJobReduceCols,
   kJobScalesFwd,
   kJobScalesBwd,
@@ -115,8 +109,10 @@ struct SmallJob {
 };
 constexpr int kMaxJobs = 4;
 hipError_t launch_jobs(const char *name, const SmallJob *jobs, int n, hipStream_t s);
+// out [out_rows][ldo] = in^T for a row-major bf16 in [rows][cols], zero-padded
 SmallJob job_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
                            int64_t ldo);
+// out [RP][ldo] = bf16(scale * H^T) for fp32 H [M][r], zero-padded
 SmallJob job_scale_transpose(const float *H, int64_t M, int r, float scale, uint16_t *out, int RP, int64_t ldo);
 SmallJob job_reduce_rows(const float *part, int S, int64_t R, int RP, int r, float scale, float *out_f32,
                          uint16_t *out_b, uint16_t *out_bt, int64_t ldt);

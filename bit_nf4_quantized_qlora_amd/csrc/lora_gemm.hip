@@ -428,18 +428,6 @@ hipError_t launch_reduce_cols(const float *part, int S, int64_t D, int RP, int r
   return launch_jobs("k_reduce_cols", &j, 1, s);
 }
 
-hipError_t launch_transpose_pad(const uint16_t *in, int64_t rows, int64_t cols, uint16_t *out, int64_t out_rows,
-                                int64_t ldo, hipStream_t s) {
-  const SmallJob j = job_transpose_pad(in, rows, cols, out, out_rows, ldo);
-  return launch_jobs("k_transpose_pad", &j, 1, s);
-}
-
-hipError_t launch_scale_transpose_f32(const float *H, int64_t M, int r, float scale, uint16_t *out, int RP,
-                                      int64_t ldo, hipStream_t s) {
-  const SmallJob j = job_scale_transpose(H, M, r, scale, out, RP, ldo);
-  return launch_jobs("k_scale_transpose_f32", &j, 1, s);
-}
-
 hipError_t launch_fill_zero_u16(uint16_t *p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   QLORA_LAUNCH("k_fill_zero_u16", k_fill_zero_u16, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, p, n);
