@@ -63,6 +63,9 @@ def test_q_proj_full(q):
     (300, 640, 130, 100, 32.0, 3),  # rank 100, partial tiles on every axis
     (96, 256, 65, 128, 16.0, 4),    # maximum rank
     (256, 1024, 300, 16, 0.0, 5),   # alpha = 0: adapters contribute nothing to Y
+    (640, 512, 200, 80, 16.0, 6),   # rank 80 (padded to 96), n % 64 == 0: the backward tile kernel
+    (1088, 320, 96, 64, 8.0, 7),    # k % 256 != 0 (5 blocks per row), 17 backward row blocks
+    (512, 768, 520, 48, 16.0, 8),   # three m tiles, rank 48 (padded to 64)
 ])
 def test_edge_shapes(q, n, k, m, r, alpha, seed):
     W = I.custom_weight(n, k, seed)
