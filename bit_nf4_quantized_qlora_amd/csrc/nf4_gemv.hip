@@ -34,8 +34,8 @@
 // positions 32(g % 2) .. +31 of it; MFMA t takes bytes 4t .. 4t+3), so one
 // load instruction reads 64 contiguous bytes of each of 16 rows and a lane
 // needs one block scale per pair; codes are fetched 4 pairs ahead.  X is
-// staged in LDS for the whole range (row m's 16-byte chunk c at
-// c ^ ((m >> 1) & 7)), so X and the weights meet in the same order.
+// staged in LDS for the whole range, one 272-byte row per (pair, m), so X
+// and the weights meet in the same order.
 //
 // H: workgroup t < nh takes rank tile t % (RP/16) and K slice t / (RP/16)
 // (512 wide, 32 per wave); its operands are loaded before anything else so
@@ -58,7 +58,8 @@ constexpr int kLdsDec = 256 * 4;           // E4M3 decode table
 constexpr int kLdsVar = kLdsAll - kLdsTab - kLdsDec - 128 - 16;  // group constants + staged X
 constexpr int kHSlice = 32 * kGvWaves;     // K per H slice: one 32-deep MFMA per wave
 constexpr int kMaxG = 4096;                // most workgroups
-constexpr int kXPer = 6;                   // staged X chunks per thread: 6 * 1024 * 16 B >= kLdsVar
+constexpr int kXRow = 272;                 // staged X row: one pair of blocks (128 bf16) + 16 B of padding
+constexpr int kXPer = 6;                   // staged 16-byte X chunks per thread (covers kLdsVar / kXRow rows)
 constexpr int kGaPer = 2;                  // group constants per thread loaded ahead of the table fill
 
 struct GemvPlan {
@@ -92,7 +93,7 @@ GemvPlan gemv_plan(int64_t M, int64_t n, int64_t k, int RP) {
     }
     p.seg = (int)seg;
     p.xoff = (int)align_up((size_t)seg * p.nkb * 4, 16);
-    return p.xoff + nbmax * M * 128 <= kLdsVar;
+    return p.xoff + nbmax / 2 * M * kXRow <= kLdsVar;
   };
   // one workgroup per CU (more only if the staged X or the H slices need
   // them), never more than there are blocks or H slices to take
@@ -205,9 +206,11 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
 #pragma unroll
   for (int j = 0; j < kGvP; ++j) load(j, 2 * j < nb);
 
-  // X columns of the range: staged row R = i*M + m holds X[m][64 kb(i) ..
-  // +63], 16-byte chunk c at c ^ ((m >> 1) & 7); the 16 lanes of one read
-  // (m = 0..15 of one block) then hit 16 distinct bank groups for any M.
+  // X columns of the range: staged row P = ip*M + m holds X[m][64 kb(2ip) ..
+  // +127] (the pair's two blocks) at P * 272 (16 B of padding per row): the
+  // 16 lanes of one read (consecutive rows, one chunk) then hit 16 distinct
+  // bank groups, and a lane's four chunks of a pair are fixed offsets from
+  // one address.
   // The LDS plan keeps nb * M * 8 <= kXPer * 1024.
   const int nxc = nb * M * 8;
   const __amdgpu_buffer_rsrc_t xrs = rsrc(X, (int64_t)M * K * 2);
@@ -220,8 +223,8 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
     const int c = tid + 1024 * u;
     xv[u] = u32x4_t{0u, 0u, 0u, 0u};
     if (64 * wave + 1024 * u < nxc) {
-      const int ch = c & 7, R = c >> 3, i = (int)(((uint32_t)R * inv_m) >> 16), m = R - i * M;
-      int kb = lkb0 + i;
+      const int ch = c & 15, R = c >> 4, ip = (int)(((uint32_t)R * inv_m) >> 16), m = R - ip * M;
+      int kb = lkb0 + 2 * ip;
       while (kb >= nkb) kb -= nkb;
       xv[u] = __builtin_amdgcn_raw_buffer_load_b128(
           xrs, c < nxc ? (uint32_t)((m * K + kb * kBlock + 8 * ch) * 2) : kOut, 0, 0);
@@ -282,8 +285,8 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
 #pragma unroll
   for (int u = 0; u < kXPer; ++u) {
     const int c = tid + 1024 * u;
-    const int ch = c & 7, R = c >> 3, m = R - (int)(((uint32_t)R * inv_m) >> 16) * M;
-    if (c < nxc) *reinterpret_cast<u32x4_t *>(s_x + R * 128 + ((ch ^ ((m >> 1) & 7)) << 4)) = xv[u];
+    const int ch = c & 15, R = c >> 4;
+    if (c < nxc) *reinterpret_cast<u32x4_t *>(s_x + R * kXRow + (ch << 4)) = xv[u];
   }
 #pragma unroll
   for (int u = 0; u < kGaPer; ++u)
@@ -297,15 +300,11 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
 
   const char *tab = reinterpret_cast<const char *>(s_tab);
   const uint32_t lane_off = (uint32_t)(lane & 31) * 8;
-  // X fragment of a pair for MFMA t: staged row (2ip + hb)*M + li, chunk
-  // 4(g & 1) + t (lanes li >= M read the zero row, which takes no step).
+  // X fragment of a pair for MFMA t: staged row ip*M + li, chunk 4g + t, at
+  // xo + 16t (lanes li >= M read the zero row, which takes no step).
   const bool xreal = li < M;
-  const int sw = (li >> 1) & 7;
-  uint32_t xo[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    xo[t] = xreal ? (uint32_t)(xbase + (hb * M + li) * 128 + (((4 * (g & 1) + t) ^ sw) << 4)) : (uint32_t)kZeroOff;
-  const uint32_t xstep = xreal ? (uint32_t)M * 256 : 0u;
+  const uint32_t xo = xreal ? (uint32_t)(xbase + li * kXRow + 64 * g) : (uint32_t)kZeroOff;
+  const uint32_t xstep = xreal ? (uint32_t)M * kXRow : 0u;
   uint32_t xoff = 0;
   // scale code byte of this lane's block in the word: 2(ip & 1) + hb
   const uint32_t ssh0 = 8u * hb, ssh1 = 16u + 8u * hb;
@@ -334,7 +333,7 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
       const float ga = *reinterpret_cast<const float *>(lds + ga_base + ((cbi >> 8) << 2));
       u32x4_t xa[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) xa[t] = *reinterpret_cast<const u32x4_t *>(lds + xo[t] + xoff);
+      for (int t = 0; t < 4; ++t) xa[t] = *reinterpret_cast<const u32x4_t *>(lds + xo + xoff + 16 * t);
       if (2 * ip + 2 < nb) xoff += xstep;
       const u32x4_t cw = cq[q];
       float2 lv[16];
