@@ -403,8 +403,8 @@ __global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const flo
                                                      bool sparse, int64_t nkb, uint16_t *__restrict__ Y,
                                                      float *__restrict__ H_out) {
   constexpr int kPv = 8, kHv = 16, kBv = kGvRows * 128 / 8 / 256;  // loads in flight per thread
-  __shared__ float s_h[128];                             // bf16(s H[m][j]) as floats
-  __shared__ __align__(16) uint16_t s_b[kGvRows * 128];  // B rows of the group, row stride r
+  __shared__ float s_h[128];                        // bf16(s H[m][j]) as floats
+  extern __shared__ __align__(16) uint16_t s_b[];   // B rows of the group, row stride r (256 r bf16)
   const int tid = threadIdx.x, m = blockIdx.y;
   const int64_t gr = blockIdx.x;
   const int64_t n = gr * kGvRows + tid;
@@ -494,11 +494,13 @@ hipError_t launch_fwd_small(const Nf4View &w, const uint16_t *X, int64_t M, cons
   const int T4 = (int)(p.T / 4);
   QLORA_LAUNCH("k_gemv_nf4", k_gemv_nf4, dim3((unsigned)p.G), dim3(1024), 0, st, w, X, (int)M, A, r, RP, hpart, part,
                T4, p.G, T4 / p.G, T4 % p.G, p.seg, p.maxcov, p.nh, p.nht, p.xoff);
+  // the group's B rows in LDS, sized by the rank (more workgroups per CU at small r)
+  const size_t bshm = (size_t)kGvRows * r * sizeof(uint16_t);
   if (r % 8 == 0)
-    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<true>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), 0, st, w.n, (int)M,
+    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<true>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), bshm, st, w.n, (int)M,
                  hpart, p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.maxcov, p.sparse, p.nkb, Y, H_out);
   else
-    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<false>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), 0, st, w.n, (int)M,
+    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<false>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), bshm, st, w.n, (int)M,
                  hpart, p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.maxcov, p.sparse, p.nkb, Y, H_out);
   return hipGetLastError();
 }
