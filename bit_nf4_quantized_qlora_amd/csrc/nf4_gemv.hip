@@ -157,55 +157,12 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   const int gfirst = b0 / nkb;
   const int lkb0 = b0 - gfirst * nkb;
 
-  // Global loads go out first: the first pairs of codes and scale words
-  // (the stream the loop waits on), then the X columns and group constants
-  // the range stages into LDS, the H slice operands and the scalar offset.
-  // The table fill runs while they are in flight.
+  // Global loads go out first: the X columns and group constants the range
+  // stages into LDS (small, so they return quickly), the H slice operands
+  // and the scalar offset, then the first pairs of codes and scale words.
+  // The table fill runs while they are in flight, and waiting for the staged
+  // values leaves the code loads in flight.
   constexpr uint32_t kOut = 0x80000000u;
-  // Per-lane streams (32-bit offsets): the codes of a pair of blocks of row
-  // n, a word of four scale codes per two pairs, and the blocks' group
-  // constants.  Rows past N read zero and give partial sums that are never
-  // used; loads past the workgroup's last block take an out-of-range offset
-  // (no memory traffic).
-  const __amdgpu_buffer_rsrc_t crs = rsrc(w.packed, N * kb2);
-  const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code, w.nb);
-  const int nrow = 16 * wave + li;  // row within the group
-  const int nkb32 = nkb;
-  const int hb = g >> 1;  // which block of a pair this lane's codes come from
-  int lkb = lkb0;
-  uint32_t lco = (uint32_t)((gfirst * kGvRows + nrow) * kb2 + lkb * 32 + 16 * g);
-  uint32_t lbi = (uint32_t)((gfirst * kGvRows + nrow) * nkb + lkb);
-  const uint32_t gstep_c = (uint32_t)(kGvRows * kb2 - nkb * 32), gstep_b = (uint32_t)(kGvRows * nkb - nkb);
-  // codes of a pair of blocks: lane (li, g) takes the 16 bytes at 16g of the
-  // row's 64 bytes (block hb, contraction positions 32(g & 1) .. +31), so a
-  // wave instruction reads 64 contiguous bytes of each of its 16 rows
-  u32x4_t cq[kGvP];
-  auto load = [&](int slot, bool real) {
-    cq[slot] = __builtin_amdgcn_raw_buffer_load_b128(crs, real ? lco : kOut, 0, 0);
-    lco += 64;
-    if ((lkb += 2) == nkb32) {
-      lkb = 0;
-      lco += gstep_c;
-    }
-  };
-  // Scale codes four blocks (two pairs) per load (ranges and row groups
-  // start on multiples of 4 blocks, and nkb % 4 == 0): word w of the row's
-  // codes, all four lanes of a row reading the same word; two in flight.
-  uint32_t scw[2];
-  int skb = lkb;
-  auto sload = [&](int slot, bool real) {
-    scw[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, real ? lbi : kOut, 0, 0);
-    lbi += 4;
-    if ((skb += 4) == nkb32) {
-      skb = 0;
-      lbi += gstep_b;
-    }
-  };
-  sload(0, 0 < nb);
-  sload(1, 4 < nb);
-#pragma unroll
-  for (int j = 0; j < kGvP; ++j) load(j, 2 * j < nb);
-
   // X columns of the range: staged row P = ip*M + m holds X[m][64 kb(2ip) ..
   // +127] (the pair's two blocks) at P * 272 (16 B of padding per row): the
   // 16 lanes of one read (consecutive rows, one chunk) then hit 16 distinct
@@ -258,6 +215,50 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
     ha = __builtin_amdgcn_raw_buffer_load_b128(ar, kin && j < r ? (uint32_t)((j * K + kh) * 2) : kOut, 0, 0);
   }
   const float offset = *w.offset;
+
+  // Per-lane streams (32-bit offsets): the codes of a pair of blocks of row
+  // n, a word of four scale codes per two pairs, and the blocks' group
+  // constants.  Rows past N read zero and give partial sums that are never
+  // used; loads past the workgroup's last block take an out-of-range offset
+  // (no memory traffic).
+  const __amdgpu_buffer_rsrc_t crs = rsrc(w.packed, N * kb2);
+  const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code, w.nb);
+  const int nrow = 16 * wave + li;  // row within the group
+  const int nkb32 = nkb;
+  const int hb = g >> 1;  // which block of a pair this lane's codes come from
+  int lkb = lkb0;
+  uint32_t lco = (uint32_t)((gfirst * kGvRows + nrow) * kb2 + lkb * 32 + 16 * g);
+  uint32_t lbi = (uint32_t)((gfirst * kGvRows + nrow) * nkb + lkb);
+  const uint32_t gstep_c = (uint32_t)(kGvRows * kb2 - nkb * 32), gstep_b = (uint32_t)(kGvRows * nkb - nkb);
+  // codes of a pair of blocks: lane (li, g) takes the 16 bytes at 16g of the
+  // row's 64 bytes (block hb, contraction positions 32(g & 1) .. +31), so a
+  // wave instruction reads 64 contiguous bytes of each of its 16 rows
+  u32x4_t cq[kGvP];
+  auto load = [&](int slot, bool real) {
+    cq[slot] = __builtin_amdgcn_raw_buffer_load_b128(crs, real ? lco : kOut, 0, 0);
+    lco += 64;
+    if ((lkb += 2) == nkb32) {
+      lkb = 0;
+      lco += gstep_c;
+    }
+  };
+  // Scale codes four blocks (two pairs) per load (ranges and row groups
+  // start on multiples of 4 blocks, and nkb % 4 == 0): word w of the row's
+  // codes, all four lanes of a row reading the same word; two in flight.
+  uint32_t scw[2];
+  int skb = lkb;
+  auto sload = [&](int slot, bool real) {
+    scw[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, real ? lbi : kOut, 0, 0);
+    lbi += 4;
+    if ((skb += 4) == nkb32) {
+      skb = 0;
+      lbi += gstep_b;
+    }
+  };
+  sload(0, 0 < nb);
+  sload(1, 4 < nb);
+#pragma unroll
+  for (int j = 0; j < kGvP; ++j) load(j, 2 * j < nb);
 
   // Level-pair table: entry e = {q[e & 15], q[e >> 4]} (low nibble = first
   // weight), copy c at byte 256e + 8c.  Wave w writes entries 16w .. 16w+15,
