@@ -8,7 +8,8 @@
 //   k_quantize_blocks  one workgroup per group of 256 blocks (64 KiB of W):
 //                      absmax, codes, packed nibbles, and the group's fp64
 //                      in-order absmax sum;
-//   k_mean             one lane folds the group sums in order -> offset;
+//   k_mean             one workgroup stages the group sums in LDS, one lane
+//                      folds them in order -> offset;
 //   k_encode_scales    one wave per group: dev = absmax - offset, group amax,
 //                      E4M3 codes.
 #include "qlora_internal.h"
@@ -16,15 +17,23 @@
 namespace qlora {
 namespace {
 
+// a if b else c, as a bit blend: the operands are wave-uniform thresholds
+// in scalar registers, so this stays a register select (a conditional
+// element choice would be turned into an indexed load from a stack copy of
+// the threshold array).
+__device__ __forceinline__ float pick(bool b, float a, float c) {
+  const uint32_t m = 0u - (uint32_t)b;
+  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(c) & ~m));
+}
+
 // Index of the nearest NF4 level from the 15 thresholds: a 4-step binary
 // search (each step a compare and selects between uniform thresholds).
-__device__ __forceinline__ uint32_t nf4_code(float x, const Thresholds &T) {
-  const bool b3 = x >= T.t[7];
-  const bool b2 = x >= (b3 ? T.t[11] : T.t[3]);
-  const float t1 = b3 ? (b2 ? T.t[13] : T.t[9]) : (b2 ? T.t[5] : T.t[1]);
-  const bool b1 = x >= t1;
-  const float t0 = b3 ? (b2 ? (b1 ? T.t[14] : T.t[12]) : (b1 ? T.t[10] : T.t[8]))
-                      : (b2 ? (b1 ? T.t[6] : T.t[4]) : (b1 ? T.t[2] : T.t[0]));
+__device__ __forceinline__ uint32_t nf4_code(float x, const float (&t)[15]) {
+  const bool b3 = x >= t[7];
+  const bool b2 = x >= pick(b3, t[11], t[3]);
+  const bool b1 = x >= pick(b3, pick(b2, t[13], t[9]), pick(b2, t[5], t[1]));
+  const float t0 = pick(b3, pick(b2, pick(b1, t[14], t[12]), pick(b1, t[10], t[8])),
+                        pick(b2, pick(b1, t[6], t[4]), pick(b1, t[2], t[0])));
   const bool b0 = x >= t0;
   return (uint32_t(b3) << 3) | (uint32_t(b2) << 2) | (uint32_t(b1) << 1) | uint32_t(b0);
 }
@@ -37,6 +46,9 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict
                                                          float *__restrict__ absmax_out,
                                                          double *__restrict__ group_sum) {
   __shared__ float s_absmax[kGroup];
+  float t[15];  // the thresholds in (scalar) registers
+#pragma unroll
+  for (int j = 0; j < 15; ++j) t[j] = T.t[j];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t first = (int64_t)blockIdx.x * kGroup;
   const int nblk = (int)min<int64_t>(kGroup, nb - first);
@@ -63,7 +75,7 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict
       for (int i = 0; i < 8; ++i) {
         // IEEE round-to-nearest division; an all-zero block normalizes to 0.
         const float x = m > 0.f ? __fdiv_rn(w[i], m) : 0.f;
-        word |= nf4_code(x, T) << (4 * i);
+        word |= nf4_code(x, t) << (4 * i);
       }
       *reinterpret_cast<uint32_t *>(packed + e0 / 2) = word;
       if ((lane & 7) == 0) {
@@ -73,28 +85,48 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0) {  // block order; eight LDS reads in flight per batch
     double acc = 0.0;
-    for (int i = 0; i < nblk; ++i) acc += (double)s_absmax[i];  // block order
+    int i = 0;
+    for (; i + 8 <= nblk; i += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = s_absmax[i + q];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc += (double)v[q];
+    }
+    for (; i < nblk; ++i) acc += (double)s_absmax[i];
     group_sum[blockIdx.x] = acc;
   }
 }
 
-// offset = fp32( (in-order fp64 fold of the group sums) / nb ).
-__global__ __launch_bounds__(64) void k_mean(const double *__restrict__ group_sum, int64_t ng, int64_t nb,
-                                            float *__restrict__ offset) {
-  if (threadIdx.x != 0) return;
-  double acc = 0.0;
-  int64_t g = 0;
-  for (; g + 4 <= ng; g += 4) {
-    const double a = group_sum[g], b = group_sum[g + 1], c = group_sum[g + 2], d = group_sum[g + 3];
-    acc += a;
-    acc += b;
-    acc += c;
-    acc += d;
+// offset = fp32( (in-order fp64 fold of the group sums) / nb ).  The whole
+// workgroup stages the group sums into LDS a chunk at a time (coalesced
+// loads, one memory round trip per chunk); one lane then folds the chunk in
+// order, eight LDS reads in flight per batch.
+constexpr int kMeanChunk = 4096;  // fp64 sums per LDS chunk (32 KB)
+__global__ __launch_bounds__(256) void k_mean(const double *__restrict__ group_sum, int64_t ng, int64_t nb,
+                                             float *__restrict__ offset) {
+  __shared__ double s_sum[kMeanChunk];
+  double acc = 0.0;  // lane 0's running fold
+  for (int64_t c0 = 0; c0 < ng; c0 += kMeanChunk) {
+    const int n = (int)min<int64_t>(kMeanChunk, ng - c0);
+    for (int i = threadIdx.x; i < n; i += 256) s_sum[i] = group_sum[c0 + i];
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int i = 0;
+      for (; i + 8 <= n; i += 8) {
+        double v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = s_sum[i + q];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc += v[q];
+      }
+      for (; i < n; ++i) acc += s_sum[i];
+    }
+    __syncthreads();
   }
-  for (; g < ng; ++g) acc += group_sum[g];
-  *offset = (float)(acc / (double)nb);
+  if (threadIdx.x == 0) *offset = (float)(acc / (double)nb);
 }
 
 // One wave per group, four block constants per lane.
@@ -142,7 +174,7 @@ hipError_t launch_quantize(const float *W, int64_t n, int64_t k, uint8_t *packed
   const int64_t ng = ceil_div(nb, kGroup);
   QLORA_LAUNCH("k_quantize_blocks", k_quantize_blocks, dim3((unsigned)ng), dim3(256), 0, s, W, nb, nf4_thresholds(), packed,
                      ws_absmax, ws_group_sum);
-  QLORA_LAUNCH("k_mean", k_mean, dim3(1), dim3(64), 0, s, ws_group_sum, ng, nb, offset);
+  QLORA_LAUNCH("k_mean", k_mean, dim3(1), dim3(256), 0, s, ws_group_sum, ng, nb, offset);
   QLORA_LAUNCH("k_encode_scales", k_encode_scales, dim3((unsigned)ceil_div(ng, 4)), dim3(256), 0, s, ws_absmax, nb, ng,
                      offset, scale_code, group_amax);
   return hipGetLastError();
