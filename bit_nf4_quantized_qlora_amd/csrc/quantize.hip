@@ -103,26 +103,34 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict
 // offset = fp32( (in-order fp64 fold of the group sums) / nb ).  The whole
 // workgroup stages the group sums into LDS a chunk at a time (coalesced
 // loads, one memory round trip per chunk); one lane then folds the chunk in
-// order, eight LDS reads in flight per batch.
+// order, reading one batch ahead.
 constexpr int kMeanChunk = 4096;  // fp64 sums per LDS chunk (32 KB)
 __global__ __launch_bounds__(256) void k_mean(const double *__restrict__ group_sum, int64_t ng, int64_t nb,
                                              float *__restrict__ offset) {
-  __shared__ double s_sum[kMeanChunk];
+  constexpr int B = 16;                    // fold batch
+  __shared__ double s_sum[kMeanChunk + B];  // + one batch of zeros to read ahead into
   double acc = 0.0;  // lane 0's running fold
   for (int64_t c0 = 0; c0 < ng; c0 += kMeanChunk) {
     const int n = (int)min<int64_t>(kMeanChunk, ng - c0);
-    for (int i = threadIdx.x; i < n; i += 256) s_sum[i] = group_sum[c0 + i];
+    for (int i = threadIdx.x; i < n + B; i += 256) s_sum[i] = i < n ? group_sum[c0 + i] : 0.0;
     __syncthreads();
     if (threadIdx.x == 0) {
-      int i = 0;
-      for (; i + 8 <= n; i += 8) {
-        double v[8];
+      // the next batch's reads go out before this batch's adds, so the
+      // dependent fp64 adds hide the LDS latency
+      const int nB = n / B * B;
+      double v[B];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = s_sum[i + q];
+      for (int q = 0; q < B; ++q) v[q] = s_sum[q];
+      for (int i = 0; i < nB; i += B) {
+        double nx[B];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc += v[q];
+        for (int q = 0; q < B; ++q) nx[q] = s_sum[i + B + q];
+#pragma unroll
+        for (int q = 0; q < B; ++q) acc += v[q];
+#pragma unroll
+        for (int q = 0; q < B; ++q) v[q] = nx[q];
       }
-      for (; i < n; ++i) acc += s_sum[i];
+      for (int i = nB; i < n; ++i) acc += s_sum[i];
     }
     __syncthreads();
   }
