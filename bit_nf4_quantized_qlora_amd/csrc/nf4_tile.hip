@@ -301,41 +301,60 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   // flight (super-step 1's codes follow in step 0's pairs 0-2); step 0
   // expanded; codes of step 1 in set 1; pair 0's fragments and piece 0's
   // table reads issued.
-  __syncthreads();  // pair table
+  //
+  // The LoRA term comes first: C += L R^T over the padded rank in 64-wide
+  // chunks, each chunk of R (rows m0 .. +255, row stride RP; columns past RP
+  // and rows past M read zero) copied into Wc1 -- idle until step 0 copies
+  // super-step 1 -- with the B-tile layout, and the matching L operands
+  // (rows o, row stride lda) loaded straight into registers.  The first
+  // chunk's loads go out before the copies of steps 0 and 1, so its MFMAs
+  // wait only for them and run while the copies are in flight.
+  const __amdgpu_buffer_rsrc_t rr = rsrc(R + m0 * RP, min<int64_t>(TM, M - m0) * RP * 2);
+  uint16_t *rtile = reinterpret_cast<uint16_t *>(Wc1);
+  const bool lvec = (lda % 8) == 0;
+  u32x4_t la[4][2];
+  auto lora_loads = [&](int jc) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 64 * wave + 8 * i + (lane >> 3);
+      const int col = jc + 8 * ((lane & 7) ^ (4 * (i & 1) + (lane >> 4)));
+      const uint32_t off = col < RP ? (uint32_t)((row * RP + col) * 2) : 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr)(rtile + (512 * wave + 64 * i) * 8), 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        la[rt][t] = load8(L, lda, NO, lda, o0 + 64 * wave + 16 * rt + li, jc + 16 * g + 8 * t, lvec);
+  };
+  // bfrag hands odd-g lanes their two 8-byte halves swapped; swap the L
+  // operand the same way so products pair up (after the loads have landed:
+  // using a loaded value makes the compiler wait for it right there)
+  auto lora_swap = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        if (g & 1) la[rt][t] = u32x4_t{la[rt][t][2], la[rt][t][3], la[rt][t][0], la[rt][t][1]};
+  };
+  __syncthreads();  // pair table; Wc1 free
+  lora_loads(0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) bload(0, std::integral_constant<int, 0>(), i);
 #pragma unroll
   for (int i = 0; i < kVmemW; ++i) wload(0, std::integral_constant<int, 0>(), i);
-
-  // The LoRA term first, while those copies are in flight: C += L R^T over
-  // the padded rank in 64-wide chunks, each chunk of R (rows m0 .. +255,
-  // row stride RP; columns past RP and rows past M read zero) copied into
-  // Wc1 -- idle until step 0 copies super-step 1 -- with the B-tile layout,
-  // and the matching L operands (rows o, row stride lda) loaded straight
-  // into registers.
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bload(1, std::integral_constant<int, 1>(), i);
   {
-    const __amdgpu_buffer_rsrc_t rr = rsrc(R + m0 * RP, min<int64_t>(TM, M - m0) * RP * 2);
-    uint16_t *rtile = reinterpret_cast<uint16_t *>(Wc1);
-    const bool lvec = (lda % 8) == 0;
     for (int jc = 0; jc < RP; jc += 64) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = 64 * wave + 8 * i + (lane >> 3);
-        const int col = jc + 8 * ((lane & 7) ^ (4 * (i & 1) + (lane >> 4)));
-        const uint32_t off = col < RP ? (uint32_t)((row * RP + col) * 2) : 0x80000000u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (lds_ptr)(rtile + (512 * wave + 64 * i) * 8), 16, off, 0, 0, 0);
+      if (jc == 0) {
+        // the 8 + kVmemW + 8 copies issued after chunk 0's loads may stay in flight
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 + kVmemW + 8) : "memory");
+      } else {
+        lora_loads(jc);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      // bfrag hands odd-g lanes their two 8-byte halves swapped; swap the
-      // L operand the same way so products pair up.
-      u32x4_t la[4][2];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4_t v = load8(L, lda, NO, lda, o0 + 64 * wave + 16 * rt + li, jc + 16 * g + 8 * t, lvec);
-          la[rt][t] = (g & 1) ? u32x4_t{v[2], v[3], v[0], v[1]} : v;
-        }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lora_swap();
       __syncthreads();
       // The MFMAs are inline asm, so the compiler does not pad the gap after
       // the VALU writes of the swap: keep those writes above this point and
@@ -353,10 +372,9 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
       __syncthreads();
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // steps 0's copies landed everywhere (step 1's B may still be in flight)
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 8; ++i) bload(1, std::integral_constant<int, 1>(), i);
   cread(std::integral_constant<int, 0>(), 0);
   cread(std::integral_constant<int, 0>(), 1);
   sread(std::integral_constant<int, 0>(), 0);
