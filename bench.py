@@ -261,6 +261,17 @@ def main():
     fwd_ms = timed(fwd_pass, max(3, args.steps // 2))
     bwd_ms = timed(bwd_pass, max(3, args.steps // 2))
 
+    # per-step spread: the same steps one at a time, events around each
+    evs = [(ev(), ev()) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) for a, b in evs)
+    spread = {"p10": round(float(np.percentile(per_step, 10)), 4), "p50": round(float(np.percentile(per_step, 50)), 4),
+              "p90": round(float(np.percentile(per_step, 90)), 4)}
+
     # --------------------------------------- per-kernel event timing (second pass)
     q.qlora_profile_begin()
     for _ in range(args.steps):
@@ -319,6 +330,15 @@ def main():
             with open(os.path.join(os.environ["QLORA_CALIB_DIR"], "calib_copy.json"), "w") as fh:
                 json.dump(calib, fh)
 
+    attainable = None
+    if not args.no_extras:
+        attainable = attainable_peaks(torch, dev, ev)
+        if roofline.get("achieved") is not None:
+            roofline["frac_attainable"] = round(roofline["achieved"] / attainable["bf16_gemm_tflops"], 4)
+        for k, v in rows["small_m"].items():
+            if isinstance(v, dict) and "kernel_gbps_packed" in v:
+                v["kernel_frac_attainable_read"] = round(v["kernel_gbps_packed"] / attainable["hbm_read_gbps"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, I, args.cpu_seconds)
@@ -333,6 +353,7 @@ def main():
                    "weights": "NF4+DQ (block 64, 8-bit E4M3 constants per 256)", "parallelism": "single_gpu"},
         "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
+        "step_ms_spread": spread,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "rows": rows,
@@ -341,7 +362,50 @@ def main():
     }
     if calib:
         out["calib_copy"] = calib
+    if attainable:
+        out["attainable"] = attainable
     print(json.dumps(out), flush=True)
+
+
+def attainable_peaks(torch, dev, ev):
+    """What the box sustains, measured beside the run (the second denominator
+    next to the spec peaks): an elementwise copy and a read-only reduction
+    over 1 GiB (the fastest of three torch reductions), and a large vendor
+    BF16 GEMM (8192^3, hipBLASLt via torch.matmul).  Medians of 10 timed
+    calls after 3 warm-ups."""
+    def med(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+    nb = 1 << 30
+    src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    copy_ms = med(lambda: torch.mul(src, 1.0, out=dst))
+    v = src.view(-1, 1 << 16)
+    reads = {"sum_all": med(lambda: torch.sum(src)), "sum_rows": med(lambda: torch.sum(v, dim=1)),
+             "amax_rows": med(lambda: torch.amax(v, dim=1))}
+    read_best = min(reads, key=reads.get)
+    read_ms = reads[read_best]
+    del src, dst, v
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    gemm_ms = med(lambda: torch.matmul(a, b))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"hbm_copy_gbps": round(2 * nb / (copy_ms * 1e-3) / 1e9, 1),
+            "hbm_read_gbps": round(nb / (read_ms * 1e-3) / 1e9, 1), "hbm_read_kernel": read_best,
+            "bf16_gemm_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+            "how": "1 GiB elementwise copy; fastest of three 1 GiB torch reductions; torch.matmul bf16 8192^3; medians of 10"}
 
 
 def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
