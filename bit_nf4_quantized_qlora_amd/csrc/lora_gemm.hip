@@ -357,10 +357,12 @@ hipError_t dispatch_tj(int RP, F &&f) {
 int lora_rank_pad(int r) { return (r + 31) / 32 * 32; }
 
 SplitPlan plan_split(int64_t tiles, int64_t steps) {
-  // Aim for ~512 workgroups (two per CU; each keeps four steps of copies in
-  // flight) with >= 8 contraction steps each, a multiple of 4.
+  // Aim for ~256 workgroups (one per CU; each keeps three steps of copies
+  // in flight) with >= 8 contraction steps each, a multiple of 4.  Measured
+  // on the 7B MLP shapes, 256 beat 512, 768 and 1024 (fewer splits write and
+  // re-read fewer fp32 partials), and a deeper 8-step copy queue did not help.
   SplitPlan p;
-  int64_t want = tiles >= 512 ? 1 : ceil_div(512, tiles);
+  int64_t want = tiles >= 256 ? 1 : ceil_div(256, tiles);
   want = std::max<int64_t>(1, std::min<int64_t>(want, steps / 8 > 0 ? steps / 8 : 1));
   p.steps_per_split = (int)(ceil_div(ceil_div(steps, want), 4) * 4);
   p.splits = (int)ceil_div(steps, p.steps_per_split);

@@ -115,6 +115,50 @@ def test_zero_weight_and_empty_batch(q):
     assert torch.all(dA.float() == 0) and torch.all(dB.float() == 0)
 
 
+def test_repeat_calls_and_shared_workspace(q):
+    """Calls are deterministic (every reduction has a fixed order): the same
+    inputs give identical bits on a second call, also after another problem
+    ran through the same workspace; the smaller problem, run after the larger
+    one left its partial sums behind, still matches the oracle."""
+    cases = [(640, 512, 300, 64, 16.0, 21), (200, 192, 37, 8, -2.0, 22)]
+    lins, data = [], []
+    for n, k, m, r, alpha, seed in cases:
+        W = I.custom_weight(n, k, seed)
+        X = I.custom_bf16((m, k), seed, 1)
+        dY = I.custom_bf16((m, n), seed, 2)
+        A = I.custom_bf16((r, k), seed, 3, bound=0.05)
+        B = I.custom_bf16((n, r), seed, 4, bound=0.05)
+        lins.append(Linear(q, gpu_quantize(q, W), X, A, B, r, alpha))
+        data.append((W, X, A, B, dY, alpha))
+    ws = torch.empty(max(int(l.ws.numel()) for l in lins), dtype=torch.uint8, device="cuda")
+    for l in lins:
+        l.ws = ws
+
+    def run(i):
+        Y, H = lins[i].fwd()
+        dX, dA, dB = lins[i].bwd(data[i][4], H=H)
+        torch.cuda.synchronize()
+        return [t.clone() for t in (Y, H, dX, dA, dB)]
+
+    first = [run(0), run(1)]
+    again = [run(1), run(0)][::-1]
+    for i in range(2):
+        for name, a, b in zip(("Y", "H", "dX", "dA", "dB"), first[i], again[i]):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), \
+                f"case {i} {name} differs between calls"
+    W, X, A, B, dY, alpha = data[1]
+    What = bf16_f64(OracleWeight(W).row_what_bits(np.arange(W.shape[0])))
+    Xf, Af, Bf, dYf = bf16_f64(X), bf16_f64(A), bf16_f64(B), bf16_f64(dY)
+    Yr, Hr = fwd(Xf, What, Af, Bf, alpha)
+    dXr, dAr, dBr, _ = bwd(Xf, dYf, What, Af, Bf, alpha)
+    Y, H, dX, dA, dB = again[1]
+    for name, got, ref in (("Y", bf16_f64(host_bf16(Y)), Yr), ("H", H.cpu().numpy(), Hr),
+                           ("dX", bf16_f64(host_bf16(dX)), dXr), ("dA", bf16_f64(host_bf16(dA)), dAr),
+                           ("dB", bf16_f64(host_bf16(dB)), dBr)):
+        assert_close(got, ref, f"shared workspace {name}")
+
+
 def _sampled(q, wname, li, m=None, backward=True):
     """Full-size layer: Y and H on sampled rows/columns, dX and dA on sampled
     64-column blocks over all M, dB on sampled rows."""
