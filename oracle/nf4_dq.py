@@ -35,6 +35,11 @@ repeated at the function that applies it):
   * the 8-bit float is OCP E4M3FN, round to nearest, ties to even;
   * block scale s = (decode(code8) * group constant) + mean, two separately
     rounded float32 operations; weight = bf16_rne(float32(q[code] * s)).
+  * the Float4 (E2M1) storage type of the teardown's data-type comparison
+    (section 'Why NF4 rather than any 4-bit type' of the reading note) uses
+    the same blockwise rule with the OCP E2M1 value set divided by its
+    largest magnitude 6 (see fp4_e2m1_codebook); everything else, double
+    quantization included, is unchanged.
 """
 from __future__ import annotations
 
@@ -97,6 +102,53 @@ def nf4_codebook() -> np.ndarray:
     negative = [F32(-nd.inv_cdf(float(p))) for p in _prob_grid_f32(delta, 8)[:-1]]
     levels = np.array(sorted(positive + [F32(0.0)] + negative), dtype=F32)
     return (levels / levels.max()).astype(F32)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """OCP E2M1 4-bit float -> float32 (exact).
+
+    Format (OCP microscaling FP4): 1 sign bit, 2 exponent bits with bias 1,
+    1 mantissa bit; exponent field 0 is subnormal (m * 2^-1 * 2^(1-1) =
+    m / 2); no infinity or NaN.  Values: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return (sign * mag).astype(F32)
+
+
+def fp4_e2m1_codebook() -> np.ndarray:
+    """The Float4 (E2M1) level set as 16 float32 levels, ascending.
+
+    [reading note, 'Why NF4 rather than any 4-bit type': Float4 (E2M1) is
+    one of the 4-bit storage types NF4 is compared with].  The pages name
+    the format only.  Reading: the distinct values of the OCP E2M1 format
+    (its +0 and -0 are one level, so there are 15), divided in float32 by
+    the largest magnitude 6 so that the block absmax lands on +-1 exactly as
+    for NF4; code j is the j-th level in ascending order.  Code 15 is never
+    produced by the nearest-level rule (it repeats the top level 1.0, and
+    ties go to the lower index); it decodes as 1.0.  The codes are indices
+    into this list, not E2M1 bit patterns.
+    """
+    vals = np.unique(e2m1_decode(np.arange(16, dtype=np.uint8)).astype(F64))  # 15 distinct, ascending
+    vals = np.where(vals == 0.0, 0.0, vals)                                    # the zero level is +0
+    levels = (vals.astype(F32) / F32(6.0)).astype(F32)
+    return np.concatenate([levels, levels[-1:]]).astype(F32)
+
+
+CODEBOOKS = ("nf4", "fp4")
+
+
+def codebook_levels(codebook: str = "nf4") -> np.ndarray:
+    """The 16 float32 levels of a storage type: 'nf4' (the default, NormalFloat)
+    or 'fp4' (Float4 E2M1)."""
+    if codebook == "nf4":
+        return nf4_codebook()
+    if codebook == "fp4":
+        return fp4_e2m1_codebook()
+    raise ValueError(f"unknown codebook {codebook!r}")
 
 
 # --------------------------------------------------------------------------
@@ -315,8 +367,9 @@ def storage_sizes(n: int, k: int):
     return n * k // 2, nb, -(-nb // GROUP)
 
 
-def quantize_nf4_dq(W) -> dict:
-    """NF4 + DQ encoding of a float32 weight W [n, k] (row-major, k % 64 == 0).
+def quantize_nf4_dq(W, codebook: str = "nf4") -> dict:
+    """NF4 + DQ encoding of a float32 weight W [n, k] (row-major, k % 64 == 0);
+    ``codebook='fp4'`` stores Float4 (E2M1) codes instead of NF4.
 
     [explainer steps 1-3; teardown sec. 3].  Returns a dict with the stored
     buffers ``packed``, ``scale_code``, ``group_amax``, ``offset`` and the
@@ -325,7 +378,7 @@ def quantize_nf4_dq(W) -> dict:
     W = np.asarray(W, dtype=F32)
     if W.ndim != 2 or W.shape[1] % BLOCK or W.size == 0:
         raise ValueError("W must be [n, k] with n >= 1, k >= 64 and k % 64 == 0")
-    codes, absmax = blockwise_quantize(W.reshape(-1), nf4_codebook(), BLOCK)
+    codes, absmax = blockwise_quantize(W.reshape(-1), codebook_levels(codebook), BLOCK)
     offset = dq_offset(absmax)
     scale_code, group_amax = dq_encode(absmax, offset)
     return {
@@ -339,7 +392,7 @@ def quantize_nf4_dq(W) -> dict:
     }
 
 
-def dequant_bf16(packed, scale_code, group_amax, offset, n: int, k: int) -> np.ndarray:
+def dequant_bf16(packed, scale_code, group_amax, offset, n: int, k: int, codebook: str = "nf4") -> np.ndarray:
     """W_hat [n, k] as bfloat16 bit patterns (uint16).
 
     [explainer step 4; teardown sec. 4 'Dequantization Helper':
@@ -350,13 +403,13 @@ def dequant_bf16(packed, scale_code, group_amax, offset, n: int, k: int) -> np.n
     if codes.size != n * k:
         raise ValueError("packed size does not match n*k")
     s = dq_block_scale(scale_code, group_amax, offset)
-    return dequant_blocks_bf16(codes.reshape(-1, BLOCK), s).reshape(n, k)
+    return dequant_blocks_bf16(codes.reshape(-1, BLOCK), s, codebook).reshape(n, k)
 
 
-def dequant_blocks_bf16(codes, scales) -> np.ndarray:
+def dequant_blocks_bf16(codes, scales, codebook: str = "nf4") -> np.ndarray:
     """w_hat = bf16_rne(float32(q[code] * s_b)) for blocks of codes
     [nblk, 64] with their block scales s_b [nblk] (any subset of blocks)."""
-    q = nf4_codebook()[np.asarray(codes, dtype=np.uint8)].reshape(-1, BLOCK)
+    q = codebook_levels(codebook)[np.asarray(codes, dtype=np.uint8)].reshape(-1, BLOCK)
     prod = (q * np.asarray(scales, dtype=F32)[:, None]).astype(F32)
     return bf16_rne_bits(prod)
 

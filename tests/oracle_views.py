@@ -12,15 +12,16 @@ from oracle import linear, nf4_dq
 
 
 class OracleWeight:
-    def __init__(self, W: np.ndarray):
+    def __init__(self, W: np.ndarray, codebook: str = "nf4"):
         self.W = np.asarray(W, np.float32)
+        self.codebook = codebook
         self.n, self.k = self.W.shape
         self.kb = self.k // nf4_dq.BLOCK
         self.absmax = nf4_dq.block_absmax(self.W)
         self.offset = nf4_dq.dq_offset(self.absmax)
         self.scale_code, self.group_amax = nf4_dq.dq_encode(self.absmax, self.offset)
         self.s = nf4_dq.dq_block_scale(self.scale_code, self.group_amax, self.offset)
-        self.levels = nf4_dq.nf4_codebook()
+        self.levels = nf4_dq.codebook_levels(codebook)
 
     def row_codes(self, rows) -> np.ndarray:
         codes, _ = nf4_dq.blockwise_quantize(self.W[rows], self.levels, nf4_dq.BLOCK)
@@ -32,7 +33,7 @@ class OracleWeight:
     def row_what_bits(self, rows) -> np.ndarray:
         rows = np.asarray(rows)
         blk = (rows[:, None] * self.kb + np.arange(self.kb)[None, :]).reshape(-1)
-        return nf4_dq.dequant_blocks_bf16(self.row_codes(rows), self.s[blk]).reshape(len(rows), self.k)
+        return nf4_dq.dequant_blocks_bf16(self.row_codes(rows), self.s[blk], self.codebook).reshape(len(rows), self.k)
 
     def colblock_what_bits(self, kblocks) -> np.ndarray:
         """W_hat[:, 64*b : 64*b+64] for each block column b, concatenated."""
@@ -41,11 +42,11 @@ class OracleWeight:
             sub = self.W[:, 64 * b:64 * b + 64]
             codes, _ = nf4_dq.blockwise_quantize(sub, self.levels, nf4_dq.BLOCK)
             s = self.s[np.arange(self.n) * self.kb + b]
-            parts.append(nf4_dq.dequant_blocks_bf16(codes, s).reshape(self.n, 64))
+            parts.append(nf4_dq.dequant_blocks_bf16(codes, s, self.codebook).reshape(self.n, 64))
         return np.concatenate(parts, axis=1)
 
     def encoding(self) -> dict:
-        enc = nf4_dq.quantize_nf4_dq(self.W)
+        enc = nf4_dq.quantize_nf4_dq(self.W, self.codebook)
         return {k: enc[k] for k in ("packed", "scale_code", "group_amax", "offset")}
 
 

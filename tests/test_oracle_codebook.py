@@ -69,3 +69,50 @@ def test_q6_is_the_constructed_float_not_the_parsed_decimal():
     q = nf4_dq.nf4_codebook()
     assert q.view(np.uint32)[6] == 0xBDBA7871
     assert np.float32(-0.09105004).view(np.uint32) == 0xBDBA7872
+
+
+# --------------------------------------------------------------------------
+# Float4 (E2M1): the comparison storage type of the reading note's
+# 'Why NF4 rather than any 4-bit type' table.  Pins from the OCP E2M1
+# format constants (largest normal 6, smallest normal 1, subnormal step 0.5,
+# one mantissa bit so two values per binade) rather than from the decoder.
+# --------------------------------------------------------------------------
+def test_fp4_levels_from_format_constants():
+    q = nf4_dq.fp4_e2m1_codebook()
+    assert q.dtype == np.float32 and q.shape == (16,)
+    mags = [0.5]                                   # the one subnormal step
+    for e in range(0, 3):                          # binades [1, 2), [2, 4), [4, 8) up to 6
+        mags += [2.0 ** e, 1.5 * 2.0 ** e]
+    assert max(mags) == 6.0
+    expect = sorted({-m for m in mags} | {0.0} | set(mags))
+    assert len(expect) == 15
+    distinct = np.array(q[:15], np.float64)
+    assert np.all(np.diff(distinct) > 0)
+    # each level is the float32 rounding of value / 6, the zero level is +0,
+    # and the unused code 15 repeats the top level
+    assert np.array_equal(q[:15], (np.array(expect, np.float32) / np.float32(6.0)).astype(np.float32))
+    assert q[7] == 0 and not np.signbit(q[7])
+    assert q[15] == q[14] == np.float32(1.0) and q[0] == np.float32(-1.0)
+
+
+def test_fp4_decoder_covers_all_sixteen_bit_patterns():
+    vals = nf4_dq.e2m1_decode(np.arange(16, dtype=np.uint8)).astype(np.float64)
+    assert sorted(set(np.abs(vals))) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.array_equal(vals[8:], -vals[:8])      # the sign bit is the top bit
+
+
+def test_fp4_nearest_level_brute_force_and_ties():
+    q = nf4_dq.fp4_e2m1_codebook()
+    rng = np.random.default_rng(5)
+    x = rng.uniform(-1, 1, 20000).astype(np.float32)
+    got = nf4_dq.nearest_level(x, q)
+    d = np.abs(x.astype(np.float64)[:, None] - q.astype(np.float64)[None, :])
+    assert np.array_equal(got, np.argmin(d, axis=1))
+    assert got.max() <= 14                             # code 15 never produced
+    # worked values: 0.3 sits nearer 1/3 than 1/4; +-1 and 0 hit their levels
+    assert nf4_dq.nearest_level(np.float32([0.3, 1.0, -1.0, 0.0, 0.04]), q).tolist() == [11, 14, 0, 7, 7]
+    # the float32 neighbours of the exact midpoint 7/24 between 1/4 and 1/3
+    mid = np.float32(7.0 / 24.0)
+    below, above = np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1))
+    lo = 10 if float(mid) <= 7.0 / 24.0 else 11
+    assert nf4_dq.nearest_level(np.float32([below, mid, above]), q).tolist() == [10, lo, 11]

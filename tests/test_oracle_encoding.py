@@ -272,6 +272,30 @@ def test_reconstruction_error_is_plausible():
     assert 0.08 < rel < 0.10
 
 
+def test_fp4_encoding_error_bound_and_shared_constants():
+    # Float4 (E2M1) storage keeps the same block constants (they depend on
+    # the absmax values only) and bounds each error by half the widest gap
+    # of the level set (1/3 between 2/3 and 1, so absmax/6), plus the
+    # block-scale error and the bf16 rounding of the product.
+    rng = np.random.default_rng(19)
+    w = (rng.standard_normal((96, 512)) * 0.02).astype(F32)
+    e4, nf = nf4_dq.quantize_nf4_dq(w, "fp4"), nf4_dq.quantize_nf4_dq(w)
+    for key in ("scale_code", "group_amax", "offset", "absmax"):
+        assert np.array_equal(np.asarray(e4[key]), np.asarray(nf[key]))
+    assert e4["codes"].max() <= 14
+    wh = nf4_dq.bf16_bits_to_f64(nf4_dq.dequant_bf16(e4["packed"], e4["scale_code"], e4["group_amax"],
+                                                     e4["offset"], 96, 512, codebook="fp4")).reshape(-1, 64)
+    s = nf4_dq.dq_block_scale(e4["scale_code"], e4["group_amax"], e4["offset"]).astype(np.float64)
+    a = e4["absmax"].astype(np.float64)
+    bound = a / 6 + np.abs(s - a) + 2.0 ** -8 * np.abs(s) + 1e-12
+    assert np.all(np.abs(wh - w.reshape(-1, 64).astype(np.float64)) <= bound[:, None])
+    # coarser than NF4 on normal weights, as the reading note's table has it
+    wn = nf4_dq.bf16_bits_to_f64(nf4_dq.dequant_bf16(nf["packed"], nf["scale_code"], nf["group_amax"],
+                                                     nf["offset"], 96, 512)).reshape(-1, 64)
+    ref = w.reshape(-1, 64).astype(np.float64)
+    assert np.mean((wh - ref) ** 2) > np.mean((wn - ref) ** 2)
+
+
 # ------------------------------------------------------------ bit arithmetic
 def test_bits_per_weight_from_buffers():
     g = _golden()["bits_per_weight"]
