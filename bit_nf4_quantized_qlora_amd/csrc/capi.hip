@@ -10,25 +10,30 @@
 
 namespace qlora {
 
-const Thresholds &nf4_thresholds() {
-  // T_j = smallest float32 strictly above the exact midpoint of levels j and
-  // j+1 (the midpoint of two float32 values is exact in double).  Then
-  // x >= T_j <=> x is nearer to a level above j, with an exact tie at the
-  // midpoint going to the lower level.
-  static const Thresholds T = [] {
-    Thresholds t;
-    for (int j = 0; j < 15; ++j) {
-      float a, b;
-      std::memcpy(&a, &kNF4Bits[j], 4);
-      std::memcpy(&b, &kNF4Bits[j + 1], 4);
-      const double mid = ((double)a + (double)b) * 0.5;
-      float v = (float)mid;
-      if ((double)v <= mid) v = std::nextafter(v, INFINITY);
-      t.t[j] = v;
-    }
-    return t;
-  }();
-  return T;
+namespace {
+// T_j = smallest float32 strictly above the exact midpoint of levels j and
+// j+1 (the midpoint of two float32 values is exact in double).  Then x >= T_j
+// <=> x is nearer to a level above j, with an exact tie at the midpoint going
+// to the lower level.  (Float4's repeated top level gives T_14 just above 1,
+// which no normalized weight reaches: code 15 is never produced.)
+Thresholds thresholds_of(const uint32_t *bits) {
+  Thresholds t;
+  for (int j = 0; j < 15; ++j) {
+    float a, b;
+    std::memcpy(&a, &bits[j], 4);
+    std::memcpy(&b, &bits[j + 1], 4);
+    const double mid = ((double)a + (double)b) * 0.5;
+    float v = (float)mid;
+    if ((double)v <= mid) v = std::nextafter(v, INFINITY);
+    t.t[j] = v;
+  }
+  return t;
+}
+}  // namespace
+
+const Thresholds &codebook_thresholds(int codebook) {
+  static const Thresholds nf4 = thresholds_of(kNF4Bits), fp4 = thresholds_of(kFP4Bits);
+  return codebook == kCodebookFP4 ? fp4 : nf4;
 }
 
 namespace {
@@ -68,6 +73,8 @@ int check_weight(const qlora_nf4_weight *w) {
     return fail(QLORA_ERR_NULL_ARG, "a weight buffer is NULL");
   if (!aligned16(w->packed) || !aligned16(w->scale_code) || !aligned16(w->group_amax) || !aligned16(w->offset))
     return fail(QLORA_ERR_MISALIGNED, "weight buffers must be 16-byte aligned");
+  if (w->codebook != QLORA_CODEBOOK_NF4 && w->codebook != QLORA_CODEBOOK_FP4_E2M1)
+    return fail(QLORA_ERR_BAD_CODEBOOK, "codebook %d is neither NF4 (0) nor Float4 E2M1 (1)", (int)w->codebook);
   return QLORA_OK;
 }
 
@@ -81,6 +88,7 @@ Nf4View view_of(const qlora_nf4_weight *w) {
   v.scale_code = w->scale_code;
   v.group_amax = w->group_amax;
   v.offset = w->offset;
+  v.codebook = w->codebook;
   return v;
 }
 
@@ -141,7 +149,7 @@ int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws,
   const int64_t nb = out->n * out->k / kBlock;
   float *ws_absmax = static_cast<float *>(ws);
   double *ws_sum = reinterpret_cast<double *>(static_cast<char *>(ws) + align_up((size_t)nb * sizeof(float), 256));
-  hipError_t e = launch_quantize(W, out->n, out->k, out->packed, out->scale_code, out->group_amax, out->offset,
+  hipError_t e = launch_quantize(W, out->n, out->k, out->codebook, out->packed, out->scale_code, out->group_amax, out->offset,
                                  ws_absmax, ws_sum, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "qlora_quantize_nf4_dq");
   return QLORA_OK;
@@ -199,13 +207,25 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
   return QLORA_OK;
 }
 
-void qlora_nf4_codebook(float out[16]) {
-  for (int j = 0; j < 16; ++j) std::memcpy(&out[j], &kNF4Bits[j], 4);
+void qlora_nf4_codebook(float out[16]) { qlora_codebook(QLORA_CODEBOOK_NF4, out); }
+
+void qlora_nf4_thresholds(float out[15]) { qlora_thresholds(QLORA_CODEBOOK_NF4, out); }
+
+int qlora_codebook(int codebook, float out[16]) {
+  if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_FP4_E2M1)
+    return fail(QLORA_ERR_BAD_CODEBOOK, "unknown codebook %d", codebook);
+  if (!out) return fail(QLORA_ERR_NULL_ARG, "out is NULL");
+  for (int j = 0; j < 16; ++j) std::memcpy(&out[j], &codebook_bits(codebook)[j], 4);
+  return QLORA_OK;
 }
 
-void qlora_nf4_thresholds(float out[15]) {
-  const Thresholds &t = nf4_thresholds();
+int qlora_thresholds(int codebook, float out[15]) {
+  if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_FP4_E2M1)
+    return fail(QLORA_ERR_BAD_CODEBOOK, "unknown codebook %d", codebook);
+  if (!out) return fail(QLORA_ERR_NULL_ARG, "out is NULL");
+  const Thresholds &t = codebook_thresholds(codebook);
   for (int j = 0; j < 15; ++j) out[j] = t.t[j];
+  return QLORA_OK;
 }
 
 const char *qlora_strerror(int status) {
@@ -218,6 +238,7 @@ const char *qlora_strerror(int status) {
     case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
     case QLORA_ERR_HIP: return "HIP runtime error";
     case QLORA_ERR_BAD_ALPHA: return "alpha is not finite";
+    case QLORA_ERR_BAD_CODEBOOK: return "unknown codebook";
     default: return "unknown status";
   }
 }

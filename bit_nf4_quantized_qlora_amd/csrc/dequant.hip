@@ -18,11 +18,11 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ pa
                                                  const uint8_t *__restrict__ scale_code,
                                                  const float *__restrict__ group_amax,
                                                  const float *__restrict__ offset_p, int64_t ndw,
-                                                 u32x4_t *__restrict__ out) {
+                                                 int codebook, u32x4_t *__restrict__ out) {
   // packed/out start at this launch's first dword, scale_code/group_amax at
   // its first block and group (slices start on group boundaries); ndw < 2^29
   __shared__ float2 s_pair[256];
-  fill_pair_table(s_pair, threadIdx.x, 256);
+  fill_pair_table(s_pair, threadIdx.x, 256, codebook);
   const int lane = threadIdx.x & 63;
   const int64_t wave_base = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 256;
   // All four steps' loads go out before any is used (past the end: zeros
@@ -67,7 +67,8 @@ hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s) {
     const int64_t grid = ceil_div(ndw, 4 * 256);
     QLORA_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(256), 0, s,
                  reinterpret_cast<const uint32_t *>(w.packed) + d0, w.scale_code + d0 / 8,
-                 w.group_amax + d0 / 8 / kGroup, w.offset, ndw, reinterpret_cast<u32x4_t *>(out) + d0);
+                 w.group_amax + d0 / 8 / kGroup, w.offset, ndw, w.codebook,
+                 reinterpret_cast<u32x4_t *>(out) + d0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

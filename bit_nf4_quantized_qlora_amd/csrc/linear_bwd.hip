@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(Nf4View w, const uint16_t *__
   const int64_t N = w.n, K = w.k, nkb = K / kBlock;
   const int64_t k0 = (int64_t)blockIdx.x * DBK, m0 = (int64_t)blockIdx.y * DBM;
   const int64_t nsteps = ceil_div_d(N, 64);
-  fill_pair_table(s_pair, tid, 256);
+  fill_pair_table(s_pair, tid, 256, w.codebook);
   const float offset = *w.offset;
   const bool dyvec = (N % 8) == 0;
 

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   const int64_t nk = NC / kBlock;                      // 64-wide steps
   const int64_t nsup = kBwd ? tile_bwd_nsup(N) : tile_fwd_nsup(K);
   const int64_t nk8 = ceil_div_d(nk, 8) * 8;  // steps run: whole 8-step rounds
-  fill_pair_table(s_pair, tid, 256);
+  fill_pair_table(s_pair, tid, 256, w.codebook);
 
   // B rows m0 .. m0+255 (row stride NC): wave-instruction i fills LDS chunks
   // [512w + 64i, +64): row 64w + 8i + lane/8, physical chunk lane & 7, so the

@@ -33,6 +33,19 @@ constexpr uint32_t kNF4Bits[16] = {
     0xbdba7871u, 0x00000000u, 0x3da2faffu, 0x3e24cae3u, 0x3e7c04ddu, 0x3ead033au,
     0x3ee1a4b8u, 0x3f1007abu, 0x3f3913b3u, 0x3f800000u};
 
+// The Float4 (E2M1) storage type that "QLoRA Paper Breakdown"'s reading note
+// compares NF4 with: the 15 distinct OCP E2M1 values (+-{0, 0.5, 1, 1.5, 2,
+// 3, 4, 6}) divided by 6 in float32, ascending; code 15 repeats 1.0 and is
+// never produced by the nearest-level rule.
+constexpr uint32_t kFP4Bits[16] = {
+    0xbf800000u, 0xbf2aaaabu, 0xbf000000u, 0xbeaaaaabu, 0xbe800000u, 0xbe2aaaabu,
+    0xbdaaaaabu, 0x00000000u, 0x3daaaaabu, 0x3e2aaaabu, 0x3e800000u, 0x3eaaaaabu,
+    0x3f000000u, 0x3f2aaaabu, 0x3f800000u, 0x3f800000u};
+
+// Storage types (the codebook field of a weight): 0 NF4, 1 Float4 (E2M1).
+constexpr int kCodebookNF4 = 0, kCodebookFP4 = 1;
+__host__ __device__ constexpr const uint32_t *codebook_bits(int cb) { return cb == kCodebookFP4 ? kFP4Bits : kNF4Bits; }
+
 // Nearest-level decision thresholds, passed by value as a kernel argument
 // (so they live in scalar registers): code = #{ j : x >= t[j] }.
 struct Thresholds {
@@ -92,10 +105,10 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
 // Level c (0..15) selected in registers by the bits of c: a per-lane index
 // into the constant array would become a memory load whose wait holds up
 // the copies a kernel issues next.
-__device__ __forceinline__ uint32_t nf4_level_bits(uint32_t c) {
+__device__ __forceinline__ uint32_t nf4_level_bits(uint32_t c, int cb) {
   uint32_t v[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = kNF4Bits[j];
+  for (int j = 0; j < 16; ++j) v[j] = cb == kCodebookFP4 ? kFP4Bits[j] : kNF4Bits[j];
 #pragma unroll
   for (int b = 0, n = 8; b < 4; ++b, n >>= 1) {
     const uint32_t m = 0u - ((c >> b) & 1u);
@@ -105,9 +118,9 @@ __device__ __forceinline__ uint32_t nf4_level_bits(uint32_t c) {
   return v[0];
 }
 
-__device__ __forceinline__ void fill_pair_table(float2 *table, int tid, int nthreads) {
+__device__ __forceinline__ void fill_pair_table(float2 *table, int tid, int nthreads, int cb) {
   for (int e = tid; e < 256; e += nthreads)
-    table[e] = make_float2(__uint_as_float(nf4_level_bits(e & 15)), __uint_as_float(nf4_level_bits(e >> 4)));
+    table[e] = make_float2(__uint_as_float(nf4_level_bits(e & 15, cb)), __uint_as_float(nf4_level_bits(e >> 4, cb)));
 }
 
 // Eight codes (one packed dword) -> eight bf16 weights in four dwords.

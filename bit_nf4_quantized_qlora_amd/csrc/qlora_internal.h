@@ -18,14 +18,16 @@ struct Nf4View {
   const uint8_t *scale_code;
   const float *group_amax;
   const float *offset;
+  int codebook;  // kCodebookNF4 or kCodebookFP4
 };
 
-const Thresholds &nf4_thresholds();
+// Decision thresholds of a codebook (kCodebookNF4 / kCodebookFP4).
+const Thresholds &codebook_thresholds(int codebook);
 
 // quantize.hip
-hipError_t launch_quantize(const float *W, int64_t n, int64_t k, uint8_t *packed, uint8_t *scale_code,
-                           float *group_amax, float *offset, float *ws_absmax, double *ws_group_sum,
-                           hipStream_t s);
+hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, uint8_t *packed,
+                           uint8_t *scale_code, float *group_amax, float *offset, float *ws_absmax,
+                           double *ws_group_sum, hipStream_t s);
 
 // dequant.hip
 hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s);

@@ -29,13 +29,18 @@ QLORA_ERR_MISALIGNED = -4
 QLORA_ERR_WORKSPACE = -5
 QLORA_ERR_HIP = -6
 QLORA_ERR_BAD_ALPHA = -7
+QLORA_ERR_BAD_CODEBOOK = -8
+
+QLORA_CODEBOOK_NF4 = 0        # NormalFloat4, the method's storage type
+QLORA_CODEBOOK_FP4_E2M1 = 1   # Float4 (E2M1), the comparison type
+CODEBOOKS = {"nf4": QLORA_CODEBOOK_NF4, "fp4": QLORA_CODEBOOK_FP4_E2M1}
 
 _c_i64, _c_int, _c_float, _c_size, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
 
 class qlora_nf4_weight(ctypes.Structure):
     _fields_ = [("n", _c_i64), ("k", _c_i64), ("packed", _vp), ("scale_code", _vp), ("group_amax", _vp),
-                ("offset", _vp)]
+                ("offset", _vp), ("codebook", ctypes.c_int32)]
 
 
 _W = ctypes.POINTER(qlora_nf4_weight)
@@ -51,6 +56,8 @@ _SIGS = {
                                   _c_size, _vp]),
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_nf4_thresholds": (None, [ctypes.POINTER(ctypes.c_float)]),
+    "qlora_codebook": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
+    "qlora_thresholds": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
     "qlora_strerror": (ctypes.c_char_p, [_c_int]),
     "qlora_profile_begin": (_c_int, []),
     "qlora_profile_end": (_c_int, []),
@@ -102,18 +109,19 @@ class NF4Weight:
     scale_code: torch.Tensor  # uint8 [n*k/64]
     group_amax: torch.Tensor  # float32 [ceil(n*k/64/256)]
     offset: torch.Tensor      # float32 [1]
+    codebook: int = QLORA_CODEBOOK_NF4
 
     @staticmethod
-    def empty(n: int, k: int, device="cuda") -> "NF4Weight":
+    def empty(n: int, k: int, device="cuda", codebook: int = QLORA_CODEBOOK_NF4) -> "NF4Weight":
         pb, sb, ng = qlora_nf4_sizes(n, k)
         return NF4Weight(n, k, torch.empty(pb, dtype=torch.uint8, device=device),
                          torch.empty(sb, dtype=torch.uint8, device=device),
                          torch.empty(ng, dtype=torch.float32, device=device),
-                         torch.empty(1, dtype=torch.float32, device=device))
+                         torch.empty(1, dtype=torch.float32, device=device), codebook)
 
     def c_struct(self) -> qlora_nf4_weight:
         return qlora_nf4_weight(self.n, self.k, self.packed.data_ptr(), self.scale_code.data_ptr(),
-                                self.group_amax.data_ptr(), self.offset.data_ptr())
+                                self.group_amax.data_ptr(), self.offset.data_ptr(), self.codebook)
 
 
 def qlora_nf4_sizes(n: int, k: int):
@@ -188,6 +196,18 @@ def qlora_nf4_codebook():
 def qlora_nf4_thresholds():
     buf = (ctypes.c_float * 15)()
     _lib.qlora_nf4_thresholds(buf)
+    return list(buf)
+
+
+def qlora_codebook(codebook: int):
+    buf = (ctypes.c_float * 16)()
+    _check("qlora_codebook", _lib.qlora_codebook(codebook, buf))
+    return list(buf)
+
+
+def qlora_thresholds(codebook: int):
+    buf = (ctypes.c_float * 15)()
+    _check("qlora_thresholds", _lib.qlora_thresholds(codebook, buf))
     return list(buf)
 
 

@@ -47,7 +47,22 @@ enum {
   QLORA_ERR_MISALIGNED = -4,  /* a tensor pointer is not 16-byte aligned              */
   QLORA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes */
   QLORA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed           */
-  QLORA_ERR_BAD_ALPHA = -7    /* alpha is not finite                                  */
+  QLORA_ERR_BAD_ALPHA = -7,   /* alpha is not finite                                  */
+  QLORA_ERR_BAD_CODEBOOK = -8 /* the weight's codebook is not one of QLORA_CODEBOOK_* */
+};
+
+/*
+ * 4-bit storage types (the `codebook` field of a weight).  NF4 is the
+ * method's own ("QLoRA Paper Breakdown" sec. 2).  Float4 (E2M1) is the
+ * 4-bit float the reading note's data-type comparison ranks below it
+ * ("Why NF4 rather than any 4-bit type"): the 15 distinct OCP E2M1 values
+ * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6} divided by 6, ascending, code 15 repeating
+ * 1.0 (never produced).  Everything else -- blocks, the nearest-level rule,
+ * double quantization, dequantization -- is the same for both.
+ */
+enum {
+  QLORA_CODEBOOK_NF4 = 0,
+  QLORA_CODEBOOK_FP4_E2M1 = 1
 };
 
 /*
@@ -59,10 +74,11 @@ enum {
  */
 typedef struct qlora_nf4_weight {
   int64_t n, k;
-  uint8_t *packed;      /* [n*k/2] NF4 codes, byte i = code[2i] | code[2i+1] << 4      */
+  uint8_t *packed;      /* [n*k/2] 4-bit codes, byte i = code[2i] | code[2i+1] << 4    */
   uint8_t *scale_code;  /* [nb] OCP E4M3FN code of (absmax_b - offset) / group_amax_g   */
   float *group_amax;    /* [ng] second-level constant: max |absmax_b - offset| in g     */
   float *offset;        /* [1] per-tensor mean of the fp32 block absmax values          */
+  int32_t codebook;     /* QLORA_CODEBOOK_NF4 (0: a zero-filled descriptor) or _FP4_E2M1 */
 } qlora_nf4_weight;
 
 /* Sizes of the four buffers of an [n, k] weight.  Host only; no GPU use.
@@ -80,7 +96,8 @@ size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
  * "QLoRA, explained." steps 1-3; "QLoRA Paper Breakdown" sec. 3 Level 1 and
  * Level 2:
  *   absmax_b = max |w| over block b;  x = fp32(w / absmax_b) (0 if absmax_b=0)
- *   code = index of the nearest NF4 level (ties to the lower index)
+ *   code = index of the nearest level of w->codebook (NF4, or Float4 E2M1;
+ *          ties to the lower index)
  *   offset = fp32( (sum over groups, in order, of the fp64 in-order sum of the
  *            group's absmax) / nb )
  *   dev_b = fp32(absmax_b - offset); group_amax_g = max |dev_b| over g
@@ -95,7 +112,7 @@ int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws,
  * Dequantize to bfloat16: W_bf16 [n, k] (device).  "QLoRA Paper Breakdown"
  * sec. 4 Dequantization Helper; "QLoRA, explained." step 4:
  *   s_b = fp32( fp32(decode(scale_code_b) * group_amax_g) + offset )
- *   w_hat = bf16_round_nearest_even( fp32(q[code] * s_b) )
+ *   w_hat = bf16_round_nearest_even( fp32(q[code] * s_b) ), q = w->codebook's levels
  * Bit-for-bit identical to the operand the fused linear kernels use.
  */
 int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream);
@@ -139,6 +156,10 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
  * levels j and j+1; code = number of thresholds <= x). */
 void qlora_nf4_codebook(float out[16]);
 void qlora_nf4_thresholds(float out[15]);
+/* The same for any storage type (QLORA_CODEBOOK_*): QLORA_OK, or
+ * QLORA_ERR_BAD_CODEBOOK / QLORA_ERR_NULL_ARG with `out` untouched. */
+int qlora_codebook(int codebook, float out[16]);
+int qlora_thresholds(int codebook, float out[15]);
 
 /* Static text for a status code; per-thread detail of the last failure. */
 const char *qlora_strerror(int status);

@@ -56,12 +56,21 @@ def test_library_codebook_equals_oracle(q):
     from oracle import nf4_dq
     lib = np.array(q.qlora_nf4_codebook(), np.float32)
     assert np.array_equal(lib.view(np.uint32), nf4_dq.nf4_codebook().view(np.uint32))
+    for name, cb in q.CODEBOOKS.items():
+        lib = np.array(q.qlora_codebook(cb), np.float32)
+        assert np.array_equal(lib.view(np.uint32), nf4_dq.codebook_levels(name).view(np.uint32)), name
+    assert q.qlora_thresholds(q.QLORA_CODEBOOK_NF4) == q.qlora_nf4_thresholds()
+    for bad in (-1, 2, 7):
+        with pytest.raises(q.QloraError) as e:
+            q.qlora_codebook(bad)
+        assert e.value.status == q.QLORA_ERR_BAD_CODEBOOK
 
 
-def test_library_thresholds_are_the_exact_midpoint_successors(q):
+@pytest.mark.parametrize("name", ["nf4", "fp4"])
+def test_library_thresholds_are_the_exact_midpoint_successors(q, name):
     from oracle import nf4_dq
-    levels = nf4_dq.nf4_codebook()
-    t = np.array(q.qlora_nf4_thresholds(), np.float32)
+    levels = nf4_dq.codebook_levels(name)
+    t = np.array(q.qlora_thresholds(q.CODEBOOKS[name]), np.float32)
     for j in range(15):
         mid = (Fraction(float(levels[j])) + Fraction(float(levels[j + 1]))) / 2
         assert Fraction(float(t[j])) > mid
@@ -70,6 +79,7 @@ def test_library_thresholds_are_the_exact_midpoint_successors(q):
     # the threshold count reproduces the oracle's nearest level everywhere near them
     xs = np.concatenate([t, np.nextafter(t, np.float32(-np.inf), dtype=np.float32),
                          np.random.default_rng(0).uniform(-1, 1, 20000).astype(np.float32)])
+    xs = xs[np.abs(xs) <= 1]  # normalized weights; Float4's top threshold lies just above 1
     via_t = (xs[:, None] >= t[None, :]).sum(axis=1)
     assert np.array_equal(via_t, nf4_dq.nearest_level(xs, levels))
 
@@ -121,5 +131,9 @@ def test_argument_errors_enqueue_nothing(q):
     assert bwd(ctypes.byref(W), P, P, 16, P, P, 8, 16.0, None, P, None, P, P, 1 << 30, None) == q.QLORA_ERR_NULL_ARG
     assert bwd(ctypes.byref(W), P, P, 16, P, P, 8, 16.0, None, P, P, P, P, 64, None) == q.QLORA_ERR_WORKSPACE
     assert "r = 0" in (fwd(ctypes.byref(W), P, 16, P, P, 0, 16.0, P, None, P, 1 << 30, None) and q.qlora_last_error())
-    for code in range(-7, 1):
+    bad_cb = q.qlora_nf4_weight(64, 64, 16, 16, 16, 16, 3)
+    assert lib.qlora_quantize_nf4_dq(P, ctypes.byref(bad_cb), P, 1 << 20, None) == q.QLORA_ERR_BAD_CODEBOOK
+    assert lib.qlora_dequant_bf16(ctypes.byref(bad_cb), P, None) == q.QLORA_ERR_BAD_CODEBOOK
+    assert fwd(ctypes.byref(bad_cb), P, 16, P, P, 8, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_BAD_CODEBOOK
+    for code in range(-8, 1):
         assert q.qlora_strerror(code) != "unknown status"

@@ -26,15 +26,15 @@ def _gpu_dequant(q, w):
     return host_bf16(out)
 
 
-def _full_check(q, W, ctx):
-    note(f"[encoding] {ctx} shape={W.shape}")
+def _full_check(q, W, ctx, codebook="nf4"):
+    note(f"[encoding] {ctx} shape={W.shape} codebook={codebook}")
     n, k = W.shape
-    w = gpu_quantize(q, W)
+    w = gpu_quantize(q, W, codebook)
     got = encoding_to_host(w)
-    ref = nf4_dq.quantize_nf4_dq(W)
+    ref = nf4_dq.quantize_nf4_dq(W, codebook)
     assert_encoding_equal(got, ref, ctx)
     wh = _gpu_dequant(q, w)
-    ref_wh = nf4_dq.dequant_bf16(ref["packed"], ref["scale_code"], ref["group_amax"], ref["offset"], n, k)
+    ref_wh = nf4_dq.dequant_bf16(ref["packed"], ref["scale_code"], ref["group_amax"], ref["offset"], n, k, codebook)
     bad = np.flatnonzero(wh.reshape(-1) != ref_wh.reshape(-1))
     assert bad.size == 0, f"{ctx} dequant: {bad.size} differ, first {bad[:5]}"
 
@@ -44,12 +44,14 @@ def test_tiny_workload(q):
     _full_check(q, I.weight(w, 0), "tiny")
 
 
-def test_decision_thresholds_and_special_values(q):
+@pytest.mark.parametrize("codebook", ["nf4", "fp4"])
+def test_decision_thresholds_and_special_values(q, codebook):
     """Blocks whose absmax is exactly 1 carry the 15 thresholds, their float32
     neighbours, every level, signed zeros and subnormals; other blocks scale
     the same pattern, hold a single nonzero, or are all zero."""
-    t = np.array(q.qlora_nf4_thresholds(), np.float32)
-    lv = nf4_dq.nf4_codebook()
+    t = np.array(q.qlora_thresholds(q.CODEBOOKS[codebook]), np.float32)
+    t = t[t <= 1]  # Float4's top threshold lies above every normalized weight
+    lv = nf4_dq.codebook_levels(codebook)
     down = np.nextafter(t, np.float32(-np.inf), dtype=np.float32)
     vals = np.concatenate([t, down, lv, np.array([0.0, -0.0, 1e-45, -1e-45, 1e-38, -3e-39], np.float32)])
     rows = []
@@ -66,7 +68,13 @@ def test_decision_thresholds_and_special_values(q):
     single[1, 63] = 2.5
     single[2, 0] = 1e-40
     W = np.concatenate([scaled, single, np.zeros((3, 64), np.float32)]).astype(np.float32)
-    _full_check(q, W, "thresholds")
+    _full_check(q, W, "thresholds", codebook)
+
+
+@pytest.mark.parametrize("shape,seed", [((5, 3840), 31), ((300, 640), 32), ((1024, 4096), 33)])
+def test_fp4_encoding(q, shape, seed):
+    """Float4 (E2M1) storage: the same bit-exact bar on ragged and full groups."""
+    _full_check(q, I.custom_weight(*shape, seed=seed), f"fp4{shape}", "fp4")
 
 
 @pytest.mark.parametrize("shape,seed", [((1, 64), 1), ((5, 3840), 2), ((7, 64 * 37), 3), ((64, 4096), 4),
