@@ -392,6 +392,33 @@ def quantize_nf4_dq(W, codebook: str = "nf4") -> dict:
     }
 
 
+def quantize_single_level(W, codebook: str = "nf4") -> dict:
+    """Single-level blockwise quantization: the codes of quantize_nf4_dq and
+    one float32 constant per block, the block absmax itself, with no second
+    level.
+
+    [teardown sec. 3 'The Hidden Memory Overhead of Block Scales': one
+    float32 scale per 64 weights, 4 + 32/64 = 4.5 bits per parameter, the
+    layout double quantization improves on].  Returns ``packed``, ``absmax``
+    [nb] float32 and ``codes`` [n*k].
+    """
+    W = np.asarray(W, dtype=F32)
+    if W.ndim != 2 or W.shape[1] % BLOCK or W.size == 0:
+        raise ValueError("W must be [n, k] with n >= 1, k >= 64 and k % 64 == 0")
+    codes, absmax = blockwise_quantize(W.reshape(-1), codebook_levels(codebook), BLOCK)
+    return {"packed": pack_nibbles(codes), "absmax": absmax, "codes": codes.reshape(-1)}
+
+
+def dequant_single_level_bf16(packed, absmax, n: int, k: int, codebook: str = "nf4") -> np.ndarray:
+    """W_hat [n, k] bfloat16 bits for single-level constants: s_b = absmax_b,
+    w_hat = bf16_rne(float32(q[code] * absmax_b)) [teardown sec. 4 with the
+    float32 constant used as stored]."""
+    codes = unpack_nibbles(packed)
+    if codes.size != n * k:
+        raise ValueError("packed size does not match n*k")
+    return dequant_blocks_bf16(codes.reshape(-1, BLOCK), np.asarray(absmax, F32), codebook).reshape(n, k)
+
+
 def dequant_bf16(packed, scale_code, group_amax, offset, n: int, k: int, codebook: str = "nf4") -> np.ndarray:
     """W_hat [n, k] as bfloat16 bit patterns (uint16).
 

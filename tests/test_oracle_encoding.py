@@ -296,6 +296,34 @@ def test_fp4_encoding_error_bound_and_shared_constants():
     assert np.mean((wh - ref) ** 2) > np.mean((wn - ref) ** 2)
 
 
+@pytest.mark.parametrize("codebook", ["nf4", "fp4"])
+def test_single_level_constants(codebook):
+    # Single-level storage keeps the double-quantized layout's codes, stores
+    # each block absmax as is (4 + 32/64 = 4.5 bits, the teardown's figure)
+    # and so bounds each error by half the widest level gap times absmax
+    # plus the bf16 rounding alone: no block-scale error.
+    rng = np.random.default_rng(23)
+    w = (rng.standard_normal((64, 768)) * 0.02).astype(F32)
+    sl, dq = nf4_dq.quantize_single_level(w, codebook), nf4_dq.quantize_nf4_dq(w, codebook)
+    assert np.array_equal(sl["packed"], dq["packed"])
+    assert np.array_equal(sl["absmax"].view(np.uint32), dq["absmax"].view(np.uint32))
+    bits = 8 * (sl["packed"].nbytes + sl["absmax"].nbytes) / w.size
+    assert bits == 4 + 32 / 64 == float(_golden()["bits_per_weight"]["single_level_total"])
+    wh = nf4_dq.bf16_bits_to_f64(nf4_dq.dequant_single_level_bf16(sl["packed"], sl["absmax"], 64, 768, codebook))
+    lv = nf4_dq.codebook_levels(codebook).astype(np.float64)
+    half_gap = np.diff(lv).max() / 2
+    a = sl["absmax"].astype(np.float64)
+    err = np.abs(wh.reshape(-1, 64) - w.reshape(-1, 64).astype(np.float64))
+    assert np.all(err <= (half_gap + 2.0 ** -8) * a[:, None])
+    # a block whose weights are all levels times one absmax round-trips exactly
+    # up to bf16: w = q * 0.5 gives w_hat = bf16(q * 0.5)
+    lvl = nf4_dq.codebook_levels(codebook)
+    blk = (np.resize(lvl, 64) * np.float32(0.5)).astype(F32).reshape(1, 64)
+    e1 = nf4_dq.quantize_single_level(blk, codebook)
+    got = nf4_dq.dequant_single_level_bf16(e1["packed"], e1["absmax"], 1, 64, codebook)
+    assert np.array_equal(got.reshape(-1), nf4_dq.bf16_rne_bits(blk.reshape(-1)))
+
+
 # ------------------------------------------------------------ bit arithmetic
 def test_bits_per_weight_from_buffers():
     g = _golden()["bits_per_weight"]
