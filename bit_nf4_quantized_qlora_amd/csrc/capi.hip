@@ -69,12 +69,20 @@ int check_shape(int64_t n, int64_t k) {
 int check_weight(const qlora_nf4_weight *w) {
   if (!w) return fail(QLORA_ERR_NULL_ARG, "weight descriptor is NULL");
   if (int e = check_shape(w->n, w->k)) return e;
-  if (!w->packed || !w->scale_code || !w->group_amax || !w->offset)
-    return fail(QLORA_ERR_NULL_ARG, "a weight buffer is NULL");
-  if (!aligned16(w->packed) || !aligned16(w->scale_code) || !aligned16(w->group_amax) || !aligned16(w->offset))
-    return fail(QLORA_ERR_MISALIGNED, "weight buffers must be 16-byte aligned");
   if (w->codebook != QLORA_CODEBOOK_NF4 && w->codebook != QLORA_CODEBOOK_FP4_E2M1)
     return fail(QLORA_ERR_BAD_CODEBOOK, "codebook %d is neither NF4 (0) nor Float4 E2M1 (1)", (int)w->codebook);
+  if (w->scales != QLORA_SCALES_DQ && w->scales != QLORA_SCALES_FP32)
+    return fail(QLORA_ERR_BAD_CODEBOOK, "scales %d is neither DQ (0) nor FP32 (1)", (int)w->scales);
+  if (w->scales == QLORA_SCALES_DQ) {
+    if (!w->packed || !w->scale_code || !w->group_amax || !w->offset)
+      return fail(QLORA_ERR_NULL_ARG, "a weight buffer is NULL");
+    if (!aligned16(w->packed) || !aligned16(w->scale_code) || !aligned16(w->group_amax) || !aligned16(w->offset))
+      return fail(QLORA_ERR_MISALIGNED, "weight buffers must be 16-byte aligned");
+  } else {
+    if (!w->packed || !w->absmax) return fail(QLORA_ERR_NULL_ARG, "a weight buffer is NULL");
+    if (!aligned16(w->packed) || !aligned16(w->absmax))
+      return fail(QLORA_ERR_MISALIGNED, "weight buffers must be 16-byte aligned");
+  }
   return QLORA_OK;
 }
 
@@ -89,6 +97,7 @@ Nf4View view_of(const qlora_nf4_weight *w) {
   v.group_amax = w->group_amax;
   v.offset = w->offset;
   v.codebook = w->codebook;
+  v.absmax = w->scales == QLORA_SCALES_FP32 ? w->absmax : nullptr;
   return v;
 }
 
@@ -147,9 +156,10 @@ int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws,
   const size_t need = quantize_ws(out->n, out->k);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
   const int64_t nb = out->n * out->k / kBlock;
-  float *ws_absmax = static_cast<float *>(ws);
+  const bool single = out->scales == QLORA_SCALES_FP32;
+  float *ws_absmax = single ? out->absmax : static_cast<float *>(ws);
   double *ws_sum = reinterpret_cast<double *>(static_cast<char *>(ws) + align_up((size_t)nb * sizeof(float), 256));
-  hipError_t e = launch_quantize(W, out->n, out->k, out->codebook, out->packed, out->scale_code, out->group_amax, out->offset,
+  hipError_t e = launch_quantize(W, out->n, out->k, out->codebook, single, out->packed, out->scale_code, out->group_amax, out->offset,
                                  ws_absmax, ws_sum, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "qlora_quantize_nf4_dq");
   return QLORA_OK;

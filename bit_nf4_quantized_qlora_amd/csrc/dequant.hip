@@ -17,8 +17,9 @@ namespace {
 __global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ packed,
                                                  const uint8_t *__restrict__ scale_code,
                                                  const float *__restrict__ group_amax,
-                                                 const float *__restrict__ offset_p, int64_t ndw,
-                                                 int codebook, u32x4_t *__restrict__ out) {
+                                                 const float *__restrict__ offset_p,
+                                                 const float *__restrict__ absmax, int64_t ndw, int codebook,
+                                                 u32x4_t *__restrict__ out) {
   // packed/out start at this launch's first dword, scale_code/group_amax at
   // its first block and group (slices start on group boundaries); ndw < 2^29
   __shared__ float2 s_pair[256];
@@ -28,8 +29,12 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ pa
   // All four steps' loads go out before any is used (past the end: zeros
   // from the buffer ranges, nothing stored).
   const int64_t nb = (ndw + 7) / 8;
-  const __amdgpu_buffer_rsrc_t prs = rsrc(packed, ndw * 4), srs = rsrc(scale_code, nb),
-                               grs = rsrc(group_amax, ((nb + 255) / 256) * 4);
+  // single-level constants (absmax != NULL): s_b = absmax_b, read through
+  // the scale-code slot's resource; otherwise the double-quantized decode
+  const bool single = absmax != nullptr;
+  const __amdgpu_buffer_rsrc_t prs = rsrc(packed, ndw * 4),
+                               srs = single ? rsrc(absmax, nb * 4) : rsrc(scale_code, nb),
+                               grs = rsrc(single ? absmax : group_amax, single ? 0 : ((nb + 255) / 256) * 4);
   uint32_t word[4], c8[4];
   float ga[4];
 #pragma unroll
@@ -38,16 +43,21 @@ __global__ __launch_bounds__(256) void k_dequant(const uint32_t *__restrict__ pa
     const int64_t b = d >> 3;                        // 8 dwords per 64-weight block
     const bool in = d < ndw;
     word[step] = __builtin_amdgcn_raw_buffer_load_b32(prs, in ? (uint32_t)(d * 4) : 0x80000000u, 0, 2);
-    c8[step] = __builtin_amdgcn_raw_buffer_load_b8(srs, in ? (uint32_t)b : 0x80000000u, 0, 0);
-    ga[step] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, in ? (uint32_t)((b >> 8) * 4) : 0x80000000u, 0, 0));
+    if (single) {
+      c8[step] = __builtin_amdgcn_raw_buffer_load_b32(srs, in ? (uint32_t)(b * 4) : 0x80000000u, 0, 0);
+      ga[step] = 0.f;
+    } else {
+      c8[step] = __builtin_amdgcn_raw_buffer_load_b8(srs, in ? (uint32_t)b : 0x80000000u, 0, 0);
+      ga[step] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, in ? (uint32_t)((b >> 8) * 4) : 0x80000000u, 0, 0));
+    }
   }
-  const float offset = *offset_p;
+  const float offset = single ? 0.f : *offset_p;
   __syncthreads();  // table
 #pragma unroll
   for (int step = 0; step < 4; ++step) {
     const int64_t d = wave_base + step * 64 + lane;
     if (d >= ndw) break;
-    const float s = block_scale(c8[step], ga[step], offset);
+    const float s = single ? __uint_as_float(c8[step]) : block_scale(c8[step], ga[step], offset);
     uint32_t o[4];
     dequant_word(word[step], s, s_pair, o);
     const u32x4_t v = {o[0], o[1], o[2], o[3]};
@@ -66,8 +76,9 @@ hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s) {
     const int64_t ndw = std::min(kSlice, ndw_all - d0);
     const int64_t grid = ceil_div(ndw, 4 * 256);
     QLORA_LAUNCH("k_dequant", k_dequant, dim3((unsigned)grid), dim3(256), 0, s,
-                 reinterpret_cast<const uint32_t *>(w.packed) + d0, w.scale_code + d0 / 8,
-                 w.group_amax + d0 / 8 / kGroup, w.offset, ndw, w.codebook,
+                 reinterpret_cast<const uint32_t *>(w.packed) + d0, w.absmax ? nullptr : w.scale_code + d0 / 8,
+                 w.absmax ? nullptr : w.group_amax + d0 / 8 / kGroup, w.offset, w.absmax ? w.absmax + d0 / 8 : nullptr,
+                 ndw, w.codebook,
                  reinterpret_cast<u32x4_t *>(out) + d0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

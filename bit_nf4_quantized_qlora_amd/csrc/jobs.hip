@@ -111,11 +111,11 @@ __device__ __forceinline__ void run_scales_fwd(const SmallJob &j, uint32_t t) {
   const int64_t n = to * kTileRows + (t & 255), nkb = w.k / kBlock;
   f32x4_t v = {0.f, 0.f, 0.f, 0.f};
   if (n < w.n) {
-    const float off = *w.offset;
+    const float off = w.absmax ? 0.f : *w.offset;
 #pragma unroll
     for (int u = 0; u < kTileSup; ++u) {
       const int64_t kb = kTileSup * sp + u, b = n * nkb + kb;
-      if (kb < nkb) v[u] = block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
+      if (kb < nkb) v[u] = w.absmax ? w.absmax[b] : block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
     }
   }
   *reinterpret_cast<f32x4_t *>(static_cast<float *>(j.out) + 4 * t) = v;
@@ -132,14 +132,14 @@ __device__ __forceinline__ void run_scales_bwd(const SmallJob &j, uint32_t t) {
   const uint32_t q = t >> 8, tk = q / nsup, sp = q - tk * nsup;
   const int64_t n = (int64_t)sp * kTileRows + (t & 255), nkb = w.k / kBlock;
   float *out = static_cast<float *>(j.out) + (size_t)q * 4 * 256 + (t & 255);
-  const float off = *w.offset;
+  const float off = w.absmax ? 0.f : *w.offset;
 #pragma unroll
   for (int blk = 0; blk < kTileSup; ++blk) {
     const int64_t kb = (int64_t)tk * kTileSup + blk;
     float v = 0.f;
     if (n < w.n && kb < nkb) {
       const int64_t b = n * nkb + kb;
-      v = block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
+      v = w.absmax ? w.absmax[b] : block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
     }
     out[blk * 256] = v;
   }

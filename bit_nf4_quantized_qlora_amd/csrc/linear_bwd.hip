@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(Nf4View w, const uint16_t *__
   const int64_t k0 = (int64_t)blockIdx.x * DBK, m0 = (int64_t)blockIdx.y * DBM;
   const int64_t nsteps = ceil_div_d(N, 64);
   fill_pair_table(s_pair, tid, 256, w.codebook);
-  const float offset = *w.offset;
+  const bool single = w.absmax != nullptr;  // s_b = absmax_b
+  const float offset = single ? 0.f : *w.offset;
   const bool dyvec = (N % 8) == 0;
 
   // Weight staging: rows n0 + 4*ng + rho (rho = 0..3), codes k0 + 8*kg .. +7.
@@ -57,8 +58,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(Nf4View w, const uint16_t *__
       const int64_t nn = ok ? n : 0, kk = ok ? kcol : 0;  // out-of-range rows read row 0
       wd[rho] = *reinterpret_cast<const uint32_t *>(w.packed + (nn * K + kk) / 2);
       const int64_t b = nn * nkb + kk / kBlock;
-      sc[rho] = w.scale_code[b];
-      ga[rho] = w.group_amax[b >> 8];
+      if (single) {
+        sc[rho] = __float_as_uint(w.absmax[b]);
+        ga[rho] = 0.f;
+      } else {
+        sc[rho] = w.scale_code[b];
+        ga[rho] = w.group_amax[b >> 8];
+      }
       wok[rho] = ok;
     }
 #pragma unroll
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(Nf4View w, const uint16_t *__
     uint32_t o[4][4];
 #pragma unroll
     for (int rho = 0; rho < 4; ++rho) {
-      dequant_word(wd[rho], block_scale(sc[rho], ga[rho], offset), s_pair, o[rho]);
+      dequant_word(wd[rho], single ? __uint_as_float(sc[rho]) : block_scale(sc[rho], ga[rho], offset), s_pair, o[rho]);
       if (!wok[rho]) o[rho][0] = o[rho][1] = o[rho][2] = o[rho][3] = 0u;
     }
     uint16_t *P = Ps + buf * DBK * DLD + 4 * ng;

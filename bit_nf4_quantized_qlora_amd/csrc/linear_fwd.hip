@@ -44,7 +44,9 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
                              uint16_t *Y, float *H_out, void *ws, hipStream_t s) {
   const int64_t M = a.M, N = a.w.n, K = a.w.k;
   if (M == 0) return hipSuccess;
-  if (small_m_supported(M, N, K, a.r)) return launch_fwd_small(a.w, X, M, A, B, a.r, a.s, Y, H_out, ws, s);
+  // the GEMV decodes double-quantized constants only; single-level weights
+  // take the tile kernels at every M
+  if (!a.w.absmax && small_m_supported(M, N, K, a.r)) return launch_fwd_small(a.w, X, M, A, B, a.r, a.s, Y, H_out, ws, s);
   const FwdWs l = fwd_ws_layout(M, N, K, a.r);
   char *base = static_cast<char *>(ws);
   float *part = reinterpret_cast<float *>(base + l.part_off);

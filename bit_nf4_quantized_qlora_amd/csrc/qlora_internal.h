@@ -18,14 +18,17 @@ struct Nf4View {
   const uint8_t *scale_code;
   const float *group_amax;
   const float *offset;
-  int codebook;  // kCodebookNF4 or kCodebookFP4
+  int codebook;         // kCodebookNF4 or kCodebookFP4
+  const float *absmax;  // single-level block constants (s_b = absmax_b); NULL: double quantization
 };
 
 // Decision thresholds of a codebook (kCodebookNF4 / kCodebookFP4).
 const Thresholds &codebook_thresholds(int codebook);
 
 // quantize.hip
-hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, uint8_t *packed,
+// single_level: write the block absmax to ws_absmax (the caller's absmax
+// buffer) and skip the second level.
+hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, bool single_level, uint8_t *packed,
                            uint8_t *scale_code, float *group_amax, float *offset, float *ws_absmax,
                            double *ws_group_sum, hipStream_t s);
 

@@ -175,13 +175,15 @@ __global__ __launch_bounds__(256) void k_encode_scales(const float *__restrict__
 
 }  // namespace
 
-hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, uint8_t *packed, uint8_t *scale_code,
+hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, bool single_level, uint8_t *packed,
+                           uint8_t *scale_code,
                            float *group_amax, float *offset, float *ws_absmax, double *ws_group_sum,
                            hipStream_t s) {
   const int64_t nb = n * k / kBlock;
   const int64_t ng = ceil_div(nb, kGroup);
   QLORA_LAUNCH("k_quantize_blocks", k_quantize_blocks, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codebook_thresholds(codebook), packed,
                      ws_absmax, ws_group_sum);
+  if (single_level) return hipGetLastError();
   QLORA_LAUNCH("k_mean", k_mean, dim3(1), dim3(256), 0, s, ws_group_sum, ng, nb, offset);
   QLORA_LAUNCH("k_encode_scales", k_encode_scales, dim3((unsigned)ceil_div(ng, 4)), dim3(256), 0, s, ws_absmax, nb, ng,
                      offset, scale_code, group_amax);

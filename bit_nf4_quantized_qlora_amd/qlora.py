@@ -34,13 +34,15 @@ QLORA_ERR_BAD_CODEBOOK = -8
 QLORA_CODEBOOK_NF4 = 0        # NormalFloat4, the method's storage type
 QLORA_CODEBOOK_FP4_E2M1 = 1   # Float4 (E2M1), the comparison type
 CODEBOOKS = {"nf4": QLORA_CODEBOOK_NF4, "fp4": QLORA_CODEBOOK_FP4_E2M1}
+QLORA_SCALES_DQ = 0           # double-quantized block constants (the method's)
+QLORA_SCALES_FP32 = 1         # one float32 absmax per block (double quantization off)
 
 _c_i64, _c_int, _c_float, _c_size, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
 
 class qlora_nf4_weight(ctypes.Structure):
     _fields_ = [("n", _c_i64), ("k", _c_i64), ("packed", _vp), ("scale_code", _vp), ("group_amax", _vp),
-                ("offset", _vp), ("codebook", ctypes.c_int32)]
+                ("offset", _vp), ("codebook", ctypes.c_int32), ("scales", ctypes.c_int32), ("absmax", _vp)]
 
 
 _W = ctypes.POINTER(qlora_nf4_weight)
@@ -102,26 +104,35 @@ def _need(t, dtype, name):
 
 @dataclass
 class NF4Weight:
-    """Device buffers of one quantized weight (torch tensors) and the C view."""
+    """Device buffers of one quantized weight (torch tensors) and the C view.
+    Double-quantized constants use scale_code / group_amax / offset;
+    single-level ones (scales == QLORA_SCALES_FP32) use absmax only."""
     n: int
     k: int
-    packed: torch.Tensor      # uint8 [n*k/2]
-    scale_code: torch.Tensor  # uint8 [n*k/64]
-    group_amax: torch.Tensor  # float32 [ceil(n*k/64/256)]
-    offset: torch.Tensor      # float32 [1]
+    packed: torch.Tensor                     # uint8 [n*k/2]
+    scale_code: torch.Tensor | None          # uint8 [n*k/64]
+    group_amax: torch.Tensor | None          # float32 [ceil(n*k/64/256)]
+    offset: torch.Tensor | None              # float32 [1]
     codebook: int = QLORA_CODEBOOK_NF4
+    scales: int = QLORA_SCALES_DQ
+    absmax: torch.Tensor | None = None       # float32 [n*k/64]
 
     @staticmethod
-    def empty(n: int, k: int, device="cuda", codebook: int = QLORA_CODEBOOK_NF4) -> "NF4Weight":
+    def empty(n: int, k: int, device="cuda", codebook: int = QLORA_CODEBOOK_NF4,
+              scales: int = QLORA_SCALES_DQ) -> "NF4Weight":
         pb, sb, ng = qlora_nf4_sizes(n, k)
-        return NF4Weight(n, k, torch.empty(pb, dtype=torch.uint8, device=device),
-                         torch.empty(sb, dtype=torch.uint8, device=device),
+        packed = torch.empty(pb, dtype=torch.uint8, device=device)
+        if scales == QLORA_SCALES_FP32:
+            return NF4Weight(n, k, packed, None, None, None, codebook, scales,
+                             torch.empty(sb, dtype=torch.float32, device=device))
+        return NF4Weight(n, k, packed, torch.empty(sb, dtype=torch.uint8, device=device),
                          torch.empty(ng, dtype=torch.float32, device=device),
-                         torch.empty(1, dtype=torch.float32, device=device), codebook)
+                         torch.empty(1, dtype=torch.float32, device=device), codebook, scales)
 
     def c_struct(self) -> qlora_nf4_weight:
-        return qlora_nf4_weight(self.n, self.k, self.packed.data_ptr(), self.scale_code.data_ptr(),
-                                self.group_amax.data_ptr(), self.offset.data_ptr(), self.codebook)
+        p = lambda t: None if t is None else t.data_ptr()
+        return qlora_nf4_weight(self.n, self.k, p(self.packed), p(self.scale_code), p(self.group_amax),
+                                p(self.offset), self.codebook, self.scales, p(self.absmax))
 
 
 def qlora_nf4_sizes(n: int, k: int):

@@ -48,7 +48,7 @@ enum {
   QLORA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes */
   QLORA_ERR_HIP = -6,         /* a HIP runtime call or kernel launch failed           */
   QLORA_ERR_BAD_ALPHA = -7,   /* alpha is not finite                                  */
-  QLORA_ERR_BAD_CODEBOOK = -8 /* the weight's codebook is not one of QLORA_CODEBOOK_* */
+  QLORA_ERR_BAD_CODEBOOK = -8 /* codebook / scales field not one of QLORA_CODEBOOK_* / _SCALES_* */
 };
 
 /*
@@ -66,6 +66,20 @@ enum {
 };
 
 /*
+ * Block constants (the `scales` field of a weight).  QLORA_SCALES_DQ is the
+ * method's double quantization (scale_code, group_amax, offset).
+ * QLORA_SCALES_FP32 is the single-level layout double quantization improves
+ * on ("QLoRA Paper Breakdown" sec. 3, the hidden overhead of block scales:
+ * one float32 per 64 weights, 4.5 bits per weight): absmax [nb] holds each
+ * block's absmax and s_b = absmax_b.  Each layout needs only its own
+ * buffers; the others may be NULL.
+ */
+enum {
+  QLORA_SCALES_DQ = 0,
+  QLORA_SCALES_FP32 = 1
+};
+
+/*
  * A quantized frozen weight W [n, k] ("QLoRA, explained.", symbol list: W^NF4
  * plus the per-block and per-group constants; "QLoRA Paper Breakdown" sec. 3).
  * Block b = 64 consecutive elements of row-major W (so k % 64 == 0 keeps a
@@ -79,6 +93,8 @@ typedef struct qlora_nf4_weight {
   float *group_amax;    /* [ng] second-level constant: max |absmax_b - offset| in g     */
   float *offset;        /* [1] per-tensor mean of the fp32 block absmax values          */
   int32_t codebook;     /* QLORA_CODEBOOK_NF4 (0: a zero-filled descriptor) or _FP4_E2M1 */
+  int32_t scales;       /* QLORA_SCALES_DQ (0) or QLORA_SCALES_FP32                     */
+  float *absmax;        /* [nb] block absmax, QLORA_SCALES_FP32 only                    */
 } qlora_nf4_weight;
 
 /* Sizes of the four buffers of an [n, k] weight.  Host only; no GPU use.
@@ -103,6 +119,8 @@ size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
  *   dev_b = fp32(absmax_b - offset); group_amax_g = max |dev_b| over g
  *   scale_code_b = E4M3FN round-to-nearest-even of fp32(dev_b / group_amax_g)
  *                  (0x00 when group_amax_g == 0)
+ * With out->scales == QLORA_SCALES_FP32 the second level is skipped and
+ * absmax_b is stored in out->absmax.
  * The result is bit-for-bit deterministic.  `ws` >= qlora_quantize_workspace_bytes.
  */
 int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
@@ -112,6 +130,7 @@ int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws,
  * Dequantize to bfloat16: W_bf16 [n, k] (device).  "QLoRA Paper Breakdown"
  * sec. 4 Dequantization Helper; "QLoRA, explained." step 4:
  *   s_b = fp32( fp32(decode(scale_code_b) * group_amax_g) + offset )
+ *         (s_b = absmax_b for QLORA_SCALES_FP32)
  *   w_hat = bf16_round_nearest_even( fp32(q[code] * s_b) ), q = w->codebook's levels
  * Bit-for-bit identical to the operand the fused linear kernels use.
  */

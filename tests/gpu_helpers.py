@@ -33,9 +33,10 @@ def bf16_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def gpu_quantize(q, W: np.ndarray, codebook: str = "nf4"):
+def gpu_quantize(q, W: np.ndarray, codebook: str = "nf4", scales: str = "dq"):
     n, k = W.shape
-    w = q.NF4Weight.empty(n, k, codebook=q.CODEBOOKS[codebook])
+    w = q.NF4Weight.empty(n, k, codebook=q.CODEBOOKS[codebook],
+                          scales=q.QLORA_SCALES_FP32 if scales == "fp32" else q.QLORA_SCALES_DQ)
     ws = torch.empty(q.qlora_quantize_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
     q.qlora_quantize_nf4_dq(dev_f32(W), w, ws)
     return w

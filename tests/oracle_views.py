@@ -12,7 +12,7 @@ from oracle import linear, nf4_dq
 
 
 class OracleWeight:
-    def __init__(self, W: np.ndarray, codebook: str = "nf4"):
+    def __init__(self, W: np.ndarray, codebook: str = "nf4", scales: str = "dq"):
         self.W = np.asarray(W, np.float32)
         self.codebook = codebook
         self.n, self.k = self.W.shape
@@ -21,6 +21,8 @@ class OracleWeight:
         self.offset = nf4_dq.dq_offset(self.absmax)
         self.scale_code, self.group_amax = nf4_dq.dq_encode(self.absmax, self.offset)
         self.s = nf4_dq.dq_block_scale(self.scale_code, self.group_amax, self.offset)
+        if scales == "fp32":   # single-level constants: s_b = absmax_b
+            self.s = self.absmax
         self.levels = nf4_dq.codebook_levels(codebook)
 
     def row_codes(self, rows) -> np.ndarray:

@@ -131,6 +131,12 @@ def test_argument_errors_enqueue_nothing(q):
     assert bwd(ctypes.byref(W), P, P, 16, P, P, 8, 16.0, None, P, None, P, P, 1 << 30, None) == q.QLORA_ERR_NULL_ARG
     assert bwd(ctypes.byref(W), P, P, 16, P, P, 8, 16.0, None, P, P, P, P, 64, None) == q.QLORA_ERR_WORKSPACE
     assert "r = 0" in (fwd(ctypes.byref(W), P, 16, P, P, 0, 16.0, P, None, P, 1 << 30, None) and q.qlora_last_error())
+    bad_sc = q.qlora_nf4_weight(64, 64, 16, 16, 16, 16, 0, 2, 16)
+    assert lib.qlora_dequant_bf16(ctypes.byref(bad_sc), P, None) == q.QLORA_ERR_BAD_CODEBOOK
+    single_null = q.qlora_nf4_weight(64, 64, 16, None, None, None, 0, q.QLORA_SCALES_FP32, None)
+    assert lib.qlora_dequant_bf16(ctypes.byref(single_null), P, None) == q.QLORA_ERR_NULL_ARG
+    single = q.qlora_nf4_weight(64, 64, 16, None, None, None, 1, q.QLORA_SCALES_FP32, 16)  # DQ buffers unused
+    assert fwd(ctypes.byref(single), P, 16, P, P, 8, 16.0, P, None, P, 16, None) == q.QLORA_ERR_WORKSPACE
     bad_cb = q.qlora_nf4_weight(64, 64, 16, 16, 16, 16, 3)
     assert lib.qlora_quantize_nf4_dq(P, ctypes.byref(bad_cb), P, 1 << 20, None) == q.QLORA_ERR_BAD_CODEBOOK
     assert lib.qlora_dequant_bf16(ctypes.byref(bad_cb), P, None) == q.QLORA_ERR_BAD_CODEBOOK

@@ -71,6 +71,25 @@ def test_decision_thresholds_and_special_values(q, codebook):
     _full_check(q, W, "thresholds", codebook)
 
 
+@pytest.mark.parametrize("codebook", ["nf4", "fp4"])
+@pytest.mark.parametrize("shape,seed", [((5, 3840), 34), ((300, 640), 35), ((1024, 4096), 36)])
+def test_single_level_encoding(q, shape, seed, codebook):
+    """Single-level constants (one float32 absmax per block): packed bytes and
+    absmax bit-exact, and the BF16 dequantization with s_b = absmax_b."""
+    W = I.custom_weight(*shape, seed=seed)
+    note(f"[encoding] single-level {shape} codebook={codebook}")
+    n, k = W.shape
+    w = gpu_quantize(q, W, codebook, "fp32")
+    torch.cuda.synchronize()
+    ref = nf4_dq.quantize_single_level(W, codebook)
+    assert np.array_equal(w.packed.cpu().numpy(), ref["packed"]), "packed"
+    assert np.array_equal(w.absmax.cpu().numpy().view(np.uint32), ref["absmax"].view(np.uint32)), "absmax"
+    wh = _gpu_dequant(q, w)
+    ref_wh = nf4_dq.dequant_single_level_bf16(ref["packed"], ref["absmax"], n, k, codebook)
+    bad = np.flatnonzero(wh.reshape(-1) != ref_wh.reshape(-1))
+    assert bad.size == 0, f"single-level dequant: {bad.size} differ, first {bad[:5]}"
+
+
 @pytest.mark.parametrize("shape,seed", [((5, 3840), 31), ((300, 640), 32), ((1024, 4096), 33)])
 def test_fp4_encoding(q, shape, seed):
     """Float4 (E2M1) storage: the same bit-exact bar on ragged and full groups."""

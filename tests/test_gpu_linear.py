@@ -18,15 +18,15 @@ def q():
     return qlora
 
 
-def _run_full(q, W, X, A, B, dY, r, alpha, ctx, h_none=False, want_dx=True, codebook="nf4"):
+def _run_full(q, W, X, A, B, dY, r, alpha, ctx, h_none=False, want_dx=True, codebook="nf4", scales="dq"):
     """Full comparison of every output (small shapes)."""
-    note(f"[linear] {ctx} W={W.shape} M={X.shape[0]} r={r} alpha={alpha} codebook={codebook}")
-    ow = OracleWeight(W, codebook)
+    note(f"[linear] {ctx} W={W.shape} M={X.shape[0]} r={r} alpha={alpha} codebook={codebook} scales={scales}")
+    ow = OracleWeight(W, codebook, scales)
     What = bf16_f64(ow.row_what_bits(np.arange(W.shape[0])))
     Xf, Af, Bf, dYf = bf16_f64(X), bf16_f64(A), bf16_f64(B), bf16_f64(dY)
     Yr, Hr = fwd(Xf, What, Af, Bf, alpha)
     dXr, dAr, dBr, _ = bwd(Xf, dYf, What, Af, Bf, alpha)
-    lin = Linear(q, gpu_quantize(q, W, codebook), X, A, B, r, alpha)
+    lin = Linear(q, gpu_quantize(q, W, codebook, scales), X, A, B, r, alpha)
     Y, H = lin.fwd()
     dX, dA, dB = lin.bwd(dY, H=None if h_none else H, want_dx=want_dx)
     torch.cuda.synchronize()
@@ -107,6 +107,21 @@ def test_fp4_linear(q, n, k, m, r, alpha, seed):
     A = I.custom_bf16((r, k), seed, 3, bound=0.05)
     B = I.custom_bf16((n, r), seed, 4, bound=0.05)
     _run_full(q, W, X, A, B, dY, r, alpha, f"fp4 n{n} k{k} m{m} r{r}", codebook="fp4")
+
+
+@pytest.mark.parametrize("n,k,m,r,alpha,seed,codebook", [
+    (640, 512, 300, 64, 16.0, 51, "nf4"),   # tile kernels both ways
+    (200, 192, 37, 5, -3.5, 52, "fp4"),     # ragged everything, fallback backward
+    (1000, 4096, 3, 16, 16.0, 53, "nf4"),   # M <= 16: tile kernels (the GEMV serves DQ weights)
+])
+def test_single_level_linear(q, n, k, m, r, alpha, seed, codebook):
+    """Single-level float32 block constants through forward and backward."""
+    W = I.custom_weight(n, k, seed)
+    X = I.custom_bf16((m, k), seed, 1)
+    dY = I.custom_bf16((m, n), seed, 2)
+    A = I.custom_bf16((r, k), seed, 3, bound=0.05)
+    B = I.custom_bf16((n, r), seed, 4, bound=0.05)
+    _run_full(q, W, X, A, B, dY, r, alpha, f"single-level n{n} k{k} m{m} r{r}", codebook=codebook, scales="fp32")
 
 
 def test_bwd_recomputes_h_and_skips_dx(q):
