@@ -315,6 +315,7 @@ def main():
                            "gbps": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1),
                            "frac_hbm_peak": round(deq_bytes / (deq_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
         rows["small_m"] = small_m_rows(q, I, np, torch, dev, dev16, ev)
+        rows["storage_types"] = storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops)
 
     calib = None
     if args.calib_copy_mib:
@@ -365,6 +366,87 @@ def main():
     if attainable:
         out["attainable"] = attainable
     print(json.dumps(out), flush=True)
+
+
+def storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops):
+    """The same fwd+bwd step with the comparison storage types: Float4 (E2M1)
+    codes instead of NF4, and single-level float32 block constants (double
+    quantization off, 4.5 bits) instead of the double-quantized ones.  Each
+    variant's step is timed alternately with the NF4+DQ step (same inputs,
+    same workspace), 3 rounds of 3 warm-up + 10 timed steps, minimum per
+    variant; plus its standalone dequantization rate on its own bytes."""
+    import torch
+    variants = {"nf4_dq": (q.QLORA_CODEBOOK_NF4, q.QLORA_SCALES_DQ),
+                "fp4_dq": (q.QLORA_CODEBOOK_FP4_E2M1, q.QLORA_SCALES_DQ),
+                "nf4_fp32_absmax": (q.QLORA_CODEBOOK_NF4, q.QLORA_SCALES_FP32),
+                "fp4_fp32_absmax": (q.QLORA_CODEBOOK_FP4_E2M1, q.QLORA_SCALES_FP32)}
+    weights = {}
+    for name, (cb, sc) in variants.items():
+        ws_list = []
+        for li, t in enumerate(layers):
+            if name == "nf4_dq":
+                ws_list.append(t["w"])
+                continue
+            L = t["L"]
+            W = torch.from_numpy(I.weight(wl, li)).to(dev)
+            w = q.NF4Weight.empty(L.n, L.k, dev, codebook=cb, scales=sc)
+            qws = torch.empty(q.qlora_quantize_workspace_bytes(L.n, L.k), dtype=torch.uint8, device=dev)
+            q.qlora_quantize_nf4_dq(W, w, qws)
+            del W, qws
+            ws_list.append(w)
+        weights[name] = ws_list
+
+    def step(wlist):
+        for t, w in zip(layers, wlist):
+            q.qlora_linear_fwd(w, t["X"], t["A"], t["B"], r, alpha, t["Y"], t["H"], ws)
+        for t, w in zip(reversed(layers), reversed(wlist)):
+            q.qlora_linear_bwd(w, t["X"], t["dY"], t["A"], t["B"], r, alpha, t["H"], t["dX"], t["dA"], t["dB"], ws)
+
+    best = {n: float("inf") for n in variants}
+    for _ in range(3):
+        for name in variants:
+            for _ in range(3):
+                step(weights[name])
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(10):
+                step(weights[name])
+            b.record()
+            torch.cuda.synchronize()
+            best[name] = min(best[name], a.elapsed_time(b) / 10)
+    out = {}
+    for name, (cb, sc) in variants.items():
+        deq_ms, deq_bytes, store_bytes, nw = 0.0, 0, 0, 0
+        for t, w in zip(layers, weights[name]):
+            L = t["L"]
+            pb, sb, ng = q.qlora_nf4_sizes(L.n, L.k)
+            enc = pb + (4 * sb if sc == q.QLORA_SCALES_FP32 else sb + 4 * ng + 4)
+            Wh = torch.empty(L.n, L.k, dtype=torch.bfloat16, device=dev)
+            q.qlora_dequant_bf16(w, Wh)
+            a, b = ev(), ev()
+            a.record()
+            for _ in range(5):
+                q.qlora_dequant_bf16(w, Wh)
+            b.record()
+            torch.cuda.synchronize()
+            deq_ms += a.elapsed_time(b) / 5
+            deq_bytes += enc + 2 * L.n * L.k
+            store_bytes += enc - (0 if sc == q.QLORA_SCALES_FP32 else 4)
+            nw += L.n * L.k
+            del Wh
+        out[name] = {"step_ms": round(best[name], 4),
+                     "tflops": round(step_flops / (best[name] * 1e-3) / 1e12, 1),
+                     "step_vs_nf4_dq": round(best[name] / best["nf4_dq"], 4),
+                     "dequant_gbps": round(deq_bytes / (deq_ms * 1e-3) / 1e9, 1),
+                     "bits_per_weight": round(8 * store_bytes / nw, 6)}
+    out["how"] = ("same 7B MLP step and inputs per storage type, alternated with nf4_dq, min of 3 x 10 steps; "
+                  "dequant rate on each type's own bytes (codes + constants + bf16 out)")
+    for name in variants:
+        if name != "nf4_dq":
+            del weights[name]
+    torch.cuda.empty_cache()
+    return out
 
 
 def attainable_peaks(torch, dev, ev):
