@@ -14,4 +14,6 @@ Modules
              to BF16, and the bits-per-weight arithmetic.
 ``linear``   the fp64 forward / backward of the frozen-base linear layer with
              its LoRA adapters.
+``merge``    folding trained adapters into the base (W_hat + s B A) and
+             re-encoding the result.
 """
