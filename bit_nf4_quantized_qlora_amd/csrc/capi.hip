@@ -173,6 +173,43 @@ int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream
   return QLORA_OK;
 }
 
+size_t qlora_merge_workspace_bytes(int64_t n, int64_t k) {
+  if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k || k > kMaxK) return 0;
+  return align_up((size_t)(n * k) * sizeof(float), 256) + quantize_ws(n, k);
+}
+
+int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B, int r, float alpha,
+                         uint16_t *W_merged, const qlora_nf4_weight *out, void *ws, size_t ws_bytes, void *stream) {
+  if (int e = check_weight(w)) return e;
+  if (r < 1 || r > 128) return fail(QLORA_ERR_BAD_RANK, "rank r = %d outside [1, 128]", r);
+  if (!std::isfinite(alpha)) return fail(QLORA_ERR_BAD_ALPHA, "alpha is not finite");
+  if (int e = check_tensor(A, "A")) return e;
+  if (int e = check_tensor(B, "B")) return e;
+  if (W_merged)
+    if (int e = check_tensor(W_merged, "W_merged")) return e;
+  if (out) {
+    if (int e = check_weight(out)) return e;
+    if (out->n != w->n || out->k != w->k) return fail(QLORA_ERR_BAD_SHAPE, "out is not [n, k] of w");
+  }
+  const size_t need = qlora_merge_workspace_bytes(w->n, w->k);
+  if (int e = check_ws(ws, ws_bytes, need)) return e;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  float *Wm = static_cast<float *>(ws);
+  hipError_t e = launch_merge(view_of(w), A, B, r, (float)alpha / (float)r, Wm, W_merged, s);
+  if (e != hipSuccess) return hip_fail(e, "qlora_merge_adapters");
+  if (out) {
+    char *qws = static_cast<char *>(ws) + align_up((size_t)(w->n * w->k) * sizeof(float), 256);
+    const int64_t nb = out->n * out->k / kBlock;
+    const bool single = out->scales == QLORA_SCALES_FP32;
+    float *ws_absmax = single ? out->absmax : reinterpret_cast<float *>(qws);
+    double *ws_sum = reinterpret_cast<double *>(qws + align_up((size_t)nb * sizeof(float), 256));
+    e = launch_quantize(Wm, out->n, out->k, out->codebook, single, out->packed, out->scale_code, out->group_amax,
+                        out->offset, ws_absmax, ws_sum, s);
+    if (e != hipSuccess) return hip_fail(e, "qlora_merge_adapters (re-encode)");
+  }
+  return QLORA_OK;
+}
+
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r) {
   if (n < 1 || k < kBlock || k % kBlock != 0 || M < 0 || r < 1 || r > 128) return 0;
   if (n > kMaxElems / k || k > kMaxK || M > kMaxElems / std::max<int64_t>(k, n)) return 0;

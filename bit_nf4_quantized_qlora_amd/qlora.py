@@ -59,6 +59,8 @@ _SIGS = {
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_nf4_thresholds": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_codebook": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
+    "qlora_merge_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "qlora_merge_adapters": (_c_int, [_W, _vp, _vp, _c_int, _c_float, _vp, _W, _vp, _c_size, _vp]),
     "qlora_thresholds": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
     "qlora_strerror": (ctypes.c_char_p, [_c_int]),
     "qlora_profile_begin": (_c_int, []),
@@ -196,6 +198,24 @@ def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
     _check("qlora_linear_bwd",
            _lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), X.shape[0], _ptr(A), _ptr(B), r, alpha,
                                  _ptr(H), _ptr(dX), _ptr(dA), _ptr(dB), wp, wb, _stream(stream)))
+
+
+def qlora_merge_workspace_bytes(n: int, k: int) -> int:
+    return _lib.qlora_merge_workspace_bytes(n, k)
+
+
+def qlora_merge_adapters(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, r: int, alpha: float,
+                         W_merged: torch.Tensor | None, out: NF4Weight | None, ws: torch.Tensor, stream=None) -> None:
+    for t, nm in ((A, "A"), (B, "B")):
+        _need(t, torch.bfloat16, nm)
+    if W_merged is not None:
+        _need(W_merged, torch.bfloat16, "W_merged")
+    st = w.c_struct()
+    ost = out.c_struct() if out is not None else None
+    wp, wb = _ws_args(ws)
+    _check("qlora_merge_adapters",
+           _lib.qlora_merge_adapters(ctypes.byref(st), _ptr(A), _ptr(B), r, alpha, _ptr(W_merged),
+                                     ctypes.byref(ost) if ost is not None else None, wp, wb, _stream(stream)))
 
 
 def qlora_nf4_codebook():

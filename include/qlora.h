@@ -169,6 +169,25 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
                      uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes,
                      void *stream);
 
+/*
+ * Fold trained adapters into the base for deployment ("QLoRA Paper
+ * Breakdown" section 'Limitations': full-rank updates merge the adapters
+ * into 16-bit weights; the merged weight is section 4's W_hat + s B A).
+ * The pages fix no arithmetic; this call's definition:
+ *   t  = sum over j = 0 .. r-1, in that order, of B[n][j] * A[j][k]  (float64)
+ *   W' = float32( float64(w_hat) + float64(s) * t ),   s = fp32(alpha / r)
+ * with every float64 operation separately rounded.  Then
+ *   W_merged [n, k] bf16 = bf16_round_nearest_even(W')   when W_merged != NULL;
+ *   `out` (same n, k; its codebook and scales chosen by the caller) = the
+ *   encoding of W' exactly as qlora_quantize_nf4_dq would give   when out != NULL.
+ * A [r, k] and B [n, r] bf16 as in the forward pass.  W' itself is left in
+ * the first n*k*4 bytes of `ws`, which needs qlora_merge_workspace_bytes.
+ */
+size_t qlora_merge_workspace_bytes(int64_t n, int64_t k);
+int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B, int r, float alpha,
+                         uint16_t *W_merged, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
+                         void *stream);
+
 /* Host copies of the library's constants (host memory, no GPU use):
  * the 16 NF4 levels ("QLoRA Paper Breakdown" sec. 2) and the 15 float32
  * decision thresholds (T_j = smallest float32 above the exact midpoint of

@@ -137,6 +137,14 @@ def test_argument_errors_enqueue_nothing(q):
     assert lib.qlora_dequant_bf16(ctypes.byref(single_null), P, None) == q.QLORA_ERR_NULL_ARG
     single = q.qlora_nf4_weight(64, 64, 16, None, None, None, 1, q.QLORA_SCALES_FP32, 16)  # DQ buffers unused
     assert fwd(ctypes.byref(single), P, 16, P, P, 8, 16.0, P, None, P, 16, None) == q.QLORA_ERR_WORKSPACE
+    merge = lib.qlora_merge_adapters
+    small = q.qlora_nf4_weight(128, 64, 16, 16, 16, 16)
+    assert merge(ctypes.byref(W), P, P, 0, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_BAD_RANK
+    assert merge(ctypes.byref(W), P, P, 8, 16.0, P, ctypes.byref(small), P, 1 << 30, None) == q.QLORA_ERR_BAD_SHAPE
+    assert merge(ctypes.byref(W), P, P, 8, 16.0, P, None, P, 64, None) == q.QLORA_ERR_WORKSPACE
+    assert merge(ctypes.byref(W), None, P, 8, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_NULL_ARG
+    assert q.qlora_merge_workspace_bytes(4096, 4096) >= 4096 * 4096 * 4 + q.qlora_quantize_workspace_bytes(4096, 4096)
+    assert q.qlora_merge_workspace_bytes(4096, 100) == 0
     bad_cb = q.qlora_nf4_weight(64, 64, 16, 16, 16, 16, 3)
     assert lib.qlora_quantize_nf4_dq(P, ctypes.byref(bad_cb), P, 1 << 20, None) == q.QLORA_ERR_BAD_CODEBOOK
     assert lib.qlora_dequant_bf16(ctypes.byref(bad_cb), P, None) == q.QLORA_ERR_BAD_CODEBOOK
