@@ -316,6 +316,7 @@ def main():
                            "frac_hbm_peak": round(deq_bytes / (deq_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
         rows["small_m"] = small_m_rows(q, I, np, torch, dev, dev16, ev)
         rows["storage_types"] = storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops)
+        rows["merge"] = merge_rows(q, layers, dev, ev, r, alpha)
 
     calib = None
     if args.calib_copy_mib:
@@ -447,6 +448,44 @@ def storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops):
             del weights[name]
     torch.cuda.empty_cache()
     return out
+
+
+def merge_rows(q, layers, dev, ev, r, alpha):
+    """Adapter merge (deployment step) on the three layers: W' = W_hat + s B A
+    in float64 (2r flops per weight), its bf16 copy and the NF4+DQ
+    re-encoding of W'.  Timed whole (events) and per kernel (library timer)."""
+    import torch
+    nmax = max(t["L"].n * t["L"].k for t in layers)
+    mws = torch.empty(max(q.qlora_merge_workspace_bytes(t["L"].n, t["L"].k) for t in layers), dtype=torch.uint8,
+                      device=dev)
+    outs = [q.NF4Weight.empty(t["L"].n, t["L"].k, dev) for t in layers]
+    Wb = torch.empty(nmax, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        for t, o in zip(layers, outs):
+            q.qlora_merge_adapters(t["w"], t["A"], t["B"], r, alpha, Wb[: t["L"].n * t["L"].k], o, mws)
+
+    run()
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(3):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 3
+    q.qlora_profile_begin()
+    run()
+    prof = q.qlora_profile_end()
+    flops = sum(2 * r * t["L"].n * t["L"].k for t in layers)
+    kern = {k: round(1e3 * v[1] / v[0], 1) for k, v in prof.items()}
+    km = prof.get("k_merge", (1, ms))[1]
+    del mws, outs, Wb
+    torch.cuda.empty_cache()
+    return {"ms_all_layers": round(ms, 4), "kernels_us": kern,
+            "merge_fp64_tflops": round(flops / (km * 1e-3) / 1e12, 2),
+            "merge_frac_fp64_peak": round(flops / (km * 1e-3) / 1e12 / 78.6, 4),
+            "how": "W_hat + s B A in float64 (2r flops per weight) + bf16 copy + NF4+DQ re-encoding, 3 layers"}
 
 
 def attainable_peaks(torch, dev, ev):
