@@ -16,4 +16,5 @@ Modules
              its LoRA adapters.
 ``merge``    folding trained adapters into the base (W_hat + s B A) and
              re-encoding the result.
+``adamw``    one AdamW step on the adapters (the paged optimizer's update).
 """
