@@ -173,6 +173,26 @@ int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream
   return QLORA_OK;
 }
 
+int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *m, float *v, int64_t count,
+                     float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream) {
+  if (count < 0 || count > kMaxElems) return fail(QLORA_ERR_BAD_SHAPE, "count = %lld", (long long)count);
+  if (step < 1) return fail(QLORA_ERR_BAD_SHAPE, "step = %lld (counts from 1)", (long long)step);
+  if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(weight_decay) || !(beta1 >= 0.f && beta1 < 1.f) ||
+      !(beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f))
+    return fail(QLORA_ERR_BAD_ALPHA, "AdamW hyperparameters out of range");
+  if (count == 0) return QLORA_OK;
+  if (int e = check_tensor(param, "param")) return e;
+  if (int e = check_tensor(grad, "grad")) return e;
+  if (int e = check_tensor(m, "m")) return e;
+  if (int e = check_tensor(v, "v")) return e;
+  if (param_bf16)
+    if (int e = check_tensor(param_bf16, "param_bf16")) return e;
+  hipError_t e = launch_adamw(param, param_bf16, grad, m, v, count, lr, beta1, beta2, eps, weight_decay, step,
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qlora_adamw_step");
+  return QLORA_OK;
+}
+
 size_t qlora_merge_workspace_bytes(int64_t n, int64_t k) {
   if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k || k > kMaxK) return 0;
   return align_up((size_t)(n * k) * sizeof(float), 256) + quantize_ws(n, k);

@@ -35,6 +35,11 @@ hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, b
 // dequant.hip
 hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s);
 
+// adamw.hip: one AdamW step over count parameters (m, v may be host memory
+// the device addresses).
+hipError_t launch_adamw(float *P, uint16_t *P16, const uint16_t *G, float *M, float *V, int64_t count, float lr,
+                        float b1, float b2, float eps, float wd, int64_t step, hipStream_t s);
+
 // merge.hip: Wm [n, k] float32 = W_hat + s B A (fixed float64 order), and
 // its bf16 rounding into Wb when Wb != NULL.
 hipError_t launch_merge(const Nf4View &w, const uint16_t *A, const uint16_t *B, int r, float s, float *Wm,

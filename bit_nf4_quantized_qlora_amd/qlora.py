@@ -60,6 +60,8 @@ _SIGS = {
     "qlora_nf4_thresholds": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_codebook": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
     "qlora_merge_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "qlora_adamw_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_float, _c_float, _c_float, _c_float, _c_float,
+                                  _c_i64, _vp]),
     "qlora_merge_adapters": (_c_int, [_W, _vp, _vp, _c_int, _c_float, _vp, _W, _vp, _c_size, _vp]),
     "qlora_thresholds": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
     "qlora_strerror": (ctypes.c_char_p, [_c_int]),
@@ -198,6 +200,21 @@ def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
     _check("qlora_linear_bwd",
            _lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), X.shape[0], _ptr(A), _ptr(B), r, alpha,
                                  _ptr(H), _ptr(dX), _ptr(dA), _ptr(dB), wp, wb, _stream(stream)))
+
+
+def qlora_adamw_step(param: torch.Tensor, param_bf16: torch.Tensor | None, grad: torch.Tensor, m, v, lr: float,
+                     beta1: float, beta2: float, eps: float, weight_decay: float, step: int, stream=None) -> None:
+    """m and v: device tensors, or (paged layout) integer device addresses of
+    mapped host memory, as ints."""
+    _need(param, torch.float32, "param")
+    _need(grad, torch.bfloat16, "grad")
+    if param_bf16 is not None:
+        _need(param_bf16, torch.bfloat16, "param_bf16")
+    mp = _vp(m) if isinstance(m, int) else _ptr(m)
+    vp = _vp(v) if isinstance(v, int) else _ptr(v)
+    _check("qlora_adamw_step",
+           _lib.qlora_adamw_step(_ptr(param), _ptr(param_bf16), _ptr(grad), mp, vp, param.numel(), lr, beta1, beta2,
+                                 eps, weight_decay, step, _stream(stream)))
 
 
 def qlora_merge_workspace_bytes(n: int, k: int) -> int:

@@ -188,6 +188,26 @@ int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uin
                          uint16_t *W_merged, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
                          void *stream);
 
+/*
+ * One AdamW step on an adapter tensor ("QLoRA Paper Breakdown" sec. 5, the
+ * paged optimizer; "QLoRA, explained." step 6).  The pages print no update
+ * rule; the published AdamW (decoupled weight decay, bias-corrected moments),
+ * in float32 with every operation separately rounded, in this order:
+ *   g = float(grad[i]);  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g);
+ *   p = p*decay - step_size * (m / (sqrt(v)/sqrt_bc2 + eps))
+ *   decay = fp32(1 - lr*wd), step_size = fp32(lr / (1 - b1^t)),
+ *   sqrt_bc2 = fp32(sqrt(1 - b2^t)),  (1-b1), (1-b2) rounded to float32,
+ *   all computed on the host in float64.
+ * param [count] float32 master values and m, v [count] float32 moments are
+ * updated in place; param_bf16 [count] (may be NULL) receives bf16 of the
+ * new values for the next forward pass; grad [count] bf16.  step = t >= 1.
+ * m and v may be host memory mapped for the device (pinned / hipHostMalloc,
+ * or hipMallocManaged): the paged layout, where the same accesses cross the
+ * host link.  QLORA_ERR_BAD_ALPHA for hyperparameters out of range.
+ */
+int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *m, float *v, int64_t count,
+                     float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream);
+
 /* Host copies of the library's constants (host memory, no GPU use):
  * the 16 NF4 levels ("QLoRA Paper Breakdown" sec. 2) and the 15 float32
  * decision thresholds (T_j = smallest float32 above the exact midpoint of
