@@ -317,6 +317,7 @@ def main():
         rows["small_m"] = small_m_rows(q, I, np, torch, dev, dev16, ev)
         rows["storage_types"] = storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops)
         rows["merge"] = merge_rows(q, layers, dev, ev, r, alpha)
+        rows["adamw"] = adamw_rows(q, layers, dev, ev)
 
     calib = None
     if args.calib_copy_mib:
@@ -486,6 +487,53 @@ def merge_rows(q, layers, dev, ev, r, alpha):
             "merge_fp64_tflops": round(flops / (km * 1e-3) / 1e12, 2),
             "merge_frac_fp64_peak": round(flops / (km * 1e-3) / 1e12 / 78.6, 4),
             "how": "W_hat + s B A in float64 (2r flops per weight) + bf16 copy + NF4+DQ re-encoding, 3 layers"}
+
+
+def adamw_rows(q, layers, dev, ev):
+    """One AdamW step over the three layers' adapters (A and B: r (k + n)
+    parameters each), moments in HBM and, the paged layout, in pinned host
+    memory mapped for the device.  28 B per parameter move in either case
+    (16 of them, the moments, cross the host link in the paged one)."""
+    import ctypes
+    import torch
+    count = sum(t["A"].numel() + t["B"].numel() for t in layers)
+    P = torch.zeros(count, dtype=torch.float32, device=dev)
+    P16 = torch.empty(count, dtype=torch.bfloat16, device=dev)
+    G = torch.full((count,), 1e-3, dtype=torch.bfloat16, device=dev)
+    md = torch.zeros(count, dtype=torch.float32, device=dev)
+    vd = torch.zeros(count, dtype=torch.float32, device=dev)
+
+    def timed(m, v, reps=20):
+        for i in range(3):
+            q.qlora_adamw_step(P, P16, G, m, v, 2e-4, 0.9, 0.999, 1e-8, 0.01, 1 + i)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for i in range(reps):
+            q.qlora_adamw_step(P, P16, G, m, v, 2e-4, 0.9, 0.999, 1e-8, 0.01, 4 + i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {"params": count}
+    ms = timed(md, vd)
+    out["hbm_state"] = {"us": round(1e3 * ms, 2), "gbps": round(28 * count / (ms * 1e-3) / 1e9, 1)}
+    mh = torch.zeros(count, dtype=torch.float32).pin_memory()
+    vh = torch.zeros(count, dtype=torch.float32).pin_memory()
+    hip = ctypes.CDLL("libamdhip64.so")
+    ptrs = []
+    for t in (mh, vh):
+        d = ctypes.c_void_p()
+        ptrs.append(d.value if hip.hipHostGetDevicePointer(ctypes.byref(d), ctypes.c_void_p(t.data_ptr()), 0) == 0
+                    else None)
+    if all(ptrs):
+        ms = timed(ptrs[0], ptrs[1], reps=5)
+        out["pinned_host_state"] = {"us": round(1e3 * ms, 2),
+                                    "host_link_gbps": round(16 * count / (ms * 1e-3) / 1e9, 1)}
+    out["how"] = "3 MLP layers' A and B; state in HBM, then in pinned host memory addressed by the kernel"
+    del P, P16, G, md, vd, mh, vh
+    torch.cuda.empty_cache()
+    return out
 
 
 def attainable_peaks(torch, dev, ev):
