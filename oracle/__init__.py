@@ -17,4 +17,5 @@ Modules
 ``merge``    folding trained adapters into the base (W_hat + s B A) and
              re-encoding the result.
 ``adamw``    one AdamW step on the adapters (the paged optimizer's update).
+``mlp``      the gate / up / SwiGLU / down block around the linears.
 """
