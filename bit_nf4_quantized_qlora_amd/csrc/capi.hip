@@ -173,6 +173,37 @@ int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream
   return QLORA_OK;
 }
 
+namespace {
+int elementwise(int op, const char *fn, const uint16_t *x0, const uint16_t *x1, const uint16_t *x2, uint16_t *y0,
+                uint16_t *y1, int64_t count, void *stream) {
+  if (count < 0 || count > kMaxElems) return fail(QLORA_ERR_BAD_SHAPE, "count = %lld", (long long)count);
+  if (count == 0) return QLORA_OK;
+  if (int e = check_tensor(x0, "input")) return e;
+  if (int e = check_tensor(x1, "input")) return e;
+  if (op == 1)
+    if (int e = check_tensor(x2, "dh")) return e;
+  if (int e = check_tensor(y0, "output")) return e;
+  if (op == 1)
+    if (int e = check_tensor(y1, "du")) return e;
+  hipError_t e = launch_swiglu(op, x0, x1, x2, y0, y1, count, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return QLORA_OK;
+}
+}  // namespace
+
+int qlora_swiglu_fwd(const uint16_t *gate, const uint16_t *up, uint16_t *h, int64_t count, void *stream) {
+  return elementwise(0, "qlora_swiglu_fwd", gate, up, nullptr, h, nullptr, count, stream);
+}
+
+int qlora_swiglu_bwd(const uint16_t *gate, const uint16_t *up, const uint16_t *dh, uint16_t *d_gate, uint16_t *d_up,
+                     int64_t count, void *stream) {
+  return elementwise(1, "qlora_swiglu_bwd", gate, up, dh, d_gate, d_up, count, stream);
+}
+
+int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t count, void *stream) {
+  return elementwise(2, "qlora_add_bf16", a, b, nullptr, out, nullptr, count, stream);
+}
+
 int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *m, float *v, int64_t count,
                      float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream) {
   if (count < 0 || count > kMaxElems) return fail(QLORA_ERR_BAD_SHAPE, "count = %lld", (long long)count);

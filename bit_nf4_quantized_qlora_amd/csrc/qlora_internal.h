@@ -35,6 +35,11 @@ hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, b
 // dequant.hip
 hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s);
 
+// swiglu.hip: op 0 y0 = bf16(silu(x0) x1); op 1 (y0, y1) = (dg, du) for
+// g = x0, u = x1, dh = x2; op 2 y0 = bf16(x0 + x1).
+hipError_t launch_swiglu(int op, const uint16_t *x0, const uint16_t *x1, const uint16_t *x2, uint16_t *y0,
+                         uint16_t *y1, int64_t count, hipStream_t s);
+
 // adamw.hip: one AdamW step over count parameters (m, v may be host memory
 // the device addresses).
 hipError_t launch_adamw(float *P, uint16_t *P16, const uint16_t *G, float *M, float *V, int64_t count, float lr,

@@ -60,6 +60,9 @@ _SIGS = {
     "qlora_nf4_thresholds": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_codebook": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
     "qlora_merge_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "qlora_swiglu_fwd": (_c_int, [_vp, _vp, _vp, _c_i64, _vp]),
+    "qlora_swiglu_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "qlora_add_bf16": (_c_int, [_vp, _vp, _vp, _c_i64, _vp]),
     "qlora_adamw_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_float, _c_float, _c_float, _c_float, _c_float,
                                   _c_i64, _vp]),
     "qlora_merge_adapters": (_c_int, [_W, _vp, _vp, _c_int, _c_float, _vp, _W, _vp, _c_size, _vp]),
@@ -200,6 +203,26 @@ def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.T
     _check("qlora_linear_bwd",
            _lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), X.shape[0], _ptr(A), _ptr(B), r, alpha,
                                  _ptr(H), _ptr(dX), _ptr(dA), _ptr(dB), wp, wb, _stream(stream)))
+
+
+def qlora_swiglu_fwd(gate: torch.Tensor, up: torch.Tensor, h: torch.Tensor, stream=None) -> None:
+    for t, nm in ((gate, "gate"), (up, "up"), (h, "h")):
+        _need(t, torch.bfloat16, nm)
+    _check("qlora_swiglu_fwd", _lib.qlora_swiglu_fwd(_ptr(gate), _ptr(up), _ptr(h), gate.numel(), _stream(stream)))
+
+
+def qlora_swiglu_bwd(gate: torch.Tensor, up: torch.Tensor, dh: torch.Tensor, d_gate: torch.Tensor,
+                     d_up: torch.Tensor, stream=None) -> None:
+    for t, nm in ((gate, "gate"), (up, "up"), (dh, "dh"), (d_gate, "d_gate"), (d_up, "d_up")):
+        _need(t, torch.bfloat16, nm)
+    _check("qlora_swiglu_bwd", _lib.qlora_swiglu_bwd(_ptr(gate), _ptr(up), _ptr(dh), _ptr(d_gate), _ptr(d_up),
+                                                     gate.numel(), _stream(stream)))
+
+
+def qlora_add_bf16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    for t, nm in ((a, "a"), (b, "b"), (out, "out")):
+        _need(t, torch.bfloat16, nm)
+    _check("qlora_add_bf16", _lib.qlora_add_bf16(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
 
 
 def qlora_adamw_step(param: torch.Tensor, param_bf16: torch.Tensor | None, grad: torch.Tensor, m, v, lr: float,

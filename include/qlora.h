@@ -189,6 +189,24 @@ int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uin
                          void *stream);
 
 /*
+ * The elementwise pieces of the MLP block the adapted linears sit in (the
+ * reading note's all-linear placement; the pages give no activation, and
+ * the LLaMA MLP whose shapes the workloads use gates with SwiGLU):
+ *   qlora_swiglu_fwd: h = bf16( silu(gate) * up ),  silu(x) = x / (1 + e^-x)
+ *   qlora_swiglu_bwd: d_up = bf16( dh * silu(gate) ),
+ *                     d_gate = bf16( dh * up * sigma(gate) (1 + gate (1 - sigma(gate))) )
+ *   qlora_add_bf16:   out = bf16( a + b )  (the two input gradients of X)
+ * count bf16 elements each, float32 inside, one rounding per output.
+ * With qlora_linear_fwd / _bwd they make the block's step; its backward may
+ * recompute the gate and up outputs from X (checkpointing) instead of
+ * keeping them.
+ */
+int qlora_swiglu_fwd(const uint16_t *gate, const uint16_t *up, uint16_t *h, int64_t count, void *stream);
+int qlora_swiglu_bwd(const uint16_t *gate, const uint16_t *up, const uint16_t *dh, uint16_t *d_gate, uint16_t *d_up,
+                     int64_t count, void *stream);
+int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t count, void *stream);
+
+/*
  * One AdamW step on an adapter tensor ("QLoRA Paper Breakdown" sec. 5, the
  * paged optimizer; "QLoRA, explained." step 6).  The pages print no update
  * rule; the published AdamW (decoupled weight decay, bias-corrected moments),
