@@ -318,6 +318,8 @@ def main():
         rows["storage_types"] = storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops)
         rows["merge"] = merge_rows(q, layers, dev, ev, r, alpha)
         rows["adamw"] = adamw_rows(q, layers, dev, ev)
+        if wl.name == "mlp_7b":
+            rows["mlp_block"] = block_rows(q, layers, dev, ev, ws, M, r, alpha, step_flops)
 
     calib = None
     if args.calib_copy_mib:
@@ -532,6 +534,56 @@ def adamw_rows(q, layers, dev, ev):
                                     "host_link_gbps": round(16 * count / (ms * 1e-3) / 1e9, 1)}
     out["how"] = "3 MLP layers' A and B; state in HBM, then in pinned host memory addressed by the kernel"
     del P, P16, G, md, vd, mh, vh
+    torch.cuda.empty_cache()
+    return out
+
+
+def block_rows(q, layers, dev, ev, ws, M, r, alpha, step_flops):
+    """The same three layers chained as the LLaMA MLP block: gate and up on
+    one X, SwiGLU, down on its output; backward through down, the gate/up
+    outputs recomputed from X (checkpointing), SwiGLU's backward, gate and
+    up, and the sum of the two input gradients."""
+    import torch
+    g, u, d = layers
+    X = g["X"]
+    n = g["L"].n
+    h = torch.empty(M, n, dtype=torch.bfloat16, device=dev)
+    dh, dg, du = (torch.empty(M, n, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    dX = torch.empty_like(g["dX"])
+
+    def fwd():
+        q.qlora_linear_fwd(g["w"], X, g["A"], g["B"], r, alpha, g["Y"], g["H"], ws)
+        q.qlora_linear_fwd(u["w"], X, u["A"], u["B"], r, alpha, u["Y"], u["H"], ws)
+        q.qlora_swiglu_fwd(g["Y"], u["Y"], h)
+        q.qlora_linear_fwd(d["w"], h, d["A"], d["B"], r, alpha, d["Y"], d["H"], ws)
+
+    def bwd():
+        q.qlora_linear_bwd(d["w"], h, d["dY"], d["A"], d["B"], r, alpha, d["H"], dh, d["dA"], d["dB"], ws)
+        q.qlora_linear_fwd(g["w"], X, g["A"], g["B"], r, alpha, g["Y"], None, ws)    # recompute
+        q.qlora_linear_fwd(u["w"], X, u["A"], u["B"], r, alpha, u["Y"], None, ws)
+        q.qlora_swiglu_bwd(g["Y"], u["Y"], dh, dg, du)
+        q.qlora_linear_bwd(g["w"], X, dg, g["A"], g["B"], r, alpha, g["H"], g["dX"], g["dA"], g["dB"], ws)
+        q.qlora_linear_bwd(u["w"], X, du, u["A"], u["B"], r, alpha, u["H"], u["dX"], u["dA"], u["dB"], ws)
+        q.qlora_add_bf16(g["dX"], u["dX"], dX)
+
+    for _ in range(5):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    a, b = ev(), ev()
+    a.record()
+    for _ in range(10):
+        fwd()
+        bwd()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 10
+    recompute = sum(2 * M * t["L"].n * t["L"].k + 2 * M * r * (t["L"].n + t["L"].k) for t in (g, u))
+    out = {"ms": round(ms, 4), "tflops": round(step_flops / (ms * 1e-3) / 1e12, 1),
+           "tflops_with_recompute": round((step_flops + recompute) / (ms * 1e-3) / 1e12, 1),
+           "how": "gate, up -> SwiGLU -> down; backward recomputes gate/up outputs; tflops counts the three "
+                  "layers' fwd+bwd flops (the step's), the second figure adds the recomputed forwards"}
+    del h, dh, dg, du, dX
     torch.cuda.empty_cache()
     return out
 
