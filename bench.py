@@ -68,9 +68,14 @@ def parse():
     return p.parse_args()
 
 
+# the dominant kernel's translation unit and the headers it includes: the
+# traffic counters stay valid until one of these changes
+TILE_SOURCES = ("nf4_tile.hip", "nf4_tile.h", "lora_gemm.h", "qlora_internal.h", "qlora_device.h")
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "bit_nf4_quantized_qlora_amd", "csrc", "*"))):
+    for f in sorted(os.path.join(ROOT, "bit_nf4_quantized_qlora_amd", "csrc", n) for n in TILE_SOURCES):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + b"\0" + fh.read())
     return h.hexdigest()
