@@ -137,6 +137,10 @@ def test_argument_errors_enqueue_nothing(q):
     assert lib.qlora_dequant_bf16(ctypes.byref(single_null), P, None) == q.QLORA_ERR_NULL_ARG
     single = q.qlora_nf4_weight(64, 64, 16, None, None, None, 1, q.QLORA_SCALES_FP32, 16)  # DQ buffers unused
     assert fwd(ctypes.byref(single), P, 16, P, P, 8, 16.0, P, None, P, 16, None) == q.QLORA_ERR_WORKSPACE
+    assert lib.qlora_swiglu_fwd(None, None, None, 0, None) == q.QLORA_OK                        # count 0
+    assert lib.qlora_swiglu_fwd(P, P, None, 8, None) == q.QLORA_ERR_NULL_ARG
+    assert lib.qlora_swiglu_bwd(P, P, ctypes.c_void_p(24), P, P, 8, None) == q.QLORA_ERR_MISALIGNED
+    assert lib.qlora_add_bf16(P, P, P, -1, None) == q.QLORA_ERR_BAD_SHAPE
     adam = lib.qlora_adamw_step
     assert adam(P, None, P, P, P, 16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0, None) == q.QLORA_ERR_BAD_SHAPE   # step 0
     assert adam(P, None, P, P, P, 16, 1e-3, 1.0, 0.999, 1e-8, 0.0, 1, None) == q.QLORA_ERR_BAD_ALPHA   # beta1 = 1
