@@ -400,15 +400,17 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
 // before any of them is used, so the kernel waits for memory once; B rows
 // (contiguous, 256 r bf16) then go through LDS.
 template <bool kVecB>  // r % 8 == 0: B staged by 16-byte loads
-__global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const float *__restrict__ hpart, int nslices,
-                                                     const float *__restrict__ part, const uint16_t *__restrict__ Bl,
-                                                     int r, int RP, float s, int64_t T, int G, int maxcov,
-                                                     bool sparse, int64_t nkb, uint16_t *__restrict__ Y,
-                                                     float *__restrict__ H_out) {
-  constexpr int kPv = 8, kHv = 16, kBv = kGvRows * 128 / 8 / 256;  // loads in flight per thread
-  __shared__ float s_h[128];                        // bf16(s H[m][j]) as floats
+__global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, int fm, const float *__restrict__ hpart,
+                                                     int nslices, const float *__restrict__ part,
+                                                     const uint16_t *__restrict__ Bl, int r, int RP, float s,
+                                                     int64_t T, int G, int maxcov, bool sparse, int64_t nkb,
+                                                     uint16_t *__restrict__ Y, float *__restrict__ H_out) {
+  // fm rows m0 .. m0+fm-1 of Y per workgroup (fm <= kFm, fm * r <= 256): the
+  // group's B rows are staged once for all of them
+  constexpr int kFm = 4, kPv = 8, kHv = 16, kBv = kGvRows * 128 / 8 / 256;  // loads in flight per thread
+  __shared__ float s_h[kFm][128];                   // bf16(s H[m][j]) as floats
   extern __shared__ __align__(16) uint16_t s_b[];   // B rows of the group, row stride r (256 r bf16)
-  const int tid = threadIdx.x, m = blockIdx.y;
+  const int tid = threadIdx.x, m0 = blockIdx.y * fm, nm = min(fm, M - m0);
   const int64_t gr = blockIdx.x;
   const int64_t n = gr * kGvRows + tid;
   const int64_t rows = std::min<int64_t>(kGvRows, N - gr * kGvRows);
@@ -418,14 +420,21 @@ __global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const flo
   const int64_t T4 = T / 4;
   const int64_t wlo = ((gr * nkb / 4 + 1) * G - 1) / T4, whi = ((((gr + 1) * nkb - 1) / 4 + 1) * G - 1) / T4;
   const int nc = (int)(whi - wlo + 1);
-  const float *p = part + ((gr * maxcov) * M + m) * kGvRows + tid;
   const bool live = n < N && !sparse;
-  float pv[kPv];
+  // every load first: partials of each row m, this thread's H slices (thread
+  // (hm, hj) = (tid / r, tid % r) sums H[m0 + hm][hj]), the group's B rows
+  float pv[kFm][kPv];
 #pragma unroll
-  for (int k = 0; k < kPv; ++k) pv[k] = live && k < nc ? p[(int64_t)k * M * kGvRows] : 0.f;
+  for (int mm = 0; mm < kFm; ++mm) {
+    const float *p = part + ((gr * maxcov) * M + m0 + mm) * kGvRows + tid;
+#pragma unroll
+    for (int k = 0; k < kPv; ++k) pv[mm][k] = live && mm < nm && k < nc ? p[(int64_t)k * M * kGvRows] : 0.f;
+  }
+  const int hm = tid / r, hj = tid - hm * r;
+  const bool hlive = hm < nm;
   float hv[kHv];
 #pragma unroll
-  for (int q = 0; q < kHv; ++q) hv[q] = tid < r && q < nslices ? hpart[((int64_t)q * M + m) * RP + tid] : 0.f;
+  for (int q = 0; q < kHv; ++q) hv[q] = hlive && q < nslices ? hpart[((int64_t)q * M + m0 + hm) * RP + hj] : 0.f;
   u32x4_t bv[kBv];
   const int nch = kVecB ? (int)(rows * r / 8) : 0;
   if constexpr (kVecB) {
@@ -436,13 +445,13 @@ __global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const flo
     }
   }
 
-  if (tid < r) {  // H[m][tid], slice order
+  if (hlive) {  // H[m0 + hm][hj], slice order
     float h = 0.f;
 #pragma unroll
     for (int q = 0; q < kHv; ++q) h += hv[q];
-    for (int q = kHv; q < nslices; ++q) h += hpart[((int64_t)q * M + m) * RP + tid];
-    if (gr == 0 && H_out) H_out[(int64_t)m * r + tid] = h;
-    s_h[tid] = bf16_to_f32(f32_to_bf16_bits(__fmul_rn(s, h)));
+    for (int q = kHv; q < nslices; ++q) h += hpart[((int64_t)q * M + m0 + hm) * RP + hj];
+    if (gr == 0 && H_out) H_out[(int64_t)(m0 + hm) * r + hj] = h;
+    s_h[hm][hj] = bf16_to_f32(f32_to_bf16_bits(__fmul_rn(s, h)));
   }
   if constexpr (kVecB) {
 #pragma unroll
@@ -453,26 +462,37 @@ __global__ __launch_bounds__(256) void k_gemv_finish(int64_t N, int M, const flo
   } else {
     for (int c = tid; c < rows * r; c += 256) s_b[c] = bsrc[c];
   }
-  float y = 0.f;
-  if (n < N) {
-    if (!sparse) {
+  float y[kFm];
 #pragma unroll
-      for (int k = 0; k < kPv; ++k) y += pv[k];
-      for (int k = kPv; k < nc; ++k) y += p[(int64_t)k * M * kGvRows];
-    } else {
-      for (int64_t q = wlo; q <= whi; ++q) {
-        // an empty range (more workgroups than 4-block units) wrote nothing
-        if (4 * ((q + 1) * T4 / G) == 4 * (q * T4 / G)) continue;
-        y += p[(q - wlo) * M * kGvRows];
+  for (int mm = 0; mm < kFm; ++mm) {
+    y[mm] = 0.f;
+    if (n < N && mm < nm) {
+      const float *p = part + ((gr * maxcov) * M + m0 + mm) * kGvRows + tid;
+      if (!sparse) {
+#pragma unroll
+        for (int k = 0; k < kPv; ++k) y[mm] += pv[mm][k];
+        for (int k = kPv; k < nc; ++k) y[mm] += p[(int64_t)k * M * kGvRows];
+      } else {
+        for (int64_t q = wlo; q <= whi; ++q) {
+          // an empty range (more workgroups than 4-block units) wrote nothing
+          if (4 * ((q + 1) * T4 / G) == 4 * (q * T4 / G)) continue;
+          y[mm] += p[(q - wlo) * M * kGvRows];
+        }
       }
     }
   }
   __syncthreads();  // s_h, s_b
   if (n >= N) return;
-  float lo = 0.f;
+  float lo[kFm] = {0.f, 0.f, 0.f, 0.f};
   const uint16_t *brow = s_b + tid * r;
-  for (int j = 0; j < r; ++j) lo = __fmaf_rn(s_h[j], bf16_to_f32(brow[j]), lo);
-  Y[(int64_t)m * N + n] = f32_to_bf16_bits(y + lo);
+  for (int j = 0; j < r; ++j) {
+    const float b = bf16_to_f32(brow[j]);
+#pragma unroll
+    for (int mm = 0; mm < kFm; ++mm) lo[mm] = __fmaf_rn(s_h[mm][j], b, lo[mm]);
+  }
+#pragma unroll
+  for (int mm = 0; mm < kFm; ++mm)
+    if (mm < nm) Y[(int64_t)(m0 + mm) * N + n] = f32_to_bf16_bits(y[mm] + lo[mm]);
 }
 
 }  // namespace
@@ -499,11 +519,16 @@ hipError_t launch_fwd_small(const Nf4View &w, const uint16_t *X, int64_t M, cons
                T4, p.G, T4 / p.G, T4 % p.G, p.seg, p.maxcov, p.nh, p.nht, p.xoff);
   // the group's B rows in LDS, sized by the rank (more workgroups per CU at small r)
   const size_t bshm = (size_t)kGvRows * r * sizeof(uint16_t);
+  // rows of Y per workgroup: up to 4 (one H-summing thread per (row, rank)),
+  // while the grid keeps at least one workgroup per CU
+  int fm = 1;
+  while (2 * fm <= std::min({4, 256 / r, (int)M}) && p.ngroups * ceil_div(M, (int64_t)(2 * fm)) >= 256) fm *= 2;
+  const dim3 fgrid((unsigned)p.ngroups, (unsigned)ceil_div(M, (int64_t)fm));
   if (r % 8 == 0)
-    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<true>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), bshm, st, w.n, (int)M,
+    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<true>, fgrid, dim3(256), bshm, st, w.n, (int)M, fm,
                  hpart, p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.maxcov, p.sparse, p.nkb, Y, H_out);
   else
-    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<false>, dim3((unsigned)p.ngroups, (unsigned)M), dim3(256), bshm, st, w.n, (int)M,
+    QLORA_LAUNCH("k_gemv_finish", k_gemv_finish<false>, fgrid, dim3(256), bshm, st, w.n, (int)M, fm,
                  hpart, p.nh / p.nht, part, B, r, RP, s, p.T, p.G, p.maxcov, p.sparse, p.nkb, Y, H_out);
   return hipGetLastError();
 }
