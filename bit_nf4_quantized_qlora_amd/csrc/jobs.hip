@@ -28,28 +28,32 @@ struct SmallJobs {
 // turns in LDS (row stride 65, so the column reads hit distinct banks).
 __device__ __forceinline__ void run_transpose(const SmallJob &j, uint32_t idx, uint16_t (*t)[65]) {
   const uint32_t tile = idx >> 8, tid = idx & 255;
-  const int64_t rows = j.a, cols = j.b, out_rows = j.c, ldo = j.d;
-  const uint32_t tiles_rr = (uint32_t)((ldo + 63) / 64);
+  const uint32_t rows = (uint32_t)j.a, cols = (uint32_t)j.b, out_rows = (uint32_t)j.c, ldo = (uint32_t)j.d;
+  const uint32_t tiles_rr = (ldo + 63) / 64;
   const uint32_t tc = tile / tiles_rr, tr = tile - tc * tiles_rr;
-  const int64_t c0 = (int64_t)tc * 64, rr0 = (int64_t)tr * 64;
-  const int col = tid & 63;
+  const uint32_t c0 = tc * 64, rr0 = tr * 64;
+  const uint32_t col = tid & 63, c = c0 + col;
+  // all 16 loads go out before any is used (out-of-range elements load
+  // element 0 and are replaced by zero), so the tile waits for memory once
+  uint32_t v[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int row = (int)(tid >> 6) + 4 * e;
-    const int64_t rr = rr0 + row, c = c0 + col;
-    uint16_t v = 0;
-    if (rr < rows && c < cols)
-      v = j.i ? f32_to_bf16_bits(j.f * static_cast<const float *>(j.in)[rr * cols + c])
-              : static_cast<const uint16_t *>(j.in)[rr * cols + c];
-    t[row][col] = v;
+    const uint32_t rr = rr0 + (tid >> 6) + 4 * e;
+    const bool ok = rr < rows && c < cols;
+    const uint32_t src = ok ? rr * cols + c : 0u;
+    v[e] = j.i ? __float_as_uint(static_cast<const float *>(j.in)[src]) : static_cast<const uint16_t *>(j.in)[src];
+    v[e] = ok ? v[e] : 0u;
   }
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    t[(tid >> 6) + 4 * e][col] = j.i ? f32_to_bf16_bits(j.f * __uint_as_float(v[e])) : (uint16_t)v[e];
   __syncthreads();
   uint16_t *out = static_cast<uint16_t *>(j.out);
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int oc = (int)(tid >> 6) + 4 * e;
-    const int64_t c = c0 + oc, rr = rr0 + col;
-    if (c < out_rows && rr < ldo) out[c * ldo + rr] = t[col][oc];
+    const uint32_t oc = (tid >> 6) + 4 * e;
+    const uint32_t cc = c0 + oc, rr = rr0 + col;
+    if (cc < out_rows && rr < ldo) out[cc * ldo + rr] = t[col][oc];
   }
 }
 
@@ -111,11 +115,25 @@ __device__ __forceinline__ void run_scales_fwd(const SmallJob &j, uint32_t t) {
   const int64_t n = to * kTileRows + (t & 255), nkb = w.k / kBlock;
   f32x4_t v = {0.f, 0.f, 0.f, 0.f};
   if (n < w.n) {
+    // every load before any use (blocks past k/64 read block 0, then give 0)
     const float off = w.absmax ? 0.f : *w.offset;
+    uint32_t c8[kTileSup];
+    float ga[kTileSup];
 #pragma unroll
     for (int u = 0; u < kTileSup; ++u) {
-      const int64_t kb = kTileSup * sp + u, b = n * nkb + kb;
-      if (kb < nkb) v[u] = w.absmax ? w.absmax[b] : block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
+      const int64_t kb = kTileSup * sp + u, b = kb < nkb ? n * nkb + kb : 0;
+      if (w.absmax) {
+        c8[u] = __float_as_uint(w.absmax[b]);
+        ga[u] = 0.f;
+      } else {
+        c8[u] = w.scale_code[b];
+        ga[u] = w.group_amax[b / kGroup];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTileSup; ++u) {
+      const int64_t kb = kTileSup * sp + u;
+      if (kb < nkb) v[u] = w.absmax ? __uint_as_float(c8[u]) : block_scale(c8[u], ga[u], off);
     }
   }
   *reinterpret_cast<f32x4_t *>(static_cast<float *>(j.out) + 4 * t) = v;
@@ -133,14 +151,27 @@ __device__ __forceinline__ void run_scales_bwd(const SmallJob &j, uint32_t t) {
   const int64_t n = (int64_t)sp * kTileRows + (t & 255), nkb = w.k / kBlock;
   float *out = static_cast<float *>(j.out) + (size_t)q * 4 * 256 + (t & 255);
   const float off = w.absmax ? 0.f : *w.offset;
+  // every load before any use (rows past n or blocks past k/64 read block 0,
+  // then give 0)
+  uint32_t c8[kTileSup];
+  float ga[kTileSup];
+#pragma unroll
+  for (int blk = 0; blk < kTileSup; ++blk) {
+    const int64_t kb = (int64_t)tk * kTileSup + blk;
+    const int64_t b = n < w.n && kb < nkb ? n * nkb + kb : 0;
+    if (w.absmax) {
+      c8[blk] = __float_as_uint(w.absmax[b]);
+      ga[blk] = 0.f;
+    } else {
+      c8[blk] = w.scale_code[b];
+      ga[blk] = w.group_amax[b / kGroup];
+    }
+  }
 #pragma unroll
   for (int blk = 0; blk < kTileSup; ++blk) {
     const int64_t kb = (int64_t)tk * kTileSup + blk;
     float v = 0.f;
-    if (n < w.n && kb < nkb) {
-      const int64_t b = n * nkb + kb;
-      v = w.absmax ? w.absmax[b] : block_scale(w.scale_code[b], w.group_amax[b / kGroup], off);
-    }
+    if (n < w.n && kb < nkb) v = w.absmax ? __uint_as_float(c8[blk]) : block_scale(c8[blk], ga[blk], off);
     out[blk * 256] = v;
   }
 }
