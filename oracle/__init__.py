@@ -18,4 +18,5 @@ Modules
              re-encoding the result.
 ``adamw``    one AdamW step on the adapters (the paged optimizer's update).
 ``mlp``      the gate / up / SwiGLU / down block around the linears.
+``attention`` the causal attention core between the q/k/v and o projections.
 """
