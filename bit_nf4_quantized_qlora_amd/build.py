@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
-SOURCES = ["capi.hip", "profile.hip", "quantize.hip", "dequant.hip", "lora_gemm.hip", "jobs.hip", "nf4_tile.hip", "nf4_gemv.hip", "linear_fwd.hip", "linear_bwd.hip", "merge.hip", "adamw.hip", "swiglu.hip"]
+SOURCES = ["capi.hip", "profile.hip", "quantize.hip", "dequant.hip", "lora_gemm.hip", "jobs.hip", "nf4_tile.hip", "nf4_gemv.hip", "linear_fwd.hip", "linear_bwd.hip", "merge.hip", "adamw.hip", "swiglu.hip", "attention.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

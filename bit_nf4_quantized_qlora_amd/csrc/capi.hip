@@ -204,6 +204,60 @@ int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t 
   return elementwise(2, "qlora_add_bf16", a, b, nullptr, out, nullptr, count, stream);
 }
 
+namespace {
+// Shapes the attention calls accept; 0 = valid.
+int check_attention(int64_t batch, int64_t seq, int64_t heads, int64_t d) {
+  if (batch < 0 || seq < 0 || batch > 65535 || seq > 65536)
+    return fail(QLORA_ERR_BAD_SHAPE, "batch = %lld, seq = %lld", (long long)batch, (long long)seq);
+  if (heads < 1 || heads > 65535) return fail(QLORA_ERR_BAD_SHAPE, "heads = %lld", (long long)heads);
+  if (d < 8 || d > 1024 || d % 8 != 0) return fail(QLORA_ERR_BAD_SHAPE, "head_dim = %lld (8..1024, a multiple of 8)", (long long)d);
+  if (batch * seq > kMaxElems / (heads * d)) return fail(QLORA_ERR_BAD_SHAPE, "attention tensors too large");
+  if (batch * heads > kMaxElems / (seq * seq + 1)) return fail(QLORA_ERR_BAD_SHAPE, "attention scores too large");
+  return QLORA_OK;
+}
+}  // namespace
+
+size_t qlora_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t head_dim) {
+  if (batch < 0 || seq < 0 || batch > 65535 || seq > 65536 || heads < 1 || heads > 65535 || head_dim < 8 ||
+      head_dim > 1024 || head_dim % 8 != 0 || batch * seq > kMaxElems / (heads * head_dim) ||
+      batch * heads > kMaxElems / (seq * seq + 1))
+    return 0;
+  return attention_workspace_bytes(batch, seq, heads);
+}
+
+int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
+                        int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
+                        void *stream) {
+  if (int e = check_attention(batch, seq, heads, head_dim)) return e;
+  if (batch == 0 || seq == 0) return QLORA_OK;
+  if (int e = check_tensor(q, "q")) return e;
+  if (int e = check_tensor(k, "k")) return e;
+  if (int e = check_tensor(v, "v")) return e;
+  if (int e = check_tensor(o, "o")) return e;
+  if (int e = check_tensor(lse, "lse")) return e;
+  if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads))) return e;
+  hipError_t e = launch_attention_fwd(q, k, v, o, lse, batch, seq, heads, head_dim, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qlora_attention_fwd");
+  return QLORA_OK;
+}
+
+int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+                        const uint16_t *d_o, const float *lse, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                        int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
+                        void *stream) {
+  if (int e = check_attention(batch, seq, heads, head_dim)) return e;
+  if (batch == 0 || seq == 0) return QLORA_OK;
+  const void *ptrs[] = {q, k, v, o, d_o, lse, dq, dk, dv};
+  const char *names[] = {"q", "k", "v", "o", "d_o", "lse", "dq", "dk", "dv"};
+  for (int i = 0; i < 9; ++i)
+    if (int e = check_tensor(ptrs[i], names[i])) return e;
+  if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads))) return e;
+  hipError_t e = launch_attention_bwd(q, k, v, o, d_o, lse, dq, dk, dv, batch, seq, heads, head_dim, ws,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "qlora_attention_bwd");
+  return QLORA_OK;
+}
+
 int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *m, float *v, int64_t count,
                      float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream) {
   if (count < 0 || count > kMaxElems) return fail(QLORA_ERR_BAD_SHAPE, "count = %lld", (long long)count);

@@ -61,6 +61,10 @@ _SIGS = {
     "qlora_codebook": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
     "qlora_merge_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
     "qlora_swiglu_fwd": (_c_int, [_vp, _vp, _vp, _c_i64, _vp]),
+    "qlora_attention_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "qlora_attention_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _c_size, _vp]),
+    "qlora_attention_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64,
+                                     _vp, _c_size, _vp]),
     "qlora_swiglu_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "qlora_add_bf16": (_c_int, [_vp, _vp, _vp, _c_i64, _vp]),
     "qlora_adamw_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_float, _c_float, _c_float, _c_float, _c_float,
@@ -223,6 +227,34 @@ def qlora_add_bf16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor, stream=N
     for t, nm in ((a, "a"), (b, "b"), (out, "out")):
         _need(t, torch.bfloat16, nm)
     _check("qlora_add_bf16", _lib.qlora_add_bf16(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
+
+
+def qlora_attention_workspace_bytes(batch: int, seq: int, heads: int, head_dim: int) -> int:
+    return _lib.qlora_attention_workspace_bytes(batch, seq, heads, head_dim)
+
+
+def qlora_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                        batch: int, seq: int, heads: int, head_dim: int, ws: torch.Tensor, stream=None) -> None:
+    """q, k, v, o: bf16 [batch*seq, heads*head_dim]; lse: float32 [batch, heads, seq]."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
+        _need(t, torch.bfloat16, nm)
+    _need(lse, torch.float32, "lse")
+    w, wb = _ws_args(ws)
+    _check("qlora_attention_fwd",
+           _lib.qlora_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), batch, seq, heads, head_dim, w, wb,
+                                    _stream(stream)))
+
+
+def qlora_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d_o: torch.Tensor,
+                        lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, batch: int, seq: int,
+                        heads: int, head_dim: int, ws: torch.Tensor, stream=None) -> None:
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _need(t, torch.bfloat16, nm)
+    _need(lse, torch.float32, "lse")
+    w, wb = _ws_args(ws)
+    _check("qlora_attention_bwd",
+           _lib.qlora_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), batch, seq, heads, head_dim, w, wb, _stream(stream)))
 
 
 def qlora_adamw_step(param: torch.Tensor, param_bf16: torch.Tensor | None, grad: torch.Tensor, m, v, lr: float,

@@ -207,6 +207,40 @@ int qlora_swiglu_bwd(const uint16_t *gate, const uint16_t *up, const uint16_t *d
 int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t count, void *stream);
 
 /*
+ * The causal attention core between the q/k/v and o projections of the
+ * decoder layer whose seven linears all hold adapters ("QLoRA, explained.",
+ * all-linear placement; the LLaMA layer of "QLoRA Explained ... Part 2/6",
+ * App. G).  The pages do not write attention out: this is the plain causal
+ * scaled dot-product attention, per sequence and head, no positional
+ * rotation (it holds no adapter):
+ *   S = Q K^T / sqrt(head_dim) over keys j <= query i,  P = softmax_j(S),
+ *   O = P V,  lse_i = log sum_j exp(S_ij);
+ *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D), D_i = dO_i . O_i,
+ *   dQ = dS K / sqrt(head_dim),  dK = dS^T Q / sqrt(head_dim).
+ * q, k, v, o, d_o, dq, dk, dv: device bf16 [batch*seq, heads*head_dim]
+ * row-major (the projections' outputs; sequence b is rows b*seq ..
+ * b*seq+seq-1, head h is columns h*head_dim ..), caller-owned, 16-byte
+ * aligned.  lse: device float32 [batch][heads][seq], written by the forward
+ * and read by the backward.  P and dS are rounded to bf16 before the
+ * products that take them; every product accumulates in float32 and rounds
+ * its output once.
+ * Shapes: head_dim a multiple of 8 in [8, 1024], heads in [1, 65535],
+ * batch in [0, 65535], seq in [0, 65536]; otherwise QLORA_ERR_BAD_SHAPE.
+ * batch == 0 or seq == 0 does nothing.  The workspace (device, 16-byte
+ * aligned) holds the float32 scores and their gradient and the bf16 P and
+ * dS, 12 * batch * heads * seq * roundup(seq, 8) bytes plus alignment:
+ * qlora_attention_workspace_bytes (0 for shapes the calls reject).
+ */
+size_t qlora_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t head_dim);
+int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
+                        int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
+                        void *stream);
+int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
+                        const uint16_t *d_o, const float *lse, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+                        int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/*
  * One AdamW step on an adapter tensor ("QLoRA Paper Breakdown" sec. 5, the
  * paged optimizer; "QLoRA, explained." step 6).  The pages print no update
  * rule; the published AdamW (decoupled weight decay, bias-corrected moments),
