@@ -19,4 +19,6 @@ Modules
 ``adamw``    one AdamW step on the adapters (the paged optimizer's update).
 ``mlp``      the gate / up / SwiGLU / down block around the linears.
 ``attention`` the causal attention core between the q/k/v and o projections.
+``layer``    the decoder layer: the seven adapted projections, attention,
+             SwiGLU and the two residual additions.
 """
