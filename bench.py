@@ -325,6 +325,7 @@ def main():
         rows["adamw"] = adamw_rows(q, layers, dev, ev)
         if wl.name == "mlp_7b":
             rows["mlp_block"] = block_rows(q, layers, dev, ev, ws, M, r, alpha, step_flops)
+            rows["decoder_layer"] = layer_rows(q, I, layers, dev, ev, M, r, alpha, wl.adapter_bound)
 
     calib = None
     if args.calib_copy_mib:
@@ -589,6 +590,75 @@ def block_rows(q, layers, dev, ev, ws, M, r, alpha, step_flops):
            "how": "gate, up -> SwiGLU -> down; backward recomputes gate/up outputs; tflops counts the three "
                   "layers' fwd+bwd flops (the step's), the second figure adds the recomputed forwards"}
     del h, dh, dg, du, dX
+    torch.cuda.empty_cache()
+    return out
+
+
+def layer_rows(q, I, layers, dev, ev, M, r, alpha, adapter_bound, seq=512, heads=32, head_dim=128):
+    """The LLaMA-7B decoder layer: q, k, v, o (4096 x 4096 NF4+DQ, each with
+    its own adapters) around the causal attention core (M / 512 sequences of
+    512 tokens, 32 heads of 128), the residuals and the MLP layers above;
+    the backward recomputes the layer from X (checkpointing).  Then the
+    attention core alone at the same shape.  Attention flops count the
+    causal pairs only: per head 4 d per pair forward (QK^T, PV) and 8 d
+    backward (dV, dP, dQ, dK)."""
+    import numpy as np
+    import torch
+    from bit_nf4_quantized_qlora_amd.layer import DecoderLayer
+    g, u, d = layers
+    hidden, batch = heads * head_dim, M // seq
+    d16 = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+    weights = {"gate": g["w"], "up": u["w"], "down": d["w"]}
+    adapters = {"gate": (g["A"], g["B"]), "up": (u["A"], u["B"]), "down": (d["A"], d["B"])}
+    qws = torch.empty(q.qlora_quantize_workspace_bytes(hidden, hidden), dtype=torch.uint8, device=dev)
+    for i, nm in enumerate(("q", "k", "v", "o")):
+        w = q.NF4Weight.empty(hidden, hidden, device=dev)
+        q.qlora_quantize_nf4_dq(torch.from_numpy(I.custom_weight(hidden, hidden, 500 + i)).to(dev), w, qws)
+        weights[nm] = w
+        adapters[nm] = (d16(I.custom_bf16((r, hidden), 510 + i, 1, bound=adapter_bound)),
+                        d16(I.custom_bf16((hidden, r), 510 + i, 2, bound=adapter_bound)))
+    del qws
+    lay = DecoderLayer(weights, adapters, r, alpha, batch, seq, heads, head_dim, device=dev)
+    X, dY = g["X"], d["dY"]
+    Y, dX, Y2 = (torch.empty(M, hidden, dtype=torch.bfloat16, device=dev) for _ in range(3))
+
+    def timed(fn, n=10, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    ms = timed(lambda: (lay.fwd(X, Y), lay.bwd(X, dY, dX, Y2)))
+    lin_f = lin_b = 0
+    for nm, w in weights.items():
+        f, b_ = layer_flops(M, w.n, w.k, r)
+        lin_f, lin_b = lin_f + f, lin_b + b_
+    pairs = batch * heads * seq * (seq + 1) // 2
+    att_f, att_b = 4 * head_dim * pairs, 8 * head_dim * pairs
+    flops, recompute = lin_f + lin_b + att_f + att_b, lin_f + att_f
+    a = lay.act
+    g_ = lay.grad
+    fwd_ms = timed(lambda: q.qlora_attention_fwd(a["q"], a["k"], a["v"], a["attn"], lay.lse, batch, seq, heads,
+                                                 head_dim, lay.ws))
+    bwd_ms = timed(lambda: q.qlora_attention_bwd(a["q"], a["k"], a["v"], g_["dattn"], lay.lse, g_["dq"],
+                                                 g_["dk"], g_["dv"], batch, seq, heads, head_dim, lay.ws))
+    tf = lambda fl, m: round(fl / (m * 1e-3) / 1e12, 1)
+    out = {"ms": round(ms, 4), "tflops": tf(flops, ms), "tflops_with_recompute": tf(flops + recompute, ms),
+           "attention": {"fwd_ms": round(fwd_ms, 4), "fwd_tflops": tf(att_f, fwd_ms),
+                         "bwd_ms": round(bwd_ms, 4), "bwd_tflops": tf(att_b, bwd_ms),
+                         "frac_bf16_peak": round((att_f + att_b) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
+                                                 / PEAK_BF16_TFLOPS, 4)},
+           "how": f"q,k,v,o (4096x4096) + gate,up,down NF4+DQ with r={r} adapters, causal attention over {batch} "
+                  f"sequences of {seq} ({heads} heads of {head_dim}), SwiGLU, residuals; fwd + checkpointed bwd; "
+                  "tflops counts the 7 projections' fwd+bwd and the causal attention pairs, the second figure adds "
+                  "the recomputed forward"}
+    del lay, Y, dX, Y2
     torch.cuda.empty_cache()
     return out
 

@@ -7,8 +7,8 @@
 // dot-product attention of a LLaMA decoder layer, per sequence and head:
 //   S = Q K^T / sqrt(d) for key j <= query i, P = softmax_j(S), O = P V,
 //   lse_i = log sum_j exp S_ij;
-//   dV = P^T dO, dP = dO V^T, dS = P (dP - D) with D_i = dO_i . O_i
-//   (= sum_j P_ij dP_ij), dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
+//   dV = P^T dO, dP = dO V^T, dS = P (dP - D) with D_i = sum_j P_ij dP_ij,
+//   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
 //
 // Q, K, V, O (and their gradients) are [batch * seq, heads * d] row-major
 // bf16, the projections' outputs as they come.  The scores are materialised
@@ -28,7 +28,8 @@
 //
 // Row kernels: one wave per query row.  The forward softmax takes the row
 // maximum and the sum of exponentials in float32 and writes P and lse; the
-// backward row pass recomputes P = exp(S - lse) and writes P and dS.  Both
+// backward row pass recomputes P = exp(S - lse), sums D from P and dP, and
+// writes P and dS.  Both
 // write zeros for the masked entries up to the end of the diagonal tile,
 // the only masked entries a product reads.
 #include <cmath>
@@ -161,8 +162,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
 // Columns a row's products read: up to the end of its diagonal tile.
 __device__ __forceinline__ int row_span(int q, int seq) { return min(seq, (q / kT + 1) * kT); }
 
@@ -187,23 +186,24 @@ __global__ __launch_bounds__(256) void k_attn_softmax(const float *__restrict__ 
   if (lane == 0) lse[r] = m + logf(zsum);
 }
 
-// Backward row pass: D = dO_q . O_q, P = exp(S - lse), dS = P (dP - D).
+// Backward row pass: P = exp(S - lse), D = sum_j P_j dP_j, dS = P (dP - D).
+// D is summed from the float32 P and dP of the row itself (a first pass
+// over the row), so each row of dS sums to zero up to float32 rounding;
+// taking D = dO . O from the bf16 output instead would carry O's rounding
+// into dP - D, which cancels where the attention is sharply peaked.
 __global__ __launch_bounds__(256) void k_attn_bwd_rows(const float *__restrict__ S, const float *__restrict__ dP,
-                                                       const float *__restrict__ lse, const uint16_t *__restrict__ O,
-                                                       const uint16_t *__restrict__ dO, uint16_t *__restrict__ P,
-                                                       uint16_t *__restrict__ dS, int64_t rows, int seq, int heads,
-                                                       int d, int64_t ldp) {
+                                                       const float *__restrict__ lse, uint16_t *__restrict__ P,
+                                                       uint16_t *__restrict__ dS, int64_t rows, int seq,
+                                                       int64_t ldp) {
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   const int lane = threadIdx.x & 63;
   const int q = (int)(r % seq), n = q + 1;
-  const int64_t bh = r / seq, b = bh / heads, h = bh - b * heads;
-  const int64_t off = (b * seq + q) * (int64_t)heads * d + h * d;
-  float D = 0.f;
-  for (int j = lane; j < d; j += 64) D += bf16_to_f32(O[off + j]) * bf16_to_f32(dO[off + j]);
-  D = wave_sum(D);
   const float L = lse[r];
   const float *s = S + r * ldp, *dp = dP + r * ldp;
+  float D = 0.f;
+  for (int j = lane; j < n; j += 64) D += expf(s[j] - L) * dp[j];
+  D = wave_sum(D);
   uint16_t *p = P + r * ldp, *ds = dS + r * ldp;
   const int span = row_span(q, seq);
   for (int j = lane; j < span; j += 64) {
@@ -290,8 +290,7 @@ hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint
   return hipGetLastError();
 }
 
-hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *O,
-                                const uint16_t *dO, const float *lse, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
+hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *dO, const float *lse, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
                                 int64_t batch, int64_t seq, int64_t heads, int64_t d, void *ws, hipStream_t s) {
   const Dims x{batch, seq, heads, d, (int64_t)align_up((size_t)seq, 8)};
   const Ws w = carve(ws, x);
@@ -301,7 +300,7 @@ hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint
   gemm<true, true, false>("k_attn_dp", x, qkv(dO, x), qkv(V, x), w.dP, true, L, L, D, 1.0f, 1, 0, s);
   const int64_t rows = batch * heads * seq;
   QLORA_LAUNCH("k_attn_bwd_rows", k_attn_bwd_rows, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, w.S, w.dP,
-               lse, O, dO, w.P, w.dS, rows, L, (int)heads, D, x.ldp);
+               lse, w.P, w.dS, rows, L, x.ldp);
   // dV = P^T dO; dK = dS^T Q / sqrt(d): rows are keys, the contraction runs over queries >= key
   gemm<false, false, true>("k_attn_dv", x, scores(w.P, x), qkv(dO, x), dV, false, L, D, L, 1.0f, 0, 2, s);
   gemm<false, false, true>("k_attn_dk", x, scores(w.dS, x), qkv(Q, x), dK, false, L, D, L, scale, 0, 2, s);

@@ -241,18 +241,18 @@ int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   return QLORA_OK;
 }
 
-int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
-                        const uint16_t *d_o, const float *lse, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *d_o, const float *lse,
+                        uint16_t *dq, uint16_t *dk, uint16_t *dv,
                         int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
                         void *stream) {
   if (int e = check_attention(batch, seq, heads, head_dim)) return e;
   if (batch == 0 || seq == 0) return QLORA_OK;
-  const void *ptrs[] = {q, k, v, o, d_o, lse, dq, dk, dv};
-  const char *names[] = {"q", "k", "v", "o", "d_o", "lse", "dq", "dk", "dv"};
-  for (int i = 0; i < 9; ++i)
+  const void *ptrs[] = {q, k, v, d_o, lse, dq, dk, dv};
+  const char *names[] = {"q", "k", "v", "d_o", "lse", "dq", "dk", "dv"};
+  for (int i = 0; i < 8; ++i)
     if (int e = check_tensor(ptrs[i], names[i])) return e;
   if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads))) return e;
-  hipError_t e = launch_attention_bwd(q, k, v, o, d_o, lse, dq, dk, dv, batch, seq, heads, head_dim, ws,
+  hipError_t e = launch_attention_bwd(q, k, v, d_o, lse, dq, dk, dv, batch, seq, heads, head_dim, ws,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "qlora_attention_bwd");
   return QLORA_OK;

@@ -41,8 +41,7 @@ hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s);
 size_t attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads);
 hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O, float *lse,
                                 int64_t batch, int64_t seq, int64_t heads, int64_t d, void *ws, hipStream_t s);
-hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *O,
-                                const uint16_t *dO, const float *lse, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
+hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *dO, const float *lse, uint16_t *dQ, uint16_t *dK, uint16_t *dV,
                                 int64_t batch, int64_t seq, int64_t heads, int64_t d, void *ws, hipStream_t s);
 hipError_t launch_swiglu(int op, const uint16_t *x0, const uint16_t *x1, const uint16_t *x2, uint16_t *y0,
                          uint16_t *y1, int64_t count, hipStream_t s);

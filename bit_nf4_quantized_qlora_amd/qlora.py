@@ -63,7 +63,7 @@ _SIGS = {
     "qlora_swiglu_fwd": (_c_int, [_vp, _vp, _vp, _c_i64, _vp]),
     "qlora_attention_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "qlora_attention_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _c_size, _vp]),
-    "qlora_attention_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64,
+    "qlora_attention_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i64, _c_i64, _c_i64, _c_i64,
                                      _vp, _c_size, _vp]),
     "qlora_swiglu_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "qlora_add_bf16": (_c_int, [_vp, _vp, _vp, _c_i64, _vp]),
@@ -245,15 +245,15 @@ def qlora_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: to
                                     _stream(stream)))
 
 
-def qlora_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, d_o: torch.Tensor,
-                        lse: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, batch: int, seq: int,
+def qlora_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor, lse: torch.Tensor,
+                        dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, batch: int, seq: int,
                         heads: int, head_dim: int, ws: torch.Tensor, stream=None) -> None:
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
         _need(t, torch.bfloat16, nm)
     _need(lse, torch.float32, "lse")
     w, wb = _ws_args(ws)
     _check("qlora_attention_bwd",
-           _lib.qlora_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
+           _lib.qlora_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
                                     _ptr(dv), batch, seq, heads, head_dim, w, wb, _stream(stream)))
 
 

@@ -215,13 +215,14 @@ int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t 
  * rotation (it holds no adapter):
  *   S = Q K^T / sqrt(head_dim) over keys j <= query i,  P = softmax_j(S),
  *   O = P V,  lse_i = log sum_j exp(S_ij);
- *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D), D_i = dO_i . O_i,
+ *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D), D_i = sum_j P_ij dP_ij,
  *   dQ = dS K / sqrt(head_dim),  dK = dS^T Q / sqrt(head_dim).
  * q, k, v, o, d_o, dq, dk, dv: device bf16 [batch*seq, heads*head_dim]
  * row-major (the projections' outputs; sequence b is rows b*seq ..
  * b*seq+seq-1, head h is columns h*head_dim ..), caller-owned, 16-byte
  * aligned.  lse: device float32 [batch][heads][seq], written by the forward
- * and read by the backward.  P and dS are rounded to bf16 before the
+ * and read by the backward, which recomputes P from it (and does not read o:
+ * D is summed from P and dP in float32).  P and dS are rounded to bf16 before the
  * products that take them; every product accumulates in float32 and rounds
  * its output once.
  * Shapes: head_dim a multiple of 8 in [8, 1024], heads in [1, 65535],
@@ -235,8 +236,8 @@ size_t qlora_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads
 int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
                         int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
                         void *stream);
-int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *o,
-                        const uint16_t *d_o, const float *lse, uint16_t *dq, uint16_t *dk, uint16_t *dv,
+int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *d_o, const float *lse,
+                        uint16_t *dq, uint16_t *dk, uint16_t *dv,
                         int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
                         void *stream);
 

@@ -173,7 +173,7 @@ def test_attention_shape_and_argument_errors(q):
     for bad in ((1, 16, 2, 60), (1, 16, 2, 0), (1, 16, 0, 64), (-1, 16, 2, 64), (1, 70000, 2, 64), (1, 16, 2, 2048)):
         assert q.qlora_attention_workspace_bytes(*bad) == 0
         assert lib.qlora_attention_fwd(P, P, P, P, P, *bad, P, big, None) == q.QLORA_ERR_BAD_SHAPE
-        assert lib.qlora_attention_bwd(P, P, P, P, P, P, P, P, P, *bad, P, big, None) == q.QLORA_ERR_BAD_SHAPE
+        assert lib.qlora_attention_bwd(P, P, P, P, P, P, P, P, *bad, P, big, None) == q.QLORA_ERR_BAD_SHAPE
     fwd, bwd = lib.qlora_attention_fwd, lib.qlora_attention_bwd
     assert fwd(P, P, P, P, P, 0, 16, 2, 64, None, 0, None) == q.QLORA_OK          # empty: nothing to do
     assert fwd(P, P, P, P, P, 2, 0, 2, 64, None, 0, None) == q.QLORA_OK
@@ -182,6 +182,6 @@ def test_attention_shape_and_argument_errors(q):
     assert fwd(P, P, ctypes.c_void_p(24), P, P, 1, 16, 2, 64, P, big, None) == q.QLORA_ERR_MISALIGNED
     assert fwd(P, P, P, P, P, 1, 16, 2, 64, P, 64, None) == q.QLORA_ERR_WORKSPACE
     assert fwd(P, P, P, P, P, 1, 16, 2, 64, None, big, None) == q.QLORA_ERR_WORKSPACE
-    assert bwd(P, P, P, P, P, P, P, P, None, 1, 16, 2, 64, P, big, None) == q.QLORA_ERR_NULL_ARG
-    assert bwd(P, P, P, P, P, P, P, P, P, 1, 16, 2, 64, P, 64, None) == q.QLORA_ERR_WORKSPACE
+    assert bwd(P, P, P, P, P, P, P, None, 1, 16, 2, 64, P, big, None) == q.QLORA_ERR_NULL_ARG
+    assert bwd(P, P, P, P, P, P, P, P, 1, 16, 2, 64, P, 64, None) == q.QLORA_ERR_WORKSPACE
     assert "head_dim" in (fwd(P, P, P, P, P, 1, 16, 2, 60, P, big, None) and q.qlora_last_error())

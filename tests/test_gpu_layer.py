@@ -1,0 +1,61 @@
+"""GPU parity of the whole decoder layer (bit_nf4_quantized_qlora_amd.layer:
+seven adapted NF4 projections, causal attention, SwiGLU, two residuals,
+backward with the activations recomputed from X) against the float64 layer
+oracle (oracle/layer.py) taking bf16 roundings at the same tensors as the
+library.  Bar: the layers' tolerance (relative Frobenius <= 5e-3, max
+<= 2e-2 of the largest value) on Y, dX and all fourteen adapter gradients.
+q and k weights are drawn 10x larger than the rest so that the attention
+is sharply peaked rather than near-uniform."""
+import numpy as np
+import pytest
+import torch
+
+from bit_nf4_quantized_qlora_amd import inputs as I
+from gpu_helpers import assert_close, dev_bf16, gpu_quantize, host_bf16, note
+from oracle import layer as olayer
+from oracle import nf4_dq
+from oracle_views import OracleWeight
+
+pytestmark = pytest.mark.gpu
+f64 = nf4_dq.bf16_bits_to_f64
+rnd = lambda x: f64(nf4_dq.bf16_rne_bits(np.asarray(x, np.float32)))
+
+
+@pytest.fixture(scope="module")
+def q():
+    from bit_nf4_quantized_qlora_amd import qlora
+    return qlora
+
+
+@pytest.mark.parametrize("batch,seq,heads,d,inter", [(2, 48, 2, 64, 192), (1, 130, 4, 32, 256)])
+def test_decoder_layer_matches_oracle(q, batch, seq, heads, d, inter):
+    from bit_nf4_quantized_qlora_amd.layer import DecoderLayer, PROJ
+    r, alpha = 8, 16.0
+    hidden, M = heads * d, batch * seq
+    note(f"[layer] batch={batch} seq={seq} heads={heads} d={d} inter={inter} r={r}")
+    shapes = {"q": (hidden, hidden), "k": (hidden, hidden), "v": (hidden, hidden), "o": (hidden, hidden),
+              "gate": (inter, hidden), "up": (inter, hidden), "down": (hidden, inter)}
+    Ws = {nm: I.custom_weight(n, k, 200 + i, scale=0.2 if nm in ("q", "k") else 0.05)
+          for i, (nm, (n, k)) in enumerate(shapes.items())}
+    ad = {nm: (I.custom_bf16((r, k), 300 + i, 1, bound=0.05), I.custom_bf16((n, r), 300 + i, 2, bound=0.05))
+          for i, (nm, (n, k)) in enumerate(shapes.items())}
+    X, dY = I.custom_bf16((M, hidden), 400 + seq, 1), I.custom_bf16((M, hidden), 400 + seq, 2)
+
+    lay = DecoderLayer({nm: gpu_quantize(q, W) for nm, W in Ws.items()},
+                       {nm: (dev_bf16(A), dev_bf16(B)) for nm, (A, B) in ad.items()}, r, alpha, batch, seq, heads, d)
+    Xd, dYd = dev_bf16(X), dev_bf16(dY)
+    Y, dX, Y2 = (torch.empty(M, hidden, dtype=torch.bfloat16, device="cuda") for _ in range(3))
+    lay.fwd(Xd, Y)
+    lay.bwd(Xd, dYd, dX, Y2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16), Y2.view(torch.int16)), "recomputed forward differs"
+
+    params = {nm: (f64(OracleWeight(W).row_what_bits(np.arange(W.shape[0]))), f64(ad[nm][0]), f64(ad[nm][1]))
+              for nm, W in Ws.items()}
+    rY, _ = olayer.fwd(f64(X), params, alpha, batch, seq, heads, d, rnd)
+    rdX, rg = olayer.bwd(f64(X), f64(dY), params, alpha, batch, seq, heads, d, rnd)
+    assert_close(f64(host_bf16(Y)), rY, "Y")
+    assert_close(f64(host_bf16(dX)), rdX, "dX")
+    for nm in PROJ:
+        assert_close(f64(host_bf16(lay.dA[nm])), rg[nm][0], f"dA_{nm}")
+        assert_close(f64(host_bf16(lay.dB[nm])), rg[nm][1], f"dB_{nm}")
