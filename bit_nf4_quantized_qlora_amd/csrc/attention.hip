@@ -75,14 +75,26 @@ __device__ __forceinline__ u32x4_t load8(const uint16_t *base, int64_t ld, int i
   return v;
 }
 
-// The staged word into the [row][contraction] LDS tile.
+// The staged word into the [row][contraction] LDS tile.  A transposed word
+// (8 rows i..i+7 of one contraction index) goes out as 8 two-byte stores.
+// Without care, the 8 lanes of a store instruction that hold i = 0, 8, .., 56
+// would hit rows 8 apart, 160 words apart: two banks.  So lane m = i / 8
+// rotates its elements by m and stores element (j + m) mod 8 at step j: the
+// rows an instruction touches then differ in their low three bits and fall
+// on eight distinct banks.
 template <bool KC>
 __device__ __forceinline__ void store8(uint16_t *tile, int i, int k, const u32x4_t &v) {
   if (KC) {
     *reinterpret_cast<u32x4_t *>(tile + i * kLd + k) = v;
   } else {
+    const int m = (i >> 3) & 7;
+    u32x4_t r = v;
+    if (m & 2) r = u32x4_t{r[1], r[2], r[3], r[0]};  // whole pairs: by 2 (m & 2) and 4 (m & 4) elements
+    if (m & 4) r = u32x4_t{r[2], r[3], r[0], r[1]};
+    if (m & 1) r = u32x4_t{(r[0] >> 16) | (r[1] << 16), (r[1] >> 16) | (r[2] << 16), (r[2] >> 16) | (r[3] << 16),
+                           (r[3] >> 16) | (r[0] << 16)};
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tile[(i + j) * kLd + k] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+    for (int j = 0; j < 8; ++j) tile[(i + ((j + m) & 7)) * kLd + k] = (uint16_t)(r[j >> 1] >> (16 * (j & 1)));
   }
 }
 
@@ -165,8 +177,41 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Columns a row's products read: up to the end of its diagonal tile.
 __device__ __forceinline__ int row_span(int q, int seq) { return min(seq, (q / kT + 1) * kT); }
 
+// Row chunks: lane l holds columns c0 + 4l .. +3 and c0 + 256 + 4l .. +3, so
+// a wave covers 512 columns with two 16-byte loads per lane, both issued
+// before either is used.  A group starting at or past `lim` reads nothing;
+// elements at or past `lim` inside a group are replaced by `fill` (a select:
+// the memory there may hold anything).  Row starts are 32-byte aligned
+// (ldp is a multiple of 8) and a group starting below lim <= ldp ends inside
+// the row, so every load stays in the workspace.
+constexpr int kChunk = 512;
+__device__ __forceinline__ void load_chunk(const float *row, int c0, int lane, int lim, float fill, float (&x)[8]) {
+  f32x4_t v[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = c0 + 256 * h + 4 * lane;
+    v[h] = c < lim ? *reinterpret_cast<const f32x4_t *>(row + c) : f32x4_t{fill, fill, fill, fill};
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * h + e] = c0 + 256 * h + 4 * lane + e < lim ? v[h][e] : fill;
+}
+
+// Four bf16 of a chunk group to row[c..c+3], cut at `span`.
+__device__ __forceinline__ void store4(uint16_t *row, int c, int span, const float (&y)[8], int h) {
+  if (c >= span) return;
+  if (c + 4 <= span) {
+    u32x2_t w = {bf16x2_rne(y[4 * h], y[4 * h + 1]), bf16x2_rne(y[4 * h + 2], y[4 * h + 3])};
+    *reinterpret_cast<u32x2_t *>(row + c) = w;
+  } else {
+    for (int e = 0; c + e < span; ++e) row[c + e] = f32_to_bf16_bits(y[4 * h + e]);
+  }
+}
+
 // Forward softmax of the (already scaled) scores, one wave per row
-// r = (sequence * heads + head) * seq + query.
+// r = (sequence * heads + head) * seq + query: a running maximum and sum
+// over 512-column chunks, then P = exp(S - max) / sum.
 __global__ __launch_bounds__(256) void k_attn_softmax(const float *__restrict__ S, uint16_t *__restrict__ P,
                                                       float *__restrict__ lse, int64_t rows, int seq, int64_t ldp) {
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -175,14 +220,30 @@ __global__ __launch_bounds__(256) void k_attn_softmax(const float *__restrict__ 
   const int q = (int)(r % seq), n = q + 1;
   const float *s = S + r * ldp;
   uint16_t *p = P + r * ldp;
-  float m = -INFINITY;
-  for (int j = lane; j < n; j += 64) m = fmaxf(m, s[j]);
-  m = wave_max(m);
-  float zsum = 0.f;
-  for (int j = lane; j < n; j += 64) zsum += expf(s[j] - m);
+  float m = -INFINITY, zsum = 0.f;
+  for (int c0 = 0; c0 < n; c0 += kChunk) {
+    float x[8];
+    load_chunk(s, c0, lane, n, -INFINITY, x);
+    float cm = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) cm = fmaxf(cm, x[e]);
+    const float mn = fmaxf(m, wave_max(cm));  // finite: every chunk holds a column < n
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part += expf(x[e] - mn);
+    zsum = zsum * expf(m - mn) + part;
+    m = mn;
+  }
   zsum = wave_sum(zsum);
   const int span = row_span(q, seq);
-  for (int j = lane; j < span; j += 64) p[j] = j < n ? f32_to_bf16_bits(expf(s[j] - m) / zsum) : uint16_t(0);
+  for (int c0 = 0; c0 < span; c0 += kChunk) {
+    float x[8], y[8];
+    load_chunk(s, c0, lane, n, -INFINITY, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = expf(x[e] - m) / zsum;  // exp(-inf) = 0 past the diagonal
+#pragma unroll
+    for (int h = 0; h < 2; ++h) store4(p, c0 + 256 * h + 4 * lane, span, y, h);
+  }
   if (lane == 0) lse[r] = m + logf(zsum);
 }
 
@@ -202,19 +263,206 @@ __global__ __launch_bounds__(256) void k_attn_bwd_rows(const float *__restrict__
   const float L = lse[r];
   const float *s = S + r * ldp, *dp = dP + r * ldp;
   float D = 0.f;
-  for (int j = lane; j < n; j += 64) D += expf(s[j] - L) * dp[j];
+  for (int c0 = 0; c0 < n; c0 += kChunk) {
+    float x[8], g[8];
+    load_chunk(s, c0, lane, n, -INFINITY, x);
+    load_chunk(dp, c0, lane, n, 0.f, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) D += expf(x[e] - L) * g[e];
+  }
   D = wave_sum(D);
   uint16_t *p = P + r * ldp, *ds = dS + r * ldp;
   const int span = row_span(q, seq);
-  for (int j = lane; j < span; j += 64) {
-    uint16_t pj = 0, dsj = 0;
-    if (j < n) {
-      const float e = expf(s[j] - L);
-      pj = f32_to_bf16_bits(e);
-      dsj = f32_to_bf16_bits(e * (dp[j] - D));
+  for (int c0 = 0; c0 < span; c0 += kChunk) {
+    float x[8], g[8], pe[8], de[8];
+    load_chunk(s, c0, lane, n, -INFINITY, x);
+    load_chunk(dp, c0, lane, n, 0.f, g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pe[e] = expf(x[e] - L);  // 0 past the diagonal
+      de[e] = pe[e] * (g[e] - D);
     }
-    p[j] = pj;
-    ds[j] = dsj;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      store4(p, c0 + 256 * h + 4 * lane, span, pe, h);
+      store4(ds, c0 + 256 * h + 4 * lane, span, de, h);
+    }
+  }
+}
+
+// V^T for the fused forward: Vt[sequence][head][dim][key] (rows of ldp keys,
+// zeros past the sequence), so the fused kernel stages V^T tiles with
+// 16-byte row copies; transposing inside it took 2-byte LDS stores that
+// fell on two banks.  One workgroup per (64 keys, head, sequence): coalesced
+// 16-byte row loads into LDS, 16-byte stores of 8 keys of one dim.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_vt(const uint16_t *__restrict__ Vg, uint16_t *__restrict__ Vt, int seq,
+                                                 int heads, int64_t ldp) {
+  constexpr int kLd = D + 8;
+  __shared__ __align__(16) uint16_t sv[kT * kLd];
+  const int k0 = blockIdx.x * kT;
+  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const int64_t ld = (int64_t)heads * D;
+  const int t = threadIdx.x;
+  for (int i = t; i < kT * (D / 8); i += 256) {
+    const int key = k0 + i / (D / 8), col = 8 * (i % (D / 8));
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (key < seq) v = *reinterpret_cast<const u32x4_t *>(Vg + (b * seq + key) * ld + h * D + col);
+    *reinterpret_cast<u32x4_t *>(sv + (i / (D / 8)) * kLd + col) = v;
+  }
+  __syncthreads();
+  uint16_t *out = Vt + (b * heads + h) * D * ldp;
+  for (int i = t; i < D * (kT / 8); i += 256) {
+    const int dim = i / (kT / 8), kk = 8 * (i % (kT / 8));
+    if (k0 + kk >= ldp) continue;
+    u32x4_t v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = (uint32_t)sv[(kk + 2 * j) * kLd + dim] | ((uint32_t)sv[(kk + 2 * j + 1) * kLd + dim] << 16);
+    *reinterpret_cast<u32x4_t *>(out + dim * ldp + k0 + kk) = v;
+  }
+}
+
+// Fused forward for head dims 32, 64, 128: one workgroup per (sequence,
+// head, 64-query tile), wave w on queries q0 + 16w .. +15; no score matrix
+// in memory.  Per 64-key block (causal: blocks up to the diagonal one):
+//   S^T = K Q^T on MFMA (A = K rows from LDS, B = Q from registers), so each
+//   lane's accumulators all belong to one query (its column l & 15): the
+//   online softmax (running max m, lane-partial sum l, rescale of the
+//   output) needs only a max over the lane's 16 values and lanes l ^ 16, 32;
+//   O^T += V^T P^T on MFMA with P rounded to bf16: the MFMA contraction
+//   slots 8g .. 8g+7 of lane group g = l >> 4 are assigned to the keys that
+//   lane already holds (4g .. 4g+3 of two 16-key tiles), so P goes from
+//   accumulator to operand without moving between lanes, and V^T is read
+//   from a transposed LDS copy at the same keys.
+// V^T comes from the copy k_attn_vt writes.  The next block's K and V^T
+// are loaded into registers while this block computes.  Keys past the
+// sequence are zero in LDS and masked to -inf.
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_fwd_fused(const uint16_t *__restrict__ Qg, const uint16_t *__restrict__ Kg,
+                                                        const uint16_t *__restrict__ Vt, uint16_t *__restrict__ Og,
+                                                        float *__restrict__ lse, int seq, int heads, int64_t ldp,
+                                                        float scale) {
+  constexpr int kLdK = D + 8, kLdV = kT + 8;   // LDS row strides (elements)
+  constexpr int kKL = D / 32;                  // 16-byte K loads per thread per block (64 x D / 8 / 256)
+  __shared__ __align__(16) uint16_t sK[kT * kLdK];
+  __shared__ __align__(16) uint16_t sVt[D * kLdV];
+  const int ntq = (seq + kT - 1) / kT;
+  const int tq = ntq - 1 - (int)blockIdx.x;   // the longest query tiles start first
+  const int q0 = tq * kT;
+  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const int64_t ld = (int64_t)heads * D;
+  const int64_t base = b * seq * ld + h * D;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4, c = lane & 15;
+  const int qi = q0 + 16 * w + c;             // this lane's query
+
+  u32x4_t qf[D / 32];                          // B operand of K Q^T: Q[qi][32 ks + 8 g ..]
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    if (qi < seq) qf[ks] = *reinterpret_cast<const u32x4_t *>(Qg + base + qi * ld + 32 * ks + 8 * g);
+  }
+  f32x4_t acc_o[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  // staging, kKL 16-byte pieces per thread and operand: K rows (key
+  // t / (D/8) + 256/(D/8) i, 8 dims at 8 (t % (D/8))) and V^T rows (dim
+  // t / 8 + 32 i, 8 keys at 8 (t % 8)) from the transposed copy
+  constexpr int kPer = D / 8;                  // 16-byte pieces per K row
+  constexpr int kRowsPer = 256 / kPer;         // K rows one pass of the workgroup covers
+  const uint16_t *vt = Vt + (b * heads + h) * D * ldp;
+  u32x4_t rk[kKL], rv[kKL];
+  auto load_block = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < kKL; ++i) {
+      const int key = k0 + t / kPer + kRowsPer * i, col = 8 * (t % kPer);
+      rk[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (key < seq) rk[i] = *reinterpret_cast<const u32x4_t *>(Kg + base + key * ld + col);
+      const int dim = t / 8 + 32 * i, kk = k0 + 8 * (t % 8);
+      rv[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (kk < ldp) rv[i] = *reinterpret_cast<const u32x4_t *>(vt + dim * ldp + kk);
+    }
+  };
+  const int nblk = tq + 1;
+  load_block(0);
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int k0 = kb * kT;
+    __syncthreads();  // the previous block's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < kKL; ++i) {
+      const int kr = t / kPer + kRowsPer * i, col = 8 * (t % kPer);
+      *reinterpret_cast<u32x4_t *>(sK + kr * kLdK + col) = rk[i];
+      *reinterpret_cast<u32x4_t *>(sVt + (t / 8 + 32 * i) * kLdV + 8 * (t % 8)) = rv[i];
+    }
+    __syncthreads();
+    if (kb + 1 < nblk) load_block(k0 + kT);
+
+    // S^T for 4 key tiles of 16
+    f32x4_t st[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) st[kt] = mfma16(lds_frag(sK, kLdK, 16 * kt, 32 * ks, lane), qf[ks], st[kt]);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key = k0 + 16 * kt + 4 * g + v;
+        const float x = (key <= qi && key < seq) ? st[kt][v] * scale : -INFINITY;
+        st[kt][v] = x;
+        bm = fmaxf(bm, x);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float mn = fmaxf(m, bm);  // finite: key 0 .. is in block 0 and key <= qi there
+    const float corr = expf(m - mn);
+    m = mn;
+    l *= corr;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) acc_o[i] *= corr;
+    uint32_t pw[4][2];  // P as bf16 pairs: tile kt, keys 4g + (0,1) and (2,3)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      float e[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        e[v] = expf(st[kt][v] - mn);
+        l += e[v];
+      }
+      pw[kt][0] = bf16x2_rne(e[0], e[1]);
+      pw[kt][1] = bf16x2_rne(e[2], e[3]);
+    }
+    // O^T += V^T P^T, two 32-key contraction steps
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t pb = {pw[2 * ks][0], pw[2 * ks][1], pw[2 * ks + 1][0], pw[2 * ks + 1][1]};
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const uint16_t *vr = sVt + (16 * dt + c) * kLdV + 32 * ks + 4 * g;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vr);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vr + 16);
+        const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+        acc_o[dt] = mfma16(va, pb, acc_o[dt]);
+      }
+    }
+  }
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (qi < seq) {
+    const float inv = 1.0f / l;
+    uint16_t *orow = Og + base + qi * ld;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x2_t o = {bf16x2_rne(acc_o[dt][0] * inv, acc_o[dt][1] * inv),
+                         bf16x2_rne(acc_o[dt][2] * inv, acc_o[dt][3] * inv)};
+      *reinterpret_cast<u32x2_t *>(orow + 16 * dt + 4 * g) = o;
+    }
+    if (g == 0) lse[(b * heads + h) * seq + qi] = m + logf(l);
   }
 }
 
@@ -252,7 +500,7 @@ void gemm(const char *name, const Dims &x, Opnd a, Opnd b, void *c, bool c_score
 
 struct Ws {
   float *S, *dP;
-  uint16_t *P, *dS;
+  uint16_t *P, *dS, *Vt;  // Vt: [batch][heads][d][ldp], the fused forward's V^T
 };
 
 Ws carve(void *ws, const Dims &x) {
@@ -266,14 +514,17 @@ Ws carve(void *ws, const Dims &x) {
   w.P = reinterpret_cast<uint16_t *>(p);
   p += align_up(e * 2, 256);
   w.dS = reinterpret_cast<uint16_t *>(p);
+  p += align_up(e * 2, 256);
+  w.Vt = reinterpret_cast<uint16_t *>(p);
   return w;
 }
 
 }  // namespace
 
-size_t attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads) {
-  const size_t e = (size_t)(batch * heads * seq * align_up((size_t)seq, 8));
-  return 2 * align_up(e * 4, 256) + 2 * align_up(e * 2, 256);
+size_t attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t d) {
+  const size_t ldp = align_up((size_t)seq, 8);
+  const size_t e = (size_t)(batch * heads * seq) * ldp;
+  return 2 * align_up(e * 4, 256) + 2 * align_up(e * 2, 256) + align_up((size_t)(batch * heads * d) * ldp * 2, 256);
 }
 
 hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O, float *lse,
@@ -282,6 +533,21 @@ hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint
   const Ws w = carve(ws, x);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   const int L = (int)seq, D = (int)d;
+  if (d == 32 || d == 64 || d == 128) {
+    const dim3 grid((unsigned)ceil_div(seq, kT), (unsigned)heads, (unsigned)batch);
+    const int H = (int)heads;
+    if (d == 32) {
+      QLORA_LAUNCH("k_attn_vt", k_attn_vt<32>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<32>, grid, dim3(256), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
+    } else if (d == 64) {
+      QLORA_LAUNCH("k_attn_vt", k_attn_vt<64>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<64>, grid, dim3(256), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
+    } else {
+      QLORA_LAUNCH("k_attn_vt", k_attn_vt<128>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<128>, grid, dim3(256), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
+    }
+    return hipGetLastError();
+  }
   gemm<true, true, false>("k_attn_scores", x, qkv(Q, x), qkv(K, x), w.S, true, L, L, D, scale, 1, 0, s);
   const int64_t rows = batch * heads * seq;
   QLORA_LAUNCH("k_attn_softmax", k_attn_softmax, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, w.S, w.P, lse,

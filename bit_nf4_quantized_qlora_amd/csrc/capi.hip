@@ -222,7 +222,7 @@ size_t qlora_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads
       head_dim > 1024 || head_dim % 8 != 0 || batch * seq > kMaxElems / (heads * head_dim) ||
       batch * heads > kMaxElems / (seq * seq + 1))
     return 0;
-  return attention_workspace_bytes(batch, seq, heads);
+  return attention_workspace_bytes(batch, seq, heads, head_dim);
 }
 
 int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
@@ -235,7 +235,7 @@ int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   if (int e = check_tensor(v, "v")) return e;
   if (int e = check_tensor(o, "o")) return e;
   if (int e = check_tensor(lse, "lse")) return e;
-  if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads))) return e;
+  if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads, head_dim))) return e;
   hipError_t e = launch_attention_fwd(q, k, v, o, lse, batch, seq, heads, head_dim, ws, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "qlora_attention_fwd");
   return QLORA_OK;
@@ -251,7 +251,7 @@ int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   const char *names[] = {"q", "k", "v", "d_o", "lse", "dq", "dk", "dv"};
   for (int i = 0; i < 8; ++i)
     if (int e = check_tensor(ptrs[i], names[i])) return e;
-  if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads))) return e;
+  if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads, head_dim))) return e;
   hipError_t e = launch_attention_bwd(q, k, v, d_o, lse, dq, dk, dv, batch, seq, heads, head_dim, ws,
                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "qlora_attention_bwd");

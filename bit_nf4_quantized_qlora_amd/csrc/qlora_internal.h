@@ -38,7 +38,7 @@ hipError_t launch_dequant(const Nf4View &w, uint16_t *out, hipStream_t s);
 // swiglu.hip: op 0 y0 = bf16(silu(x0) x1); op 1 (y0, y1) = (dg, du) for
 // g = x0, u = x1, dh = x2; op 2 y0 = bf16(x0 + x1).
 // Causal attention core (attention.hip).
-size_t attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads);
+size_t attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t d);
 hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O, float *lse,
                                 int64_t batch, int64_t seq, int64_t heads, int64_t d, void *ws, hipStream_t s);
 hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *dO, const float *lse, uint16_t *dQ, uint16_t *dK, uint16_t *dV,

@@ -228,8 +228,9 @@ int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t 
  * Shapes: head_dim a multiple of 8 in [8, 1024], heads in [1, 65535],
  * batch in [0, 65535], seq in [0, 65536]; otherwise QLORA_ERR_BAD_SHAPE.
  * batch == 0 or seq == 0 does nothing.  The workspace (device, 16-byte
- * aligned) holds the float32 scores and their gradient and the bf16 P and
- * dS, 12 * batch * heads * seq * roundup(seq, 8) bytes plus alignment:
+ * aligned) holds the float32 scores and their gradient, the bf16 P and dS
+ * and a transposed copy of v: (12 * seq + 2 * head_dim) * batch * heads *
+ * roundup(seq, 8) bytes plus alignment:
  * qlora_attention_workspace_bytes (0 for shapes the calls reject).
  */
 size_t qlora_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t head_dim);
