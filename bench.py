@@ -62,6 +62,9 @@ def parse():
                    help="also run a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--small-m-only", action="store_true",
                    help="print only rows.small_m (the small-M forward), as one JSON line")
+    p.add_argument("--layer-only", action="store_true",
+                   help="print only rows.decoder_layer (the 7B decoder layer and its attention core), as one JSON "
+                        "line; use with --no-extras")
     p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="write profiles/traffic_counters.json from two rocprofv3 --pmc output folders "
                         "(FETCH_SIZE, WRITE_SIZE) of a run with --calib-copy-mib, then exit")
@@ -217,6 +220,10 @@ def main():
     ws_bytes = max(q.qlora_linear_workspace_bytes(M, t["L"].n, t["L"].k, r) for t in layers)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     torch.cuda.empty_cache()
+    if args.layer_only:
+        print(json.dumps({"decoder_layer": layer_rows(q, I, layers, dev, ev, M, r, alpha, wl.adapter_bound)}),
+              flush=True)
+        return
 
     def fwd_pass():
         for t in layers:
