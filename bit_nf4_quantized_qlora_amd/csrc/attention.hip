@@ -20,9 +20,9 @@
 // Products: one batched MFMA kernel, 64 x 64 output tiles, 4 waves of 2 x 2
 // 16x16x32 bf16 MFMAs, a 32-deep contraction step staged through LDS with
 // the next step's operands loaded into registers meanwhile.  Each operand is
-// read along whichever axis is contiguous in memory (template flags); LDS
-// always holds [row][contraction], so one fragment read is 16 contiguous
-// bytes.  Causality prunes work: score tiles wholly above the diagonal are
+// read along whichever axis is contiguous in memory (template flags) and
+// staged as it lies; fragments of row-contiguous operands come from
+// transposing LDS reads.  Causality prunes work: score tiles wholly above the diagonal are
 // skipped, and the products with P or dS stop (or start) their contraction
 // at the tile's diagonal.
 //
@@ -51,9 +51,9 @@ struct Opnd {
 struct GemmArgs {
   Opnd a, b;
   void *c;
+  float alpha;
   int64_t ldc, csb, csh;
   int M, N, K, tiles_n;
-  float alpha;
   int mask;    // 1: skip tiles whose every column index exceeds every row index
   int krange;  // 0: whole contraction; 1: k < m0 + 64 (k <= row); 2: k >= m0 (k >= row)
 };
@@ -75,27 +75,35 @@ __device__ __forceinline__ u32x4_t load8(const uint16_t *base, int64_t ld, int i
   return v;
 }
 
-// The staged word into the [row][contraction] LDS tile.  A transposed word
-// (8 rows i..i+7 of one contraction index) goes out as 8 two-byte stores.
-// Without care, the 8 lanes of a store instruction that hold i = 0, 8, .., 56
-// would hit rows 8 apart, 160 words apart: two banks.  So lane m = i / 8
-// rotates its elements by m and stores element (j + m) mod 8 at step j: the
-// rows an instruction touches then differ in their low three bits and fall
-// on eight distinct banks.
+// LDS tiles of one contraction step.  An operand with its contraction
+// contiguous in memory (KC) is staged [row][contraction] (64 x kLd) and a
+// fragment is one 16-byte read.  An operand with its rows contiguous is
+// staged as it lies, [contraction][row] (32 x kLdT), by 16-byte copies, and
+// a fragment is two ds_read_b64_tr_b16: in a 16-lane group, lane i receives
+// element i & 3 of the 8 bytes addressed by lanes 4q + i/4 (q = 0..3), so
+// lanes addressing contraction rows 8g + 4h + q, columns row0 + 4(j & 3)
+// hand lane i four consecutive contraction elements of row row0 + i.
+// (Writing such operands transposed into LDS took eight 2-byte stores per
+// thread and step.)  kLdT = 72: a 144-byte row stride, at most two lanes of
+// a half-wave per bank for these reads.
+constexpr int kLdT = kT + 8;
+static_assert(kKs * kLdT <= kT * kLd, "both staging layouts fit one buffer");
+
 template <bool KC>
 __device__ __forceinline__ void store8(uint16_t *tile, int i, int k, const u32x4_t &v) {
-  if (KC) {
-    *reinterpret_cast<u32x4_t *>(tile + i * kLd + k) = v;
-  } else {
-    const int m = (i >> 3) & 7;
-    u32x4_t r = v;
-    if (m & 2) r = u32x4_t{r[1], r[2], r[3], r[0]};  // whole pairs: by 2 (m & 2) and 4 (m & 4) elements
-    if (m & 4) r = u32x4_t{r[2], r[3], r[0], r[1]};
-    if (m & 1) r = u32x4_t{(r[0] >> 16) | (r[1] << 16), (r[1] >> 16) | (r[2] << 16), (r[2] >> 16) | (r[3] << 16),
-                           (r[3] >> 16) | (r[0] << 16)};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[(i + ((j + m) & 7)) * kLd + k] = (uint16_t)(r[j >> 1] >> (16 * (j & 1)));
-  }
+  *reinterpret_cast<u32x4_t *>(tile + (KC ? i * kLd + k : k * kLdT + i)) = v;
+}
+
+template <bool KC>
+__device__ __forceinline__ u32x4_t frag(const uint16_t *tile, int row0, int lane) {
+  if (KC) return lds_frag(tile, kLd, row0, 0, lane);
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const int j = lane & 15, g = lane >> 4;
+  const uint16_t *p = tile + (8 * g + (j >> 2)) * kLdT + row0 + 4 * (j & 3);
+  const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)p);
+  const s16x4_t h1 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(p + 4 * kLdT));
+  return __builtin_bit_cast(u32x4_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Thread t's staging coordinates in a 64 x 32 tile: 4 threads x 8 contraction
@@ -146,7 +154,16 @@ __global__ __launch_bounds__(256) void k_attn_gemm(GemmArgs g) {
       va = load8<AKC>(A, g.a.ld, m0 + ia, k0 + kKs + ka, g.M, ke);
       vb = load8<BKC>(B, g.b.ld, n0 + ib, k0 + kKs + kbb, g.N, ke);
     }
-    mma_step<2, 2>(acc, sA, sB, kLd, wm, wn, 0, lane);
+    u32x4_t fa[2], fb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      fa[u] = frag<AKC>(sA, wm + 16 * u, lane);
+      fb[u] = frag<BKC>(sB, wn + 16 * u, lane);
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = mfma16(fa[ti], fb[tj], acc[ti][tj]);
   }
 
   const int64_t coff = z * g.csb + y * g.csh;
@@ -484,6 +501,7 @@ void gemm(const char *name, const Dims &x, Opnd a, Opnd b, void *c, bool c_score
   g.a = a;
   g.b = b;
   g.c = c;
+  g.alpha = alpha;
   g.ldc = c_scores ? x.ldp : x.heads * x.d;
   g.csb = c_scores ? x.heads * x.seq * x.ldp : x.seq * x.heads * x.d;
   g.csh = c_scores ? x.seq * x.ldp : x.d;
@@ -491,7 +509,6 @@ void gemm(const char *name, const Dims &x, Opnd a, Opnd b, void *c, bool c_score
   g.N = N;
   g.K = K;
   g.tiles_n = (int)ceil_div(N, kT);
-  g.alpha = alpha;
   g.mask = mask;
   g.krange = krange;
   const dim3 grid((unsigned)(ceil_div(M, kT) * g.tiles_n), (unsigned)x.heads, (unsigned)x.batch);
@@ -562,6 +579,7 @@ hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint
   const Ws w = carve(ws, x);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   const int L = (int)seq, D = (int)d;
+  // (one launch computing both products over the same tiles was slower: 189 against 81 + 98 us)
   gemm<true, true, false>("k_attn_scores", x, qkv(Q, x), qkv(K, x), w.S, true, L, L, D, scale, 1, 0, s);
   gemm<true, true, false>("k_attn_dp", x, qkv(dO, x), qkv(V, x), w.dP, true, L, L, D, 1.0f, 1, 0, s);
   const int64_t rows = batch * heads * seq;
