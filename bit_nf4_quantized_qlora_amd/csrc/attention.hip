@@ -279,8 +279,15 @@ __global__ __launch_bounds__(256) void k_attn_bwd_rows(const float *__restrict__
   const int q = (int)(r % seq), n = q + 1;
   const float L = lse[r];
   const float *s = S + r * ldp, *dp = dP + r * ldp;
+  // the first chunk stays in registers for the second pass (rows up to 512
+  // columns are read once)
+  float x0[8], g0[8];
+  load_chunk(s, 0, lane, n, -INFINITY, x0);
+  load_chunk(dp, 0, lane, n, 0.f, g0);
   float D = 0.f;
-  for (int c0 = 0; c0 < n; c0 += kChunk) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) D += expf(x0[e] - L) * g0[e];
+  for (int c0 = kChunk; c0 < n; c0 += kChunk) {
     float x[8], g[8];
     load_chunk(s, c0, lane, n, -INFINITY, x);
     load_chunk(dp, c0, lane, n, 0.f, g);
@@ -292,8 +299,16 @@ __global__ __launch_bounds__(256) void k_attn_bwd_rows(const float *__restrict__
   const int span = row_span(q, seq);
   for (int c0 = 0; c0 < span; c0 += kChunk) {
     float x[8], g[8], pe[8], de[8];
-    load_chunk(s, c0, lane, n, -INFINITY, x);
-    load_chunk(dp, c0, lane, n, 0.f, g);
+    if (c0 == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = x0[e];
+        g[e] = g0[e];
+      }
+    } else {
+      load_chunk(s, c0, lane, n, -INFINITY, x);
+      load_chunk(dp, c0, lane, n, 0.f, g);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       pe[e] = expf(x[e] - L);  // 0 past the diagonal

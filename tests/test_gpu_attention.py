@@ -7,8 +7,10 @@ lse within 1e-5 relative + 1e-5 absolute (float32 sums of exponentials,
 no bf16 rounding on the way).  The GPU rounds P and dS to bf16 before the
 products that take them (2^-9 relative per element, independent in sign),
 which the Frobenius bar holds with room.  Shapes span several 64-wide
-tiles, ragged sequence tails, one-token sequences, head dims 64 and 128,
-and the LLaMA-7B layer's 32 heads of 128 on 512-token sequences."""
+tiles, ragged sequence tails, one-token sequences, rows longer than one
+512-column chunk of the row kernels (seq 600, 700), head dims 8 (the
+non-fused forward), 64 and 128, and the LLaMA-7B layer's 32 heads of 128
+on 512-token sequences."""
 import numpy as np
 import pytest
 import torch
@@ -48,7 +50,7 @@ def _run(q, batch, seq, heads, d, seed):
 
 
 @pytest.mark.parametrize("batch,seq,heads,d", [(2, 77, 3, 64), (1, 130, 2, 128), (3, 1, 2, 64), (2, 200, 1, 8),
-                                               (1, 512, 4, 128)])
+                                               (1, 512, 4, 128), (1, 700, 2, 64), (1, 600, 1, 8)])
 def test_attention_matches_oracle(q, batch, seq, heads, d):
     note(f"[attention] batch={batch} seq={seq} heads={heads} d={d}")
     (Qb, Kb, Vb, dOb), (O, lse, dQ, dK, dV) = _run(q, batch, seq, heads, d, seed=seq + 7 * heads + d)
