@@ -355,9 +355,9 @@ __global__ __launch_bounds__(256) void k_attn_vt(const uint16_t *__restrict__ Vg
   }
 }
 
-// Fused forward for head dims 32, 64, 128: one workgroup per (sequence,
-// head, 64-query tile), wave w on queries q0 + 16w .. +15; no score matrix
-// in memory.  Per 64-key block (causal: blocks up to the diagonal one):
+// Fused forward for head dims 32, 64, 128: one workgroup of 8 waves per
+// (sequence, head, 128-query tile), wave w on queries q0 + 16w .. +15, so a
+// staged key block serves 128 queries; no score matrix in memory.  Per 64-key block (causal: blocks up to the diagonal one):
 //   S^T = K Q^T on MFMA (A = K rows from LDS, B = Q from registers), so each
 //   lane's accumulators all belong to one query (its column l & 15): the
 //   online softmax (running max m, lane-partial sum l, rescale of the
@@ -370,18 +370,20 @@ __global__ __launch_bounds__(256) void k_attn_vt(const uint16_t *__restrict__ Vg
 // V^T comes from the copy k_attn_vt writes.  The next block's K and V^T
 // are loaded into registers while this block computes.  Keys past the
 // sequence are zero in LDS and masked to -inf.
+constexpr int kQT = 128;  // queries per fused-forward workgroup
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_fwd_fused(const uint16_t *__restrict__ Qg, const uint16_t *__restrict__ Kg,
+__global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restrict__ Qg, const uint16_t *__restrict__ Kg,
                                                         const uint16_t *__restrict__ Vt, uint16_t *__restrict__ Og,
                                                         float *__restrict__ lse, int seq, int heads, int64_t ldp,
                                                         float scale) {
   constexpr int kLdK = D + 8, kLdV = kT + 8;   // LDS row strides (elements)
-  constexpr int kKL = D / 32;                  // 16-byte K loads per thread per block (64 x D / 8 / 256)
+  constexpr int kPieces = 8 * D;               // 16-byte pieces per staged block and operand (64 x D / 8)
+  constexpr int kKL = (kPieces + 511) / 512;   // per thread
   __shared__ __align__(16) uint16_t sK[kT * kLdK];
   __shared__ __align__(16) uint16_t sVt[D * kLdV];
-  const int ntq = (seq + kT - 1) / kT;
+  const int ntq = (seq + kQT - 1) / kQT;
   const int tq = ntq - 1 - (int)blockIdx.x;   // the longest query tiles start first
-  const int q0 = tq * kT;
+  const int q0 = tq * kQT;
   const int64_t h = blockIdx.y, b = blockIdx.z;
   const int64_t ld = (int64_t)heads * D;
   const int64_t base = b * seq * ld + h * D;
@@ -399,34 +401,36 @@ __global__ __launch_bounds__(256) void k_attn_fwd_fused(const uint16_t *__restri
   for (int i = 0; i < D / 16; ++i) acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
 
-  // staging, kKL 16-byte pieces per thread and operand: K rows (key
-  // t / (D/8) + 256/(D/8) i, 8 dims at 8 (t % (D/8))) and V^T rows (dim
-  // t / 8 + 32 i, 8 keys at 8 (t % 8)) from the transposed copy
-  constexpr int kPer = D / 8;                  // 16-byte pieces per K row
-  constexpr int kRowsPer = 256 / kPer;         // K rows one pass of the workgroup covers
+  // staging, kKL 16-byte pieces per thread and operand: piece e is K row
+  // e / (D/8), dims 8 (e % (D/8)) .. +7, and V^T row (dim) e / 8, keys
+  // 8 (e % 8) .. +7 of the transposed copy
   const uint16_t *vt = Vt + (b * heads + h) * D * ldp;
   u32x4_t rk[kKL], rv[kKL];
   auto load_block = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < kKL; ++i) {
-      const int key = k0 + t / kPer + kRowsPer * i, col = 8 * (t % kPer);
-      rk[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (key < seq) rk[i] = *reinterpret_cast<const u32x4_t *>(Kg + base + key * ld + col);
-      const int dim = t / 8 + 32 * i, kk = k0 + 8 * (t % 8);
-      rv[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (kk < ldp) rv[i] = *reinterpret_cast<const u32x4_t *>(vt + dim * ldp + kk);
+      const int e = t + 512 * i;
+      rk[i] = rv[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (e < kPieces) {
+        const int key = k0 + e / (D / 8), col = 8 * (e % (D / 8));
+        if (key < seq) rk[i] = *reinterpret_cast<const u32x4_t *>(Kg + base + key * ld + col);
+        const int dim = e / 8, kk = k0 + 8 * (e % 8);
+        if (kk < ldp) rv[i] = *reinterpret_cast<const u32x4_t *>(vt + dim * ldp + kk);
+      }
     }
   };
-  const int nblk = tq + 1;
+  const int nblk = min((seq + kT - 1) / kT, (q0 + kQT) / kT);  // key blocks up to the diagonal
   load_block(0);
   for (int kb = 0; kb < nblk; ++kb) {
     const int k0 = kb * kT;
     __syncthreads();  // the previous block's LDS reads are done
 #pragma unroll
     for (int i = 0; i < kKL; ++i) {
-      const int kr = t / kPer + kRowsPer * i, col = 8 * (t % kPer);
-      *reinterpret_cast<u32x4_t *>(sK + kr * kLdK + col) = rk[i];
-      *reinterpret_cast<u32x4_t *>(sVt + (t / 8 + 32 * i) * kLdV + 8 * (t % 8)) = rv[i];
+      const int e = t + 512 * i;
+      if (e < kPieces) {
+        *reinterpret_cast<u32x4_t *>(sK + (e / (D / 8)) * kLdK + 8 * (e % (D / 8))) = rk[i];
+        *reinterpret_cast<u32x4_t *>(sVt + (e / 8) * kLdV + 8 * (e % 8)) = rv[i];
+      }
     }
     __syncthreads();
     if (kb + 1 < nblk) load_block(k0 + kT);
@@ -451,7 +455,9 @@ __global__ __launch_bounds__(256) void k_attn_fwd_fused(const uint16_t *__restri
       }
     bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
     bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float mn = fmaxf(m, bm);  // finite: key 0 .. is in block 0 and key <= qi there
+    // finite: block 0 holds key 0 <= qi; a later block whose keys all lie
+    // past this wave's queries leaves m unchanged (corr = 1, e = 0)
+    const float mn = fmaxf(m, bm);
     const float corr = expf(m - mn);
     m = mn;
     l *= corr;
@@ -568,15 +574,16 @@ hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint
   if (d == 32 || d == 64 || d == 128) {
     const dim3 grid((unsigned)ceil_div(seq, kT), (unsigned)heads, (unsigned)batch);
     const int H = (int)heads;
+    const dim3 gq((unsigned)ceil_div(seq, kQT), (unsigned)heads, (unsigned)batch);
     if (d == 32) {
       QLORA_LAUNCH("k_attn_vt", k_attn_vt<32>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
-      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<32>, grid, dim3(256), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<32>, gq, dim3(512), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
     } else if (d == 64) {
       QLORA_LAUNCH("k_attn_vt", k_attn_vt<64>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
-      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<64>, grid, dim3(256), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<64>, gq, dim3(512), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
     } else {
       QLORA_LAUNCH("k_attn_vt", k_attn_vt<128>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
-      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<128>, grid, dim3(256), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<128>, gq, dim3(512), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
     }
     return hipGetLastError();
   }
