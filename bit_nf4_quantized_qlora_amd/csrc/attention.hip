@@ -40,8 +40,8 @@ namespace qlora {
 namespace {
 
 constexpr int kT = 64;          // output tile edge
-constexpr int kKs = 32;         // contraction per step
-constexpr int kLd = kKs + 8;    // LDS row stride in elements (80 B: rows start on staggered banks)
+constexpr int kKs = 64;         // contraction per step (two 32-deep MFMA sub-steps)
+constexpr int kLd = kKs + 8;    // LDS row stride in elements (144 B: a 16-lane fragment read is conflict-free)
 
 struct Opnd {
   const uint16_t *p;
@@ -95,23 +95,24 @@ __device__ __forceinline__ void store8(uint16_t *tile, int i, int k, const u32x4
 }
 
 template <bool KC>
-__device__ __forceinline__ u32x4_t frag(const uint16_t *tile, int row0, int lane) {
-  if (KC) return lds_frag(tile, kLd, row0, 0, lane);
+__device__ __forceinline__ u32x4_t frag(const uint16_t *tile, int row0, int kk0, int lane) {
+  if (KC) return lds_frag(tile, kLd, row0, kk0, lane);
   typedef short s16x4_t __attribute__((ext_vector_type(4)));
   const int j = lane & 15, g = lane >> 4;
-  const uint16_t *p = tile + (8 * g + (j >> 2)) * kLdT + row0 + 4 * (j & 3);
+  const uint16_t *p = tile + (kk0 + 8 * g + (j >> 2)) * kLdT + row0 + 4 * (j & 3);
   const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)p);
   const s16x4_t h1 =
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(p + 4 * kLdT));
   return __builtin_bit_cast(u32x4_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Thread t's staging coordinates in a 64 x 32 tile: 4 threads x 8 contraction
-// elements per row (KC), or 8 threads x 8 rows per contraction index.
+// Staging coordinates of 16-byte piece e (0..511) of a 64 x 64 tile: 8
+// pieces of 8 contraction elements per row (KC), or 8 pieces of 8 rows per
+// contraction index.
 template <bool KC>
-__device__ __forceinline__ void stage_coords(int t, int &i, int &k) {
-  i = KC ? t >> 2 : (t & 7) * 8;
-  k = KC ? (t & 3) * 8 : t >> 3;
+__device__ __forceinline__ void stage_coords(int e, int &i, int &k) {
+  i = KC ? e >> 3 : (e & 7) * 8;
+  k = KC ? (e & 7) * 8 : e >> 3;
 }
 
 // C[m][n] = alpha * sum_k A(m, k) B(n, k), one 64 x 64 tile per workgroup;
@@ -130,9 +131,12 @@ __global__ __launch_bounds__(256) void k_attn_gemm(GemmArgs g) {
   const int ke = g.krange == 1 ? min(g.K, m0 + kT) : g.K;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = (w >> 1) * 32, wn = (w & 1) * 32;
-  int ia, ka, ib, kbb;
-  stage_coords<AKC>(t, ia, ka);
-  stage_coords<BKC>(t, ib, kbb);
+  int ia[2], ka[2], ib[2], kbb[2];  // two pieces per thread and operand
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    stage_coords<AKC>(t + 256 * u, ia[u], ka[u]);
+    stage_coords<BKC>(t + 256 * u, ib[u], kbb[u]);
+  }
 
   f32x4_t acc[2][2];
 #pragma unroll
@@ -140,30 +144,43 @@ __global__ __launch_bounds__(256) void k_attn_gemm(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t va = {0u, 0u, 0u, 0u}, vb = va;
-  if (kb < ke) {
-    va = load8<AKC>(A, g.a.ld, m0 + ia, kb + ka, g.M, ke);
-    vb = load8<BKC>(B, g.b.ld, n0 + ib, kb + kbb, g.N, ke);
+  u32x4_t va[2], vb[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    va[u] = vb[u] = u32x4_t{0u, 0u, 0u, 0u};
+    if (kb < ke) {
+      va[u] = load8<AKC>(A, g.a.ld, m0 + ia[u], kb + ka[u], g.M, ke);
+      vb[u] = load8<BKC>(B, g.b.ld, n0 + ib[u], kb + kbb[u], g.N, ke);
+    }
   }
   for (int k0 = kb; k0 < ke; k0 += kKs) {
     __syncthreads();  // the previous step's fragment reads are done
-    store8<AKC>(sA, ia, ka, va);
-    store8<BKC>(sB, ib, kbb, vb);
-    __syncthreads();
-    if (k0 + kKs < ke) {
-      va = load8<AKC>(A, g.a.ld, m0 + ia, k0 + kKs + ka, g.M, ke);
-      vb = load8<BKC>(B, g.b.ld, n0 + ib, k0 + kKs + kbb, g.N, ke);
-    }
-    u32x4_t fa[2], fb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      fa[u] = frag<AKC>(sA, wm + 16 * u, lane);
-      fb[u] = frag<BKC>(sB, wn + 16 * u, lane);
+      store8<AKC>(sA, ia[u], ka[u], va[u]);
+      store8<BKC>(sB, ib[u], kbb[u], vb[u]);
+    }
+    __syncthreads();
+    if (k0 + kKs < ke) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        va[u] = load8<AKC>(A, g.a.ld, m0 + ia[u], k0 + kKs + ka[u], g.M, ke);
+        vb[u] = load8<BKC>(B, g.b.ld, n0 + ib[u], k0 + kKs + kbb[u], g.N, ke);
+      }
     }
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int kk0 = 0; kk0 < kKs; kk0 += 32) {
+      u32x4_t fa[2], fb[2];
 #pragma unroll
-      for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = mfma16(fa[ti], fb[tj], acc[ti][tj]);
+      for (int u = 0; u < 2; ++u) {
+        fa[u] = frag<AKC>(sA, wm + 16 * u, kk0, lane);
+        fb[u] = frag<BKC>(sB, wn + 16 * u, kk0, lane);
+      }
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = mfma16(fa[ti], fb[tj], acc[ti][tj]);
+    }
   }
 
   const int64_t coff = z * g.csb + y * g.csh;
