@@ -18,13 +18,13 @@
 // and the six products are small next to the seven projections.
 //
 // Products: one batched MFMA kernel, 64 x 64 output tiles, 4 waves of 2 x 2
-// 16x16x32 bf16 MFMAs, a 32-deep contraction step staged through LDS with
+// 16x16x32 bf16 MFMAs, a 64-deep contraction step staged through LDS with
 // the next step's operands loaded into registers meanwhile.  Each operand is
 // read along whichever axis is contiguous in memory (template flags) and
 // staged as it lies; fragments of row-contiguous operands come from
-// transposing LDS reads.  Causality prunes work: score tiles wholly above the diagonal are
-// skipped, and the products with P or dS stop (or start) their contraction
-// at the tile's diagonal.
+// transposing LDS reads.  Causality prunes work: score tiles wholly above
+// the diagonal are skipped, and the products with P or dS stop (or start)
+// their contraction at the tile's diagonal.
 //
 // Row kernels: one wave per query row.  The forward softmax takes the row
 // maximum and the sum of exponentials in float32 and writes P and lse; the
@@ -78,11 +78,12 @@ __device__ __forceinline__ u32x4_t load8(const uint16_t *base, int64_t ld, int i
 // LDS tiles of one contraction step.  An operand with its contraction
 // contiguous in memory (KC) is staged [row][contraction] (64 x kLd) and a
 // fragment is one 16-byte read.  An operand with its rows contiguous is
-// staged as it lies, [contraction][row] (32 x kLdT), by 16-byte copies, and
+// staged as it lies, [contraction][row] (64 x kLdT), by 16-byte copies, and
 // a fragment is two ds_read_b64_tr_b16: in a 16-lane group, lane i receives
 // element i & 3 of the 8 bytes addressed by lanes 4q + i/4 (q = 0..3), so
-// lanes addressing contraction rows 8g + 4h + q, columns row0 + 4(j & 3)
-// hand lane i four consecutive contraction elements of row row0 + i.
+// lanes addressing contraction rows kk0 + 8g + 4h + q, columns
+// row0 + 4(j & 3) hand lane i four consecutive contraction elements of row
+// row0 + i.
 // (Writing such operands transposed into LDS took eight 2-byte stores per
 // thread and step.)  kLdT = 72: a 144-byte row stride, at most two lanes of
 // a half-wave per bank for these reads.
