@@ -605,7 +605,8 @@ def layer_rows(q, I, layers, dev, ev, M, r, alpha, adapter_bound, seq=512, heads
     """The LLaMA-7B decoder layer: q, k, v, o (4096 x 4096 NF4+DQ, each with
     its own adapters) around the causal attention core (M / 512 sequences of
     512 tokens, 32 heads of 128), the residuals and the MLP layers above;
-    the backward recomputes the layer from X (checkpointing).  Then the
+    the backward recomputes from X the activations up to the SwiGLU output
+    (checkpointing).  Then the
     attention core alone at the same shape.  Attention flops count the
     causal pairs only: per head 4 d per pair forward (QK^T, PV) and 8 d
     backward (dV, dP, dQ, dK)."""
@@ -627,7 +628,7 @@ def layer_rows(q, I, layers, dev, ev, M, r, alpha, adapter_bound, seq=512, heads
     del qws
     lay = DecoderLayer(weights, adapters, r, alpha, batch, seq, heads, head_dim, device=dev)
     X, dY = g["X"], d["dY"]
-    Y, dX, Y2 = (torch.empty(M, hidden, dtype=torch.bfloat16, device=dev) for _ in range(3))
+    Y, dX = (torch.empty(M, hidden, dtype=torch.bfloat16, device=dev) for _ in range(2))
 
     def timed(fn, n=10, warm=3):
         for _ in range(warm):
@@ -641,14 +642,15 @@ def layer_rows(q, I, layers, dev, ev, M, r, alpha, adapter_bound, seq=512, heads
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    ms = timed(lambda: (lay.fwd(X, Y), lay.bwd(X, dY, dX, Y2)))
+    ms = timed(lambda: (lay.fwd(X, Y), lay.bwd(X, dY, dX)))
     lin_f = lin_b = 0
     for nm, w in weights.items():
         f, b_ = layer_flops(M, w.n, w.k, r)
         lin_f, lin_b = lin_f + f, lin_b + b_
     pairs = batch * heads * seq * (seq + 1) // 2
     att_f, att_b = 4 * head_dim * pairs, 8 * head_dim * pairs
-    flops, recompute = lin_f + lin_b + att_f + att_b, lin_f + att_f
+    down_f = layer_flops(M, weights["down"].n, weights["down"].k, r)[0]
+    flops, recompute = lin_f + lin_b + att_f + att_b, lin_f - down_f + att_f   # the backward recomputes up to h
     a = lay.act
     g_ = lay.grad
     fwd_ms = timed(lambda: q.qlora_attention_fwd(a["q"], a["k"], a["v"], a["attn"], lay.lse, batch, seq, heads,
@@ -662,10 +664,10 @@ def layer_rows(q, I, layers, dev, ev, M, r, alpha, adapter_bound, seq=512, heads
                          "frac_bf16_peak": round((att_f + att_b) / ((fwd_ms + bwd_ms) * 1e-3) / 1e12
                                                  / PEAK_BF16_TFLOPS, 4)},
            "how": f"q,k,v,o (4096x4096) + gate,up,down NF4+DQ with r={r} adapters, causal attention over {batch} "
-                  f"sequences of {seq} ({heads} heads of {head_dim}), SwiGLU, residuals; fwd + checkpointed bwd; "
+                  f"sequences of {seq} ({heads} heads of {head_dim}), SwiGLU, residuals; fwd + checkpointed bwd (recomputes up to the SwiGLU output); "
                   "tflops counts the 7 projections' fwd+bwd and the causal attention pairs, the second figure adds "
                   "the recomputed forward"}
-    del lay, Y, dX, Y2
+    del lay, Y, dX
     torch.cuda.empty_cache()
     return out
 

@@ -6,8 +6,10 @@ App. G), as an ordered sequence of libqlora calls.
     Y1 = X + o(O);  Y = Y1 + down(swiglu(gate(Y1), up(Y1)))
 
 Normalisation and positional rotation are frozen maps without adapters and
-are not part of the layer here.  The backward recomputes the layer's
-activations from X (checkpointing at layer granularity), then runs each
+are not part of the layer here.  The backward recomputes from X the
+activations it needs (checkpointing at layer granularity: everything up to
+the SwiGLU output; the down projection's output and the final sum are not
+needed), then runs each
 projection's frozen-base backward (dX, dA, dB; no weight gradient), the
 attention and SwiGLU backwards and the residual gradient sums.
 
@@ -61,7 +63,8 @@ class DecoderLayer:
         Q.qlora_linear_bwd(self.w[name], X, dY, A, B, self.r, self.alpha, self.H[name], dX, self.dA[name],
                            self.dB[name], self.ws)
 
-    def fwd(self, X: torch.Tensor, Y: torch.Tensor) -> None:
+    def _activations(self, X: torch.Tensor) -> None:
+        """Everything up to h = swiglu(gate(Y1), up(Y1))."""
         a = self.act
         self._fwd("q", X, a["q"])
         self._fwd("k", X, a["k"])
@@ -73,13 +76,17 @@ class DecoderLayer:
         self._fwd("gate", a["y1"], a["gate"])
         self._fwd("up", a["y1"], a["up"])
         Q.qlora_swiglu_fwd(a["gate"], a["up"], a["h"])
+
+    def fwd(self, X: torch.Tensor, Y: torch.Tensor) -> None:
+        self._activations(X)
+        a = self.act
         self._fwd("down", a["h"], a["down_out"])
         Q.qlora_add_bf16(a["y1"], a["down_out"], Y)
 
-    def bwd(self, X: torch.Tensor, dY: torch.Tensor, dX: torch.Tensor, scratch_y: torch.Tensor) -> None:
-        """dX and self.dA / self.dB; scratch_y ([M, hidden] bf16) takes the recomputed output."""
+    def bwd(self, X: torch.Tensor, dY: torch.Tensor, dX: torch.Tensor) -> None:
+        """dX and self.dA / self.dB."""
         a, g = self.act, self.grad
-        self.fwd(X, scratch_y)                                   # recompute the activations
+        self._activations(X)                                     # recompute what the backward reads
         self._bwd("down", a["h"], dY, g["dh"])
         Q.qlora_swiglu_bwd(a["gate"], a["up"], g["dh"], g["dgate"], g["dup"])
         self._bwd("gate", a["y1"], g["dgate"], g["dxg"])
