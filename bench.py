@@ -62,6 +62,8 @@ def parse():
                    help="also run a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--small-m-only", action="store_true",
                    help="print only rows.small_m (the small-M forward), as one JSON line")
+    p.add_argument("--configs-only", action="store_true",
+                   help="print only the 7B q_proj and 65B block rows (M = 512), as one JSON line")
     p.add_argument("--layer-only", action="store_true",
                    help="print only rows.decoder_layer (the 7B decoder layer and its attention core), as one JSON "
                         "line; use with --no-extras")
@@ -167,6 +169,11 @@ def main():
 
     def dev16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.configs_only:
+        print(json.dumps({c: config_rows(q, I, c, dev, lambda: torch.cuda.Event(enable_timing=True), dev16)
+                          for c in ("q_proj_7b", "block_65b")}), flush=True)
+        return
 
     if args.small_m_only:
         print(json.dumps({"small_m": small_m_rows(q, I, np, torch, dev, dev16, lambda: torch.cuda.Event(enable_timing=True))}),
@@ -285,10 +292,7 @@ def main():
               "p90": round(float(np.percentile(per_step, 90)), 4)}
 
     # --------------------------------------- per-kernel event timing (second pass)
-    q.qlora_profile_begin()
-    for _ in range(args.steps):
-        step()
-    prof = q.qlora_profile_end()
+    prof = traced(q, step, args.steps)
     kernels = {name: {"launches_per_step": n / args.steps, "avg_us": 1e3 * ms / n,
                       "ms_per_step": ms / args.steps} for name, (n, ms) in prof.items()}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
@@ -320,6 +324,8 @@ def main():
                 "frac_bf16_peak": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
     }
     if not args.no_extras:
+        for cname in ("q_proj_7b", "block_65b"):
+            rows[cname] = config_rows(q, I, cname, dev, ev, dev16)
         rows["quantize"] = {"ms_all_layers": round(quant_ms, 4),
                             "gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
                             "frac_hbm_peak": round(quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
@@ -383,6 +389,99 @@ def main():
     if attainable:
         out["attainable"] = attainable
     print(json.dumps(out), flush=True)
+
+
+def config_rows(q, I, name, dev, ev, dev16, steps=20, warmup=10):
+    """One workload's step at its own shapes (every layer's forward, then
+    every backward in reverse order, independent seeded inputs per layer, as
+    the main step): time per step, TFLOP/s against the BF16 peak, the
+    per-kernel times from a traced pass, and each layer's launch plan (tile
+    path and contraction splits)."""
+    import torch
+    wl = I.WORKLOADS[name]
+    M, r, alpha = wl.ms[0], wl.r, wl.alpha
+    layers = []
+    for li, L in enumerate(wl.layers):
+        W = torch.from_numpy(I.weight(wl, li)).to(dev)
+        w = q.NF4Weight.empty(L.n, L.k, dev)
+        qws = torch.empty(q.qlora_quantize_workspace_bytes(L.n, L.k), dtype=torch.uint8, device=dev)
+        q.qlora_quantize_nf4_dq(W, w, qws)
+        del W, qws
+        A, B = I.adapters(wl, li)
+        layers.append({"L": L, "w": w, "X": dev16(I.activation(wl, li, M)), "dY": dev16(I.grad_output(wl, li, M)),
+                       "A": dev16(A), "B": dev16(B),
+                       "Y": torch.empty(M, L.n, dtype=torch.bfloat16, device=dev),
+                       "H": torch.empty(M, r, dtype=torch.float32, device=dev),
+                       "dX": torch.empty(M, L.k, dtype=torch.bfloat16, device=dev),
+                       "dA": torch.empty(r, L.k, dtype=torch.bfloat16, device=dev),
+                       "dB": torch.empty(L.n, r, dtype=torch.bfloat16, device=dev)})
+    ws = torch.empty(max(q.qlora_linear_workspace_bytes(M, t["L"].n, t["L"].k, r) for t in layers),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    def fwd_pass():
+        for t in layers:
+            q.qlora_linear_fwd(t["w"], t["X"], t["A"], t["B"], r, alpha, t["Y"], t["H"], ws)
+
+    def bwd_pass():
+        for t in reversed(layers):
+            q.qlora_linear_bwd(t["w"], t["X"], t["dY"], t["A"], t["B"], r, alpha, t["H"], t["dX"], t["dA"],
+                               t["dB"], ws)
+
+    def step():
+        fwd_pass()
+        bwd_pass()
+
+    def timed(fn, n):
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ms = timed(step, steps)
+    fwd_ms, bwd_ms = timed(fwd_pass, steps), timed(bwd_pass, steps)
+    ff = bf = 0
+    for t in layers:
+        f, b = layer_flops(M, t["L"].n, t["L"].k, r)
+        ff, bf = ff + f, bf + b
+    prof = traced(q, step, 5)
+    tf = lambda fl, m: round(fl / (m * 1e-3) / 1e12, 1)
+    out = {"workload": f"{name}: " + ", ".join(f"{t['L'].name} {t['L'].k}->{t['L'].n}" for t in layers) +
+                       f"; M = {M}, r = {r}",
+           "ms": round(ms, 4), "tflops": tf(ff + bf, ms), "frac_bf16_peak": round((ff + bf) / (ms * 1e-3) / 1e12 /
+                                                                                    PEAK_BF16_TFLOPS, 4),
+           "fwd_ms": round(fwd_ms, 4), "fwd_tflops": tf(ff, fwd_ms), "bwd_ms": round(bwd_ms, 4),
+           "bwd_tflops": tf(bf, bwd_ms), "flops_per_step": ff + bf,
+           "plans": {t["L"].name: q.qlora_linear_plan(M, t["L"].n, t["L"].k, r) for t in layers},
+           "kernels_us": {k: {"launches_per_step": n / 5, "avg_us": round(1e3 * v / n, 2)}
+                          for k, (n, v) in sorted(prof.items())}}
+    del layers, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def traced(q, fn, reps):
+    """Per-kernel event times of `reps` calls of fn through the tracing build
+    of the library (same kernels; events recorded on each launch's stream):
+    {kernel: (launches, total ms)}.  One untimed call first loads its code."""
+    import torch
+    q.use_tracing_library(True)
+    try:
+        fn()
+        torch.cuda.synchronize()
+        q.qlora_profile_begin()
+        for _ in range(reps):
+            fn()
+        return q.qlora_profile_end()
+    finally:
+        q.use_tracing_library(False)
 
 
 def storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops):
@@ -490,9 +589,7 @@ def merge_rows(q, layers, dev, ev, r, alpha):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / 3
-    q.qlora_profile_begin()
-    run()
-    prof = q.qlora_profile_end()
+    prof = traced(q, run, 1)
     flops = sum(2 * r * t["L"].n * t["L"].k for t in layers)
     kern = {k: round(1e3 * v[1] / v[0], 1) for k, v in prof.items()}
     km = prof.get("k_merge", (1, ms))[1]
@@ -750,10 +847,9 @@ def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
         gbps = packed_bytes / (us * 1e-6) / 1e9
         row = {"us": round(us, 2), "gbps_packed": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
         # the streaming kernel on its own (library event timer, separate pass)
-        q.qlora_profile_begin()
-        for i in range(reps):
-            q.qlora_linear_fwd(ws_list[i % copies], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws)
-        prof = q.qlora_profile_end()
+        it = iter(range(10 ** 9))
+        prof = traced(q, lambda: q.qlora_linear_fwd(ws_list[next(it) % copies], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws),
+                      reps)
         if "k_gemv_nf4" in prof:
             n, ms = prof["k_gemv_nf4"]
             kus = 1e3 * ms / n

@@ -1,7 +1,10 @@
 """Build libqlora.so (gfx950) in-tree from csrc/*.hip with hipcc.
 
 Every call recompiles: the objects go to ``_build/`` next to this file and the
-shared library to ``libqlora.so`` beside them.
+shared library to ``libqlora.so`` beside them.  A second library from the
+same sources, ``libqlora_prof.so``, is built with -DQLORA_PROFILE: it adds
+the per-kernel event timer (profile.hip, include/qlora_profile.h) that the
+benchmark's tracing pass uses; the product library carries no timer.
 """
 from __future__ import annotations
 
@@ -14,7 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
-SOURCES = ["capi.hip", "profile.hip", "quantize.hip", "dequant.hip", "lora_gemm.hip", "jobs.hip", "nf4_tile.hip", "nf4_gemv.hip", "linear_fwd.hip", "linear_bwd.hip", "merge.hip", "adamw.hip", "swiglu.hip", "attention.hip"]
+LIB_PROF = os.path.join(PKG, "libqlora_prof.so")
+SOURCES = ["capi.hip", "quantize.hip", "dequant.hip", "lora_gemm.hip", "jobs.hip", "nf4_tile.hip", "nf4_gemv.hip", "linear_fwd.hip", "linear_bwd.hip", "merge.hip", "adamw.hip", "swiglu.hip", "attention.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -42,17 +46,23 @@ def _run(cmd):
 
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
     cc = hipcc()
-    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
-    cmds = [[cc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    variants = [(LIB, os.path.join(BUILD, "lib"), SOURCES, []),
+                (LIB_PROF, os.path.join(BUILD, "prof"), SOURCES + ["profile.hip"], ["-DQLORA_PROFILE=1"])]
+    cmds, links = [], []
+    for lib, odir, srcs, extra in variants:
+        os.makedirs(odir, exist_ok=True)
+        objs = [os.path.join(odir, s.replace(".hip", ".o")) for s in srcs]
+        cmds += [[cc, *FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(srcs, objs)]
+        links.append((lib, objs))
     with ThreadPoolExecutor(max_workers=jobs or min(8, len(cmds))) as ex:
         for msg in ex.map(_run, cmds):
             if verbose and msg.strip():
                 print(msg)
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    for lib, objs in links:
+        tmp = lib + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-o", tmp, *objs])
+        os.replace(tmp, lib)
     return LIB
 
 

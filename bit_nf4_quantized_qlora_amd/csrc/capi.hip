@@ -56,56 +56,92 @@ int hip_fail(hipError_t e, const char *where) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // sanity bound on n*k and M*k, M*n
-constexpr int64_t kMaxK = int64_t(1) << 22;      // tile-relative byte offsets in the GEMMs stay 32-bit
+constexpr int64_t kMaxK = int64_t(1) << 22;      // k < 2^22: a 256-row activation tile stays below 2^31 bytes
 
 int check_shape(int64_t n, int64_t k) {
   if (n < 1 || k < kBlock || k % kBlock != 0)
     return fail(QLORA_ERR_BAD_SHAPE, "weight shape [%lld, %lld]: need n >= 1, k >= 64, k %% 64 == 0",
                 (long long)n, (long long)k);
-  if (n > kMaxElems / k || k > kMaxK) return fail(QLORA_ERR_BAD_SHAPE, "weight too large");
+  if (n > kMaxElems / k || k >= kMaxK) return fail(QLORA_ERR_BAD_SHAPE, "weight too large");
   return QLORA_OK;
 }
 
-int check_weight(const qlora_nf4_weight *w) {
+// A weight descriptor of either ABI form, flattened.
+struct WeightIn {
+  int64_t n = 0, k = 0;
+  uint8_t *packed = nullptr, *scale_code = nullptr;
+  float *group_amax = nullptr, *offset = nullptr;
+  int codebook = QLORA_CODEBOOK_NF4, scales = QLORA_SCALES_DQ;
+  float *absmax = nullptr;
+};
+
+int take(const qlora_nf4_weight *w, WeightIn *o) {
   if (!w) return fail(QLORA_ERR_NULL_ARG, "weight descriptor is NULL");
-  if (int e = check_shape(w->n, w->k)) return e;
-  if (w->codebook != QLORA_CODEBOOK_NF4 && w->codebook != QLORA_CODEBOOK_FP4_E2M1)
-    return fail(QLORA_ERR_BAD_CODEBOOK, "codebook %d is neither NF4 (0) nor Float4 E2M1 (1)", (int)w->codebook);
-  if (w->scales != QLORA_SCALES_DQ && w->scales != QLORA_SCALES_FP32)
-    return fail(QLORA_ERR_BAD_CODEBOOK, "scales %d is neither DQ (0) nor FP32 (1)", (int)w->scales);
-  if (w->scales == QLORA_SCALES_DQ) {
-    if (!w->packed || !w->scale_code || !w->group_amax || !w->offset)
+  o->n = w->n;
+  o->k = w->k;
+  o->packed = w->packed;
+  o->scale_code = w->scale_code;
+  o->group_amax = w->group_amax;
+  o->offset = w->offset;
+  return QLORA_OK;
+}
+
+int take_ex(const qlora_weight_ex *w, WeightIn *o) {
+  if (!w) return fail(QLORA_ERR_NULL_ARG, "weight descriptor is NULL");
+  if (w->size < sizeof(qlora_weight_ex))
+    return fail(QLORA_ERR_BAD_CODEBOOK, "qlora_weight_ex.size = %zu < %zu", w->size, sizeof(qlora_weight_ex));
+  if (int e = take(&w->base, o)) return e;
+  o->codebook = w->codebook;
+  o->scales = w->scales;
+  o->absmax = w->absmax;
+  return QLORA_OK;
+}
+
+int check_weight(const WeightIn &w) {
+  if (int e = check_shape(w.n, w.k)) return e;
+  if (w.codebook != QLORA_CODEBOOK_NF4 && w.codebook != QLORA_CODEBOOK_FP4_E2M1)
+    return fail(QLORA_ERR_BAD_CODEBOOK, "codebook %d is neither NF4 (0) nor Float4 E2M1 (1)", (int)w.codebook);
+  if (w.scales != QLORA_SCALES_DQ && w.scales != QLORA_SCALES_FP32)
+    return fail(QLORA_ERR_BAD_CODEBOOK, "scales %d is neither DQ (0) nor FP32 (1)", (int)w.scales);
+  if (w.scales == QLORA_SCALES_DQ) {
+    if (!w.packed || !w.scale_code || !w.group_amax || !w.offset)
       return fail(QLORA_ERR_NULL_ARG, "a weight buffer is NULL");
-    if (!aligned16(w->packed) || !aligned16(w->scale_code) || !aligned16(w->group_amax) || !aligned16(w->offset))
+    if (!aligned16(w.packed) || !aligned16(w.scale_code) || !aligned16(w.group_amax) || !aligned16(w.offset))
       return fail(QLORA_ERR_MISALIGNED, "weight buffers must be 16-byte aligned");
   } else {
-    if (!w->packed || !w->absmax) return fail(QLORA_ERR_NULL_ARG, "a weight buffer is NULL");
-    if (!aligned16(w->packed) || !aligned16(w->absmax))
+    if (!w.packed || !w.absmax) return fail(QLORA_ERR_NULL_ARG, "a weight buffer is NULL");
+    if (!aligned16(w.packed) || !aligned16(w.absmax))
       return fail(QLORA_ERR_MISALIGNED, "weight buffers must be 16-byte aligned");
   }
   return QLORA_OK;
 }
 
-Nf4View view_of(const qlora_nf4_weight *w) {
+Nf4View view_of(const WeightIn &w) {
   Nf4View v;
-  v.n = w->n;
-  v.k = w->k;
-  v.nb = w->n * w->k / kBlock;
+  v.n = w.n;
+  v.k = w.k;
+  v.nb = w.n * w.k / kBlock;
   v.ng = ceil_div(v.nb, kGroup);
-  v.packed = w->packed;
-  v.scale_code = w->scale_code;
-  v.group_amax = w->group_amax;
-  v.offset = w->offset;
-  v.codebook = w->codebook;
-  v.absmax = w->scales == QLORA_SCALES_FP32 ? w->absmax : nullptr;
+  v.packed = w.packed;
+  v.scale_code = w.scale_code;
+  v.group_amax = w.group_amax;
+  v.offset = w.offset;
+  v.codebook = w.codebook;
+  v.absmax = w.scales == QLORA_SCALES_FP32 ? w.absmax : nullptr;
   return v;
 }
 
-int check_linear(const qlora_nf4_weight *w, int64_t M, int r, float alpha) {
-  if (int e = check_weight(w)) return e;
+int check_linear_shape(int64_t n, int64_t k, int64_t M, int r) {
+  if (int e = check_shape(n, k)) return e;
   if (M < 0) return fail(QLORA_ERR_BAD_SHAPE, "M = %lld < 0", (long long)M);
-  if (M > kMaxElems / std::max<int64_t>(w->k, w->n)) return fail(QLORA_ERR_BAD_SHAPE, "M too large");
+  if (M > kMaxElems / std::max<int64_t>(k, n)) return fail(QLORA_ERR_BAD_SHAPE, "M too large");
   if (r < 1 || r > 128) return fail(QLORA_ERR_BAD_RANK, "rank r = %d outside [1, 128]", r);
+  return QLORA_OK;
+}
+
+int check_linear(const WeightIn &w, int64_t M, int r, float alpha) {
+  if (int e = check_weight(w)) return e;
+  if (int e = check_linear_shape(w.n, w.k, M, r)) return e;
   if (!std::isfinite(alpha)) return fail(QLORA_ERR_BAD_ALPHA, "alpha is not finite");
   return QLORA_OK;
 }
@@ -146,36 +182,62 @@ int qlora_nf4_sizes(int64_t n, int64_t k, size_t *packed_bytes, size_t *scale_co
 }
 
 size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k) {
-  if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k || k > kMaxK) return 0;
+  if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k || k >= kMaxK) return 0;
   return quantize_ws(n, k);
 }
 
-int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws, size_t ws_bytes, void *stream) {
+namespace {
+int quantize_impl(const char *fn, const float *W, const WeightIn &out, void *ws, size_t ws_bytes, hipStream_t s) {
   if (int e = check_weight(out)) return e;
   if (int e = check_tensor(W, "W")) return e;
-  const size_t need = quantize_ws(out->n, out->k);
+  const size_t need = quantize_ws(out.n, out.k);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
-  const int64_t nb = out->n * out->k / kBlock;
-  const bool single = out->scales == QLORA_SCALES_FP32;
-  float *ws_absmax = single ? out->absmax : static_cast<float *>(ws);
+  const int64_t nb = out.n * out.k / kBlock;
+  const bool single = out.scales == QLORA_SCALES_FP32;
+  float *ws_absmax = single ? out.absmax : static_cast<float *>(ws);
   double *ws_sum = reinterpret_cast<double *>(static_cast<char *>(ws) + align_up((size_t)nb * sizeof(float), 256));
-  hipError_t e = launch_quantize(W, out->n, out->k, out->codebook, single, out->packed, out->scale_code, out->group_amax, out->offset,
-                                 ws_absmax, ws_sum, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "qlora_quantize_nf4_dq");
+  hipError_t e = launch_quantize(W, out.n, out.k, out.codebook, single, out.packed, out.scale_code, out.group_amax,
+                                 out.offset, ws_absmax, ws_sum, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
   return QLORA_OK;
 }
 
-int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream) {
+int dequant_impl(const char *fn, const WeightIn &w, uint16_t *W_bf16, hipStream_t s) {
   if (int e = check_weight(w)) return e;
   if (int e = check_tensor(W_bf16, "W_bf16")) return e;
-  hipError_t e = launch_dequant(view_of(w), W_bf16, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "qlora_dequant_bf16");
+  hipError_t e = launch_dequant(view_of(w), W_bf16, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
   return QLORA_OK;
+}
+}  // namespace
+
+int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  WeightIn o;
+  if (int e = take(out, &o)) return e;
+  return quantize_impl("qlora_quantize_nf4_dq", W, o, ws, ws_bytes, stream);
+}
+
+int qlora_quantize_ex(const float *W, const qlora_weight_ex *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  WeightIn o;
+  if (int e = take_ex(out, &o)) return e;
+  return quantize_impl("qlora_quantize_ex", W, o, ws, ws_bytes, stream);
+}
+
+int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, hipStream_t stream) {
+  WeightIn v;
+  if (int e = take(w, &v)) return e;
+  return dequant_impl("qlora_dequant_bf16", v, W_bf16, stream);
+}
+
+int qlora_dequant_bf16_ex(const qlora_weight_ex *w, uint16_t *W_bf16, hipStream_t stream) {
+  WeightIn v;
+  if (int e = take_ex(w, &v)) return e;
+  return dequant_impl("qlora_dequant_bf16_ex", v, W_bf16, stream);
 }
 
 namespace {
 int elementwise(int op, const char *fn, const uint16_t *x0, const uint16_t *x1, const uint16_t *x2, uint16_t *y0,
-                uint16_t *y1, int64_t count, void *stream) {
+                uint16_t *y1, int64_t count, hipStream_t stream) {
   if (count < 0 || count > kMaxElems) return fail(QLORA_ERR_BAD_SHAPE, "count = %lld", (long long)count);
   if (count == 0) return QLORA_OK;
   if (int e = check_tensor(x0, "input")) return e;
@@ -185,22 +247,22 @@ int elementwise(int op, const char *fn, const uint16_t *x0, const uint16_t *x1, 
   if (int e = check_tensor(y0, "output")) return e;
   if (op == 1)
     if (int e = check_tensor(y1, "du")) return e;
-  hipError_t e = launch_swiglu(op, x0, x1, x2, y0, y1, count, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_swiglu(op, x0, x1, x2, y0, y1, count, stream);
   if (e != hipSuccess) return hip_fail(e, fn);
   return QLORA_OK;
 }
 }  // namespace
 
-int qlora_swiglu_fwd(const uint16_t *gate, const uint16_t *up, uint16_t *h, int64_t count, void *stream) {
+int qlora_swiglu_fwd(const uint16_t *gate, const uint16_t *up, uint16_t *h, int64_t count, hipStream_t stream) {
   return elementwise(0, "qlora_swiglu_fwd", gate, up, nullptr, h, nullptr, count, stream);
 }
 
 int qlora_swiglu_bwd(const uint16_t *gate, const uint16_t *up, const uint16_t *dh, uint16_t *d_gate, uint16_t *d_up,
-                     int64_t count, void *stream) {
+                     int64_t count, hipStream_t stream) {
   return elementwise(1, "qlora_swiglu_bwd", gate, up, dh, d_gate, d_up, count, stream);
 }
 
-int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t count, void *stream) {
+int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t count, hipStream_t stream) {
   return elementwise(2, "qlora_add_bf16", a, b, nullptr, out, nullptr, count, stream);
 }
 
@@ -227,7 +289,7 @@ size_t qlora_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads
 
 int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
                         int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
-                        void *stream) {
+                        hipStream_t stream) {
   if (int e = check_attention(batch, seq, heads, head_dim)) return e;
   if (batch == 0 || seq == 0) return QLORA_OK;
   if (int e = check_tensor(q, "q")) return e;
@@ -236,7 +298,7 @@ int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
   if (int e = check_tensor(o, "o")) return e;
   if (int e = check_tensor(lse, "lse")) return e;
   if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads, head_dim))) return e;
-  hipError_t e = launch_attention_fwd(q, k, v, o, lse, batch, seq, heads, head_dim, ws, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_attention_fwd(q, k, v, o, lse, batch, seq, heads, head_dim, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "qlora_attention_fwd");
   return QLORA_OK;
 }
@@ -244,7 +306,7 @@ int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *d_o, const float *lse,
                         uint16_t *dq, uint16_t *dk, uint16_t *dv,
                         int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
-                        void *stream) {
+                        hipStream_t stream) {
   if (int e = check_attention(batch, seq, heads, head_dim)) return e;
   if (batch == 0 || seq == 0) return QLORA_OK;
   const void *ptrs[] = {q, k, v, d_o, lse, dq, dk, dv};
@@ -253,13 +315,13 @@ int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     if (int e = check_tensor(ptrs[i], names[i])) return e;
   if (int e = check_ws(ws, ws_bytes, attention_workspace_bytes(batch, seq, heads, head_dim))) return e;
   hipError_t e = launch_attention_bwd(q, k, v, d_o, lse, dq, dk, dv, batch, seq, heads, head_dim, ws,
-                                      static_cast<hipStream_t>(stream));
+                                      stream);
   if (e != hipSuccess) return hip_fail(e, "qlora_attention_bwd");
   return QLORA_OK;
 }
 
 int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *m, float *v, int64_t count,
-                     float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream) {
+                     float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step, hipStream_t stream) {
   if (count < 0 || count > kMaxElems) return fail(QLORA_ERR_BAD_SHAPE, "count = %lld", (long long)count);
   if (step < 1) return fail(QLORA_ERR_BAD_SHAPE, "step = %lld (counts from 1)", (long long)step);
   if (!std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(weight_decay) || !(beta1 >= 0.f && beta1 < 1.f) ||
@@ -273,18 +335,21 @@ int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, f
   if (param_bf16)
     if (int e = check_tensor(param_bf16, "param_bf16")) return e;
   hipError_t e = launch_adamw(param, param_bf16, grad, m, v, count, lr, beta1, beta2, eps, weight_decay, step,
-                              static_cast<hipStream_t>(stream));
+                              stream);
   if (e != hipSuccess) return hip_fail(e, "qlora_adamw_step");
   return QLORA_OK;
 }
 
 size_t qlora_merge_workspace_bytes(int64_t n, int64_t k) {
-  if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k || k > kMaxK) return 0;
+  if (n < 1 || k < kBlock || k % kBlock != 0 || n > kMaxElems / k || k >= kMaxK) return 0;
   return align_up((size_t)(n * k) * sizeof(float), 256) + quantize_ws(n, k);
 }
 
-int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B, int r, float alpha,
-                         uint16_t *W_merged, const qlora_nf4_weight *out, void *ws, size_t ws_bytes, void *stream) {
+int qlora_merge_adapters(const qlora_weight_ex *wx, const uint16_t *A, const uint16_t *B, int r, float alpha,
+                         uint16_t *W_merged, const qlora_weight_ex *outx, void *ws, size_t ws_bytes,
+                         hipStream_t s) {
+  WeightIn w, out;
+  if (int e = take_ex(wx, &w)) return e;
   if (int e = check_weight(w)) return e;
   if (r < 1 || r > 128) return fail(QLORA_ERR_BAD_RANK, "rank r = %d outside [1, 128]", r);
   if (!std::isfinite(alpha)) return fail(QLORA_ERR_BAD_ALPHA, "alpha is not finite");
@@ -292,24 +357,24 @@ int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uin
   if (int e = check_tensor(B, "B")) return e;
   if (W_merged)
     if (int e = check_tensor(W_merged, "W_merged")) return e;
-  if (out) {
+  if (outx) {
+    if (int e = take_ex(outx, &out)) return e;
     if (int e = check_weight(out)) return e;
-    if (out->n != w->n || out->k != w->k) return fail(QLORA_ERR_BAD_SHAPE, "out is not [n, k] of w");
+    if (out.n != w.n || out.k != w.k) return fail(QLORA_ERR_BAD_SHAPE, "out is not [n, k] of w");
   }
-  const size_t need = qlora_merge_workspace_bytes(w->n, w->k);
+  const size_t need = qlora_merge_workspace_bytes(w.n, w.k);
   if (int e = check_ws(ws, ws_bytes, need)) return e;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   float *Wm = static_cast<float *>(ws);
   hipError_t e = launch_merge(view_of(w), A, B, r, (float)alpha / (float)r, Wm, W_merged, s);
   if (e != hipSuccess) return hip_fail(e, "qlora_merge_adapters");
-  if (out) {
-    char *qws = static_cast<char *>(ws) + align_up((size_t)(w->n * w->k) * sizeof(float), 256);
-    const int64_t nb = out->n * out->k / kBlock;
-    const bool single = out->scales == QLORA_SCALES_FP32;
-    float *ws_absmax = single ? out->absmax : reinterpret_cast<float *>(qws);
+  if (outx) {
+    char *qws = static_cast<char *>(ws) + align_up((size_t)(w.n * w.k) * sizeof(float), 256);
+    const int64_t nb = out.n * out.k / kBlock;
+    const bool single = out.scales == QLORA_SCALES_FP32;
+    float *ws_absmax = single ? out.absmax : reinterpret_cast<float *>(qws);
     double *ws_sum = reinterpret_cast<double *>(qws + align_up((size_t)nb * sizeof(float), 256));
-    e = launch_quantize(Wm, out->n, out->k, out->codebook, single, out->packed, out->scale_code, out->group_amax,
-                        out->offset, ws_absmax, ws_sum, s);
+    e = launch_quantize(Wm, out.n, out.k, out.codebook, single, out.packed, out.scale_code, out.group_amax,
+                        out.offset, ws_absmax, ws_sum, s);
     if (e != hipSuccess) return hip_fail(e, "qlora_merge_adapters (re-encode)");
   }
   return QLORA_OK;
@@ -317,13 +382,14 @@ int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uin
 
 size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r) {
   if (n < 1 || k < kBlock || k % kBlock != 0 || M < 0 || r < 1 || r > 128) return 0;
-  if (n > kMaxElems / k || k > kMaxK || M > kMaxElems / std::max<int64_t>(k, n)) return 0;
+  if (n > kMaxElems / k || k >= kMaxK || M > kMaxElems / std::max<int64_t>(k, n)) return 0;
   if (M == 0) return 0;
   return std::max(fwd_workspace_bytes(M, n, k, r), bwd_workspace_bytes(M, n, k, r));
 }
 
-int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B,
-                     int r, float alpha, uint16_t *Y, float *H_out, void *ws, size_t ws_bytes, void *stream) {
+namespace {
+int fwd_impl(const char *fn, const WeightIn &w, const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B,
+             int r, float alpha, uint16_t *Y, float *H_out, void *ws, size_t ws_bytes, hipStream_t s) {
   if (int e = check_linear(w, M, r, alpha)) return e;
   if (M == 0) return QLORA_OK;
   if (int e = check_tensor(X, "X")) return e;
@@ -331,16 +397,16 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
   if (int e = check_tensor(B, "B")) return e;
   if (int e = check_tensor(Y, "Y")) return e;
   if (H_out && !aligned16(H_out)) return fail(QLORA_ERR_MISALIGNED, "H_out is not 16-byte aligned");
-  if (int e = check_ws(ws, ws_bytes, fwd_workspace_bytes(M, w->n, w->k, r))) return e;
+  if (int e = check_ws(ws, ws_bytes, fwd_workspace_bytes(M, w.n, w.k, r))) return e;
   LinearArgs a{view_of(w), M, r, (float)alpha / (float)r};
-  hipError_t e = launch_linear_fwd(a, X, A, B, Y, H_out, ws, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd");
+  hipError_t e = launch_linear_fwd(a, X, A, B, Y, H_out, ws, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
   return QLORA_OK;
 }
 
-int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY, int64_t M, const uint16_t *A,
-                     const uint16_t *B, int r, float alpha, const float *H, uint16_t *dX, uint16_t *dA,
-                     uint16_t *dB, void *ws, size_t ws_bytes, void *stream) {
+int bwd_impl(const char *fn, const WeightIn &w, const uint16_t *X, const uint16_t *dY, int64_t M, const uint16_t *A,
+             const uint16_t *B, int r, float alpha, const float *H, uint16_t *dX, uint16_t *dA, uint16_t *dB,
+             void *ws, size_t ws_bytes, hipStream_t s) {
   if (int e = check_linear(w, M, r, alpha)) return e;
   if (int e = check_tensor(dA, "dA")) return e;
   if (int e = check_tensor(dB, "dB")) return e;
@@ -351,11 +417,55 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
     if (int e = check_tensor(B, "B")) return e;
     if (dX && !aligned16(dX)) return fail(QLORA_ERR_MISALIGNED, "dX is not 16-byte aligned");
     if (H && !aligned16(H)) return fail(QLORA_ERR_MISALIGNED, "H is not 16-byte aligned");
-    if (int e = check_ws(ws, ws_bytes, bwd_workspace_bytes(M, w->n, w->k, r))) return e;
+    if (int e = check_ws(ws, ws_bytes, bwd_workspace_bytes(M, w.n, w.k, r))) return e;
   }
   LinearArgs a{view_of(w), M, r, (float)alpha / (float)r};
-  hipError_t e = launch_linear_bwd(a, X, dY, A, B, H, dX, dA, dB, ws, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "qlora_linear_bwd");
+  hipError_t e = launch_linear_bwd(a, X, dY, A, B, H, dX, dA, dB, ws, s);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return QLORA_OK;
+}
+}  // namespace
+
+int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B,
+                     int r, float alpha, uint16_t *Y, float *H_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  WeightIn v;
+  if (int e = take(w, &v)) return e;
+  return fwd_impl("qlora_linear_fwd", v, X, M, A, B, r, alpha, Y, H_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_ex(const qlora_weight_ex *w, const uint16_t *X, int64_t M, const uint16_t *A, const uint16_t *B,
+                        int r, float alpha, uint16_t *Y, float *H_out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  WeightIn v;
+  if (int e = take_ex(w, &v)) return e;
+  return fwd_impl("qlora_linear_fwd_ex", v, X, M, A, B, r, alpha, Y, H_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY, int64_t M, const uint16_t *A,
+                     const uint16_t *B, int r, float alpha, const float *H, uint16_t *dX, uint16_t *dA,
+                     uint16_t *dB, void *ws, size_t ws_bytes, hipStream_t stream) {
+  WeightIn v;
+  if (int e = take(w, &v)) return e;
+  return bwd_impl("qlora_linear_bwd", v, X, dY, M, A, B, r, alpha, H, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_ex(const qlora_weight_ex *w, const uint16_t *X, const uint16_t *dY, int64_t M, const uint16_t *A,
+                        const uint16_t *B, int r, float alpha, const float *H, uint16_t *dX, uint16_t *dA,
+                        uint16_t *dB, void *ws, size_t ws_bytes, hipStream_t stream) {
+  WeightIn v;
+  if (int e = take_ex(w, &v)) return e;
+  return bwd_impl("qlora_linear_bwd_ex", v, X, dY, M, A, B, r, alpha, H, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_plan(int64_t M, int64_t n, int64_t k, int r, int32_t scales, qlora_linear_plan_info *out) {
+  if (!out) return fail(QLORA_ERR_NULL_ARG, "out is NULL");
+  if (scales != QLORA_SCALES_DQ && scales != QLORA_SCALES_FP32)
+    return fail(QLORA_ERR_BAD_CODEBOOK, "scales %d is neither DQ (0) nor FP32 (1)", (int)scales);
+  if (int e = check_linear_shape(n, k, M, r)) return e;
+  const LinearPlan p = plan_linear(M, n, k, r, scales == QLORA_SCALES_FP32);
+  out->fwd_path = p.fwd_path;
+  out->fwd_splits = p.fwd_splits;
+  out->dx_path = p.dx_path;
+  out->dx_splits = p.dx_splits;
   return QLORA_OK;
 }
 

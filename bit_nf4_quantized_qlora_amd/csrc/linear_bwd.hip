@@ -5,8 +5,9 @@
 // explained." step 5: gradients reach the adapters only.  With
 // Y = X W_hat^T + s (X A^T) B^T:
 //   G  = s dY B            (k_nt_splitk on dY and B^T)
-//   dX = dY W_hat + G A    (k_bwd_dx_nf4 in nf4_tile.hip; k_bwd_dx below when
-//                           n % 64 != 0)
+//   dX = dY W_hat + G A    (k_bwd_dx_nf4 in nf4_tile.hip, its contraction
+//                           split when the tiles cannot fill the GPU;
+//                           k_bwd_dx below when n % 64 != 0)
 //   dB = s dY^T H          (k_tn_splitk on dY and (sH)^T)
 //   dA = G^T X             (k_tn_splitk on X and G^T; one launch with dB's)
 // The small layout copies (B^T, A^T, (sH)^T), the tile kernel's block-scale
@@ -147,7 +148,7 @@ struct BwdWs {
   int RP;
   int64_t Mp;
   SplitPlan sp_h, sp_g, sp_b, sp_a;
-  size_t part_off, parta_off, h_off, sht_off, bt_off, at_off, gb_off, gt_off, scale_off, total;
+  size_t part_off, parta_off, h_off, sht_off, bt_off, at_off, gb_off, gt_off, scale_off, tpart_off, total;
 };
 
 BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, int r) {
@@ -177,6 +178,7 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, int r) {
   l.gb_off = take((size_t)M * l.RP * 2);
   l.gt_off = take((size_t)l.RP * l.Mp * 2);
   l.scale_off = take(tile_scales_bytes(N, K));
+  l.tpart_off = take(tile_partial_bytes(M, N, K));
   l.total = off;
   return l;
 }
@@ -219,7 +221,7 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   }
   // layouts: sHt = bf16(s H)^T [RP][Mp], Bt [RP][N], At [K][RP]; and the dX
   // tile kernel's block-scale table -- one launch
-  const bool tiles = dX != nullptr && bwd_tiles_supported(N, K);
+  const bool tiles = dX != nullptr && plan_linear(M, N, K, r, a.w.absmax != nullptr).dx_path == QLORA_PATH_TILE;
   float *scales = reinterpret_cast<float *>(base + l.scale_off);
   SmallJob prep[kMaxJobs];
   int np = 0;
@@ -233,7 +235,8 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   QLORA_TRY(launch_reduce_rows(part, l.sp_g.splits, M, RP, r, a.s, nullptr, Gb, Gt, l.Mp, s));
   if (dX != nullptr) {
     if (tiles) {
-      QLORA_TRY(launch_bwd_dx_tiles(a.w, scales, dY, M, At, RP, Gb, dX, s));
+      QLORA_TRY(launch_bwd_dx_tiles(a.w, scales, dY, M, At, RP, Gb, dX,
+                                    reinterpret_cast<float *>(base + l.tpart_off), s));
     } else {  // ragged n: the general 128 x 128 kernel
       const dim3 grid((unsigned)ceil_div(K, DBK), (unsigned)ceil_div(M, DBM));
       QLORA_LAUNCH("k_bwd_dx", k_bwd_dx, grid, dim3(256), 0, s, a.w, dY, M, At, Gb, RP, dX);

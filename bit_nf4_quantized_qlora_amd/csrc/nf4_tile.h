@@ -16,9 +16,22 @@ __host__ __device__ inline int64_t tile_bwd_nsup(int64_t n) { return (n + kTileR
 // weight (the larger of the two layouts).
 size_t tile_scales_bytes(int64_t n, int64_t k);
 
-// Whether launch_bwd_dx_tiles handles this weight shape: n % 64 == 0 and the
-// packed weight below 2^31 bytes (32-bit offsets into it).
+// Whether launch_bwd_dx_tiles handles this weight shape: n % 64 == 0, and
+// the packed weight and a 256-row dY tile below 2^31 bytes (32-bit offsets).
 bool bwd_tiles_supported(int64_t n, int64_t k);
+
+// Contraction splits of one tile launch: `splits` workgroups per output
+// tile, each over `lsteps` 64-wide steps (a multiple of 8), whose float32
+// partial tiles a reduction kernel sums in split order.
+struct TileSplit {
+  int splits = 1;
+  int lsteps = 8;
+};
+TileSplit plan_tile_split(int64_t tiles, int64_t nk, int64_t M, int64_t NO);
+TileSplit plan_fwd_tiles(int64_t M, int64_t n, int64_t k);
+TileSplit plan_dx_tiles(int64_t M, int64_t n, int64_t k);
+// Device bytes of the partial tiles either launch writes (0 when unsplit).
+size_t tile_partial_bytes(int64_t M, int64_t n, int64_t k);
 
 // The block-scale tables the two tile kernels stream (jobs.hip, run by
 // launch_jobs before the tile launch): `scales` is device scratch of
@@ -29,14 +42,15 @@ SmallJob job_scales_bwd(const Nf4View &w, float *scales);
 // Y[M, n] = bf16( X W_hat^T + sH B_lora^T ):  X [M, k], sH [M, RP] = bf16(s H)
 // with the rank padded to RP by zeros, B_lora [n, r] (row stride r).
 // `scales`: the table job_scales_fwd wrote.
+// `tpart`: device scratch of tile_partial_bytes (may be NULL when it is 0).
 hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, int64_t M, const uint16_t *Bl, int r,
-                            int RP, const uint16_t *sH, uint16_t *Y, hipStream_t s);
+                            int RP, const uint16_t *sH, uint16_t *Y, float *tpart, hipStream_t s);
 
 // dX[M, k] = bf16( dY W_hat + G At^T ):  dY [M, n], At [k, RP] (A_lora
 // transposed, rank padded), G [M, RP].  Requires bwd_tiles_supported;
 // `scales`: the table job_scales_bwd wrote.
 hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
-                               int RP, const uint16_t *Gb, uint16_t *dX, hipStream_t s);
+                               int RP, const uint16_t *Gb, uint16_t *dX, float *tpart, hipStream_t s);
 
 // Small-M forward (nf4_gemv.hip): the whole forward -- H, and
 // Y = X W_hat^T + bf16(s H) B^T -- for 1 <= M <= kGemvMaxM in one pass over

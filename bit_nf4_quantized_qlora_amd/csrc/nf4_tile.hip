@@ -121,12 +121,62 @@ __device__ __forceinline__ void store_tile(const f32x4_t (&acc)[4][16], uint8_t 
   }
 }
 
+// Split-contraction output: the float32 partial tile of split `sidx`, in the
+// tile's own register order (slot j = 16rt + ct of thread t at
+// ((split * ntiles + tile) * 64 + j) * 256 + t), so each wave writes 1 KB
+// contiguous per store; k_split_reduce sums the splits in order.
+__device__ __forceinline__ void store_partial(const f32x4_t (&acc)[4][16], f32x4_t *__restrict__ part,
+                                              int64_t slot) {
+  f32x4_t *p = part + slot * 64 * 256 + threadIdx.x;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 16; ++ct) p[(rt * 16 + ct) * 256] = acc[rt][ct];
+}
+
+// out[m][o] = bf16( sum over s = 0 .. splits-1, in that order, of the
+// partial tiles ), one thread per float4 slot of the partial layout above.
+__global__ __launch_bounds__(256) void k_split_reduce(const f32x4_t *__restrict__ part, int splits, int ntiles,
+                                                      int tiles_o, int64_t M, int64_t NO,
+                                                      uint16_t *__restrict__ out) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t tj = blockIdx.x;  // tile * 64 + j
+  const int j = (int)(tj & 63);
+  const int64_t tile = tj >> 6;
+  const int64_t to = tile % tiles_o, mt = tile / tiles_o;
+  const int64_t o = to * TO + 64 * wave + 16 * (j >> 4) + 4 * (lane >> 4);
+  const int64_t m = mt * TM + 16 * (j & 15) + (lane & 15);
+  if (m >= M || o >= NO) return;
+  const int64_t slot = tj * 256 + t, stride = (int64_t)ntiles * 64 * 256;
+  f32x4_t a = part[slot];
+  for (int s = 1; s < splits; ++s) {
+    const f32x4_t b = part[s * stride + slot];
+    a = f32x4_t{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+  }
+  uint16_t *dst = out + m * NO + o;
+  if ((NO & 3) == 0) {
+    *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{bf16x2_rne(a[0], a[1]), bf16x2_rne(a[2], a[3])};
+  } else {
+    const uint32_t lo = bf16x2_rne(a[0], a[1]), hi = bf16x2_rne(a[2], a[3]);
+    const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (o + v < NO) dst[v] = e[v];
+  }
+}
+
+// Grid: tiles x splits workgroups.  With splits > 1, workgroup (tile, s)
+// runs contraction steps s*lsteps .. min(nk, (s+1)*lsteps) - 1 (lsteps a
+// multiple of 8; split 0 also adds the LoRA term) and writes its float32
+// partial tile to `part`; otherwise lsteps covers the whole contraction and
+// the tile is rounded to bf16 into `out`.
 template <bool kBwd>
 __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__restrict__ Sp,
                                                      const uint16_t *__restrict__ Bact, int64_t M,
                                                      const uint16_t *__restrict__ L, int lda, int RP,
                                                      const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
-                                                     int tiles_o) {
+                                                     int tiles_o, int splits, int lsteps,
+                                                     f32x4_t *__restrict__ part) {
   __shared__ __align__(16) uint16_t Bs0[TM * 64];
   __shared__ __align__(16) uint16_t Bs1[TM * 64];
   __shared__ __align__(16) uint8_t Wc0[256 * 128];
@@ -141,8 +191,11 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   // Tiles in bands of ob o-tiles, m-major inside a band; each XCD takes a
   // contiguous run of that order (xcd_tile), so the tiles it holds form an
   // m x ob block and share both operand panels in its L2.
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int tiles_m = gridDim.x / tiles_o;
+  const int ntiles = (int)gridDim.x / splits;
+  const int lin = xcd_tile(blockIdx.x, gridDim.x);
+  const int sidx = lin / ntiles;  // contraction split (split-major order)
+  const int tile = lin - sidx * ntiles;
+  const int tiles_m = ntiles / tiles_o;
   const int ob = (tiles_o + 1) / 2;
   const int band = tile / (ob * tiles_m), within = tile - band * ob * tiles_m;
   const int obw = min(ob, tiles_o - band * ob);  // the last band may be narrower
@@ -150,15 +203,19 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   const int64_t o0 = (int64_t)to * TO, m0 = (int64_t)(within / obw) * TM;
   const int64_t N = w.n, K = w.k;
   const int64_t NO = kBwd ? K : N, NC = kBwd ? N : K;  // output width, contraction length
-  const int64_t nk = NC / kBlock;                      // 64-wide steps
-  const int64_t nsup = kBwd ? tile_bwd_nsup(N) : tile_fwd_nsup(K);
+  const int64_t ks0 = (int64_t)sidx * lsteps;                // first step of this split
+  const int64_t nk = min<int64_t>(NC / kBlock - ks0, lsteps);  // 64-wide steps of this split
+  const int64_t nsup_all = kBwd ? tile_bwd_nsup(N) : tile_fwd_nsup(K);
+  const int64_t nsup = ceil_div_d(nk, kSup);  // super-steps of this split (ks0 % 8 == 0)
   const int64_t nk8 = ceil_div_d(nk, 8) * 8;  // steps run: whole 8-step rounds
+  const int RPe = sidx == 0 ? RP : 0;         // the LoRA term goes into split 0 only
   fill_pair_table(s_pair, tid, 256, w.codebook);
 
   // B rows m0 .. m0+255 (row stride NC): wave-instruction i fills LDS chunks
   // [512w + 64i, +64): row 64w + 8i + lane/8, physical chunk lane & 7, so the
   // logical chunk it copies depends on the parity of i.
-  const int bbytes = (int)(min<int64_t>(TM, M - m0) * NC * 2);
+  // (this split's contraction columns start ks0 * 64 elements into each row)
+  const int bbytes = (int)(min<int64_t>(TM, M - m0) * NC * 2 - ks0 * 128);
   uint32_t bv[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par)
@@ -166,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   // Instruction i (0..7) of the B-tile copy of step kt.
   auto bload = [&](int64_t kt, auto D, int i) {
     uint16_t *dst = decltype(D)::value ? Bs1 : Bs0;
-    const __amdgpu_buffer_rsrc_t rs = rsrc(Bact + m0 * NC, kt < nk ? bbytes : 0);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(Bact + m0 * NC + ks0 * 64, kt < nk ? bbytes : 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
                                              bv[i & 1] + (uint32_t)(i * 16 * NC), (int)(kt * 128), 0, 0);
   };
@@ -175,14 +232,14 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   // k).  Backward: row r = weight row 256sp + r, bytes o0/2 .. (the tile's
   // 256 columns k).  Scales: 4 KB per super-step, 1 KB per wave.
   const int64_t kb2 = K / 2;  // packed bytes per weight row
-  const uint8_t *wbase_g = kBwd ? w.packed : w.packed + o0 * kb2;
-  const int wbytes = (int)(kBwd ? N * kb2 : min<int64_t>(TO, N - o0) * kb2);
+  const uint8_t *wbase_g = kBwd ? w.packed + ks0 * 64 * kb2 : w.packed + o0 * kb2 + ks0 * 32;
+  const int wbytes = (int)(kBwd ? (N - ks0 * 64) * kb2 : min<int64_t>(TO, N - o0) * kb2 - ks0 * 32);
   uint32_t wv[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par)
     wv[par] = (uint32_t)((64 * wave + (lane >> 3)) * kb2 + (kBwd ? o0 / 2 : 0) +
                          16 * ((lane & 7) ^ (4 * par + (lane >> 4))));
-  const float *Spt = Sp + (int64_t)to * nsup * 256 * kSup;
+  const float *Spt = Sp + ((int64_t)to * nsup_all + ks0 / kSup) * 256 * kSup;
   // Instruction i (0..8) of the code and scale copy of super-step sp: eight
   // for the codes, the last for the scales.
   auto wload = [&](int64_t sp, auto D, int i) {
@@ -338,7 +395,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
         if (g & 1) la[rt][t] = u32x4_t{la[rt][t][2], la[rt][t][3], la[rt][t][0], la[rt][t][1]};
   };
   __syncthreads();  // pair table; Wc1 free
-  lora_loads(0);
+  if (RPe > 0) lora_loads(0);
 #pragma unroll
   for (int i = 0; i < 8; ++i) bload(0, std::integral_constant<int, 0>(), i);
 #pragma unroll
@@ -346,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
 #pragma unroll
   for (int i = 0; i < 8; ++i) bload(1, std::integral_constant<int, 1>(), i);
   {
-    for (int jc = 0; jc < RP; jc += 64) {
+    for (int jc = 0; jc < RPe; jc += 64) {
       if (jc == 0) {
         // the 8 + kVmemW + 8 copies issued after chunk 0's loads may stay in flight
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 + kVmemW + 8) : "memory");
@@ -461,6 +518,10 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   mfma_acc_fence();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if (splits > 1) {
+    store_partial(acc, part, (int64_t)sidx * ntiles + (m0 / TM) * tiles_o + to);
+    return;
+  }
   uint8_t *const bufs[4] = {reinterpret_cast<uint8_t *>(Bs0), reinterpret_cast<uint8_t *>(Bs1), Wc0, Wc1};
   store_tile(acc, bufs, out, NO, M, o0, m0, wave);
 }
@@ -473,22 +534,95 @@ size_t tile_scales_bytes(int64_t n, int64_t k) {
   return std::max(f, b) * sizeof(float);
 }
 
-bool bwd_tiles_supported(int64_t n, int64_t k) { return n % 64 == 0 && n * (k / 2) < (int64_t(1) << 31); }
+// n % 64 == 0 (whole 64-row steps), the packed weight below 2^31 bytes and a
+// 256-row dY tile (512 n bytes) below 2^31 bytes: 32-bit buffer offsets.
+bool bwd_tiles_supported(int64_t n, int64_t k) {
+  return n % 64 == 0 && n * (k / 2) < (int64_t(1) << 31) && 512 * n < (int64_t(1) << 31);
+}
+
+// Contraction splits of a tile launch.  Cost in units of one 64-wide step of
+// a tile (~1.6 us): rounds of 256 workgroups x (steps per split + ~4 for the
+// prologue and epilogue), plus, when split, the float32 partials written
+// and read back once (~8 MB per unit) and the reduction launch (~2 units).
+// Only launches with too few tiles to fill the 256 CUs gain; the others
+// stay at one split.
+TileSplit plan_tile_split(int64_t tiles, int64_t nk, int64_t M, int64_t NO) {
+  (void)M;
+  (void)NO;
+  TileSplit best;
+  best.splits = 1;
+  best.lsteps = (int)std::max<int64_t>(8, ceil_div(nk, 8) * 8);
+  if (nk <= 8 || tiles < 1) return best;  // nothing to split
+  auto cost = [&](int64_t S, int64_t L) {
+    const double rounds = (double)ceil_div(tiles * S, 256);
+    const double red = S > 1 ? 2.0 * S * tiles * 65536.0 * 4.0 / 8e6 + 2.0 : 0.0;
+    return rounds * (double)(L + 4) + red;
+  };
+  double bc = cost(1, best.lsteps);
+  for (int64_t want = 2; want <= 16; ++want) {
+    const int64_t L = ceil_div(ceil_div(nk, want), 8) * 8;
+    const int64_t S = ceil_div(nk, L);
+    if (S < 2) continue;
+    const double c = cost(S, L);
+    if (c < 0.97 * bc) {
+      bc = c;
+      best.splits = (int)S;
+      best.lsteps = (int)L;
+    }
+  }
+  return best;
+}
+
+TileSplit plan_fwd_tiles(int64_t M, int64_t n, int64_t k) {
+  return plan_tile_split(ceil_div(n, TO) * ceil_div(M, TM), k / kBlock, M, n);
+}
+
+TileSplit plan_dx_tiles(int64_t M, int64_t n, int64_t k) {
+  return plan_tile_split(ceil_div(k, TO) * ceil_div(M, TM), n / kBlock, M, k);
+}
+
+size_t tile_partial_bytes(int64_t M, int64_t n, int64_t k) {
+  const TileSplit f = plan_fwd_tiles(M, n, k);
+  const size_t pf = f.splits > 1 ? (size_t)f.splits * ceil_div(n, TO) * ceil_div(M, TM) * 65536 * 4 : 0;
+  size_t pb = 0;
+  if (bwd_tiles_supported(n, k)) {
+    const TileSplit b = plan_dx_tiles(M, n, k);
+    pb = b.splits > 1 ? (size_t)b.splits * ceil_div(k, TO) * ceil_div(M, TM) * 65536 * 4 : 0;
+  }
+  return std::max(pf, pb);
+}
+
+namespace {
+hipError_t reduce_splits(const char *name, const TileSplit &sp, int tiles_o, int tiles_m, int64_t M, int64_t NO,
+                         const float *tpart, uint16_t *out, hipStream_t s) {
+  const int ntiles = tiles_o * tiles_m;
+  QLORA_LAUNCH(name, k_split_reduce, dim3((unsigned)(ntiles * 64)), dim3(256), 0, s,
+               reinterpret_cast<const f32x4_t *>(tpart), sp.splits, ntiles, tiles_o, M, NO, out);
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, int64_t M, const uint16_t *Bl, int r,
-                            int RP, const uint16_t *sH, uint16_t *Y, hipStream_t s) {
+                            int RP, const uint16_t *sH, uint16_t *Y, float *tpart, hipStream_t s) {
   const int tiles_o = (int)ceil_div(w.n, TO), tiles_m = (int)ceil_div(M, TM);
-  QLORA_LAUNCH("k_fwd_nf4", k_nf4_tile<false>, dim3((unsigned)(tiles_o * tiles_m)), dim3(256), 0, s, w, scales, X,
-               M, Bl, r, RP, sH, Y, tiles_o);
-  return hipGetLastError();
+  const TileSplit sp = plan_fwd_tiles(M, w.n, w.k);
+  QLORA_LAUNCH("k_fwd_nf4", k_nf4_tile<false>, dim3((unsigned)(tiles_o * tiles_m * sp.splits)), dim3(256), 0, s, w,
+               scales, X, M, Bl, r, RP, sH, Y, tiles_o, sp.splits, sp.lsteps, reinterpret_cast<f32x4_t *>(tpart));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.splits == 1) return e;
+  return reduce_splits("k_split_reduce", sp, tiles_o, tiles_m, M, w.n, tpart, Y, s);
 }
 
 hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
-                               int RP, const uint16_t *Gb, uint16_t *dX, hipStream_t s) {
+                               int RP, const uint16_t *Gb, uint16_t *dX, float *tpart, hipStream_t s) {
   const int tiles_o = (int)ceil_div(w.k, TO), tiles_m = (int)ceil_div(M, TM);
-  QLORA_LAUNCH("k_bwd_dx_nf4", k_nf4_tile<true>, dim3((unsigned)(tiles_o * tiles_m)), dim3(256), 0, s, w, scales,
-               dY, M, At, RP, RP, Gb, dX, tiles_o);
-  return hipGetLastError();
+  const TileSplit sp = plan_dx_tiles(M, w.n, w.k);
+  QLORA_LAUNCH("k_bwd_dx_nf4", k_nf4_tile<true>, dim3((unsigned)(tiles_o * tiles_m * sp.splits)), dim3(256), 0, s,
+               w, scales, dY, M, At, RP, RP, Gb, dX, tiles_o, sp.splits, sp.lsteps,
+               reinterpret_cast<f32x4_t *>(tpart));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.splits == 1) return e;
+  return reduce_splits("k_split_reduce", sp, tiles_o, tiles_m, M, w.k, tpart, dX, s);
 }
 
 }  // namespace qlora

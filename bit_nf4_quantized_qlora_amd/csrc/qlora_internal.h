@@ -65,6 +65,15 @@ struct LinearArgs {
 };
 
 size_t fwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
+
+// The kernels a call of this shape runs (QLORA_PATH_*; splits of the tile
+// launches' contraction): the one decision the launches and
+// qlora_linear_plan share.
+struct LinearPlan {
+  int fwd_path = QLORA_PATH_NONE, fwd_splits = 1;
+  int dx_path = QLORA_PATH_NONE, dx_splits = 1;
+};
+LinearPlan plan_linear(int64_t M, int64_t n, int64_t k, int r, bool single_level);
 size_t bwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
 
 hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint16_t *A, const uint16_t *B,
@@ -73,7 +82,10 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
                              const uint16_t *B, const float *H, uint16_t *dX, uint16_t *dA, uint16_t *dB,
                              void *ws, hipStream_t s);
 
-// Opt-in per-kernel event timing (profile.hip): a scope around each launch.
+#ifdef QLORA_PROFILE
+// Per-kernel event timing, compiled into the separate tracing build
+// libqlora_prof.so only (profile.hip): a scope around each launch.  The
+// product library has no timer and no state behind it.
 class ProfScope {
  public:
   ProfScope(const char *name, hipStream_t s);
@@ -92,6 +104,10 @@ class ProfScope {
     ::qlora::ProfScope qlora_prof_scope_(name, stream);                        \
     hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);       \
   } while (0)
+#else
+#define QLORA_LAUNCH(name, kernel, grid, block, shmem, stream, ...) \
+  hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__)
+#endif
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

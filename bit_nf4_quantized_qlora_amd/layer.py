@@ -8,10 +8,12 @@ App. G), as an ordered sequence of libqlora calls.
 Normalisation and positional rotation are frozen maps without adapters and
 are not part of the layer here.  The backward recomputes from X the
 activations it needs (checkpointing at layer granularity: everything up to
-the SwiGLU output; the down projection's output and the final sum are not
-needed), then runs each
-projection's frozen-base backward (dX, dA, dB; no weight gradient), the
-attention and SwiGLU backwards and the residual gradient sums.
+the SwiGLU output, with the adapter products H = x A^T of q, k, v, o, gate
+and up; the down projection's output and the final sum are not needed, and
+the down projection's H is recomputed by its own backward call), then runs
+each projection's frozen-base backward (dX, dA, dB; no weight gradient),
+the attention and SwiGLU backwards and the residual gradient sums.  Nothing
+the backward reads is left over from an earlier forward call.
 
 This module holds buffers and orders calls; every step runs in the library's
 kernels on the current stream.
@@ -58,10 +60,17 @@ class DecoderLayer:
         A, B = self.ad[name]
         Q.qlora_linear_fwd(self.w[name], X, A, B, self.r, self.alpha, Y, self.H[name], self.ws)
 
-    def _bwd(self, name, X, dY, dX):
+    def _bwd(self, name, X, dY, dX, H="saved"):
         A, B = self.ad[name]
-        Q.qlora_linear_bwd(self.w[name], X, dY, A, B, self.r, self.alpha, self.H[name], dX, self.dA[name],
+        H = self.H[name] if H == "saved" else H
+        Q.qlora_linear_bwd(self.w[name], X, dY, A, B, self.r, self.alpha, H, dX, self.dA[name],
                            self.dB[name], self.ws)
+
+    def _check_io(self, **tensors) -> None:
+        hidden = self.heads * self.d
+        for name, t in tensors.items():
+            if tuple(t.shape) != (self.M, hidden) or t.dtype != torch.bfloat16:
+                raise ValueError(f"{name} must be bf16 [{self.M}, {hidden}], got {t.dtype} {tuple(t.shape)}")
 
     def _activations(self, X: torch.Tensor) -> None:
         """Everything up to h = swiglu(gate(Y1), up(Y1))."""
@@ -78,6 +87,7 @@ class DecoderLayer:
         Q.qlora_swiglu_fwd(a["gate"], a["up"], a["h"])
 
     def fwd(self, X: torch.Tensor, Y: torch.Tensor) -> None:
+        self._check_io(X=X, Y=Y)
         self._activations(X)
         a = self.act
         self._fwd("down", a["h"], a["down_out"])
@@ -85,9 +95,10 @@ class DecoderLayer:
 
     def bwd(self, X: torch.Tensor, dY: torch.Tensor, dX: torch.Tensor) -> None:
         """dX and self.dA / self.dB."""
+        self._check_io(X=X, dY=dY, dX=dX)
         a, g = self.act, self.grad
         self._activations(X)                                     # recompute what the backward reads
-        self._bwd("down", a["h"], dY, g["dh"])
+        self._bwd("down", a["h"], dY, g["dh"], H=None)          # H = h A^T recomputed by the call
         Q.qlora_swiglu_bwd(a["gate"], a["up"], g["dh"], g["dgate"], g["dup"])
         self._bwd("gate", a["y1"], g["dgate"], g["dxg"])
         self._bwd("up", a["y1"], g["dup"], g["dxu"])

@@ -2,9 +2,18 @@
 same names.  Argument marshalling only -- every step of the layer runs in
 the library's HIP kernels.  torch supplies device memory and the stream.
 
+Each wrapper checks, before the library is called, that every tensor is a
+contiguous device tensor of the dtype and shape the call reads or writes
+(ValueError / TypeError otherwise), so a mismatch never reaches a kernel as
+an out-of-bounds pointer.  A weight in the method's storage type (NF4 codes,
+double-quantized constants) goes through the plain calls with the six-field
+descriptor; the comparison storage types go through the ``*_ex`` calls.
+
 Importing this module loads ``libqlora.so`` and raises ImportError if it has
 not been built (``python -m bit_nf4_quantized_qlora_amd.build``); there is no
-fallback path.
+fallback path.  ``use_tracing_library(True)`` switches every call to the
+tracing build ``libqlora_prof.so`` (same kernels plus the per-kernel event
+timer of the ``qlora_profile_*`` calls).
 """
 from __future__ import annotations
 
@@ -17,9 +26,12 @@ from dataclasses import dataclass
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora.so")
+PROF_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqlora_prof.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built: run `python -m bit_nf4_quantized_qlora_amd.build`")
-_lib = ctypes.CDLL(LIB_PATH)
+_product = ctypes.CDLL(LIB_PATH)
+_tracing = None
+_lib = _product
 
 QLORA_OK = 0
 QLORA_ERR_NULL_ARG = -1
@@ -40,22 +52,43 @@ QLORA_SCALES_FP32 = 1         # one float32 absmax per block (double quantizatio
 _c_i64, _c_int, _c_float, _c_size, _vp = ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
 
+QLORA_PATH_NONE, QLORA_PATH_TILE, QLORA_PATH_GEMV, QLORA_PATH_GENERAL = 0, 1, 2, 3
+
+
 class qlora_nf4_weight(ctypes.Structure):
     _fields_ = [("n", _c_i64), ("k", _c_i64), ("packed", _vp), ("scale_code", _vp), ("group_amax", _vp),
-                ("offset", _vp), ("codebook", ctypes.c_int32), ("scales", ctypes.c_int32), ("absmax", _vp)]
+                ("offset", _vp)]
+
+
+class qlora_weight_ex(ctypes.Structure):
+    _fields_ = [("size", _c_size), ("base", qlora_nf4_weight), ("codebook", ctypes.c_int32),
+                ("scales", ctypes.c_int32), ("absmax", _vp)]
+
+
+class qlora_linear_plan_info(ctypes.Structure):
+    _fields_ = [("fwd_path", ctypes.c_int32), ("fwd_splits", ctypes.c_int32), ("dx_path", ctypes.c_int32),
+                ("dx_splits", ctypes.c_int32)]
 
 
 _W = ctypes.POINTER(qlora_nf4_weight)
+_WX = ctypes.POINTER(qlora_weight_ex)
 _SIGS = {
     "qlora_nf4_sizes": (_c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_size), ctypes.POINTER(_c_size),
                                  ctypes.POINTER(_c_size)]),
     "qlora_quantize_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
     "qlora_quantize_nf4_dq": (_c_int, [_vp, _W, _vp, _c_size, _vp]),
+    "qlora_quantize_ex": (_c_int, [_vp, _WX, _vp, _c_size, _vp]),
     "qlora_dequant_bf16": (_c_int, [_W, _vp, _vp]),
+    "qlora_dequant_bf16_ex": (_c_int, [_WX, _vp, _vp]),
     "qlora_linear_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int]),
     "qlora_linear_fwd": (_c_int, [_W, _vp, _c_i64, _vp, _vp, _c_int, _c_float, _vp, _vp, _vp, _c_size, _vp]),
     "qlora_linear_bwd": (_c_int, [_W, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_float, _vp, _vp, _vp, _vp, _vp,
                                   _c_size, _vp]),
+    "qlora_linear_fwd_ex": (_c_int, [_WX, _vp, _c_i64, _vp, _vp, _c_int, _c_float, _vp, _vp, _vp, _c_size, _vp]),
+    "qlora_linear_bwd_ex": (_c_int, [_WX, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_float, _vp, _vp, _vp, _vp, _vp,
+                                     _c_size, _vp]),
+    "qlora_linear_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_int, ctypes.c_int32,
+                                   ctypes.POINTER(qlora_linear_plan_info)]),
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_nf4_thresholds": (None, [ctypes.POINTER(ctypes.c_float)]),
     "qlora_codebook": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
@@ -69,19 +102,39 @@ _SIGS = {
     "qlora_add_bf16": (_c_int, [_vp, _vp, _vp, _c_i64, _vp]),
     "qlora_adamw_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_float, _c_float, _c_float, _c_float, _c_float,
                                   _c_i64, _vp]),
-    "qlora_merge_adapters": (_c_int, [_W, _vp, _vp, _c_int, _c_float, _vp, _W, _vp, _c_size, _vp]),
+    "qlora_merge_adapters": (_c_int, [_WX, _vp, _vp, _c_int, _c_float, _vp, _WX, _vp, _c_size, _vp]),
     "qlora_thresholds": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_float)]),
     "qlora_strerror": (ctypes.c_char_p, [_c_int]),
+    "qlora_last_error": (ctypes.c_char_p, []),
+}
+_PROF_SIGS = {
     "qlora_profile_begin": (_c_int, []),
     "qlora_profile_end": (_c_int, []),
     "qlora_profile_count": (_c_int, []),
     "qlora_profile_entry": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_c_i64),
                                      ctypes.POINTER(ctypes.c_double)]),
-    "qlora_last_error": (ctypes.c_char_p, []),
 }
-for _name, (_res, _args) in _SIGS.items():
-    _f = getattr(_lib, _name)
-    _f.restype, _f.argtypes = _res, _args
+
+
+def _declare(lib, sigs):
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+
+
+_declare(_product, _SIGS)
+
+
+def use_tracing_library(on: bool) -> None:
+    """Route every call to libqlora_prof.so (on) or back to libqlora.so."""
+    global _lib, _tracing
+    if on and _tracing is None:
+        if not os.path.exists(PROF_LIB_PATH):
+            raise ImportError(f"{PROF_LIB_PATH} is not built")
+        _tracing = ctypes.CDLL(PROF_LIB_PATH)
+        _declare(_tracing, _SIGS)
+        _declare(_tracing, _PROF_SIGS)
+    _lib = _tracing if on else _product
 
 
 class QloraError(RuntimeError):
@@ -108,16 +161,33 @@ def _stream(stream):
     return _vp(s.cuda_stream)
 
 
-def _need(t, dtype, name):
+def _need(t, dtype, name, shape=None, numel=None):
+    """dtype, shape (or element count) and contiguity of one tensor the
+    library will read or write, checked before any call; the device is
+    checked by _on_gpu once every shape has passed."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, the call needs {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, the call needs {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if isinstance(t, torch.Tensor) and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
 
 
 @dataclass
 class NF4Weight:
-    """Device buffers of one quantized weight (torch tensors) and the C view.
-    Double-quantized constants use scale_code / group_amax / offset;
-    single-level ones (scales == QLORA_SCALES_FP32) use absmax only."""
+    """Device buffers of one quantized weight (torch tensors) and its C
+    descriptors.  Double-quantized constants use scale_code / group_amax /
+    offset; single-level ones (scales == QLORA_SCALES_FP32) use absmax only."""
     n: int
     k: int
     packed: torch.Tensor                     # uint8 [n*k/2]
@@ -140,10 +210,35 @@ class NF4Weight:
                          torch.empty(ng, dtype=torch.float32, device=device),
                          torch.empty(1, dtype=torch.float32, device=device), codebook, scales)
 
+    @property
+    def is_method_type(self) -> bool:
+        """NF4 codes with double-quantized constants: the plain calls' type."""
+        return self.codebook == QLORA_CODEBOOK_NF4 and self.scales == QLORA_SCALES_DQ
+
+    def buffers(self) -> dict:
+        return {"packed": self.packed, "scale_code": self.scale_code, "group_amax": self.group_amax,
+                "offset": self.offset, "absmax": self.absmax}
+
+    def check_buffers(self) -> None:
+        """Element counts and dtypes of the buffers the calls read (device: _on_gpu)."""
+        pb, sb, ng = qlora_nf4_sizes(self.n, self.k)
+        _need(self.packed, torch.uint8, "packed", numel=pb)
+        if self.scales == QLORA_SCALES_FP32:
+            _need(self.absmax, torch.float32, "absmax", numel=sb)
+        else:
+            _need(self.scale_code, torch.uint8, "scale_code", numel=sb)
+            _need(self.group_amax, torch.float32, "group_amax", numel=ng)
+            _need(self.offset, torch.float32, "offset", numel=1)
+
     def c_struct(self) -> qlora_nf4_weight:
         p = lambda t: None if t is None else t.data_ptr()
         return qlora_nf4_weight(self.n, self.k, p(self.packed), p(self.scale_code), p(self.group_amax),
-                                p(self.offset), self.codebook, self.scales, p(self.absmax))
+                                p(self.offset))
+
+    def c_ex(self) -> qlora_weight_ex:
+        p = lambda t: None if t is None else t.data_ptr()
+        return qlora_weight_ex(ctypes.sizeof(qlora_weight_ex), self.c_struct(), self.codebook, self.scales,
+                               p(self.absmax))
 
 
 def qlora_nf4_sizes(n: int, k: int):
@@ -156,76 +251,125 @@ def qlora_quantize_workspace_bytes(n: int, k: int) -> int:
     return _lib.qlora_quantize_workspace_bytes(n, k)
 
 
+def _ws_args(ws):
+    if ws is None:
+        return None, 0
+    _need(ws, torch.uint8, "ws")
+    _on_gpu(ws=ws)
+    return _ptr(ws), ws.numel()
+
+
 def qlora_quantize_nf4_dq(W: torch.Tensor, out: NF4Weight, ws: torch.Tensor, stream=None) -> None:
-    _need(W, torch.float32, "W")
-    st = out.c_struct()
-    _check("qlora_quantize_nf4_dq",
-           _lib.qlora_quantize_nf4_dq(_ptr(W), ctypes.byref(st), _ptr(ws), ws.numel() * ws.element_size(),
-                                      _stream(stream)))
+    """Quantize W [n, k] float32 into `out` (any storage type: the _ex call
+    when it is not NF4 with double-quantized constants)."""
+    _need(W, torch.float32, "W", shape=(out.n, out.k))
+    out.check_buffers()
+    _on_gpu(W=W, **out.buffers())
+    wp, wb = _ws_args(ws)
+    if out.is_method_type:
+        st = out.c_struct()
+        _check("qlora_quantize_nf4_dq", _lib.qlora_quantize_nf4_dq(_ptr(W), ctypes.byref(st), wp, wb, _stream(stream)))
+    else:
+        st = out.c_ex()
+        _check("qlora_quantize_ex", _lib.qlora_quantize_ex(_ptr(W), ctypes.byref(st), wp, wb, _stream(stream)))
 
 
 def qlora_dequant_bf16(w: NF4Weight, W_bf16: torch.Tensor, stream=None) -> None:
-    _need(W_bf16, torch.bfloat16, "W_bf16")
-    st = w.c_struct()
-    _check("qlora_dequant_bf16", _lib.qlora_dequant_bf16(ctypes.byref(st), _ptr(W_bf16), _stream(stream)))
+    _need(W_bf16, torch.bfloat16, "W_bf16", numel=w.n * w.k)
+    w.check_buffers()
+    _on_gpu(W_bf16=W_bf16, **w.buffers())
+    if w.is_method_type:
+        st = w.c_struct()
+        _check("qlora_dequant_bf16", _lib.qlora_dequant_bf16(ctypes.byref(st), _ptr(W_bf16), _stream(stream)))
+    else:
+        st = w.c_ex()
+        _check("qlora_dequant_bf16_ex", _lib.qlora_dequant_bf16_ex(ctypes.byref(st), _ptr(W_bf16), _stream(stream)))
 
 
 def qlora_linear_workspace_bytes(M: int, n: int, k: int, r: int) -> int:
     return _lib.qlora_linear_workspace_bytes(M, n, k, r)
 
 
-def _ws_args(ws):
-    if ws is None:
-        return None, 0
-    return _ptr(ws), ws.numel() * ws.element_size()
+def qlora_linear_plan(M: int, n: int, k: int, r: int, scales: int = QLORA_SCALES_DQ) -> dict:
+    """The kernels a call of this shape runs (host only)."""
+    info = qlora_linear_plan_info()
+    _check("qlora_linear_plan", _lib.qlora_linear_plan(M, n, k, r, scales, ctypes.byref(info)))
+    return {"fwd_path": info.fwd_path, "fwd_splits": info.fwd_splits, "dx_path": info.dx_path,
+            "dx_splits": info.dx_splits}
 
 
 def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, r: int, alpha: float,
                      Y: torch.Tensor, H_out: torch.Tensor | None, ws: torch.Tensor | None, stream=None) -> None:
-    for t, nm in ((X, "X"), (A, "A"), (B, "B"), (Y, "Y")):
-        _need(t, torch.bfloat16, nm)
+    if X.dim() != 2:
+        raise ValueError(f"X must be [M, {w.k}], got shape {tuple(X.shape)}")
+    M = X.shape[0]
+    _need(X, torch.bfloat16, "X", shape=(M, w.k))
+    _need(A, torch.bfloat16, "A", shape=(r, w.k))
+    _need(B, torch.bfloat16, "B", shape=(w.n, r))
+    _need(Y, torch.bfloat16, "Y", shape=(M, w.n))
     if H_out is not None:
-        _need(H_out, torch.float32, "H_out")
-    st = w.c_struct()
+        _need(H_out, torch.float32, "H_out", shape=(M, r))
+    w.check_buffers()
+    _on_gpu(X=X, A=A, B=B, Y=Y, H_out=H_out, **w.buffers())
     wp, wb = _ws_args(ws)
-    _check("qlora_linear_fwd",
-           _lib.qlora_linear_fwd(ctypes.byref(st), _ptr(X), X.shape[0], _ptr(A), _ptr(B), r, alpha, _ptr(Y),
-                                 _ptr(H_out), wp, wb, _stream(stream)))
+    if w.is_method_type:
+        st, fn, name = w.c_struct(), _lib.qlora_linear_fwd, "qlora_linear_fwd"
+    else:
+        st, fn, name = w.c_ex(), _lib.qlora_linear_fwd_ex, "qlora_linear_fwd_ex"
+    _check(name, fn(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, alpha, _ptr(Y), _ptr(H_out), wp, wb,
+                    _stream(stream)))
 
 
 def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor, B: torch.Tensor, r: int,
                      alpha: float, H: torch.Tensor | None, dX: torch.Tensor | None, dA: torch.Tensor,
                      dB: torch.Tensor, ws: torch.Tensor | None, stream=None) -> None:
-    for t, nm in ((X, "X"), (dY, "dY"), (A, "A"), (B, "B"), (dA, "dA"), (dB, "dB")):
-        _need(t, torch.bfloat16, nm)
+    if X.dim() != 2:
+        raise ValueError(f"X must be [M, {w.k}], got shape {tuple(X.shape)}")
+    M = X.shape[0]
+    _need(X, torch.bfloat16, "X", shape=(M, w.k))
+    _need(dY, torch.bfloat16, "dY", shape=(M, w.n))
+    _need(A, torch.bfloat16, "A", shape=(r, w.k))
+    _need(B, torch.bfloat16, "B", shape=(w.n, r))
+    _need(dA, torch.bfloat16, "dA", shape=(r, w.k))
+    _need(dB, torch.bfloat16, "dB", shape=(w.n, r))
     if dX is not None:
-        _need(dX, torch.bfloat16, "dX")
+        _need(dX, torch.bfloat16, "dX", shape=(M, w.k))
     if H is not None:
-        _need(H, torch.float32, "H")
-    st = w.c_struct()
+        _need(H, torch.float32, "H", shape=(M, r))
+    w.check_buffers()
+    _on_gpu(X=X, dY=dY, A=A, B=B, dA=dA, dB=dB, dX=dX, H=H, **w.buffers())
     wp, wb = _ws_args(ws)
-    _check("qlora_linear_bwd",
-           _lib.qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), X.shape[0], _ptr(A), _ptr(B), r, alpha,
-                                 _ptr(H), _ptr(dX), _ptr(dA), _ptr(dB), wp, wb, _stream(stream)))
+    if w.is_method_type:
+        st, fn, name = w.c_struct(), _lib.qlora_linear_bwd, "qlora_linear_bwd"
+    else:
+        st, fn, name = w.c_ex(), _lib.qlora_linear_bwd_ex, "qlora_linear_bwd_ex"
+    _check(name, fn(ctypes.byref(st), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, alpha, _ptr(H), _ptr(dX),
+                    _ptr(dA), _ptr(dB), wp, wb, _stream(stream)))
+
+
+def _same_numel(name0, t0, *others):
+    for t, nm in others:
+        _need(t, torch.bfloat16, nm, numel=t0.numel())
+    _on_gpu(**{name0: t0}, **{nm: t for t, nm in others})
 
 
 def qlora_swiglu_fwd(gate: torch.Tensor, up: torch.Tensor, h: torch.Tensor, stream=None) -> None:
-    for t, nm in ((gate, "gate"), (up, "up"), (h, "h")):
-        _need(t, torch.bfloat16, nm)
+    _need(gate, torch.bfloat16, "gate")
+    _same_numel("gate", gate, (up, "up"), (h, "h"))
     _check("qlora_swiglu_fwd", _lib.qlora_swiglu_fwd(_ptr(gate), _ptr(up), _ptr(h), gate.numel(), _stream(stream)))
 
 
 def qlora_swiglu_bwd(gate: torch.Tensor, up: torch.Tensor, dh: torch.Tensor, d_gate: torch.Tensor,
                      d_up: torch.Tensor, stream=None) -> None:
-    for t, nm in ((gate, "gate"), (up, "up"), (dh, "dh"), (d_gate, "d_gate"), (d_up, "d_up")):
-        _need(t, torch.bfloat16, nm)
+    _need(gate, torch.bfloat16, "gate")
+    _same_numel("gate", gate, (up, "up"), (dh, "dh"), (d_gate, "d_gate"), (d_up, "d_up"))
     _check("qlora_swiglu_bwd", _lib.qlora_swiglu_bwd(_ptr(gate), _ptr(up), _ptr(dh), _ptr(d_gate), _ptr(d_up),
                                                      gate.numel(), _stream(stream)))
 
 
 def qlora_add_bf16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor, stream=None) -> None:
-    for t, nm in ((a, "a"), (b, "b"), (out, "out")):
-        _need(t, torch.bfloat16, nm)
+    _need(a, torch.bfloat16, "a")
+    _same_numel("a", a, (b, "b"), (out, "out"))
     _check("qlora_add_bf16", _lib.qlora_add_bf16(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
 
 
@@ -236,9 +380,11 @@ def qlora_attention_workspace_bytes(batch: int, seq: int, heads: int, head_dim: 
 def qlora_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
                         batch: int, seq: int, heads: int, head_dim: int, ws: torch.Tensor, stream=None) -> None:
     """q, k, v, o: bf16 [batch*seq, heads*head_dim]; lse: float32 [batch, heads, seq]."""
+    shape = (batch * seq, heads * head_dim)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o")):
-        _need(t, torch.bfloat16, nm)
-    _need(lse, torch.float32, "lse")
+        _need(t, torch.bfloat16, nm, shape=shape)
+    _need(lse, torch.float32, "lse", numel=batch * heads * seq)
+    _on_gpu(q=q, k=k, v=v, o=o, lse=lse)
     w, wb = _ws_args(ws)
     _check("qlora_attention_fwd",
            _lib.qlora_attention_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), batch, seq, heads, head_dim, w, wb,
@@ -248,9 +394,11 @@ def qlora_attention_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: to
 def qlora_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: torch.Tensor, lse: torch.Tensor,
                         dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor, batch: int, seq: int,
                         heads: int, head_dim: int, ws: torch.Tensor, stream=None) -> None:
+    shape = (batch * seq, heads * head_dim)
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _need(t, torch.bfloat16, nm)
-    _need(lse, torch.float32, "lse")
+        _need(t, torch.bfloat16, nm, shape=shape)
+    _need(lse, torch.float32, "lse", numel=batch * heads * seq)
+    _on_gpu(q=q, k=k, v=v, d_o=d_o, lse=lse, dq=dq, dk=dk, dv=dv)
     w, wb = _ws_args(ws)
     _check("qlora_attention_bwd",
            _lib.qlora_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
@@ -260,15 +408,20 @@ def qlora_attention_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, d_o: 
 def qlora_adamw_step(param: torch.Tensor, param_bf16: torch.Tensor | None, grad: torch.Tensor, m, v, lr: float,
                      beta1: float, beta2: float, eps: float, weight_decay: float, step: int, stream=None) -> None:
     """m and v: device tensors, or (paged layout) integer device addresses of
-    mapped host memory, as ints."""
+    mapped host memory holding param.numel() float32 values each."""
     _need(param, torch.float32, "param")
-    _need(grad, torch.bfloat16, "grad")
+    count = param.numel()
+    _need(grad, torch.bfloat16, "grad", numel=count)
     if param_bf16 is not None:
-        _need(param_bf16, torch.bfloat16, "param_bf16")
+        _need(param_bf16, torch.bfloat16, "param_bf16", numel=count)
+    for t, nm in ((m, "m"), (v, "v")):
+        if not isinstance(t, int):
+            _need(t, torch.float32, nm, numel=count)
+    _on_gpu(param=param, grad=grad, param_bf16=param_bf16, m=m, v=v)
     mp = _vp(m) if isinstance(m, int) else _ptr(m)
     vp = _vp(v) if isinstance(v, int) else _ptr(v)
     _check("qlora_adamw_step",
-           _lib.qlora_adamw_step(_ptr(param), _ptr(param_bf16), _ptr(grad), mp, vp, param.numel(), lr, beta1, beta2,
+           _lib.qlora_adamw_step(_ptr(param), _ptr(param_bf16), _ptr(grad), mp, vp, count, lr, beta1, beta2,
                                  eps, weight_decay, step, _stream(stream)))
 
 
@@ -278,12 +431,19 @@ def qlora_merge_workspace_bytes(n: int, k: int) -> int:
 
 def qlora_merge_adapters(w: NF4Weight, A: torch.Tensor, B: torch.Tensor, r: int, alpha: float,
                          W_merged: torch.Tensor | None, out: NF4Weight | None, ws: torch.Tensor, stream=None) -> None:
-    for t, nm in ((A, "A"), (B, "B")):
-        _need(t, torch.bfloat16, nm)
+    _need(A, torch.bfloat16, "A", shape=(r, w.k))
+    _need(B, torch.bfloat16, "B", shape=(w.n, r))
     if W_merged is not None:
-        _need(W_merged, torch.bfloat16, "W_merged")
-    st = w.c_struct()
-    ost = out.c_struct() if out is not None else None
+        _need(W_merged, torch.bfloat16, "W_merged", numel=w.n * w.k)
+    w.check_buffers()
+    if out is not None:
+        if (out.n, out.k) != (w.n, w.k):
+            raise ValueError(f"out is [{out.n}, {out.k}], the weight is [{w.n}, {w.k}]")
+        out.check_buffers()
+        _on_gpu(**{"out_" + k: v for k, v in out.buffers().items()})
+    _on_gpu(A=A, B=B, W_merged=W_merged, **w.buffers())
+    st = w.c_ex()
+    ost = out.c_ex() if out is not None else None
     wp, wb = _ws_args(ws)
     _check("qlora_merge_adapters",
            _lib.qlora_merge_adapters(ctypes.byref(st), _ptr(A), _ptr(B), r, alpha, _ptr(W_merged),
@@ -323,6 +483,9 @@ def qlora_last_error() -> str:
 
 
 def qlora_profile_begin() -> None:
+    """Start the per-kernel event timer (tracing library only)."""
+    if _lib is not _tracing:
+        raise RuntimeError("the event timer lives in libqlora_prof.so: call use_tracing_library(True) first")
     _check("qlora_profile_begin", _lib.qlora_profile_begin())
 
 
@@ -339,5 +502,5 @@ def qlora_profile_end() -> dict:
 
 
 def raw_library() -> ctypes.CDLL:
-    """The loaded ctypes library (used by the symbol-export check)."""
-    return _lib
+    """The product library (used by the symbol-export check)."""
+    return _product

@@ -35,6 +35,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* HIP's stream handle, declared exactly as the HIP runtime header declares it
+ * (an identical typedef may be repeated), so this header needs no HIP include. */
+typedef struct ihipStream_t *hipStream_t;
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -80,11 +84,14 @@ enum {
 };
 
 /*
- * A quantized frozen weight W [n, k] ("QLoRA, explained.", symbol list: W^NF4
- * plus the per-block and per-group constants; "QLoRA Paper Breakdown" sec. 3).
- * Block b = 64 consecutive elements of row-major W (so k % 64 == 0 keeps a
- * block inside one row); group g = 256 consecutive blocks; nb = n*k/64,
- * ng = ceil(nb/256).  All buffers are device memory owned by the caller.
+ * A quantized frozen weight W [n, k] in the method's own storage type: NF4
+ * codes with double-quantized block constants ("QLoRA, explained.", symbol
+ * list: W^NF4 plus the per-block and per-group constants; "QLoRA Paper
+ * Breakdown" sec. 3).  Block b = 64 consecutive elements of row-major W (so
+ * k % 64 == 0 keeps a block inside one row); group g = 256 consecutive
+ * blocks; nb = n*k/64, ng = ceil(nb/256).  All buffers are device memory
+ * owned by the caller.  The four calls of the layer (quantize, dequantize,
+ * forward, backward) take this descriptor.
  */
 typedef struct qlora_nf4_weight {
   int64_t n, k;
@@ -92,10 +99,24 @@ typedef struct qlora_nf4_weight {
   uint8_t *scale_code;  /* [nb] OCP E4M3FN code of (absmax_b - offset) / group_amax_g   */
   float *group_amax;    /* [ng] second-level constant: max |absmax_b - offset| in g     */
   float *offset;        /* [1] per-tensor mean of the fp32 block absmax values          */
-  int32_t codebook;     /* QLORA_CODEBOOK_NF4 (0: a zero-filled descriptor) or _FP4_E2M1 */
-  int32_t scales;       /* QLORA_SCALES_DQ (0) or QLORA_SCALES_FP32                     */
-  float *absmax;        /* [nb] block absmax, QLORA_SCALES_FP32 only                    */
 } qlora_nf4_weight;
+
+/*
+ * Extended descriptor: the same weight in any storage type (codebook x
+ * block constants above).  `size` must be set to sizeof(qlora_weight_ex) as
+ * the caller compiled it; a smaller value is QLORA_ERR_BAD_CODEBOOK, so
+ * fields appended later are never read from an older caller's struct.
+ * codebook = QLORA_CODEBOOK_NF4 with scales = QLORA_SCALES_DQ is exactly
+ * `base` passed to the plain calls.  With QLORA_SCALES_FP32 only base.n,
+ * base.k, base.packed and `absmax` are read.
+ */
+typedef struct qlora_weight_ex {
+  size_t size;            /* sizeof(qlora_weight_ex)                                   */
+  qlora_nf4_weight base;  /* shape, codes and (QLORA_SCALES_DQ) the DQ constants       */
+  int32_t codebook;       /* QLORA_CODEBOOK_NF4 or QLORA_CODEBOOK_FP4_E2M1             */
+  int32_t scales;         /* QLORA_SCALES_DQ or QLORA_SCALES_FP32                      */
+  float *absmax;          /* [nb] block absmax, QLORA_SCALES_FP32 only                 */
+} qlora_weight_ex;
 
 /* Sizes of the four buffers of an [n, k] weight.  Host only; no GPU use.
  * Returns QLORA_ERR_BAD_SHAPE unless n >= 1, k >= 64 and k % 64 == 0. */
@@ -112,29 +133,32 @@ size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
  * "QLoRA, explained." steps 1-3; "QLoRA Paper Breakdown" sec. 3 Level 1 and
  * Level 2:
  *   absmax_b = max |w| over block b;  x = fp32(w / absmax_b) (0 if absmax_b=0)
- *   code = index of the nearest level of w->codebook (NF4, or Float4 E2M1;
- *          ties to the lower index)
+ *   code = index of the nearest NF4 level (ties to the lower index)
  *   offset = fp32( (sum over groups, in order, of the fp64 in-order sum of the
  *            group's absmax) / nb )
  *   dev_b = fp32(absmax_b - offset); group_amax_g = max |dev_b| over g
  *   scale_code_b = E4M3FN round-to-nearest-even of fp32(dev_b / group_amax_g)
  *                  (0x00 when group_amax_g == 0)
- * With out->scales == QLORA_SCALES_FP32 the second level is skipped and
- * absmax_b is stored in out->absmax.
  * The result is bit-for-bit deterministic.  `ws` >= qlora_quantize_workspace_bytes.
  */
 int qlora_quantize_nf4_dq(const float *W, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
-                          void *stream);
+                          hipStream_t stream);
+/* The same for any storage type: the nearest level of out->codebook, and with
+ * out->scales == QLORA_SCALES_FP32 the second level skipped and absmax_b
+ * stored in out->absmax. */
+int qlora_quantize_ex(const float *W, const qlora_weight_ex *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Dequantize to bfloat16: W_bf16 [n, k] (device).  "QLoRA Paper Breakdown"
  * sec. 4 Dequantization Helper; "QLoRA, explained." step 4:
  *   s_b = fp32( fp32(decode(scale_code_b) * group_amax_g) + offset )
- *         (s_b = absmax_b for QLORA_SCALES_FP32)
- *   w_hat = bf16_round_nearest_even( fp32(q[code] * s_b) ), q = w->codebook's levels
+ *   w_hat = bf16_round_nearest_even( fp32(q[code] * s_b) ), q = the NF4 levels
  * Bit-for-bit identical to the operand the fused linear kernels use.
  */
-int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, void *stream);
+int qlora_dequant_bf16(const qlora_nf4_weight *w, uint16_t *W_bf16, hipStream_t stream);
+/* The same for any storage type: q = w->codebook's levels; s_b = absmax_b
+ * for QLORA_SCALES_FP32. */
+int qlora_dequant_bf16_ex(const qlora_weight_ex *w, uint16_t *W_bf16, hipStream_t stream);
 
 /* Workspace (device bytes) for qlora_linear_fwd / qlora_linear_bwd at these
  * sizes (the larger of the two).  0 for an invalid shape or rank. */
@@ -151,7 +175,10 @@ size_t qlora_linear_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
  */
 int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
                      const uint16_t *B, int r, float alpha, uint16_t *Y, float *H_out, void *ws,
-                     size_t ws_bytes, void *stream);
+                     size_t ws_bytes, hipStream_t stream);
+int qlora_linear_fwd_ex(const qlora_weight_ex *w, const uint16_t *X, int64_t M, const uint16_t *A,
+                        const uint16_t *B, int r, float alpha, uint16_t *Y, float *H_out, void *ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 /*
  * Backward pass ("QLoRA Paper Breakdown" sec. 4: dY/dX through the
@@ -167,7 +194,34 @@ int qlora_linear_fwd(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, co
 int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_t *dY, int64_t M,
                      const uint16_t *A, const uint16_t *B, int r, float alpha, const float *H,
                      uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes,
-                     void *stream);
+                     hipStream_t stream);
+int qlora_linear_bwd_ex(const qlora_weight_ex *w, const uint16_t *X, const uint16_t *dY, int64_t M,
+                        const uint16_t *A, const uint16_t *B, int r, float alpha, const float *H,
+                        uint16_t *dX, uint16_t *dA, uint16_t *dB, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * Which kernels a forward / backward call of this shape runs (host only, no
+ * GPU use; the same decision the calls take).  Lets a caller or a test see
+ * the path a shape takes:
+ *   QLORA_PATH_TILE     256 x 256 output tiles with the weights expanded
+ *                       into MFMA operands; `*_splits` > 1 when the
+ *                       contraction is cut into that many equal ranges whose
+ *                       float32 partial tiles are then summed in split order
+ *                       (shapes with too few tiles to fill the GPU);
+ *   QLORA_PATH_GEMV     forward only, 1 <= M <= 16 with double-quantized
+ *                       constants: one bandwidth-bound pass over the weight;
+ *   QLORA_PATH_GENERAL  input gradient only: the general kernel (n % 64 != 0,
+ *                       or n * 512 at or above 2^31);
+ *   QLORA_PATH_NONE     M == 0.
+ * QLORA_OK, or the same argument errors as the calls.
+ */
+enum { QLORA_PATH_NONE = 0, QLORA_PATH_TILE = 1, QLORA_PATH_GEMV = 2, QLORA_PATH_GENERAL = 3 };
+typedef struct qlora_linear_plan_info {
+  int32_t fwd_path, fwd_splits;
+  int32_t dx_path, dx_splits;
+} qlora_linear_plan_info;
+int qlora_linear_plan(int64_t M, int64_t n, int64_t k, int r, int32_t scales, qlora_linear_plan_info *out);
 
 /*
  * Fold trained adapters into the base for deployment ("QLoRA Paper
@@ -179,14 +233,15 @@ int qlora_linear_bwd(const qlora_nf4_weight *w, const uint16_t *X, const uint16_
  * with every float64 operation separately rounded.  Then
  *   W_merged [n, k] bf16 = bf16_round_nearest_even(W')   when W_merged != NULL;
  *   `out` (same n, k; its codebook and scales chosen by the caller) = the
- *   encoding of W' exactly as qlora_quantize_nf4_dq would give   when out != NULL.
+ *   encoding of W' exactly as qlora_quantize_ex would give   when out != NULL.
+ * Both descriptors are extended ones (any storage type on either side).
  * A [r, k] and B [n, r] bf16 as in the forward pass.  W' itself is left in
  * the first n*k*4 bytes of `ws`, which needs qlora_merge_workspace_bytes.
  */
 size_t qlora_merge_workspace_bytes(int64_t n, int64_t k);
-int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uint16_t *B, int r, float alpha,
-                         uint16_t *W_merged, const qlora_nf4_weight *out, void *ws, size_t ws_bytes,
-                         void *stream);
+int qlora_merge_adapters(const qlora_weight_ex *w, const uint16_t *A, const uint16_t *B, int r, float alpha,
+                         uint16_t *W_merged, const qlora_weight_ex *out, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
 
 /*
  * The elementwise pieces of the MLP block the adapted linears sit in (the
@@ -201,10 +256,10 @@ int qlora_merge_adapters(const qlora_nf4_weight *w, const uint16_t *A, const uin
  * recompute the gate and up outputs from X (checkpointing) instead of
  * keeping them.
  */
-int qlora_swiglu_fwd(const uint16_t *gate, const uint16_t *up, uint16_t *h, int64_t count, void *stream);
+int qlora_swiglu_fwd(const uint16_t *gate, const uint16_t *up, uint16_t *h, int64_t count, hipStream_t stream);
 int qlora_swiglu_bwd(const uint16_t *gate, const uint16_t *up, const uint16_t *dh, uint16_t *d_gate, uint16_t *d_up,
-                     int64_t count, void *stream);
-int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t count, void *stream);
+                     int64_t count, hipStream_t stream);
+int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t count, hipStream_t stream);
 
 /*
  * The causal attention core between the q/k/v and o projections of the
@@ -236,11 +291,11 @@ int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t 
 size_t qlora_attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t head_dim);
 int qlora_attention_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, uint16_t *o, float *lse,
                         int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
-                        void *stream);
+                        hipStream_t stream);
 int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *d_o, const float *lse,
                         uint16_t *dq, uint16_t *dk, uint16_t *dv,
                         int64_t batch, int64_t seq, int64_t heads, int64_t head_dim, void *ws, size_t ws_bytes,
-                        void *stream);
+                        hipStream_t stream);
 
 /*
  * One AdamW step on an adapter tensor ("QLoRA Paper Breakdown" sec. 5, the
@@ -260,7 +315,7 @@ int qlora_attention_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * host link.  QLORA_ERR_BAD_ALPHA for hyperparameters out of range.
  */
 int qlora_adamw_step(float *param, uint16_t *param_bf16, const uint16_t *grad, float *m, float *v, int64_t count,
-                     float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step, void *stream);
+                     float lr, float beta1, float beta2, float eps, float weight_decay, int64_t step, hipStream_t stream);
 
 /* Host copies of the library's constants (host memory, no GPU use):
  * the 16 NF4 levels ("QLoRA Paper Breakdown" sec. 2) and the 15 float32

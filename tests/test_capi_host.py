@@ -15,10 +15,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
            if h.endswith(".h")]
 LIB = os.path.join(ROOT, "bit_nf4_quantized_qlora_amd", "libqlora.so")
+PROF_LIB = os.path.join(ROOT, "bit_nf4_quantized_qlora_amd", "libqlora_prof.so")
 
 
 def _ensure_built():
-    if not os.path.exists(LIB):
+    if not (os.path.exists(LIB) and os.path.exists(PROF_LIB)):
         from bit_nf4_quantized_qlora_amd import build
         build.build()
 
@@ -30,8 +31,9 @@ def q():
     return qlora
 
 
-def _declared_functions():
-    text = "".join(open(h).read() for h in HEADERS)
+def _declared_functions(headers=None):
+    headers = HEADERS if headers is None else [os.path.join(ROOT, "include", h) for h in headers]
+    text = "".join(open(h).read() for h in headers)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
 
@@ -43,13 +45,22 @@ def test_header_declares_the_four_calls():
 
 
 def test_every_declared_symbol_is_exported(q):
+    """libqlora.so exports exactly qlora.h; the tracing build exports that
+    plus the event timer of qlora_profile.h."""
+    product = set(_declared_functions(["qlora.h"]))
+    timer = set(_declared_functions(["qlora_profile.h"]))
+    assert product and timer and not (product & timer)
+    assert set(_declared_functions()) == product | timer
     lib = q.raw_library()
-    for name in _declared_functions():
+    for name in product:
         assert hasattr(lib, name), name
-    # and nothing C++-mangled leaks under a qlora_ name
-    out = os.popen(f"nm -D --defined-only {LIB}").read()
-    exported = set(re.findall(r"\bT (qlora_\w+)", out))
-    assert exported == set(_declared_functions())
+    for path, want in ((LIB, product), (PROF_LIB, product | timer)):
+        out = os.popen(f"nm -D --defined-only {path}").read()
+        assert set(re.findall(r"\bT (qlora_\w+)", out)) == want, path
+    # the product library keeps no event timer
+    assert not hasattr(lib, "qlora_profile_begin")
+    with pytest.raises(RuntimeError):
+        q.qlora_profile_begin()
 
 
 def test_library_codebook_equals_oracle(q):
@@ -95,6 +106,26 @@ def test_sizes_and_bits(q):
     assert e.value.status == q.QLORA_ERR_BAD_SHAPE
 
 
+def test_workspace_and_plan_over_many_shapes(q):
+    """Every size query and plan answers (host arithmetic only) over a sweep
+    of shapes, degenerate ones included; split plans stay consistent."""
+    ns = (1, 7, 63, 64, 65, 200, 256, 1000, 4096, 22016)
+    ks = (64, 128, 192, 320, 4096, 22016)
+    for n in ns:
+        for k in ks:
+            for m in (0, 1, 5, 16, 17, 256, 512, 4096):
+                for r in (1, 64, 128):
+                    nbytes = q.qlora_linear_workspace_bytes(m, n, k, r)
+                    assert (nbytes == 0) == (m == 0)
+                    p = q.qlora_linear_plan(m, n, k, r)
+                    if m == 0:
+                        assert p["fwd_path"] == q.QLORA_PATH_NONE
+                        continue
+                    assert p["fwd_splits"] >= 1 and p["dx_splits"] >= 1
+                    assert p["fwd_splits"] <= max(1, k // 64) and p["dx_splits"] <= max(1, n // 64)
+                    assert p["dx_path"] == (q.QLORA_PATH_TILE if n % 64 == 0 else q.QLORA_PATH_GENERAL)
+
+
 def test_workspace_queries(q):
     assert q.qlora_quantize_workspace_bytes(4096, 4096) >= 4096 * 4096 // 64 * 4
     assert q.qlora_quantize_workspace_bytes(4096, 100) == 0
@@ -102,6 +133,17 @@ def test_workspace_queries(q):
     assert q.qlora_linear_workspace_bytes(512, 4096, 4096, 0) == 0
     assert q.qlora_linear_workspace_bytes(512, 4096, 4096, 129) == 0
     assert q.qlora_linear_workspace_bytes(0, 4096, 4096, 64) == 0
+
+
+def _ex(q, base, codebook=0, scales=0, absmax=None, size=None):
+    return q.qlora_weight_ex(ctypes.sizeof(q.qlora_weight_ex) if size is None else size, base, codebook, scales,
+                             absmax)
+
+
+def test_descriptor_layouts(q):
+    """The six-field descriptor of the four calls and the extended one."""
+    assert ctypes.sizeof(q.qlora_nf4_weight) == 48
+    assert q.qlora_weight_ex.base.offset == 8 and ctypes.sizeof(q.qlora_weight_ex) == 72
 
 
 def test_argument_errors_enqueue_nothing(q):
@@ -131,12 +173,17 @@ def test_argument_errors_enqueue_nothing(q):
     assert bwd(ctypes.byref(W), P, P, 16, P, P, 8, 16.0, None, P, None, P, P, 1 << 30, None) == q.QLORA_ERR_NULL_ARG
     assert bwd(ctypes.byref(W), P, P, 16, P, P, 8, 16.0, None, P, P, P, P, 64, None) == q.QLORA_ERR_WORKSPACE
     assert "r = 0" in (fwd(ctypes.byref(W), P, 16, P, P, 0, 16.0, P, None, P, 1 << 30, None) and q.qlora_last_error())
-    bad_sc = q.qlora_nf4_weight(64, 64, 16, 16, 16, 16, 0, 2, 16)
-    assert lib.qlora_dequant_bf16(ctypes.byref(bad_sc), P, None) == q.QLORA_ERR_BAD_CODEBOOK
-    single_null = q.qlora_nf4_weight(64, 64, 16, None, None, None, 0, q.QLORA_SCALES_FP32, None)
-    assert lib.qlora_dequant_bf16(ctypes.byref(single_null), P, None) == q.QLORA_ERR_NULL_ARG
-    single = q.qlora_nf4_weight(64, 64, 16, None, None, None, 1, q.QLORA_SCALES_FP32, 16)  # DQ buffers unused
-    assert fwd(ctypes.byref(single), P, 16, P, P, 8, 16.0, P, None, P, 16, None) == q.QLORA_ERR_WORKSPACE
+    bad_sc = _ex(q, W, 0, 2, 16)
+    assert lib.qlora_dequant_bf16_ex(ctypes.byref(bad_sc), P, None) == q.QLORA_ERR_BAD_CODEBOOK
+    single_null = _ex(q, q.qlora_nf4_weight(64, 64, 16, None, None, None), 0, q.QLORA_SCALES_FP32, None)
+    assert lib.qlora_dequant_bf16_ex(ctypes.byref(single_null), P, None) == q.QLORA_ERR_NULL_ARG
+    single = _ex(q, q.qlora_nf4_weight(64, 64, 16, None, None, None), 1, q.QLORA_SCALES_FP32, 16)  # DQ bufs unused
+    fwd_ex = lib.qlora_linear_fwd_ex
+    assert fwd_ex(ctypes.byref(single), P, 16, P, P, 8, 16.0, P, None, P, 16, None) == q.QLORA_ERR_WORKSPACE
+    short = _ex(q, W, size=ctypes.sizeof(q.qlora_weight_ex) - 8)      # an older, shorter struct
+    assert lib.qlora_dequant_bf16_ex(ctypes.byref(short), P, None) == q.QLORA_ERR_BAD_CODEBOOK
+    assert "size" in q.qlora_last_error()
+    assert lib.qlora_dequant_bf16_ex(None, P, None) == q.QLORA_ERR_NULL_ARG
     assert lib.qlora_swiglu_fwd(None, None, None, 0, None) == q.QLORA_OK                        # count 0
     assert lib.qlora_swiglu_fwd(P, P, None, 8, None) == q.QLORA_ERR_NULL_ARG
     assert lib.qlora_swiglu_bwd(P, P, ctypes.c_void_p(24), P, P, 8, None) == q.QLORA_ERR_MISALIGNED
@@ -149,17 +196,24 @@ def test_argument_errors_enqueue_nothing(q):
     assert adam(P, None, P, ctypes.c_void_p(20), P, 16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None) == q.QLORA_ERR_MISALIGNED
     assert adam(None, None, None, None, None, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None) == q.QLORA_OK  # count 0
     merge = lib.qlora_merge_adapters
-    small = q.qlora_nf4_weight(128, 64, 16, 16, 16, 16)
-    assert merge(ctypes.byref(W), P, P, 0, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_BAD_RANK
-    assert merge(ctypes.byref(W), P, P, 8, 16.0, P, ctypes.byref(small), P, 1 << 30, None) == q.QLORA_ERR_BAD_SHAPE
-    assert merge(ctypes.byref(W), P, P, 8, 16.0, P, None, P, 64, None) == q.QLORA_ERR_WORKSPACE
-    assert merge(ctypes.byref(W), None, P, 8, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_NULL_ARG
+    WX = _ex(q, W)
+    small = _ex(q, q.qlora_nf4_weight(128, 64, 16, 16, 16, 16))
+    assert merge(ctypes.byref(WX), P, P, 0, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_BAD_RANK
+    assert merge(ctypes.byref(WX), P, P, 8, 16.0, P, ctypes.byref(small), P, 1 << 30, None) == q.QLORA_ERR_BAD_SHAPE
+    assert merge(ctypes.byref(WX), P, P, 8, 16.0, P, None, P, 64, None) == q.QLORA_ERR_WORKSPACE
+    assert merge(ctypes.byref(WX), None, P, 8, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_NULL_ARG
     assert q.qlora_merge_workspace_bytes(4096, 4096) >= 4096 * 4096 * 4 + q.qlora_quantize_workspace_bytes(4096, 4096)
     assert q.qlora_merge_workspace_bytes(4096, 100) == 0
-    bad_cb = q.qlora_nf4_weight(64, 64, 16, 16, 16, 16, 3)
-    assert lib.qlora_quantize_nf4_dq(P, ctypes.byref(bad_cb), P, 1 << 20, None) == q.QLORA_ERR_BAD_CODEBOOK
-    assert lib.qlora_dequant_bf16(ctypes.byref(bad_cb), P, None) == q.QLORA_ERR_BAD_CODEBOOK
-    assert fwd(ctypes.byref(bad_cb), P, 16, P, P, 8, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_BAD_CODEBOOK
+    bad_cb = _ex(q, W, 3)
+    assert lib.qlora_quantize_ex(P, ctypes.byref(bad_cb), P, 1 << 20, None) == q.QLORA_ERR_BAD_CODEBOOK
+    assert lib.qlora_dequant_bf16_ex(ctypes.byref(bad_cb), P, None) == q.QLORA_ERR_BAD_CODEBOOK
+    assert fwd_ex(ctypes.byref(bad_cb), P, 16, P, P, 8, 16.0, P, None, P, 1 << 30, None) == q.QLORA_ERR_BAD_CODEBOOK
+    bwd_ex = lib.qlora_linear_bwd_ex
+    assert bwd_ex(ctypes.byref(bad_cb), P, P, 16, P, P, 8, 16.0, None, P, P, P, P, 1 << 30, None) == \
+        q.QLORA_ERR_BAD_CODEBOOK
+    # k at or above 2^22 is rejected (a 256-row activation tile would reach 2^31 bytes)
+    big_k = q.qlora_nf4_weight(1, 1 << 22, 16, 16, 16, 16)
+    assert fwd(ctypes.byref(big_k), P, 16, P, P, 8, 16.0, P, None, P, 1 << 40, None) == q.QLORA_ERR_BAD_SHAPE
     for code in range(-8, 1):
         assert q.qlora_strerror(code) != "unknown status"
 
@@ -185,3 +239,102 @@ def test_attention_shape_and_argument_errors(q):
     assert bwd(P, P, P, P, P, P, P, None, 1, 16, 2, 64, P, big, None) == q.QLORA_ERR_NULL_ARG
     assert bwd(P, P, P, P, P, P, P, P, 1, 16, 2, 64, P, 64, None) == q.QLORA_ERR_WORKSPACE
     assert "head_dim" in (fwd(P, P, P, P, P, 1, 16, 2, 60, P, big, None) and q.qlora_last_error())
+
+
+def test_linear_plan_paths(q):
+    """The kernels each shape takes; the same decision the calls make."""
+    T, G, V = q.QLORA_PATH_TILE, q.QLORA_PATH_GENERAL, q.QLORA_PATH_GEMV
+    p = q.qlora_linear_plan(4096, 11008, 4096, 64)            # 7B MLP: enough tiles, no splits
+    assert (p["fwd_path"], p["fwd_splits"], p["dx_path"], p["dx_splits"]) == (T, 1, T, 1)
+    assert q.qlora_linear_plan(4096, 4096, 11008, 64)["fwd_splits"] == 1
+    p = q.qlora_linear_plan(512, 4096, 4096, 64)              # 7B q_proj at M = 512: 32 tiles, split
+    assert p["fwd_path"] == T and p["fwd_splits"] > 1 and p["dx_splits"] > 1
+    for n, k in ((8192, 8192), (8192, 22016)):                # 65B block at M = 512
+        assert q.qlora_linear_plan(512, n, k, 64)["fwd_splits"] > 1
+    assert q.qlora_linear_plan(512, 22016, 8192, 64)["dx_splits"] > 1
+    for m in (1, 4, 16):                                      # small M: the GEMV forward
+        assert q.qlora_linear_plan(m, 22016, 8192, 16)["fwd_path"] == V
+        assert q.qlora_linear_plan(m, 22016, 8192, 16, q.QLORA_SCALES_FP32)["fwd_path"] == T
+    assert q.qlora_linear_plan(37, 200, 192, 5)["dx_path"] == G          # n % 64 != 0
+    assert q.qlora_linear_plan(64, 640, 512, 64)["fwd_splits"] == 1      # 8 steps: nothing to split
+    # dY tiles of 256 rows x 512 n bytes must stay below 2^31: n = 2^22 takes the general kernel
+    assert q.qlora_linear_plan(1, (1 << 22) - 64, 64, 1)["dx_path"] == T
+    assert q.qlora_linear_plan(1, 1 << 22, 64, 1)["dx_path"] == G
+    assert q.qlora_linear_plan(1, 1 << 23, 64, 1)["dx_path"] == G
+    assert q.qlora_linear_plan(0, 64, 64, 1)["fwd_path"] == q.QLORA_PATH_NONE
+    for bad in ((16, 64, 96, 8), (16, 64, 64, 0), (-1, 64, 64, 8)):
+        with pytest.raises(q.QloraError):
+            q.qlora_linear_plan(*bad)
+
+
+def test_binding_rejects_bad_tensors_before_the_call(q):
+    """Shape, dtype and device mismatches raise in Python before any pointer
+    reaches the library (CPU tensors here: nothing is launched)."""
+    import torch
+    bf = lambda *s: torch.zeros(*s, dtype=torch.bfloat16)
+    w = q.NF4Weight.empty(128, 256, device="cpu")
+    M, r = 8, 4
+    X, A, B, Y, H = bf(M, 256), bf(r, 256), bf(128, r), bf(M, 128), torch.zeros(M, r)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="X has shape"):
+        q.qlora_linear_fwd(w, bf(M, 128), A, B, r, 16.0, Y, H, ws)
+    with pytest.raises(ValueError, match="A has shape"):
+        q.qlora_linear_fwd(w, X, bf(r + 1, 256), B, r, 16.0, Y, H, ws)
+    with pytest.raises(ValueError, match="B has shape"):
+        q.qlora_linear_fwd(w, X, A, bf(256, r), r, 16.0, Y, H, ws)
+    with pytest.raises(ValueError, match="Y has shape"):
+        q.qlora_linear_fwd(w, X, A, B, r, 16.0, bf(M + 1, 128), H, ws)
+    with pytest.raises(ValueError, match="H_out has shape"):
+        q.qlora_linear_fwd(w, X, A, B, r, 16.0, Y, torch.zeros(M, r + 1), ws)
+    with pytest.raises(TypeError):
+        q.qlora_linear_fwd(w, X.float(), A, B, r, 16.0, Y, H, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        q.qlora_linear_fwd(w, X, A, B, r, 16.0, Y, H, ws)
+    with pytest.raises(ValueError, match="dY has shape"):
+        q.qlora_linear_bwd(w, X, bf(M, 127), A, B, r, 16.0, H, bf(M, 256), bf(r, 256), bf(128, r), ws)
+    with pytest.raises(ValueError, match="dX has shape"):
+        q.qlora_linear_bwd(w, X, Y, A, B, r, 16.0, H, bf(M, 255), bf(r, 256), bf(128, r), ws)
+    with pytest.raises(ValueError, match="dB has shape"):
+        q.qlora_linear_bwd(w, X, Y, A, B, r, 16.0, H, None, bf(r, 256), bf(r, 128), ws)
+    with pytest.raises(ValueError, match="W has shape"):
+        q.qlora_quantize_nf4_dq(torch.zeros(128, 255), w, ws)
+    with pytest.raises(ValueError, match="elements"):
+        q.qlora_dequant_bf16(w, bf(128, 255))
+    short = q.NF4Weight(128, 256, w.packed[:-1], w.scale_code, w.group_amax, w.offset)
+    with pytest.raises(ValueError, match="packed"):
+        q.qlora_dequant_bf16(short, bf(128, 256))
+    with pytest.raises(ValueError, match="elements"):
+        q.qlora_swiglu_fwd(bf(10), bf(10), bf(9))
+    with pytest.raises(ValueError, match="elements"):
+        q.qlora_add_bf16(bf(10), bf(11), bf(10))
+    with pytest.raises(ValueError, match="has shape"):
+        q.qlora_attention_fwd(bf(32, 64), bf(32, 64), bf(32, 64), bf(32, 63), torch.zeros(2, 1, 16), 2, 16, 1, 64, ws)
+    with pytest.raises(ValueError, match="lse"):
+        q.qlora_attention_fwd(bf(32, 64), bf(32, 64), bf(32, 64), bf(32, 64), torch.zeros(2, 1, 15), 2, 16, 1, 64, ws)
+    with pytest.raises(ValueError, match="grad"):
+        q.qlora_adamw_step(torch.zeros(16), None, bf(15), torch.zeros(16), torch.zeros(16), 1e-3, 0.9, 0.999, 1e-8,
+                           0.0, 1)
+    with pytest.raises(ValueError, match="A has shape"):
+        q.qlora_merge_adapters(w, bf(r, 128), B, r, 16.0, None, None, ws)
+
+
+def test_decoder_layer_rejects_bad_shapes(q):
+    import torch
+    from bit_nf4_quantized_qlora_amd.layer import DecoderLayer
+    hidden, inter, r, batch, seq, heads, d = 64, 128, 4, 2, 8, 2, 32
+    shapes = {"q": (hidden, hidden), "k": (hidden, hidden), "v": (hidden, hidden), "o": (hidden, hidden),
+              "gate": (inter, hidden), "up": (inter, hidden), "down": (hidden, inter)}
+    weights = {nm: q.NF4Weight.empty(n, k, device="cpu") for nm, (n, k) in shapes.items()}
+    adapters = {nm: (torch.zeros(r, k, dtype=torch.bfloat16), torch.zeros(n, r, dtype=torch.bfloat16))
+                for nm, (n, k) in shapes.items()}
+    lay = DecoderLayer(weights, adapters, r, 16.0, batch, seq, heads, d, device="cpu")
+    M = batch * seq
+    good = torch.zeros(M, hidden, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="X must be"):
+        lay.fwd(torch.zeros(M + 1, hidden, dtype=torch.bfloat16), good)
+    with pytest.raises(ValueError, match="dY must be"):
+        lay.bwd(good, torch.zeros(M, hidden + 1, dtype=torch.bfloat16), good)
+    with pytest.raises(ValueError, match="X must be"):
+        lay.fwd(good.float(), good)
+    with pytest.raises(ValueError, match="GPU tensor"):     # right shapes: the binding's device check
+        lay.fwd(good, good.clone())

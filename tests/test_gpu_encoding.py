@@ -117,14 +117,15 @@ def test_q_proj_full_tensor(q):
     _full_check(q, I.weight(w, 0), "q_proj_7b")
 
 
-@pytest.mark.parametrize("wname,li", [("mlp_7b", 0), ("mlp_7b", 2), ("up_65b", 0), ("block_65b", 0),
-                                      ("block_65b", 6)])
+@pytest.mark.parametrize("wname,li", [("up_65b", 0)] + [("block_65b", i) for i in range(7)])
 def test_full_size_sampled(q, wname, li):
-    """Full-size layers: every scale code, group constant and the offset
-    compared whole; packed bytes and BF16 weights on sampled rows."""
+    """Full-size 65B layers (the 7B MLP layers are compared whole in the
+    linear tests): every scale code, group constant and the offset compared
+    whole; packed bytes and BF16 weights on a random row of every 256-row
+    group plus both ends."""
     wl = I.WORKLOADS[wname]
     W = I.weight(wl, li)
-    note(f"[encoding] {wname}[{li}] {W.shape} sampled")
+    note(f"[encoding] {wname}[{li}] {W.shape} sampled per 256-row group")
     n, k = W.shape
     ow = OracleWeight(W)
     w = gpu_quantize(q, W)
@@ -132,7 +133,8 @@ def test_full_size_sampled(q, wname, li):
     assert np.array_equal(got["scale_code"], ow.scale_code), "scale_code"
     assert np.array_equal(got["group_amax"].view(np.uint32), ow.group_amax.view(np.uint32)), "group_amax"
     assert np.float32(got["offset"]).view(np.uint32) == np.float32(ow.offset).view(np.uint32), "offset"
-    rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(li).choice(n, 24, replace=False)]))
+    g = np.random.default_rng(li)
+    rows = np.unique(np.concatenate([[0, n - 1]] + [g.integers(r0, min(r0 + 256, n), 1) for r0 in range(0, n, 256)]))
     gp = got["packed"].reshape(n, k // 2)[rows]
     assert np.array_equal(gp, ow.row_packed(rows)), "packed rows"
     wh = _gpu_dequant(q, w)[rows]

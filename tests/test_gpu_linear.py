@@ -6,7 +6,8 @@ import pytest
 import torch
 
 from bit_nf4_quantized_qlora_amd import inputs as I
-from gpu_helpers import Linear, assert_close, gpu_quantize, host_bf16, note
+from gpu_helpers import Linear, assert_close, assert_encoding_equal, encoding_to_host, gpu_quantize, host_bf16, note
+from oracle import nf4_dq
 from oracle_views import OracleWeight, bf16_f64, bwd, fwd
 
 pytestmark = pytest.mark.gpu
@@ -74,6 +75,38 @@ def test_edge_shapes(q, n, k, m, r, alpha, seed):
     A = I.custom_bf16((r, k), seed, 3, bound=0.05)
     B = I.custom_bf16((n, r), seed, 4, bound=0.05)
     _run_full(q, W, X, A, B, dY, r, alpha, f"edge n{n} k{k} m{m} r{r}")
+
+
+# Shapes whose tile launches split the contraction (few tiles, long
+# contraction), each with what it exercises; test_split_shapes_take_the_split_path
+# checks the plan so the cases cannot silently stop covering it.
+SPLIT_CASES = [
+    (640, 4096, 300, 64, 16.0, 61),    # fwd 8 splits x 8 steps, two m tiles (ragged); dX 2 splits, the last 2 steps
+    (1000, 2560, 77, 16, 16.0, 62),    # ragged n (1000) and M: fwd 5 splits; dX on the general kernel
+    (300, 3200, 50, 8, -2.0, 63),      # 50 steps: last fwd split of 2 steps inside a partial super-step
+    (1088, 320, 96, 64, 8.0, 64),      # dX: 17 row steps as splits of 8, 8 and 1 (a partial super-step)
+    (2048, 4096, 512, 64, 16.0, 65),   # M = 512 on both passes with rank 64 (the q_proj regime, smaller n)
+    (512, 8192, 33, 128, 16.0, 66),    # maximum rank on split 0, 128 steps
+]
+
+
+@pytest.mark.parametrize("n,k,m,r,alpha,seed", SPLIT_CASES)
+def test_split_contraction(q, n, k, m, r, alpha, seed):
+    """Tile launches with a split contraction: every output compared."""
+    W = I.custom_weight(n, k, seed)
+    X = I.custom_bf16((m, k), seed, 1)
+    dY = I.custom_bf16((m, n), seed, 2)
+    A = I.custom_bf16((r, k), seed, 3, bound=0.05)
+    B = I.custom_bf16((n, r), seed, 4, bound=0.05)
+    _run_full(q, W, X, A, B, dY, r, alpha, f"split n{n} k{k} m{m} r{r} plan {q.qlora_linear_plan(m, n, k, r)}")
+
+
+def test_split_shapes_take_the_split_path(q):
+    plans = [q.qlora_linear_plan(m, n, k, r) for n, k, m, r, _, _ in SPLIT_CASES]
+    assert all(p["fwd_path"] == q.QLORA_PATH_TILE for p in plans)
+    assert sum(p["fwd_splits"] > 1 for p in plans) >= 5
+    assert sum(p["dx_path"] == q.QLORA_PATH_TILE and p["dx_splits"] > 1 for p in plans) >= 3
+    assert plans[3]["dx_splits"] == 3 and plans[0]["fwd_splits"] == 8
 
 
 @pytest.mark.parametrize("n,k,m,r,alpha,seed", [
@@ -189,23 +222,47 @@ def test_repeat_calls_and_shared_workspace(q):
         assert_close(got, ref, f"shared workspace {name}")
 
 
+def _per_tile(extent: int, rng, per: int = 1, tile: int = 256) -> np.ndarray:
+    """Sample indices along one output axis: `per` random ones inside every
+    256-wide tile (the tile kernels' and the GEMV's row groups) plus both
+    ends, so every output tile of a launch is compared somewhere."""
+    picks = [0, extent - 1]
+    for t0 in range(0, extent, tile):
+        hi = min(t0 + tile, extent)
+        picks += list(rng.choice(np.arange(t0, hi), min(per, hi - t0), replace=False))
+    return np.unique(np.asarray(picks, np.int64))
+
+
+def _per_tile_blocks(k: int, rng) -> list:
+    """One random 64-column block inside every 256-column tile of k, plus the
+    first and last block."""
+    nb = k // 64
+    picks = {0, nb - 1}
+    for t0 in range(0, nb, 4):
+        picks.add(int(rng.integers(t0, min(t0 + 4, nb))))
+    return sorted(picks)
+
+
 def _sampled(q, wname, li, m=None, backward=True):
-    """Full-size layer: Y and H on sampled rows/columns, dX and dA on sampled
-    64-column blocks over all M, dB on sampled rows."""
+    """Full-size layer on samples that touch every 256 x 256 output tile of
+    every launch: Y on rows of every m tile x columns of every n tile, H on
+    those rows; dX and dA on one 64-column block of every k tile over all M;
+    dB on the sampled rows of every n tile."""
     wl = I.WORKLOADS[wname]
     m = m or wl.ms[0]
     W, X, A, B, dY = _workload_inputs(wl, li, m)
     n, k = W.shape
-    note(f"[linear] {wname}[{li}] W={W.shape} M={m} sampled")
+    plan = q.qlora_linear_plan(m, n, k, wl.r)
+    note(f"[linear] {wname}[{li}] W={W.shape} M={m} sampled per tile, plan {plan}")
     lin = Linear(q, gpu_quantize(q, W), X, A, B, wl.r, wl.alpha)
     Y, H = lin.fwd()
     if backward:
         dX, dA, dB = lin.bwd(dY, H=H)
     torch.cuda.synchronize()
     rng = np.random.default_rng(1000 + li)
-    ns = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 40, replace=False)]))
-    ms = np.unique(np.concatenate([[0, m - 1], rng.choice(m, min(m, 24), replace=False)]))
-    kbs = sorted({0, k // 64 - 1, int(rng.integers(k // 64))})
+    ns = _per_tile(n, rng)
+    ms = _per_tile(m, rng, per=4)
+    kbs = _per_tile_blocks(k, rng)
     kcols = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in kbs])
     ow = OracleWeight(W)
     Xf, Af, Bf, dYf = bf16_f64(X), bf16_f64(A), bf16_f64(B), bf16_f64(dY)
@@ -223,9 +280,45 @@ def _sampled(q, wname, li, m=None, backward=True):
     assert_close(bf16_f64(host_bf16(dB))[ns], dBr, f"{wname}[{li}] dB")
 
 
+def _full_size(q, wname, li):
+    """Full-size layer compared whole: the encoding and the BF16 weights bit
+    for bit, and every element of Y, H, dX, dA and dB against the fp64
+    oracle on the oracle's own BF16 weights."""
+    wl = I.WORKLOADS[wname]
+    m = wl.ms[0]
+    W, X, A, B, dY = _workload_inputs(wl, li, m)
+    n, k = W.shape
+    note(f"[linear] {wname}[{li}] W={W.shape} M={m} full, plan {q.qlora_linear_plan(m, n, k, wl.r)}")
+    ref = nf4_dq.quantize_nf4_dq(W)
+    w = gpu_quantize(q, W)
+    assert_encoding_equal(encoding_to_host(w), ref, f"{wname}[{li}]")
+    ref_wh = nf4_dq.dequant_bf16(ref["packed"], ref["scale_code"], ref["group_amax"], ref["offset"], n, k)
+    Wh = torch.empty(n, k, dtype=torch.bfloat16, device="cuda")
+    q.qlora_dequant_bf16(w, Wh)
+    torch.cuda.synchronize()
+    bad = np.flatnonzero(host_bf16(Wh).reshape(-1) != ref_wh.reshape(-1))
+    assert bad.size == 0, f"{wname}[{li}] dequant: {bad.size} differ, first {bad[:5]}"
+    del Wh
+    lin = Linear(q, w, X, A, B, wl.r, wl.alpha)
+    Y, H = lin.fwd()
+    dX, dA, dB = lin.bwd(dY, H=H)
+    torch.cuda.synchronize()
+    What = bf16_f64(ref_wh)
+    del ref, ref_wh
+    Xf, Af, Bf, dYf = bf16_f64(X), bf16_f64(A), bf16_f64(B), bf16_f64(dY)
+    Yr, Hr = fwd(Xf, What, Af, Bf, wl.alpha)
+    assert_close(bf16_f64(host_bf16(Y)), Yr, f"{wname}[{li}] Y")
+    assert_close(H.cpu().numpy(), Hr, f"{wname}[{li}] H")
+    del Yr, Y
+    dXr, dAr, dBr, _ = bwd(Xf, dYf, What, Af, Bf, wl.alpha, H=Hr)
+    assert_close(bf16_f64(host_bf16(dX)), dXr, f"{wname}[{li}] dX")
+    assert_close(bf16_f64(host_bf16(dA)), dAr, f"{wname}[{li}] dA")
+    assert_close(bf16_f64(host_bf16(dB)), dBr, f"{wname}[{li}] dB")
+
+
 @pytest.mark.parametrize("li", [0, 1, 2])
-def test_mlp_7b(q, li):
-    _sampled(q, "mlp_7b", li)
+def test_mlp_7b_full(q, li):
+    _full_size(q, "mlp_7b", li)
 
 
 @pytest.mark.parametrize("m", [1, 4, 16])
