@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "qlora_internal.h"
 
@@ -157,6 +158,43 @@ int check_ws(void *ws, size_t have, size_t need) {
   if (!ws) return fail(QLORA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (have < need) return fail(QLORA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
   if (!aligned16(ws)) return fail(QLORA_ERR_MISALIGNED, "workspace is not 16-byte aligned");
+  return QLORA_OK;
+}
+
+// Workspace of qlora_linear_fwd_noalloc: a fixed array in device memory
+// (every GPU the library runs on holds its own copy until the process ends).
+// In host code `scratch` names a host-side stand-in; kernels get the device
+// address hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+}  // namespace qlora
+
+static __device__ __align__(256) unsigned char scratch[qlora::kNoallocScratchBytes];
+
+namespace qlora {
+namespace {
+
+// The current device's copy of `scratch` (looked up on its first use, with
+// that device current).
+int device_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QLORA_ERR_HIP, "qlora_linear_fwd_noalloc: device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "qlora_linear_fwd_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(QLORA_ERR_HIP, "qlora_linear_fwd_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return QLORA_OK;
 }
 
@@ -454,6 +492,23 @@ int qlora_linear_bwd_ex(const qlora_weight_ex *w, const uint16_t *X, const uint1
   WeightIn v;
   if (int e = take_ex(w, &v)) return e;
   return bwd_impl("qlora_linear_bwd_ex", v, X, dY, M, A, B, r, alpha, H, dX, dA, dB, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
+                             const uint16_t *B, int r, float alpha, uint16_t *Y, float *H_out, hipStream_t stream) {
+  WeightIn v;
+  if (int e = take(w, &v)) return e;
+  if (int e = check_linear(v, M, r, alpha)) return e;
+  if (M == 0) return QLORA_OK;
+  const size_t need = fwd_workspace_bytes(M, v.n, v.k, r);
+  if (need > kNoallocScratchBytes)
+    return fail(QLORA_ERR_WORKSPACE,
+                "qlora_linear_fwd_noalloc: M = %lld, [%lld, %lld], r = %d needs %zu bytes of scratch, above the "
+                "library's fixed %zu",
+                (long long)M, (long long)v.n, (long long)v.k, r, need, kNoallocScratchBytes);
+  void *ptr = nullptr;
+  if (int e = device_scratch(&ptr)) return e;
+  return fwd_impl("qlora_linear_fwd_noalloc", v, X, M, A, B, r, alpha, Y, H_out, ptr, kNoallocScratchBytes, stream);
 }
 
 int qlora_linear_plan(int64_t M, int64_t n, int64_t k, int r, int32_t scales, qlora_linear_plan_info *out) {

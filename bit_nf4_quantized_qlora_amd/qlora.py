@@ -87,6 +87,7 @@ _SIGS = {
     "qlora_linear_fwd_ex": (_c_int, [_WX, _vp, _c_i64, _vp, _vp, _c_int, _c_float, _vp, _vp, _vp, _c_size, _vp]),
     "qlora_linear_bwd_ex": (_c_int, [_WX, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_float, _vp, _vp, _vp, _vp, _vp,
                                      _c_size, _vp]),
+    "qlora_linear_fwd_noalloc": (_c_int, [_W, _vp, _c_i64, _vp, _vp, _c_int, _c_float, _vp, _vp, _vp]),
     "qlora_linear_plan": (_c_int, [_c_i64, _c_i64, _c_i64, _c_int, ctypes.c_int32,
                                    ctypes.POINTER(qlora_linear_plan_info)]),
     "qlora_nf4_codebook": (None, [ctypes.POINTER(ctypes.c_float)]),
@@ -318,6 +319,29 @@ def qlora_linear_fwd(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Te
         st, fn, name = w.c_ex(), _lib.qlora_linear_fwd_ex, "qlora_linear_fwd_ex"
     _check(name, fn(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, alpha, _ptr(Y), _ptr(H_out), wp, wb,
                     _stream(stream)))
+
+
+def qlora_linear_fwd_noalloc(w: NF4Weight, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, r: int, alpha: float,
+                             Y: torch.Tensor, H_out: torch.Tensor | None, stream=None) -> None:
+    """qlora_linear_fwd on the library's fixed device scratch (no workspace;
+    NF4 weights with double-quantized constants)."""
+    if not w.is_method_type:
+        raise ValueError("qlora_linear_fwd_noalloc takes NF4 weights with double-quantized constants")
+    if X.dim() != 2:
+        raise ValueError(f"X must be [M, {w.k}], got shape {tuple(X.shape)}")
+    M = X.shape[0]
+    _need(X, torch.bfloat16, "X", shape=(M, w.k))
+    _need(A, torch.bfloat16, "A", shape=(r, w.k))
+    _need(B, torch.bfloat16, "B", shape=(w.n, r))
+    _need(Y, torch.bfloat16, "Y", shape=(M, w.n))
+    if H_out is not None:
+        _need(H_out, torch.float32, "H_out", shape=(M, r))
+    w.check_buffers()
+    _on_gpu(X=X, A=A, B=B, Y=Y, H_out=H_out, **w.buffers())
+    st = w.c_struct()
+    _check("qlora_linear_fwd_noalloc",
+           _lib.qlora_linear_fwd_noalloc(ctypes.byref(st), _ptr(X), M, _ptr(A), _ptr(B), r, alpha, _ptr(Y),
+                                         _ptr(H_out), _stream(stream)))
 
 
 def qlora_linear_bwd(w: NF4Weight, X: torch.Tensor, dY: torch.Tensor, A: torch.Tensor, B: torch.Tensor, r: int,

@@ -211,6 +211,14 @@ def test_argument_errors_enqueue_nothing(q):
     bwd_ex = lib.qlora_linear_bwd_ex
     assert bwd_ex(ctypes.byref(bad_cb), P, P, 16, P, P, 8, 16.0, None, P, P, P, P, 1 << 30, None) == \
         q.QLORA_ERR_BAD_CODEBOOK
+    # the allocation-free forward: shapes beyond its fixed scratch are rejected before any GPU use
+    noalloc = lib.qlora_linear_fwd_noalloc
+    big = q.qlora_nf4_weight(8192, 8192, 16, 16, 16, 16)
+    assert noalloc(ctypes.byref(big), P, 512, P, P, 64, 16.0, P, None, None) == q.QLORA_ERR_WORKSPACE
+    assert "scratch" in q.qlora_last_error()
+    assert noalloc(ctypes.byref(W), P, 16, P, P, 0, 16.0, P, None, None) == q.QLORA_ERR_BAD_RANK
+    assert noalloc(None, P, 16, P, P, 8, 16.0, P, None, None) == q.QLORA_ERR_NULL_ARG
+    assert noalloc(ctypes.byref(W), P, 0, None, None, 8, 16.0, None, None, None) == q.QLORA_OK   # M = 0
     # k at or above 2^22 is rejected (a 256-row activation tile would reach 2^31 bytes)
     big_k = q.qlora_nf4_weight(1, 1 << 22, 16, 16, 16, 16)
     assert fwd(ctypes.byref(big_k), P, 16, P, P, 8, 16.0, P, None, P, 1 << 40, None) == q.QLORA_ERR_BAD_SHAPE
