@@ -46,7 +46,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fused NF4-QLoRA linear fwd+bwd TFLOP/s & GB/s, % of MI355X roofline"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+# HBM traffic counters per kernel family, each valid for the sources it was
+# taken with (see source_digest)
+TRAFFIC_FILES = {"tile": os.path.join(ROOT, "profiles", "traffic_counters.json"),
+                 "gemv": os.path.join(ROOT, "profiles", "traffic_counters_gemv.json")}
 
 
 def parse():
@@ -68,19 +71,23 @@ def parse():
                    help="print only rows.decoder_layer (the 7B decoder layer and its attention core), as one JSON "
                         "line; use with --no-extras")
     p.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                   help="write profiles/traffic_counters.json from two rocprofv3 --pmc output folders "
+                   help="write the traffic-counter file of --pmc-target from two rocprofv3 --pmc output folders "
                         "(FETCH_SIZE, WRITE_SIZE) of a run with --calib-copy-mib, then exit")
+    p.add_argument("--pmc-target", choices=sorted(TRAFFIC_FILES), default="tile",
+                   help="kernel family whose counters --ingest-pmc records (tile: the 7B MLP step; gemv: the "
+                        "small-M forward, from a --small-m-only run)")
     return p.parse_args()
 
 
-# the dominant kernel's translation unit and the headers it includes: the
+# each kernel family's translation unit and the headers it includes: its
 # traffic counters stay valid until one of these changes
-TILE_SOURCES = ("nf4_tile.hip", "nf4_tile.h", "lora_gemm.h", "qlora_internal.h", "qlora_device.h")
+COUNTER_SOURCES = {"tile": ("nf4_tile.hip", "nf4_tile.h", "lora_gemm.h", "qlora_internal.h", "qlora_device.h"),
+                   "gemv": ("nf4_gemv.hip", "nf4_tile.h", "lora_gemm.h", "qlora_internal.h", "qlora_device.h")}
 
 
-def source_digest() -> str:
+def source_digest(target: str = "tile") -> str:
     h = hashlib.sha256()
-    for f in sorted(os.path.join(ROOT, "bit_nf4_quantized_qlora_amd", "csrc", n) for n in TILE_SOURCES):
+    for f in sorted(os.path.join(ROOT, "bit_nf4_quantized_qlora_amd", "csrc", n) for n in COUNTER_SOURCES[target]):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -102,7 +109,18 @@ def short_kernel_name(name: str) -> str:
     return KERNEL_ALIASES.get(base, base)
 
 
-def ingest_pmc(fetch_dir: str, write_dir: str) -> None:
+def load_traffic(target: str) -> dict:
+    """{kernel: counters} of one family when its file matches the current
+    sources, else {}."""
+    path = TRAFFIC_FILES[target]
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        tc = json.load(f)
+    return tc.get("kernels", {}) if tc.get("source_sha256") == source_digest(target) else {}
+
+
+def ingest_pmc(fetch_dir: str, write_dir: str, target: str) -> None:
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) -> bytes per launch, each
     scaled so the calibration copy reads and writes its known size."""
     def load(folder, counter):
@@ -132,11 +150,12 @@ def ingest_pmc(fetch_dir: str, write_dir: str) -> None:
             kernels[k] = {"dispatches": len(fetch[k]), "fetch_raw_per_launch": round(fm, 1),
                           "write_raw_per_launch": round(wm, 1),
                           "fetch_bytes_per_launch": round(fm * f_scale), "write_bytes_per_launch": round(wm * w_scale)}
-    out = {"source_sha256": source_digest(), "counters": ["FETCH_SIZE", "WRITE_SIZE"],
+    out = {"source_sha256": source_digest(target), "sources": list(COUNTER_SOURCES[target]),
+           "counters": ["FETCH_SIZE", "WRITE_SIZE"],
            "calibration": {"kernel": ck, "copy_bytes": copy_bytes, "fetch_raw": f_raw, "write_raw": w_raw,
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "kernels": kernels}
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(TRAFFIC_FILES[target], "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out["calibration"]))
     for k, v in kernels.items():
@@ -147,7 +166,7 @@ def ingest_pmc(fetch_dir: str, write_dir: str) -> None:
 def main():
     args = parse()
     if args.ingest_pmc:
-        ingest_pmc(*args.ingest_pmc)
+        ingest_pmc(*args.ingest_pmc, args.pmc_target)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -169,6 +188,8 @@ def main():
 
     def dev16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    calib = calib_copy(torch, dev, args.calib_copy_mib) if args.calib_copy_mib else None
 
     if args.configs_only:
         print(json.dumps({c: config_rows(q, I, c, dev, lambda: torch.cuda.Event(enable_timing=True), dev16)
@@ -302,12 +323,9 @@ def main():
     dx_launch = sum(2 * M * t["L"].n * t["L"].k + 2 * M * t["L"].k * r for t in layers) / len(layers)
     per_launch_flops = {"k_fwd_nf4": fwd_launch, "k_bwd_dx_nf4": dx_launch, "k_bwd_dx": dx_launch}
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tc = json.load(f)
-        if tc.get("source_sha256") == source_digest() and dom in tc.get("kernels", {}):
-            kk = tc["kernels"][dom]
-            traffic = kk["fetch_bytes_per_launch"] + kk["write_bytes_per_launch"]
+    tile_tc = load_traffic("tile")
+    if dom in tile_tc:
+        traffic = tile_tc[dom]["fetch_bytes_per_launch"] + tile_tc[dom]["write_bytes_per_launch"]
     if dom in per_launch_flops:
         ach = per_launch_flops[dom] / (kernels[dom]["avg_us"] * 1e-6) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
@@ -334,31 +352,23 @@ def main():
                            "frac_hbm_peak": round(deq_bytes / (deq_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
         rows["small_m"] = small_m_rows(q, I, np, torch, dev, dev16, ev)
         rows["storage_types"] = storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops)
+        rows["storage_types"]["bf16_weights_fwd"] = bf16_weight_rows(q, layers, dev, ev, ws, M, r, alpha)
         rows["merge"] = merge_rows(q, layers, dev, ev, r, alpha)
         rows["adamw"] = adamw_rows(q, layers, dev, ev)
         if wl.name == "mlp_7b":
             rows["mlp_block"] = block_rows(q, layers, dev, ev, ws, M, r, alpha, step_flops)
             rows["decoder_layer"] = layer_rows(q, I, layers, dev, ev, M, r, alpha, wl.adapter_bound)
 
-    calib = None
-    if args.calib_copy_mib:
-        nbytes = args.calib_copy_mib << 20
-        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):  # an elementwise kernel (a plain copy_ may go to a DMA engine)
-            torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        calib = {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "kernel": "elementwise mul by 1"}
-        del src, dst
-        if os.environ.get("QLORA_CALIB_DIR"):
-            with open(os.path.join(os.environ["QLORA_CALIB_DIR"], "calib_copy.json"), "w") as fh:
-                json.dump(calib, fh)
 
     attainable = None
     if not args.no_extras:
         attainable = attainable_peaks(torch, dev, ev)
+        attainable["mfma_bf16_tflops"] = round(q.mfma_peak_tflops(), 1)
+        attainable["mfma_how"] = ("tracing library's k_mfma_peak: v_mfma_f32_16x16x32_bf16 back to back on 8 "
+                                  "independent accumulator tiles per wave, 2 waves per SIMD, no memory traffic; "
+                                  "fastest of 5 launches")
         if roofline.get("achieved") is not None:
-            roofline["frac_attainable"] = round(roofline["achieved"] / attainable["bf16_gemm_tflops"], 4)
+            roofline["frac_attainable"] = round(roofline["achieved"] / attainable["mfma_bf16_tflops"], 4)
         for k, v in rows["small_m"].items():
             if isinstance(v, dict) and "kernel_gbps_packed" in v:
                 v["kernel_frac_attainable_read"] = round(v["kernel_gbps_packed"] / attainable["hbm_read_gbps"], 4)
@@ -382,7 +392,7 @@ def main():
         "cpu_baseline": cpu,
         "rows": rows,
         "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in sorted(kernels.items())},
-        "source_sha256": source_digest(),
+        "source_sha256": source_digest("tile"),
     }
     if calib:
         out["calib_copy"] = calib
@@ -465,6 +475,24 @@ def config_rows(q, I, name, dev, ev, dev16, steps=20, warmup=10):
     del layers, ws
     torch.cuda.empty_cache()
     return out
+
+
+def calib_copy(torch, dev, mib):
+    """A plain elementwise copy of known size (counter calibration): each
+    traffic counter is scaled by what it reads for this kernel."""
+    nbytes = mib << 20
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):  # an elementwise kernel (a plain copy_ may go to a DMA engine)
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    calib = {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "kernel": "elementwise mul by 1"}
+    del src, dst
+    torch.cuda.empty_cache()
+    if os.environ.get("QLORA_CALIB_DIR"):
+        with open(os.path.join(os.environ["QLORA_CALIB_DIR"], "calib_copy.json"), "w") as fh:
+            json.dump(calib, fh)
+    return calib
 
 
 def traced(q, fn, reps):
@@ -561,6 +589,61 @@ def storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops):
     for name in variants:
         if name != "nf4_dq":
             del weights[name]
+    torch.cuda.empty_cache()
+    return out
+
+
+def bf16_weight_rows(q, layers, dev, ev, ws, M, r, alpha):
+    """The 16-bit baseline on the same kernels: the forward of the three
+    layers with NF4+DQ weights (codes expanded in the tile kernel, block-scale
+    table job) against the same forward with the weights already in BF16
+    (W_hat, the same tile kernel reading BF16 tiles: no expansion, no table),
+    both through the tracing library, alternated, 3 rounds of 3 warm-up +
+    10 timed passes, minimum each; plus each tile kernel's average launch.
+    Bytes per weight read by the tile kernel: 0.516 (NF4+DQ) vs 2 (BF16)."""
+    import torch
+    W16 = []
+    for t in layers:
+        Wh = torch.empty(t["L"].n, t["L"].k, dtype=torch.bfloat16, device=dev)
+        q.qlora_dequant_bf16(t["w"], Wh)
+        W16.append(Wh)
+
+    def fwd_nf4():
+        for t in layers:
+            q.qlora_linear_fwd(t["w"], t["X"], t["A"], t["B"], r, alpha, t["Y"], t["H"], ws)
+
+    def fwd_bf16():
+        for t, Wh in zip(layers, W16):
+            q.qlora_profile_linear_fwd_bf16w(Wh, t["X"], t["A"], t["B"], r, alpha, t["Y"], t["H"], ws)
+
+    best = {"nf4_dq": float("inf"), "bf16": float("inf")}
+    q.use_tracing_library(True)
+    try:
+        for _ in range(3):
+            for name, fn in (("nf4_dq", fwd_nf4), ("bf16", fwd_bf16)):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                a, b = ev(), ev()
+                a.record()
+                for _ in range(10):
+                    fn()
+                b.record()
+                torch.cuda.synchronize()
+                best[name] = min(best[name], a.elapsed_time(b) / 10)
+    finally:
+        q.use_tracing_library(False)
+    kn = traced(q, fwd_nf4, 5).get("k_fwd_nf4")
+    kb = traced(q, fwd_bf16, 5).get("k_fwd_bf16w")
+    out = {"fwd_ms_nf4_dq": round(best["nf4_dq"], 4), "fwd_ms_bf16": round(best["bf16"], 4),
+           "fwd_nf4_over_bf16": round(best["nf4_dq"] / best["bf16"], 4)}
+    if kn and kb:
+        out["tile_us_nf4_dq"] = round(1e3 * kn[1] / kn[0], 2)
+        out["tile_us_bf16"] = round(1e3 * kb[1] / kb[0], 2)
+        out["tile_nf4_over_bf16"] = round(kn[1] / kn[0] / (kb[1] / kb[0]), 4)
+    out["how"] = ("7B MLP forward (gate, up, down; M = 4096): NF4+DQ expanded in the tile kernel vs the same tile "
+                  "kernel on W_hat in BF16 (qlora_profile_linear_fwd_bf16w), identical outputs bit for bit")
+    del W16
     torch.cuda.empty_cache()
     return out
 
@@ -773,8 +856,9 @@ def attainable_peaks(torch, dev, ev):
     """What the box sustains, measured beside the run (the second denominator
     next to the spec peaks): an elementwise copy and a read-only reduction
     over 1 GiB (the fastest of three torch reductions), and a large vendor
-    BF16 GEMM (8192^3, hipBLASLt via torch.matmul).  Medians of 10 timed
-    calls after 3 warm-ups."""
+    BF16 GEMM (8192^3, hipBLASLt via torch.matmul) as context.  Medians of 10
+    timed calls after 3 warm-ups.  The matrix-core denominator itself is the
+    library's MFMA microbenchmark (mfma_bf16_tflops, added by the caller)."""
     def med(fn, n=10):
         for _ in range(3):
             fn()
@@ -850,6 +934,11 @@ def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
         it = iter(range(10 ** 9))
         prof = traced(q, lambda: q.qlora_linear_fwd(ws_list[next(it) % copies], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws),
                       reps)
+        gemv_tc = load_traffic("gemv").get("k_gemv_nf4")
+        if gemv_tc:
+            row["kernel_traffic_bytes"] = {"fetch": gemv_tc["fetch_bytes_per_launch"],
+                                           "write": gemv_tc["write_bytes_per_launch"],
+                                           "fetch_vs_packed": round(gemv_tc["fetch_bytes_per_launch"] / packed_bytes, 4)}
         if "k_gemv_nf4" in prof:
             n, ms = prof["k_gemv_nf4"]
             kus = 1e3 * ms / n

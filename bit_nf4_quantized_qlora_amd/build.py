@@ -4,7 +4,8 @@ Every call recompiles: the objects go to ``_build/`` next to this file and the
 shared library to ``libqlora.so`` beside them.  A second library from the
 same sources, ``libqlora_prof.so``, is built with -DQLORA_PROFILE: it adds
 the per-kernel event timer (profile.hip, include/qlora_profile.h) that the
-benchmark's tracing pass uses; the product library carries no timer.
+benchmark's tracing pass uses, and the matrix-core peak microbenchmark
+(peak.hip); the product library carries neither.
 """
 from __future__ import annotations
 
@@ -48,7 +49,7 @@ def _run(cmd):
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     cc = hipcc()
     variants = [(LIB, os.path.join(BUILD, "lib"), SOURCES, []),
-                (LIB_PROF, os.path.join(BUILD, "prof"), SOURCES + ["profile.hip"], ["-DQLORA_PROFILE=1"])]
+                (LIB_PROF, os.path.join(BUILD, "prof"), SOURCES + ["profile.hip", "peak.hip"], ["-DQLORA_PROFILE=1"])]
     cmds, links = [], []
     for lib, odir, srcs, extra in variants:
         os.makedirs(odir, exist_ok=True)

@@ -104,76 +104,70 @@ __device__ __forceinline__ void run_reduce_cols(const SmallJob &j, uint32_t idx)
   static_cast<uint16_t *>(j.out)[idx] = f32_to_bf16_bits(sum_splits(part, S, (size_t)RP * D, src));
 }
 
+// The four block scales of row n, blocks 4 kq .. 4 kq + 3 (0 past k/64 or n):
+// with double-quantized constants and k/64 % 4 == 0 the four scale codes are
+// one aligned 32-bit word and share one group constant (groups are 256
+// blocks, so an aligned run of four never straddles two); otherwise one load
+// per block.  Every load is issued before any use.  block_scale is the
+// dequantization's own (bit-identical).
+__device__ __forceinline__ void row_quad_scales(const Nf4View &w, int64_t n, int64_t kq, float (&v)[kTileSup]) {
+  const int64_t nkb = w.k / kBlock;
+#pragma unroll
+  for (int u = 0; u < kTileSup; ++u) v[u] = 0.f;
+  if (n >= w.n) return;
+  const int64_t b0 = n * nkb + kTileSup * kq;
+  if (!w.absmax && nkb % kTileSup == 0) {
+    if (kTileSup * kq >= nkb) return;
+    const uint32_t word = *reinterpret_cast<const uint32_t *>(w.scale_code + b0);
+    const float ga = w.group_amax[b0 / kGroup], off = *w.offset;
+#pragma unroll
+    for (int u = 0; u < kTileSup; ++u) v[u] = block_scale((word >> (8 * u)) & 0xFFu, ga, off);
+    return;
+  }
+  const float off = w.absmax ? 0.f : *w.offset;
+  uint32_t c8[kTileSup];
+  float ga[kTileSup];
+#pragma unroll
+  for (int u = 0; u < kTileSup; ++u) {
+    const int64_t kb = kTileSup * kq + u, b = kb < nkb ? n * nkb + kb : 0;  // past k/64: block 0, then 0
+    if (w.absmax) {
+      c8[u] = __float_as_uint(w.absmax[b]);
+      ga[u] = 0.f;
+    } else {
+      c8[u] = w.scale_code[b];
+      ga[u] = w.group_amax[b / kGroup];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kTileSup; ++u)
+    if (kTileSup * kq + u < nkb) v[u] = w.absmax ? __uint_as_float(c8[u]) : block_scale(c8[u], ga[u], off);
+}
+
 // Forward scale table: for weight tile to (rows 256to ..) and super-step sp
 // (blocks 4sp .. 4sp+3 of each row) one contiguous 4 KB run,
 // Sp[((to*nsup + sp)*256 + row)*4 + q]; rows past n and blocks past k/64 hold
-// 0.  block_scale is the dequantization's own (bit-identical).
+// 0.
 __device__ __forceinline__ void run_scales_fwd(const SmallJob &j, uint32_t t) {
-  const Nf4View &w = j.w;
   const uint32_t nsup = (uint32_t)j.a;
   const uint32_t q = t >> 8, to = q / nsup, sp = q - to * nsup;
-  const int64_t n = to * kTileRows + (t & 255), nkb = w.k / kBlock;
-  f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-  if (n < w.n) {
-    // every load before any use (blocks past k/64 read block 0, then give 0)
-    const float off = w.absmax ? 0.f : *w.offset;
-    uint32_t c8[kTileSup];
-    float ga[kTileSup];
-#pragma unroll
-    for (int u = 0; u < kTileSup; ++u) {
-      const int64_t kb = kTileSup * sp + u, b = kb < nkb ? n * nkb + kb : 0;
-      if (w.absmax) {
-        c8[u] = __float_as_uint(w.absmax[b]);
-        ga[u] = 0.f;
-      } else {
-        c8[u] = w.scale_code[b];
-        ga[u] = w.group_amax[b / kGroup];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kTileSup; ++u) {
-      const int64_t kb = kTileSup * sp + u;
-      if (kb < nkb) v[u] = w.absmax ? __uint_as_float(c8[u]) : block_scale(c8[u], ga[u], off);
-    }
-  }
-  *reinterpret_cast<f32x4_t *>(static_cast<float *>(j.out) + 4 * t) = v;
+  float v[kTileSup];
+  row_quad_scales(j.w, (int64_t)to * kTileRows + (t & 255), sp, v);
+  *reinterpret_cast<f32x4_t *>(static_cast<float *>(j.out) + 4 * t) = f32x4_t{v[0], v[1], v[2], v[3]};
 }
 
 // Backward scale table: for column tile tk (k-blocks 4tk .. 4tk+3) and
 // super-step sp (weight rows 256sp .. 256sp+255) one contiguous 4 KB run,
 // Sp[((tk*nsup + sp)*4 + blk)*256 + row]; rows past n and blocks past k/64
-// hold 0.  One thread per (tk, sp, row): the row's four consecutive scale
-// codes, four coalesced stores.
+// hold 0.  One thread per (tk, sp, row): the row's four scales, four
+// coalesced stores.
 __device__ __forceinline__ void run_scales_bwd(const SmallJob &j, uint32_t t) {
-  const Nf4View &w = j.w;
   const uint32_t nsup = (uint32_t)j.a;
   const uint32_t q = t >> 8, tk = q / nsup, sp = q - tk * nsup;
-  const int64_t n = (int64_t)sp * kTileRows + (t & 255), nkb = w.k / kBlock;
+  float v[kTileSup];
+  row_quad_scales(j.w, (int64_t)sp * kTileRows + (t & 255), tk, v);
   float *out = static_cast<float *>(j.out) + (size_t)q * 4 * 256 + (t & 255);
-  const float off = w.absmax ? 0.f : *w.offset;
-  // every load before any use (rows past n or blocks past k/64 read block 0,
-  // then give 0)
-  uint32_t c8[kTileSup];
-  float ga[kTileSup];
 #pragma unroll
-  for (int blk = 0; blk < kTileSup; ++blk) {
-    const int64_t kb = (int64_t)tk * kTileSup + blk;
-    const int64_t b = n < w.n && kb < nkb ? n * nkb + kb : 0;
-    if (w.absmax) {
-      c8[blk] = __float_as_uint(w.absmax[b]);
-      ga[blk] = 0.f;
-    } else {
-      c8[blk] = w.scale_code[b];
-      ga[blk] = w.group_amax[b / kGroup];
-    }
-  }
-#pragma unroll
-  for (int blk = 0; blk < kTileSup; ++blk) {
-    const int64_t kb = (int64_t)tk * kTileSup + blk;
-    float v = 0.f;
-    if (n < w.n && kb < nkb) v = w.absmax ? __uint_as_float(c8[blk]) : block_scale(c8[blk], ga[blk], off);
-    out[blk * 256] = v;
-  }
+  for (int blk = 0; blk < kTileSup; ++blk) out[blk * 256] = v[blk];
 }
 
 __global__ __launch_bounds__(256) void k_small_jobs(SmallJobs js) {

@@ -85,4 +85,25 @@ hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint1
   return launch_fwd_tiles(a.w, scales, X, M, B, a.r, l.RP, sH, Y, tpart, s);
 }
 
+#ifdef QLORA_PROFILE
+// The forward with BF16 weights on the same kernels (tracing build): H and
+// its reduction exactly as above, then the tile kernel reading Wb instead of
+// expanding codes.  No block-scale table is needed.
+hipError_t launch_linear_fwd_bf16w(const uint16_t *Wb, int64_t N, int64_t K, int64_t M, int r, float s_lora,
+                                   const uint16_t *X, const uint16_t *A, const uint16_t *B, uint16_t *Y, float *H_out,
+                                   void *ws, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const FwdWs l = fwd_ws_layout(M, N, K, r);
+  char *base = static_cast<char *>(ws);
+  float *part = reinterpret_cast<float *>(base + l.part_off);
+  uint16_t *sH = reinterpret_cast<uint16_t *>(base + l.sh_off);
+  hipError_t e = launch_nt_splitk(X, M, A, r, l.RP, K, K, l.sp, part, s);
+  if (e != hipSuccess) return e;
+  const SmallJob jobs[1] = {job_reduce_rows(part, l.sp.splits, M, l.RP, r, s_lora, H_out, sH, nullptr, 0)};
+  e = launch_jobs("k_prep_fwd", jobs, 1, s);
+  if (e != hipSuccess) return e;
+  return launch_fwd_tiles_bf16w(Wb, N, K, X, M, B, r, l.RP, sH, Y, s);
+}
+#endif
+
 }  // namespace qlora

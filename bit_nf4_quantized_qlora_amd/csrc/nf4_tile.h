@@ -46,6 +46,14 @@ SmallJob job_scales_bwd(const Nf4View &w, float *scales);
 hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, int64_t M, const uint16_t *Bl, int r,
                             int RP, const uint16_t *sH, uint16_t *Y, float *tpart, hipStream_t s);
 
+#ifdef QLORA_PROFILE
+// The same forward tile kernel on BF16 weights Wb [n, k] (no expansion):
+// the 16-bit baseline of the tracing build.  One split, every shape the
+// forward takes.
+hipError_t launch_fwd_tiles_bf16w(const uint16_t *Wb, int64_t n, int64_t k, const uint16_t *X, int64_t M,
+                                  const uint16_t *Bl, int r, int RP, const uint16_t *sH, uint16_t *Y, hipStream_t s);
+#endif
+
 // dX[M, k] = bf16( dY W_hat + G At^T ):  dY [M, n], At [k, RP] (A_lora
 // transposed, rank padded), G [M, RP].  Requires bwd_tiles_supported;
 // `scales`: the table job_scales_bwd wrote.

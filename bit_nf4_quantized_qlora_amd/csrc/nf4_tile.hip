@@ -170,13 +170,23 @@ __global__ __launch_bounds__(256) void k_split_reduce(const f32x4_t *__restrict_
 // multiple of 8; split 0 also adds the LoRA term) and writes its float32
 // partial tile to `part`; otherwise lsteps covers the whole contraction and
 // the tile is rounded to bf16 into `out`.
-template <bool kBwd>
+//
+// kW16 (forward only): the same kernel on weights already in BF16 (`Wb`
+// [n][k] row-major, e.g. qlora_dequant_bf16's output) -- the 16-bit
+// baseline the dequantization overhead is measured against.  The code
+// buffers then hold one step of the BF16 weight tile each (256 rows x 128 B,
+// the B tile's layout and swizzle), copied three steps ahead; an expansion
+// piece becomes two 8-byte fragment reads (in the table-read slots) and four
+// register moves (in the arithmetic slots), so the operands, their order and
+// the result are bit for bit those of the NF4 kernel on the same W_hat.
+template <bool kBwd, bool kW16 = false>
 __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__restrict__ Sp,
                                                      const uint16_t *__restrict__ Bact, int64_t M,
                                                      const uint16_t *__restrict__ L, int lda, int RP,
                                                      const uint16_t *__restrict__ R, uint16_t *__restrict__ out,
                                                      int tiles_o, int splits, int lsteps,
-                                                     f32x4_t *__restrict__ part) {
+                                                     f32x4_t *__restrict__ part, const uint16_t *__restrict__ Wb) {
+  static_assert(!(kBwd && kW16), "the BF16-weight variant is forward only");
   __shared__ __align__(16) uint16_t Bs0[TM * 64];
   __shared__ __align__(16) uint16_t Bs1[TM * 64];
   __shared__ __align__(16) uint8_t Wc0[256 * 128];
@@ -209,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   const int64_t nsup = ceil_div_d(nk, kSup);  // super-steps of this split (ks0 % 8 == 0)
   const int64_t nk8 = ceil_div_d(nk, 8) * 8;  // steps run: whole 8-step rounds
   const int RPe = sidx == 0 ? RP : 0;         // the LoRA term goes into split 0 only
-  fill_pair_table(s_pair, tid, 256, w.codebook);
+  if constexpr (!kW16) fill_pair_table(s_pair, tid, 256, w.codebook);
 
   // B rows m0 .. m0+255 (row stride NC): wave-instruction i fills LDS chunks
   // [512w + 64i, +64): row 64w + 8i + lane/8, physical chunk lane & 7, so the
@@ -224,6 +234,15 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   auto bload = [&](int64_t kt, auto D, int i) {
     uint16_t *dst = decltype(D)::value ? Bs1 : Bs0;
     const __amdgpu_buffer_rsrc_t rs = rsrc(Bact + m0 * NC + ks0 * 64, kt < nk ? bbytes : 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
+                                             bv[i & 1] + (uint32_t)(i * 16 * NC), (int)(kt * 128), 0, 0);
+  };
+  // kW16: instruction i (0..7) of the BF16 weight tile of step kt (rows o0
+  // .. o0+255, row stride K), into code buffer D, the B tile's pattern.
+  const int abytes = (int)(min<int64_t>(TO, N - o0) * NC * 2 - ks0 * 128);
+  auto aload = [&](int64_t kt, auto D, int i) {
+    uint16_t *dst = reinterpret_cast<uint16_t *>(decltype(D)::value ? Wc1 : Wc0);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(Wb + o0 * NC + ks0 * 64, kt < nk ? abytes : 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr)(dst + (512 * wave + 64 * i) * 8), 16,
                                              bv[i & 1] + (uint32_t)(i * 16 * NC), (int)(kt * 128), 0, 0);
   };
@@ -257,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
                                                (uint32_t)(wave * 1024 + lane * 16), (int)(sp * 256 * kSup * 4), 0, 0);
     }
   };
-  constexpr int kVmemW = 9;  // code-copy instructions per wave and super-step
+  constexpr int kVmemW = kW16 ? 8 : 9;  // copy instructions per wave: code super-step / W16 step
 
   // Codes and scales of step s live in set s % 2 (q4 = s % 4 within its
   // super-step).  Forward: lane reads bytes 8g .. 8g+7 of its row's 32 bytes
@@ -271,6 +290,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   float sreg[2][kBwd ? 16 : 4];
   const int crow = kBwd ? 16 * g + li : 64 * wave + li;  // + 64q4 (bwd) / + 16rt (fwd)
   auto cread = [&](auto S, int half) {  // step with (step % 8) == S; row tiles 2half, 2half+1
+    if constexpr (kW16) return;
     constexpr int s8 = decltype(S)::value, q4 = s8 & 3, d = s8 & 1;
     const uint8_t *wc = ((s8 >> 2) & 1) ? Wc1 : Wc0;
 #pragma unroll
@@ -289,6 +309,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   // Backward scales: register chunk a (4 floats) of lane (li, g) holds rows
   // 16g + 4(a ^ (g%2)) .. +3 -- the same half swap as the code bytes (tread).
   auto sread = [&](auto S, int half) {
+    if constexpr (kW16) return;
     constexpr int s8 = decltype(S)::value, q4 = s8 & 3, d = s8 & 1;
     const float *sc = ((s8 >> 2) & 1) ? Sc1 : Sc0;
     if constexpr (kBwd) {
@@ -307,19 +328,44 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   u32x4_t a0[4], a1[2][4];  // A operands: sub-step 0; sub-step 1 by step parity
   u32x4_t bq[2][4];         // B fragments of a pair, by pair parity
   float2 pq[2][4];          // table reads of an expansion piece, by piece parity
+  u32x2_t aq[2][2];         // kW16: the two halves of a piece's fragment, by piece parity
   // Lanes of odd g hold their B fragment halves swapped (see bfrag), so
   // operand dword i takes code byte i ^ 2 there.
   uint32_t bsh[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) bsh[i] = (uint32_t)(8 * (i ^ (2 * (g & 1))));
-  // Table read i of piece p from code set d into pq[p % 2][i].
+  // B fragment offsets (elements within a tile) of lane (li, g), sub-step t,
+  // read i: row li, logical chunk 2g + t, 8-byte half i ^ (g % 2).
+  uint32_t xb[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) xb[t][i] = (uint32_t)(li * 64 + (((2 * g + t) ^ (li >> 1)) << 3) + 4 * (i ^ (g & 1)));
+  // Table read i of piece p from code set d into pq[p % 2][i].  kW16: reads
+  // 0 and 1 are the two halves of the piece's fragment (row tile p % 4,
+  // sub-step p < 4) from the weight tile in buffer d, at the B fragment's
+  // offsets (same swizzle, same half order), so each lane holds exactly the
+  // contraction positions its B fragment holds.
   auto tread = [&](int d, int p, int i) {
-    const uint32_t word = wcr[d][p & 3][p < 4 ? 1 : 0];
-    pq[p & 1][i] = s_pair[__builtin_amdgcn_ubfe(word, bsh[i], 8)];
+    if constexpr (kW16) {
+      if (i < 2) {
+        const uint16_t *ab = reinterpret_cast<const uint16_t *>(d ? Wc1 : Wc0);
+        aq[p & 1][i] = *reinterpret_cast<const u32x2_t *>(ab + 4096 * wave + 1024 * (p & 3) + xb[p < 4 ? 1 : 0][i]);
+      }
+    } else {
+      const uint32_t word = wcr[d][p & 3][p < 4 ? 1 : 0];
+      pq[p & 1][i] = s_pair[__builtin_amdgcn_ubfe(word, bsh[i], 8)];
+    }
   };
   // Quarter i of piece p's arithmetic (scales of set d); operands for a step
   // of parity e.
   auto tmath = [&](int d, int e, int p, int i) {
+    if constexpr (kW16) {  // dword i of the fragment into its operand slot
+      const uint32_t x = aq[p & 1][i >> 1][i & 1];
+      if (p < 4) a1[e][p & 3][i] = x;
+      else a0[p & 3][i] = x;
+      return;
+    }
     const float2 v = pq[p & 1][i];
     float sa, sb;
     if constexpr (kBwd) {
@@ -336,11 +382,6 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   // B fragment (column tile ct, sub-step t) of lane (li, g): row 16ct + li,
   // logical chunk 2g + t, read as two 8-byte halves, the first being half
   // g % 2.  The row term 16ct*64 elements is an immediate.
-  uint32_t xb[2][2];  // [t][read] element offsets within a tile
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) xb[t][i] = (uint32_t)(li * 64 + (((2 * g + t) ^ (li >> 1)) << 3) + 4 * (i ^ (g & 1)));
   auto bfrag = [&](const uint16_t *bs, int P, int cc) -> u32x4_t {
     const int t = P >> 2, ct = 4 * (P & 3) + cc;
     const u32x2_t h0 = *reinterpret_cast<const u32x2_t *>(bs + xb[t][0] + 1024 * ct);
@@ -399,7 +440,10 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
 #pragma unroll
   for (int i = 0; i < 8; ++i) bload(0, std::integral_constant<int, 0>(), i);
 #pragma unroll
-  for (int i = 0; i < kVmemW; ++i) wload(0, std::integral_constant<int, 0>(), i);
+  for (int i = 0; i < kVmemW; ++i) {
+    if constexpr (kW16) aload(0, std::integral_constant<int, 0>(), i);  // weight tile of step 0
+    else wload(0, std::integral_constant<int, 0>(), i);
+  }
 #pragma unroll
   for (int i = 0; i < 8; ++i) bload(1, std::integral_constant<int, 1>(), i);
   {
@@ -429,8 +473,15 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
       __syncthreads();
     }
   }
-  // steps 0's copies landed everywhere (step 1's B may still be in flight)
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (kW16) {
+    // the LoRA chunks are done with Wc1: the weight tile of step 1 goes there
+#pragma unroll
+    for (int i = 0; i < 8; ++i) aload(1, std::integral_constant<int, 1>(), i);
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // step 0's copies landed (B and W of step 1 in flight)
+  } else {
+    // steps 0's copies landed everywhere (step 1's B may still be in flight)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  }
   __syncthreads();
   cread(std::integral_constant<int, 0>(), 0);
   cread(std::integral_constant<int, 0>(), 1);
@@ -449,6 +500,14 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
   sread(std::integral_constant<int, 1>(), 1);
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) bq[0][cc] = bfrag(Bs0, 0, cc);
+  if constexpr (kW16) {
+    // step 1's tile landed and every wave is done reading step 0's: step 2's
+    // tile goes into Wc0 (it lands by the first barrier of the loop)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) aload(2, std::integral_constant<int, 0>(), i);
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) tread(1, 0, i);
 
@@ -462,7 +521,7 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
       if (P == 7) {
         // B(kt): the B tile of step kt+1 landed everywhere, every wave done
         // reading Bs[kt % 2]; then refill it with step kt+2.
-        if constexpr (j == 0)
+        if constexpr (j == 0 && !kW16)
           asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kVmemW) : "memory");
         else
           asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -477,7 +536,11 @@ __global__ __launch_bounds__(256, 1) void k_nf4_tile(Nf4View w, const float *__r
         // tile of step kt+2 into Bs[kt % 2]; when kt % 4 == 0, in pairs 0-2,
         // the codes and scales of super-step kt/4 + 1 into set (kt/4 + 1) % 2.
         if (P == 7 && (s & 1) == 0) bload(kt + 2, std::integral_constant<int, e>(), s >> 1);
-        if constexpr (j == 0) {
+        // kW16: the weight tile of step kt+3 into the buffer step kt+1's
+        // pieces have finished reading (before B(kt))
+        if constexpr (kW16)
+          if (P == 7 && (s & 1) == 1) aload(kt + 3, std::integral_constant<int, (u + 3) & 1>(), s >> 1);
+        if constexpr (j == 0 && !kW16) {
           if (P < 3 && s % 5 == 0 && 4 * P + s / 5 < kVmemW)
             wload((kt >> 2) + 1, std::integral_constant<int, ((u >> 2) + 1) & 1>(), 4 * P + s / 5);
         }
@@ -607,11 +670,26 @@ hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, 
   const int tiles_o = (int)ceil_div(w.n, TO), tiles_m = (int)ceil_div(M, TM);
   const TileSplit sp = plan_fwd_tiles(M, w.n, w.k);
   QLORA_LAUNCH("k_fwd_nf4", k_nf4_tile<false>, dim3((unsigned)(tiles_o * tiles_m * sp.splits)), dim3(256), 0, s, w,
-               scales, X, M, Bl, r, RP, sH, Y, tiles_o, sp.splits, sp.lsteps, reinterpret_cast<f32x4_t *>(tpart));
+               scales, X, M, Bl, r, RP, sH, Y, tiles_o, sp.splits, sp.lsteps, reinterpret_cast<f32x4_t *>(tpart),
+               nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.splits == 1) return e;
   return reduce_splits("k_split_reduce", sp, tiles_o, tiles_m, M, w.n, tpart, Y, s);
 }
+
+#ifdef QLORA_PROFILE
+hipError_t launch_fwd_tiles_bf16w(const uint16_t *Wb, int64_t n, int64_t k, const uint16_t *X, int64_t M,
+                                  const uint16_t *Bl, int r, int RP, const uint16_t *sH, uint16_t *Y, hipStream_t s) {
+  Nf4View w{};
+  w.n = n;
+  w.k = k;
+  const int tiles_o = (int)ceil_div(n, TO), tiles_m = (int)ceil_div(M, TM);
+  const int lsteps = (int)(ceil_div(k / kBlock, 8) * 8);  // one split
+  QLORA_LAUNCH("k_fwd_bf16w", (k_nf4_tile<false, true>), dim3((unsigned)(tiles_o * tiles_m)), dim3(256), 0, s, w,
+               nullptr, X, M, Bl, r, RP, sH, Y, tiles_o, 1, lsteps, nullptr, Wb);
+  return hipGetLastError();
+}
+#endif
 
 hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
                                int RP, const uint16_t *Gb, uint16_t *dX, float *tpart, hipStream_t s) {
@@ -619,7 +697,7 @@ hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *
   const TileSplit sp = plan_dx_tiles(M, w.n, w.k);
   QLORA_LAUNCH("k_bwd_dx_nf4", k_nf4_tile<true>, dim3((unsigned)(tiles_o * tiles_m * sp.splits)), dim3(256), 0, s,
                w, scales, dY, M, At, RP, RP, Gb, dX, tiles_o, sp.splits, sp.lsteps,
-               reinterpret_cast<f32x4_t *>(tpart));
+               reinterpret_cast<f32x4_t *>(tpart), nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.splits == 1) return e;
   return reduce_splits("k_split_reduce", sp, tiles_o, tiles_m, M, w.k, tpart, dX, s);

@@ -107,4 +107,24 @@ int qlora_profile_entry(int i, const char **name, int64_t *launches, double *tot
   return QLORA_OK;
 }
 
+int qlora_profile_linear_fwd_bf16w(const uint16_t *W_bf16, int64_t n, int64_t k, const uint16_t *X, int64_t M,
+                                   const uint16_t *A, const uint16_t *B, int r, float alpha, uint16_t *Y, float *H_out,
+                                   void *ws, size_t ws_bytes, hipStream_t stream) {
+  const size_t need = qlora_linear_workspace_bytes(M, n, k, r);
+  if (n < 1 || k < 64 || k % 64 != 0 || k >= (int64_t(1) << 22) || M < 0 || r < 1 || r > 128 ||
+      (M > 0 && need == 0))
+    return QLORA_ERR_BAD_SHAPE;
+  if (!(alpha == alpha) || alpha - alpha != 0.f) return QLORA_ERR_BAD_ALPHA;
+  if (M == 0) return QLORA_OK;
+  const void *ptrs[] = {W_bf16, X, A, B, Y, ws};
+  for (const void *ptr : ptrs) {
+    if (!ptr) return QLORA_ERR_NULL_ARG;
+    if (reinterpret_cast<uintptr_t>(ptr) & 15u) return QLORA_ERR_MISALIGNED;
+  }
+  if (H_out && (reinterpret_cast<uintptr_t>(H_out) & 15u)) return QLORA_ERR_MISALIGNED;
+  if (ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  hipError_t e = launch_linear_fwd_bf16w(W_bf16, n, k, M, r, (float)alpha / (float)r, X, A, B, Y, H_out, ws, stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
 }  // extern "C"

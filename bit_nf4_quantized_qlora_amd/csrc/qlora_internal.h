@@ -78,6 +78,11 @@ size_t bwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
 
 hipError_t launch_linear_fwd(const LinearArgs &a, const uint16_t *X, const uint16_t *A, const uint16_t *B,
                              uint16_t *Y, float *H_out, void *ws, hipStream_t s);
+#ifdef QLORA_PROFILE
+hipError_t launch_linear_fwd_bf16w(const uint16_t *Wb, int64_t N, int64_t K, int64_t M, int r, float s_lora,
+                                   const uint16_t *X, const uint16_t *A, const uint16_t *B, uint16_t *Y, float *H_out,
+                                   void *ws, hipStream_t s);
+#endif
 hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint16_t *dY, const uint16_t *A,
                              const uint16_t *B, const float *H, uint16_t *dX, uint16_t *dA, uint16_t *dB,
                              void *ws, hipStream_t s);

@@ -114,6 +114,9 @@ _PROF_SIGS = {
     "qlora_profile_count": (_c_int, []),
     "qlora_profile_entry": (_c_int, [_c_int, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_c_i64),
                                      ctypes.POINTER(ctypes.c_double)]),
+    "qlora_profile_mfma_peak": (_c_int, [_c_i64, ctypes.c_int32, _vp, ctypes.POINTER(ctypes.c_double), _vp]),
+    "qlora_profile_linear_fwd_bf16w": (_c_int, [_vp, _c_i64, _c_i64, _vp, _c_i64, _vp, _vp, _c_int, _c_float, _vp,
+                                                _vp, _vp, _c_size, _vp]),
 }
 
 
@@ -523,6 +526,55 @@ def qlora_profile_end() -> dict:
                                                                ctypes.byref(ms)))
         out[name.value.decode()] = (n.value, ms.value)
     return out
+
+
+def qlora_profile_linear_fwd_bf16w(W_bf16: torch.Tensor, X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, r: int,
+                                   alpha: float, Y: torch.Tensor, H_out: torch.Tensor | None, ws: torch.Tensor,
+                                   stream=None) -> None:
+    """The forward on BF16 weights [n, k] through the same tile kernel
+    (tracing library: call use_tracing_library(True) first)."""
+    if _lib is not _tracing:
+        raise RuntimeError("qlora_profile_linear_fwd_bf16w lives in libqlora_prof.so: call use_tracing_library(True)")
+    if W_bf16.dim() != 2 or X.dim() != 2:
+        raise ValueError("W_bf16 and X must be 2-D")
+    n, k = W_bf16.shape
+    M = X.shape[0]
+    _need(W_bf16, torch.bfloat16, "W_bf16", shape=(n, k))
+    _need(X, torch.bfloat16, "X", shape=(M, k))
+    _need(A, torch.bfloat16, "A", shape=(r, k))
+    _need(B, torch.bfloat16, "B", shape=(n, r))
+    _need(Y, torch.bfloat16, "Y", shape=(M, n))
+    if H_out is not None:
+        _need(H_out, torch.float32, "H_out", shape=(M, r))
+    _on_gpu(W_bf16=W_bf16, X=X, A=A, B=B, Y=Y, H_out=H_out)
+    wp, wb = _ws_args(ws)
+    _check("qlora_profile_linear_fwd_bf16w",
+           _lib.qlora_profile_linear_fwd_bf16w(_ptr(W_bf16), n, k, _ptr(X), M, _ptr(A), _ptr(B), r, alpha, _ptr(Y),
+                                               _ptr(H_out), wp, wb, _stream(stream)))
+
+
+def mfma_peak_tflops(iters: int = 20000, workgroups: int = 512, reps: int = 5) -> float:
+    """The attainable BF16 MFMA rate (TFLOP/s): the tracing library's
+    back-to-back v_mfma_f32_16x16x32_bf16 kernel, timed with events on the
+    current stream; the fastest of `reps` launches after one warm-up."""
+    use_tracing_library(True)
+    try:
+        out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+        flops = ctypes.c_double()
+        st = _stream(None)
+        best = float("inf")
+        for i in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            _check("qlora_profile_mfma_peak", _lib.qlora_profile_mfma_peak(iters, workgroups, _ptr(out),
+                                                                          ctypes.byref(flops), st))
+            b.record()
+            torch.cuda.synchronize()
+            if i:
+                best = min(best, a.elapsed_time(b))
+        return flops.value / (best * 1e-3) / 1e12
+    finally:
+        use_tracing_library(False)
 
 
 def raw_library() -> ctypes.CDLL:

@@ -329,3 +329,41 @@ def test_up_65b_small_m(q, m):
 @pytest.mark.parametrize("li", range(7))
 def test_block_65b(q, li):
     _sampled(q, "block_65b", li)
+
+
+@pytest.mark.parametrize("n,k,m,r,alpha,seed", [
+    (640, 512, 300, 64, 16.0, 81),     # two m tiles, one 8-step round
+    (200, 192, 37, 5, -3.5, 82),       # ragged n, k, M and rank, negative alpha
+    (1088, 320, 96, 128, 16.0, 83),    # ragged row tile, maximum rank (two LoRA chunks)
+    (11008, 4096, 4096, 64, 16.0, 84),  # the 7B gate/up shape (688 tiles)
+    (4096, 11008, 4096, 64, 16.0, 85),  # the 7B down shape (172 steps)
+])
+def test_bf16_weight_forward_is_the_nf4_forward(q, n, k, m, r, alpha, seed):
+    """The tile kernel on pre-expanded BF16 weights (the 16-bit baseline of
+    the tracing library), given the dequantized W_hat, reproduces the NF4
+    forward bit for bit: the expansion hands the MFMAs exactly these
+    operands.  The small case is also checked against the fp64 oracle."""
+    assert q.qlora_linear_plan(m, n, k, r)["fwd_splits"] == 1
+    W = I.custom_weight(n, k, seed)
+    X = I.custom_bf16((m, k), seed, 1)
+    A = I.custom_bf16((r, k), seed, 3, bound=0.05)
+    B = I.custom_bf16((n, r), seed, 4, bound=0.05)
+    note(f"[bf16-weight fwd] n={n} k={k} M={m} r={r}")
+    lin = Linear(q, gpu_quantize(q, W), X, A, B, r, alpha)
+    Y, H = lin.fwd()
+    Wh = torch.empty(n, k, dtype=torch.bfloat16, device="cuda")
+    q.qlora_dequant_bf16(lin.w, Wh)
+    Y16 = torch.empty_like(Y)
+    H16 = torch.empty_like(H)
+    q.use_tracing_library(True)
+    try:
+        q.qlora_profile_linear_fwd_bf16w(Wh, lin.X, lin.A, lin.B, r, alpha, Y16, H16, lin.ws)
+        torch.cuda.synchronize()
+    finally:
+        q.use_tracing_library(False)
+    assert torch.equal(Y16.view(torch.int16), Y.view(torch.int16)), "Y differs from the NF4 forward"
+    assert torch.equal(H16.view(torch.int32), H.view(torch.int32)), "H differs from the NF4 forward"
+    if n * k <= 1 << 20:
+        What = bf16_f64(host_bf16(Wh))
+        Yr, Hr = fwd(bf16_f64(X), What, bf16_f64(A), bf16_f64(B), alpha)
+        assert_close(bf16_f64(host_bf16(Y16)), Yr, "bf16-weight Y")
