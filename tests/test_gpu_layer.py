@@ -61,3 +61,49 @@ def test_decoder_layer_matches_oracle(q, batch, seq, heads, d, inter):
     for nm in PROJ:
         assert_close(f64(host_bf16(lay.dA[nm])), rg[nm][0], f"dA_{nm}")
         assert_close(f64(host_bf16(lay.dB[nm])), rg[nm][1], f"dB_{nm}")
+
+
+def test_backward_reads_nothing_from_an_earlier_forward(q):
+    """Gradient accumulation / checkpointing order: a forward on one input,
+    then the backward of another.  Every adapter input the backward reads
+    must come from its own recompute.  Reference: the backward of X1 on a
+    fresh layer whose saved H are all 1e30.  Then the same layer runs fwd(X2),
+    every saved H is overwritten with NaN, and bwd(X1) must give the same
+    dX, dA and dB bit for bit (a stale H of the down projection would change
+    its dB).  The down projection's dA and dB, which the attention backward
+    does not touch, are also checked against the oracle for X1."""
+    from bit_nf4_quantized_qlora_amd.layer import DecoderLayer, PROJ
+    batch, seq, heads, d, inter, r, alpha = 1, 64, 2, 32, 128, 8, 16.0
+    hidden, M = heads * d, batch * seq
+    note(f"[layer] stale-state check batch={batch} seq={seq} heads={heads} d={d} inter={inter}")
+    shapes = {"q": (hidden, hidden), "k": (hidden, hidden), "v": (hidden, hidden), "o": (hidden, hidden),
+              "gate": (inter, hidden), "up": (inter, hidden), "down": (hidden, inter)}
+    Ws = {nm: I.custom_weight(n, k, 600 + i, scale=0.2 if nm in ("q", "k") else 0.05)
+          for i, (nm, (n, k)) in enumerate(shapes.items())}
+    ad = {nm: (I.custom_bf16((r, k), 700 + i, 1, bound=0.05), I.custom_bf16((n, r), 700 + i, 2, bound=0.05))
+          for i, (nm, (n, k)) in enumerate(shapes.items())}
+    X1, X2 = I.custom_bf16((M, hidden), 801, 1), I.custom_bf16((M, hidden), 802, 1)
+    dY = I.custom_bf16((M, hidden), 801, 2)
+    lay = DecoderLayer({nm: gpu_quantize(q, W) for nm, W in Ws.items()},
+                       {nm: (dev_bf16(A), dev_bf16(B)) for nm, (A, B) in ad.items()}, r, alpha, batch, seq, heads, d)
+    Y, dX = (torch.empty(M, hidden, dtype=torch.bfloat16, device="cuda") for _ in range(2))
+    X1d, dYd = dev_bf16(X1), dev_bf16(dY)
+    for nm in PROJ:
+        lay.H[nm].fill_(1e30)
+    lay.bwd(X1d, dYd, dX)
+    torch.cuda.synchronize()
+    ref = [dX.clone()] + [lay.dA[nm].clone() for nm in PROJ] + [lay.dB[nm].clone() for nm in PROJ]
+    lay.fwd(dev_bf16(X2), Y)
+    for nm in PROJ:
+        lay.H[nm].fill_(float("nan"))
+    lay.bwd(X1d, dYd, dX)
+    torch.cuda.synchronize()
+    got = [dX] + [lay.dA[nm] for nm in PROJ] + [lay.dB[nm] for nm in PROJ]
+    names = ["dX"] + [f"dA_{nm}" for nm in PROJ] + [f"dB_{nm}" for nm in PROJ]
+    for nm, a, b in zip(names, ref, got):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{nm} depends on the earlier forward"
+    params = {nm: (f64(OracleWeight(W).row_what_bits(np.arange(W.shape[0]))), f64(ad[nm][0]), f64(ad[nm][1]))
+              for nm, W in Ws.items()}
+    _, rg = olayer.bwd(f64(X1), f64(dY), params, alpha, batch, seq, heads, d, rnd)
+    assert_close(f64(host_bf16(lay.dA["down"])), rg["down"][0], "dA_down")
+    assert_close(f64(host_bf16(lay.dB["down"])), rg["down"][1], "dB_down")
