@@ -100,7 +100,9 @@ def layer_flops(M, N, K, r):
 
 
 # rocprofv3 kernel names -> the names the library's event timer uses
-KERNEL_ALIASES = {"k_nf4_tile<false>": "k_fwd_nf4", "k_nf4_tile<true>": "k_bwd_dx_nf4"}
+KERNEL_ALIASES = {"k_nf4_tile<false>": "k_fwd_nf4", "k_nf4_tile<true>": "k_bwd_dx_nf4",
+                  "k_nf4_tile<false, false>": "k_fwd_nf4", "k_nf4_tile<true, false>": "k_bwd_dx_nf4",
+                  "k_nf4_tile<false, true>": "k_fwd_bf16w"}
 
 
 def short_kernel_name(name: str) -> str:
