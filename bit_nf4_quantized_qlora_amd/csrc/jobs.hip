@@ -184,6 +184,10 @@ __global__ __launch_bounds__(256) void k_small_jobs(SmallJobs js) {
     case kJobReduceCols: run_reduce_cols(j, idx); break;
     case kJobScalesFwd: run_scales_fwd(j, idx); break;
     case kJobScalesBwd: run_scales_bwd(j, idx); break;
+    case kJobSplitReduce:
+      split_reduce_slot(static_cast<const f32x4_t *>(j.in), j.i, (int)j.c, j.j, j.a, j.b,
+                        static_cast<uint16_t *>(j.out), idx);
+      break;
     default: break;
   }
 }

@@ -9,7 +9,8 @@
 //                           split when the tiles cannot fill the GPU;
 //                           k_bwd_dx below when n % 64 != 0)
 //   dB = s dY^T H          (k_tn_splitk on dY and (sH)^T)
-//   dA = G^T X             (k_tn_splitk on X and G^T; one launch with dB's)
+//   dA = G^T X             (k_tn_splitk on X and G^T; one launch with dB's,
+//                           before the dX launch)
 // The small layout copies (B^T, A^T, (sH)^T), the tile kernel's block-scale
 // table and the partial reductions run as jobs.hip launches, several jobs
 // per launch.
@@ -233,24 +234,25 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
   // G = s dY B -> Gb [M][RP], Gt [RP][Mp]
   QLORA_TRY(launch_nt_splitk(dY, M, Bt, RP, RP, N, N, l.sp_g, part, s));
   QLORA_TRY(launch_reduce_rows(part, l.sp_g.splits, M, RP, r, a.s, nullptr, Gb, Gt, l.Mp, s));
+  // dB = dY^T sH and dA = G^T X: one launch of split partials (before the
+  // dX launch, so a split dX launch's reduction can share the launch of
+  // their fixed-order reductions)
+  float *part_b = part, *part_a = reinterpret_cast<float *>(base + l.part_off + l.parta_off);
+  QLORA_TRY(launch_tn_pair(TnProblem{dY, N, sHt, l.Mp, l.sp_b, true, part_b},
+                           TnProblem{X, K, Gt, l.Mp, l.sp_a, false, part_a}, M, RP, s));
+  SmallJob red[3] = {job_reduce_cols(part_b, l.sp_b.splits, N, RP, r, true, dB),
+                     job_reduce_cols(part_a, l.sp_a.splits, K, RP, r, false, dA), SmallJob{}};
   if (dX != nullptr) {
     if (tiles) {
       QLORA_TRY(launch_bwd_dx_tiles(a.w, scales, dY, M, At, RP, Gb, dX,
-                                    reinterpret_cast<float *>(base + l.tpart_off), s));
+                                    reinterpret_cast<float *>(base + l.tpart_off), s, &red[2]));
     } else {  // ragged n: the general 128 x 128 kernel
       const dim3 grid((unsigned)ceil_div(K, DBK), (unsigned)ceil_div(M, DBM));
       QLORA_LAUNCH("k_bwd_dx", k_bwd_dx, grid, dim3(256), 0, s, a.w, dY, M, At, Gb, RP, dX);
     }
     QLORA_TRY(hipGetLastError());
   }
-  // dB = dY^T sH and dA = G^T X: one launch of split partials, one of their
-  // fixed-order reductions
-  float *part_b = part, *part_a = reinterpret_cast<float *>(base + l.part_off + l.parta_off);
-  QLORA_TRY(launch_tn_pair(TnProblem{dY, N, sHt, l.Mp, l.sp_b, true, part_b},
-                           TnProblem{X, K, Gt, l.Mp, l.sp_a, false, part_a}, M, RP, s));
-  const SmallJob red[2] = {job_reduce_cols(part_b, l.sp_b.splits, N, RP, r, true, dB),
-                           job_reduce_cols(part_a, l.sp_a.splits, K, RP, r, false, dA)};
-  QLORA_TRY(launch_jobs("k_reduce_grads", red, 2, s));
+  QLORA_TRY(launch_jobs("k_reduce_grads", red, 3, s));
 #undef QLORA_TRY
   return hipSuccess;
 }

@@ -96,6 +96,7 @@ enum JobKind : int {
   kJobReduceCols,
   kJobScalesFwd,
   kJobScalesBwd,
+  kJobSplitReduce,  // a split tile launch's partials, summed in split order (nf4_tile.h)
 };
 struct SmallJob {
   int kind = 0;

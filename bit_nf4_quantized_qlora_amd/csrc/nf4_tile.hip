@@ -134,35 +134,12 @@ __device__ __forceinline__ void store_partial(const f32x4_t (&acc)[4][16], f32x4
     for (int ct = 0; ct < 16; ++ct) p[(rt * 16 + ct) * 256] = acc[rt][ct];
 }
 
-// out[m][o] = bf16( sum over s = 0 .. splits-1, in that order, of the
-// partial tiles ), one thread per float4 slot of the partial layout above.
+// out = bf16 of the partial tiles summed in split order, one thread per
+// float4 slot of the partial layout above.
 __global__ __launch_bounds__(256) void k_split_reduce(const f32x4_t *__restrict__ part, int splits, int ntiles,
                                                       int tiles_o, int64_t M, int64_t NO,
                                                       uint16_t *__restrict__ out) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t tj = blockIdx.x;  // tile * 64 + j
-  const int j = (int)(tj & 63);
-  const int64_t tile = tj >> 6;
-  const int64_t to = tile % tiles_o, mt = tile / tiles_o;
-  const int64_t o = to * TO + 64 * wave + 16 * (j >> 4) + 4 * (lane >> 4);
-  const int64_t m = mt * TM + 16 * (j & 15) + (lane & 15);
-  if (m >= M || o >= NO) return;
-  const int64_t slot = tj * 256 + t, stride = (int64_t)ntiles * 64 * 256;
-  f32x4_t a = part[slot];
-  for (int s = 1; s < splits; ++s) {
-    const f32x4_t b = part[s * stride + slot];
-    a = f32x4_t{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
-  }
-  uint16_t *dst = out + m * NO + o;
-  if ((NO & 3) == 0) {
-    *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{bf16x2_rne(a[0], a[1]), bf16x2_rne(a[2], a[3])};
-  } else {
-    const uint32_t lo = bf16x2_rne(a[0], a[1]), hi = bf16x2_rne(a[2], a[3]);
-    const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (o + v < NO) dst[v] = e[v];
-  }
+  split_reduce_slot(part, splits, ntiles, tiles_o, M, NO, out, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 // Grid: tiles x splits workgroups.  With splits > 1, workgroup (tile, s)
@@ -691,14 +668,34 @@ hipError_t launch_fwd_tiles_bf16w(const uint16_t *Wb, int64_t n, int64_t k, cons
 }
 #endif
 
+SmallJob job_split_reduce(const TileSplit &sp, int tiles_o, int tiles_m, int64_t M, int64_t NO, const float *tpart,
+                          uint16_t *out) {
+  SmallJob j;
+  j.kind = kJobSplitReduce;
+  j.count = sp.splits > 1 ? (int64_t)tiles_o * tiles_m * 64 * 256 : 0;
+  j.in = tpart;
+  j.out = out;
+  j.a = M;
+  j.b = NO;
+  j.c = (int64_t)tiles_o * tiles_m;
+  j.i = sp.splits;
+  j.j = tiles_o;
+  return j;
+}
+
 hipError_t launch_bwd_dx_tiles(const Nf4View &w, float *scales, const uint16_t *dY, int64_t M, const uint16_t *At,
-                               int RP, const uint16_t *Gb, uint16_t *dX, float *tpart, hipStream_t s) {
+                               int RP, const uint16_t *Gb, uint16_t *dX, float *tpart, hipStream_t s,
+                               SmallJob *split_job) {
   const int tiles_o = (int)ceil_div(w.k, TO), tiles_m = (int)ceil_div(M, TM);
   const TileSplit sp = plan_dx_tiles(M, w.n, w.k);
   QLORA_LAUNCH("k_bwd_dx_nf4", k_nf4_tile<true>, dim3((unsigned)(tiles_o * tiles_m * sp.splits)), dim3(256), 0, s,
                w, scales, dY, M, At, RP, RP, Gb, dX, tiles_o, sp.splits, sp.lsteps,
                reinterpret_cast<f32x4_t *>(tpart), nullptr);
   hipError_t e = hipGetLastError();
+  if (split_job) {
+    *split_job = job_split_reduce(sp, tiles_o, tiles_m, M, w.k, tpart, dX);
+    return e;
+  }
   if (e != hipSuccess || sp.splits == 1) return e;
   return reduce_splits("k_split_reduce", sp, tiles_o, tiles_m, M, w.k, tpart, dX, s);
 }
