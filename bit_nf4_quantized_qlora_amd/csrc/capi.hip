@@ -165,7 +165,7 @@ int check_ws(void *ws, size_t have, size_t need) {
 // (every GPU the library runs on holds its own copy until the process ends).
 // In host code `scratch` names a host-side stand-in; kernels get the device
 // address hipGetSymbolAddress returns, looked up once per device.
-constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+constexpr size_t kNoallocScratchBytes = size_t(128) << 20;
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices] = {};
@@ -435,7 +435,8 @@ int fwd_impl(const char *fn, const WeightIn &w, const uint16_t *X, int64_t M, co
   if (int e = check_tensor(B, "B")) return e;
   if (int e = check_tensor(Y, "Y")) return e;
   if (H_out && !aligned16(H_out)) return fail(QLORA_ERR_MISALIGNED, "H_out is not 16-byte aligned");
-  if (int e = check_ws(ws, ws_bytes, fwd_workspace_bytes(M, w.n, w.k, r))) return e;
+  if (int e = check_ws(ws, ws_bytes, fwd_workspace_bytes_for(M, w.n, w.k, r, w.scales == QLORA_SCALES_FP32)))
+    return e;
   LinearArgs a{view_of(w), M, r, (float)alpha / (float)r};
   hipError_t e = launch_linear_fwd(a, X, A, B, Y, H_out, ws, s);
   if (e != hipSuccess) return hip_fail(e, fn);
@@ -500,7 +501,7 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64
   if (int e = take(w, &v)) return e;
   if (int e = check_linear(v, M, r, alpha)) return e;
   if (M == 0) return QLORA_OK;
-  const size_t need = fwd_workspace_bytes(M, v.n, v.k, r);
+  const size_t need = fwd_workspace_bytes_for(M, v.n, v.k, r, false);
   if (need > kNoallocScratchBytes)
     return fail(QLORA_ERR_WORKSPACE,
                 "qlora_linear_fwd_noalloc: M = %lld, [%lld, %lld], r = %d needs %zu bytes of scratch, above the "

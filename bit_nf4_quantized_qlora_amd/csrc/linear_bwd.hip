@@ -179,7 +179,7 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, int r) {
   l.gb_off = take((size_t)M * l.RP * 2);
   l.gt_off = take((size_t)l.RP * l.Mp * 2);
   l.scale_off = take(tile_scales_bytes(N, K));
-  l.tpart_off = take(tile_partial_bytes(M, N, K));
+  l.tpart_off = take(tile_dx_partial_bytes(M, N, K));
   l.total = off;
   return l;
 }

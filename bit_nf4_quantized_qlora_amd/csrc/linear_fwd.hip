@@ -26,6 +26,7 @@ struct FwdWs {
   size_t part_off, sh_off, scale_off, tpart_off, total;
 };
 
+// Tile-path layout (the small-M GEMV path lays out its own workspace).
 FwdWs fwd_ws_layout(int64_t M, int64_t n, int64_t k, int r) {
   FwdWs l;
   l.RP = lora_rank_pad(r);
@@ -34,14 +35,21 @@ FwdWs fwd_ws_layout(int64_t M, int64_t n, int64_t k, int r) {
   l.sh_off = align_up((size_t)l.sp.splits * M * l.RP * sizeof(float), 256);
   l.scale_off = l.sh_off + align_up((size_t)M * l.RP * sizeof(uint16_t), 256);
   l.tpart_off = l.scale_off + align_up(tile_scales_bytes(n, k), 256);
-  l.total = l.tpart_off + align_up(tile_partial_bytes(M, n, k), 256);
-  if (small_m_supported(M, n, k, r)) l.total = std::max(l.total, small_m_workspace_bytes(M, n, k, r));
+  l.total = l.tpart_off + align_up(tile_fwd_partial_bytes(M, n, k), 256);
   return l;
 }
 
 }  // namespace
 
-size_t fwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r) { return fwd_ws_layout(M, n, k, r).total; }
+size_t fwd_workspace_bytes_for(int64_t M, int64_t n, int64_t k, int r, bool single_level) {
+  if (plan_linear(M, n, k, r, single_level).fwd_path == QLORA_PATH_GEMV) return small_m_workspace_bytes(M, n, k, r);
+  return fwd_ws_layout(M, n, k, r).total;
+}
+
+// Either storage type's need (the public query does not know the type).
+size_t fwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r) {
+  return std::max(fwd_workspace_bytes_for(M, n, k, r, false), fwd_workspace_bytes_for(M, n, k, r, true));
+}
 
 LinearPlan plan_linear(int64_t M, int64_t n, int64_t k, int r, bool single_level) {
   LinearPlan p;

@@ -30,8 +30,10 @@ struct TileSplit {
 TileSplit plan_tile_split(int64_t tiles, int64_t nk, int64_t M, int64_t NO);
 TileSplit plan_fwd_tiles(int64_t M, int64_t n, int64_t k);
 TileSplit plan_dx_tiles(int64_t M, int64_t n, int64_t k);
-// Device bytes of the partial tiles either launch writes (0 when unsplit).
-size_t tile_partial_bytes(int64_t M, int64_t n, int64_t k);
+// Device bytes of the partial tiles the forward / the dX tile launch writes
+// (0 when unsplit).
+size_t tile_fwd_partial_bytes(int64_t M, int64_t n, int64_t k);
+size_t tile_dx_partial_bytes(int64_t M, int64_t n, int64_t k);
 
 // One float4 slot of a split launch's partial tiles (slot = (tile * 64 + j)
 // * 256 + t, the tile kernel's register order): out[m][o..o+3] = bf16( sum
@@ -80,7 +82,7 @@ SmallJob job_scales_bwd(const Nf4View &w, float *scales);
 // Y[M, n] = bf16( X W_hat^T + sH B_lora^T ):  X [M, k], sH [M, RP] = bf16(s H)
 // with the rank padded to RP by zeros, B_lora [n, r] (row stride r).
 // `scales`: the table job_scales_fwd wrote.
-// `tpart`: device scratch of tile_partial_bytes (may be NULL when it is 0).
+// `tpart`: device scratch of tile_fwd_partial_bytes (may be NULL when it is 0).
 hipError_t launch_fwd_tiles(const Nf4View &w, float *scales, const uint16_t *X, int64_t M, const uint16_t *Bl, int r,
                             int RP, const uint16_t *sH, uint16_t *Y, float *tpart, hipStream_t s);
 

@@ -583,7 +583,9 @@ bool bwd_tiles_supported(int64_t n, int64_t k) {
 // Contraction splits of a tile launch.  Cost in units of one 64-wide step of
 // a tile (~1.6 us): rounds of 256 workgroups x (steps per split + ~4 for the
 // prologue and epilogue), plus, when split, the float32 partials written
-// and read back once (~8 MB per unit) and the reduction launch (~2 units).
+// and read back once (~16 MB per unit: the writes overlap other workgroups'
+// steps and the reads mostly hit the last-level cache; measured on the 4096
+// and 8192 square layers at M = 512) and the reduction launch (~2 units).
 // Only launches with too few tiles to fill the 256 CUs gain; the others
 // stay at one split.
 TileSplit plan_tile_split(int64_t tiles, int64_t nk, int64_t M, int64_t NO) {
@@ -595,7 +597,7 @@ TileSplit plan_tile_split(int64_t tiles, int64_t nk, int64_t M, int64_t NO) {
   if (nk <= 8 || tiles < 1) return best;  // nothing to split
   auto cost = [&](int64_t S, int64_t L) {
     const double rounds = (double)ceil_div(tiles * S, 256);
-    const double red = S > 1 ? 2.0 * S * tiles * 65536.0 * 4.0 / 8e6 + 2.0 : 0.0;
+    const double red = S > 1 ? 2.0 * S * tiles * 65536.0 * 4.0 / 16e6 + 2.0 : 0.0;
     return rounds * (double)(L + 4) + red;
   };
   double bc = cost(1, best.lsteps);
@@ -621,15 +623,15 @@ TileSplit plan_dx_tiles(int64_t M, int64_t n, int64_t k) {
   return plan_tile_split(ceil_div(k, TO) * ceil_div(M, TM), n / kBlock, M, k);
 }
 
-size_t tile_partial_bytes(int64_t M, int64_t n, int64_t k) {
+size_t tile_fwd_partial_bytes(int64_t M, int64_t n, int64_t k) {
   const TileSplit f = plan_fwd_tiles(M, n, k);
-  const size_t pf = f.splits > 1 ? (size_t)f.splits * ceil_div(n, TO) * ceil_div(M, TM) * 65536 * 4 : 0;
-  size_t pb = 0;
-  if (bwd_tiles_supported(n, k)) {
-    const TileSplit b = plan_dx_tiles(M, n, k);
-    pb = b.splits > 1 ? (size_t)b.splits * ceil_div(k, TO) * ceil_div(M, TM) * 65536 * 4 : 0;
-  }
-  return std::max(pf, pb);
+  return f.splits > 1 ? (size_t)f.splits * ceil_div(n, TO) * ceil_div(M, TM) * 65536 * 4 : 0;
+}
+
+size_t tile_dx_partial_bytes(int64_t M, int64_t n, int64_t k) {
+  if (!bwd_tiles_supported(n, k)) return 0;
+  const TileSplit b = plan_dx_tiles(M, n, k);
+  return b.splits > 1 ? (size_t)b.splits * ceil_div(k, TO) * ceil_div(M, TM) * 65536 * 4 : 0;
 }
 
 namespace {

@@ -65,6 +65,8 @@ struct LinearArgs {
 };
 
 size_t fwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r);
+// The forward workspace of the path one storage type's call takes.
+size_t fwd_workspace_bytes_for(int64_t M, int64_t n, int64_t k, int r, bool single_level);
 
 // The kernels a call of this shape runs (QLORA_PATH_*; splits of the tile
 // launches' contraction): the one decision the launches and

@@ -204,16 +204,16 @@ int qlora_linear_bwd_ex(const qlora_weight_ex *w, const uint16_t *X, const uint1
  * qlora_linear_fwd without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, kernels and results as
- * qlora_linear_fwd (bit for bit); the workspace is instead a fixed 64 MiB
+ * qlora_linear_fwd (bit for bit); the workspace is instead a fixed 128 MiB
  * array of device memory inside the library, one per GPU it runs on, held
- * until the process ends.  Shapes whose qlora_linear_workspace_bytes-style
- * forward workspace exceeds 64 MiB return QLORA_ERR_WORKSPACE (the 7B MLP
- * layers at M = 4096, the 7B q_proj at M = 512 and every M <= 16 fit; the
- * 65B q/k/v/o/down layers at M = 512 do not).  Every call on one GPU shares
- * that GPU's array: calls that overlap on one GPU (two streams, two host
- * threads) race and must be serialized by the caller.  Uses the current
- * device's array; `stream` must belong to the current device.  Nothing in
- * the array needs to start at zero: every call writes what it reads.
+ * until the process ends.  Shapes whose forward workspace exceeds 128 MiB
+ * return QLORA_ERR_WORKSPACE (every layer of the benchmark workloads fits:
+ * the largest, a 65B down projection at M = 512, needs ~80 MB).  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (two
+ * streams, two host threads) race and must be serialized by the caller.
+ * Uses the current device's array; `stream` must belong to the current
+ * device.  Nothing in the array needs to start at zero: every call writes
+ * what it reads.
  */
 int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64_t M, const uint16_t *A,
                              const uint16_t *B, int r, float alpha, uint16_t *Y, float *H_out, hipStream_t stream);

@@ -213,7 +213,7 @@ def test_argument_errors_enqueue_nothing(q):
         q.QLORA_ERR_BAD_CODEBOOK
     # the allocation-free forward: shapes beyond its fixed scratch are rejected before any GPU use
     noalloc = lib.qlora_linear_fwd_noalloc
-    big = q.qlora_nf4_weight(8192, 8192, 16, 16, 16, 16)
+    big = q.qlora_nf4_weight(262144, 8192, 16, 16, 16, 16)   # a 128 MB block-scale table alone
     assert noalloc(ctypes.byref(big), P, 512, P, P, 64, 16.0, P, None, None) == q.QLORA_ERR_WORKSPACE
     assert "scratch" in q.qlora_last_error()
     assert noalloc(ctypes.byref(W), P, 16, P, P, 0, 16.0, P, None, None) == q.QLORA_ERR_BAD_RANK

@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 # (n, k, M, r, alpha, seed); the first of each pair is the larger problem
 SEQUENCES = {
-    "tile": [(2048, 4096, 512, 64, 16.0, 71),   # tile path, contraction split 8 ways (~34 MB of scratch)
+    "tile": [(4096, 4096, 512, 64, 16.0, 71),   # the 7B q_proj shape: contraction split 8 ways (~69 MB of scratch)
              (640, 512, 37, 8, -2.0, 72)],      # tile path, one split, ragged M
     "gemv": [(4096, 8192, 16, 16, 16.0, 73),    # small-M GEMV, M = 16
              (300, 768, 5, 100, 32.0, 74)],     # GEMV, two ragged row groups, rank 100
