@@ -11,27 +11,36 @@
 //   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d).
 //
 // Q, K, V, O (and their gradients) are [batch * seq, heads * d] row-major
-// bf16, the projections' outputs as they come.  The scores are materialised
-// per (sequence, head) in the workspace: float32 S and dP, bf16 P and dS,
-// each [batch][heads][seq][ldp] with ldp = seq rounded up to 8.  At the
-// LLaMA-7B layer (32 heads of 128, sequence 512) that is 6 MB per sequence,
-// and the six products are small next to the seven projections.
+// bf16, the projections' outputs as they come.
 //
-// Products: one batched MFMA kernel, 64 x 64 output tiles, 4 waves of 2 x 2
-// 16x16x32 bf16 MFMAs, a 64-deep contraction step staged through LDS with
-// the next step's operands loaded into registers meanwhile.  Each operand is
-// read along whichever axis is contiguous in memory (template flags) and
-// staged as it lies; fragments of row-contiguous operands come from
-// transposing LDS reads.  Causality prunes work: score tiles wholly above
-// the diagonal are skipped, and the products with P or dS stop (or start)
-// their contraction at the tile's diagonal.
+// Head dims 32, 64 and 128 (the LLaMA layers') take fused kernels that keep
+// no score matrix in memory: a forward with an online softmax, and a
+// backward in two launches, a query side (D_i = sum_j P_ij dP_ij from the
+// row's own float32 P and dP, then dQ) and a key side (dK, dV).  Each
+// recomputes S and dP per 64-row block on MFMA; P and dS are rounded to
+// bf16 in the lane that computes them, the same rounding points as the
+// materialised path below.
 //
-// Row kernels: one wave per query row.  The forward softmax takes the row
-// maximum and the sum of exponentials in float32 and writes P and lse; the
-// backward row pass recomputes P = exp(S - lse), sums D from P and dP, and
-// writes P and dS.  Both
-// write zeros for the masked entries up to the end of the diagonal tile,
-// the only masked entries a product reads.
+// Other head dims materialise the scores per (sequence, head) in the
+// workspace: float32 S and dP, bf16 P and dS, each [batch][heads][seq][ldp]
+// with ldp = seq rounded up to 8.
+//
+// Products of the materialised path: one batched MFMA kernel, 64 x 64
+// output tiles, 4 waves of 2 x 2 16x16x32 bf16 MFMAs, a 64-deep contraction
+// step staged through LDS with the next step's operands loaded into
+// registers meanwhile.  Each operand is read along whichever axis is
+// contiguous in memory (template flags) and staged as it lies; fragments of
+// row-contiguous operands come from transposing LDS reads.  Causality
+// prunes work: score tiles wholly above the diagonal are skipped, and the
+// products with P or dS stop (or start) their contraction at the tile's
+// diagonal.
+//
+// Row kernels of the materialised path: one wave per query row.  The
+// forward softmax takes the row maximum and the sum of exponentials in
+// float32 and writes P and lse; the backward row pass recomputes
+// P = exp(S - lse), sums D from P and dP, and writes P and dS.  Both write
+// zeros for the masked entries up to the end of the diagonal tile, the only
+// masked entries a product reads.
 #include <cmath>
 
 #include "qlora_internal.h"
@@ -40,6 +49,14 @@ namespace qlora {
 namespace {
 
 constexpr int kT = 64;          // output tile edge
+
+// Exponentials in base 2 on the hardware's v_exp_f32 / v_log_f32 (about one
+// ulp; exp2(-inf) = 0): the kernels carry scores in base-2 exponent units,
+// s * scale * log2(e), and lse in natural units.
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.69314718055994530942f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 constexpr int kKs = 64;         // contraction per step (two 32-deep MFMA sub-steps)
 constexpr int kLd = kKs + 8;    // LDS row stride in elements (144 B: a 16-lane fragment read is conflict-free)
 
@@ -340,75 +357,103 @@ __global__ __launch_bounds__(256) void k_attn_bwd_rows(const float *__restrict__
   }
 }
 
-// V^T for the fused forward: Vt[sequence][head][dim][key] (rows of ldp keys,
-// zeros past the sequence), so the fused kernel stages V^T tiles with
-// 16-byte row copies; transposing inside it took 2-byte LDS stores that
-// fell on two banks.  One workgroup per (64 keys, head, sequence): coalesced
-// 16-byte row loads into LDS, 16-byte stores of 8 keys of one dim.
-template <int D>
-__global__ __launch_bounds__(256) void k_attn_vt(const uint16_t *__restrict__ Vg, uint16_t *__restrict__ Vt, int seq,
-                                                 int heads, int64_t ldp) {
-  constexpr int kLd = D + 8;
-  __shared__ __align__(16) uint16_t sv[kT * kLd];
-  const int k0 = blockIdx.x * kT;
-  const int64_t h = blockIdx.y, b = blockIdx.z;
-  const int64_t ld = (int64_t)heads * D;
-  const int t = threadIdx.x;
-  for (int i = t; i < kT * (D / 8); i += 256) {
-    const int key = k0 + i / (D / 8), col = 8 * (i % (D / 8));
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (key < seq) v = *reinterpret_cast<const u32x4_t *>(Vg + (b * seq + key) * ld + h * D + col);
-    *reinterpret_cast<u32x4_t *>(sv + (i / (D / 8)) * kLd + col) = v;
-  }
-  __syncthreads();
-  uint16_t *out = Vt + (b * heads + h) * D * ldp;
-  for (int i = t; i < D * (kT / 8); i += 256) {
-    const int dim = i / (kT / 8), kk = 8 * (i % (kT / 8));
-    if (k0 + kk >= ldp) continue;
-    u32x4_t v;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v[j] = (uint32_t)sv[(kk + 2 * j) * kLd + dim] | ((uint32_t)sv[(kk + 2 * j + 1) * kLd + dim] << 16);
-    *reinterpret_cast<u32x4_t *>(out + dim * ldp + k0 + kk) = v;
-  }
+// Fused kernels (head dims 32, 64, 128).  Each workgroup streams 64-row
+// blocks of the other side's operands (K and V for a query tile, Q and dO
+// for a key tile) through LDS, rows staged as they lie with row stride
+// D + kRowPad, in two stages: block i is read while block i+1 is stored and
+// block i+2 is loaded into registers, one barrier per block.  Fragments of
+// a staged operand are 16-byte row reads (rows as MFMA rows, dims as the
+// contraction) or transposing reads (dims as MFMA rows, rows as the
+// contraction, at the rows whose scores the lane holds).  A row stride of
+// D + 16 puts the four rows of a transposing read's 16-lane group on four
+// disjoint bank octets (D + 8 doubled those reads: 105 against 117 us key
+// side, 132 against 150 us query side at 8 x 512 x 32 x 128).
+constexpr int kRowPad = 16;
+constexpr int kQT = 128;                    // queries per fused-forward workgroup (8 waves)
+constexpr int kBwdWaves = 8;                // waves per backward workgroup, 16 queries or keys each
+constexpr int kBwdRows = 16 * kBwdWaves;    // queries (keys) per query-side (key-side) backward workgroup
+
+// Two transposing LDS reads (ds_read_b64_tr_b16): lane (g = l >> 4,
+// i = l & 15) receives X[r0 + 4g + e][c0 + i] for e = 0..3, then
+// X[r1 + 4g + e][c0 + i], from a row-major LDS array X (row stride ld
+// elements, a multiple of 8).  As an MFMA operand that is row c0 + i of X^T
+// with contraction slots 8g .. 8g+3 on rows r0 + 4g .. +3 and 8g+4 .. 8g+7
+// on rows r1 + 4g .. +3: the rows whose scores accumulator lanes of group g
+// hold in the 16-row output tiles at r0 and r1.
+__device__ __forceinline__ u32x4_t lds_frag_t2(const uint16_t *X, int ld, int r0, int r1, int c0, int lane) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const int j = lane & 15, g = lane >> 4;
+  const int off = (4 * g + (j >> 2)) * ld + c0 + 4 * (j & 3);
+  const s16x4_t h0 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(X + r0 * ld + off));
+  const s16x4_t h1 =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t *)(X + r1 * ld + off));
+  return __builtin_bit_cast(u32x4_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Fused forward for head dims 32, 64, 128: one workgroup of 8 waves per
-// (sequence, head, 128-query tile), wave w on queries q0 + 16w .. +15, so a
-// staged key block serves 128 queries; no score matrix in memory.  Per 64-key block (causal: blocks up to the diagonal one):
+// 64 rows of an operand [row][D] (rows past the sequence zero) in kPL
+// 16-byte pieces per thread of an NT-thread workgroup: piece e is row
+// e / (D/8), columns 8 (e % (D/8)) .. +7.
+template <int D, int NT>
+struct Rows64 {
+  static constexpr int kPieces = 8 * D;
+  static constexpr int kPL = (kPieces + NT - 1) / NT;
+  static constexpr int kLd = D + kRowPad;  // LDS row stride (elements)
+  u32x4_t r[kPL];
+  __device__ __forceinline__ void load(const uint16_t *g, int64_t ld, int row0, int seq, int t) {
+#pragma unroll
+    for (int i = 0; i < kPL; ++i) {
+      const int e = t + NT * i;
+      r[i] = u32x4_t{0u, 0u, 0u, 0u};
+      if (e < kPieces) {
+        const int row = row0 + e / (D / 8);
+        if (row < seq) r[i] = *reinterpret_cast<const u32x4_t *>(g + (int64_t)row * ld + 8 * (e % (D / 8)));
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t *lds, int t) const {
+#pragma unroll
+    for (int i = 0; i < kPL; ++i) {
+      const int e = t + NT * i;
+      if (e < kPieces) *reinterpret_cast<u32x4_t *>(lds + (e / (D / 8)) * kLd + 8 * (e % (D / 8))) = r[i];
+    }
+  }
+};
+
+// Fused forward: one workgroup of 8 waves per (sequence, head, 128-query
+// tile), wave w on queries q0 + 16w .. +15, so a staged key block serves 128
+// queries; no score matrix in memory.  Per 64-key block (causal: blocks up
+// to the diagonal one; a wave skips blocks wholly past its queries):
 //   S^T = K Q^T on MFMA (A = K rows from LDS, B = Q from registers), so each
 //   lane's accumulators all belong to one query (its column l & 15): the
-//   online softmax (running max m, lane-partial sum l, rescale of the
-//   output) needs only a max over the lane's 16 values and lanes l ^ 16, 32;
+//   online softmax (running max m in base-2 units, lane-partial sum l,
+//   rescale of the output when some lane's maximum grew) needs only a max
+//   over the lane's 16 values and lanes l ^ 16, 32;
 //   O^T += V^T P^T on MFMA with P rounded to bf16: the MFMA contraction
 //   slots 8g .. 8g+7 of lane group g = l >> 4 are assigned to the keys that
 //   lane already holds (4g .. 4g+3 of two 16-key tiles), so P goes from
-//   accumulator to operand without moving between lanes, and V^T is read
-//   from a transposed LDS copy at the same keys.
-// V^T comes from the copy k_attn_vt writes.  The next block's K and V^T
-// are loaded into registers while this block computes.  Keys past the
-// sequence are zero in LDS and masked to -inf.
-constexpr int kQT = 128;  // queries per fused-forward workgroup
+//   accumulator to operand without moving between lanes, and V^T comes from
+//   transposing reads of the staged V rows at the same keys.
+// Only the diagonal block masks (keys past the query, which covers keys past
+// the sequence for every query in it).
 template <int D>
 __global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restrict__ Qg, const uint16_t *__restrict__ Kg,
-                                                        const uint16_t *__restrict__ Vt, uint16_t *__restrict__ Og,
-                                                        float *__restrict__ lse, int seq, int heads, int64_t ldp,
-                                                        float scale) {
-  constexpr int kLdK = D + 8, kLdV = kT + 8;   // LDS row strides (elements)
-  constexpr int kPieces = 8 * D;               // 16-byte pieces per staged block and operand (64 x D / 8)
-  constexpr int kKL = (kPieces + 511) / 512;   // per thread
-  __shared__ __align__(16) uint16_t sK[kT * kLdK];
-  __shared__ __align__(16) uint16_t sVt[D * kLdV];
+                                                        const uint16_t *__restrict__ Vg, uint16_t *__restrict__ Og,
+                                                        float *__restrict__ lse, int seq, int heads, float scale) {
+  using R = Rows64<D, 512>;
+  constexpr int kLd = R::kLd;
+  __shared__ __align__(16) uint16_t sK[2][kT * kLd];
+  __shared__ __align__(16) uint16_t sV[2][kT * kLd];
   const int ntq = (seq + kQT - 1) / kQT;
-  const int tq = ntq - 1 - (int)blockIdx.x;   // the longest query tiles start first
-  const int q0 = tq * kQT;
+  const int q0 = (ntq - 1 - (int)blockIdx.x) * kQT;  // the longest query tiles start first
   const int64_t h = blockIdx.y, b = blockIdx.z;
   const int64_t ld = (int64_t)heads * D;
   const int64_t base = b * seq * ld + h * D;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 4, c = lane & 15;
-  const int qi = q0 + 16 * w + c;             // this lane's query
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int qw = q0 + 16 * w, qi = qw + c;  // this wave's first query, this lane's query
 
-  u32x4_t qf[D / 32];                          // B operand of K Q^T: Q[qi][32 ks + 8 g ..]
+  u32x4_t qf[D / 32];  // B operand of K Q^T: Q[qi][32 ks + 8 g ..]
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
     qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
@@ -418,40 +463,31 @@ __global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restri
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) acc_o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, l = 0.f;
+  const float c2 = scale * kLog2e;  // scores in base-2 exponent units
 
-  // staging, kKL 16-byte pieces per thread and operand: piece e is K row
-  // e / (D/8), dims 8 (e % (D/8)) .. +7, and V^T row (dim) e / 8, keys
-  // 8 (e % 8) .. +7 of the transposed copy
-  const uint16_t *vt = Vt + (b * heads + h) * D * ldp;
-  u32x4_t rk[kKL], rv[kKL];
-  auto load_block = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < kKL; ++i) {
-      const int e = t + 512 * i;
-      rk[i] = rv[i] = u32x4_t{0u, 0u, 0u, 0u};
-      if (e < kPieces) {
-        const int key = k0 + e / (D / 8), col = 8 * (e % (D / 8));
-        if (key < seq) rk[i] = *reinterpret_cast<const u32x4_t *>(Kg + base + key * ld + col);
-        const int dim = e / 8, kk = k0 + 8 * (e % 8);
-        if (kk < ldp) rv[i] = *reinterpret_cast<const u32x4_t *>(vt + dim * ldp + kk);
-      }
-    }
-  };
   const int nblk = min((seq + kT - 1) / kT, (q0 + kQT) / kT);  // key blocks up to the diagonal
-  load_block(0);
+  R rk, rv;
+  rk.load(Kg + base, ld, 0, seq, t);
+  rv.load(Vg + base, ld, 0, seq, t);
+  rk.store(sK[0], t);
+  rv.store(sV[0], t);
+  if (nblk > 1) {
+    rk.load(Kg + base, ld, kT, seq, t);
+    rv.load(Vg + base, ld, kT, seq, t);
+  }
   for (int kb = 0; kb < nblk; ++kb) {
     const int k0 = kb * kT;
-    __syncthreads();  // the previous block's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < kKL; ++i) {
-      const int e = t + 512 * i;
-      if (e < kPieces) {
-        *reinterpret_cast<u32x4_t *>(sK + (e / (D / 8)) * kLdK + 8 * (e % (D / 8))) = rk[i];
-        *reinterpret_cast<u32x4_t *>(sVt + (e / 8) * kLdV + 8 * (e % 8)) = rv[i];
+    const uint16_t *cK = sK[kb & 1], *cV = sV[kb & 1];
+    __syncthreads();  // stage kb & 1 is stored; every read of the other stage (block kb - 1) is done
+    if (kb + 1 < nblk) {
+      rk.store(sK[(kb + 1) & 1], t);
+      rv.store(sV[(kb + 1) & 1], t);
+      if (kb + 2 < nblk) {
+        rk.load(Kg + base, ld, k0 + 2 * kT, seq, t);
+        rv.load(Vg + base, ld, k0 + 2 * kT, seq, t);
       }
     }
-    __syncthreads();
-    if (kb + 1 < nblk) load_block(k0 + kT);
+    if (k0 > qw + 15) continue;  // every key of the block follows every query of this wave
 
     // S^T for 4 key tiles of 16
     f32x4_t st[4];
@@ -459,35 +495,38 @@ __global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restri
     for (int kt = 0; kt < 4; ++kt) {
       st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) st[kt] = mfma16(lds_frag(sK, kLdK, 16 * kt, 32 * ks, lane), qf[ks], st[kt]);
+      for (int ks = 0; ks < D / 32; ++ks) st[kt] = mfma16(lds_frag(cK, kLd, 16 * kt, 32 * ks, lane), qf[ks], st[kt]);
+    }
+    if (k0 + kT - 1 > qw) {  // the diagonal block
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (k0 + 16 * kt + 4 * g + v > qi) st[kt][v] = -INFINITY;
     }
     float bm = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int key = k0 + 16 * kt + 4 * g + v;
-        const float x = (key <= qi && key < seq) ? st[kt][v] * scale : -INFINITY;
-        st[kt][v] = x;
-        bm = fmaxf(bm, x);
-      }
+    for (int kt = 0; kt < 4; ++kt) bm = fmaxf(bm, fmaxf(fmaxf(st[kt][0], st[kt][1]), fmaxf(st[kt][2], st[kt][3])));
     bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
     bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    // finite: block 0 holds key 0 <= qi; a later block whose keys all lie
-    // past this wave's queries leaves m unchanged (corr = 1, e = 0)
-    const float mn = fmaxf(m, bm);
-    const float corr = expf(m - mn);
-    m = mn;
-    l *= corr;
+    // finite for a lane whose query is in the sequence: block 0 holds key 0
+    // <= qi, and a later diagonal block holds keys up to qi or leaves
+    // bm = -inf (m unchanged)
+    const float mn = fmaxf(m, bm * c2);
+    if (__any(mn > m)) {  // rescale only when some running maximum grew
+      const float corr = exp2_fast(m - mn);
+      l *= corr;
 #pragma unroll
-    for (int i = 0; i < D / 16; ++i) acc_o[i] *= corr;
+      for (int i = 0; i < D / 16; ++i) acc_o[i] *= corr;
+    }
+    m = mn;
     uint32_t pw[4][2];  // P as bf16 pairs: tile kt, keys 4g + (0,1) and (2,3)
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       float e[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        e[v] = expf(st[kt][v] - mn);
+        e[v] = exp2_fast(fmaf(st[kt][v], c2, -mn));
         l += e[v];
       }
       pw[kt][0] = bf16x2_rne(e[0], e[1]);
@@ -498,13 +537,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restri
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t pb = {pw[2 * ks][0], pw[2 * ks][1], pw[2 * ks + 1][0], pw[2 * ks + 1][1]};
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const uint16_t *vr = sVt + (16 * dt + c) * kLdV + 32 * ks + 4 * g;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vr);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vr + 16);
-        const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
-        acc_o[dt] = mfma16(va, pb, acc_o[dt]);
-      }
+      for (int dt = 0; dt < D / 16; ++dt)
+        acc_o[dt] = mfma16(lds_frag_t2(cV, kLd, 32 * ks, 32 * ks + 16, 16 * dt, lane), pb, acc_o[dt]);
     }
   }
   l += __shfl_xor(l, 16, 64);
@@ -518,7 +552,293 @@ __global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restri
                          bf16x2_rne(acc_o[dt][2] * inv, acc_o[dt][3] * inv)};
       *reinterpret_cast<u32x2_t *>(orow + 16 * dt + 4 * g) = o;
     }
-    if (g == 0) lse[(b * heads + h) * seq + qi] = m + logf(l);
+    if (g == 0) lse[(b * heads + h) * seq + qi] = (m + log2_fast(l)) * kLn2;
+  }
+}
+
+// Backward, query side, for head dims 32, 64, 128: one workgroup of 8 waves
+// per (sequence, head, 128-query tile), wave w on queries q0 + 16w .. +15,
+// key blocks of 64 (K and V rows staged in LDS as they lie, the next block
+// loaded into registers meanwhile) up to the diagonal, twice:
+//   pass 1: S^T = K Q^T and dP^T = V dO^T on MFMA (A from LDS, B = the
+//     lane's query row of Q or dO in registers), P = exp(S - lse), and each
+//     lane sums P dP over its keys; the sums of the four lane groups give
+//     D = sum_j P_j dP_j for the lane's query (float32, from the row's own
+//     P and dP, as the materialised path sums it), written for the key side;
+//   pass 2: the same S^T and dP^T, dS^T = P^T (dP^T - D) rounded to bf16 in
+//     the lane that computed it, dQ^T += K^T dS^T on MFMA with K^T read from
+//     the staged K rows by transposing LDS reads at the keys the lane holds
+//     (contraction slots as in the forward's O^T = V^T P^T).
+// Blocks wholly past a wave's queries are skipped; only diagonal blocks
+// mask.  A lane whose query lies past the sequence takes lse = +inf, so its
+// P is 0, and writes nothing.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_bwd_q(const uint16_t *__restrict__ Qg, const uint16_t *__restrict__ Kg,
+                                                    const uint16_t *__restrict__ Vg, const uint16_t *__restrict__ dOg,
+                                                    const float *__restrict__ lse, float *__restrict__ Dg,
+                                                    uint16_t *__restrict__ dQg, int seq, int heads, float scale) {
+  constexpr int NT = 64 * NW, QT = 16 * NW;
+  using R = Rows64<D, NT>;
+  constexpr int kLd = R::kLd;
+  __shared__ __align__(16) uint16_t sK[2][kT * kLd];  // two stages: block i computes while block i+1 is stored
+  __shared__ __align__(16) uint16_t sV[2][kT * kLd];
+  const int ntq = (seq + QT - 1) / QT;
+  const int q0 = (ntq - 1 - (int)blockIdx.x) * QT;  // the longest query tiles start first
+  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const int64_t ld = (int64_t)heads * D;
+  const int64_t base = b * seq * ld + h * D;
+  const int64_t row = (b * heads + h) * seq;
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int qw = q0 + 16 * w, qi = qw + c;
+  const bool qok = qi < seq;
+
+  u32x4_t qf[D / 32], of[D / 32];  // B operands: Q and dO of the lane's query, dims 32 ks + 8 g ..
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    qf[ks] = of[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    if (qok) {
+      qf[ks] = *reinterpret_cast<const u32x4_t *>(Qg + base + qi * ld + 32 * ks + 8 * g);
+      of[ks] = *reinterpret_cast<const u32x4_t *>(dOg + base + qi * ld + 32 * ks + 8 * g);
+    }
+  }
+  const float c2 = scale * kLog2e;
+  const float l2 = qok ? lse[row + qi] * kLog2e : INFINITY;
+  f32x4_t acc[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float dsum = 0.f, Dq = 0.f;
+
+  const int nblk = min((seq + kT - 1) / kT, (q0 + QT + kT - 1) / kT);  // key blocks up to the diagonal
+  // iteration it < nblk is pass 1 on key block it, it >= nblk pass 2 on
+  // block it - nblk; block(it) is staged in LDS stage it & 1
+  auto block = [&](int it) { return (it < nblk ? it : it - nblk) * kT; };
+  R rk, rv;
+  rk.load(Kg + base, ld, 0, seq, t);
+  rv.load(Vg + base, ld, 0, seq, t);
+  rk.store(sK[0], t);
+  rv.store(sV[0], t);
+  rk.load(Kg + base, ld, block(1), seq, t);  // 2 * nblk >= 2 iterations
+  rv.load(Vg + base, ld, block(1), seq, t);
+  for (int it = 0; it < 2 * nblk; ++it) {
+    const bool second = it >= nblk;
+    const int k0 = block(it);
+    const uint16_t *cK = sK[it & 1], *cV = sV[it & 1];
+    if (it == nblk) {
+      Dq = dsum + __shfl_xor(dsum, 16, 64);
+      Dq += __shfl_xor(Dq, 32, 64);
+      if (qok && g == 0) Dg[row + qi] = Dq;
+    }
+    __syncthreads();  // stage it & 1 is stored; every read of the other stage (iteration it - 1) is done
+    if (it + 1 < 2 * nblk) {
+      rk.store(sK[(it + 1) & 1], t);
+      rv.store(sV[(it + 1) & 1], t);
+      if (it + 2 < 2 * nblk) {
+        rk.load(Kg + base, ld, block(it + 2), seq, t);
+        rv.load(Vg + base, ld, block(it + 2), seq, t);
+      }
+    }
+    if (k0 > qw + 15) continue;  // every key of the block follows every query of this wave
+
+    f32x4_t st[4], dp[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      st[kt] = dp[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        st[kt] = mfma16(lds_frag(cK, kLd, 16 * kt, 32 * ks, lane), qf[ks], st[kt]);
+        dp[kt] = mfma16(lds_frag(cV, kLd, 16 * kt, 32 * ks, lane), of[ks], dp[kt]);
+      }
+    }
+    float p[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) p[kt][v] = exp2_fast(fmaf(st[kt][v], c2, -l2));
+    if (k0 + kT - 1 > qw) {  // the diagonal block: keys past the query drop out
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (k0 + 16 * kt + 4 * g + v > qi) p[kt][v] = 0.f;
+    }
+    if (!second) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dsum = fmaf(p[kt][v], dp[kt][v], dsum);
+      continue;
+    }
+    uint32_t sw[4][2];  // dS^T as bf16 pairs: tile kt, keys 4g + (0,1) and (2,3)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sw[kt][0] = bf16x2_rne(p[kt][0] * (dp[kt][0] - Dq), p[kt][1] * (dp[kt][1] - Dq));
+      sw[kt][1] = bf16x2_rne(p[kt][2] * (dp[kt][2] - Dq), p[kt][3] * (dp[kt][3] - Dq));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t sb = {sw[2 * ks][0], sw[2 * ks][1], sw[2 * ks + 1][0], sw[2 * ks + 1][1]};
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        acc[dt] = mfma16(lds_frag_t2(cK, kLd, 32 * ks, 32 * ks + 16, 16 * dt, lane), sb, acc[dt]);
+    }
+  }
+  if (qok) {
+    uint16_t *orow = dQg + base + qi * ld;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x2_t o = {bf16x2_rne(acc[dt][0] * scale, acc[dt][1] * scale),
+                         bf16x2_rne(acc[dt][2] * scale, acc[dt][3] * scale)};
+      *reinterpret_cast<u32x2_t *>(orow + 16 * dt + 4 * g) = o;
+    }
+  }
+}
+
+// Backward, key side, for head dims 32, 64, 128: one workgroup of 8 waves
+// per (sequence, head, 128-key tile), wave w on keys k0 + 16w .. +15 (the
+// lane's key row of K and V in registers), query blocks of 64 from the
+// diagonal to the end of the sequence (Q and dO rows staged in LDS as they
+// lie, with lse and the query side's D):
+//   S = Q K^T and dP = dO V^T on MFMA (A = Q or dO rows from LDS, B = the
+//   lane's key), so each lane holds 16 queries of its key; P = exp(S - lse),
+//   dS = P (dP - D), both rounded to bf16 in that lane;
+//   dV^T += dO^T P and dK^T += Q^T dS on MFMA, dO^T and Q^T read from the
+//   staged rows by transposing LDS reads at the queries the lane holds.
+// Queries past the sequence are staged with lse = +inf and D = 0 (P = dS
+// = 0).  dK is scaled by 1/sqrt(d) once, at the store.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_bwd_kv(const uint16_t *__restrict__ Qg, const uint16_t *__restrict__ Kg,
+                                                     const uint16_t *__restrict__ Vg,
+                                                     const uint16_t *__restrict__ dOg, const float *__restrict__ lse,
+                                                     const float *__restrict__ Dg, uint16_t *__restrict__ dKg,
+                                                     uint16_t *__restrict__ dVg, int seq, int heads, float scale) {
+  constexpr int NT = 64 * NW, KT = 16 * NW;
+  using R = Rows64<D, NT>;
+  constexpr int kLd = R::kLd;
+  __shared__ __align__(16) uint16_t sQ[2][kT * kLd];  // two stages, as on the query side
+  __shared__ __align__(16) uint16_t sO[2][kT * kLd];
+  __shared__ __align__(16) float sL[2][kT];
+  __shared__ __align__(16) float sD[2][kT];
+  const int k0 = (int)blockIdx.x * KT;  // the longest key tiles (most queries) start first
+  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const int64_t ld = (int64_t)heads * D;
+  const int64_t base = b * seq * ld + h * D;
+  const int64_t row = (b * heads + h) * seq;
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kw = k0 + 16 * w, kj = kw + c;
+  const bool kok = kj < seq;
+
+  u32x4_t kf[D / 32], vf[D / 32];  // B operands: K and V of the lane's key
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+    kf[ks] = vf[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    if (kok) {
+      kf[ks] = *reinterpret_cast<const u32x4_t *>(Kg + base + kj * ld + 32 * ks + 8 * g);
+      vf[ks] = *reinterpret_cast<const u32x4_t *>(Vg + base + kj * ld + 32 * ks + 8 * g);
+    }
+  }
+  const float c2 = scale * kLog2e;
+  f32x4_t ak[D / 16], av[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) ak[i] = av[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int qb0 = k0 / kT, nqb = (seq + kT - 1) / kT;
+  R rq, ro;
+  // threads 0..63: lse and D of query q0 + t, used only after the next
+  // loop-top wait (scaling lse here would wait for every load in flight)
+  float rl = INFINITY, rd = 0.f;
+  auto load_block = [&](int q0) {
+    rq.load(Qg + base, ld, q0, seq, t);
+    ro.load(dOg + base, ld, q0, seq, t);
+    if (t < kT) {
+      rl = INFINITY;
+      rd = 0.f;
+      if (q0 + t < seq) {
+        rl = lse[row + q0 + t];
+        rd = Dg[row + q0 + t];
+      }
+    }
+  };
+  auto store_block = [&](int stage) {
+    rq.store(sQ[stage], t);
+    ro.store(sO[stage], t);
+    if (t < kT) {
+      sL[stage][t] = rl * kLog2e;  // base-2 units (+inf past the sequence)
+      sD[stage][t] = rd;
+    }
+  };
+  load_block(qb0 * kT);
+  store_block(0);
+  if (qb0 + 1 < nqb) load_block((qb0 + 1) * kT);
+  for (int qb = qb0; qb < nqb; ++qb) {
+    const int q0 = qb * kT, cur = (qb - qb0) & 1;
+    const uint16_t *cQ = sQ[cur], *cO = sO[cur];
+    const float *cL = sL[cur], *cD = sD[cur];
+    __syncthreads();  // stage cur is stored; every read of the other stage (block qb - 1) is done
+    if (qb + 1 < nqb) {
+      store_block(cur ^ 1);
+      if (qb + 2 < nqb) load_block(q0 + 2 * kT);
+    }
+    if (kw > q0 + kT - 1) continue;  // every query of the block precedes every key of this wave
+
+    f32x4_t st[4], dp[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      st[qt] = dp[qt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        st[qt] = mfma16(lds_frag(cQ, kLd, 16 * qt, 32 * ks, lane), kf[ks], st[qt]);
+        dp[qt] = mfma16(lds_frag(cO, kLd, 16 * qt, 32 * ks, lane), vf[ks], dp[qt]);
+      }
+    }
+    float p[4][4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(cL + 16 * qt + 4 * g);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) p[qt][v] = exp2_fast(fmaf(st[qt][v], c2, -l4[v]));
+    }
+    if (kw + 15 > q0) {  // the diagonal block: queries before the key drop out
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (kj > q0 + 16 * qt + 4 * g + v) p[qt][v] = 0.f;
+    }
+    uint32_t pw[4][2], sw[4][2];  // P and dS as bf16 pairs: tile qt, queries 4g + (0,1) and (2,3)
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(cD + 16 * qt + 4 * g);
+      float ds[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ds[v] = p[qt][v] * (dp[qt][v] - d4[v]);
+      pw[qt][0] = bf16x2_rne(p[qt][0], p[qt][1]);
+      pw[qt][1] = bf16x2_rne(p[qt][2], p[qt][3]);
+      sw[qt][0] = bf16x2_rne(ds[0], ds[1]);
+      sw[qt][1] = bf16x2_rne(ds[2], ds[3]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t pb = {pw[2 * ks][0], pw[2 * ks][1], pw[2 * ks + 1][0], pw[2 * ks + 1][1]};
+      const u32x4_t sb = {sw[2 * ks][0], sw[2 * ks][1], sw[2 * ks + 1][0], sw[2 * ks + 1][1]};
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        av[dt] = mfma16(lds_frag_t2(cO, kLd, 32 * ks, 32 * ks + 16, 16 * dt, lane), pb, av[dt]);
+        ak[dt] = mfma16(lds_frag_t2(cQ, kLd, 32 * ks, 32 * ks + 16, 16 * dt, lane), sb, ak[dt]);
+      }
+    }
+  }
+  if (kok) {
+    uint16_t *krow = dKg + base + kj * ld, *vrow = dVg + base + kj * ld;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const u32x2_t k = {bf16x2_rne(ak[dt][0] * scale, ak[dt][1] * scale),
+                         bf16x2_rne(ak[dt][2] * scale, ak[dt][3] * scale)};
+      const u32x2_t v = {bf16x2_rne(av[dt][0], av[dt][1]), bf16x2_rne(av[dt][2], av[dt][3])};
+      *reinterpret_cast<u32x2_t *>(krow + 16 * dt + 4 * g) = k;
+      *reinterpret_cast<u32x2_t *>(vrow + 16 * dt + 4 * g) = v;
+    }
   }
 }
 
@@ -554,15 +874,24 @@ void gemm(const char *name, const Dims &x, Opnd a, Opnd b, void *c, bool c_score
   QLORA_LAUNCH(name, (k_attn_gemm<AKC, BKC, OUT_BF16>), grid, dim3(256), 0, s, g);
 }
 
+bool fused(int64_t d) { return d == 32 || d == 64 || d == 128; }
+
+// Materialised path (other head dims): float32 S and dP, bf16 P and dS,
+// each [batch][heads][seq][ldp].  Fused path: the backward's D
+// [batch][heads][seq] (the fused forward needs no workspace).
 struct Ws {
-  float *S, *dP;
-  uint16_t *P, *dS, *Vt;  // Vt: [batch][heads][d][ldp], the fused forward's V^T
+  float *S, *dP, *D;
+  uint16_t *P, *dS;
 };
 
 Ws carve(void *ws, const Dims &x) {
-  const size_t e = (size_t)(x.batch * x.heads * x.seq * x.ldp);
   char *p = static_cast<char *>(ws);
-  Ws w;
+  Ws w{};
+  if (fused(x.d)) {
+    w.D = reinterpret_cast<float *>(p);
+    return w;
+  }
+  const size_t e = (size_t)(x.batch * x.heads * x.seq * x.ldp);
   w.S = reinterpret_cast<float *>(p);
   p += align_up(e * 4, 256);
   w.dP = reinterpret_cast<float *>(p);
@@ -570,8 +899,6 @@ Ws carve(void *ws, const Dims &x) {
   w.P = reinterpret_cast<uint16_t *>(p);
   p += align_up(e * 2, 256);
   w.dS = reinterpret_cast<uint16_t *>(p);
-  p += align_up(e * 2, 256);
-  w.Vt = reinterpret_cast<uint16_t *>(p);
   return w;
 }
 
@@ -579,8 +906,9 @@ Ws carve(void *ws, const Dims &x) {
 
 size_t attention_workspace_bytes(int64_t batch, int64_t seq, int64_t heads, int64_t d) {
   const size_t ldp = align_up((size_t)seq, 8);
+  if (fused(d)) return align_up((size_t)(batch * heads * seq) * 4, 256);
   const size_t e = (size_t)(batch * heads * seq) * ldp;
-  return 2 * align_up(e * 4, 256) + 2 * align_up(e * 2, 256) + align_up((size_t)(batch * heads * d) * ldp * 2, 256);
+  return 2 * align_up(e * 4, 256) + 2 * align_up(e * 2, 256);
 }
 
 hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint16_t *V, uint16_t *O, float *lse,
@@ -589,20 +917,15 @@ hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint
   const Ws w = carve(ws, x);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   const int L = (int)seq, D = (int)d;
-  if (d == 32 || d == 64 || d == 128) {
-    const dim3 grid((unsigned)ceil_div(seq, kT), (unsigned)heads, (unsigned)batch);
+  if (fused(d)) {
     const int H = (int)heads;
     const dim3 gq((unsigned)ceil_div(seq, kQT), (unsigned)heads, (unsigned)batch);
-    if (d == 32) {
-      QLORA_LAUNCH("k_attn_vt", k_attn_vt<32>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
-      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<32>, gq, dim3(512), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
-    } else if (d == 64) {
-      QLORA_LAUNCH("k_attn_vt", k_attn_vt<64>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
-      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<64>, gq, dim3(512), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
-    } else {
-      QLORA_LAUNCH("k_attn_vt", k_attn_vt<128>, grid, dim3(256), 0, s, V, w.Vt, L, H, x.ldp);
-      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<128>, gq, dim3(512), 0, s, Q, K, w.Vt, O, lse, L, H, x.ldp, scale);
-    }
+    if (d == 32)
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<32>, gq, dim3(512), 0, s, Q, K, V, O, lse, L, H, scale);
+    else if (d == 64)
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<64>, gq, dim3(512), 0, s, Q, K, V, O, lse, L, H, scale);
+    else
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<128>, gq, dim3(512), 0, s, Q, K, V, O, lse, L, H, scale);
     return hipGetLastError();
   }
   gemm<true, true, false>("k_attn_scores", x, qkv(Q, x), qkv(K, x), w.S, true, L, L, D, scale, 1, 0, s);
@@ -619,6 +942,26 @@ hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint
   const Ws w = carve(ws, x);
   const float scale = (float)(1.0 / std::sqrt((double)d));
   const int L = (int)seq, D = (int)d;
+  if (fused(d)) {
+    const int H = (int)heads;
+    const dim3 gq((unsigned)ceil_div(seq, kBwdRows), (unsigned)heads, (unsigned)batch);
+    const dim3 gk((unsigned)ceil_div(seq, kBwdRows), (unsigned)heads, (unsigned)batch);
+    const dim3 blk(64 * kBwdWaves);
+#define QLORA_ATTN_BWD(DD)                                                                                     \
+  QLORA_LAUNCH("k_attn_bwd_q", (k_attn_bwd_q<DD, kBwdWaves>), gq, blk, 0, s, Q, K, V, dO, lse, w.D, dQ, L, H,   \
+               scale);                                                                                         \
+  QLORA_LAUNCH("k_attn_bwd_kv", (k_attn_bwd_kv<DD, kBwdWaves>), gk, blk, 0, s, Q, K, V, dO, lse, w.D, dK, dV, L, \
+               H, scale)
+    if (d == 32) {
+      QLORA_ATTN_BWD(32);
+    } else if (d == 64) {
+      QLORA_ATTN_BWD(64);
+    } else {
+      QLORA_ATTN_BWD(128);
+    }
+#undef QLORA_ATTN_BWD
+    return hipGetLastError();
+  }
   // (one launch computing both products over the same tiles was slower: 189 against 81 + 98 us)
   gemm<true, true, false>("k_attn_scores", x, qkv(Q, x), qkv(K, x), w.S, true, L, L, D, scale, 1, 0, s);
   gemm<true, true, false>("k_attn_dp", x, qkv(dO, x), qkv(V, x), w.dP, true, L, L, D, 1.0f, 1, 0, s);

@@ -230,8 +230,12 @@ def test_attention_shape_and_argument_errors(q):
     lib = q.raw_library()
     P = ctypes.c_void_p(16)
     big = 1 << 40
-    assert q.qlora_attention_workspace_bytes(8, 512, 32, 128) >= 12 * 8 * 32 * 512 * 512
-    assert q.qlora_attention_workspace_bytes(1, 13, 2, 64) >= 12 * 2 * 13 * 16
+    up = lambda x: (x + 255) // 256 * 256
+    # head dims 32/64/128: the backward's D per query
+    assert q.qlora_attention_workspace_bytes(8, 512, 32, 128) == up(8 * 32 * 512 * 4)
+    assert q.qlora_attention_workspace_bytes(1, 13, 2, 64) == up(2 * 13 * 4)
+    # other head dims: float32 S and dP, bf16 P and dS, rows of roundup(seq, 8)
+    assert q.qlora_attention_workspace_bytes(1, 13, 2, 8) == 2 * up(2 * 13 * 16 * 4) + 2 * up(2 * 13 * 16 * 2)
     for bad in ((1, 16, 2, 60), (1, 16, 2, 0), (1, 16, 0, 64), (-1, 16, 2, 64), (1, 70000, 2, 64), (1, 16, 2, 2048)):
         assert q.qlora_attention_workspace_bytes(*bad) == 0
         assert lib.qlora_attention_fwd(P, P, P, P, P, *bad, P, big, None) == q.QLORA_ERR_BAD_SHAPE

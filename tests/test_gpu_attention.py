@@ -8,9 +8,11 @@ no bf16 rounding on the way).  The GPU rounds P and dS to bf16 before the
 products that take them (2^-9 relative per element, independent in sign),
 which the Frobenius bar holds with room.  Shapes span several 64-wide
 tiles, ragged sequence tails, one-token sequences, rows longer than one
-512-column chunk of the row kernels (seq 600, 700), head dims 8 (the
-non-fused forward), 64 and 128, and the LLaMA-7B layer's 32 heads of 128
-on 512-token sequences."""
+512-column chunk of the row kernels (seq 600, 700), sequences of several
+128-row workgroup tiles with a ragged last one (seq 1000) or one row past
+a tile (seq 65), head dims 8 (the materialised path), 32, 64 and 128 (the
+fused kernels), and the LLaMA-7B layer's 32 heads of 128 on 512-token
+sequences."""
 import numpy as np
 import pytest
 import torch
@@ -50,7 +52,8 @@ def _run(q, batch, seq, heads, d, seed):
 
 
 @pytest.mark.parametrize("batch,seq,heads,d", [(2, 77, 3, 64), (1, 130, 2, 128), (3, 1, 2, 64), (2, 200, 1, 8),
-                                               (1, 512, 4, 128), (1, 700, 2, 64), (1, 600, 1, 8)])
+                                               (1, 512, 4, 128), (1, 700, 2, 64), (1, 600, 1, 8), (2, 200, 3, 32),
+                                               (1, 1000, 1, 128), (2, 65, 1, 128)])
 def test_attention_matches_oracle(q, batch, seq, heads, d):
     note(f"[attention] batch={batch} seq={seq} heads={heads} d={d}")
     (Qb, Kb, Vb, dOb), (O, lse, dQ, dK, dV) = _run(q, batch, seq, heads, d, seed=seq + 7 * heads + d)
