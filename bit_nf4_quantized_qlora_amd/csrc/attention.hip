@@ -391,9 +391,12 @@ __device__ __forceinline__ u32x4_t lds_frag_t2(const uint16_t *X, int ld, int r0
   return __builtin_bit_cast(u32x4_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 64 rows of an operand [row][D] (rows past the sequence zero) in kPL
-// 16-byte pieces per thread of an NT-thread workgroup: piece e is row
-// e / (D/8), columns 8 (e % (D/8)) .. +7.
+// 64 rows of an operand [row][D] in kPL 16-byte pieces per thread of an
+// NT-thread workgroup: piece e is row e / (D/8), columns 8 (e % (D/8)) .. +7.
+// Rows past the sequence repeat its last row (row0 < seq): every load is
+// in bounds and unconditional, and the kernels make such rows contribute
+// exactly nothing (their P is selected to 0, so their dS is 0 too), so they
+// need only hold finite values.
 template <int D, int NT>
 struct Rows64 {
   static constexpr int kPieces = 8 * D;
@@ -404,10 +407,9 @@ struct Rows64 {
 #pragma unroll
     for (int i = 0; i < kPL; ++i) {
       const int e = t + NT * i;
-      r[i] = u32x4_t{0u, 0u, 0u, 0u};
       if (e < kPieces) {
-        const int row = row0 + e / (D / 8);
-        if (row < seq) r[i] = *reinterpret_cast<const u32x4_t *>(g + (int64_t)row * ld + 8 * (e % (D / 8)));
+        const int row = min(row0 + e / (D / 8), seq - 1);
+        r[i] = *reinterpret_cast<const u32x4_t *>(g + (int64_t)row * ld + 8 * (e % (D / 8)));
       }
     }
   }
@@ -640,6 +642,10 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_q(const uint16_t *__restri
     }
     if (k0 > qw + 15) continue;  // every key of the block follows every query of this wave
 
+    // the MFMA groups run at raised wave priority, so the other wave of a
+    // SIMD, in its exponential or dS arithmetic, yields the issue slot to
+    // them (120 against 128 us at 8 x 512 x 32 x 128; no gain on the key side)
+    __builtin_amdgcn_s_setprio(1);
     f32x4_t st[4], dp[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -650,6 +656,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_q(const uint16_t *__restri
         dp[kt] = mfma16(lds_frag(cV, kLd, 16 * kt, 32 * ks, lane), of[ks], dp[kt]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     float p[4][4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
@@ -675,6 +682,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_q(const uint16_t *__restri
       sw[kt][0] = bf16x2_rne(p[kt][0] * (dp[kt][0] - Dq), p[kt][1] * (dp[kt][1] - Dq));
       sw[kt][1] = bf16x2_rne(p[kt][2] * (dp[kt][2] - Dq), p[kt][3] * (dp[kt][3] - Dq));
     }
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4_t sb = {sw[2 * ks][0], sw[2 * ks][1], sw[2 * ks + 1][0], sw[2 * ks + 1][1]};
@@ -682,6 +690,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_q(const uint16_t *__restri
       for (int dt = 0; dt < D / 16; ++dt)
         acc[dt] = mfma16(lds_frag_t2(cK, kLd, 32 * ks, 32 * ks + 16, 16 * dt, lane), sb, acc[dt]);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   if (qok) {
     uint16_t *orow = dQg + base + qi * ld;
