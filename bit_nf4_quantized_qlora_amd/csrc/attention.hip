@@ -422,6 +422,27 @@ struct Rows64 {
   }
 };
 
+// Which (tile, head, sequence) a workgroup of a fused kernel takes.  The
+// grid is (tiles, heads, batch); workgroups go to the eight XCDs in turn by
+// linear id, so ids are renumbered to give each XCD a contiguous run of
+// (sequence, head, tile) triples: the tiles of one (sequence, head), which
+// stream the same K and V (or Q and dO) blocks, then share an XCD's L2 and
+// start together.  Within a (sequence, head) the tiles go in the order given
+// (the longest first).  A bijection on the grid, in 64-bit arithmetic.
+struct AttnTile {
+  int tile;
+  int64_t h, b;
+};
+__device__ __forceinline__ AttnTile attn_tile() {
+  const int64_t T = gridDim.x, H = gridDim.y;
+  const int64_t n = T * H * (int64_t)gridDim.z;
+  const int64_t L = blockIdx.x + T * (blockIdx.y + H * (int64_t)blockIdx.z);
+  const int64_t q = n >> 3, rem = n & 7, x = L & 7, p = L >> 3;
+  const int64_t lin = (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + p;
+  const int64_t bh = lin / T;
+  return AttnTile{(int)(lin - bh * T), bh % H, bh / H};
+}
+
 // Fused forward: one workgroup of 8 waves per (sequence, head, 128-query
 // tile), wave w on queries q0 + 16w .. +15, so a staged key block serves 128
 // queries; no score matrix in memory.  Per 64-key block (causal: blocks up
@@ -446,9 +467,9 @@ __global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restri
   constexpr int kLd = R::kLd;
   __shared__ __align__(16) uint16_t sK[2][kT * kLd];
   __shared__ __align__(16) uint16_t sV[2][kT * kLd];
-  const int ntq = (seq + kQT - 1) / kQT;
-  const int q0 = (ntq - 1 - (int)blockIdx.x) * kQT;  // the longest query tiles start first
-  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const AttnTile at = attn_tile();
+  const int q0 = ((int)gridDim.x - 1 - at.tile) * kQT;  // the longest query tiles start first
+  const int64_t h = at.h, b = at.b;
   const int64_t ld = (int64_t)heads * D;
   const int64_t base = b * seq * ld + h * D;
   const int t = threadIdx.x, lane = t & 63, g = lane >> 4, c = lane & 15;
@@ -584,9 +605,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_q(const uint16_t *__restri
   constexpr int kLd = R::kLd;
   __shared__ __align__(16) uint16_t sK[2][kT * kLd];  // two stages: block i computes while block i+1 is stored
   __shared__ __align__(16) uint16_t sV[2][kT * kLd];
-  const int ntq = (seq + QT - 1) / QT;
-  const int q0 = (ntq - 1 - (int)blockIdx.x) * QT;  // the longest query tiles start first
-  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const AttnTile at = attn_tile();
+  const int q0 = ((int)gridDim.x - 1 - at.tile) * QT;  // the longest query tiles start first
+  const int64_t h = at.h, b = at.b;
   const int64_t ld = (int64_t)heads * D;
   const int64_t base = b * seq * ld + h * D;
   const int64_t row = (b * heads + h) * seq;
@@ -728,8 +749,9 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_kv(const uint16_t *__restr
   __shared__ __align__(16) uint16_t sO[2][kT * kLd];
   __shared__ __align__(16) float sL[2][kT];
   __shared__ __align__(16) float sD[2][kT];
-  const int k0 = (int)blockIdx.x * KT;  // the longest key tiles (most queries) start first
-  const int64_t h = blockIdx.y, b = blockIdx.z;
+  const AttnTile at = attn_tile();
+  const int k0 = at.tile * KT;  // the longest key tiles (most queries) start first
+  const int64_t h = at.h, b = at.b;
   const int64_t ld = (int64_t)heads * D;
   const int64_t base = b * seq * ld + h * D;
   const int64_t row = (b * heads + h) * seq;
