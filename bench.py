@@ -464,6 +464,8 @@ def config_rows(q, I, name, dev, ev, dev16, steps=20, warmup=10):
         f, b = layer_flops(M, t["L"].n, t["L"].k, r)
         ff, bf = ff + f, bf + b
     prof = traced(q, step, 5)
+    graph_ms, graph_same = graph_step(torch, step, [t[k] for t in layers for k in ("Y", "H", "dX", "dA", "dB")],
+                                      timed, steps)
     tf = lambda fl, m: round(fl / (m * 1e-3) / 1e12, 1)
     out = {"workload": f"{name}: " + ", ".join(f"{t['L'].name} {t['L'].k}->{t['L'].n}" for t in layers) +
                        f"; M = {M}, r = {r}",
@@ -471,12 +473,50 @@ def config_rows(q, I, name, dev, ev, dev16, steps=20, warmup=10):
                                                                                     PEAK_BF16_TFLOPS, 4),
            "fwd_ms": round(fwd_ms, 4), "fwd_tflops": tf(ff, fwd_ms), "bwd_ms": round(bwd_ms, 4),
            "bwd_tflops": tf(bf, bwd_ms), "flops_per_step": ff + bf,
+           "graph": {"ms": round(graph_ms, 4), "tflops": tf(ff + bf, graph_ms),
+                     "frac_bf16_peak": round((ff + bf) / (graph_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "replays_equal_eager": graph_same,
+                     "how": "the same step captured once as a HIP graph (torch.cuda.graph on the current stream) "
+                            "and replayed: no host launch cost per kernel; three replays compared bit for bit "
+                            "with the eager step's outputs first"},
            "plans": {t["L"].name: q.qlora_linear_plan(M, t["L"].n, t["L"].k, r) for t in layers},
            "kernels_us": {k: {"launches_per_step": n / 5, "avg_us": round(1e3 * v / n, 2)}
                           for k, (n, v) in sorted(prof.items())}}
     del layers, ws
     torch.cuda.empty_cache()
     return out
+
+
+def graph_step(torch, step, outs, timed, steps):
+    """Capture step() as a HIP graph and replay it: the replay time per step,
+    and whether three replays (outputs overwritten with NaN before each)
+    equal the eager step's outputs bit for bit."""
+    bits = lambda v: v.view(torch.int32) if v.dtype == torch.float32 else v.view(torch.int16)
+    step()
+    torch.cuda.synchronize()
+    ref = [v.clone() for v in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one run off the capture first, as torch asks
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    same = True
+    for _ in range(3):
+        for v in outs:
+            v.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        same = same and all(torch.equal(bits(v), bits(r)) for v, r in zip(outs, ref))
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = timed(g.replay, steps)
+    del g
+    return ms, same
 
 
 def calib_copy(torch, dev, mib):
