@@ -55,7 +55,7 @@ TRAFFIC_FILES = {"tile": os.path.join(ROOT, "profiles", "traffic_counters.json")
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=100)  # ~0.2 s of timed steps at the 7B MLP shape
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="mlp_7b")
     p.add_argument("--no-cpu-baseline", action="store_true")
