@@ -861,15 +861,32 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_kv(const uint16_t *__restr
       }
     }
   }
-  if (kok) {
-    uint16_t *krow = dKg + base + kj * ld, *vrow = dVg + base + kj * ld;
+  // dK and dV go out through LDS (the staged-block buffers, free once every
+  // wave is past its last read): the lane's 8-byte pieces of its key row
+  // meet there, and each row then leaves in 16-byte pieces, whole lines at
+  // a time.  (Stored straight from the accumulators, two outputs
+  // interleaved, lines were written back half filled: 126 MB written for
+  // 67 MB of output at 8 x 512 x 32 x 128.)
+  constexpr int kLo = D + 8;  // staging row stride (elements)
+  static_assert(NW * 16 * kLo <= 2 * kT * kLd, "the staged rows fit a block buffer");
+  __syncthreads();
+  uint16_t *stk = &sQ[0][0] + w * 16 * kLo, *stv = &sO[0][0] + w * 16 * kLo;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x2_t k = {bf16x2_rne(ak[dt][0] * scale, ak[dt][1] * scale),
-                         bf16x2_rne(ak[dt][2] * scale, ak[dt][3] * scale)};
-      const u32x2_t v = {bf16x2_rne(av[dt][0], av[dt][1]), bf16x2_rne(av[dt][2], av[dt][3])};
-      *reinterpret_cast<u32x2_t *>(krow + 16 * dt + 4 * g) = k;
-      *reinterpret_cast<u32x2_t *>(vrow + 16 * dt + 4 * g) = v;
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const u32x2_t k = {bf16x2_rne(ak[dt][0] * scale, ak[dt][1] * scale),
+                       bf16x2_rne(ak[dt][2] * scale, ak[dt][3] * scale)};
+    const u32x2_t v = {bf16x2_rne(av[dt][0], av[dt][1]), bf16x2_rne(av[dt][2], av[dt][3])};
+    *reinterpret_cast<u32x2_t *>(stk + c * kLo + 16 * dt + 4 * g) = k;
+    *reinterpret_cast<u32x2_t *>(stv + c * kLo + 16 * dt + 4 * g) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {  // 16 rows x D/8 pieces per output and wave: D/32 per lane
+    const int e = lane + 64 * j, row = e / (D / 8), col = 8 * (e % (D / 8));
+    if (kw + row < seq) {
+      const int64_t go = base + (int64_t)(kw + row) * ld + col;
+      *reinterpret_cast<u32x4_t *>(dKg + go) = *reinterpret_cast<const u32x4_t *>(stk + row * kLo + col);
+      *reinterpret_cast<u32x4_t *>(dVg + go) = *reinterpret_cast<const u32x4_t *>(stv + row * kLo + col);
     }
   }
 }
