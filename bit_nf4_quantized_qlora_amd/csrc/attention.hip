@@ -444,6 +444,37 @@ __device__ __forceinline__ AttnTile attn_tile() {
   return AttnTile{(int)(L / HB), bh % H, bh / H};
 }
 
+// Output of a wave's 16 x D tile held in the accumulator layout (lane
+// (g, c) holds row c, columns 16 dt + 4g .. +3 of tile dt): the lane's
+// 8-byte pieces, scaled and rounded to bf16, meet in LDS (stg: this wave's
+// 16 rows of kOutLd elements), and after a barrier each row leaves in
+// 16-byte pieces, whole lines at a time.  Stored straight from the
+// accumulators the pieces of one line came from four lanes and, with two
+// outputs interleaved, lines were written back half filled.
+template <int D>
+constexpr int kOutLd = D + 8;
+template <int D>
+__device__ __forceinline__ void stage_rows16(const f32x4_t (&acc)[D / 16], float mul, uint16_t *stg, int lane) {
+  const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const u32x2_t v = {bf16x2_rne(acc[dt][0] * mul, acc[dt][1] * mul), bf16x2_rne(acc[dt][2] * mul, acc[dt][3] * mul)};
+    *reinterpret_cast<u32x2_t *>(stg + c * kOutLd<D> + 16 * dt + 4 * g) = v;
+  }
+}
+// rows row0 .. row0+15 below nrows of a row-major bf16 array (stride ld)
+template <int D>
+__device__ __forceinline__ void flush_rows16(const uint16_t *stg, uint16_t *out, int64_t ld, int row0, int nrows,
+                                             int lane) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {  // 16 rows x D/8 pieces per wave: D/32 per lane
+    const int e = lane + 64 * j, row = e / (D / 8), col = 8 * (e % (D / 8));
+    if (row0 + row < nrows)
+      *reinterpret_cast<u32x4_t *>(out + (int64_t)(row0 + row) * ld + col) =
+          *reinterpret_cast<const u32x4_t *>(stg + row * kOutLd<D> + col);
+  }
+}
+
 // Fused forward: one workgroup of 8 waves per (sequence, head, 128-query
 // tile), wave w on queries q0 + 16w .. +15, so a staged key block serves 128
 // queries; no score matrix in memory.  Per 64-key block (causal: blocks up
@@ -567,17 +598,16 @@ __global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restri
   }
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (qi < seq) {
-    const float inv = 1.0f / l;
-    uint16_t *orow = Og + base + qi * ld;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x2_t o = {bf16x2_rne(acc_o[dt][0] * inv, acc_o[dt][1] * inv),
-                         bf16x2_rne(acc_o[dt][2] * inv, acc_o[dt][3] * inv)};
-      *reinterpret_cast<u32x2_t *>(orow + 16 * dt + 4 * g) = o;
-    }
-    if (g == 0) lse[(b * heads + h) * seq + qi] = (m + log2_fast(l)) * kLn2;
-  }
+  if (qi < seq && g == 0) lse[(b * heads + h) * seq + qi] = (m + log2_fast(l)) * kLn2;
+  // O through LDS (the staged-block buffers, free once every wave is past
+  // its last read); a lane whose query lies past the sequence stages
+  // whatever it holds, and its row is not written
+  static_assert(8 * 16 * kOutLd<D> <= 2 * kT * kLd, "a wave's output rows fit the block buffer");
+  uint16_t *stg = &sK[0][0] + w * 16 * kOutLd<D>;
+  __syncthreads();
+  stage_rows16<D>(acc_o, 1.0f / l, stg, lane);
+  __syncthreads();
+  flush_rows16<D>(stg, Og + base, ld, qw, seq, lane);
 }
 
 // Backward, query side, for head dims 32, 64, 128: one workgroup of 8 waves
@@ -714,15 +744,13 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_q(const uint16_t *__restri
     }
     __builtin_amdgcn_s_setprio(0);
   }
-  if (qok) {
-    uint16_t *orow = dQg + base + qi * ld;
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x2_t o = {bf16x2_rne(acc[dt][0] * scale, acc[dt][1] * scale),
-                         bf16x2_rne(acc[dt][2] * scale, acc[dt][3] * scale)};
-      *reinterpret_cast<u32x2_t *>(orow + 16 * dt + 4 * g) = o;
-    }
-  }
+  // dQ through LDS, as the forward's O
+  static_assert(NW * 16 * kOutLd<D> <= 2 * kT * kLd, "a wave's output rows fit the block buffer");
+  uint16_t *stg = &sK[0][0] + w * 16 * kOutLd<D>;
+  __syncthreads();
+  stage_rows16<D>(acc, scale, stg, lane);
+  __syncthreads();
+  flush_rows16<D>(stg, dQg + base, ld, qw, seq, lane);
 }
 
 // Backward, key side, for head dims 32, 64, 128: one workgroup of 8 waves
@@ -861,34 +889,17 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_kv(const uint16_t *__restr
       }
     }
   }
-  // dK and dV go out through LDS (the staged-block buffers, free once every
-  // wave is past its last read): the lane's 8-byte pieces of its key row
-  // meet there, and each row then leaves in 16-byte pieces, whole lines at
-  // a time.  (Stored straight from the accumulators, two outputs
-  // interleaved, lines were written back half filled: 126 MB written for
-  // 67 MB of output at 8 x 512 x 32 x 128.)
-  constexpr int kLo = D + 8;  // staging row stride (elements)
-  static_assert(NW * 16 * kLo <= 2 * kT * kLd, "the staged rows fit a block buffer");
+  // dK and dV through LDS, as the forward's O (stored straight from the
+  // accumulators, the two outputs interleaved, they took 126 MB of writes
+  // for 67 MB of output at 8 x 512 x 32 x 128: 76 against 70 us)
+  static_assert(NW * 16 * kOutLd<D> <= 2 * kT * kLd, "a wave's output rows fit a block buffer");
+  uint16_t *stk = &sQ[0][0] + w * 16 * kOutLd<D>, *stv = &sO[0][0] + w * 16 * kOutLd<D>;
   __syncthreads();
-  uint16_t *stk = &sQ[0][0] + w * 16 * kLo, *stv = &sO[0][0] + w * 16 * kLo;
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    const u32x2_t k = {bf16x2_rne(ak[dt][0] * scale, ak[dt][1] * scale),
-                       bf16x2_rne(ak[dt][2] * scale, ak[dt][3] * scale)};
-    const u32x2_t v = {bf16x2_rne(av[dt][0], av[dt][1]), bf16x2_rne(av[dt][2], av[dt][3])};
-    *reinterpret_cast<u32x2_t *>(stk + c * kLo + 16 * dt + 4 * g) = k;
-    *reinterpret_cast<u32x2_t *>(stv + c * kLo + 16 * dt + 4 * g) = v;
-  }
+  stage_rows16<D>(ak, scale, stk, lane);
+  stage_rows16<D>(av, 1.0f, stv, lane);
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < D / 32; ++j) {  // 16 rows x D/8 pieces per output and wave: D/32 per lane
-    const int e = lane + 64 * j, row = e / (D / 8), col = 8 * (e % (D / 8));
-    if (kw + row < seq) {
-      const int64_t go = base + (int64_t)(kw + row) * ld + col;
-      *reinterpret_cast<u32x4_t *>(dKg + go) = *reinterpret_cast<const u32x4_t *>(stk + row * kLo + col);
-      *reinterpret_cast<u32x4_t *>(dVg + go) = *reinterpret_cast<const u32x4_t *>(stv + row * kLo + col);
-    }
-  }
+  flush_rows16<D>(stk, dKg + base, ld, kw, seq, lane);
+  flush_rows16<D>(stv, dVg + base, ld, kw, seq, lane);
 }
 
 struct Dims {
