@@ -13,7 +13,7 @@
 // Q, K, V, O (and their gradients) are [batch * seq, heads * d] row-major
 // bf16, the projections' outputs as they come.
 //
-// Head dims 32, 64 and 128 (the LLaMA layers') take fused kernels that keep
+// Head dims 32, 64, 96 and 128 (the LLaMA layers' among them) take fused kernels that keep
 // no score matrix in memory: a forward with an online softmax, and a
 // backward in two launches, a query side (D_i = sum_j P_ij dP_ij from the
 // row's own float32 P and dP, then dQ) and a key side (dK, dV).  Each
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(256) void k_attn_bwd_rows(const float *__restrict__
   }
 }
 
-// Fused kernels (head dims 32, 64, 128).  Each workgroup streams 64-row
+// Fused kernels (head dims 32, 64, 96, 128).  Each workgroup streams 64-row
 // blocks of the other side's operands (K and V for a query tile, Q and dO
 // for a key tile) through LDS, rows staged as they lie with row stride
 // D + kRowPad, in two stages: block i is read while block i+1 is stored and
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd_fused(const uint16_t *__restri
   flush_rows16<D>(stg, Og + base, ld, qw, seq, lane);
 }
 
-// Backward, query side, for head dims 32, 64, 128: one workgroup of 8 waves
+// Backward, query side, for head dims 32, 64, 96, 128: one workgroup of 8 waves
 // per (sequence, head, 128-query tile), wave w on queries q0 + 16w .. +15,
 // key blocks of 64 (K and V rows staged in LDS as they lie, the next block
 // loaded into registers meanwhile) up to the diagonal, twice:
@@ -753,7 +753,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_bwd_q(const uint16_t *__restri
   flush_rows16<D>(stg, dQg + base, ld, qw, seq, lane);
 }
 
-// Backward, key side, for head dims 32, 64, 128: one workgroup of 8 waves
+// Backward, key side, for head dims 32, 64, 96, 128: one workgroup of 8 waves
 // per (sequence, head, 128-key tile), wave w on keys k0 + 16w .. +15 (the
 // lane's key row of K and V in registers), query blocks of 64 from the
 // diagonal to the end of the sequence (Q and dO rows staged in LDS as they
@@ -934,7 +934,7 @@ void gemm(const char *name, const Dims &x, Opnd a, Opnd b, void *c, bool c_score
   QLORA_LAUNCH(name, (k_attn_gemm<AKC, BKC, OUT_BF16>), grid, dim3(256), 0, s, g);
 }
 
-bool fused(int64_t d) { return d == 32 || d == 64 || d == 128; }
+bool fused(int64_t d) { return d == 32 || d == 64 || d == 96 || d == 128; }
 
 // Materialised path (other head dims): float32 S and dP, bf16 P and dS,
 // each [batch][heads][seq][ldp].  Fused path: the backward's D
@@ -984,6 +984,8 @@ hipError_t launch_attention_fwd(const uint16_t *Q, const uint16_t *K, const uint
       QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<32>, gq, dim3(512), 0, s, Q, K, V, O, lse, L, H, scale);
     else if (d == 64)
       QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<64>, gq, dim3(512), 0, s, Q, K, V, O, lse, L, H, scale);
+    else if (d == 96)
+      QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<96>, gq, dim3(512), 0, s, Q, K, V, O, lse, L, H, scale);
     else
       QLORA_LAUNCH("k_attn_fwd_fused", k_attn_fwd_fused<128>, gq, dim3(512), 0, s, Q, K, V, O, lse, L, H, scale);
     return hipGetLastError();
@@ -1016,6 +1018,8 @@ hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint
       QLORA_ATTN_BWD(32);
     } else if (d == 64) {
       QLORA_ATTN_BWD(64);
+    } else if (d == 96) {
+      QLORA_ATTN_BWD(96);
     } else {
       QLORA_ATTN_BWD(128);
     }

@@ -301,7 +301,7 @@ int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t 
  * Shapes: head_dim a multiple of 8 in [8, 1024], heads in [1, 65535],
  * batch in [0, 65535], seq in [0, 65536]; otherwise QLORA_ERR_BAD_SHAPE.
  * batch == 0 or seq == 0 does nothing.  The workspace (device, 16-byte
- * aligned) holds, for head_dim 32, 64 and 128 (fused kernels, no score
+ * aligned) holds, for head_dim 32, 64, 96 and 128 (fused kernels, no score
  * matrix in memory), the backward's D per query: 4 * seq * batch * heads
  * bytes (the forward uses none of it); for other head dims the float32
  * scores and their gradient and the bf16 P and dS: 12 * seq * roundup(seq,

@@ -231,9 +231,10 @@ def test_attention_shape_and_argument_errors(q):
     P = ctypes.c_void_p(16)
     big = 1 << 40
     up = lambda x: (x + 255) // 256 * 256
-    # head dims 32/64/128: the backward's D per query
+    # head dims 32/64/96/128: the backward's D per query
     assert q.qlora_attention_workspace_bytes(8, 512, 32, 128) == up(8 * 32 * 512 * 4)
     assert q.qlora_attention_workspace_bytes(1, 13, 2, 64) == up(2 * 13 * 4)
+    assert q.qlora_attention_workspace_bytes(1, 13, 2, 96) == up(2 * 13 * 4)
     # other head dims: float32 S and dP, bf16 P and dS, rows of roundup(seq, 8)
     assert q.qlora_attention_workspace_bytes(1, 13, 2, 8) == 2 * up(2 * 13 * 16 * 4) + 2 * up(2 * 13 * 16 * 2)
     for bad in ((1, 16, 2, 60), (1, 16, 2, 0), (1, 16, 0, 64), (-1, 16, 2, 64), (1, 70000, 2, 64), (1, 16, 2, 2048)):

@@ -10,7 +10,7 @@ which the Frobenius bar holds with room.  Shapes span several 64-wide
 tiles, ragged sequence tails, one-token sequences, rows longer than one
 512-column chunk of the row kernels (seq 600, 700), sequences of several
 128-row workgroup tiles with a ragged last one (seq 1000) or one row past
-a tile (seq 65), head dims 8 (the materialised path), 32, 64 and 128 (the
+a tile (seq 65), head dims 8 (the materialised path), 32, 64, 96 and 128 (the
 fused kernels), and the LLaMA-7B layer's 32 heads of 128 on 512-token
 sequences."""
 import numpy as np
@@ -53,7 +53,7 @@ def _run(q, batch, seq, heads, d, seed):
 
 @pytest.mark.parametrize("batch,seq,heads,d", [(2, 77, 3, 64), (1, 130, 2, 128), (3, 1, 2, 64), (2, 200, 1, 8),
                                                (1, 512, 4, 128), (1, 700, 2, 64), (1, 600, 1, 8), (2, 200, 3, 32),
-                                               (1, 1000, 1, 128), (2, 65, 1, 128)])
+                                               (1, 1000, 1, 128), (2, 65, 1, 128), (1, 300, 3, 96), (2, 100, 2, 96)])
 def test_attention_matches_oracle(q, batch, seq, heads, d):
     note(f"[attention] batch={batch} seq={seq} heads={heads} d={d}")
     (Qb, Kb, Vb, dOb), (O, lse, dQ, dK, dV) = _run(q, batch, seq, heads, d, seed=seq + 7 * heads + d)
