@@ -323,9 +323,9 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   int ckb = lkb0;
   const int np = nb >> 1;
   f32x4_t acc = zero;
-  // Pairs past the end (the loop runs whole rounds of kGvP) read zero codes,
-  // the last real X rows and in-range group constants; their sums are never
-  // stored.
+  // The loop leaves after the range's last pair (a uniform branch), so no
+  // wave computes pairs it would not store; the codes and scale words loaded
+  // ahead past the end take out-of-range offsets and are never used.
   for (int p0 = 0; p0 < np; p0 += kGvP) {
 #pragma unroll
     for (int q = 0; q < kGvP; ++q) {
@@ -370,6 +370,7 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
           ++cgr;
         }
       }
+      if (ip + 1 >= np) break;  // the last real pair (uniform)
     }
   }
 
