@@ -11,8 +11,8 @@ tiles, ragged sequence tails, one-token sequences, rows longer than one
 512-column chunk of the row kernels (seq 600, 700), sequences of several
 128-row workgroup tiles with a ragged last one (seq 1000) or one row past
 a tile (seq 65), head dims 8 (the materialised path), 32, 64, 96 and 128 (the
-fused kernels), and the LLaMA-7B layer's 32 heads of 128 on 512-token
-sequences."""
+fused kernels), the LLaMA-7B layer's 32 heads of 128 on 512-token
+sequences, and peaked attention (Q scaled by 8 or 20)."""
 import numpy as np
 import pytest
 import torch
@@ -35,10 +35,10 @@ def _bits(rng, shape, scale=1.0):
     return nf4_dq.bf16_rne_bits((rng.standard_normal(shape) * scale).astype(np.float32))
 
 
-def _run(q, batch, seq, heads, d, seed):
+def _run(q, batch, seq, heads, d, seed, qscale=1.0):
     rng = np.random.default_rng(seed)
     shape = (batch * seq, heads * d)
-    Qb, Kb, Vb, dOb = (_bits(rng, shape) for _ in range(4))
+    Qb, Kb, Vb, dOb = (_bits(rng, shape, scale) for scale in (qscale, 1.0, 1.0, 1.0))
     Q, K, V, dO = (dev_bf16(t) for t in (Qb, Kb, Vb, dOb))
     O = torch.empty_like(Q)
     lse = torch.empty(batch, heads, seq, dtype=torch.float32, device="cuda")
@@ -67,6 +67,26 @@ def test_attention_matches_oracle(q, batch, seq, heads, d):
             # exactly 0 in exact arithmetic; dP - D cancels only to float32 rounding here
             assert np.abs(f64(got)).max() <= 1e-4, f"{name} must vanish for one-token sequences"
             continue
+        assert_close(f64(got), ref, name)
+
+
+@pytest.mark.parametrize("batch,seq,heads,d,qscale", [(1, 300, 2, 128, 8.0), (2, 130, 2, 64, 20.0),
+                                                      (1, 200, 1, 96, 8.0), (1, 150, 1, 32, 20.0),
+                                                      (1, 100, 2, 8, 20.0)])
+def test_attention_peaked_matches_oracle(q, batch, seq, heads, d, qscale):
+    """Peaked attention: Q scaled so the logits spread over tens of units and
+    most rows put nearly all their weight on one or two keys.  The running
+    maximum then jumps by large amounts inside a row (the online rescale),
+    most exponentials underflow to zero, and dP - D cancels to a few leading
+    bits, the case where a D taken from the bf16-rounded O went wrong."""
+    note(f"[attention] peaked batch={batch} seq={seq} heads={heads} d={d} qscale={qscale}")
+    (Qb, Kb, Vb, dOb), (O, lse, dQ, dK, dV) = _run(q, batch, seq, heads, d, seed=5 * seq + d, qscale=qscale)
+    Qf, Kf, Vf, dOf = (f64(t) for t in (Qb, Kb, Vb, dOb))
+    rO, rlse = at.fwd(Qf, Kf, Vf, batch, seq, heads, d)
+    np.testing.assert_allclose(lse, rlse, rtol=1e-5, atol=1e-5)
+    assert_close(f64(O), rO, "O")
+    rdQ, rdK, rdV = at.bwd(Qf, Kf, Vf, dOf, batch, seq, heads, d)
+    for name, got, ref in (("dQ", dQ, rdQ), ("dK", dK, rdK), ("dV", dV, rdV)):
         assert_close(f64(got), ref, name)
 
 
