@@ -31,6 +31,8 @@ def _oracle_what(W, codebook, scales):
     (300, 640, 100, 32.0, 62, ("nf4", "dq"), ("fp4", "dq")),       # ragged rows, rank 100, Float4 out
     (1024, 4096, 64, 16.0, 63, ("fp4", "fp32"), ("nf4", "fp32")),  # single-level in and out
     (5, 3840, 1, -2.0, 64, ("nf4", "dq"), None),                   # rank 1, merged bf16 only
+    (67, 512, 16, 16.0, 65, ("nf4", "dq"), ("nf4", "dq")),         # rows not a multiple of a thread's 4, B read 8 at a time
+    (66, 1024, 12, 24.0, 66, ("fp4", "dq"), ("nf4", "dq")),        # the same with a rank not a multiple of 8
 ])
 def test_merge_adapters(q, n, k, r, alpha, seed, src, dst):
     note(f"[merge] n={n} k={k} r={r} src={src} dst={dst}")
