@@ -8,8 +8,9 @@
 //   k_quantize_blocks  one workgroup per group of 256 blocks (64 KiB of W):
 //                      absmax, codes, packed nibbles, and the group's fp64
 //                      in-order absmax sum;
-//   k_mean             one workgroup stages the group sums in LDS, one lane
-//                      folds them in order -> offset;
+//   k_mean             one workgroup: group sums staged in LDS, each lane of
+//                      a wave folds one run of 256 of them in order, then
+//                      one lane the run sums -> offset;
 //   k_encode_scales    one wave per group: dev = absmax - offset, group amax,
 //                      E4M3 codes.
 #include "qlora_internal.h"
@@ -100,41 +101,66 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict
   }
 }
 
-// offset = fp32( (in-order fp64 fold of the group sums) / nb ).  The whole
-// workgroup stages the group sums into LDS a chunk at a time (coalesced
-// loads, one memory round trip per chunk); one lane then folds the chunk in
-// order, reading one batch ahead.
-constexpr int kMeanChunk = 4096;  // fp64 sums per LDS chunk (32 KB)
-__global__ __launch_bounds__(256) void k_mean(const double *__restrict__ group_sum, int64_t ng, int64_t nb,
-                                             float *__restrict__ offset) {
-  constexpr int B = 16;                    // fold batch
-  __shared__ double s_sum[kMeanChunk + B];  // + one batch of zeros to read ahead into
-  double acc = 0.0;  // lane 0's running fold
-  for (int64_t c0 = 0; c0 < ng; c0 += kMeanChunk) {
-    const int n = (int)min<int64_t>(kMeanChunk, ng - c0);
-    for (int i = threadIdx.x; i < n + B; i += 256) s_sum[i] = i < n ? group_sum[c0 + i] : 0.0;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      // the next batch's reads go out before this batch's adds, so the
-      // dependent fp64 adds hide the LDS latency
-      const int nB = n / B * B;
-      double v[B];
+// offset = fp32( total / nb ) with the mean's fixed float64 order: each
+// run of kMeanRun consecutive group sums folded left to right, then the run
+// sums folded left to right.  One 1024-lane workgroup takes kMeanRuns runs
+// per pass: every lane stages its share of their group sums in LDS (all
+// loads issued before any store, one memory round trip), lane t of the
+// first wave folds run t from LDS (reads a batch ahead of the adds; rows
+// kMeanLd apart, so the lanes' reads spread over the banks), and lane 0
+// folds the pass's run sums into the total.  Sums are non-negative, so the
+// zeros that pad a short last run leave it unchanged.
+constexpr int kMeanRun = 256;               // group sums per run
+constexpr int kMeanRuns = 64;               // runs per pass (one wave)
+constexpr int kMeanLd = kMeanRun + 1;       // LDS stride of a staged run (doubles)
+constexpr int kMeanLanes = 1024;
+constexpr int kMeanPer = kMeanRuns * kMeanRun / kMeanLanes;  // staged sums per lane and pass
+__global__ __launch_bounds__(kMeanLanes) void k_mean(const double *__restrict__ group_sum, int64_t ng, int64_t nb,
+                                                     float *__restrict__ offset) {
+  constexpr int B = 16;  // LDS reads ahead of the adds
+  __shared__ double s_sum[kMeanRuns * kMeanLd];
+  __shared__ double s_run[kMeanRuns];
+  const int64_t nruns = (ng + kMeanRun - 1) / kMeanRun;
+  double total = 0.0;  // lane 0's fold of the run sums
+  for (int64_t r0 = 0; r0 < nruns; r0 += kMeanRuns) {
+    const int64_t g0 = r0 * kMeanRun;
+    const int64_t n = min<int64_t>(kMeanRuns * kMeanRun, ng - g0);  // group sums of this pass
+    double v[kMeanPer];
 #pragma unroll
-      for (int q = 0; q < B; ++q) v[q] = s_sum[q];
-      for (int i = 0; i < nB; i += B) {
-        double nx[B];
+    for (int u = 0; u < kMeanPer; ++u) {
+      const int e = (int)threadIdx.x + kMeanLanes * u;
+      v[u] = e < n ? group_sum[g0 + e] : 0.0;
+    }
 #pragma unroll
-        for (int q = 0; q < B; ++q) nx[q] = s_sum[i + B + q];
-#pragma unroll
-        for (int q = 0; q < B; ++q) acc += v[q];
-#pragma unroll
-        for (int q = 0; q < B; ++q) v[q] = nx[q];
-      }
-      for (int i = nB; i < n; ++i) acc += s_sum[i];
+    for (int u = 0; u < kMeanPer; ++u) {
+      const int e = (int)threadIdx.x + kMeanLanes * u;
+      s_sum[(e / kMeanRun) * kMeanLd + e % kMeanRun] = v[u];
     }
     __syncthreads();
+    if (threadIdx.x < kMeanRuns) {
+      const double *p = s_sum + threadIdx.x * kMeanLd;
+      double acc = 0.0, cur[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) cur[q] = p[q];
+      for (int i = 0; i < kMeanRun; i += B) {
+        double nx[B];
+#pragma unroll
+        for (int q = 0; q < B; ++q) nx[q] = i + B < kMeanRun ? p[i + B + q] : 0.0;
+#pragma unroll
+        for (int q = 0; q < B; ++q) acc += cur[q];
+#pragma unroll
+        for (int q = 0; q < B; ++q) cur[q] = nx[q];
+      }
+      s_run[threadIdx.x] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int m = (int)min<int64_t>(kMeanRuns, nruns - r0);
+      for (int i = 0; i < m; ++i) total += s_run[i];
+    }
+    __syncthreads();  // the next pass overwrites s_sum and s_run
   }
-  if (threadIdx.x == 0) *offset = (float)(acc / (double)nb);
+  if (threadIdx.x == 0) *offset = (float)(total / (double)nb);
 }
 
 // One wave per group, four block constants per lane.
@@ -184,7 +210,7 @@ hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, b
   QLORA_LAUNCH("k_quantize_blocks", k_quantize_blocks, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codebook_thresholds(codebook), packed,
                      ws_absmax, ws_group_sum);
   if (single_level) return hipGetLastError();
-  QLORA_LAUNCH("k_mean", k_mean, dim3(1), dim3(256), 0, s, ws_group_sum, ng, nb, offset);
+  QLORA_LAUNCH("k_mean", k_mean, dim3(1), dim3(kMeanLanes), 0, s, ws_group_sum, ng, nb, offset);
   QLORA_LAUNCH("k_encode_scales", k_encode_scales, dim3((unsigned)ceil_div(ng, 4)), dim3(256), 0, s, ws_absmax, nb, ng,
                      offset, scale_code, group_amax);
   return hipGetLastError();

@@ -52,6 +52,7 @@ F64 = np.float64
 
 BLOCK = 64   # weights per first-level block  [explainer step 2; teardown sec. 3, B_1]
 GROUP = 256  # block constants per second-level group  [explainer step 3; teardown sec. 3, B_2]
+MEAN_RUN = 256  # group sums per run in the mean's summation order (a reading, not the pages')
 
 
 # --------------------------------------------------------------------------
@@ -293,12 +294,17 @@ def unpack_nibbles(packed) -> np.ndarray:
 # --------------------------------------------------------------------------
 # Level 2: double quantization of the block constants
 # --------------------------------------------------------------------------
-def _groups_padded(values, fill) -> np.ndarray:
+def _rows_padded(values, width: int, fill) -> np.ndarray:
+    """values as rows of `width`, the last row padded with `fill`."""
     v = np.asarray(values).reshape(-1)
-    ng = -(-v.size // GROUP)
-    out = np.full(ng * GROUP, fill, dtype=v.dtype)
+    rows = -(-v.size // width)
+    out = np.full(rows * width, fill, dtype=v.dtype)
     out[:v.size] = v
-    return out.reshape(ng, GROUP)
+    return out.reshape(rows, width)
+
+
+def _groups_padded(values, fill) -> np.ndarray:
+    return _rows_padded(values, GROUP, fill)
 
 
 def dq_offset(absmax) -> np.float32:
@@ -307,18 +313,22 @@ def dq_offset(absmax) -> np.float32:
     [explainer step 3 'after subtracting their mean'; teardown sec. 3 Level 2
     mean(c_1)].  Reading: one mean per tensor (the video page's idealized
     4.126953125 bits/weight leaves mean offsets out, which a per-group mean
-    would not allow).  Summation order, fixed so that the float32 result is
-    unique: float64 sequential in block order inside each group of 256, then
-    float64 sequential over the group partial sums, then divide by the block
-    count in float64 and round to float32.  (np.add.accumulate is a
-    left-to-right fold; the zero padding of a short last group adds +0.0,
-    which leaves a non-negative sum unchanged.)
+    would not allow).  The pages fix no summation order; this one is fixed so
+    that the float32 result is unique, in three float64 levels, each a
+    left-to-right fold: the block absmax values inside each group of 256
+    blocks, then the group sums inside each run of MEAN_RUN consecutive
+    groups, then the run sums; the total is divided by the block count in
+    float64 and rounded to float32.  (np.add.accumulate is a left-to-right
+    fold; the zero padding of a short last group or run adds +0.0, which
+    leaves a non-negative sum unchanged.  A tensor of at most MEAN_RUN groups
+    has one run, whose fold is the fold over all group sums.)
     """
     a = np.asarray(absmax, dtype=F32).astype(F64)
     if a.size == 0:
         raise ValueError("no blocks")
     per_group = np.add.accumulate(_groups_padded(a, 0.0), axis=1)[:, -1]
-    total = np.add.accumulate(per_group)[-1]
+    per_run = np.add.accumulate(_rows_padded(per_group, MEAN_RUN, 0.0), axis=1)[:, -1]
+    total = np.add.accumulate(per_run)[-1]
     return F32(total / F64(a.size))
 
 

@@ -187,13 +187,47 @@ def test_toy_three_bit_example():
 # -------------------------------------------------------- double quantization
 def test_mean_matches_exact_rational_mean():
     rng = np.random.default_rng(4)
-    for nb in (1, 255, 256, 257, 5000):
+    # up to 256 groups the group sums form one run; 65537 and 140000 blocks
+    # take two and three runs (the last one short)
+    for nb in (1, 255, 256, 257, 5000, 65537, 140000):
         a = np.abs(rng.standard_normal(nb) * 0.05).astype(F32)
         exact = sum((Fraction(float(v)) for v in a), Fraction(0)) / nb
         off = nf4_dq.dq_offset(a)
         ulp = np.spacing(F32(float(exact)))
         # float64 partial sums add at most ~nb * 2^-53 relative error
         assert abs(Fraction(float(off)) - exact) <= Fraction(float(ulp)) / 2 + exact * Fraction(nb, 2**52)
+
+
+def test_mean_of_one_run_is_the_fold_over_the_group_sums():
+    """The vectorized folds (padded reshapes) against plain scalar loops: up
+    to MEAN_RUN groups the run level is one fold over every group sum; past
+    it, the run sums of consecutive groups are folded in order."""
+    rng = np.random.default_rng(8)
+    for nb in (3000, 256 * nf4_dq.MEAN_RUN, 256 * nf4_dq.MEAN_RUN + 1000):
+        a = np.abs(rng.standard_normal(nb) * 0.05).astype(F32).astype(np.float64)
+        ng = -(-nb // 256)
+        seq = 0.0
+        for i in range(0, nb, 256):  # the group's own left-to-right fold
+            g = 0.0
+            for v in a[i:i + 256]:
+                g += v
+            seq += g
+        runs = []
+        for r0 in range(0, ng, nf4_dq.MEAN_RUN):
+            acc = 0.0
+            for i in range(r0 * 256, min(nb, (r0 + nf4_dq.MEAN_RUN) * 256), 256):
+                g = 0.0
+                for v in a[i:i + 256]:
+                    g += v
+                acc += g
+            runs.append(acc)
+        tot = 0.0
+        for v in runs:
+            tot += v
+        off = nf4_dq.dq_offset(a.astype(F32))
+        assert off == np.float32(tot / nb)
+        if len(runs) == 1:
+            assert off == np.float32(seq / nb)
 
 
 def test_single_block_tensor_is_lossless():
