@@ -134,8 +134,9 @@ size_t qlora_quantize_workspace_bytes(int64_t n, int64_t k);
  * Level 2:
  *   absmax_b = max |w| over block b;  x = fp32(w / absmax_b) (0 if absmax_b=0)
  *   code = index of the nearest NF4 level (ties to the lower index)
- *   offset = fp32( (sum over groups, in order, of the fp64 in-order sum of the
- *            group's absmax) / nb )
+ *   offset = fp32( T / nb ), T in fp64, every sum a left-to-right fold: the
+ *            absmax values of each group of 256 blocks, then the group sums
+ *            of each run of 256 consecutive groups, then the run sums
  *   dev_b = fp32(absmax_b - offset); group_amax_g = max |dev_b| over g
  *   scale_code_b = E4M3FN round-to-nearest-even of fp32(dev_b / group_amax_g)
  *                  (0x00 when group_amax_g == 0)
