@@ -18,25 +18,52 @@
 namespace qlora {
 namespace {
 
-// a if b else c, as a bit blend: the operands are wave-uniform thresholds
-// in scalar registers, so this stays a register select (a conditional
-// element choice would be turned into an indexed load from a stack copy of
-// the threshold array).
-__device__ __forceinline__ float pick(bool b, float a, float c) {
-  const uint32_t m = 0u - (uint32_t)b;
-  return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(c) & ~m));
+// Nearest-level code from a 129-entry table: code(x) = #{ j : x >= t[j] }
+// for x = w / absmax in [-1, 1].  Bucket i = floor(64 x) + 64 covers
+// [(i - 64)/64, (i - 63)/64) (x = 1 alone in bucket 128); 64 x is exact, so
+// the bucket is too.  Entry i holds the count of thresholds at or below the
+// bucket's lower edge and the one threshold strictly inside it (+inf if
+// none), so code = count + (x >= inside).  Both codebooks' thresholds are
+// more than 1/64 apart, so no bucket holds two.
+struct CodeEntry {
+  float inside;
+  uint32_t count;
+};
+constexpr int kCodeBuckets = 129;
+
+__device__ __forceinline__ void fill_code_table(CodeEntry *tab, const float (&t)[15], int tid) {
+  if (tid < kCodeBuckets) {
+    const float lo = (float)(tid - 64) * (1.f / 64.f), hi = lo + 1.f / 64.f;  // exact
+    uint32_t count = 0;
+    float inside = __builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+      count += t[j] <= lo ? 1u : 0u;
+      if (t[j] > lo && t[j] < hi) inside = t[j];
+    }
+    tab[tid] = CodeEntry{inside, count};
+  }
 }
 
-// Index of the nearest NF4 level from the 15 thresholds: a 4-step binary
-// search (each step a compare and selects between uniform thresholds).
-__device__ __forceinline__ uint32_t nf4_code(float x, const float (&t)[15]) {
-  const bool b3 = x >= t[7];
-  const bool b2 = x >= pick(b3, t[11], t[3]);
-  const bool b1 = x >= pick(b3, pick(b2, t[13], t[9]), pick(b2, t[5], t[1]));
-  const float t0 = pick(b3, pick(b2, pick(b1, t[14], t[12]), pick(b1, t[10], t[8])),
-                        pick(b2, pick(b1, t[6], t[4]), pick(b1, t[2], t[0])));
-  const bool b0 = x >= t0;
-  return (uint32_t(b3) << 3) | (uint32_t(b2) << 2) | (uint32_t(b1) << 1) | uint32_t(b0);
+__device__ __forceinline__ uint32_t code_of(float x, const CodeEntry *tab) {
+  const int b = min(max((int)floorf(x * 64.f) + 64, 0), kCodeBuckets - 1);  // the clamp only guards the read
+  const CodeEntry e = tab[b];
+  return e.count + (x >= e.inside ? 1u : 0u);
+}
+
+// x = RN(w / m) for |w| <= m.  For 2^-60 <= m <= 2^60 with y = RN(1 / m):
+// q0 = RN(w y), the remainder w - q0 m is exact as one FMA, and
+// RN(q0 + r y) is the correctly rounded quotient (Markstein's correction
+// step for round-to-nearest); quotients that would be subnormal may differ
+// by an ulp there, which no code decision sees (every threshold is more than
+// 0.03 from zero).  Other m: the IEEE division.
+__device__ __forceinline__ float quotient(float w, float m, float y, bool fast) {
+  if (fast) {
+    const float q0 = __fmul_rn(w, y);
+    const float r = __fmaf_rn(-q0, m, w);
+    return __fmaf_rn(r, y, q0);
+  }
+  return m > 0.f ? __fdiv_rn(w, m) : 0.f;  // an all-zero block normalizes to 0
 }
 
 // Eight consecutive weights per lane, eight lanes per 64-weight block, so a
@@ -47,9 +74,12 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict
                                                          float *__restrict__ absmax_out,
                                                          double *__restrict__ group_sum) {
   __shared__ float s_absmax[kGroup];
+  __shared__ CodeEntry s_code[kCodeBuckets];
   float t[15];  // the thresholds in (scalar) registers
 #pragma unroll
   for (int j = 0; j < 15; ++j) t[j] = T.t[j];
+  fill_code_table(s_code, t, threadIdx.x);
+  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t first = (int64_t)blockIdx.x * kGroup;
   const int nblk = (int)min<int64_t>(kGroup, nb - first);
@@ -71,13 +101,11 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict
     m = fmaxf(m, __shfl_xor(m, 4, 64));
     if (valid) {
       const float w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      const bool fast = m >= 0x1p-60f && m <= 0x1p60f;
+      const float y = fast ? __fdiv_rn(1.f, m) : 0.f;
       uint32_t word = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // IEEE round-to-nearest division; an all-zero block normalizes to 0.
-        const float x = m > 0.f ? __fdiv_rn(w[i], m) : 0.f;
-        word |= nf4_code(x, t) << (4 * i);
-      }
+      for (int i = 0; i < 8; ++i) word |= code_of(quotient(w[i], m, y, fast), s_code) << (4 * i);
       *reinterpret_cast<uint32_t *>(packed + e0 / 2) = word;
       if ((lane & 7) == 0) {
         absmax_out[first + lb] = m;
@@ -86,17 +114,47 @@ __global__ __launch_bounds__(256) void k_quantize_blocks(const float *__restrict
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {  // block order; eight LDS reads in flight per batch
+  // The group's float64 sum in block order.  Every absmax is a multiple of
+  // 2^lo (the smallest ulp among them) and every partial sum is below
+  // 2^(hi + 9) (256 values under 2^(hi+1)); when that span fits float64's 53
+  // bits no addition rounds, so a tree over the waves gives the in-order
+  // fold's bits exactly.  Otherwise one lane folds in block order.
+  const float v = threadIdx.x < nblk ? s_absmax[threadIdx.x] : 0.f;
+  const int ex = (int)((__float_as_uint(v) >> 23) & 0xFFu);
+  int hi = v > 0.f ? (ex ? ex - 127 : -126) : -1000;  // v < 2^(hi+1)
+  int lo = v > 0.f ? (ex ? ex - 150 : -149) : 1000;   // v is a multiple of 2^lo
+  double sum = (double)v;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    hi = max(hi, __shfl_xor(hi, o, 64));
+    lo = min(lo, __shfl_xor(lo, o, 64));
+    sum += __shfl_xor(sum, o, 64);
+  }
+  __shared__ double s_wsum[4];
+  __shared__ int s_span[4][2];
+  if (lane == 0) {
+    s_wsum[wave] = sum;
+    s_span[wave][0] = hi;
+    s_span[wave][1] = lo;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int ghi = max(max(s_span[0][0], s_span[1][0]), max(s_span[2][0], s_span[3][0]));
+    const int glo = min(min(s_span[0][1], s_span[1][1]), min(s_span[2][1], s_span[3][1]));
     double acc = 0.0;
-    int i = 0;
-    for (; i + 8 <= nblk; i += 8) {
-      float v[8];
+    if (ghi + 9 - glo <= 53) {
+      acc = ((s_wsum[0] + s_wsum[1]) + s_wsum[2]) + s_wsum[3];
+    } else {  // block order; eight LDS reads in flight per batch
+      int i = 0;
+      for (; i + 8 <= nblk; i += 8) {
+        float u[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = s_absmax[i + q];
+        for (int q = 0; q < 8; ++q) u[q] = s_absmax[i + q];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc += (double)v[q];
+        for (int q = 0; q < 8; ++q) acc += (double)u[q];
+      }
+      for (; i < nblk; ++i) acc += (double)s_absmax[i];
     }
-    for (; i < nblk; ++i) acc += (double)s_absmax[i];
     group_sum[blockIdx.x] = acc;
   }
 }

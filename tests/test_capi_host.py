@@ -95,6 +95,20 @@ def test_library_thresholds_are_the_exact_midpoint_successors(q, name):
     assert np.array_equal(via_t, nf4_dq.nearest_level(xs, levels))
 
 
+@pytest.mark.parametrize("name", ["nf4", "fp4"])
+def test_thresholds_fit_the_quantizer_bucket_table(q, name):
+    """The quantizer finds a code from a table of 64ths of [-1, 1]: bucket
+    floor(64 x) + 64 holds the count of thresholds at or below its lower edge
+    and at most one threshold inside.  That needs the thresholds more than
+    1/64 apart and, past -1, no threshold below -1 (x >= -1)."""
+    t = np.array(q.qlora_thresholds(q.CODEBOOKS[name]), np.float64)
+    assert np.all(np.diff(t) > 1.0 / 64.0)
+    assert t[0] > -1.0
+    for i in range(129):
+        lo, hi = (i - 64) / 64.0, (i - 63) / 64.0
+        assert np.count_nonzero((t > lo) & (t < hi)) <= 1
+
+
 def test_sizes_and_bits(q):
     for n, k in ((256, 256), (4096, 4096), (11008, 4096), (8192, 22016), (3, 64)):
         pb, sb, ng = q.qlora_nf4_sizes(n, k)
