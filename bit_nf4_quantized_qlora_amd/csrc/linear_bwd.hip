@@ -4,16 +4,17 @@
 // dequantized again on the fly, and dL/dW is never materialized; "QLoRA,
 // explained." step 5: gradients reach the adapters only.  With
 // Y = X W_hat^T + s (X A^T) B^T:
-//   G  = s dY B            (k_nt_splitk on dY and B^T)
+//   G  = s dY B            (k_nt_dma on dY and B as it lies for r % 8 == 0,
+//                           r <= 64; otherwise on dY and a copy of B^T)
 //   dX = dY W_hat + G A    (k_bwd_dx_nf4 in nf4_tile.hip, its contraction
 //                           split when the tiles cannot fill the GPU;
 //                           k_bwd_dx below when n % 64 != 0)
 //   dB = s dY^T H          (k_tn_splitk on dY and (sH)^T)
 //   dA = G^T X             (k_tn_splitk on X and G^T; one launch with dB's,
 //                           before the dX launch)
-// The small layout copies (B^T, A^T, (sH)^T), the tile kernel's block-scale
-// table and the partial reductions run as jobs.hip launches, several jobs
-// per launch.
+// The small layout copies (A^T, (sH)^T, and B^T where needed), the tile
+// kernel's block-scale table and the partial reductions run as jobs.hip
+// launches, several jobs per launch.
 //
 // k_bwd_dx, the general fallback, contracts over n, the row index of W, by
 // laying the dequantized tile into LDS transposed: each thread expands one
@@ -220,20 +221,29 @@ hipError_t launch_linear_bwd(const LinearArgs &a, const uint16_t *X, const uint1
     QLORA_TRY(launch_reduce_rows(part, l.sp_h.splits, M, RP, r, 1.f, Hw, nullptr, nullptr, 0, s));
     H = Hw;
   }
-  // layouts: sHt = bf16(s H)^T [RP][Mp], Bt [RP][N], At [K][RP]; and the dX
-  // tile kernel's block-scale table -- one launch
+  // layouts: sHt = bf16(s H)^T [RP][Mp], At [K][RP]; and the dX tile
+  // kernel's block-scale table.  G = s dY B -> Gb [M][RP], Gt [RP][Mp].
+  // When the product can read B [N][r] as it lies (r % 8 == 0, r <= 64), G's
+  // split partials come first and their reduction joins the layout jobs in
+  // one launch; otherwise B is transposed to Bt [RP][N] first.
   const bool tiles = dX != nullptr && plan_linear(M, N, K, r, a.w.absmax != nullptr).dx_path == QLORA_PATH_TILE;
   float *scales = reinterpret_cast<float *>(base + l.scale_off);
+  const bool b_rows = nt_rows_supported(r, N);
   SmallJob prep[kMaxJobs];
   int np = 0;
   prep[np++] = job_scale_transpose(H, M, r, a.s, sHt, RP, l.Mp);
-  prep[np++] = job_transpose_pad(B, N, r, Bt, RP, N);
   prep[np++] = job_transpose_pad(A, r, K, At, K, RP);
   if (tiles) prep[np++] = job_scales_bwd(a.w, scales);
-  QLORA_TRY(launch_jobs("k_prep_bwd", prep, np, s));
-  // G = s dY B -> Gb [M][RP], Gt [RP][Mp]
-  QLORA_TRY(launch_nt_splitk(dY, M, Bt, RP, RP, N, N, l.sp_g, part, s));
-  QLORA_TRY(launch_reduce_rows(part, l.sp_g.splits, M, RP, r, a.s, nullptr, Gb, Gt, l.Mp, s));
+  if (b_rows) {
+    QLORA_TRY(launch_nt_rows(dY, M, B, r, RP, N, N, l.sp_g, part, s));
+    prep[np++] = job_reduce_rows(part, l.sp_g.splits, M, RP, r, a.s, nullptr, Gb, Gt, l.Mp);
+    QLORA_TRY(launch_jobs("k_prep_bwd", prep, np, s));
+  } else {
+    prep[np++] = job_transpose_pad(B, N, r, Bt, RP, N);
+    QLORA_TRY(launch_jobs("k_prep_bwd", prep, np, s));
+    QLORA_TRY(launch_nt_splitk(dY, M, Bt, RP, RP, N, N, l.sp_g, part, s));
+    QLORA_TRY(launch_reduce_rows(part, l.sp_g.splits, M, RP, r, a.s, nullptr, Gb, Gt, l.Mp, s));
+  }
   // dB = dY^T sH and dA = G^T X: one launch of split partials (before the
   // dX launch, so a split dX launch's reduction can share the launch of
   // their fixed-order reductions)

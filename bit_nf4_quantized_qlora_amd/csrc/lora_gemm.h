@@ -59,6 +59,12 @@ SplitPlan plan_split(int64_t tiles, int64_t steps);
 
 hipError_t launch_nt_splitk(const uint16_t *P, int64_t rowsP, const uint16_t *Q, int rowsQ, int RP, int64_t lenC,
                             int64_t ld, const SplitPlan &sp, float *part, hipStream_t s);
+// The same partials with Q given as its transpose Qr [lenC][r] (row stride
+// r): Q[j][c] = Qr[c][j] for j < r, zero for r <= j < RP.  Needs
+// nt_rows_supported (r % 8 == 0, r <= 64, ld % 8 == 0).
+bool nt_rows_supported(int r, int64_t ld);
+hipError_t launch_nt_rows(const uint16_t *P, int64_t rowsP, const uint16_t *Qr, int r, int RP, int64_t lenC,
+                          int64_t ld, const SplitPlan &sp, float *part, hipStream_t s);
 // rows_out: partials as [S][D][RP] (reduced with rows_out into [D][r]);
 // otherwise [S][RP][D].
 hipError_t launch_tn_splitk(const uint16_t *P, int64_t M, int64_t D, const uint16_t *Qt, int64_t ldq, int RP,

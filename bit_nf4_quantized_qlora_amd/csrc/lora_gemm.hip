@@ -157,13 +157,21 @@ __device__ __forceinline__ void dma_tile(const uint16_t *base, int64_t nrows, in
 
 // part[s][i][j] = sum over split s of P[i][c] Q[j][c]: 64 rows of P per
 // workgroup (16 per wave), all RP rows of Q.
-template <int TJ>
+// kQRows: Q is given as its transpose, Qr [lenC][ldqr] (row c holds Q[.][c],
+// its first rowsQ entries real; RP <= 64): each step stages the [64 c][64 j]
+// tile of Qr as it lies and reads the MFMA operands down its columns with
+// ds_read_b64_tr_b16 (as k_tn_dma reads its P tile), so no transposed copy
+// of Q is needed.
+template <int TJ, bool kQRows = false>
 __global__ __launch_bounds__(256) void k_nt_dma(const uint16_t *__restrict__ P, int64_t rowsP,
                                                 const uint16_t *__restrict__ Q, int rowsQ, int64_t lenC, int64_t ld,
-                                                int steps_per_split, float *__restrict__ part) {
-  constexpr int RP = 16 * TJ, NQ = RP / 32, NV = 2 + NQ;  // copy instructions per wave and step
+                                                int steps_per_split, float *__restrict__ part, int64_t ldqr = 0) {
+  static_assert(!kQRows || TJ <= 4, "the transposed Q form stages one 64-column tile");
+  constexpr int RP = 16 * TJ, NQ = kQRows ? 2 : RP / 32, NV = 2 + NQ;  // copy instructions per wave and step
+  constexpr int QT = kQRows ? 64 * 64 : RP * 64;  // elements of one staged Q tile
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
   __shared__ __align__(16) uint16_t P0[64 * 64], P1[64 * 64], P2[64 * 64], P3[64 * 64];
-  __shared__ __align__(16) uint16_t Q0[RP * 64], Q1[RP * 64], Q2[RP * 64], Q3[RP * 64];
+  __shared__ __align__(16) uint16_t Q0[QT], Q1[QT], Q2[QT], Q3[QT];
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t i0 = (int64_t)blockIdx.x * 64;
@@ -181,11 +189,20 @@ __global__ __launch_bounds__(256) void k_nt_dma(const uint16_t *__restrict__ P, 
   auto copy = [&](int64_t st, auto B) {
     const bool live = st < s1;
     dma_tile<2>(P, rowsP, lenC, ld, i0, st * 64, live, pbuf(B), 16 * wave, lane);
-    dma_tile<NQ>(Q, rowsQ, lenC, ld, 0, st * 64, live, qbuf(B), 8 * NQ * wave, lane);
+    if constexpr (kQRows)
+      dma_tile<2>(Q, lenC, rowsQ, ldqr, st * 64, 0, live, qbuf(B), 16 * wave, lane);
+    else
+      dma_tile<NQ>(Q, rowsQ, lenC, ld, 0, st * 64, live, qbuf(B), 8 * NQ * wave, lane);
   };
   f32x4_t acc[TJ];
 #pragma unroll
   for (int t = 0; t < TJ; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // kQRows: transposed-read address of lane (li, g) for sub-step t, half h
+  // and column tile jt: row 32t + 8g + 4h + li/4, columns 16jt + 4(li & 3) ..
+  auto tr_off = [&](int t, int h, int jt) -> int {
+    const int row = 32 * t + 8 * g + 4 * h + (li >> 2), col = 16 * jt + 4 * (li & 3);
+    return row * 64 + swz_chunk(row, col >> 3) * 8 + (col & 7);
+  };
 
   copy(s0, std::integral_constant<int, 0>());
   copy(s0 + 1, std::integral_constant<int, 1>());
@@ -202,8 +219,17 @@ __global__ __launch_bounds__(256) void k_nt_dma(const uint16_t *__restrict__ P, 
       const u32x4_t a = *reinterpret_cast<const u32x4_t *>(ps + row * 64 + swz_chunk(row, c) * 8);
 #pragma unroll
       for (int jt = 0; jt < TJ; ++jt) {
-        const int qr = 16 * jt + li;
-        const u32x4_t b = *reinterpret_cast<const u32x4_t *>(qs + qr * 64 + swz_chunk(qr, c) * 8);
+        u32x4_t b;
+        if constexpr (kQRows) {
+          const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t *)(qs + tr_off(t, 0, jt)));
+          const s16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4_t *)(qs + tr_off(t, 1, jt)));
+          b = __builtin_bit_cast(u32x4_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          const int qr = 16 * jt + li;
+          b = *reinterpret_cast<const u32x4_t *>(qs + qr * 64 + swz_chunk(qr, c) * 8);
+        }
         acc[jt] = mfma16(a, b, acc[jt]);
       }
     }
@@ -382,6 +408,21 @@ hipError_t launch_nt_splitk(const uint16_t *P, int64_t rowsP, const uint16_t *Q,
                    ld, vec_ok, sp.steps_per_split, part);
     return hipGetLastError();
   });
+}
+
+bool nt_rows_supported(int r, int64_t ld) { return r % 8 == 0 && r <= 64 && ld % 8 == 0; }
+
+hipError_t launch_nt_rows(const uint16_t *P, int64_t rowsP, const uint16_t *Qr, int r, int RP, int64_t lenC,
+                          int64_t ld, const SplitPlan &sp, float *part, hipStream_t s) {
+  if (!nt_rows_supported(r, ld) || RP > 64) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)ceil_div(rowsP, 64), (unsigned)sp.splits);
+  if (RP == 32)
+    QLORA_LAUNCH("k_nt_dma", (k_nt_dma<2, true>), grid, dim3(256), 0, s, P, rowsP, Qr, r, lenC, ld,
+                 sp.steps_per_split, part, (int64_t)r);
+  else
+    QLORA_LAUNCH("k_nt_dma", (k_nt_dma<4, true>), grid, dim3(256), 0, s, P, rowsP, Qr, r, lenC, ld,
+                 sp.steps_per_split, part, (int64_t)r);
+  return hipGetLastError();
 }
 
 hipError_t launch_tn_splitk(const uint16_t *P, int64_t M, int64_t D, const uint16_t *Qt, int64_t ldq, int RP,
