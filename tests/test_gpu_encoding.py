@@ -117,6 +117,35 @@ def test_q_proj_full_tensor(q):
     _full_check(q, I.weight(w, 0), "q_proj_7b")
 
 
+def test_mean_offset_past_one_staging_pass(q):
+    """A weight of 4,259,840 blocks (16,640 groups, 65 runs of group sums):
+    the mean's run folds take two passes through LDS.  One nonzero per block
+    makes every absmax a known draw, so the oracle's offset, scale codes and
+    group constants come from those values alone; the packed codes of every
+    block's first byte are checked too (the nonzero codes to the top or
+    bottom level, the rest to zero)."""
+    n, k = 8192, 33280  # 520 blocks per row
+    nb = n * k // 64
+    note(f"[encoding] mean over {nb} blocks, {-(-nb // 256)} groups")
+    rng = np.random.default_rng(21)
+    a = (2.0 ** rng.uniform(-9, 2, nb)).astype(np.float32)
+    sign = np.where(rng.random(nb) < 0.5, -1.0, 1.0).astype(np.float32)
+    W = np.zeros((nb, 64), np.float32)
+    W[:, 0] = a * sign
+    W = W.reshape(n, k)
+    w = gpu_quantize(q, W)
+    del W
+    got = encoding_to_host(w)
+    off = nf4_dq.dq_offset(a)
+    assert np.float32(got["offset"]).view(np.uint32) == np.float32(off).view(np.uint32), "offset"
+    code, amax = nf4_dq.dq_encode(a, off)
+    assert np.array_equal(got["scale_code"], code), "scale_code"
+    assert np.array_equal(got["group_amax"].view(np.uint32), amax.view(np.uint32)), "group_amax"
+    first = got["packed"].reshape(nb, 32)[:, 0]
+    assert np.array_equal(first, np.where(sign > 0, 0x7F, 0x70).astype(np.uint8)), "first byte of each block"
+    assert np.all(got["packed"].reshape(nb, 32)[:, 1:] == 0x77), "the zero weights"
+
+
 @pytest.mark.parametrize("wname,li", [("up_65b", 0)] + [("block_65b", i) for i in range(7)])
 def test_full_size_sampled(q, wname, li):
     """Full-size 65B layers (the 7B MLP layers are compared whole in the
