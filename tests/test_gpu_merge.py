@@ -7,6 +7,7 @@ import torch
 from bit_nf4_quantized_qlora_amd import inputs as I
 from gpu_helpers import dev_bf16, encoding_to_host, gpu_quantize, host_bf16, note
 from oracle import merge, nf4_dq
+from oracle_views import OracleWeight
 
 pytestmark = pytest.mark.gpu
 
@@ -66,3 +67,28 @@ def test_merge_adapters(q, n, k, r, alpha, seed, src, dst):
             assert np.array_equal(h[key], e[key]), f"re-encoded {key}"
         assert np.array_equal(h["group_amax"].view(np.uint32), e["group_amax"].view(np.uint32)), "group_amax"
         assert np.float32(h["offset"]).view(np.uint32) == np.float32(e["offset"]).view(np.uint32), "offset"
+
+
+def test_merge_full_size_sampled(q):
+    """The 7B gate layer (11008 x 4096, r = 64): W' and its bf16 copy bit for
+    bit on a random row of every 256-row group and both ends, against the
+    oracle's merge of those rows (each row of W' depends only on its own row
+    of W_hat and of B)."""
+    wl = I.WORKLOADS["mlp_7b"]
+    W = I.weight(wl, 0)
+    n, k = W.shape
+    note(f"[merge] full size {n}x{k} r={wl.r}, sampled rows")
+    Ab, Bb = I.adapters(wl, 0)
+    w = gpu_quantize(q, W)
+    Wb = torch.empty(n, k, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(q.qlora_merge_workspace_bytes(n, k), dtype=torch.uint8, device="cuda")
+    q.qlora_merge_adapters(w, dev_bf16(Ab), dev_bf16(Bb), wl.r, wl.alpha, Wb, None, ws)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, n - 1]] + [g.integers(r0, min(r0 + 256, n), 1) for r0 in range(0, n, 256)]))
+    ow = OracleWeight(W)
+    ref = merge.merged_f32(ow.row_what_bits(rows), Ab, Bb[rows], wl.alpha)
+    got = ws[: n * k * 4].view(torch.float32).view(n, k)[torch.as_tensor(rows, device="cuda")].cpu().numpy()
+    bad = np.flatnonzero(got.view(np.uint32) != ref.view(np.uint32))
+    assert bad.size == 0, f"merged float32 rows: {bad.size} differ, first {bad[:5]}"
+    assert np.array_equal(host_bf16(Wb)[rows], nf4_dq.bf16_rne_bits(ref)), "merged bf16 rows"
