@@ -4,7 +4,7 @@
 // (alpha/r) X L_1 L_2, with the weights expanded from NF4 to BF16 on every
 // use ("QLoRA, explained." step 4).
 //
-//   1. H = X A^T (k_nt_splitk, then its reduction in one launch with the
+//   1. H = X A^T (k_nt_dma, then its reduction in one launch with the
 //      tile kernel's block-scale table): fp32 H (optional output) and
 //      bf16(s*H) for the LoRA term.
 //   2. k_fwd_nf4 (nf4_tile.hip): Y = X W_hat^T + sH B^T on

@@ -5,14 +5,18 @@
 // adapters only ("QLoRA, explained." step 5).  The products here are skinny:
 // one side has r <= 128 rows, the contraction runs over k, n or M.
 //
-//   k_nt_splitk    part[s][i][j] = sum_{c in split s} P[i][c] * Q[j][c]
-//                  (both operands contraction-contiguous): H = X A^T and
-//                  G = dY B (with B pre-transposed).
-//   k_tn_splitk    part[s][j][i] = sum_{m in split s} P[m][i] * Qt[j][m]
-//                  (P is a big row-major [M][D] operand, transposed while it
-//                  is staged to LDS): dB = dY^T (sH) and dA = G^T X.
-//   k_reduce_*     sum the split partials in a fixed order (deterministic)
-//                  and write the fp32 / bf16 / transposed forms needed next.
+//   k_nt_dma       part[s][i][j] = sum_{c in split s} P[i][c] * Q[j][c]
+//                  (both operands contraction-contiguous): H = X A^T; and,
+//                  with Q given as it lies ([c][j], read down its columns),
+//                  G = dY B without a transposed copy of B.
+//   k_tn_dma       part[s][j][i] = sum_{m in split s} P[m][i] * Qt[j][m]
+//                  (P is a big row-major [M][D] operand, read transposed out
+//                  of LDS): dB = dY^T (sH) and dA = G^T X, one launch.
+//   k_nt_splitk,   the same products for row strides that are not a
+//   k_tn_splitk    multiple of 8 elements (no 16-byte DMA copies).
+//   Reductions     the split partials summed in a fixed order (deterministic)
+//                  into the fp32 / bf16 / transposed forms needed next, as
+//                  jobs of jobs.hip.
 #include "lora_gemm.h"
 
 namespace qlora {
