@@ -10,8 +10,8 @@ which the Frobenius bar holds with room.  Shapes span several 64-wide
 tiles, ragged sequence tails, one-token sequences, rows longer than one
 512-column chunk of the row kernels (seq 600, 700), sequences of several
 128-row workgroup tiles with a ragged last one (seq 1000) or one row past
-a tile (seq 65), head dims 8 (the materialised path), 32, 64, 96 and 128 (the
-fused kernels), the LLaMA-7B layer's 32 heads of 128 on 512-token
+a tile (seq 65), head dims 8, 48 and 160 (the materialised path), 32, 64, 96
+and 128 (the fused kernels), the LLaMA-7B layer's 32 heads of 128 on 512-token
 sequences, and peaked attention (Q scaled by 8 or 20)."""
 import numpy as np
 import pytest
@@ -53,7 +53,8 @@ def _run(q, batch, seq, heads, d, seed, qscale=1.0):
 
 @pytest.mark.parametrize("batch,seq,heads,d", [(2, 77, 3, 64), (1, 130, 2, 128), (3, 1, 2, 64), (2, 200, 1, 8),
                                                (1, 512, 4, 128), (1, 700, 2, 64), (1, 600, 1, 8), (2, 200, 3, 32),
-                                               (1, 1000, 1, 128), (2, 65, 1, 128), (1, 300, 3, 96), (2, 100, 2, 96)])
+                                               (1, 1000, 1, 128), (2, 65, 1, 128), (1, 300, 3, 96), (2, 100, 2, 96),
+                                               (2, 150, 2, 48), (1, 130, 1, 160)])
 def test_attention_matches_oracle(q, batch, seq, heads, d):
     note(f"[attention] batch={batch} seq={seq} heads={heads} d={d}")
     (Qb, Kb, Vb, dOb), (O, lse, dQ, dK, dV) = _run(q, batch, seq, heads, d, seed=seq + 7 * heads + d)
@@ -72,7 +73,7 @@ def test_attention_matches_oracle(q, batch, seq, heads, d):
 
 @pytest.mark.parametrize("batch,seq,heads,d,qscale", [(1, 300, 2, 128, 8.0), (2, 130, 2, 64, 20.0),
                                                       (1, 200, 1, 96, 8.0), (1, 150, 1, 32, 20.0),
-                                                      (1, 100, 2, 8, 20.0)])
+                                                      (1, 100, 2, 8, 20.0), (1, 90, 2, 48, 20.0)])
 def test_attention_peaked_matches_oracle(q, batch, seq, heads, d, qscale):
     """Peaked attention: Q scaled so the logits spread over tens of units and
     most rows put nearly all their weight on one or two keys.  The running
