@@ -6,8 +6,10 @@ library.  Bar: the linear calls' tolerance (relative Frobenius <= 5e-3, max
 <= 2e-2 of the largest value) on Y and dX; twice the Frobenius bar on the
 fourteen adapter gradients (see GRAD_FRO); in sharply peaked attention the
 larger of that and the oracle's own sensitivity (see the last test).
-q and k weights are drawn 10x larger than the rest so that the attention
-is sharply peaked rather than near-uniform."""
+In the first two cases the q and k weights are drawn 4x larger than the
+rest so that the attention is peaked rather than near-uniform; the head dim
+128 case draws them at the same scale, and its sharply peaked variant is
+the last test."""
 import numpy as np
 import pytest
 import torch
