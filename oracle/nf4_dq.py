@@ -39,7 +39,10 @@ repeated at the function that applies it):
     (section 'Why NF4 rather than any 4-bit type' of the reading note) uses
     the same blockwise rule with the OCP E2M1 value set divided by its
     largest magnitude 6 (see fp4_e2m1_codebook); everything else, double
-    quantization included, is unchanged.
+    quantization included, is unchanged;
+  * the Float4 (E3M0) storage type of the same table likewise, with the
+    values of a sign + 3-exponent-bit float with no mantissa bits divided by
+    their largest magnitude (see fp4_e3m0_codebook).
 """
 from __future__ import annotations
 
@@ -139,16 +142,51 @@ def fp4_e2m1_codebook() -> np.ndarray:
     return np.concatenate([levels, levels[-1:]]).astype(F32)
 
 
-CODEBOOKS = ("nf4", "fp4")
+def e3m0_decode(codes) -> np.ndarray:
+    """E3M0 4-bit float -> float32 (exact).
+
+    Format: 1 sign bit (bit 3), 3 exponent bits with bias 3, no mantissa
+    bits.  Reading (the pages name the format only): exponent field 0 is the
+    subnormal range, which with no fraction bits holds only zero; fields 1..7
+    are 2^(e - 3); no field is kept for infinity or NaN, as in the OCP
+    sub-byte floats.  Values: +-{0, 1/4, 1/2, 1, 2, 4, 8, 16}.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = c & 0x7
+    mag = np.where(e == 0, 0.0, np.exp2(e - 3.0))
+    return (sign * mag).astype(F32)
+
+
+def fp4_e3m0_codebook() -> np.ndarray:
+    """The Float4 (E3M0) level set as 16 float32 levels, ascending.
+
+    [reading note, 'Why NF4 rather than any 4-bit type': Float4 (E3M0) is the
+    other Float4 variant NF4 is compared with].  Built as fp4_e2m1_codebook
+    is: the 15 distinct values of the format (one zero level), divided by the
+    largest magnitude 16 so that the block absmax lands on +-1 (the division
+    is exact: the levels are 0 and +-2^-j, j = 0..6), code j the j-th level
+    in ascending order, and code 15 repeating the top level 1.0 (never
+    produced by the nearest-level rule).
+    """
+    vals = np.unique(e3m0_decode(np.arange(16, dtype=np.uint8)).astype(F64))  # 15 distinct, ascending
+    vals = np.where(vals == 0.0, 0.0, vals)                                    # the zero level is +0
+    levels = (vals.astype(F32) / F32(16.0)).astype(F32)
+    return np.concatenate([levels, levels[-1:]]).astype(F32)
+
+
+CODEBOOKS = ("nf4", "fp4", "fp4_e3m0")
 
 
 def codebook_levels(codebook: str = "nf4") -> np.ndarray:
-    """The 16 float32 levels of a storage type: 'nf4' (the default, NormalFloat)
-    or 'fp4' (Float4 E2M1)."""
+    """The 16 float32 levels of a storage type: 'nf4' (the default, NormalFloat),
+    'fp4' (Float4 E2M1) or 'fp4_e3m0' (Float4 E3M0)."""
     if codebook == "nf4":
         return nf4_codebook()
     if codebook == "fp4":
         return fp4_e2m1_codebook()
+    if codebook == "fp4_e3m0":
+        return fp4_e3m0_codebook()
     raise ValueError(f"unknown codebook {codebook!r}")
 
 

@@ -116,3 +116,46 @@ def test_fp4_nearest_level_brute_force_and_ties():
     below, above = np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1))
     lo = 10 if float(mid) <= 7.0 / 24.0 else 11
     assert nf4_dq.nearest_level(np.float32([below, mid, above]), q).tolist() == [10, lo, 11]
+
+
+# --------------------------------------------------------------------------
+# Float4 (E3M0): the other Float4 row of the same table.  Pins from what the
+# format's shape fixes (3 exponent bits and no mantissa bits: one value per
+# binade, so consecutive magnitudes differ by exactly 2; seven binades plus
+# zero), not from the decoder's arithmetic.
+# --------------------------------------------------------------------------
+def test_e3m0_levels_from_format_constants():
+    q = nf4_dq.fp4_e3m0_codebook()
+    assert q.dtype == np.float32 and q.shape == (16,)
+    pos = np.array(q[8:15], np.float64)
+    assert pos[-1] == 1.0 and np.all(pos[1:] / pos[:-1] == 2.0)   # 2^-6 .. 2^0
+    assert pos[0] == 2.0 ** -6
+    assert np.array_equal(q[:7], -q[8:15][::-1])                    # symmetric
+    assert q[7] == 0 and not np.signbit(q[7])
+    assert q[15] == q[14] == np.float32(1.0)
+    assert np.all(np.diff(np.array(q[:15], np.float64)) > 0)
+
+
+def test_e3m0_decoder_covers_all_sixteen_bit_patterns():
+    vals = nf4_dq.e3m0_decode(np.arange(16, dtype=np.uint8)).astype(np.float64)
+    assert sorted(set(np.abs(vals))) == [0.0] + [2.0 ** e for e in range(-2, 5)]
+    assert np.array_equal(vals[8:], -vals[:8])      # the sign bit is the top bit
+    assert vals[0] == 0 and np.all(vals[2:8] == 2 * vals[1:7])  # field 0 is zero; each exponent step doubles
+
+
+def test_e3m0_nearest_level_brute_force_and_ties():
+    q = nf4_dq.fp4_e3m0_codebook()
+    rng = np.random.default_rng(6)
+    # log-uniform magnitudes: the levels crowd towards zero
+    x = (np.sign(rng.uniform(-1, 1, 20000)) * 2.0 ** rng.uniform(-9, 0, 20000)).astype(np.float32)
+    got = nf4_dq.nearest_level(x, q)
+    d = np.abs(x.astype(np.float64)[:, None] - q.astype(np.float64)[None, :])
+    assert np.array_equal(got, np.argmin(d, axis=1))
+    assert got.max() <= 14
+    # every midpoint 3 * 2^-j is a float32, so exact ties occur; they go to
+    # the lower index: 3/128 to 1/64 (code 8), -3/128 to -1/32 (code 5),
+    # 3/4 to 1/2 (code 13), 1/128 to 0 (code 7), -1/128 to -1/64 (code 6)
+    ties = np.float32([3 / 128, -3 / 128, 0.75, 1 / 128, -1 / 128])
+    assert nf4_dq.nearest_level(ties, q).tolist() == [8, 5, 13, 7, 6]
+    above = np.nextafter(ties, np.float32(2))
+    assert nf4_dq.nearest_level(above, q).tolist() == [9, 6, 14, 8, 7]
