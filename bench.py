@@ -556,7 +556,8 @@ def traced(q, fn, reps):
 
 def storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops):
     """The same fwd+bwd step with the comparison storage types: Float4 (E2M1)
-    codes instead of NF4, and single-level float32 block constants (double
+    and Float4 (E3M0) codes instead of NF4, and single-level float32 block
+    constants (double
     quantization off, 4.5 bits) instead of the double-quantized ones.  Each
     variant's step is timed alternately with the NF4+DQ step (same inputs,
     same workspace), 3 rounds of 3 warm-up + 10 timed steps, minimum per
@@ -564,6 +565,7 @@ def storage_rows(q, I, wl, layers, dev, ev, ws, M, r, alpha, step_flops):
     import torch
     variants = {"nf4_dq": (q.QLORA_CODEBOOK_NF4, q.QLORA_SCALES_DQ),
                 "fp4_dq": (q.QLORA_CODEBOOK_FP4_E2M1, q.QLORA_SCALES_DQ),
+                "fp4e3m0_dq": (q.QLORA_CODEBOOK_FP4_E3M0, q.QLORA_SCALES_DQ),
                 "nf4_fp32_absmax": (q.QLORA_CODEBOOK_NF4, q.QLORA_SCALES_FP32),
                 "fp4_fp32_absmax": (q.QLORA_CODEBOOK_FP4_E2M1, q.QLORA_SCALES_FP32)}
     weights = {}

@@ -33,8 +33,9 @@ Thresholds thresholds_of(const uint32_t *bits) {
 }  // namespace
 
 const Thresholds &codebook_thresholds(int codebook) {
-  static const Thresholds nf4 = thresholds_of(kNF4Bits), fp4 = thresholds_of(kFP4Bits);
-  return codebook == kCodebookFP4 ? fp4 : nf4;
+  static const Thresholds nf4 = thresholds_of(kNF4Bits), fp4 = thresholds_of(kFP4Bits),
+                          e3m0 = thresholds_of(kE3M0Bits);
+  return codebook == kCodebookE3M0 ? e3m0 : codebook == kCodebookFP4 ? fp4 : nf4;
 }
 
 namespace {
@@ -98,10 +99,15 @@ int take_ex(const qlora_weight_ex *w, WeightIn *o) {
   return QLORA_OK;
 }
 
+bool known_codebook(int cb) {
+  return cb == QLORA_CODEBOOK_NF4 || cb == QLORA_CODEBOOK_FP4_E2M1 || cb == QLORA_CODEBOOK_FP4_E3M0;
+}
+
 int check_weight(const WeightIn &w) {
   if (int e = check_shape(w.n, w.k)) return e;
-  if (w.codebook != QLORA_CODEBOOK_NF4 && w.codebook != QLORA_CODEBOOK_FP4_E2M1)
-    return fail(QLORA_ERR_BAD_CODEBOOK, "codebook %d is neither NF4 (0) nor Float4 E2M1 (1)", (int)w.codebook);
+  if (!known_codebook(w.codebook))
+    return fail(QLORA_ERR_BAD_CODEBOOK, "codebook %d is none of NF4 (0), Float4 E2M1 (1), Float4 E3M0 (2)",
+                (int)w.codebook);
   if (w.scales != QLORA_SCALES_DQ && w.scales != QLORA_SCALES_FP32)
     return fail(QLORA_ERR_BAD_CODEBOOK, "scales %d is neither DQ (0) nor FP32 (1)", (int)w.scales);
   if (w.scales == QLORA_SCALES_DQ) {
@@ -530,16 +536,14 @@ void qlora_nf4_codebook(float out[16]) { qlora_codebook(QLORA_CODEBOOK_NF4, out)
 void qlora_nf4_thresholds(float out[15]) { qlora_thresholds(QLORA_CODEBOOK_NF4, out); }
 
 int qlora_codebook(int codebook, float out[16]) {
-  if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_FP4_E2M1)
-    return fail(QLORA_ERR_BAD_CODEBOOK, "unknown codebook %d", codebook);
+  if (!known_codebook(codebook)) return fail(QLORA_ERR_BAD_CODEBOOK, "unknown codebook %d", codebook);
   if (!out) return fail(QLORA_ERR_NULL_ARG, "out is NULL");
   for (int j = 0; j < 16; ++j) std::memcpy(&out[j], &codebook_bits(codebook)[j], 4);
   return QLORA_OK;
 }
 
 int qlora_thresholds(int codebook, float out[15]) {
-  if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_FP4_E2M1)
-    return fail(QLORA_ERR_BAD_CODEBOOK, "unknown codebook %d", codebook);
+  if (!known_codebook(codebook)) return fail(QLORA_ERR_BAD_CODEBOOK, "unknown codebook %d", codebook);
   if (!out) return fail(QLORA_ERR_NULL_ARG, "out is NULL");
   const Thresholds &t = codebook_thresholds(codebook);
   for (int j = 0; j < 15; ++j) out[j] = t.t[j];

@@ -265,13 +265,13 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   // so q[e >> 4] is wave-uniform and q[e & 15] one of two constants: no
   // per-lane loads of the codebook (they would wait behind the loads above).
   {
-    const bool fp4 = w.codebook == kCodebookFP4;
-    const float qhi = __uint_as_float(fp4 ? kFP4Bits[wave] : kNF4Bits[wave]);
+    const int cb = w.codebook;
+    const float qhi = __uint_as_float(codebook_level_bits(cb, wave));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int e = 16 * wave + 2 * i + (lane >> 5), c = lane & 31;
       const uint32_t hi_half = 0u - (uint32_t)(lane >> 5);  // all ones for lanes 32..63
-      const uint32_t q0 = fp4 ? kFP4Bits[2 * i] : kNF4Bits[2 * i], q1 = fp4 ? kFP4Bits[2 * i + 1] : kNF4Bits[2 * i + 1];
+      const uint32_t q0 = codebook_level_bits(cb, 2 * i), q1 = codebook_level_bits(cb, 2 * i + 1);
       const float qlo = __uint_as_float((q0 & ~hi_half) | (q1 & hi_half));
       s_tab[e * 32 + c] = make_float2(qlo, qhi);
     }

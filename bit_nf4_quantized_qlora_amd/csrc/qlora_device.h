@@ -42,9 +42,25 @@ constexpr uint32_t kFP4Bits[16] = {
     0xbdaaaaabu, 0x00000000u, 0x3daaaaabu, 0x3e2aaaabu, 0x3e800000u, 0x3eaaaaabu,
     0x3f000000u, 0x3f2aaaabu, 0x3f800000u, 0x3f800000u};
 
-// Storage types (the codebook field of a weight): 0 NF4, 1 Float4 (E2M1).
-constexpr int kCodebookNF4 = 0, kCodebookFP4 = 1;
-__host__ __device__ constexpr const uint32_t *codebook_bits(int cb) { return cb == kCodebookFP4 ? kFP4Bits : kNF4Bits; }
+// The Float4 (E3M0) storage type of the same comparison: a sign and three
+// exponent bits with no mantissa (field 0 is zero, no infinity or NaN), so
+// the 15 distinct values are 0 and +-2^-j, j = 0..6, once divided by the
+// largest magnitude; ascending, code 15 repeating 1.0 as for E2M1.
+constexpr uint32_t kE3M0Bits[16] = {
+    0xbf800000u, 0xbf000000u, 0xbe800000u, 0xbe000000u, 0xbd800000u, 0xbd000000u,
+    0xbc800000u, 0x00000000u, 0x3c800000u, 0x3d000000u, 0x3d800000u, 0x3e000000u,
+    0x3e800000u, 0x3f000000u, 0x3f800000u, 0x3f800000u};
+
+// Storage types (the codebook field of a weight): 0 NF4, 1 Float4 (E2M1),
+// 2 Float4 (E3M0).
+constexpr int kCodebookNF4 = 0, kCodebookFP4 = 1, kCodebookE3M0 = 2;
+__host__ __device__ constexpr const uint32_t *codebook_bits(int cb) {
+  return cb == kCodebookE3M0 ? kE3M0Bits : cb == kCodebookFP4 ? kFP4Bits : kNF4Bits;
+}
+// Level j of codebook cb (cb uniform across the wave: scalar selects).
+__host__ __device__ constexpr uint32_t codebook_level_bits(int cb, int j) {
+  return cb == kCodebookE3M0 ? kE3M0Bits[j] : cb == kCodebookFP4 ? kFP4Bits[j] : kNF4Bits[j];
+}
 
 // Nearest-level decision thresholds, passed by value as a kernel argument
 // (so they live in scalar registers): code = #{ j : x >= t[j] }.
@@ -108,7 +124,7 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
 __device__ __forceinline__ uint32_t nf4_level_bits(uint32_t c, int cb) {
   uint32_t v[16];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = cb == kCodebookFP4 ? kFP4Bits[j] : kNF4Bits[j];
+  for (int j = 0; j < 16; ++j) v[j] = codebook_level_bits(cb, j);
 #pragma unroll
   for (int b = 0, n = 8; b < 4; ++b, n >>= 1) {
     const uint32_t m = 0u - ((c >> b) & 1u);

@@ -18,11 +18,11 @@ struct Nf4View {
   const uint8_t *scale_code;
   const float *group_amax;
   const float *offset;
-  int codebook;         // kCodebookNF4 or kCodebookFP4
+  int codebook;         // kCodebookNF4, kCodebookFP4 or kCodebookE3M0
   const float *absmax;  // single-level block constants (s_b = absmax_b); NULL: double quantization
 };
 
-// Decision thresholds of a codebook (kCodebookNF4 / kCodebookFP4).
+// Decision thresholds of a codebook (kCodebookNF4 / kCodebookFP4 / kCodebookE3M0).
 const Thresholds &codebook_thresholds(int codebook);
 
 // quantize.hip

@@ -23,8 +23,10 @@ namespace {
 // [(i - 64)/64, (i - 63)/64) (x = 1 alone in bucket 128); 64 x is exact, so
 // the bucket is too.  Entry i holds the count of thresholds at or below the
 // bucket's lower edge and the one threshold strictly inside it (+inf if
-// none), so code = count + (x >= inside).  Both codebooks' thresholds are
-// more than 1/64 apart, so no bucket holds two.
+// none), so code = count + (x >= inside).  No bucket of any of the three
+// codebooks holds two thresholds (NF4's and E2M1's are more than 1/64
+// apart; E3M0's sit just above +-1/128, +-3/128 and +-3/64 .. +-3/4, one to
+// a bucket).
 struct CodeEntry {
   float inside;
   uint32_t count;
@@ -56,7 +58,7 @@ __device__ __forceinline__ uint32_t code_of(float x, const CodeEntry *tab) {
 // RN(q0 + r y) is the correctly rounded quotient (Markstein's correction
 // step for round-to-nearest); quotients that would be subnormal may differ
 // by an ulp there, which no code decision sees (every threshold is more than
-// 0.03 from zero).  Other m: the IEEE division.
+// 2^-8 from zero).  Other m: the IEEE division.
 __device__ __forceinline__ float quotient(float w, float m, float y, bool fast) {
   if (fast) {
     const float q0 = __fmul_rn(w, y);

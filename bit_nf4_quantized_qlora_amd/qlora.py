@@ -44,8 +44,9 @@ QLORA_ERR_BAD_ALPHA = -7
 QLORA_ERR_BAD_CODEBOOK = -8
 
 QLORA_CODEBOOK_NF4 = 0        # NormalFloat4, the method's storage type
-QLORA_CODEBOOK_FP4_E2M1 = 1   # Float4 (E2M1), the comparison type
-CODEBOOKS = {"nf4": QLORA_CODEBOOK_NF4, "fp4": QLORA_CODEBOOK_FP4_E2M1}
+QLORA_CODEBOOK_FP4_E2M1 = 1   # Float4 (E2M1), a comparison type
+QLORA_CODEBOOK_FP4_E3M0 = 2   # Float4 (E3M0), the other comparison type
+CODEBOOKS = {"nf4": QLORA_CODEBOOK_NF4, "fp4": QLORA_CODEBOOK_FP4_E2M1, "fp4_e3m0": QLORA_CODEBOOK_FP4_E3M0}
 QLORA_SCALES_DQ = 0           # double-quantized block constants (the method's)
 QLORA_SCALES_FP32 = 1         # one float32 absmax per block (double quantization off)
 

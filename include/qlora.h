@@ -61,12 +61,17 @@ enum {
  * 4-bit float the reading note's data-type comparison ranks below it
  * ("Why NF4 rather than any 4-bit type"): the 15 distinct OCP E2M1 values
  * +-{0, 0.5, 1, 1.5, 2, 3, 4, 6} divided by 6, ascending, code 15 repeating
- * 1.0 (never produced).  Everything else -- blocks, the nearest-level rule,
- * double quantization, dequantization -- is the same for both.
+ * 1.0 (never produced).  Float4 (E3M0), the table's other 4-bit float: a
+ * sign and 3 exponent bits with no mantissa (field 0 is zero, no infinity
+ * or NaN), so its 15 distinct values divided by the largest are 0 and
+ * +-2^-j, j = 0..6; ascending, code 15 repeating 1.0 (never produced).
+ * Everything else -- blocks, the nearest-level rule, double quantization,
+ * dequantization -- is the same for all three.
  */
 enum {
   QLORA_CODEBOOK_NF4 = 0,
-  QLORA_CODEBOOK_FP4_E2M1 = 1
+  QLORA_CODEBOOK_FP4_E2M1 = 1,
+  QLORA_CODEBOOK_FP4_E3M0 = 2
 };
 
 /*
@@ -113,7 +118,7 @@ typedef struct qlora_nf4_weight {
 typedef struct qlora_weight_ex {
   size_t size;            /* sizeof(qlora_weight_ex)                                   */
   qlora_nf4_weight base;  /* shape, codes and (QLORA_SCALES_DQ) the DQ constants       */
-  int32_t codebook;       /* QLORA_CODEBOOK_NF4 or QLORA_CODEBOOK_FP4_E2M1             */
+  int32_t codebook;       /* QLORA_CODEBOOK_NF4, _FP4_E2M1 or _FP4_E3M0                */
   int32_t scales;         /* QLORA_SCALES_DQ or QLORA_SCALES_FP32                      */
   float *absmax;          /* [nb] block absmax, QLORA_SCALES_FP32 only                 */
 } qlora_weight_ex;

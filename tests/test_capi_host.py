@@ -71,13 +71,13 @@ def test_library_codebook_equals_oracle(q):
         lib = np.array(q.qlora_codebook(cb), np.float32)
         assert np.array_equal(lib.view(np.uint32), nf4_dq.codebook_levels(name).view(np.uint32)), name
     assert q.qlora_thresholds(q.QLORA_CODEBOOK_NF4) == q.qlora_nf4_thresholds()
-    for bad in (-1, 2, 7):
+    for bad in (-1, 3, 7):
         with pytest.raises(q.QloraError) as e:
             q.qlora_codebook(bad)
         assert e.value.status == q.QLORA_ERR_BAD_CODEBOOK
 
 
-@pytest.mark.parametrize("name", ["nf4", "fp4"])
+@pytest.mark.parametrize("name", ["nf4", "fp4", "fp4_e3m0"])
 def test_library_thresholds_are_the_exact_midpoint_successors(q, name):
     from oracle import nf4_dq
     levels = nf4_dq.codebook_levels(name)
@@ -95,14 +95,16 @@ def test_library_thresholds_are_the_exact_midpoint_successors(q, name):
     assert np.array_equal(via_t, nf4_dq.nearest_level(xs, levels))
 
 
-@pytest.mark.parametrize("name", ["nf4", "fp4"])
+@pytest.mark.parametrize("name", ["nf4", "fp4", "fp4_e3m0"])
 def test_thresholds_fit_the_quantizer_bucket_table(q, name):
     """The quantizer finds a code from a table of 64ths of [-1, 1]: bucket
     floor(64 x) + 64 holds the count of thresholds at or below its lower edge
-    and at most one threshold inside.  That needs the thresholds more than
-    1/64 apart and, past -1, no threshold below -1 (x >= -1)."""
+    and at most one threshold strictly inside.  That needs no bucket to hold
+    two (thresholds more than 1/64 apart would do; E3M0's -3/128 and -1/128
+    successors are a hair closer, yet fall in buckets -2 and -1) and, past
+    -1, no threshold below -1 (x >= -1)."""
     t = np.array(q.qlora_thresholds(q.CODEBOOKS[name]), np.float64)
-    assert np.all(np.diff(t) > 1.0 / 64.0)
+    assert np.all(np.diff(t) > 0)
     assert t[0] > -1.0
     for i in range(129):
         lo, hi = (i - 64) / 64.0, (i - 63) / 64.0

@@ -44,7 +44,7 @@ def test_tiny_workload(q):
     _full_check(q, I.weight(w, 0), "tiny")
 
 
-@pytest.mark.parametrize("codebook", ["nf4", "fp4"])
+@pytest.mark.parametrize("codebook", ["nf4", "fp4", "fp4_e3m0"])
 def test_decision_thresholds_and_special_values(q, codebook):
     """Blocks whose absmax is exactly 1 carry the 15 thresholds, their float32
     neighbours, every level, signed zeros and subnormals; other blocks scale
@@ -71,7 +71,7 @@ def test_decision_thresholds_and_special_values(q, codebook):
     _full_check(q, W, "thresholds", codebook)
 
 
-@pytest.mark.parametrize("codebook", ["nf4", "fp4"])
+@pytest.mark.parametrize("codebook", ["nf4", "fp4", "fp4_e3m0"])
 @pytest.mark.parametrize("shape,seed", [((5, 3840), 34), ((300, 640), 35), ((1024, 4096), 36)])
 def test_single_level_encoding(q, shape, seed, codebook):
     """Single-level constants (one float32 absmax per block): packed bytes and
@@ -90,10 +90,11 @@ def test_single_level_encoding(q, shape, seed, codebook):
     assert bad.size == 0, f"single-level dequant: {bad.size} differ, first {bad[:5]}"
 
 
+@pytest.mark.parametrize("codebook", ["fp4", "fp4_e3m0"])
 @pytest.mark.parametrize("shape,seed", [((5, 3840), 31), ((300, 640), 32), ((1024, 4096), 33)])
-def test_fp4_encoding(q, shape, seed):
-    """Float4 (E2M1) storage: the same bit-exact bar on ragged and full groups."""
-    _full_check(q, I.custom_weight(*shape, seed=seed), f"fp4{shape}", "fp4")
+def test_fp4_encoding(q, shape, seed, codebook):
+    """Float4 (E2M1, E3M0) storage: the same bit-exact bar on ragged and full groups."""
+    _full_check(q, I.custom_weight(*shape, seed=seed), f"{codebook}{shape}", codebook)
 
 
 @pytest.mark.parametrize("shape,seed", [((1, 64), 1), ((5, 3840), 2), ((7, 64 * 37), 3), ((64, 4096), 4),

@@ -127,25 +127,27 @@ def test_small_m_shapes(q, n, k, m, r, alpha, seed):
     _run_full(q, W, X, A, B, dY, r, alpha, f"small-M n{n} k{k} m{m} r{r}")
 
 
+@pytest.mark.parametrize("codebook", ["fp4", "fp4_e3m0"])
 @pytest.mark.parametrize("n,k,m,r,alpha,seed", [
     (640, 512, 300, 64, 16.0, 41),   # tile kernels, backward tile (n % 64 == 0), two m tiles
     (200, 192, 37, 5, -3.5, 42),     # ragged everything, fallback backward
     (1000, 4096, 3, 16, 16.0, 43),   # small-M GEMV forward
 ])
-def test_fp4_linear(q, n, k, m, r, alpha, seed):
-    """Float4 (E2M1) weights through every forward / backward path."""
+def test_fp4_linear(q, n, k, m, r, alpha, seed, codebook):
+    """Float4 (E2M1, E3M0) weights through every forward / backward path."""
     W = I.custom_weight(n, k, seed)
     X = I.custom_bf16((m, k), seed, 1)
     dY = I.custom_bf16((m, n), seed, 2)
     A = I.custom_bf16((r, k), seed, 3, bound=0.05)
     B = I.custom_bf16((n, r), seed, 4, bound=0.05)
-    _run_full(q, W, X, A, B, dY, r, alpha, f"fp4 n{n} k{k} m{m} r{r}", codebook="fp4")
+    _run_full(q, W, X, A, B, dY, r, alpha, f"{codebook} n{n} k{k} m{m} r{r}", codebook=codebook)
 
 
 @pytest.mark.parametrize("n,k,m,r,alpha,seed,codebook", [
     (640, 512, 300, 64, 16.0, 51, "nf4"),   # tile kernels both ways
     (200, 192, 37, 5, -3.5, 52, "fp4"),     # ragged everything, fallback backward
     (1000, 4096, 3, 16, 16.0, 53, "nf4"),   # M <= 16: tile kernels (the GEMV serves DQ weights)
+    (640, 512, 300, 64, 16.0, 54, "fp4_e3m0"),
 ])
 def test_single_level_linear(q, n, k, m, r, alpha, seed, codebook):
     """Single-level float32 block constants through forward and backward."""

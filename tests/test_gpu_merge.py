@@ -34,6 +34,7 @@ def _oracle_what(W, codebook, scales):
     (5, 3840, 1, -2.0, 64, ("nf4", "dq"), None),                   # rank 1, merged bf16 only
     (67, 512, 16, 16.0, 65, ("nf4", "dq"), ("nf4", "dq")),         # rows not a multiple of a thread's 4, B read 8 at a time
     (66, 1024, 12, 24.0, 66, ("fp4", "dq"), ("nf4", "dq")),        # the same with a rank not a multiple of 8
+    (128, 768, 32, 16.0, 67, ("fp4_e3m0", "dq"), ("fp4_e3m0", "fp32")),  # Float4 (E3M0) in and out
 ])
 def test_merge_adapters(q, n, k, r, alpha, seed, src, dst):
     note(f"[merge] n={n} k={k} r={r} src={src} dst={dst}")

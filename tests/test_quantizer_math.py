@@ -68,7 +68,7 @@ def test_corrected_quotient_is_the_rounded_quotient(seed):
     _check_quotients(w, m)
 
 
-@pytest.mark.parametrize("codebook", ["nf4", "fp4"])
+@pytest.mark.parametrize("codebook", ["nf4", "fp4", "fp4_e3m0"])
 def test_corrected_quotient_next_to_every_midpoint(codebook):
     rng = np.random.default_rng(7)
     lv = nf4_dq.codebook_levels(codebook).astype(F64)
@@ -84,7 +84,7 @@ def test_corrected_quotient_next_to_every_midpoint(codebook):
             _check_quotients(w, m)
 
 
-@pytest.mark.parametrize("codebook", ["nf4", "fp4"])
+@pytest.mark.parametrize("codebook", ["nf4", "fp4", "fp4_e3m0"])
 def test_bucket_lookup_is_the_threshold_count(codebook):
     from bit_nf4_quantized_qlora_amd import qlora as q
     t = np.array(q.qlora_thresholds(q.CODEBOOKS[codebook]), F32)
