@@ -16,7 +16,8 @@ Also reported, each against its roofline:
   rows.small_m      65B up_proj (8192->22016) forward at M = 1, 4, 16, GB/s on the
                     packed-weight bytes, rotating 6 weight copies (558 MB) so the
                     256 MB last-level cache cannot hold them: the whole call, and
-                    the streaming kernel alone
+                    the streaming kernel alone; M1_single_level: M = 1 with
+                    single-level float32 block constants (4.5 bits)
   kernels           per-kernel average duration from the library's event timer
   roofline          the dominant kernel (largest summed time in a step)
   cpu_baseline      the CPU oracle (NumPy fp64) on a bounded sample of the step
@@ -939,25 +940,40 @@ def attainable_peaks(torch, dev, ev):
 
 
 def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
-    """65B up_proj forward at M = 1, 4, 16 on rotating weight copies."""
+    """65B up_proj forward at M = 1, 4, 16 on rotating weight copies; and at
+    M = 1 with single-level float32 block constants (4.5 bits) for the
+    bandwidth double quantization saves on the same kernel."""
     wl = I.WORKLOADS["up_65b"]
     L = wl.layers[0]
     W = torch.from_numpy(I.weight(wl, 0)).to(dev)
     qws = torch.empty(q.qlora_quantize_workspace_bytes(L.n, L.k), dtype=torch.uint8, device=dev)
-    ws_list = []
-    for _ in range(copies):
-        w = q.NF4Weight.empty(L.n, L.k, dev)
-        q.qlora_quantize_nf4_dq(W, w, qws)
-        ws_list.append(w)
-    del W, qws
+
+    def encode(scales):
+        lst = []
+        for _ in range(copies):
+            w = q.NF4Weight.empty(L.n, L.k, dev, scales=scales)
+            q.qlora_quantize_nf4_dq(W, w, qws)
+            lst.append(w)
+        return lst
+
+    ws_list = encode(q.QLORA_SCALES_DQ)
     torch.cuda.synchronize()
-    torch.cuda.empty_cache()
     pb, sb, ng = q.qlora_nf4_sizes(L.n, L.k)
     packed_bytes = pb + sb + 4 * ng
     A, B = I.adapters(wl, 0)
     Ad, Bd = dev16(A), dev16(B)
     out = {"workload": f"up_proj {L.k}->{L.n}", "packed_weight_bytes": packed_bytes, "copies": copies}
-    for m in wl.ms:
+    for m in list(wl.ms) + ["1_single_level"]:
+        if m == "1_single_level":  # the DQ copies make room for the 4.5-bit ones
+            del ws_list
+            torch.cuda.empty_cache()
+            ws_list = encode(q.QLORA_SCALES_FP32)
+            torch.cuda.synchronize()
+            packed_bytes = pb + 4 * sb
+            m = 1
+            key = "M1_single_level"
+        else:
+            key = f"M{m}"
         X = dev16(I.activation(wl, 0, m))
         Y = torch.empty(m, L.n, dtype=torch.bfloat16, device=dev)
         H = torch.empty(m, wl.r, dtype=torch.float32, device=dev)
@@ -974,12 +990,14 @@ def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
         us = 1e3 * a.elapsed_time(b) / reps
         gbps = packed_bytes / (us * 1e-6) / 1e9
         row = {"us": round(us, 2), "gbps_packed": round(gbps, 1), "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4)}
+        if key != f"M{m}":
+            row["weight_bytes"] = packed_bytes
         # the streaming kernel on its own (library event timer, separate pass)
         it = iter(range(10 ** 9))
         prof = traced(q, lambda: q.qlora_linear_fwd(ws_list[next(it) % copies], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws),
                       reps)
         gemv_tc = load_traffic("gemv").get("k_gemv_nf4")
-        if gemv_tc:
+        if gemv_tc and key == f"M{m}":
             row["kernel_traffic_bytes"] = {"fetch": gemv_tc["fetch_bytes_per_launch"],
                                            "write": gemv_tc["write_bytes_per_launch"],
                                            "fetch_vs_packed": round(gemv_tc["fetch_bytes_per_launch"] / packed_bytes, 4)}
@@ -990,7 +1008,8 @@ def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
             row["kernel_us"] = round(kus, 2)
             row["kernel_gbps_packed"] = round(packed_bytes / (kus * 1e-6) / 1e9, 1)
             row["kernel_frac_hbm_peak"] = round(packed_bytes / (kus * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
-        out[f"M{m}"] = row
+        out[key] = row
+    del W, qws
     return out
 
 

@@ -54,9 +54,8 @@ size_t fwd_workspace_bytes(int64_t M, int64_t n, int64_t k, int r) {
 LinearPlan plan_linear(int64_t M, int64_t n, int64_t k, int r, bool single_level) {
   LinearPlan p;
   if (M == 0) return p;
-  // the GEMV decodes double-quantized constants only; single-level weights
-  // take the tile kernels at every M
-  if (!single_level && small_m_supported(M, n, k, r)) {
+  (void)single_level;  // the GEMV takes either kind of block constants
+  if (small_m_supported(M, n, k, r)) {
     p.fwd_path = QLORA_PATH_GEMV;
   } else {
     p.fwd_path = QLORA_PATH_TILE;

@@ -37,6 +37,10 @@
 // staged in LDS for the whole range, one 272-byte row per (pair, m), so X
 // and the weights meet in the same order.
 //
+// Single-level weights (a float32 absmax per block, no double quantization)
+// take the same kernel with s_b = absmax_b read four blocks per 16-byte load
+// in place of the scale-code word, E4M3 table and group constants.
+//
 // H: workgroup t < nh takes rank tile t % (RP/16) and K slice t / (RP/16)
 // (512 wide, 32 per wave); its operands are loaded before anything else so
 // their latency hides under the table fill, one MFMA per wave, and the 16
@@ -128,6 +132,10 @@ SmallWs small_ws_layout(int64_t M, int64_t n, int64_t k, int RP) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// kSingle: single-level block constants (s_b = absmax_b, a float32 per
+// block) instead of the double-quantized E4M3 codes, group constants and
+// offset; four blocks' constants (two pairs) per 16-byte load.
+template <bool kSingle>
 __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t *__restrict__ X, int M,
                                                       const uint16_t *__restrict__ A, int r, int RP,
                                                       float *__restrict__ hpart, float *__restrict__ part,
@@ -190,15 +198,18 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   // group constants of the touched row groups: s_ga[t] = group_amax[gfirst*nkb + t]
   // (past the last group: zero, from the buffer range)
   const int64_t gi0 = (int64_t)gfirst * nkb;
-  const int nga = seg * nkb;
-  const __amdgpu_buffer_rsrc_t grs = rsrc(w.group_amax + gi0, (w.ng - gi0) * 4);
+  const int nga = kSingle ? 0 : seg * nkb;
   float gv[kGaPer];
 #pragma unroll
-  for (int u = 0; u < kGaPer; ++u) {
-    const int t = tid + 1024 * u;
-    gv[u] = 0.f;
-    if (64 * wave + 1024 * u < nga)
-      gv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, t < nga ? (uint32_t)t * 4 : kOut, 0, 0));
+  for (int u = 0; u < kGaPer; ++u) gv[u] = 0.f;
+  if constexpr (!kSingle) {
+    const __amdgpu_buffer_rsrc_t grs = rsrc(w.group_amax + gi0, (w.ng - gi0) * 4);
+#pragma unroll
+    for (int u = 0; u < kGaPer; ++u) {
+      const int t = tid + 1024 * u;
+      if (64 * wave + 1024 * u < nga)
+        gv[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(grs, t < nga ? (uint32_t)t * 4 : kOut, 0, 0));
+    }
   }
 
   // H slice operands: X rows li < M and A rows 16 jt + li < r at
@@ -214,7 +225,8 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
     hx = __builtin_amdgcn_raw_buffer_load_b128(xrs, kin && li < M ? (uint32_t)((li * K + kh) * 2) : kOut, 0, 0);
     ha = __builtin_amdgcn_raw_buffer_load_b128(ar, kin && j < r ? (uint32_t)((j * K + kh) * 2) : kOut, 0, 0);
   }
-  const float offset = *w.offset;
+  float offset = 0.f;
+  if constexpr (!kSingle) offset = *w.offset;
 
   // Per-lane streams (32-bit offsets): the codes of a pair of blocks of row
   // n, a word of four scale codes per two pairs, and the blocks' group
@@ -222,7 +234,7 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   // used; loads past the workgroup's last block take an out-of-range offset
   // (no memory traffic).
   const __amdgpu_buffer_rsrc_t crs = rsrc(w.packed, N * kb2);
-  const __amdgpu_buffer_rsrc_t srs = rsrc(w.scale_code, w.nb);
+  const __amdgpu_buffer_rsrc_t srs = kSingle ? rsrc(w.absmax, w.nb * 4) : rsrc(w.scale_code, w.nb);
   const int nrow = 16 * wave + li;  // row within the group
   const int nkb32 = nkb;
   const int hb = g >> 1;  // which block of a pair this lane's codes come from
@@ -245,10 +257,15 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
   // Scale codes four blocks (two pairs) per load (ranges and row groups
   // start on multiples of 4 blocks, and nkb % 4 == 0): word w of the row's
   // codes, all four lanes of a row reading the same word; two in flight.
+  // (kSingle: the four blocks' float32 constants, 16 bytes, in scw4.)
   uint32_t scw[2];
+  u32x4_t scw4[2];
   int skb = lkb;
   auto sload = [&](int slot, bool real) {
-    scw[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, real ? lbi : kOut, 0, 0);
+    if constexpr (kSingle)
+      scw4[slot] = __builtin_amdgcn_raw_buffer_load_b128(srs, real ? lbi * 4u : kOut, 0, 0);
+    else
+      scw[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, real ? lbi : kOut, 0, 0);
     lbi += 4;
     if ((skb += 4) == nkb32) {
       skb = 0;
@@ -276,7 +293,7 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
       s_tab[e * 32 + c] = make_float2(qlo, qhi);
     }
   }
-  if (tid < 256) s_dec[tid] = e4m3_decode((uint32_t)tid);
+  if (!kSingle && tid < 256) s_dec[tid] = e4m3_decode((uint32_t)tid);
   if (tid < 8) *reinterpret_cast<u32x4_t *>(lds + kZeroOff + 16 * tid) = u32x4_t{0u, 0u, 0u, 0u};
   // this workgroup's partial slot in its first row group: block b lies in
   // workgroup ((b/4 + 1) G - 1) / (T/4), so the group's first covering
@@ -330,10 +347,16 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
 #pragma unroll
     for (int q = 0; q < kGvP; ++q) {
       const int ip = p0 + q;
-      const uint32_t sc = (scw[(q >> 1) & 1] >> ((q & 1) ? ssh1 : ssh0)) & 0xFFu;
-      const float sd = s_dec[sc];
+      float sd = 0.f, ga = 0.f, s1 = 0.f;
+      if constexpr (kSingle) {  // this lane's block: 2(ip & 1) + hb of the four
+        const u32x4_t v = scw4[(q >> 1) & 1];
+        s1 = __uint_as_float(hb ? v[2 * (q & 1) + 1] : v[2 * (q & 1)]);
+      } else {
+        const uint32_t sc = (scw[(q >> 1) & 1] >> ((q & 1) ? ssh1 : ssh0)) & 0xFFu;
+        sd = s_dec[sc];
+      }
       if (q & 1) sload((q >> 1) & 1, 2 * ip + 6 < nb);  // blocks 2ip+6 .. 2ip+9
-      const float ga = *reinterpret_cast<const float *>(lds + ga_base + ((cbi >> 8) << 2));
+      if constexpr (!kSingle) ga = *reinterpret_cast<const float *>(lds + ga_base + ((cbi >> 8) << 2));
       u32x4_t xa[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) xa[t] = *reinterpret_cast<const u32x4_t *>(lds + xo + xoff + 16 * t);
@@ -348,7 +371,7 @@ __global__ __launch_bounds__(1024, 1) void k_gemv_nf4(Nf4View w, const uint16_t 
               tab + __builtin_amdgcn_perm(cw[t], lane_off, 0x0C0C0000u | ((4u + e) << 8)));
       load(q, 2 * ip + 2 * kGvP < nb);
       // the block scale, bit for bit the dequantization's block_scale
-      const float s = __fadd_rn(__fmul_rn(sd, ga), offset);
+      const float s = kSingle ? s1 : __fadd_rn(__fmul_rn(sd, ga), offset);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         u32x4_t wb;
@@ -516,8 +539,12 @@ hipError_t launch_fwd_small(const Nf4View &w, const uint16_t *X, int64_t M, cons
   float *hpart = reinterpret_cast<float *>(base + l.h_off);
   float *part = reinterpret_cast<float *>(base + l.part_off);
   const int T4 = (int)(p.T / 4);
-  QLORA_LAUNCH("k_gemv_nf4", k_gemv_nf4, dim3((unsigned)p.G), dim3(1024), 0, st, w, X, (int)M, A, r, RP, hpart, part,
-               T4, p.G, T4 / p.G, T4 % p.G, p.seg, p.maxcov, p.nh, p.nht, p.xoff);
+  if (w.absmax)
+    QLORA_LAUNCH("k_gemv_nf4", k_gemv_nf4<true>, dim3((unsigned)p.G), dim3(1024), 0, st, w, X, (int)M, A, r, RP,
+                 hpart, part, T4, p.G, T4 / p.G, T4 % p.G, p.seg, p.maxcov, p.nh, p.nht, p.xoff);
+  else
+    QLORA_LAUNCH("k_gemv_nf4", k_gemv_nf4<false>, dim3((unsigned)p.G), dim3(1024), 0, st, w, X, (int)M, A, r, RP,
+                 hpart, part, T4, p.G, T4 / p.G, T4 % p.G, p.seg, p.maxcov, p.nh, p.nht, p.xoff);
   // the group's B rows in LDS, sized by the rank (more workgroups per CU at small r)
   const size_t bshm = (size_t)kGvRows * r * sizeof(uint16_t);
   // rows of Y per workgroup: up to 4 (one H-summing thread per (row, rank)),

@@ -233,8 +233,8 @@ int qlora_linear_fwd_noalloc(const qlora_nf4_weight *w, const uint16_t *X, int64
  *                       contraction is cut into that many equal ranges whose
  *                       float32 partial tiles are then summed in split order
  *                       (shapes with too few tiles to fill the GPU);
- *   QLORA_PATH_GEMV     forward only, 1 <= M <= 16 with double-quantized
- *                       constants: one bandwidth-bound pass over the weight;
+ *   QLORA_PATH_GEMV     forward only, 1 <= M <= 16 (either kind of block
+ *                       constants): one bandwidth-bound pass over the weight;
  *   QLORA_PATH_GENERAL  input gradient only: the general kernel (n % 64 != 0,
  *                       or n * 512 at or above 2^31);
  *   QLORA_PATH_NONE     M == 0.

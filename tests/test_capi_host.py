@@ -283,7 +283,7 @@ def test_linear_plan_paths(q):
     assert q.qlora_linear_plan(512, 22016, 8192, 64)["dx_splits"] > 1
     for m in (1, 4, 16):                                      # small M: the GEMV forward
         assert q.qlora_linear_plan(m, 22016, 8192, 16)["fwd_path"] == V
-        assert q.qlora_linear_plan(m, 22016, 8192, 16, q.QLORA_SCALES_FP32)["fwd_path"] == T
+        assert q.qlora_linear_plan(m, 22016, 8192, 16, q.QLORA_SCALES_FP32)["fwd_path"] == V
     assert q.qlora_linear_plan(37, 200, 192, 5)["dx_path"] == G          # n % 64 != 0
     assert q.qlora_linear_plan(64, 640, 512, 64)["fwd_splits"] == 1      # 8 steps: nothing to split
     # dY tiles of 256 rows x 512 n bytes must stay below 2^31: n = 2^22 takes the general kernel

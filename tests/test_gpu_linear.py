@@ -146,11 +146,16 @@ def test_fp4_linear(q, n, k, m, r, alpha, seed, codebook):
 @pytest.mark.parametrize("n,k,m,r,alpha,seed,codebook", [
     (640, 512, 300, 64, 16.0, 51, "nf4"),   # tile kernels both ways
     (200, 192, 37, 5, -3.5, 52, "fp4"),     # ragged everything, fallback backward
-    (1000, 4096, 3, 16, 16.0, 53, "nf4"),   # M <= 16: tile kernels (the GEMV serves DQ weights)
+    (1000, 4096, 3, 16, 16.0, 53, "nf4"),   # M <= 16: the GEMV with float32 block constants
     (640, 512, 300, 64, 16.0, 54, "fp4_e3m0"),
+    (300, 1024, 16, 8, 2.0, 55, "fp4"),     # the GEMV at M = 16, rows past a row group, Float4
+    (4352, 4096, 1, 64, 16.0, 56, "nf4"),   # the GEMV at M = 1: 272 four-block units on 256 workgroups, so ranges straddle row groups
 ])
 def test_single_level_linear(q, n, k, m, r, alpha, seed, codebook):
-    """Single-level float32 block constants through forward and backward."""
+    """Single-level float32 block constants through forward and backward
+    (M <= 16 with k % 256 == 0: the small-M GEMV forward)."""
+    if m <= 16 and k % 256 == 0:
+        assert q.qlora_linear_plan(m, n, k, r, q.QLORA_SCALES_FP32)["fwd_path"] == q.QLORA_PATH_GEMV
     W = I.custom_weight(n, k, seed)
     X = I.custom_bf16((m, k), seed, 1)
     dY = I.custom_bf16((m, n), seed, 2)
