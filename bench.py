@@ -103,7 +103,8 @@ def layer_flops(M, N, K, r):
 # rocprofv3 kernel names -> the names the library's event timer uses
 KERNEL_ALIASES = {"k_nf4_tile<false>": "k_fwd_nf4", "k_nf4_tile<true>": "k_bwd_dx_nf4",
                   "k_nf4_tile<false, false>": "k_fwd_nf4", "k_nf4_tile<true, false>": "k_bwd_dx_nf4",
-                  "k_nf4_tile<false, true>": "k_fwd_bf16w"}
+                  "k_nf4_tile<false, true>": "k_fwd_bf16w",
+                  "k_gemv_nf4<false>": "k_gemv_nf4", "k_gemv_nf4<true>": "k_gemv_nf4_single"}
 
 
 def short_kernel_name(name: str) -> str:
@@ -996,8 +997,8 @@ def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
         it = iter(range(10 ** 9))
         prof = traced(q, lambda: q.qlora_linear_fwd(ws_list[next(it) % copies], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws),
                       reps)
-        gemv_tc = load_traffic("gemv").get("k_gemv_nf4")
-        if gemv_tc and key == f"M{m}":
+        gemv_tc = load_traffic("gemv").get("k_gemv_nf4" if key == f"M{m}" else "k_gemv_nf4_single")
+        if gemv_tc:
             row["kernel_traffic_bytes"] = {"fetch": gemv_tc["fetch_bytes_per_launch"],
                                            "write": gemv_tc["write_bytes_per_launch"],
                                            "fetch_vs_packed": round(gemv_tc["fetch_bytes_per_launch"] / packed_bytes, 4)}
