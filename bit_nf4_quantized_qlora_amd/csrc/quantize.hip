@@ -4,15 +4,17 @@
 // blockwise absmax and nearest NF4 code; Level 2: mean-subtracted block
 // constants coded to 8-bit floats with one fp32 constant per 256).
 //
-// Three launches, all HBM-streaming:
+// Two or three launches:
 //   k_quantize_blocks  one workgroup per group of 256 blocks (64 KiB of W):
 //                      absmax, codes, packed nibbles, and the group's fp64
-//                      in-order absmax sum;
+//                      in-order absmax sum (HBM-streaming);
 //   k_mean             one workgroup: group sums staged in LDS, each lane of
 //                      a wave folds one run of 256 of them in order, then
 //                      one lane the run sums -> offset;
 //   k_encode_scales    one wave per group: dev = absmax - offset, group amax,
-//                      E4M3 codes.
+//                      E4M3 codes;
+//   k_mean_encode      the last two in one launch for tensors of at most
+//                      16384 groups (each workgroup folds the mean itself).
 #include "qlora_internal.h"
 
 namespace qlora {
@@ -175,11 +177,10 @@ constexpr int kMeanRuns = 64;               // runs per pass (one wave)
 constexpr int kMeanLd = kMeanRun + 1;       // LDS stride of a staged run (doubles)
 constexpr int kMeanLanes = 1024;
 constexpr int kMeanPer = kMeanRuns * kMeanRun / kMeanLanes;  // staged sums per lane and pass
-__global__ __launch_bounds__(kMeanLanes) void k_mean(const double *__restrict__ group_sum, int64_t ng, int64_t nb,
-                                                     float *__restrict__ offset) {
+// The fold by the workgroup's kMeanLanes lanes; every lane gets the total.
+__device__ __forceinline__ double mean_fold(const double *__restrict__ group_sum, int64_t ng, double *s_sum,
+                                            double *s_run) {
   constexpr int B = 16;  // LDS reads ahead of the adds
-  __shared__ double s_sum[kMeanRuns * kMeanLd];
-  __shared__ double s_run[kMeanRuns];
   const int64_t nruns = (ng + kMeanRun - 1) / kMeanRun;
   double total = 0.0;  // lane 0's fold of the run sums
   for (int64_t r0 = 0; r0 < nruns; r0 += kMeanRuns) {
@@ -220,18 +221,23 @@ __global__ __launch_bounds__(kMeanLanes) void k_mean(const double *__restrict__ 
     }
     __syncthreads();  // the next pass overwrites s_sum and s_run
   }
+  if (threadIdx.x == 0) s_run[0] = total;
+  __syncthreads();
+  return s_run[0];
+}
+
+__global__ __launch_bounds__(kMeanLanes) void k_mean(const double *__restrict__ group_sum, int64_t ng, int64_t nb,
+                                                     float *__restrict__ offset) {
+  __shared__ double s_sum[kMeanRuns * kMeanLd];
+  __shared__ double s_run[kMeanRuns];
+  const double total = mean_fold(group_sum, ng, s_sum, s_run);
   if (threadIdx.x == 0) *offset = (float)(total / (double)nb);
 }
 
-// One wave per group, four block constants per lane.
-__global__ __launch_bounds__(256) void k_encode_scales(const float *__restrict__ absmax, int64_t nb,
-                                                       int64_t ng, const float *__restrict__ offset_p,
-                                                       uint8_t *__restrict__ scale_code,
-                                                       float *__restrict__ group_amax) {
-  const int lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= ng) return;
-  const float offset = *offset_p;
+// Group g's 8-bit constants, by one wave: four block constants per lane.
+__device__ __forceinline__ void encode_group(const float *__restrict__ absmax, int64_t nb, int64_t g, float offset,
+                                             int lane, uint8_t *__restrict__ scale_code,
+                                             float *__restrict__ group_amax) {
   const int64_t b0 = g * kGroup + lane * 4;
   float dev[4];
   float m = 0.f;
@@ -259,6 +265,36 @@ __global__ __launch_bounds__(256) void k_encode_scales(const float *__restrict__
   if (lane == 0) group_amax[g] = m;
 }
 
+// One wave per group.
+__global__ __launch_bounds__(256) void k_encode_scales(const float *__restrict__ absmax, int64_t nb,
+                                                       int64_t ng, const float *__restrict__ offset_p,
+                                                       uint8_t *__restrict__ scale_code,
+                                                       float *__restrict__ group_amax) {
+  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g >= ng) return;
+  encode_group(absmax, nb, g, *offset_p, (int)threadIdx.x & 63, scale_code, group_amax);
+}
+
+// Both in one launch when the group sums fit one staging pass (ng <=
+// kMeanRuns * kMeanRun): every workgroup folds the mean itself, in the same
+// order (so all hold the same offset, and workgroup 0 stores it), then its
+// 16 waves encode groups blockIdx.x * 16 + wave, strided by the grid.
+constexpr int64_t kFusedMeanMaxGroups = (int64_t)kMeanRuns * kMeanRun;
+__global__ __launch_bounds__(kMeanLanes) void k_mean_encode(const double *__restrict__ group_sum,
+                                                            const float *__restrict__ absmax, int64_t nb,
+                                                            int64_t ng, float *__restrict__ offset_out,
+                                                            uint8_t *__restrict__ scale_code,
+                                                            float *__restrict__ group_amax) {
+  __shared__ double s_sum[kMeanRuns * kMeanLd];
+  __shared__ double s_run[kMeanRuns];
+  const double total = mean_fold(group_sum, ng, s_sum, s_run);
+  const float offset = (float)(total / (double)nb);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *offset_out = offset;
+  const int wave = (int)threadIdx.x >> 6;
+  for (int64_t g = (int64_t)blockIdx.x * (kMeanLanes / 64) + wave; g < ng; g += (int64_t)gridDim.x * (kMeanLanes / 64))
+    encode_group(absmax, nb, g, offset, (int)threadIdx.x & 63, scale_code, group_amax);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, bool single_level, uint8_t *packed,
@@ -270,6 +306,12 @@ hipError_t launch_quantize(const float *W, int64_t n, int64_t k, int codebook, b
   QLORA_LAUNCH("k_quantize_blocks", k_quantize_blocks, dim3((unsigned)ng), dim3(256), 0, s, W, nb, codebook_thresholds(codebook), packed,
                      ws_absmax, ws_group_sum);
   if (single_level) return hipGetLastError();
+  if (ng <= kFusedMeanMaxGroups) {  // one staging pass: mean and encoding in one launch
+    const int64_t grid = std::min<int64_t>(256, ceil_div(ng, (int64_t)(kMeanLanes / 64)));
+    QLORA_LAUNCH("k_mean_encode", k_mean_encode, dim3((unsigned)grid), dim3(kMeanLanes), 0, s, ws_group_sum,
+                 ws_absmax, nb, ng, offset, scale_code, group_amax);
+    return hipGetLastError();
+  }
   QLORA_LAUNCH("k_mean", k_mean, dim3(1), dim3(kMeanLanes), 0, s, ws_group_sum, ng, nb, offset);
   QLORA_LAUNCH("k_encode_scales", k_encode_scales, dim3((unsigned)ceil_div(ng, 4)), dim3(256), 0, s, ws_absmax, nb, ng,
                      offset, scale_code, group_amax);

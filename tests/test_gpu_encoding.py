@@ -118,14 +118,18 @@ def test_q_proj_full_tensor(q):
     _full_check(q, I.weight(w, 0), "q_proj_7b")
 
 
-def test_mean_offset_past_one_staging_pass(q):
-    """A weight of 4,259,840 blocks (16,640 groups, 65 runs of group sums):
-    the mean's run folds take two passes through LDS.  One nonzero per block
-    makes every absmax a known draw, so the oracle's offset, scale codes and
-    group constants come from those values alone; the packed codes of every
-    block's first byte are checked too (the nonzero codes to the top or
-    bottom level, the rest to zero)."""
-    n, k = 8192, 33280  # 520 blocks per row
+@pytest.mark.parametrize("k", [32768, 33280])
+def test_mean_offset_past_one_staging_pass(q, k):
+    """A weight of 4,194,304 blocks (k = 32768: 16,384 groups, 64 runs of
+    group sums, the most one staging pass holds, so the mean and the scale
+    encoding share one launch) or 4,259,840 blocks (k = 33280: 16,640
+    groups, 65 runs: the mean's run folds take two passes through LDS, in a
+    launch of their own).  One nonzero per block makes every absmax a known
+    draw, so the oracle's offset, scale codes and group constants come from
+    those values alone; the packed codes of every block's first byte are
+    checked too (the nonzero codes to the top or bottom level, the rest to
+    zero)."""
+    n = 8192  # k / 64 blocks per row
     nb = n * k // 64
     note(f"[encoding] mean over {nb} blocks, {-(-nb // 256)} groups")
     rng = np.random.default_rng(21)
