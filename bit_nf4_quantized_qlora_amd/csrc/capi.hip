@@ -310,6 +310,19 @@ int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t 
   return elementwise(2, "qlora_add_bf16", a, b, nullptr, out, nullptr, count, stream);
 }
 
+int qlora_add_bf16_n(const uint16_t *const *xs, int n, uint16_t *out, int64_t count, hipStream_t stream) {
+  if (n < 2 || n > 4) return fail(QLORA_ERR_BAD_SHAPE, "n = %d (2..4 summands)", n);
+  if (count < 0 || count > kMaxElems) return fail(QLORA_ERR_BAD_SHAPE, "count = %lld", (long long)count);
+  if (count == 0) return QLORA_OK;
+  if (!xs) return fail(QLORA_ERR_NULL_ARG, "xs is NULL");
+  for (int i = 0; i < n; ++i)
+    if (int e = check_tensor(xs[i], "summand")) return e;
+  if (int e = check_tensor(out, "output")) return e;
+  hipError_t e = launch_add_chain(xs, n, out, count, stream);
+  if (e != hipSuccess) return hip_fail(e, "qlora_add_bf16_n");
+  return QLORA_OK;
+}
+
 namespace {
 // Shapes the attention calls accept; 0 = valid.
 int check_attention(int64_t batch, int64_t seq, int64_t heads, int64_t d) {

@@ -45,6 +45,8 @@ hipError_t launch_attention_bwd(const uint16_t *Q, const uint16_t *K, const uint
                                 int64_t batch, int64_t seq, int64_t heads, int64_t d, void *ws, hipStream_t s);
 hipError_t launch_swiglu(int op, const uint16_t *x0, const uint16_t *x1, const uint16_t *x2, uint16_t *y0,
                          uint16_t *y1, int64_t count, hipStream_t s);
+// y = the left-to-right bf16-rounded sum of xs[0 .. n-1], 2 <= n <= 4.
+hipError_t launch_add_chain(const uint16_t *const *xs, int n, uint16_t *y, int64_t count, hipStream_t s);
 
 // adamw.hip: one AdamW step over count parameters (m, v may be host memory
 // the device addresses).

@@ -67,7 +67,56 @@ __global__ __launch_bounds__(256) void k_elementwise(const uint16_t *__restrict_
   }
 }
 
+// out = bf16(...bf16(bf16(x0 + x1) + x2)... + x[n-1]), n = 2..4: each
+// addition in float32 and rounded to bf16 before the next, left to right --
+// the same operations, in the same order, as n - 1 chained k_add_bf16
+// launches, in one pass (no intermediate written or read back).
+__global__ __launch_bounds__(256) void k_add_chain(const uint16_t *__restrict__ x0, const uint16_t *__restrict__ x1,
+                                                   const uint16_t *__restrict__ x2, const uint16_t *__restrict__ x3,
+                                                   int n, uint16_t *__restrict__ y, int64_t count) {
+  const int64_t i0 = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+  if (i0 >= count) return;
+  auto rnd = [](float v) { return __uint_as_float((uint32_t)f32_to_bf16_bits(v) << 16); };
+  if (i0 + 8 <= count) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(x0 + i0);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t *>(x1 + i0);
+    u32x4_t c = {0u, 0u, 0u, 0u}, d = {0u, 0u, 0u, 0u};
+    if (n > 2) c = *reinterpret_cast<const u32x4_t *>(x2 + i0);
+    if (n > 3) d = *reinterpret_cast<const u32x4_t *>(x3 + i0);
+    u32x4_t r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float lo = bf(a[q], 0) + bf(b[q], 0), hi = bf(a[q], 1) + bf(b[q], 1);
+      if (n > 2) {
+        lo = rnd(lo) + bf(c[q], 0);
+        hi = rnd(hi) + bf(c[q], 1);
+      }
+      if (n > 3) {
+        lo = rnd(lo) + bf(d[q], 0);
+        hi = rnd(hi) + bf(d[q], 1);
+      }
+      r[q] = bf16x2_rne(lo, hi);
+    }
+    *reinterpret_cast<u32x4_t *>(y + i0) = r;
+  } else {
+    for (int64_t i = i0; i < count; ++i) {
+      float v = bf(x0[i], 0) + bf(x1[i], 0);
+      if (n > 2) v = rnd(v) + bf(x2[i], 0);
+      if (n > 3) v = rnd(v) + bf(x3[i], 0);
+      y[i] = f32_to_bf16_bits(v);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_add_chain(const uint16_t *const *xs, int n, uint16_t *y, int64_t count, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  const dim3 grid((unsigned)ceil_div(ceil_div(count, 8), 256));
+  QLORA_LAUNCH("k_add_chain", k_add_chain, grid, dim3(256), 0, s, xs[0], xs[1], n > 2 ? xs[2] : nullptr,
+               n > 3 ? xs[3] : nullptr, n, y, count);
+  return hipGetLastError();
+}
 
 hipError_t launch_swiglu(int op, const uint16_t *x0, const uint16_t *x1, const uint16_t *x2, uint16_t *y0,
                          uint16_t *y1, int64_t count, hipStream_t s) {

@@ -47,8 +47,7 @@ class DecoderLayer:
         self.act.update({k: bf(inter) for k in ("gate", "up", "h")})
         self.lse = torch.empty(batch, heads, seq, dtype=torch.float32, device=device)
         self.H = {n: torch.empty(M, r, dtype=torch.float32, device=device) for n in PROJ}
-        self.grad = {k: bf(hidden) for k in ("dq", "dk", "dv", "dattn", "dxg", "dxu", "t", "dy1", "dxq", "dxk",
-                                             "dxv", "t2", "t3")}
+        self.grad = {k: bf(hidden) for k in ("dq", "dk", "dv", "dattn", "dxg", "dxu", "dy1", "dxq", "dxk", "dxv")}
         self.grad.update({k: bf(inter) for k in ("dh", "dgate", "dup")})
         self.dA = {n: torch.empty_like(adapters[n][0]) for n in PROJ}
         self.dB = {n: torch.empty_like(adapters[n][1]) for n in PROJ}
@@ -102,14 +101,11 @@ class DecoderLayer:
         Q.qlora_swiglu_bwd(a["gate"], a["up"], g["dh"], g["dgate"], g["dup"])
         self._bwd("gate", a["y1"], g["dgate"], g["dxg"])
         self._bwd("up", a["y1"], g["dup"], g["dxu"])
-        Q.qlora_add_bf16(g["dxg"], g["dxu"], g["t"])
-        Q.qlora_add_bf16(dY, g["t"], g["dy1"])
+        Q.qlora_add_bf16_n([g["dxg"], g["dxu"], dY], g["dy1"])      # bf16(bf16(dxg + dxu) + dY)
         self._bwd("o", a["attn"], g["dy1"], g["dattn"])
         Q.qlora_attention_bwd(a["q"], a["k"], a["v"], g["dattn"], self.lse, g["dq"], g["dk"], g["dv"],
                               self.batch, self.seq, self.heads, self.d, self.ws)
         self._bwd("q", X, g["dq"], g["dxq"])
         self._bwd("k", X, g["dk"], g["dxk"])
         self._bwd("v", X, g["dv"], g["dxv"])
-        Q.qlora_add_bf16(g["dxq"], g["dxk"], g["t2"])
-        Q.qlora_add_bf16(g["t2"], g["dxv"], g["t3"])
-        Q.qlora_add_bf16(g["dy1"], g["t3"], dX)
+        Q.qlora_add_bf16_n([g["dxq"], g["dxk"], g["dxv"], g["dy1"]], dX)  # ((dxq + dxk) + dxv) + dy1

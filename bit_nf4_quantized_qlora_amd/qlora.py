@@ -102,6 +102,7 @@ _SIGS = {
                                      _vp, _c_size, _vp]),
     "qlora_swiglu_bwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "qlora_add_bf16": (_c_int, [_vp, _vp, _vp, _c_i64, _vp]),
+    "qlora_add_bf16_n": (_c_int, [ctypes.POINTER(_vp), _c_int, _vp, _c_i64, _vp]),
     "qlora_adamw_step": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_i64, _c_float, _c_float, _c_float, _c_float, _c_float,
                                   _c_i64, _vp]),
     "qlora_merge_adapters": (_c_int, [_WX, _vp, _vp, _c_int, _c_float, _vp, _WX, _vp, _c_size, _vp]),
@@ -399,6 +400,16 @@ def qlora_add_bf16(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor, stream=N
     _need(a, torch.bfloat16, "a")
     _same_numel("a", a, (b, "b"), (out, "out"))
     _check("qlora_add_bf16", _lib.qlora_add_bf16(_ptr(a), _ptr(b), _ptr(out), a.numel(), _stream(stream)))
+
+
+def qlora_add_bf16_n(xs, out: torch.Tensor, stream=None) -> None:
+    """out = the left-to-right bf16-rounded sum of the 2..4 tensors in xs."""
+    for i, t in enumerate(xs):
+        _need(t, torch.bfloat16, f"xs[{i}]")
+    _need(out, torch.bfloat16, "out")
+    _same_numel("xs[0]", xs[0], *[(t, f"xs[{i}]") for i, t in enumerate(xs) if i > 0], (out, "out"))
+    ptrs = (_vp * len(xs))(*[_ptr(t) for t in xs])
+    _check("qlora_add_bf16_n", _lib.qlora_add_bf16_n(ptrs, len(xs), _ptr(out), out.numel(), _stream(stream)))
 
 
 def qlora_attention_workspace_bytes(batch: int, seq: int, heads: int, head_dim: int) -> int:

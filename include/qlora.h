@@ -284,6 +284,15 @@ int qlora_swiglu_fwd(const uint16_t *gate, const uint16_t *up, uint16_t *h, int6
 int qlora_swiglu_bwd(const uint16_t *gate, const uint16_t *up, const uint16_t *dh, uint16_t *d_gate, uint16_t *d_up,
                      int64_t count, hipStream_t stream);
 int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t count, hipStream_t stream);
+/* The sum of n = 2..4 bf16 tensors (host array xs of n device pointers, each
+ * 16-byte aligned, count elements) in one pass: out = bf16(...bf16(bf16(
+ * xs[0] + xs[1]) + xs[2]) ... + xs[n-1]), every addition in float32 and
+ * rounded to bf16 before the next, so it equals n - 1 chained qlora_add_bf16
+ * calls bit for bit (the layer backward's sums of input gradients).  out may
+ * alias xs[0].  QLORA_ERR_BAD_SHAPE for n outside 2..4 or a bad count,
+ * QLORA_ERR_NULL_ARG / _MISALIGNED for the pointers; nothing is launched
+ * then. */
+int qlora_add_bf16_n(const uint16_t *const *xs, int n, uint16_t *out, int64_t count, hipStream_t stream);
 
 /*
  * The causal attention core between the q/k/v and o projections of the

@@ -204,6 +204,13 @@ def test_argument_errors_enqueue_nothing(q):
     assert lib.qlora_swiglu_fwd(P, P, None, 8, None) == q.QLORA_ERR_NULL_ARG
     assert lib.qlora_swiglu_bwd(P, P, ctypes.c_void_p(24), P, P, 8, None) == q.QLORA_ERR_MISALIGNED
     assert lib.qlora_add_bf16(P, P, P, -1, None) == q.QLORA_ERR_BAD_SHAPE
+    xs = (ctypes.c_void_p * 4)(P, P, P, P)
+    assert lib.qlora_add_bf16_n(xs, 1, P, 8, None) == q.QLORA_ERR_BAD_SHAPE
+    assert lib.qlora_add_bf16_n(xs, 5, P, 8, None) == q.QLORA_ERR_BAD_SHAPE
+    assert lib.qlora_add_bf16_n(None, 3, P, 8, None) == q.QLORA_ERR_NULL_ARG
+    assert lib.qlora_add_bf16_n(xs, 3, None, 8, None) == q.QLORA_ERR_NULL_ARG
+    assert lib.qlora_add_bf16_n((ctypes.c_void_p * 2)(P, 24), 2, P, 8, None) == q.QLORA_ERR_MISALIGNED
+    assert lib.qlora_add_bf16_n(None, 2, None, 0, None) == q.QLORA_OK                          # count 0
     adam = lib.qlora_adamw_step
     assert adam(P, None, P, P, P, 16, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0, None) == q.QLORA_ERR_BAD_SHAPE   # step 0
     assert adam(P, None, P, P, P, 16, 1e-3, 1.0, 0.999, 1e-8, 0.0, 1, None) == q.QLORA_ERR_BAD_ALPHA   # beta1 = 1

@@ -61,6 +61,34 @@ def test_swiglu_elementwise(q, count, seed):
     assert np.array_equal(host_bf16(s), want), "add"
 
 
+@pytest.mark.parametrize("count,seed", [(9, 3), (1000003, 4)])
+def test_add_chain_equals_chained_adds(q, count, seed):
+    """qlora_add_bf16_n over 2, 3 and 4 summands: bit for bit the chained
+    qlora_add_bf16 calls and the float32 sums rounded to bf16 after each
+    addition (left to right); also with the output aliasing the first
+    summand.  The values mix magnitudes so the intermediate roundings show."""
+    note(f"[mlp] add chain count={count}")
+    rng = np.random.default_rng(seed)
+    xs = [rb(rng.standard_normal(count) * 10.0 ** rng.integers(-3, 4, count)) for _ in range(4)]
+    X = [dev_bf16(x) for x in xs]
+    for n in (2, 3, 4):
+        out = torch.empty_like(X[0])
+        q.qlora_add_bf16_n(X[:n], out)
+        chained = X[0].clone()
+        for j in range(1, n):
+            q.qlora_add_bf16(chained, X[j], chained)
+        alias = X[0].clone()
+        q.qlora_add_bf16_n([alias] + X[1:n], alias)
+        torch.cuda.synchronize()
+        want = xs[0]                                   # bf16 bit patterns throughout
+        for j in range(1, n):
+            want = rb(f64(want).astype(np.float32) + f64(xs[j]).astype(np.float32))
+        got = host_bf16(out)
+        assert np.array_equal(got, host_bf16(chained)), f"n={n}: chained calls"
+        assert np.array_equal(got, host_bf16(alias)), f"n={n}: aliased output"
+        assert np.array_equal(got, want), f"n={n}: reference"
+
+
 def test_mlp_block_composed(q):
     """A small LLaMA-style block: gate, up (n = 320), SwiGLU, down (k = 192),
     M = 70, rank 8, every projection with its own adapters; backward with
