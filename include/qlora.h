@@ -289,7 +289,8 @@ int qlora_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *out, int64_t 
  * xs[0] + xs[1]) + xs[2]) ... + xs[n-1]), every addition in float32 and
  * rounded to bf16 before the next, so it equals n - 1 chained qlora_add_bf16
  * calls bit for bit (the layer backward's sums of input gradients).  out may
- * alias xs[0].  QLORA_ERR_BAD_SHAPE for n outside 2..4 or a bad count,
+ * be the same pointer as any xs[i] (each element is read before it is
+ * written); partly overlapping buffers are not allowed.  QLORA_ERR_BAD_SHAPE for n outside 2..4 or a bad count,
  * QLORA_ERR_NULL_ARG / _MISALIGNED for the pointers; nothing is launched
  * then. */
 int qlora_add_bf16_n(const uint16_t *const *xs, int n, uint16_t *out, int64_t count, hipStream_t stream);
