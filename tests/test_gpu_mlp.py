@@ -65,8 +65,8 @@ def test_swiglu_elementwise(q, count, seed):
 def test_add_chain_equals_chained_adds(q, count, seed):
     """qlora_add_bf16_n over 2, 3 and 4 summands: bit for bit the chained
     qlora_add_bf16 calls and the float32 sums rounded to bf16 after each
-    addition (left to right); also with the output aliasing the first
-    summand.  The values mix magnitudes so the intermediate roundings show."""
+    addition (left to right); also with the output aliasing the first or
+    the last summand.  The values mix magnitudes so the intermediate roundings show."""
     note(f"[mlp] add chain count={count}")
     rng = np.random.default_rng(seed)
     xs = [rb(rng.standard_normal(count) * 10.0 ** rng.integers(-3, 4, count)) for _ in range(4)]
@@ -79,13 +79,16 @@ def test_add_chain_equals_chained_adds(q, count, seed):
             q.qlora_add_bf16(chained, X[j], chained)
         alias = X[0].clone()
         q.qlora_add_bf16_n([alias] + X[1:n], alias)
+        alias_last = X[n - 1].clone()
+        q.qlora_add_bf16_n(X[:n - 1] + [alias_last], alias_last)
         torch.cuda.synchronize()
         want = xs[0]                                   # bf16 bit patterns throughout
         for j in range(1, n):
             want = rb(f64(want).astype(np.float32) + f64(xs[j]).astype(np.float32))
         got = host_bf16(out)
         assert np.array_equal(got, host_bf16(chained)), f"n={n}: chained calls"
-        assert np.array_equal(got, host_bf16(alias)), f"n={n}: aliased output"
+        assert np.array_equal(got, host_bf16(alias)), f"n={n}: output aliasing the first summand"
+        assert np.array_equal(got, host_bf16(alias_last)), f"n={n}: output aliasing the last summand"
         assert np.array_equal(got, want), f"n={n}: reference"
 
 
