@@ -250,18 +250,19 @@ def _per_tile_blocks(k: int, rng) -> list:
     return sorted(picks)
 
 
-def _sampled(q, wname, li, m=None, backward=True):
+def _sampled(q, wname, li, m=None, backward=True, codebook="nf4", scales="dq"):
     """Full-size layer on samples that touch every 256 x 256 output tile of
     every launch: Y on rows of every m tile x columns of every n tile, H on
     those rows; dX and dA on one 64-column block of every k tile over all M;
-    dB on the sampled rows of every n tile."""
+    dB on the sampled rows of every n tile.  codebook / scales pick the
+    storage type (the oracle's weights follow it)."""
     wl = I.WORKLOADS[wname]
     m = m or wl.ms[0]
     W, X, A, B, dY = _workload_inputs(wl, li, m)
     n, k = W.shape
-    plan = q.qlora_linear_plan(m, n, k, wl.r)
-    note(f"[linear] {wname}[{li}] W={W.shape} M={m} sampled per tile, plan {plan}")
-    lin = Linear(q, gpu_quantize(q, W), X, A, B, wl.r, wl.alpha)
+    plan = q.qlora_linear_plan(m, n, k, wl.r, q.QLORA_SCALES_FP32 if scales == "fp32" else q.QLORA_SCALES_DQ)
+    note(f"[linear] {wname}[{li}] W={W.shape} M={m} {codebook}/{scales} sampled per tile, plan {plan}")
+    lin = Linear(q, gpu_quantize(q, W, codebook, scales), X, A, B, wl.r, wl.alpha)
     Y, H = lin.fwd()
     if backward:
         dX, dA, dB = lin.bwd(dY, H=H)
@@ -271,7 +272,7 @@ def _sampled(q, wname, li, m=None, backward=True):
     ms = _per_tile(m, rng, per=4)
     kbs = _per_tile_blocks(k, rng)
     kcols = np.concatenate([np.arange(64 * b, 64 * b + 64) for b in kbs])
-    ow = OracleWeight(W)
+    ow = OracleWeight(W, codebook, scales)
     Xf, Af, Bf, dYf = bf16_f64(X), bf16_f64(A), bf16_f64(B), bf16_f64(dY)
     Yr, Hr = fwd(Xf[ms], bf16_f64(ow.row_what_bits(ns)), Af, Bf[ns], wl.alpha)
     assert_close(bf16_f64(host_bf16(Y))[np.ix_(ms, ns)], Yr, f"{wname}[{li}] Y")
@@ -285,6 +286,14 @@ def _sampled(q, wname, li, m=None, backward=True):
     assert_close(bf16_f64(host_bf16(dA))[:, kcols], dAr, f"{wname}[{li}] dA")
     _, _, dBr, _ = bwd(Xf, dYf[:, ns], bf16_f64(ow.row_what_bits(ns)), Af, Bf[ns], wl.alpha, H=Hfull)
     assert_close(bf16_f64(host_bf16(dB))[ns], dBr, f"{wname}[{li}] dB")
+
+
+@pytest.mark.parametrize("codebook,scales", [("fp4", "dq"), ("fp4_e3m0", "dq"), ("nf4", "fp32")])
+def test_storage_types_full_size_sampled(q, codebook, scales):
+    """The comparison storage types at the 7B gate layer's full shape
+    (M = 4096: 688 forward tiles in three rounds, 256 input-gradient tiles),
+    every output tile of both launches compared on samples."""
+    _sampled(q, "mlp_7b", 0, codebook=codebook, scales=scales)
 
 
 def _full_size(q, wname, li):
