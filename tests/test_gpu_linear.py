@@ -342,6 +342,15 @@ def test_up_65b_small_m(q, m):
     _sampled(q, "up_65b", 0, m=m, backward=False)
 
 
+@pytest.mark.parametrize("m,codebook", [(1, "nf4"), (16, "fp4_e3m0")])
+def test_up_65b_small_m_single_level(q, m, codebook):
+    """The small-M GEMV on single-level constants at the 65B up_proj shape
+    (2,752 four-block units over 256 workgroups: ranges straddle row
+    groups), sampled in every 256-row group."""
+    assert q.qlora_linear_plan(m, 22016, 8192, 16, q.QLORA_SCALES_FP32)["fwd_path"] == q.QLORA_PATH_GEMV
+    _sampled(q, "up_65b", 0, m=m, backward=False, codebook=codebook, scales="fp32")
+
+
 @pytest.mark.parametrize("li", range(7))
 def test_block_65b(q, li):
     _sampled(q, "block_65b", li)
