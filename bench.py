@@ -1009,6 +1009,24 @@ def small_m_rows(q, I, np, torch, dev, dev16, ev, copies=6):
             row["kernel_us"] = round(kus, 2)
             row["kernel_gbps_packed"] = round(packed_bytes / (kus * 1e-6) / 1e9, 1)
             row["kernel_frac_hbm_peak"] = round(packed_bytes / (kus * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)
+        if key == "M1":  # the same calls as one replayed HIP graph (a decode loop's usual form)
+            def calls():
+                for i in range(copies):
+                    q.qlora_linear_fwd(ws_list[i], X, Ad, Bd, wl.r, wl.alpha, Y, H, lws)
+
+            def timed_g(fn, n):
+                a, b = ev(), ev()
+                a.record()
+                for _ in range(n):
+                    fn()
+                b.record()
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) / n
+
+            gms, same = graph_step(torch, calls, [Y, H], timed_g, 10)
+            row["graph"] = {"us": round(1e3 * gms / copies, 2), "replays_equal_eager": same,
+                            "how": f"the {copies} rotating calls captured once as a HIP graph and replayed 10 "
+                                   "times (per call: no host launch cost); replays compared bit for bit first"}
         out[key] = row
     del W, qws
     return out
