@@ -57,17 +57,24 @@ __device__ __forceinline__ void run_transpose(const SmallJob &j, uint32_t idx, u
   }
 }
 
-// Sum over s < S of part[s * stride + src], in order of s: the first kSumBatch
-// loads are issued together, so the sum waits for memory once.
-constexpr int kSumBatch = 8;
+// Sum over s < S of part[s * stride + src], in order of s.  The loads go out
+// a batch at a time, all before any is used: up to 8 splits (the adapter
+// gradients' products) in one short batch; the H and G products at M = 512
+// split their contraction 16-29 ways, which take batches of 32, so the sum
+// waits for memory once per batch rather than once per split.
+template <int kBatch>
+__device__ __forceinline__ float sum_batch(const float *part, int s0, int S, size_t stride, size_t src, float acc) {
+  float v[kBatch];
+#pragma unroll
+  for (int s = 0; s < kBatch; ++s) v[s] = s0 + s < S ? part[(size_t)(s0 + s) * stride + src] : 0.f;
+#pragma unroll
+  for (int s = 0; s < kBatch; ++s) acc += v[s];  // the zeros past S leave acc unchanged (acc is never -0)
+  return acc;
+}
 __device__ __forceinline__ float sum_splits(const float *part, int S, size_t stride, size_t src) {
-  float v[kSumBatch];
-#pragma unroll
-  for (int s = 0; s < kSumBatch; ++s) v[s] = s < S ? part[s * stride + src] : 0.f;
+  if (S <= 8) return sum_batch<8>(part, 0, S, stride, src, 0.f);
   float acc = 0.f;
-#pragma unroll
-  for (int s = 0; s < kSumBatch; ++s) acc += v[s];
-  for (int s = kSumBatch; s < S; ++s) acc += part[s * stride + src];
+  for (int s0 = 0; s0 < S; s0 += 32) acc = sum_batch<32>(part, s0, S, stride, src, acc);
   return acc;
 }
 
@@ -143,31 +150,91 @@ __device__ __forceinline__ void row_quad_scales(const Nf4View &w, int64_t n, int
     if (kTileSup * kq + u < nkb) v[u] = w.absmax ? __uint_as_float(c8[u]) : block_scale(c8[u], ga[u], off);
 }
 
+// The scale tables are built one thread per (row, run of kRun consecutive
+// quads of its blocks), so each thread reads kRun consecutive scale-code
+// words of its row and the row's other quads -- the rest of the same 128-byte
+// lines -- are read by the neighbouring workgroups, which k_small_jobs keeps
+// on one XCD (one fetch of each line into that XCD's L2).  Thread t: row t %
+// 256 of a 256-row tile, run (t / 256) % runs, tile (t / 256) / runs.
+constexpr int kRun = 4;
+
+// The block scales of row n, quads q0 .. q0 + kRun - 1 (blocks 4 q0 ..);
+// zero past k/64 or n.  Bit for bit row_quad_scales, with every load of the
+// run issued before any use.
+__device__ __forceinline__ void row_run_scales(const Nf4View &w, int64_t n, int64_t q0,
+                                               float (&v)[kRun][kTileSup]) {
+  const int64_t nkb = w.k / kBlock;
+  // quads straddling rows, or absmax values not 16-byte aligned: block by block
+  if (nkb % kTileSup != 0 || (w.absmax && (reinterpret_cast<uintptr_t>(w.absmax) & 15) != 0)) {
+#pragma unroll
+    for (int u = 0; u < kRun; ++u) row_quad_scales(w, n, q0 + u, v[u]);
+    return;
+  }
+  const int64_t nq = nkb / kTileSup;
+#pragma unroll
+  for (int u = 0; u < kRun; ++u)
+#pragma unroll
+    for (int b = 0; b < kTileSup; ++b) v[u][b] = 0.f;
+  if (n >= w.n) return;
+  const int64_t b0 = n * nkb + kTileSup * q0;
+  if (w.absmax) {  // single-level: the absmax values themselves, four per 16-byte load
+    f32x4_t a[kRun];
+#pragma unroll
+    for (int u = 0; u < kRun; ++u)
+      a[u] = q0 + u < nq ? *reinterpret_cast<const f32x4_t *>(w.absmax + b0 + kTileSup * u)
+                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kRun; ++u)
+#pragma unroll
+      for (int b = 0; b < kTileSup; ++b) v[u][b] = a[u][b];
+    return;
+  }
+  uint32_t word[kRun];
+  float ga[kRun];
+#pragma unroll
+  for (int u = 0; u < kRun; ++u) {
+    const bool in = q0 + u < nq;
+    word[u] = in ? *reinterpret_cast<const uint32_t *>(w.scale_code + b0 + kTileSup * u) : 0u;
+    ga[u] = in ? w.group_amax[(b0 + kTileSup * u) / kGroup] : 0.f;
+  }
+  const float off = *w.offset;
+#pragma unroll
+  for (int u = 0; u < kRun; ++u)
+    if (q0 + u < nq)
+#pragma unroll
+      for (int b = 0; b < kTileSup; ++b) v[u][b] = block_scale((word[u] >> (8 * b)) & 0xFFu, ga[u], off);
+}
+
 // Forward scale table: for weight tile to (rows 256to ..) and super-step sp
 // (blocks 4sp .. 4sp+3 of each row) one contiguous 4 KB run,
 // Sp[((to*nsup + sp)*256 + row)*4 + q]; rows past n and blocks past k/64 hold
-// 0.
+// 0.  A wave's store covers 64 consecutive rows (1 KB).
 __device__ __forceinline__ void run_scales_fwd(const SmallJob &j, uint32_t t) {
-  const uint32_t nsup = (uint32_t)j.a;
-  const uint32_t q = t >> 8, to = q / nsup, sp = q - to * nsup;
-  float v[kTileSup];
-  row_quad_scales(j.w, (int64_t)to * kTileRows + (t & 255), sp, v);
-  *reinterpret_cast<f32x4_t *>(static_cast<float *>(j.out) + 4 * t) = f32x4_t{v[0], v[1], v[2], v[3]};
+  const uint32_t nsup = (uint32_t)j.a, runs = (nsup + kRun - 1) / kRun;
+  const uint32_t q = t >> 8, to = q / runs, sp0 = (q - to * runs) * kRun, row = t & 255;
+  float v[kRun][kTileSup];
+  row_run_scales(j.w, (int64_t)to * kTileRows + row, sp0, v);
+  f32x4_t *out = reinterpret_cast<f32x4_t *>(j.out) + ((size_t)to * nsup + sp0) * 256 + row;
+#pragma unroll
+  for (int u = 0; u < kRun; ++u)
+    if (sp0 + u < nsup) out[u * 256] = f32x4_t{v[u][0], v[u][1], v[u][2], v[u][3]};
 }
 
 // Backward scale table: for column tile tk (k-blocks 4tk .. 4tk+3) and
 // super-step sp (weight rows 256sp .. 256sp+255) one contiguous 4 KB run,
 // Sp[((tk*nsup + sp)*4 + blk)*256 + row]; rows past n and blocks past k/64
-// hold 0.  One thread per (tk, sp, row): the row's four scales, four
-// coalesced stores.
+// hold 0.  A wave's store covers 64 consecutive rows of one block (256 B).
 __device__ __forceinline__ void run_scales_bwd(const SmallJob &j, uint32_t t) {
-  const uint32_t nsup = (uint32_t)j.a;
-  const uint32_t q = t >> 8, tk = q / nsup, sp = q - tk * nsup;
-  float v[kTileSup];
-  row_quad_scales(j.w, (int64_t)sp * kTileRows + (t & 255), tk, v);
-  float *out = static_cast<float *>(j.out) + (size_t)q * 4 * 256 + (t & 255);
+  const uint32_t nsup = (uint32_t)j.a, ntk = (uint32_t)j.b, runs = (ntk + kRun - 1) / kRun;
+  const uint32_t q = t >> 8, sp = q / runs, tk0 = (q - sp * runs) * kRun, row = t & 255;
+  float v[kRun][kTileSup];
+  row_run_scales(j.w, (int64_t)sp * kTileRows + row, tk0, v);
+  float *out = static_cast<float *>(j.out) + ((size_t)tk0 * nsup + sp) * 4 * 256 + row;
 #pragma unroll
-  for (int blk = 0; blk < kTileSup; ++blk) out[blk * 256] = v[blk];
+  for (int u = 0; u < kRun; ++u)
+    if (tk0 + u < ntk)
+#pragma unroll
+      for (int blk = 0; blk < kTileSup; ++blk) out[((size_t)u * nsup * 4 + blk) * 256] = v[u][blk];
 }
 
 __global__ __launch_bounds__(256) void k_small_jobs(SmallJobs js) {
@@ -176,7 +243,13 @@ __global__ __launch_bounds__(256) void k_small_jobs(SmallJobs js) {
   int q = 0;
   while (q + 1 < js.n && blk >= js.start[q + 1]) ++q;
   const SmallJob &j = js.j[q];
-  const uint32_t idx = (uint32_t)(blk - js.start[q]) * 256u + threadIdx.x;
+  uint32_t lb = (uint32_t)(blk - js.start[q]);
+  // scale tables: consecutive runs of one row tile share code lines, so a
+  // contiguous range of them goes to each XCD (blocks are dealt to the XCDs
+  // round-robin)
+  if (j.kind == kJobScalesFwd || j.kind == kJobScalesBwd)
+    lb = (uint32_t)xcd_tile((int)lb, (int)(js.start[q + 1] - js.start[q]));
+  const uint32_t idx = lb * 256u + threadIdx.x;
   if (idx >= j.count) return;
   switch (j.kind) {
     case kJobTranspose: run_transpose(j, idx, t); break;
@@ -282,7 +355,7 @@ SmallJob job_scales_fwd(const Nf4View &w, float *scales) {
   SmallJob j;
   j.kind = kJobScalesFwd;
   j.a = tile_fwd_nsup(w.k);
-  j.count = ceil_div(w.n, kTileRows) * j.a * 256;
+  j.count = ceil_div(w.n, kTileRows) * ceil_div(j.a, kRun) * 256;
   j.out = scales;
   j.w = w;
   return j;
@@ -292,7 +365,8 @@ SmallJob job_scales_bwd(const Nf4View &w, float *scales) {
   SmallJob j;
   j.kind = kJobScalesBwd;
   j.a = tile_bwd_nsup(w.n);
-  j.count = ceil_div(w.k, kTileRows) * j.a * 256;
+  j.b = ceil_div(w.k, kTileRows);  // column tiles of four blocks
+  j.count = j.a * ceil_div(j.b, kRun) * 256;
   j.out = scales;
   j.w = w;
   return j;
