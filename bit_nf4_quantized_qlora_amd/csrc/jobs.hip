@@ -164,8 +164,7 @@ constexpr int kRun = 4;
 __device__ __forceinline__ void row_run_scales(const Nf4View &w, int64_t n, int64_t q0,
                                                float (&v)[kRun][kTileSup]) {
   const int64_t nkb = w.k / kBlock;
-  // quads straddling rows, or absmax values not 16-byte aligned: block by block
-  if (nkb % kTileSup != 0 || (w.absmax && (reinterpret_cast<uintptr_t>(w.absmax) & 15) != 0)) {
+  if (nkb % kTileSup != 0) {  // quads straddle rows: block by block
 #pragma unroll
     for (int u = 0; u < kRun; ++u) row_quad_scales(w, n, q0 + u, v[u]);
     return;
@@ -177,7 +176,8 @@ __device__ __forceinline__ void row_run_scales(const Nf4View &w, int64_t n, int6
     for (int b = 0; b < kTileSup; ++b) v[u][b] = 0.f;
   if (n >= w.n) return;
   const int64_t b0 = n * nkb + kTileSup * q0;
-  if (w.absmax) {  // single-level: the absmax values themselves, four per 16-byte load
+  if (w.absmax) {  // single-level: the absmax values themselves, four per 16-byte load (the C ABI
+                   // requires the buffer 16-byte aligned, and b0 is a multiple of 4)
     f32x4_t a[kRun];
 #pragma unroll
     for (int u = 0; u < kRun; ++u)
